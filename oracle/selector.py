@@ -1,0 +1,151 @@
+"""Block summaries, block scores, candidates and top-k selection (float64, CPU).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+The method, as the COBS explainer states it:
+
+* Keys are grouped into contiguous, non-overlapping blocks (technical summary
+  section 1; section 5 names "non-overlapping blocks").  Block b holds tokens
+  [b*S, (b+1)*S).  Only complete blocks have a summary; the reading is that a
+  partly filled tail block is never a candidate and its tokens are reached only
+  through the window.
+* Selection oracle (section 2.1): the ideal ranking orders blocks by their
+  attention mass m_b = sum over the block's keys of exp(q.k).  The explainer
+  prints the exponent without the softmax scale; the reading taken is that the
+  mass is the one of the attention actually run, so q is scaled by 1/sqrt(d)
+  first (attention glossary, step 2).  ``exact_mass_scores`` is this ranking.
+* Cumulant expansion (section 2.2): ln m_b = ln L + q.kappa1 + 1/2 q^T kappa2 q + ...
+  with kappa1 the block's mean key and kappa2 its key covariance.  The
+  reading of L is the number of keys in the block (the expansion is that of
+  the log of a sum of L exponentials); it is the same for every complete
+  block, so it is dropped from the score, as the COBS score drops it.  kappa2
+  is the second cumulant of the block's empirical key distribution, so it is
+  normalised by 1/L (not 1/(L-1)).
+* First-order score (section 2.2): q.mean.  Second-order COBS score
+  (section 2.3): q.mean + 1/2 q^T Sigma q, with Sigma replaced by its top-r
+  eigenpairs (low-rank factorisation, section 2.3): 1/2 sum_i lambda_i (v_i.q)^2.
+  The factor is stored as rows sqrt(lambda_i) v_i; r <= 8 (section 4.3).
+* Grouped heads (attention glossary FAQ Q2: query heads share a K/V head).
+  Reading: one block set per K/V head, ranked by the log of the group's summed
+  mass, ln sum_h m_{b,h}; each m_{b,h} is estimated by exp(score_{b,h}).
+* Forced tokens (SWA glossary "SWAの拡張手法": sink tokens always attended;
+  sliding window; local-global glossary: global tokens).  The decode query is
+  the last cached token t = n - 1 and the window [t-W+1, t] contains it.
+  Candidates are complete blocks with at least one token outside the forced
+  set; the top-k are chosen among them, in addition to the forced tokens.
+* Top-k: largest group score first, equal scores broken by the lower block
+  index; the chosen indices are returned in ascending order, padded with -1
+  when there are fewer than k candidates.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+
+def block_summaries(K, S, rank):
+    """Per complete block of ``K`` [n, d]: mean [NB, d] and low-rank factor [NB, rank, d].
+
+    factor[b, i] = sqrt(lambda_i) * v_i for the i-th largest eigenpair of the block's
+    covariance Sigma_b = (1/L) sum_r (k_r - mean)(k_r - mean)^T, L = S.  Eigenvalues below
+    zero (rounding) are clamped to 0.  Each row's sign is fixed so that its entry of
+    largest magnitude (first such entry on ties) is positive; the sign never changes a
+    score because the score only uses squares of projections.
+    """
+    K = np.asarray(K, dtype=np.float64)
+    n, d = K.shape
+    nb = n // S
+    X = K[: nb * S].reshape(nb, S, d)
+    mean = X.mean(axis=1)
+    if rank == 0:
+        return mean, np.zeros((nb, 0, d))
+    if not 0 < rank <= d:
+        raise ValueError("rank must be in [0, d]")
+    C = X - mean[:, None, :]
+    sigma = np.einsum("brd,bre->bde", C, C) / S
+    lam, vec = np.linalg.eigh(sigma)  # ascending; vec[:, :, i] is the i-th eigenvector
+    lam = lam[:, ::-1][:, :rank]
+    vec = vec[:, :, ::-1][:, :, :rank]
+    lam = np.clip(lam, 0.0, None)
+    rows = np.transpose(vec, (0, 2, 1)) * np.sqrt(lam)[:, :, None]  # [nb, rank, d]
+    big = np.argmax(np.abs(rows), axis=2)
+    sign = np.sign(np.take_along_axis(rows, big[:, :, None], axis=2))
+    sign[sign == 0] = 1.0
+    return mean, rows * sign
+
+
+def head_scores(q_scaled, mean, factor=None):
+    """Per-head block scores s[h, b] for scaled queries ``q_scaled`` [G, d].
+
+    First order: q.mean.  With a factor [NB, r, d] (r > 0) the COBS second-order term
+    1/2 sum_i (factor_i . q)^2 = 1/2 q^T (sum_i lambda_i v_i v_i^T) q is added.
+    """
+    q = np.asarray(q_scaled, dtype=np.float64)
+    s = q @ np.asarray(mean, dtype=np.float64).T
+    if factor is not None and factor.shape[1] > 0:
+        proj = np.einsum("hd,brd->hbr", q, np.asarray(factor, dtype=np.float64))
+        s = s + 0.5 * (proj ** 2).sum(axis=2)
+    return s
+
+
+def exact_mass_scores(q_scaled, K, S):
+    """Log attention mass of every complete block: s*[h, b] = ln sum_{j in b} exp(q_h.k_j).
+
+    This is the selection oracle's ranking (COBS explainer section 2.1), which reads every
+    key; it serves as a reference ranking and a diagnostic, not as a selector on the path.
+    """
+    q = np.asarray(q_scaled, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    nb = K.shape[0] // S
+    logits = (q @ K[: nb * S].T).reshape(q.shape[0], nb, S)
+    m = logits.max(axis=2, keepdims=True)
+    return (m + np.log(np.exp(logits - m).sum(axis=2, keepdims=True)))[:, :, 0]
+
+
+def group_scores(s):
+    """Group score per block: ln sum_h exp(s[h, b]) over the query heads sharing a K/V head."""
+    s = np.asarray(s, dtype=np.float64)
+    m = s.max(axis=0)
+    return m + np.log(np.exp(s - m).sum(axis=0))
+
+
+def forced_token_mask(n, n_sink, window, global_pos=()):
+    """Tokens every decode step attends: sinks [0, n_sink), window [t-W+1, t], globals.
+
+    t = n - 1 is the query's own position.  Sizes past n are clamped; ``window`` <= 0
+    means no window.
+    """
+    forced = np.zeros(n, dtype=bool)
+    forced[: max(0, min(n_sink, n))] = True
+    if window > 0:
+        t = n - 1
+        forced[max(0, t - window + 1): t + 1] = True
+    g = np.asarray(global_pos, dtype=np.int64)
+    if g.size:
+        if g.min() < 0 or g.max() >= n:
+            raise ValueError("global position out of range")
+        forced[g] = True
+    return forced
+
+
+def candidate_blocks(n, S, forced):
+    """Complete blocks ((b+1)*S <= n) holding at least one token outside ``forced``."""
+    nb = n // S
+    if nb == 0:
+        return np.zeros(0, dtype=np.int64)
+    not_forced = ~np.asarray(forced[: nb * S]).reshape(nb, S)
+    return np.nonzero(not_forced.any(axis=1))[0]
+
+
+def top_k_blocks(score, cand, k):
+    """The k best candidates by (score descending, block index ascending), in ascending order.
+
+    Returns an int64 array of length k padded with -1 when fewer than k candidates exist.
+    """
+    cand = np.asarray(cand, dtype=np.int64)
+    score = np.asarray(score, dtype=np.float64)
+    order = sorted(cand.tolist(), key=lambda b: (-score[b], b))
+    chosen = sorted(order[:k])
+    out = np.full(k, -1, dtype=np.int64)
+    out[: len(chosen)] = chosen
+    return out

@@ -1,0 +1,270 @@
+"""Pins of the oracle's block summaries, scores, candidates and top-k (CPU only).
+
+The pins come from outside the oracle's own code: exact identities of the
+cumulant expansion (single-token blocks, a two-point block in closed form,
+the O(eps^3) remainder), numpy's covariance routine, torch's softmax, planted
+spectra with known eigenpairs, and brute force over all subsets.
+"""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import (block_summaries, candidate_blocks, exact_mass_scores, forced_token_mask,
+                    group_scores, head_scores, top_k_blocks)
+from synthetic import WORKLOADS
+
+
+# ---------------------------------------------------------------- summaries
+
+
+def test_factor_rows_are_eigenpairs_of_the_population_covariance():
+    rng = np.random.default_rng(0)
+    S, d, r = 16, 8, 4
+    K = rng.standard_normal((3 * S, d))
+    mean, factor = block_summaries(K, S, r)
+    for b in range(3):
+        X = K[b * S:(b + 1) * S]
+        np.testing.assert_allclose(mean[b], X.mean(axis=0), atol=1e-15)
+        cov = np.cov(X, rowvar=False, bias=True)  # 1/L normalisation
+        lam = np.einsum("id,id->i", factor[b], factor[b])
+        assert np.all(np.diff(lam) <= 1e-12), "eigenvalues must be descending"
+        for i in range(r):
+            v = factor[b, i] / math.sqrt(lam[i])
+            np.testing.assert_allclose(cov @ v, lam[i] * v, atol=1e-12)
+            assert abs(np.linalg.norm(v) - 1) < 1e-12
+            assert factor[b, i][np.argmax(np.abs(factor[b, i]))] > 0
+        gram = factor[b] @ factor[b].T
+        np.testing.assert_allclose(gram - np.diag(np.diag(gram)), 0, atol=1e-12)
+        # the top-r eigenvalues of numpy's covariance, from a separate routine
+        ref = np.sort(np.linalg.eigvalsh(cov))[::-1][:r]
+        np.testing.assert_allclose(lam, ref, atol=1e-12)
+
+
+def test_full_rank_factor_reproduces_the_trace_and_matrix():
+    rng = np.random.default_rng(1)
+    S, d = 16, 6
+    K = rng.standard_normal((S, d))
+    _, factor = block_summaries(K, S, d)
+    cov = np.cov(K, rowvar=False, bias=True)
+    np.testing.assert_allclose(factor[0].T @ factor[0], cov, atol=1e-12)
+    assert abs((factor[0] ** 2).sum() - np.trace(cov)) < 1e-12
+
+
+def test_planted_spike_closed_form():
+    """Keys mu + a_r u: mean mu + mean(a) u, one eigenpair (var(a), u), the rest zero."""
+    rng = np.random.default_rng(2)
+    S, d = 64, 16
+    mu = rng.standard_normal(d)
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    a = rng.standard_normal(S) * 3
+    K = mu[None, :] + a[:, None] * u[None, :]
+    mean, factor = block_summaries(K, S, 3)
+    np.testing.assert_allclose(mean[0], mu + a.mean() * u, atol=1e-13)
+    var = ((a - a.mean()) ** 2).mean()
+    expect = math.sqrt(var) * u * np.sign(u[np.argmax(np.abs(u))])
+    np.testing.assert_allclose(factor[0, 0], expect, atol=1e-12)
+    np.testing.assert_allclose(factor[0, 1:], 0, atol=1e-7)
+
+
+def test_rank_is_at_most_block_length_minus_one():
+    rng = np.random.default_rng(3)
+    S, d = 4, 10
+    K = rng.standard_normal((S, d))
+    _, factor = block_summaries(K, S, 8)
+    lam = (factor[0] ** 2).sum(axis=1)
+    assert (lam[: S - 1] > 1e-6).all()
+    np.testing.assert_allclose(lam[S - 1:], 0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- scores
+
+
+def test_single_token_blocks_make_every_score_the_exact_log_mass():
+    """S = 1: mean = k, covariance 0, so first order = second order = ln exp(q.k) exactly,
+    and the group score is torch's logsumexp of the group's scaled logits."""
+    rng = np.random.default_rng(4)
+    G, n, d = 4, 9, 8
+    q = rng.standard_normal((G, d)) / math.sqrt(d)
+    K = rng.standard_normal((n, d))
+    mean, factor = block_summaries(K, 1, 3)
+    s1 = head_scores(q, mean)
+    s2 = head_scores(q, mean, factor)
+    s_star = exact_mass_scores(q, K, 1)
+    np.testing.assert_allclose(s2, s1, atol=1e-15)
+    np.testing.assert_allclose(s_star, s1, atol=1e-14)
+    ref = torch.logsumexp(torch.from_numpy(q) @ torch.from_numpy(K).T, dim=0).numpy()
+    np.testing.assert_allclose(group_scores(s2), ref, atol=1e-13)
+
+
+def test_exact_mass_matches_torch_softmax_block_sums():
+    """exp(s*_b) / sum_b' exp(s*_b') is the softmax weight landing in block b."""
+    rng = np.random.default_rng(5)
+    n, d, S = 256, 16, 32
+    q = rng.standard_normal((1, d)) / 4
+    K = rng.standard_normal((n, d))
+    s_star = exact_mass_scores(q, K, S)[0]
+    p = torch.softmax(torch.from_numpy(q[0]) @ torch.from_numpy(K).T, dim=0).numpy()
+    block_mass = p.reshape(-1, S).sum(axis=1)
+    frac = np.exp(s_star - s_star.max())
+    np.testing.assert_allclose(frac / frac.sum(), block_mass, atol=1e-14)
+
+
+@pytest.mark.parametrize("delta", [1e-3, 0.05, 0.3, 1.0])
+def test_two_point_block_closed_forms(delta):
+    """Keys mu +- delta u.  Exact: s* - ln 2 - q.mu = ln cosh(delta q.u).
+    COBS second order: s2 - q.mu = 1/2 (delta q.u)^2 (covariance delta^2 u u^T with 1/L)."""
+    rng = np.random.default_rng(6)
+    d = 8
+    mu, u = rng.standard_normal(d), rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    q = rng.standard_normal((1, d))
+    K = np.vstack([mu + delta * u, mu - delta * u])
+    mean, factor = block_summaries(K, 2, 1)
+    x = delta * float(q[0] @ u)
+    qmu = float(q[0] @ mu)
+    s_star = exact_mass_scores(q, K, 2)[0, 0]
+    s2 = head_scores(q, mean, factor)[0, 0]
+    assert abs((s_star - math.log(2) - qmu) - math.log(math.cosh(x))) < 1e-12
+    assert abs((s2 - qmu) - 0.5 * x * x) < 1e-12
+    # both agree to leading order: ln cosh x = x^2/2 - x^4/12 + ...
+    assert abs((s_star - math.log(2)) - s2) <= x ** 4 / 12 + 1e-12
+
+
+def test_full_rank_second_order_equals_the_quadratic_form():
+    rng = np.random.default_rng(7)
+    S, d, G = 32, 8, 3
+    K = rng.standard_normal((2 * S, d))
+    q = rng.standard_normal((G, d)) / math.sqrt(d)
+    mean, factor = block_summaries(K, S, d)
+    s2 = head_scores(q, mean, factor)
+    for b in range(2):
+        cov = np.cov(K[b * S:(b + 1) * S], rowvar=False, bias=True)
+        expect = q @ K[b * S:(b + 1) * S].mean(axis=0) + 0.5 * np.einsum("hd,de,he->h", q, cov, q)
+        np.testing.assert_allclose(s2[:, b], expect, atol=1e-12)
+
+
+def test_second_order_remainder_is_third_order_in_the_spread():
+    """Keys mu + eps z: s* - ln L - s2 = O(eps^3) (cumulant expansion, COBS explainer 2.2),
+    while the first-order remainder is O(eps^2)."""
+    rng = np.random.default_rng(8)
+    S, d = 64, 8
+    mu, Z = rng.standard_normal(d), rng.standard_normal((S, d))
+    Z -= Z.mean(axis=0)
+    Z[:, 0] += 0.8 * (Z[:, 1] ** 2 - (Z[:, 1] ** 2).mean())  # some skew, so the cubic term is nonzero
+    q = rng.standard_normal((1, d))
+    res2, res1 = [], []
+    for eps in (0.02, 0.01):
+        K = mu + eps * Z
+        mean, factor = block_summaries(K, S, d)
+        s_star = exact_mass_scores(q, K, S)[0, 0]
+        res2.append(abs(s_star - math.log(S) - head_scores(q, mean, factor)[0, 0]))
+        res1.append(abs(s_star - math.log(S) - head_scores(q, mean)[0, 0]))
+    assert 6.0 < res2[0] / res2[1] < 10.0
+    assert 3.0 < res1[0] / res1[1] < 5.0
+
+
+def test_group_score_of_identical_heads_adds_log_g():
+    s = np.array([[0.3, -1.0, 2.0]] * 4)
+    np.testing.assert_allclose(group_scores(s), s[0] + math.log(4), atol=1e-15)
+    np.testing.assert_array_equal(group_scores(s[:1]), s[0])
+
+
+def test_group_score_is_the_log_of_the_group_exact_mass():
+    """With exact masses the group score is the log of the group's total softmax numerator
+    over the block: torch logsumexp over (head, token) pairs."""
+    rng = np.random.default_rng(9)
+    G, n, d, S = 4, 128, 8, 16
+    q = rng.standard_normal((G, d)) / math.sqrt(d)
+    K = rng.standard_normal((n, d))
+    gs = group_scores(exact_mass_scores(q, K, S))
+    logits = (torch.from_numpy(q) @ torch.from_numpy(K).T).reshape(G, n // S, S)
+    ref = torch.logsumexp(logits.permute(1, 0, 2).reshape(n // S, -1), dim=1).numpy()
+    np.testing.assert_allclose(gs, ref, atol=1e-13)
+
+
+# ---------------------------------------------------------------- forced set and candidates
+
+
+@pytest.mark.parametrize("name,first,last", [
+    ("tiny_decode_1k", 1, 14), ("first_order_decode_32k", 1, 503), ("cobs_decode_128k", 1, 2031)])
+def test_candidates_of_the_workloads(name, first, last):
+    w = WORKLOADS[name]
+    forced = forced_token_mask(w.n_ctx, w.n_sink, w.window)
+    cand = candidate_blocks(w.n_ctx, w.block_size, forced)
+    np.testing.assert_array_equal(cand, np.arange(first, last + 1))
+
+
+def test_forced_set_edges():
+    f = forced_token_mask(10, 3, 4, (5,))
+    assert f.tolist() == [1, 1, 1, 0, 0, 1, 1, 1, 1, 1]
+    assert forced_token_mask(5, 100, 0).all()
+    assert forced_token_mask(5, 0, 100).all()
+    assert not forced_token_mask(5, 0, 0).any()
+    with pytest.raises(ValueError):
+        forced_token_mask(5, 0, 0, (5,))
+
+
+def test_candidates_skip_tail_and_fully_forced_blocks():
+    S = 4
+    # n = 18: blocks 0..3 complete, tokens 16, 17 form a tail block
+    forced = forced_token_mask(18, 4, 3, (8, 9, 10, 11, 13))
+    # block 0 = sinks (forced), block 2 = globals 8..11 (forced), block 3 has 13 forced only
+    assert candidate_blocks(18, S, forced).tolist() == [1, 3]
+    assert candidate_blocks(3, S, forced_token_mask(3, 0, 1)).tolist() == []
+
+
+# ---------------------------------------------------------------- top-k
+
+
+def _brute_top_k(score, cand, k):
+    best = None
+    for sub in itertools.combinations(cand, min(k, len(cand))):
+        key = (sum(score[b] for b in sub), -sum(sub))
+        if best is None or key > best[0]:
+            best = (key, sub)
+    return sorted(best[1])
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_top_k_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    nb = 10
+    score = np.round(rng.standard_normal(nb), 1)  # coarse values: ties happen
+    cand = np.sort(rng.choice(nb, size=8, replace=False))
+    for k in (1, 3, 5, 8, 12):
+        got = top_k_blocks(score, cand, k)
+        ref = _brute_top_k(score, cand.tolist(), k)
+        assert got[: len(ref)].tolist() == ref
+        assert (got[len(ref):] == -1).all()
+
+
+def test_top_k_ties_prefer_lower_index_and_output_ascends():
+    score = np.array([1.0, 5.0, 5.0, 5.0, 0.0])
+    assert top_k_blocks(score, np.arange(5), 2).tolist() == [1, 2]
+    assert top_k_blocks(score, np.array([4, 3, 2]), 2).tolist() == [2, 3]
+
+
+def test_top_k_with_exact_mass_captures_the_most_attention():
+    """Ranking by exact mass (COBS explainer 2.1) maximises the softmax mass kept."""
+    rng = np.random.default_rng(12)
+    n, d, S = 96, 8, 8
+    q = rng.standard_normal((1, d)) / 2
+    K = rng.standard_normal((n, d))
+    s_star = exact_mass_scores(q, K, S)[0]
+    p = torch.softmax(torch.from_numpy(q[0]) @ torch.from_numpy(K).T, dim=0).numpy().reshape(-1, S).sum(1)
+    cand = np.arange(n // S)
+    got = top_k_blocks(s_star, cand, 3)
+    best = max(itertools.combinations(cand, 3), key=lambda sub: p[list(sub)].sum())
+    assert got.tolist() == sorted(best)
+
+
+def test_rank_guidance_of_the_page(golden_dir):
+    facts = json.load(open(os.path.join(golden_dir, "pages_printed.json")))
+    assert WORKLOADS["cobs_decode_128k"].rank <= facts["cobs_rank_guidance"]["max_rank"]
