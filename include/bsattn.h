@@ -1,0 +1,179 @@
+/*
+ * bsattn.h -- block-sparse, sliding-window and local+global attention on
+ * AMD Instinct MI355X (gfx950).  C ABI: plain pointers and sizes only.
+ *
+ * Sources, cited by page title and section:
+ *  [COBS]  "COBS: Cumulant Order Block Sparse Attention", explainer at
+ *          gist.science/ja/paper/2607.09052, technical summary sections
+ *          1 (problem: decode is bound by reading the KV cache), 2.1
+ *          (selection by attention mass), 2.2 (cumulant expansion), 2.3
+ *          (second-order score, low-rank covariance), 4.3 (rank <= 8).
+ *  [ATT]   "LLMアテンション機構" (LLM attention mechanism), jisaku.com glossary:
+ *          the four steps of scaled dot-product attention; GQA (FAQ Q2);
+ *          KV cache section.
+ *  [SWA]   "スライディングウィンドウアテンション" (sliding window attention),
+ *          jisaku.com glossary: band matrix (概要と動作原理), sink and
+ *          global extensions (SWAの拡張手法), skipping tiles outside the
+ *          window (FlashAttentionとの組み合わせ).
+ *  [LG]    "ローカル・グローバルアテンション" (local-global attention),
+ *          jisaku.com glossary: local window, bidirectional global tokens,
+ *          uniform placement of globals.
+ *
+ * Conventions shared by every call
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    allocates nothing and keeps no state between calls.  Host arrays are
+ *    marked _host and are read during the call only.
+ *  - Calls are asynchronous on the given HIP stream (NULL = default stream).
+ *    Every argument is checked on the host before any launch; a bad argument
+ *    returns BSATTN_ERR_INVALID or BSATTN_ERR_UNSUPPORTED and launches nothing.
+ *    A failed launch returns BSATTN_ERR_HIP.  Faults inside a kernel surface
+ *    at the caller's next synchronisation.  bsattn_last_error() gives a
+ *    message for the last failure on the calling thread.
+ *  - Layouts are dense, row-major (C order), 16-byte aligned base pointers:
+ *      decode  Q [B, Hq, d],          O [B, Hq, d] fp32, lse [B, Hq] fp32
+ *      prefill Q [B, Hq, N, d],       O [B, Hq, N, d] fp32, lse [B, Hq, N] fp32
+ *      K, V    [B, Hkv, kv_capacity, d]  (token t of (b, g) at row t)
+ *      mean    [B, Hkv, nblk_capacity, d] fp32
+ *      factor  [B, Hkv, nblk_capacity, rank, d] fp32
+ *  - GQA [ATT FAQ Q2]: query head h reads K/V head h / (Hq / Hkv).
+ *  - Blocks [COBS 1, 2.1]: block j holds tokens [j*S, (j+1)*S); only complete
+ *    blocks ((j+1)*S <= n_ctx) have summaries and can be selected.
+ *  - Softmax scale: shape.scale, or 1/sqrt(d) when it is 0 [ATT step 2].
+ *    lse is the natural log of the softmax normaliser of the scaled logits.
+ */
+#ifndef BSATTN_H
+#define BSATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BSATTN_OK = 0,
+  BSATTN_ERR_INVALID = 1,     /* argument out of range, NULL, inconsistent shape  */
+  BSATTN_ERR_UNSUPPORTED = 2, /* valid request this build does not implement       */
+  BSATTN_ERR_HIP = 3,         /* a HIP launch or runtime call failed               */
+  BSATTN_ERR_WORKSPACE = 4    /* workspace missing or smaller than required        */
+} bsattn_status;
+
+typedef enum { BSATTN_F32 = 0, BSATTN_BF16 = 1 } bsattn_dtype;
+
+typedef struct {
+  int32_t batch;       /* B >= 1                                                   */
+  int32_t n_q_heads;   /* Hq >= 1, a multiple of n_kv_heads                        */
+  int32_t n_kv_heads;  /* Hkv >= 1                                                 */
+  int32_t head_dim;    /* d: 64 or 128                                             */
+  int32_t n_ctx;       /* decode: tokens in the cache; prefill: sequence length N  */
+  int32_t kv_capacity; /* token stride of K/V per (b, kv head), >= n_ctx           */
+  int32_t block_size;  /* S: 64                                                    */
+  float scale;         /* softmax scale; 0 => 1/sqrt(d)                             */
+  int32_t dtype;       /* bsattn_dtype of Q, K, V                                   */
+} bsattn_shape;
+
+#define BSATTN_MAX_RANK 8        /* [COBS 4.3]: rank <= 8 recommended               */
+#define BSATTN_MAX_GLOBAL 256    /* global token positions per call                  */
+#define BSATTN_MAX_TOP_K 1024
+#define BSATTN_MAX_BLOCKS 65536  /* complete blocks per (b, kv head) for selection   */
+#define BSATTN_MAX_GROUP 16      /* query heads per K/V head (Hq / Hkv)              */
+
+/*
+ * Per-block key summaries [COBS 2.2, 2.3].
+ * For every (b, g) and every block j in [first_block, first_block + n_blocks):
+ *   mean[b,g,j,:]     = (1/L) sum_{t in block j} K[b,g,t,:]          (L = S)
+ *   factor[b,g,j,i,:] = sqrt(lambda_i) v_i, i < rank, the i-th largest
+ *                       eigenpair of Sigma = (1/L) sum (k - mean)(k - mean)^T,
+ *                       sign fixed so the entry of largest magnitude is > 0;
+ *                       eigenvalues below 0 clamp to 0.
+ * Built once per block, as blocks fill (incremental use: pass the new range).
+ * K dtype: F32 or BF16.  rank in [0, BSATTN_MAX_RANK]; factor may be NULL
+ * when rank == 0.  Requires (first_block + n_blocks) * S <= n_ctx and
+ * first_block + n_blocks <= nblk_capacity.  n_blocks == 0 is a no-op.
+ */
+bsattn_status bsattn_build_summaries(const bsattn_shape* shape, const void* K, int32_t rank,
+                                     int32_t first_block, int32_t n_blocks,
+                                     int32_t nblk_capacity, float* mean, float* factor,
+                                     void* hip_stream);
+
+/*
+ * Block selection for the decode query (the last cached token, t = n_ctx - 1).
+ *  1. Per query head h and complete block j, with q~ = scale * Q[b,h]:
+ *       s[h,j] = q~ . mean_j                                (rank == 0) [COBS 2.2]
+ *       s[h,j] = q~ . mean_j + 1/2 sum_i (factor_{j,i} . q~)^2  (rank > 0) [COBS 2.3]
+ *  2. Group score per K/V head g: scores[b,g,j] = ln sum_{h in g} exp(s[h,j]),
+ *     the log of the group's estimated attention mass [COBS 2.1].
+ *  3. Forced tokens F: [0, n_sink) sinks [SWA 拡張手法], the window
+ *     [t - window + 1, t] [SWA], and the global positions [LG].
+ *     Candidates: complete blocks with at least one token outside F.
+ *  4. sel[b,g,:] = the top_k candidates by (score descending, index
+ *     ascending), written in ascending order, padded with -1.
+ * Q: [B,Hq,d] of shape.dtype.  mean/factor as built above (factor NULL iff
+ * rank == 0).  scores: REQUIRED [B,Hkv,nblk_capacity] fp32; entries of complete
+ * blocks are written (it is also the buffer the top-k pass reads).
+ * global_pos_host: sorted, unique, in [0, n_ctx), n_global <= BSATTN_MAX_GLOBAL.
+ * top_k in [1, BSATTN_MAX_TOP_K]; n_ctx / S <= BSATTN_MAX_BLOCKS.
+ * window >= 0 (0: no window), n_sink >= 0; sizes past n_ctx are clamped.
+ */
+bsattn_status bsattn_select_topk(const bsattn_shape* shape, const void* Q, const float* mean,
+                                 const float* factor, int32_t rank, int32_t nblk_capacity,
+                                 int32_t top_k, int32_t window, int32_t n_sink,
+                                 const int32_t* global_pos_host, int32_t n_global, int32_t* sel,
+                                 float* scores, void* hip_stream);
+
+/* Bytes of device workspace bsattn_decode needs for these arguments (0 if invalid). */
+size_t bsattn_decode_workspace_bytes(const bsattn_shape* shape, int32_t top_k, int32_t window,
+                                     int32_t n_sink, int32_t n_global);
+
+/*
+ * Sparse decode [COBS 1, 2.1; SWA 拡張手法; LG]: for every query head h of
+ * K/V head g, one softmax of scale * Q[b,h] . K[b,g,t] over the token set
+ *   T = F  union  { tokens of block j : j in sel[b,g,:], j >= 0 }
+ * (a set: a token reached two ways counts once), O[b,h] = sum_T p_t V[b,g,t],
+ * lse[b,h] = ln sum_T exp(logit_t).  sel: [B,Hkv,top_k] int32 as written by
+ * bsattn_select_topk (ascending, -1 padded, each entry a complete block).
+ * dtype F32 or BF16.  workspace: device memory of at least
+ * bsattn_decode_workspace_bytes(...) bytes, 256-byte aligned, contents need
+ * not be initialised.  lse may be NULL.  Calls that share a workspace must
+ * be ordered (same stream); calls with separate workspaces may overlap.
+ */
+bsattn_status bsattn_decode(const bsattn_shape* shape, const void* Q, const void* K,
+                            const void* V, const int32_t* sel, int32_t top_k, int32_t window,
+                            int32_t n_sink, const int32_t* global_pos_host, int32_t n_global,
+                            float* O, float* lse, void* workspace, size_t ws_bytes,
+                            void* hip_stream);
+
+/*
+ * Masked prefill attention, BF16 Q/K/V, fp32 O and lse.  Query i sees key j iff
+ *   (i - window_left <= j <= i + window_right) [and j <= i when causal]
+ *   or i is a global position or j is a global position.
+ * A negative window_left / window_right means no limit on that side.
+ *  - Causal band [SWA 概要と動作原理]: window_left = w - 1, window_right = 0,
+ *    causal = 1 (each token sees itself and the w - 1 tokens before it).
+ *  - Local + global [LG]: window_left = window_right = 256, causal = 0 and
+ *    the global positions (sorted, unique, in [0, N), at most BSATTN_MAX_GLOBAL).
+ * Global tokens are bidirectional; causal = 1 with n_global > 0 returns
+ * BSATTN_ERR_UNSUPPORTED.  Key tiles wholly outside the mask are skipped
+ * [SWA FlashAttentionとの組み合わせ].  lse may be NULL.  Q/O row stride is
+ * N = n_ctx; K/V row stride is kv_capacity.
+ */
+bsattn_status bsattn_prefill(const bsattn_shape* shape, const void* Q, const void* K,
+                             const void* V, int32_t window_left, int32_t window_right,
+                             int32_t causal, const int32_t* global_pos_host, int32_t n_global,
+                             float* O, float* lse, void* hip_stream);
+
+/* Static description of a status code. */
+const char* bsattn_status_string(bsattn_status status);
+
+/* Message describing the last failed call on this thread ("" if none). */
+const char* bsattn_last_error(void);
+
+/* Library version string. */
+const char* bsattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSATTN_H */

@@ -1,0 +1,121 @@
+"""Python binding of the bsattn C ABI (include/bsattn.h).
+
+Argument marshalling only: every function takes torch tensors that already live
+on the GPU (PyTorch is used for device memory and streams), checks their dtype
+and layout, and passes raw pointers to the same-named C entry point.  All the
+work runs in the HIP kernels of libbsattn.so; there is no CPU path and no
+fallback.  A non-OK status raises ``BsattnError``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+
+from . import _lib
+from ._lib import BSATTN_BF16, BSATTN_F32, Shape
+
+__all__ = [
+    "BsattnError", "Shape", "make_shape", "library", "bsattn_build_summaries",
+    "bsattn_select_topk", "bsattn_decode_workspace_bytes", "bsattn_decode", "bsattn_prefill",
+    "bsattn_status_string", "bsattn_version", "BSATTN_F32", "BSATTN_BF16",
+]
+
+
+class BsattnError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+def library():
+    """The loaded ctypes library (raises OSError if it was never built)."""
+    return _lib.load()
+
+
+def make_shape(batch, n_q_heads, n_kv_heads, head_dim, n_ctx, kv_capacity=None, block_size=64,
+               scale=0.0, dtype="bf16"):
+    dt = {"bf16": BSATTN_BF16, "f32": BSATTN_F32}[dtype] if isinstance(dtype, str) else int(dtype)
+    return Shape(batch, n_q_heads, n_kv_heads, head_dim, n_ctx,
+                 n_ctx if kv_capacity is None else kv_capacity, block_size, float(scale), dt)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _globals(global_pos):
+    g = [] if global_pos is None else [int(x) for x in global_pos]
+    arr = (ctypes.c_int32 * max(1, len(g)))(*g)
+    return (arr if g else None), len(g)
+
+
+def _check(status):
+    if status != 0:
+        lib = library()
+        msg = lib.bsattn_last_error().decode() or lib.bsattn_status_string(status).decode()
+        raise BsattnError(status, msg)
+
+
+def bsattn_status_string(status):
+    return library().bsattn_status_string(status).decode()
+
+
+def bsattn_version():
+    return library().bsattn_version().decode()
+
+
+def bsattn_build_summaries(shape, K, rank, first_block, n_blocks, nblk_capacity, mean, factor=None,
+                           stream=None):
+    _check(library().bsattn_build_summaries(ctypes.byref(shape), _ptr(K), rank, first_block,
+                                            n_blocks, nblk_capacity, _ptr(mean), _ptr(factor),
+                                            _stream(stream)))
+
+
+def bsattn_select_topk(shape, Q, mean, factor, rank, nblk_capacity, top_k, window, n_sink,
+                       global_pos, sel, scores, stream=None):
+    g, ng = _globals(global_pos)
+    _check(library().bsattn_select_topk(ctypes.byref(shape), _ptr(Q), _ptr(mean), _ptr(factor),
+                                        rank, nblk_capacity, top_k, window, n_sink, g, ng,
+                                        _ptr(sel), _ptr(scores), _stream(stream)))
+
+
+def bsattn_decode_workspace_bytes(shape, top_k, window, n_sink, n_global=0):
+    return int(library().bsattn_decode_workspace_bytes(ctypes.byref(shape), top_k, window, n_sink,
+                                                       n_global))
+
+
+def bsattn_decode(shape, Q, K, V, sel, top_k, window, n_sink, global_pos, O, lse, workspace,
+                  stream=None):
+    g, ng = _globals(global_pos)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(library().bsattn_decode(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(sel),
+                                   top_k, window, n_sink, g, ng, _ptr(O), _ptr(lse),
+                                   _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def bsattn_prefill(shape, Q, K, V, window_left, window_right, causal, global_pos, O, lse=None,
+                   stream=None):
+    g, ng = _globals(global_pos)
+    _check(library().bsattn_prefill(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), window_left,
+                                    window_right, int(bool(causal)), g, ng, _ptr(O), _ptr(lse),
+                                    _stream(stream)))
+
+
+def default_scale(head_dim):
+    return 1.0 / math.sqrt(head_dim)

@@ -1,0 +1,305 @@
+// C-ABI entry points: host-side validation, the forced-token description of a
+// decode step, workspace sizing, and kernel launches.  Every check runs before
+// any launch; the library allocates nothing and keeps no state.
+#include "../../include/bsattn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+bsattn_status fail(bsattn_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+float effective_scale(const bsattn_shape* s) {
+  return s->scale != 0.f ? s->scale : 1.0f / std::sqrt((float)s->head_dim);
+}
+
+bsattn_status check_shape(const bsattn_shape* s, bool decode) {
+  if (s == nullptr) return fail(BSATTN_ERR_INVALID, "shape is NULL");
+  if (s->batch < 1 || s->n_q_heads < 1 || s->n_kv_heads < 1)
+    return fail(BSATTN_ERR_INVALID, "batch and head counts must be >= 1");
+  if (s->n_q_heads % s->n_kv_heads != 0)
+    return fail(BSATTN_ERR_INVALID, "n_q_heads (%d) must be a multiple of n_kv_heads (%d)",
+                s->n_q_heads, s->n_kv_heads);
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(BSATTN_ERR_UNSUPPORTED, "head_dim %d: only 64 and 128 are built", s->head_dim);
+  if (s->n_ctx < 1) return fail(BSATTN_ERR_INVALID, "n_ctx must be >= 1");
+  if (s->kv_capacity < s->n_ctx) return fail(BSATTN_ERR_INVALID, "kv_capacity < n_ctx");
+  if (s->block_size != 64) return fail(BSATTN_ERR_UNSUPPORTED, "block_size %d: only 64 is built", s->block_size);
+  if (s->dtype != BSATTN_F32 && s->dtype != BSATTN_BF16) return fail(BSATTN_ERR_INVALID, "unknown dtype %d", s->dtype);
+  if (!(s->scale >= 0.f) || !std::isfinite(s->scale)) return fail(BSATTN_ERR_INVALID, "scale must be finite and >= 0");
+  if (decode && s->n_q_heads / s->n_kv_heads > BSATTN_MAX_GROUP)
+    return fail(BSATTN_ERR_UNSUPPORTED, "query heads per K/V head must be <= %d", BSATTN_MAX_GROUP);
+  if ((long long)s->batch * s->n_kv_heads > 65535)
+    return fail(BSATTN_ERR_UNSUPPORTED, "batch * n_kv_heads must be <= 65535");
+  return BSATTN_OK;
+}
+
+bsattn_status check_globals(const int32_t* gpos, int32_t n_global, int32_t n_ctx) {
+  if (n_global < 0 || n_global > BSATTN_MAX_GLOBAL)
+    return fail(BSATTN_ERR_INVALID, "n_global must be in [0, %d]", BSATTN_MAX_GLOBAL);
+  if (n_global > 0 && gpos == nullptr) return fail(BSATTN_ERR_INVALID, "global_pos_host is NULL");
+  for (int i = 0; i < n_global; ++i) {
+    if (gpos[i] < 0 || gpos[i] >= n_ctx)
+      return fail(BSATTN_ERR_INVALID, "global position %d out of [0, %d)", gpos[i], n_ctx);
+    if (i > 0 && gpos[i] <= gpos[i - 1])
+      return fail(BSATTN_ERR_INVALID, "global positions must be sorted and unique");
+  }
+  return BSATTN_OK;
+}
+
+bsattn::ForcedSet make_forced(int32_t n_ctx, int32_t window, int32_t n_sink, const int32_t* gpos,
+                              int32_t n_global) {
+  bsattn::ForcedSet f;
+  std::memset(&f, 0, sizeof(f));
+  f.n_ctx = n_ctx;
+  f.sink_end = n_sink < 0 ? 0 : (n_sink > n_ctx ? n_ctx : n_sink);
+  const long long t = n_ctx - 1;
+  f.win_lo = window > 0 ? (int32_t)(t - window + 1 < 0 ? 0 : t - window + 1) : n_ctx;
+  f.n_global = n_global;
+  for (int i = 0; i < n_global; ++i) f.gpos[i] = gpos[i];
+  return f;
+}
+
+// Forced blocks in visiting order: sink range, window range (merged when they
+// touch), then blocks holding a global token outside both ranges.
+bsattn::ForcedBlocks make_forced_blocks(const bsattn::ForcedSet& f) {
+  bsattn::ForcedBlocks fb;
+  std::memset(&fb, 0, sizeof(fb));
+  const int S = bsattn::kBlock;
+  int s_lo = 0, s_hi = (f.sink_end + S - 1) / S;  // [s_lo, s_hi)
+  int w_lo = f.win_lo / S, w_hi = f.win_lo < f.n_ctx ? (f.n_ctx - 1) / S + 1 : w_lo;
+  if (s_hi > s_lo && w_hi > w_lo && w_lo <= s_hi) {
+    fb.r0_lo = 0;
+    fb.r0_n = (w_hi > s_hi ? w_hi : s_hi);
+  } else {
+    if (s_hi > s_lo) { fb.r0_lo = s_lo; fb.r0_n = s_hi - s_lo; }
+    if (w_hi > w_lo) {
+      if (fb.r0_n == 0) { fb.r0_lo = w_lo; fb.r0_n = w_hi - w_lo; }
+      else { fb.r1_lo = w_lo; fb.r1_n = w_hi - w_lo; }
+    }
+  }
+  int last = -1;
+  for (int i = 0; i < f.n_global; ++i) {
+    const int blk = f.gpos[i] / S;
+    const bool in0 = blk >= fb.r0_lo && blk < fb.r0_lo + fb.r0_n;
+    const bool in1 = blk >= fb.r1_lo && blk < fb.r1_lo + fb.r1_n;
+    if (in0 || in1 || blk == last) continue;
+    fb.gblk[fb.n_gblk++] = blk;
+    last = blk;
+  }
+  return fb;
+}
+
+int forced_block_bound(int32_t n_ctx, int32_t window, int32_t n_sink, int32_t n_global) {
+  bsattn::ForcedSet f = make_forced(n_ctx, window, n_sink, nullptr, 0);
+  bsattn::ForcedBlocks fb = make_forced_blocks(f);
+  return fb.r0_n + fb.r1_n + n_global;
+}
+
+size_t workspace_for(const bsattn_shape* s, int n_items) {
+  int ips, nsplit;
+  bsattn::decode_split_geometry(n_items, s->head_dim, s->dtype == BSATTN_BF16, &ips, &nsplit);
+  const size_t rows = (size_t)s->batch * s->n_q_heads * nsplit;
+  size_t o_bytes = rows * s->head_dim * sizeof(float);
+  o_bytes = (o_bytes + 255) & ~(size_t)255;
+  return o_bytes + rows * 2 * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bsattn_status_string(bsattn_status st) {
+  switch (st) {
+    case BSATTN_OK: return "ok";
+    case BSATTN_ERR_INVALID: return "invalid argument";
+    case BSATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case BSATTN_ERR_HIP: return "HIP error";
+    case BSATTN_ERR_WORKSPACE: return "workspace too small";
+  }
+  return "unknown status";
+}
+
+const char* bsattn_last_error(void) { return g_err; }
+
+const char* bsattn_version(void) { return "bsattn 0.1.0 gfx950"; }
+
+bsattn_status bsattn_build_summaries(const bsattn_shape* shape, const void* K, int32_t rank,
+                                     int32_t first_block, int32_t n_blocks, int32_t nblk_capacity,
+                                     float* mean, float* factor, void* hip_stream) {
+  g_err[0] = 0;
+  bsattn_status st = check_shape(shape, false);
+  if (st != BSATTN_OK) return st;
+  if (K == nullptr || mean == nullptr) return fail(BSATTN_ERR_INVALID, "K and mean must be non-NULL");
+  if (rank < 0 || rank > BSATTN_MAX_RANK) return fail(BSATTN_ERR_INVALID, "rank must be in [0, %d]", BSATTN_MAX_RANK);
+  if (rank > 0 && factor == nullptr) return fail(BSATTN_ERR_INVALID, "factor is NULL with rank > 0");
+  if (first_block < 0 || n_blocks < 0) return fail(BSATTN_ERR_INVALID, "negative block range");
+  if ((long long)(first_block + (long long)n_blocks) * shape->block_size > shape->n_ctx)
+    return fail(BSATTN_ERR_INVALID, "blocks past n_ctx are not complete");
+  if ((long long)first_block + n_blocks > nblk_capacity)
+    return fail(BSATTN_ERR_INVALID, "block range exceeds nblk_capacity");
+  if (!aligned16(K) || !aligned16(mean) || (factor && !aligned16(factor)))
+    return fail(BSATTN_ERR_INVALID, "device pointers must be 16-byte aligned");
+  if (n_blocks == 0) return BSATTN_OK;
+  bsattn::SummaryArgs a;
+  a.K = K; a.mean = mean; a.factor = factor;
+  a.bh = shape->batch * shape->n_kv_heads;
+  a.kv_capacity = shape->kv_capacity;
+  a.nblk_capacity = nblk_capacity;
+  a.first_block = first_block;
+  a.n_blocks = n_blocks;
+  a.rank = rank;
+  a.head_dim = shape->head_dim;
+  a.bf16 = shape->dtype == BSATTN_BF16;
+  hipError_t e = bsattn::launch_summaries(a, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return fail(BSATTN_ERR_HIP, "summaries launch: %s", hipGetErrorString(e));
+  return BSATTN_OK;
+}
+
+bsattn_status bsattn_select_topk(const bsattn_shape* shape, const void* Q, const float* mean,
+                                 const float* factor, int32_t rank, int32_t nblk_capacity,
+                                 int32_t top_k, int32_t window, int32_t n_sink,
+                                 const int32_t* global_pos_host, int32_t n_global, int32_t* sel,
+                                 float* scores, void* hip_stream) {
+  g_err[0] = 0;
+  bsattn_status st = check_shape(shape, true);
+  if (st != BSATTN_OK) return st;
+  if (Q == nullptr || mean == nullptr || sel == nullptr || scores == nullptr)
+    return fail(BSATTN_ERR_INVALID, "Q, mean, sel and scores must be non-NULL");
+  if (rank < 0 || rank > BSATTN_MAX_RANK) return fail(BSATTN_ERR_INVALID, "rank must be in [0, %d]", BSATTN_MAX_RANK);
+  if (rank > 0 && factor == nullptr) return fail(BSATTN_ERR_INVALID, "factor is NULL with rank > 0");
+  if (top_k < 1 || top_k > BSATTN_MAX_TOP_K) return fail(BSATTN_ERR_INVALID, "top_k must be in [1, %d]", BSATTN_MAX_TOP_K);
+  if (window < 0 || n_sink < 0) return fail(BSATTN_ERR_INVALID, "window and n_sink must be >= 0");
+  const int nb = shape->n_ctx / shape->block_size;
+  if (nb > BSATTN_MAX_BLOCKS) return fail(BSATTN_ERR_UNSUPPORTED, "more than %d complete blocks", BSATTN_MAX_BLOCKS);
+  if (nblk_capacity < nb) return fail(BSATTN_ERR_INVALID, "nblk_capacity < n_ctx / block_size");
+  st = check_globals(global_pos_host, n_global, shape->n_ctx);
+  if (st != BSATTN_OK) return st;
+  if (!aligned16(Q) || !aligned16(mean) || (factor && !aligned16(factor)))
+    return fail(BSATTN_ERR_INVALID, "device pointers must be 16-byte aligned");
+  bsattn::SelectArgs a;
+  a.Q = Q; a.mean = mean; a.factor = rank > 0 ? factor : nullptr; a.sel = sel; a.scores = scores;
+  a.batch = shape->batch; a.n_q_heads = shape->n_q_heads; a.n_kv_heads = shape->n_kv_heads;
+  a.head_dim = shape->head_dim;
+  a.n_blocks = nb;
+  a.nblk_capacity = nblk_capacity;
+  a.rank = rank;
+  a.top_k = top_k;
+  a.scale = effective_scale(shape);
+  a.bf16 = shape->dtype == BSATTN_BF16;
+  a.forced = make_forced(shape->n_ctx, window, n_sink, global_pos_host, n_global);
+  hipError_t e = bsattn::launch_select_topk(a, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return fail(BSATTN_ERR_HIP, "select launch: %s", hipGetErrorString(e));
+  return BSATTN_OK;
+}
+
+size_t bsattn_decode_workspace_bytes(const bsattn_shape* shape, int32_t top_k, int32_t window,
+                                     int32_t n_sink, int32_t n_global) {
+  if (check_shape(shape, true) != BSATTN_OK) return 0;
+  if (top_k < 1 || top_k > BSATTN_MAX_TOP_K || window < 0 || n_sink < 0 || n_global < 0 ||
+      n_global > BSATTN_MAX_GLOBAL)
+    return 0;
+  const int n_items = top_k + forced_block_bound(shape->n_ctx, window, n_sink, n_global);
+  return workspace_for(shape, n_items);
+}
+
+bsattn_status bsattn_decode(const bsattn_shape* shape, const void* Q, const void* K, const void* V,
+                            const int32_t* sel, int32_t top_k, int32_t window, int32_t n_sink,
+                            const int32_t* global_pos_host, int32_t n_global, float* O, float* lse,
+                            void* workspace, size_t ws_bytes, void* hip_stream) {
+  g_err[0] = 0;
+  bsattn_status st = check_shape(shape, true);
+  if (st != BSATTN_OK) return st;
+  if (Q == nullptr || K == nullptr || V == nullptr || sel == nullptr || O == nullptr)
+    return fail(BSATTN_ERR_INVALID, "Q, K, V, sel and O must be non-NULL");
+  if (top_k < 1 || top_k > BSATTN_MAX_TOP_K) return fail(BSATTN_ERR_INVALID, "top_k must be in [1, %d]", BSATTN_MAX_TOP_K);
+  if (window < 0 || n_sink < 0) return fail(BSATTN_ERR_INVALID, "window and n_sink must be >= 0");
+  st = check_globals(global_pos_host, n_global, shape->n_ctx);
+  if (st != BSATTN_OK) return st;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O))
+    return fail(BSATTN_ERR_INVALID, "device pointers must be 16-byte aligned");
+  bsattn::DecodeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.forced = make_forced(shape->n_ctx, window, n_sink, global_pos_host, n_global);
+  a.fblocks = make_forced_blocks(a.forced);
+  a.n_items = top_k + a.fblocks.r0_n + a.fblocks.r1_n + a.fblocks.n_gblk;
+  const size_t need = workspace_for(shape, a.n_items);
+  if (workspace == nullptr || ws_bytes < need)
+    return fail(BSATTN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(BSATTN_ERR_INVALID, "workspace must be 256-byte aligned");
+  bsattn::decode_split_geometry(a.n_items, shape->head_dim, shape->dtype == BSATTN_BF16,
+                                &a.items_per_split, &a.n_split);
+  const size_t rows = (size_t)shape->batch * shape->n_q_heads * a.n_split;
+  size_t o_bytes = (rows * shape->head_dim * sizeof(float) + 255) & ~(size_t)255;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+  a.Q = Q; a.K = K; a.V = V; a.sel = sel; a.O = O; a.lse = lse;
+  a.batch = shape->batch; a.n_q_heads = shape->n_q_heads; a.n_kv_heads = shape->n_kv_heads;
+  a.head_dim = shape->head_dim;
+  a.kv_capacity = shape->kv_capacity;
+  a.top_k = top_k;
+  a.scale = effective_scale(shape);
+  a.bf16 = shape->dtype == BSATTN_BF16;
+  hipError_t e = bsattn::launch_decode(a, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return fail(BSATTN_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return BSATTN_OK;
+}
+
+bsattn_status bsattn_prefill(const bsattn_shape* shape, const void* Q, const void* K, const void* V,
+                             int32_t window_left, int32_t window_right, int32_t causal,
+                             const int32_t* global_pos_host, int32_t n_global, float* O, float* lse,
+                             void* hip_stream) {
+  g_err[0] = 0;
+  bsattn_status st = check_shape(shape, false);
+  if (st != BSATTN_OK) return st;
+  if (shape->dtype != BSATTN_BF16) return fail(BSATTN_ERR_UNSUPPORTED, "prefill takes bf16 Q/K/V only");
+  if (Q == nullptr || K == nullptr || V == nullptr || O == nullptr)
+    return fail(BSATTN_ERR_INVALID, "Q, K, V and O must be non-NULL");
+  if (causal != 0 && causal != 1) return fail(BSATTN_ERR_INVALID, "causal must be 0 or 1");
+  st = check_globals(global_pos_host, n_global, shape->n_ctx);
+  if (st != BSATTN_OK) return st;
+  if (causal && n_global > 0)
+    return fail(BSATTN_ERR_UNSUPPORTED, "global tokens are bidirectional; causal masks take none");
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O))
+    return fail(BSATTN_ERR_INVALID, "device pointers must be 16-byte aligned");
+  const long long n_qt = (shape->n_ctx + 127) / 128;
+  const long long n_wg = n_qt * shape->batch * shape->n_q_heads +
+                         (long long)shape->batch * shape->n_q_heads * ((n_global + 31) / 32);
+  if (n_wg > 0x7fffffffLL) return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");
+  bsattn::PrefillArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.Q = Q; a.K = K; a.V = V; a.O = O; a.lse = lse;
+  a.batch = shape->batch; a.n_q_heads = shape->n_q_heads; a.n_kv_heads = shape->n_kv_heads;
+  a.head_dim = shape->head_dim;
+  a.seq_len = shape->n_ctx;
+  a.kv_capacity = shape->kv_capacity;
+  a.window_left = window_left < 0 ? -1 : window_left;
+  a.window_right = window_right < 0 ? -1 : window_right;
+  a.causal = causal;
+  a.scale = effective_scale(shape);
+  a.n_global = n_global;
+  for (int i = 0; i < n_global; ++i) a.gpos[i] = global_pos_host[i];
+  hipError_t e = bsattn::launch_prefill(a, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return fail(BSATTN_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+  return BSATTN_OK;
+}
+
+}  // extern "C"

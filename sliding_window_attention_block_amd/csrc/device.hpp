@@ -1,0 +1,121 @@
+// Device-side helpers shared by the gfx950 kernels: bf16 conversion, MFMA
+// wrappers, wave reductions and the forced-token mask of a decode step.
+//
+// MFMA operand layouts (gfx950, checked on the device with an in-bounds probe):
+//  v_mfma_f32_16x16x32_bf16   A[i][k]: lane i + 16*(k/8), element k%8
+//                             B[k][j]: lane j + 16*(k/8), element k%8
+//                             D[i][j]: lane j + 16*(i/4), element i%4
+//  v_mfma_f32_32x32x16_bf16   A[i][k]: lane i + 32*(k/8), element k%8
+//                             B[k][j]: lane j + 32*(k/8), element k%8
+//                             D[i][j]: lane j + 32*((i/4)%2), element 4*(i/8) + i%4
+//  ds_read_b64_tr_b16         within each 16-lane group, lane a supplies an
+//                             8-byte row M[a][0..3]; lane i receives
+//                             element e of M[4e + i/4][i%4].
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kBlock = 64;  // tokens per KV block (S)
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+// Low / high bf16 of a packed pair to fp32.
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round-to-nearest-even fp32 -> bf16 of two values packed into one dword (lo = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
+  ua = (ua + 0x7fffu + ((ua >> 16) & 1u)) >> 16;
+  ub = (ub + 0x7fffu + ((ub >> 16) & 1u)) & 0xffff0000u;
+  return ua | ub;
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Transposing 8-byte LDS read (gfx950).  `byte_off` is a byte offset into dynamic/static LDS.
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* lds_base, uint32_t byte_off) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const __attribute__((address_space(3))) char* p =
+      (const __attribute__((address_space(3))) char*)lds_base + byte_off;
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+  return __builtin_bit_cast(u32x2, r);
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// ------------------------------------------------------------------ forced tokens
+//
+// The tokens every decode step attends regardless of selection: sinks
+// [0, n_sink), the window [win_lo, t] with t = n_ctx - 1, and the global
+// positions (sorted).  A block whose 64 tokens are all forced is not a
+// candidate for selection.
+struct ForcedSet {
+  int32_t n_ctx;
+  int32_t sink_end;  // min(n_sink, n_ctx)
+  int32_t win_lo;    // first window token (n_ctx when there is no window)
+  int32_t n_global;
+  int32_t gpos[256];
+};
+
+// 64-bit mask of `lo <= token < hi` within block [base, base + 64).
+__device__ __forceinline__ uint64_t range_mask64(int base, int lo, int hi) {
+  int a = max(lo - base, 0), b = min(hi - base, 64);
+  if (a >= b) return 0ull;
+  uint64_t hiMask = (b == 64) ? ~0ull : ((1ull << b) - 1ull);
+  uint64_t loMask = (a == 0) ? 0ull : ((1ull << a) - 1ull);
+  return hiMask & ~loMask;
+}
+
+__device__ __forceinline__ int lower_bound_i32(const int32_t* a, int n, int x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    int mid = (lo + hi) >> 1;
+    if (a[mid] < x) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+// Forced tokens of block `blk`, restricted to tokens < n_ctx.
+__device__ __forceinline__ uint64_t forced_mask(const ForcedSet& f, int blk) {
+  const int base = blk * kBlock;
+  uint64_t m = range_mask64(base, 0, f.sink_end) | range_mask64(base, f.win_lo, f.n_ctx);
+  if (f.n_global > 0) {
+    int i = lower_bound_i32(f.gpos, f.n_global, base);
+    for (; i < f.n_global && f.gpos[i] < base + kBlock; ++i) m |= 1ull << (f.gpos[i] - base);
+  }
+  return m;
+}
+
+}  // namespace bsattn

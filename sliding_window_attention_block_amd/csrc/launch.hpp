@@ -1,0 +1,97 @@
+// Internal launch interface between the C-ABI host layer (bsattn.cpp) and the
+// kernels.  Every function launches asynchronously on `stream` and returns the
+// launch status; arguments have already been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device.hpp"
+
+namespace bsattn {
+
+struct SummaryArgs {
+  const void* K;
+  float* mean;
+  float* factor;
+  int32_t bh;            // B * Hkv
+  int32_t kv_capacity;   // token stride
+  int32_t nblk_capacity;
+  int32_t first_block;
+  int32_t n_blocks;
+  int32_t rank;
+  int32_t head_dim;
+  bool bf16;
+};
+hipError_t launch_summaries(const SummaryArgs& a, hipStream_t stream);
+
+struct SelectArgs {
+  const void* Q;
+  const float* mean;
+  const float* factor;
+  int32_t* sel;
+  float* scores;
+  int32_t batch, n_q_heads, n_kv_heads, head_dim;
+  int32_t n_blocks;       // complete blocks = n_ctx / 64
+  int32_t nblk_capacity;
+  int32_t rank;
+  int32_t top_k;
+  float scale;
+  bool bf16;
+  ForcedSet forced;
+};
+hipError_t launch_select_topk(const SelectArgs& a, hipStream_t stream);
+
+// Forced blocks of a decode step, in the order the decode kernel visits them:
+// two block ranges (sinks, window; merged when they touch) and the remaining
+// blocks that hold a global token.
+struct ForcedBlocks {
+  int32_t r0_lo, r0_n;  // blocks [r0_lo, r0_lo + r0_n)
+  int32_t r1_lo, r1_n;
+  int32_t n_gblk;
+  int32_t gblk[256];
+};
+
+struct DecodeArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const int32_t* sel;
+  float* O;
+  float* lse;
+  float* part_o;  // [B*Hq, n_split, d]
+  float* part_ml; // [B*Hq, n_split, 2]
+  int32_t batch, n_q_heads, n_kv_heads, head_dim;
+  int32_t kv_capacity;
+  int32_t top_k;
+  int32_t n_items;       // top_k + forced blocks
+  int32_t items_per_split;
+  int32_t n_split;
+  float scale;
+  bool bf16;
+  ForcedSet forced;
+  ForcedBlocks fblocks;
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// Split geometry the decode launch uses for a given item count (also sizes the workspace).
+void decode_split_geometry(int n_items, int head_dim, bool bf16, int* items_per_split, int* n_split);
+
+struct PrefillArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  float* O;
+  float* lse;
+  int32_t batch, n_q_heads, n_kv_heads, head_dim;
+  int32_t seq_len;
+  int32_t kv_capacity;
+  int32_t window_left;   // < 0: unbounded
+  int32_t window_right;  // < 0: unbounded
+  int32_t causal;
+  float scale;
+  int32_t n_global;
+  int32_t gpos[256];
+};
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+}  // namespace bsattn

@@ -1,0 +1,111 @@
+"""Helpers for the GPU parity tests: device copies, a full decode step through the
+C ABI, and the comparison rules (selected sets with the near-tie allowance,
+outputs at max-abs 2e-3)."""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+import oracle
+from synthetic import bf16_bits_to_f32
+
+OUT_TOL = 2e-3       # max-abs on outputs, compared in fp32
+TIE_REL = 1e-4       # relative gap of the oracle's k-th and (k+1)-th scores
+
+
+def torch_mod():
+    import torch
+    return torch
+
+
+def to_dev(arr):
+    """numpy float32 -> cuda float32; numpy uint16 (bf16 bits) -> cuda bfloat16."""
+    torch = torch_mod()
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).cuda()
+
+
+def as_f64(arr):
+    return (bf16_bits_to_f32(arr) if arr.dtype == np.uint16 else np.asarray(arr, np.float32)).astype(np.float64)
+
+
+def gpu_decode_step(api, x, w, kv_capacity=None, nblk_capacity=None, global_pos=(), dev=None):
+    """Run summaries -> select/top-k -> decode on the GPU through the binding.
+
+    ``x`` holds Q, K, V numpy arrays (float32 or bf16 bits) of workload ``w``.
+    Returns numpy copies of mean, factor, scores, sel, O, lse.
+    """
+    torch = torch_mod()
+    B, Hq, Hkv, d, n = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_ctx
+    cap = x["K"].shape[2] if kv_capacity is None else kv_capacity
+    nb = n // w.block_size
+    nbcap = nb if nblk_capacity is None else nblk_capacity
+    dev = dev or {}
+    Q = dev["Q"] if "Q" in dev else to_dev(x["Q"])
+    K = dev["K"] if "K" in dev else to_dev(x["K"])
+    V = dev["V"] if "V" in dev else to_dev(x["V"])
+    shape = api.make_shape(B, Hq, Hkv, d, n, kv_capacity=cap, dtype=w.dtype)
+    mean = torch.full((B, Hkv, max(nbcap, 1), d), float("nan"), device="cuda")
+    factor = (torch.full((B, Hkv, max(nbcap, 1), w.rank, d), float("nan"), device="cuda")
+              if w.rank > 0 else None)
+    api.bsattn_build_summaries(shape, K, w.rank, 0, nb, max(nbcap, 1), mean, factor)
+    scores = torch.full((B, Hkv, max(nbcap, 1)), float("nan"), device="cuda")
+    sel = torch.full((B, Hkv, w.top_k), -7, dtype=torch.int32, device="cuda")
+    api.bsattn_select_topk(shape, Q, mean, factor, w.rank, max(nbcap, 1), w.top_k, w.window,
+                           w.n_sink, list(global_pos), sel, scores)
+    ws = torch.empty(api.bsattn_decode_workspace_bytes(shape, w.top_k, w.window, w.n_sink,
+                                                       len(global_pos)), dtype=torch.uint8,
+                     device="cuda")
+    O = torch.full((B, Hq, d), float("nan"), device="cuda")
+    lse = torch.full((B, Hq), float("nan"), device="cuda")
+    api.bsattn_decode(shape, Q, K, V, sel, w.top_k, w.window, w.n_sink, list(global_pos), O, lse, ws)
+    torch.cuda.synchronize()
+    return dict(mean=mean.cpu().numpy(), factor=None if factor is None else factor.cpu().numpy(),
+                scores=scores.cpu().numpy(), sel=sel.cpu().numpy(), O=O.cpu().numpy(),
+                lse=lse.cpu().numpy())
+
+
+def compare_selection(sel_gpu, scores_oracle, cand, k):
+    """True/False for a (b, kv head) pair, plus whether the oracle has a near tie at k.
+
+    Sets must be identical, except at a near tie (relative gap of the oracle's k-th and
+    (k+1)-th candidate scores < 1e-4), where only blocks whose oracle scores lie in the
+    tie band may differ.
+    """
+    ref = oracle.top_k_blocks(scores_oracle, cand, k)
+    got = np.asarray(sel_gpu)
+    valid = got[got >= 0]
+    if len(valid) and (np.any(np.diff(valid) <= 0) or np.any(got[len(valid):] >= 0)):
+        return False, False  # not ascending / padding not at the end
+    if np.array_equal(got, ref):
+        return True, False
+    if len(cand) <= k:
+        return False, False
+    cs = np.sort(scores_oracle[cand])[::-1]
+    sk, sk1 = cs[k - 1], cs[k]
+    scale = max(abs(sk), abs(sk1))
+    near = abs(sk - sk1) <= TIE_REL * scale
+    if not near:
+        return False, False
+    diff = set(valid.tolist()) ^ set(ref[ref >= 0].tolist())
+    lo, hi = sk1 - TIE_REL * scale, sk + TIE_REL * scale
+    ok = all(lo <= scores_oracle[b] <= hi for b in diff) and len(valid) == len(ref[ref >= 0])
+    return ok, True
+
+
+def oracle_decode_with_sel(q, Kbg, Vbg, n, S, window, n_sink, global_pos, sel, scale):
+    """Oracle output for a given selected set (the output is unique given the set)."""
+    forced = oracle.forced_token_mask(n, n_sink, window, global_pos)
+    tokens = oracle.decode_token_set(n, S, forced, sel)
+    return oracle.sparse_decode_group(q, Kbg[:n], Vbg[:n], tokens, scale)
+
+
+def max_abs(a, b):
+    return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64)))) if np.size(a) else 0.0
+
+
+def default_scale(d):
+    return 1.0 / math.sqrt(d)

@@ -1,0 +1,166 @@
+"""GPU parity of the decode path (summaries -> select/top-k -> sparse decode) against
+the fp64 oracle, through the C ABI.
+
+Bar: selected sets identical per (b, K/V head) except at the oracle's near ties
+(relative gap < 1e-4 between its k-th and (k+1)-th scores); outputs and lse within
+max-abs 2e-3 of the oracle's attention over the GPU's selected set; summaries and
+scores within fp32 rounding of the oracle's float64 values.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from synthetic import WORKLOADS, DecodeWorkload, make_decode_inputs
+
+from gpu_util import (OUT_TOL, as_f64, compare_selection, default_scale, gpu_decode_step,
+                      max_abs, oracle_decode_with_sel)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def api():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need the GPU"
+    import sliding_window_attention_block_amd as m
+    m.library()
+    return m
+
+
+def _w(name, B, Hq, Hkv, d, n, rank, k, W, ns, dtype, seed):
+    return DecodeWorkload(name=name, batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, n_ctx=n,
+                          block_size=64, rank=rank, top_k=k, window=W, n_sink=ns, dtype=dtype,
+                          seed=seed)
+
+
+SMALL = [
+    # name                    B  Hq Hkv  d    n     r  k   W    ns  dtype  seed  globals           extra cap
+    (_w("bf16_g4_d128_r0", 2, 8, 2, 128, 1000, 0, 3, 100, 5, "bf16", 10), (), 0),
+    (_w("bf16_g8_d128_r4", 1, 16, 2, 128, 2065, 4, 5, 130, 64, "bf16", 11), (), 0),
+    (_w("bf16_g16_d64_r2", 1, 16, 1, 64, 777, 2, 4, 64, 0, "bf16", 12), (3, 200, 201, 500, 776), 0),
+    (_w("bf16_g1_d64_r8", 2, 2, 2, 64, 1500, 8, 6, 1, 1, "bf16", 13), (), 100),
+    (_w("f32_g8_d128_r4", 1, 8, 1, 128, 640, 4, 2, 64, 64, "f32", 14), (70,), 0),
+    (_w("f32_g2_d64_r0", 3, 4, 2, 64, 129, 0, 1, 3, 2, "f32", 15), (), 7),
+    (_w("k_exceeds_candidates", 1, 4, 1, 64, 600, 0, 50, 64, 64, "bf16", 16), (), 0),
+    (_w("window_covers_all", 1, 4, 1, 64, 300, 0, 4, 1000, 0, "bf16", 17), (), 0),
+    (_w("short_context", 1, 8, 1, 128, 40, 1, 2, 16, 4, "bf16", 18), (), 0),
+]
+
+
+def _check_case(api, w, globals_, extra_cap):
+    x = make_decode_inputs(w, kv_capacity=w.n_ctx + extra_cap)
+    print(f"[decode parity] {w.name}", flush=True)
+    got = gpu_decode_step(api, x, w, global_pos=globals_)
+    Q, K, V = as_f64(x["Q"]), as_f64(x["K"]), as_f64(x["V"])
+    S, n, G, d = w.block_size, w.n_ctx, w.n_q_heads // w.n_kv_heads, w.head_dim
+    scale = default_scale(d)
+    nb = n // S
+    forced = oracle.forced_token_mask(n, w.n_sink, w.window, globals_)
+    cand = oracle.candidate_blocks(n, S, forced)
+    ties = 0
+    for b in range(w.batch):
+        for g in range(w.n_kv_heads):
+            mean, factor = oracle.block_summaries(K[b, g, :n], S, w.rank)
+            assert max_abs(got["mean"][b, g, :nb], mean) < 1e-5
+            if w.rank > 0:
+                proj_gpu = np.einsum("bid,bie->bde", got["factor"][b, g, :nb].astype(np.float64),
+                                     got["factor"][b, g, :nb].astype(np.float64))
+                proj_ref = np.einsum("bid,bie->bde", factor, factor)
+                lam = (factor ** 2).sum(axis=2)
+                full = np.linalg.eigvalsh(np.einsum("brd,bre->bde",
+                                                    K[b, g, :nb * S].reshape(nb, S, d) - mean[:, None],
+                                                    K[b, g, :nb * S].reshape(nb, S, d) - mean[:, None]) / S)
+                full = full[:, ::-1]
+                gap = (full[:, w.rank - 1] - full[:, w.rank]) / np.maximum(full[:, 0], 1e-30)
+                ok = gap > 1e-3
+                err = np.abs(proj_gpu - proj_ref).max(axis=(1, 2)) / np.maximum(lam[:, 0], 1e-30)
+                assert np.all(err[ok] < 1e-3), f"rank-{w.rank} projector error {err[ok].max()}"
+            qs = scale * Q[b, g * G:(g + 1) * G]
+            s_ref = oracle.group_scores(oracle.head_scores(qs, mean, factor if w.rank else None))
+            if nb:
+                assert max_abs(got["scores"][b, g, :nb], s_ref) < (2e-4 if w.rank else 3e-5)
+            ok, tie = compare_selection(got["sel"][b, g], s_ref, cand, w.top_k)
+            ties += tie
+            assert ok, f"selection mismatch at (b={b}, g={g}): gpu {got['sel'][b, g]} vs " \
+                       f"oracle {oracle.top_k_blocks(s_ref, cand, w.top_k)}"
+            o_ref, lse_ref = oracle_decode_with_sel(Q[b, g * G:(g + 1) * G], K[b, g], V[b, g], n, S,
+                                                    w.window, w.n_sink, globals_, got["sel"][b, g],
+                                                    scale)
+            assert max_abs(got["O"][b, g * G:(g + 1) * G], o_ref) < OUT_TOL
+            assert max_abs(got["lse"][b, g * G:(g + 1) * G], lse_ref) < OUT_TOL
+    return ties
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0].name for c in SMALL])
+def test_decode_small_cases(api, case):
+    w, globals_, extra = case
+    _check_case(api, w, globals_, extra)
+
+
+def test_tiny_decode_workload(api):
+    """The 1K-token fp32 workload end to end: G = 4, d = 64, top-4 + sink block + last block."""
+    _check_case(api, WORKLOADS["tiny_decode_1k"], (), 0)
+
+
+def test_k_covering_all_candidates_equals_dense_causal(api):
+    w = _w("dense", 2, 8, 2, 128, 900, 0, 64, 32, 0, "bf16", 21)
+    x = make_decode_inputs(w)
+    got = gpu_decode_step(api, x, w)
+    Q, K, V = as_f64(x["Q"]), as_f64(x["K"]), as_f64(x["V"])
+    for b in range(2):
+        for g in range(2):
+            o, lse = oracle.masked_attention_rows(Q[b, 4 * g:4 * g + 4], K[b, g], V[b, g],
+                                                  np.ones((4, 900), bool), default_scale(128))
+            assert max_abs(got["O"][b, 4 * g:4 * g + 4], o) < OUT_TOL
+            assert max_abs(got["lse"][b, 4 * g:4 * g + 4], lse) < OUT_TOL
+
+
+def _full_size(api, name, pairs):
+    import torch
+    w = WORKLOADS[name]
+    print(f"[decode full size] {name}: generating inputs", flush=True)
+    x = make_decode_inputs(w)
+    print(f"[decode full size] {name}: running on the GPU", flush=True)
+    got = gpu_decode_step(api, x, w)
+    torch.cuda.empty_cache()
+    # properties over every pair
+    S, n = w.block_size, w.n_ctx
+    forced = oracle.forced_token_mask(n, w.n_sink, w.window)
+    cand = oracle.candidate_blocks(n, S, forced)
+    candset = set(cand.tolist())
+    for b in range(w.batch):
+        for g in range(w.n_kv_heads):
+            s = got["sel"][b, g]
+            assert len(set(s.tolist())) == w.top_k and all(v in candset for v in s.tolist())
+            assert np.all(np.diff(s) > 0)
+    assert np.isfinite(got["O"]).all() and np.isfinite(got["lse"]).all()
+    # oracle on sampled pairs
+    Q = as_f64(x["Q"])
+    G, d = w.n_q_heads // w.n_kv_heads, w.head_dim
+    scale = default_scale(d)
+    ties = 0
+    for (b, g) in pairs:
+        print(f"[decode full size] {name}: oracle for pair ({b}, {g})", flush=True)
+        Kbg, Vbg = as_f64(x["K"][b, g]), as_f64(x["V"][b, g])
+        mean, factor = oracle.block_summaries(Kbg, S, w.rank)
+        assert max_abs(got["mean"][b, g], mean) < 1e-5
+        s_ref = oracle.group_scores(oracle.head_scores(scale * Q[b, g * G:(g + 1) * G], mean,
+                                                       factor if w.rank else None))
+        assert max_abs(got["scores"][b, g], s_ref) < (2e-4 if w.rank else 3e-5)
+        ok, tie = compare_selection(got["sel"][b, g], s_ref, cand, w.top_k)
+        ties += tie
+        assert ok, f"selection mismatch at ({b}, {g})"
+        o_ref, lse_ref = oracle_decode_with_sel(Q[b, g * G:(g + 1) * G], Kbg, Vbg, n, S, w.window,
+                                                w.n_sink, (), got["sel"][b, g], scale)
+        assert max_abs(got["O"][b, g * G:(g + 1) * G], o_ref) < OUT_TOL
+        assert max_abs(got["lse"][b, g * G:(g + 1) * G], lse_ref) < OUT_TOL
+    print(f"[decode full size] {name}: near ties among sampled pairs: {ties}", flush=True)
+
+
+def test_first_order_decode_32k_full_size(api):
+    _full_size(api, "first_order_decode_32k", [(0, 0), (5, 3), (15, 7)])
+
+
+def test_cobs_decode_128k_full_size(api):
+    _full_size(api, "cobs_decode_128k", [(0, 0), (3, 7)])
