@@ -1,0 +1,350 @@
+#!/usr/bin/env python3
+"""Throughput of the block-sparse attention hot path on one MI355X.
+
+Step (the timed unit): one decode step of the first-order 32K workload (batch
+16, 32 query / 8 K/V heads, d 128, 64-token blocks, top-16 + sink block + 512-
+token window): selector scoring + top-k, then the split sparse decode and its
+merge.  `value` is tokens/s = batch / step time.  Summaries are built once
+before timing (as the method builds them when blocks fill); their build time is
+reported separately, as are the COBS 128K decode step and the two prefills.
+
+Every timed loop cycles through R device-resident replicas of its inputs so the
+reuse distance exceeds the 256 MB Infinity Cache: each step reads HBM, not
+cache.  Kernel durations come from HIP events on the stream the library
+launches on (torch's current stream).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
+BF16_PEAK = 2.5e15         # flop/s, MI355X dense bf16 MFMA
+MALL_BYTES = 256 << 20
+METRIC = "sparse-decode tokens/s and gathered-KV GB/s (% HBM peak); prefill % MFMA peak"
+HEADLINE = "first_order_decode_32k"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- models
+def attended_tokens(n, S, window, n_sink, global_pos, sel_row):
+    """Size of the decode token set: forced tokens union the selected blocks' tokens."""
+    inT = np.zeros(n, dtype=bool)
+    inT[: min(n_sink, n)] = True
+    if window > 0:
+        inT[max(0, n - window):] = True
+    if len(global_pos):
+        inT[np.asarray(global_pos)] = True
+    for b in sel_row:
+        if b >= 0:
+            inT[b * S:(b + 1) * S] = True
+    return int(inT.sum())
+
+
+def prefill_pairs(N, wl, wr, causal, global_pos):
+    """Allowed (query, key) pairs per (b, h) of the prefill mask, by per-row closed form."""
+    i = np.arange(N, dtype=np.int64)
+    lo = np.zeros(N, np.int64) if wl < 0 else np.maximum(0, i - wl)
+    right = 0 if causal else wr
+    hi = np.full(N, N - 1, np.int64) if right < 0 else np.minimum(N - 1, i + right)
+    cnt = hi - lo + 1
+    g = np.asarray(sorted(global_pos), dtype=np.int64)
+    if g.size:
+        inside = np.searchsorted(g, hi, side="right") - np.searchsorted(g, lo, side="left")
+        cnt = cnt + (g.size - inside)
+        cnt[g] = N
+    return int(cnt.sum())
+
+
+def replicas_for(step_bytes):
+    return max(2, int(np.ceil(2 * MALL_BYTES / max(step_bytes, 1))) + 1)
+
+
+# ----------------------------------------------------------------------------- decode
+def to_dev(torch, a):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def bench_decode(api, torch, w, x, steps, warmup, with_events=True):
+    B, Hq, Hkv, d, n, S = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_ctx, w.block_size
+    nb = n // S
+    shape = api.make_shape(B, Hq, Hkv, d, n, dtype=w.dtype)
+    ws_bytes = api.bsattn_decode_workspace_bytes(shape, w.top_k, w.window, w.n_sink, 0)
+    elem = 2 if w.dtype == "bf16" else 4
+    summ_bytes = B * Hkv * nb * d * 4 * (1 + w.rank)
+    kv_est = B * Hkv * (w.top_k * S + w.n_sink + w.window) * d * 2 * elem
+    R = replicas_for(summ_bytes + kv_est)
+    log(f"[bench] {w.name}: {R} replicas, {2 * x['K'].nbytes * R / 2**30:.1f} GiB of K/V")
+    K0, V0, Q0 = to_dev(torch, x["K"]), to_dev(torch, x["V"]), to_dev(torch, x["Q"])
+    reps = []
+    for r in range(R):
+        K = K0 if r == 0 else K0.clone()
+        V = V0 if r == 0 else V0.clone()
+        Q = Q0 if r == 0 else Q0.clone()
+        mean = torch.empty((B, Hkv, nb, d), device="cuda")
+        factor = torch.empty((B, Hkv, nb, w.rank, d), device="cuda") if w.rank else None
+        scores = torch.empty((B, Hkv, nb), device="cuda")
+        sel = torch.empty((B, Hkv, w.top_k), dtype=torch.int32, device="cuda")
+        ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+        O = torch.empty((B, Hq, d), device="cuda")
+        lse = torch.empty((B, Hq), device="cuda")
+        reps.append(dict(K=K, V=V, Q=Q, mean=mean, factor=factor, scores=scores, sel=sel, ws=ws, O=O, lse=lse))
+    del K0, V0, Q0
+    # A1: summaries (built once per block; timed on every replica)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    build_ms = []
+    for rp in reps:
+        ev[0].record()
+        api.bsattn_build_summaries(shape, rp["K"], w.rank, 0, nb, nb, rp["mean"], rp["factor"])
+        ev[1].record()
+        torch.cuda.synchronize()
+        build_ms.append(ev[0].elapsed_time(ev[1]))
+
+    def select(rp):
+        api.bsattn_select_topk(shape, rp["Q"], rp["mean"], rp["factor"], w.rank, nb, w.top_k,
+                               w.window, w.n_sink, None, rp["sel"], rp["scores"])
+
+    def decode(rp):
+        api.bsattn_decode(shape, rp["Q"], rp["K"], rp["V"], rp["sel"], w.top_k, w.window, w.n_sink,
+                          None, rp["O"], rp["lse"], rp["ws"])
+
+    for i in range(warmup):
+        rp = reps[i % R]
+        select(rp)
+        decode(rp)
+    torch.cuda.synchronize()
+    # token-set size from the actual selection (identical on every replica)
+    sel_h = reps[0]["sel"].cpu().numpy()
+    tokens = sum(attended_tokens(n, S, w.window, w.n_sink, (), sel_h[b, g])
+                 for b in range(B) for g in range(Hkv))
+    kv_bytes = tokens * d * 2 * elem
+    io_bytes = B * Hq * d * elem + B * Hq * (d + 1) * 4 + B * Hkv * w.top_k * 4  # Q in, O + lse out, sel
+    sel_bytes = summ_bytes + B * Hq * d * elem + B * Hkv * w.top_k * 4
+    # timed steps
+    ev_sel = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    ev_dec = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        rp = reps[i % R]
+        if with_events:
+            ev_sel[i][0].record()
+        select(rp)
+        if with_events:
+            ev_sel[i][1].record()
+            ev_dec[i][0].record()
+        decode(rp)
+        if with_events:
+            ev_dec[i][1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / steps
+    sel_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_sel])) if with_events else None
+    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_dec])) if with_events else None
+    res = dict(
+        workload=w.name, ms_per_step=ms_step, tokens_per_s=B / (ms_step * 1e-3),
+        replicas=R, attended_tokens=tokens, gathered_kv_bytes=kv_bytes,
+        select_ms=sel_ms, decode_ms=dec_ms,
+        select_bytes=sel_bytes, decode_bytes=kv_bytes + io_bytes,
+        summary_build_ms=float(np.median(build_ms)),
+        summary_build_bytes=B * Hkv * nb * S * d * elem + summ_bytes,
+    )
+    if with_events:
+        res["gathered_kv_GBps"] = kv_bytes / (dec_ms * 1e-3) / 1e9
+        res["gathered_kv_frac_hbm"] = res["gathered_kv_GBps"] * 1e9 / HBM_PEAK
+        res["decode_GBps"] = (kv_bytes + io_bytes) / (dec_ms * 1e-3) / 1e9
+        res["select_GBps"] = sel_bytes / (sel_ms * 1e-3) / 1e9
+        res["step_GBps"] = (kv_bytes + io_bytes + sel_bytes) / (ms_step * 1e-3) / 1e9
+    del reps
+    torch.cuda.empty_cache()
+    return res
+
+
+# ----------------------------------------------------------------------------- prefill
+def bench_prefill(api, torch, w, x, steps, warmup):
+    B, Hq, Hkv, N, d = w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len, w.head_dim
+    shape = api.make_shape(B, Hq, Hkv, d, N, dtype="bf16")
+    io = (x["Q"].nbytes + x["K"].nbytes + x["V"].nbytes) + B * Hq * N * (d + 1) * 4
+    R = replicas_for(io)
+    Q0, K0, V0 = to_dev(torch, x["Q"]), to_dev(torch, x["K"]), to_dev(torch, x["V"])
+    reps = []
+    for r in range(R):
+        reps.append(dict(Q=Q0 if r == 0 else Q0.clone(), K=K0 if r == 0 else K0.clone(),
+                         V=V0 if r == 0 else V0.clone(),
+                         O=torch.empty((B, Hq, N, d), device="cuda"),
+                         lse=torch.empty((B, Hq, N), device="cuda")))
+    g = list(w.global_pos)
+
+    def run(rp):
+        api.bsattn_prefill(shape, rp["Q"], rp["K"], rp["V"], w.window_left, w.window_right,
+                           w.causal, g, rp["O"], rp["lse"])
+
+    for i in range(warmup):
+        run(reps[i % R])
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        evs[i][0].record()
+        run(reps[i % R])
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    pairs = prefill_pairs(N, w.window_left, w.window_right, w.causal, g)
+    flops = 4.0 * d * pairs * B * Hq
+    del reps
+    torch.cuda.empty_cache()
+    return dict(workload=w.name, kernel_ms=k_ms, wall_ms_per_call=(t1 - t0) * 1e3 / steps,
+                pairs_per_head=pairs, gflop=flops / 1e9, tflops=flops / (k_ms * 1e-3) / 1e12,
+                frac_mfma=flops / (k_ms * 1e-3) / BF16_PEAK, io_bytes=io,
+                hbm_GBps=io / (k_ms * 1e-3) / 1e9, frac_hbm=io / (k_ms * 1e-3) / HBM_PEAK,
+                replicas=R)
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+def cpu_baseline(w, x):
+    """The oracle's decode step (score + top-k + attention over the token set) on the
+    host cores, on the whole batch of one step; summaries are built before timing."""
+    import oracle
+    from synthetic import bf16_bits_to_f32
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = len(os.sched_getaffinity(0))
+    Q = bf16_bits_to_f32(x["Q"]) if x["Q"].dtype == np.uint16 else x["Q"]
+    pairs = [(b, g) for b in range(w.batch) for g in range(w.n_kv_heads)]
+    summaries = {}
+    Kf = {}
+    Vf = {}
+    for (b, g) in pairs:
+        Kf[(b, g)] = bf16_bits_to_f32(x["K"][b, g]) if x["K"].dtype == np.uint16 else x["K"][b, g]
+        Vf[(b, g)] = bf16_bits_to_f32(x["V"][b, g]) if x["V"].dtype == np.uint16 else x["V"][b, g]
+        summaries[(b, g)] = oracle.block_summaries(Kf[(b, g)].astype(np.float64), w.block_size, w.rank)
+    t0 = time.perf_counter()
+    done = 0
+    for (b, g) in pairs:
+        Kb = np.zeros((1, 1) + Kf[(b, g)].shape, np.float32)
+        Kb[0, 0] = Kf[(b, g)]
+        Vb = np.zeros_like(Kb)
+        Vb[0, 0] = Vf[(b, g)]
+        qb = Q[b:b + 1, g * (w.n_q_heads // w.n_kv_heads):(g + 1) * (w.n_q_heads // w.n_kv_heads)]
+        oracle.decode_step(qb, Kb, Vb, w.n_ctx, w.block_size, w.rank, w.top_k, w.window, w.n_sink,
+                           summaries={(0, 0): summaries[(b, g)]})
+        done += 1
+    dt = time.perf_counter() - t0
+    step_s = dt / done * len(pairs)
+    return dict(value=w.batch / step_s, unit="tokens/s", cores=int(threads), kind="oracle",
+                sample=f"one full decode step of {w.name}: all {len(pairs)} (batch, K/V head) pairs, "
+                       f"numpy float64 oracle, summaries prebuilt and untimed ({dt:.1f} s)")
+
+
+# ----------------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--only", default=None,
+                    help="run one workload only (first_order_decode_32k, cobs_decode_128k, "
+                         "swa_prefill_8k, local_global_prefill_16k); prints its result")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the block-sparse attention path here has no "
+              "multi-GPU part (see the sharding notes in DESIGN.md); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sliding_window_attention_block_amd as api
+    from synthetic import WORKLOADS, make_decode_inputs, make_prefill_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    api.library()
+    names = [args.only] if args.only else [HEADLINE, "cobs_decode_128k", "swa_prefill_8k",
+                                            "local_global_prefill_16k"]
+    results = {}
+    inputs = {}
+    for name in names:
+        w = WORKLOADS[name]
+        t = time.perf_counter()
+        x = make_decode_inputs(w) if name.endswith(("32k", "128k")) else make_prefill_inputs(w)
+        log(f"[bench] {name}: inputs generated in {time.perf_counter() - t:.1f} s")
+        if name.endswith(("32k", "128k")):
+            results[name] = bench_decode(api, torch, w, x, args.steps, args.warmup)
+        else:
+            results[name] = bench_prefill(api, torch, w, x, args.steps, args.warmup)
+        log(f"[bench] {name}: {json.dumps(results[name])}")
+        if name == HEADLINE:
+            inputs[name] = x
+        del x
+
+    if args.only and args.only != HEADLINE:
+        print(json.dumps({"workload": args.only, **results[args.only]}))
+        return
+
+    h = results[HEADLINE]
+    w = WORKLOADS[HEADLINE]
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle) ...")
+        cpu = cpu_baseline(w, inputs[HEADLINE])
+        log(f"[bench] cpu baseline: {cpu}")
+    line = {
+        "metric": METRIC,
+        "value": h["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": h["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": HEADLINE, "batch": w.batch, "context": w.n_ctx,
+                   "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
+                   "block": w.block_size, "top_k": w.top_k, "window": w.window, "sink": w.n_sink,
+                   "rank": w.rank, "parallelism": "single GPU"},
+        "gathered_kv_GBps": h.get("gathered_kv_GBps"),
+        "gathered_kv_frac_hbm": h.get("gathered_kv_frac_hbm"),
+        "roofline": {
+            "kernel": "bsattn_decode (sparse flash-decode split kernel + log-sum-exp merge)",
+            "bound": "hbm",
+            "achieved": h["decode_bytes"] / (h["decode_ms"] * 1e-3) / 1e9,
+            "peak": HBM_PEAK / 1e9,
+            "unit": "GB/s",
+            "frac": h["decode_bytes"] / (h["decode_ms"] * 1e-3) / HBM_PEAK,
+            "traffic": None,
+            "bytes_per_launch": h["decode_bytes"],
+            "avg_launch_ms": h["decode_ms"],
+        },
+        "cpu_baseline": cpu,
+        "rows": results,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -134,9 +134,10 @@ size_t bsattn_decode_workspace_bytes(const bsattn_shape* shape, int32_t top_k, i
  * lse[b,h] = ln sum_T exp(logit_t).  sel: [B,Hkv,top_k] int32 as written by
  * bsattn_select_topk (ascending, -1 padded, each entry a complete block).
  * dtype F32 or BF16.  workspace: device memory of at least
- * bsattn_decode_workspace_bytes(...) bytes, 256-byte aligned, contents need
- * not be initialised.  lse may be NULL.  Calls that share a workspace must
- * be ordered (same stream); calls with separate workspaces may overlap.
+ * bsattn_decode_workspace_bytes(...) bytes, 256-byte aligned, holding the
+ * split partials; its contents need not be initialised.  lse may be NULL.
+ * Calls that share a workspace must be ordered (same stream); calls with
+ * separate workspaces may overlap.
  */
 bsattn_status bsattn_decode(const bsattn_shape* shape, const void* Q, const void* K,
                             const void* V, const int32_t* sel, int32_t top_k, int32_t window,

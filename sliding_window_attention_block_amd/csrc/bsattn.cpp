@@ -12,6 +12,9 @@
 
 #include "launch.hpp"
 
+static_assert(bsattn::kMaxTopK == BSATTN_MAX_TOP_K, "device top-k limit matches the header");
+static_assert(bsattn::kMaxBlocks == BSATTN_MAX_BLOCKS, "device block limit matches the header");
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -113,14 +116,23 @@ int forced_block_bound(int32_t n_ctx, int32_t window, int32_t n_sink, int32_t n_
   return fb.r0_n + fb.r1_n + n_global;
 }
 
-size_t workspace_for(const bsattn_shape* s, int n_items) {
-  int ips, nsplit;
-  bsattn::decode_split_geometry(n_items, s->head_dim, s->dtype == BSATTN_BF16, &ips, &nsplit);
-  const size_t rows = (size_t)s->batch * s->n_q_heads * nsplit;
-  size_t o_bytes = rows * s->head_dim * sizeof(float);
-  o_bytes = (o_bytes + 255) & ~(size_t)255;
-  return o_bytes + rows * 2 * sizeof(float);
+// Workspace layout: partial numerators [B*Hq, n_wg, d] | partial (max, sum) [B*Hq, n_wg, 2],
+// each region 256-byte aligned.
+struct WsLayout {
+  size_t o_off, ml_off, total;
+};
+WsLayout workspace_layout(const bsattn_shape* s, int n_items) {
+  int ipw, n_wg;
+  bsattn::decode_split_geometry(n_items, &ipw, &n_wg);
+  const size_t rows = (size_t)s->batch * s->n_q_heads * n_wg;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  WsLayout l;
+  l.o_off = 0;
+  l.ml_off = up(rows * s->head_dim * sizeof(float));
+  l.total = l.ml_off + up(rows * 2 * sizeof(float));
+  return l;
 }
+size_t workspace_for(const bsattn_shape* s, int n_items) { return workspace_layout(s, n_items).total; }
 
 }  // namespace
 
@@ -245,12 +257,10 @@ bsattn_status bsattn_decode(const bsattn_shape* shape, const void* Q, const void
     return fail(BSATTN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return fail(BSATTN_ERR_INVALID, "workspace must be 256-byte aligned");
-  bsattn::decode_split_geometry(a.n_items, shape->head_dim, shape->dtype == BSATTN_BF16,
-                                &a.items_per_split, &a.n_split);
-  const size_t rows = (size_t)shape->batch * shape->n_q_heads * a.n_split;
-  size_t o_bytes = (rows * shape->head_dim * sizeof(float) + 255) & ~(size_t)255;
-  a.part_o = static_cast<float*>(workspace);
-  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+  bsattn::decode_split_geometry(a.n_items, &a.items_per_wave, &a.n_wg);
+  const WsLayout lay = workspace_layout(shape, a.n_items);
+  a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.o_off);
+  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.ml_off);
   a.Q = Q; a.K = K; a.V = V; a.sel = sel; a.O = O; a.lse = lse;
   a.batch = shape->batch; a.n_q_heads = shape->n_q_heads; a.n_kv_heads = shape->n_kv_heads;
   a.head_dim = shape->head_dim;

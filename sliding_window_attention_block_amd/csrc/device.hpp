@@ -28,6 +28,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kBlock = 64;  // tokens per KV block (S)
+constexpr int kMaxBlocks = 65536;  // complete blocks per (b, K/V head) the top-k handles
+constexpr int kMaxTopK = 1024;     // selected blocks per (b, K/V head)
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);

@@ -59,14 +59,14 @@ struct DecodeArgs {
   const int32_t* sel;
   float* O;
   float* lse;
-  float* part_o;  // [B*Hq, n_split, d]
-  float* part_ml; // [B*Hq, n_split, 2]
+  float* part_o;      // [B*Hq, n_wg, d]  per-workgroup partial numerators
+  float* part_ml;     // [B*Hq, n_wg, 2]  per-workgroup (max, normaliser), log2 domain
   int32_t batch, n_q_heads, n_kv_heads, head_dim;
   int32_t kv_capacity;
   int32_t top_k;
-  int32_t n_items;       // top_k + forced blocks
-  int32_t items_per_split;
-  int32_t n_split;
+  int32_t n_items;        // top_k + forced blocks
+  int32_t items_per_wave;
+  int32_t n_wg;           // workgroups per (b, K/V head)
   float scale;
   bool bf16;
   ForcedSet forced;
@@ -74,7 +74,8 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 // Split geometry the decode launch uses for a given item count (also sizes the workspace).
-void decode_split_geometry(int n_items, int head_dim, bool bf16, int* items_per_split, int* n_split);
+void decode_split_geometry(int n_items, int* items_per_wave, int* n_wg);
+constexpr int kDecodeWaves = 4;  // waves per decode workgroup
 
 struct PrefillArgs {
   const void* Q;

@@ -10,18 +10,25 @@
 //
 // Scoring streams every summary once: 16 lanes share one block, each lane
 // owning d/16 consecutive dims of every query head in registers, so each
-// summary row is read with coalesced 16-byte loads.  Top-k is an exact
-// 4-pass radix select on order-preserving 32-bit keys in LDS.
+// summary row is read with coalesced 16-byte loads.  All of a block's rows
+// (mean and up to 8 factor rows) are loaded before any arithmetic, so a wave
+// waits on HBM once per block rather than once per row.
+//
+// Top-k: one wave per (b, K/V head), an exact 4-pass radix select (8 bits a
+// pass) on order-preserving 32-bit keys: a 256-bin LDS histogram per pass and
+// a wave-wide scan to find the digit of the k-th largest key; then every lane
+// emits its candidates above the threshold, and the lowest-index ones equal
+// to it, in index order.
 #include "launch.hpp"
 
 namespace bsattn {
 namespace {
 
-constexpr int kBlocksPerWg = 64;
-
-template <int D, int GM, bool BF16>
+template <int D, int GM, int RM, bool BF16>
 __global__ __launch_bounds__(256) void select_scores_kernel(SelectArgs a) {
-  constexpr int SL = D / 16;  // dims per lane
+  constexpr int SL = D / 16;               // dims per lane
+  constexpr int PB = RM == 0 ? 4 : (RM <= 4 ? 2 : 1);  // blocks per slot, loaded together
+  constexpr int BPW = 16 * PB;             // blocks per workgroup
   const int tid = threadIdx.x;
   const int sub = tid & 15, slot = tid >> 4;
   const int bh = blockIdx.y;
@@ -31,69 +38,107 @@ __global__ __launch_bounds__(256) void select_scores_kernel(SelectArgs a) {
   float q[GM][SL];
 #pragma unroll
   for (int h = 0; h < GM; ++h) {
-    const int hq = g * G + h;
-    const size_t off = ((size_t)b * a.n_q_heads + hq) * D + sub * SL;
+    const size_t off = ((size_t)b * a.n_q_heads + g * G + h) * D + sub * SL;
+    if (h < G) {
+      if constexpr (BF16) {
+        // SL bf16 values = SL * 2 bytes, 16-byte aligned (SL is 4 or 8)
+        const uint16_t* src = reinterpret_cast<const uint16_t*>(a.Q) + off;
 #pragma unroll
-    for (int e = 0; e < SL; ++e) {
-      float v = 0.f;
-      if (h < G) {
-        if constexpr (BF16) v = bf16_to_f32(reinterpret_cast<const uint16_t*>(a.Q)[off + e]);
-        else v = reinterpret_cast<const float*>(a.Q)[off + e];
+        for (int c = 0; c < SL / 8 + (SL % 8 ? 1 : 0); ++c) {
+          if constexpr (SL >= 8) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(src + 8 * c);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              q[h][8 * c + 2 * t] = bf16lo(v[t]) * a.scale;
+              q[h][8 * c + 2 * t + 1] = bf16hi(v[t]) * a.scale;
+            }
+          } else {
+            const u32x2 v = *reinterpret_cast<const u32x2*>(src);
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              q[h][2 * t] = bf16lo(v[t]) * a.scale;
+              q[h][2 * t + 1] = bf16hi(v[t]) * a.scale;
+            }
+          }
+        }
+      } else {
+        const float4* src = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.Q) + off);
+#pragma unroll
+        for (int c = 0; c < SL / 4; ++c) {
+          const float4 v = src[c];
+          q[h][4 * c] = v.x * a.scale; q[h][4 * c + 1] = v.y * a.scale;
+          q[h][4 * c + 2] = v.z * a.scale; q[h][4 * c + 3] = v.w * a.scale;
+        }
       }
-      q[h][e] = v * a.scale;
+    } else {
+#pragma unroll
+      for (int e = 0; e < SL; ++e) q[h][e] = 0.f;
     }
   }
 
-  for (int pass = 0; pass < kBlocksPerWg / 16; ++pass) {
-    const int j = blockIdx.x * kBlocksPerWg + pass * 16 + slot;
-    if (j >= a.n_blocks) break;  // uniform across the 16 lanes of a slot
-    const size_t row = (size_t)bh * a.nblk_capacity + j;
-    float m[SL];
-    {
-      const float4* src = reinterpret_cast<const float4*>(a.mean + row * D + sub * SL);
+  // load phase
+  float vec[PB][1 + RM][SL];
+  int jj[PB];
 #pragma unroll
-      for (int c = 0; c < SL / 4; ++c) {
-        const float4 v = src[c];
-        m[4 * c] = v.x; m[4 * c + 1] = v.y; m[4 * c + 2] = v.z; m[4 * c + 3] = v.w;
+  for (int p = 0; p < PB; ++p) {
+    const int j = blockIdx.x * BPW + p * 16 + slot;
+    jj[p] = j;
+    const int jc = min(j, a.n_blocks - 1);
+    const size_t row = (size_t)bh * a.nblk_capacity + jc;
+    const float4* src = reinterpret_cast<const float4*>(a.mean + row * D + sub * SL);
+#pragma unroll
+    for (int c = 0; c < SL / 4; ++c) {
+      const float4 v = src[c];
+      vec[p][0][4 * c] = v.x; vec[p][0][4 * c + 1] = v.y; vec[p][0][4 * c + 2] = v.z; vec[p][0][4 * c + 3] = v.w;
+    }
+#pragma unroll
+    for (int i = 0; i < RM; ++i) {
+      if (i < a.rank) {
+        const float4* fs = reinterpret_cast<const float4*>(a.factor + (row * a.rank + i) * D + sub * SL);
+#pragma unroll
+        for (int c = 0; c < SL / 4; ++c) {
+          const float4 v = fs[c];
+          vec[p][1 + i][4 * c] = v.x; vec[p][1 + i][4 * c + 1] = v.y;
+          vec[p][1 + i][4 * c + 2] = v.z; vec[p][1 + i][4 * c + 3] = v.w;
+        }
       }
     }
+  }
+  // compute phase
+#pragma unroll
+  for (int p = 0; p < PB; ++p) {
     float s[GM];
 #pragma unroll
     for (int h = 0; h < GM; ++h) {
       float acc = 0.f;
 #pragma unroll
-      for (int e = 0; e < SL; ++e) acc = fmaf(q[h][e], m[e], acc);
+      for (int e = 0; e < SL; ++e) acc = fmaf(q[h][e], vec[p][0][e], acc);
       s[h] = acc;
     }
 #pragma unroll
     for (int o = 8; o > 0; o >>= 1)
 #pragma unroll
       for (int h = 0; h < GM; ++h) s[h] += __shfl_xor(s[h], o);
-
-    for (int i = 0; i < a.rank; ++i) {
-      const float4* src =
-          reinterpret_cast<const float4*>(a.factor + (row * a.rank + i) * D + sub * SL);
 #pragma unroll
-      for (int c = 0; c < SL / 4; ++c) {
-        const float4 v = src[c];
-        m[4 * c] = v.x; m[4 * c + 1] = v.y; m[4 * c + 2] = v.z; m[4 * c + 3] = v.w;
+    for (int i = 0; i < RM; ++i) {
+      if (i < a.rank) {
+        float pr[GM];
+#pragma unroll
+        for (int h = 0; h < GM; ++h) {
+          float acc = 0.f;
+#pragma unroll
+          for (int e = 0; e < SL; ++e) acc = fmaf(q[h][e], vec[p][1 + i][e], acc);
+          pr[h] = acc;
+        }
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1)
+#pragma unroll
+          for (int h = 0; h < GM; ++h) pr[h] += __shfl_xor(pr[h], o);
+#pragma unroll
+        for (int h = 0; h < GM; ++h) s[h] = fmaf(0.5f * pr[h], pr[h], s[h]);
       }
-      float p[GM];
-#pragma unroll
-      for (int h = 0; h < GM; ++h) {
-        float acc = 0.f;
-#pragma unroll
-        for (int e = 0; e < SL; ++e) acc = fmaf(q[h][e], m[e], acc);
-        p[h] = acc;
-      }
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1)
-#pragma unroll
-        for (int h = 0; h < GM; ++h) p[h] += __shfl_xor(p[h], o);
-#pragma unroll
-      for (int h = 0; h < GM; ++h) s[h] = fmaf(0.5f * p[h], p[h], s[h]);
     }
-    if (sub == 0) {
+    if (sub == 0 && jj[p] < a.n_blocks) {
       float mx = s[0];
 #pragma unroll
       for (int h = 1; h < GM; ++h)
@@ -102,7 +147,7 @@ __global__ __launch_bounds__(256) void select_scores_kernel(SelectArgs a) {
 #pragma unroll
       for (int h = 0; h < GM; ++h)
         if (h < G) sum += expf(s[h] - mx);
-      a.scores[row] = mx + logf(sum);
+      a.scores[(size_t)bh * a.nblk_capacity + jj[p]] = mx + logf(sum);
     }
   }
 }
@@ -112,127 +157,163 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive prefix sum over a 1024-thread workgroup.  `tmp` holds 16 ints.
-__device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  int x = v;
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const int y = __shfl_up(x, o);
     if (lane >= o) x += y;
   }
-  if (lane == 63) tmp[wid] = x;
-  __syncthreads();
-  if (wid == 0) {
-    int w = lane < 16 ? tmp[lane] : 0;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const int y = __shfl_up(w, o);
-      if (lane >= o) w += y;
-    }
-    if (lane < 16) tmp[16 + lane] = w;  // inclusive wave prefix
-  }
-  __syncthreads();
-  const int before = (wid == 0 ? 0 : tmp[16 + wid - 1]) + x - v;
-  *total = tmp[31];
-  __syncthreads();
-  return before;
+  return x;
 }
 
-__global__ __launch_bounds__(1024) void topk_kernel(SelectArgs a) {
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkWaves = kTopkThreads / 64;
+
+// Exclusive prefix sum over the workgroup; `tmp` holds kTopkWaves ints.  Returns the
+// exclusive prefix and writes the total.
+__device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(v);
+  if (lane == 63) tmp[wid] = incl;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) {
+    const int t = tmp[w];
+    before += (w < wid) ? t : 0;
+    tot += t;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + incl - v;
+}
+
+// One workgroup of 1024 threads per (b, K/V head).  Thread t owns the contiguous
+// block range [t*per, (t+1)*per); keys stay in registers when per <= KPT.
+template <int KPT>
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
   __shared__ uint32_t hist[256];
-  __shared__ int scan_tmp[32];
-  __shared__ uint32_t s_prefix, s_pmask;
-  __shared__ int s_remaining;
-  const int tid = threadIdx.x;
+  __shared__ int scan_tmp[kTopkWaves];
+  __shared__ int s_digit, s_above;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int bh = blockIdx.x;
   const int NB = a.n_blocks;
-  const int per = (NB + 1023) / 1024;
+  const int per = (NB + kTopkThreads - 1) / kTopkThreads;
   const int j0 = min(tid * per, NB), j1 = min(j0 + per, NB);
   const float* sc = a.scores + (size_t)bh * a.nblk_capacity;
   int32_t* out = a.sel + (size_t)bh * a.top_k;
 
-  uint64_t cand = 0ull;  // bit (j - j0): block j is a candidate
-  int ncand_mine = 0;
-  for (int j = j0; j < j1; ++j) {
-    if (forced_mask(a.forced, j) != ~0ull) {
-      cand |= 1ull << (j - j0);
-      ++ncand_mine;
-    }
-  }
-  int ncand;
-  block_exclusive_scan(ncand_mine, scan_tmp, &ncand);
-  const int kk = min(a.top_k, ncand);
-  if (kk > 0) {
-    if (tid == 0) { s_prefix = 0u; s_pmask = 0u; s_remaining = kk; }
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      if (tid < 256) hist[tid] = 0u;
-      __syncthreads();
-      const uint32_t prefix = s_prefix, pmask = s_pmask;
-      for (int j = j0; j < j1; ++j) {
-        if (!((cand >> (j - j0)) & 1ull)) continue;
-        const uint32_t key = order_key(sc[j]);
-        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      if (tid == 0) {
-        int rem = s_remaining, cum = 0, digit = 0;
-        for (int dgt = 255; dgt >= 0; --dgt) {
-          const int h = (int)hist[dgt];
-          if (cum + h >= rem) { digit = dgt; break; }
-          cum += h;
-        }
-        s_remaining = rem - cum;
-        s_prefix = prefix | ((uint32_t)digit << shift);
-        s_pmask = pmask | (255u << shift);
-      }
-      __syncthreads();
-    }
-  }
-  const uint32_t T = s_prefix;
-  const int need_eq = kk > 0 ? s_remaining : 0;
-  int gt = 0, eq = 0;
-  if (kk > 0) {
-    for (int j = j0; j < j1; ++j) {
-      if (!((cand >> (j - j0)) & 1ull)) continue;
-      const uint32_t key = order_key(sc[j]);
-      gt += key > T;
-      eq += key == T;
+  // keys of my candidates (non-candidates are never counted); registers if they fit
+  uint32_t kreg[KPT];
+  uint64_t cmask = 0ull;  // bit t: block j0 + t is a candidate
+#pragma unroll
+  for (int t = 0; t < KPT; ++t) {
+    const int j = j0 + t;
+    kreg[t] = 0u;
+    if (j < j1) {
+      kreg[t] = order_key(sc[j]);
+      if (forced_mask(a.forced, j) != ~0ull) cmask |= 1ull << t;
     }
   }
   int tot;
-  const int eq_before = block_exclusive_scan(eq, scan_tmp, &tot);
-  const int take_eq = max(0, min(eq, need_eq - eq_before));
-  const int pos0 = block_exclusive_scan(gt + take_eq, scan_tmp, &tot);
+  const int ncand_dummy = block_excl_scan(__popcll(cmask), scan_tmp, &tot);
+  (void)ncand_dummy;
+  const int kk = min(a.top_k, tot);
+
+  uint32_t prefix = 0u, pmask = 0u;
+  int remaining = kk;
   if (kk > 0) {
-    int pos = pos0, taken = 0;
-    for (int j = j0; j < j1; ++j) {
-      if (!((cand >> (j - j0)) & 1ull)) continue;
-      const uint32_t key = order_key(sc[j]);
-      if (key > T || (key == T && taken < take_eq)) {
-        taken += key == T;
-        out[pos++] = j;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      if (tid < 256) hist[tid] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int t = 0; t < KPT; ++t)
+        if (((cmask >> t) & 1ull) && (kreg[t] & pmask) == prefix) atomicAdd(&hist[(kreg[t] >> shift) & 255u], 1u);
+      __syncthreads();
+      if (wid == 0) {
+        // lane l owns digits 255-4l .. 252-4l (descending order)
+        int c[4], sum = 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          c[t] = (int)hist[255 - 4 * lane - t];
+          sum += c[t];
+        }
+        int cum = wave_incl_scan(sum) - sum;
+        int found = -1, above = 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if (found < 0 && cum + c[t] >= remaining) { found = 255 - 4 * lane - t; above = cum; }
+          cum += c[t];
+        }
+        const uint64_t hit = __ballot(found >= 0);
+        const int src = __ffsll((unsigned long long)hit) - 1;
+        if (lane == src) { s_digit = found; s_above = above; }
+      }
+      __syncthreads();
+      remaining -= s_above;
+      prefix |= (uint32_t)s_digit << shift;
+      pmask |= 255u << shift;
+    }
+  }
+  // emit: keys above the threshold, then the lowest-index keys equal to it
+  const uint32_t T = prefix;
+  int gt = 0, eq = 0;
+  if (kk > 0) {
+#pragma unroll
+    for (int t = 0; t < KPT; ++t) {
+      if (!((cmask >> t) & 1ull)) continue;
+      gt += kreg[t] > T;
+      eq += kreg[t] == T;
+    }
+  }
+  const int eq_before = block_excl_scan(eq, scan_tmp, &tot);
+  const int take_eq = max(0, min(eq, remaining - eq_before));
+  const int cnt = gt + take_eq;
+  int pos = block_excl_scan(cnt, scan_tmp, &tot);
+  if (kk > 0 && cnt > 0) {
+    int taken = 0;
+#pragma unroll
+    for (int t = 0; t < KPT; ++t) {
+      if (!((cmask >> t) & 1ull)) continue;
+      if (kreg[t] > T || (kreg[t] == T && taken < take_eq)) {
+        taken += kreg[t] == T;
+        out[pos++] = j0 + t;
       }
     }
   }
-  for (int i = kk + tid; i < a.top_k; i += 1024) out[i] = -1;
+  for (int i = kk + tid; i < a.top_k; i += kTopkThreads) out[i] = -1;
+}
+
+template <int D, int GM, int RM, bool BF16>
+hipError_t launch_t(const SelectArgs& a, hipStream_t stream) {
+  constexpr int BPW = 16 * (RM == 0 ? 4 : (RM <= 4 ? 2 : 1));
+  dim3 grid((a.n_blocks + BPW - 1) / BPW, a.batch * a.n_kv_heads);
+  if (a.n_blocks > 0)
+    hipLaunchKernelGGL((select_scores_kernel<D, GM, RM, BF16>), grid, dim3(256), 0, stream, a);
+  const int per = (a.n_blocks + kTopkThreads - 1) / kTopkThreads;
+  const dim3 tg(a.batch * a.n_kv_heads), tb(kTopkThreads);
+  if (per <= 2) hipLaunchKernelGGL(topk_kernel<2>, tg, tb, 0, stream, a);
+  else if (per <= 8) hipLaunchKernelGGL(topk_kernel<8>, tg, tb, 0, stream, a);
+  else if (per <= 32) hipLaunchKernelGGL(topk_kernel<32>, tg, tb, 0, stream, a);
+  else hipLaunchKernelGGL(topk_kernel<64>, tg, tb, 0, stream, a);
+  return hipGetLastError();
 }
 
 template <int D, int GM, bool BF16>
-hipError_t launch_t(const SelectArgs& a, hipStream_t stream) {
-  dim3 grid((a.n_blocks + kBlocksPerWg - 1) / kBlocksPerWg, a.batch * a.n_kv_heads);
-  if (a.n_blocks > 0)
-    hipLaunchKernelGGL((select_scores_kernel<D, GM, BF16>), grid, dim3(256), 0, stream, a);
-  hipLaunchKernelGGL(topk_kernel, dim3(a.batch * a.n_kv_heads), dim3(1024), 0, stream, a);
-  return hipGetLastError();
+hipError_t launch_r(const SelectArgs& a, hipStream_t stream) {
+  if (a.rank == 0) return launch_t<D, GM, 0, BF16>(a, stream);
+  if (a.rank <= 4) return launch_t<D, GM, 4, BF16>(a, stream);
+  return launch_t<D, GM, 8, BF16>(a, stream);
 }
 
 template <int D, bool BF16>
 hipError_t launch_g(const SelectArgs& a, hipStream_t stream) {
   const int G = a.n_q_heads / a.n_kv_heads;
-  if (G <= 4) return launch_t<D, 4, BF16>(a, stream);
-  if (G <= 8) return launch_t<D, 8, BF16>(a, stream);
-  return launch_t<D, 16, BF16>(a, stream);
+  if (G <= 4) return launch_r<D, 4, BF16>(a, stream);
+  if (G <= 8) return launch_r<D, 8, BF16>(a, stream);
+  return launch_r<D, 16, BF16>(a, stream);
 }
 
 }  // namespace

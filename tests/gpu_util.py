@@ -56,7 +56,7 @@ def gpu_decode_step(api, x, w, kv_capacity=None, nblk_capacity=None, global_pos=
     sel = torch.full((B, Hkv, w.top_k), -7, dtype=torch.int32, device="cuda")
     api.bsattn_select_topk(shape, Q, mean, factor, w.rank, max(nbcap, 1), w.top_k, w.window,
                            w.n_sink, list(global_pos), sel, scores)
-    ws = torch.empty(api.bsattn_decode_workspace_bytes(shape, w.top_k, w.window, w.n_sink,
+    ws = torch.zeros(api.bsattn_decode_workspace_bytes(shape, w.top_k, w.window, w.n_sink,
                                                        len(global_pos)), dtype=torch.uint8,
                      device="cuda")
     O = torch.full((B, Hq, d), float("nan"), device="cuda")

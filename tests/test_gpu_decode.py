@@ -164,3 +164,37 @@ def test_first_order_decode_32k_full_size(api):
 
 def test_cobs_decode_128k_full_size(api):
     _full_size(api, "cobs_decode_128k", [(0, 0), (3, 7)])
+
+
+def test_repeated_calls_reuse_the_workspace(api):
+    """The workspace only holds split partials: it needs no initialisation, and
+    repeated calls (and a smaller call after a larger one) on one workspace give
+    identical results."""
+    import torch
+    w = _w("reuse", 2, 16, 2, 128, 3000, 2, 8, 256, 64, "bf16", 22)
+    x = make_decode_inputs(w)
+    ref = gpu_decode_step(api, x, w)
+    Q, K, V = (torch.from_numpy(np.ascontiguousarray(x[k]).view(np.int16)).view(torch.bfloat16).cuda()
+               for k in ("Q", "K", "V"))
+    shape = api.make_shape(2, 16, 2, 128, 3000)
+    sel = torch.from_numpy(ref["sel"]).cuda()
+    nbytes = api.bsattn_decode_workspace_bytes(shape, w.top_k, w.window, w.n_sink, 0)
+    ws = torch.full((nbytes,), 255, dtype=torch.uint8, device="cuda")  # garbage contents
+    for rep in range(3):
+        O = torch.full((2, 16, 128), float("nan"), device="cuda")
+        lse = torch.full((2, 16), float("nan"), device="cuda")
+        api.bsattn_decode(shape, Q, K, V, sel, w.top_k, w.window, w.n_sink, None, O, lse, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(O.cpu().numpy(), ref["O"]), rep
+        assert np.array_equal(lse.cpu().numpy(), ref["lse"]), rep
+    # a smaller problem on the same workspace
+    small = _w("reuse_small", 1, 4, 1, 128, 700, 0, 2, 64, 0, "bf16", 23)
+    xs = make_decode_inputs(small)
+    got = gpu_decode_step(api, xs, small)
+    Qs, Ks, Vs = (torch.from_numpy(np.ascontiguousarray(xs[k]).view(np.int16)).view(torch.bfloat16).cuda()
+                  for k in ("Q", "K", "V"))
+    O = torch.empty((1, 4, 128), device="cuda")
+    api.bsattn_decode(api.make_shape(1, 4, 1, 128, 700), Qs, Ks, Vs, torch.from_numpy(got["sel"]).cuda(),
+                      2, 64, 0, None, O, None, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(O.cpu().numpy(), got["O"])
