@@ -191,10 +191,13 @@ def bench_prefill(api, torch, w, x, steps, warmup):
                          O=torch.empty((B, Hq, N, d), device="cuda"),
                          lse=torch.empty((B, Hq, N), device="cuda")))
     g = list(w.global_pos)
+    ws_bytes = api.bsattn_prefill_workspace_bytes(shape, len(g))
+    for rp in reps:
+        rp["ws"] = torch.empty((ws_bytes,), dtype=torch.uint8, device="cuda") if ws_bytes else None
 
     def run(rp):
         api.bsattn_prefill(shape, rp["Q"], rp["K"], rp["V"], w.window_left, w.window_right,
-                           w.causal, g, rp["O"], rp["lse"])
+                           w.causal, g, rp["O"], rp["lse"], rp["ws"])
 
     for i in range(warmup):
         run(reps[i % R])

@@ -158,11 +158,21 @@ bsattn_status bsattn_decode(const bsattn_shape* shape, const void* Q, const void
  * BSATTN_ERR_UNSUPPORTED.  Key tiles wholly outside the mask are skipped
  * [SWA FlashAttentionとの組み合わせ].  lse may be NULL.  Q/O row stride is
  * N = n_ctx; K/V row stride is kv_capacity.
+ * workspace: with n_global > 0, device memory of at least
+ * bsattn_prefill_workspace_bytes(shape, n_global) bytes, 256-byte aligned (the
+ * key-split partials of the global query rows; contents need not be
+ * initialised); with n_global == 0 it is not read and may be NULL.  Calls that
+ * share a workspace must be ordered (same stream).
  */
 bsattn_status bsattn_prefill(const bsattn_shape* shape, const void* Q, const void* K,
                              const void* V, int32_t window_left, int32_t window_right,
                              int32_t causal, const int32_t* global_pos_host, int32_t n_global,
-                             float* O, float* lse, void* hip_stream);
+                             float* O, float* lse, void* workspace, size_t ws_bytes,
+                             void* hip_stream);
+
+/* Bytes of device workspace bsattn_prefill needs with n_global global positions
+ * (0 when n_global == 0 or the arguments are invalid). */
+size_t bsattn_prefill_workspace_bytes(const bsattn_shape* shape, int32_t n_global);
 
 /* Static description of a status code. */
 const char* bsattn_status_string(bsattn_status status);

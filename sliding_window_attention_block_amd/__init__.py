@@ -18,6 +18,7 @@ from ._lib import BSATTN_BF16, BSATTN_F32, Shape
 __all__ = [
     "BsattnError", "Shape", "make_shape", "library", "bsattn_build_summaries",
     "bsattn_select_topk", "bsattn_decode_workspace_bytes", "bsattn_decode", "bsattn_prefill",
+    "bsattn_prefill_workspace_bytes",
     "bsattn_status_string", "bsattn_version", "BSATTN_F32", "BSATTN_BF16",
 ]
 
@@ -109,12 +110,17 @@ def bsattn_decode(shape, Q, K, V, sel, top_k, window, n_sink, global_pos, O, lse
                                    _ptr(workspace), ws_bytes, _stream(stream)))
 
 
+def bsattn_prefill_workspace_bytes(shape, n_global):
+    return int(library().bsattn_prefill_workspace_bytes(ctypes.byref(shape), int(n_global)))
+
+
 def bsattn_prefill(shape, Q, K, V, window_left, window_right, causal, global_pos, O, lse=None,
-                   stream=None):
+                   workspace=None, stream=None):
     g, ng = _globals(global_pos)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(library().bsattn_prefill(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), window_left,
                                     window_right, int(bool(causal)), g, ng, _ptr(O), _ptr(lse),
-                                    _stream(stream)))
+                                    _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def default_scale(head_dim):

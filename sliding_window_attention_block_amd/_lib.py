@@ -26,6 +26,7 @@ EXPORTS = (
     "bsattn_decode_workspace_bytes",
     "bsattn_decode",
     "bsattn_prefill",
+    "bsattn_prefill_workspace_bytes",
     "bsattn_status_string",
     "bsattn_last_error",
     "bsattn_version",
@@ -75,8 +76,10 @@ def load():
                                   _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.bsattn_decode.restype = _st
     lib.bsattn_prefill.argtypes = [_pshape, _vp, _vp, _vp, _i32, _i32, _i32, _pi32, _i32,
-                                   _vp, _vp, _vp]
+                                   _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.bsattn_prefill.restype = _st
+    lib.bsattn_prefill_workspace_bytes.argtypes = [_pshape, _i32]
+    lib.bsattn_prefill_workspace_bytes.restype = ctypes.c_size_t
     lib.bsattn_status_string.argtypes = [_st]
     lib.bsattn_status_string.restype = ctypes.c_char_p
     lib.bsattn_last_error.argtypes = []

@@ -134,6 +134,24 @@ WsLayout workspace_layout(const bsattn_shape* s, int n_items) {
 }
 size_t workspace_for(const bsattn_shape* s, int n_items) { return workspace_layout(s, n_items).total; }
 
+// Prefill workspace (global query rows only): partial numerators
+// [B*Hq, ceil(n_global/32), splits, 32, d] | partial (max, sum) [..., 2], 256-byte aligned.
+struct PrefillWs {
+  int splits, keys_per_split, n_wg;
+  size_t o_off, ml_off, total;
+};
+PrefillWs prefill_workspace_layout(const bsattn_shape* s, int n_global) {
+  PrefillWs l;
+  bsattn::prefill_global_geometry(s->n_ctx, n_global, s->batch, s->n_q_heads, &l.splits,
+                                  &l.keys_per_split, &l.n_wg);
+  const size_t rows = (size_t)s->batch * s->n_q_heads * ((n_global + 31) / 32) * l.splits * 32;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  l.o_off = 0;
+  l.ml_off = up(rows * s->head_dim * sizeof(float));
+  l.total = n_global > 0 ? l.ml_off + up(rows * 2 * sizeof(float)) : 0;
+  return l;
+}
+
 }  // namespace
 
 extern "C" {
@@ -273,10 +291,16 @@ bsattn_status bsattn_decode(const bsattn_shape* shape, const void* Q, const void
   return BSATTN_OK;
 }
 
+size_t bsattn_prefill_workspace_bytes(const bsattn_shape* shape, int32_t n_global) {
+  if (check_shape(shape, false) != BSATTN_OK) return 0;
+  if (n_global <= 0 || n_global > BSATTN_MAX_GLOBAL) return 0;
+  return prefill_workspace_layout(shape, n_global).total;
+}
+
 bsattn_status bsattn_prefill(const bsattn_shape* shape, const void* Q, const void* K, const void* V,
                              int32_t window_left, int32_t window_right, int32_t causal,
                              const int32_t* global_pos_host, int32_t n_global, float* O, float* lse,
-                             void* hip_stream) {
+                             void* workspace, size_t ws_bytes, void* hip_stream) {
   g_err[0] = 0;
   bsattn_status st = check_shape(shape, false);
   if (st != BSATTN_OK) return st;
@@ -290,9 +314,15 @@ bsattn_status bsattn_prefill(const bsattn_shape* shape, const void* Q, const voi
     return fail(BSATTN_ERR_UNSUPPORTED, "global tokens are bidirectional; causal masks take none");
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O))
     return fail(BSATTN_ERR_INVALID, "device pointers must be 16-byte aligned");
+  const PrefillWs lay = prefill_workspace_layout(shape, n_global);
+  if (lay.total > 0) {
+    if (workspace == nullptr || ws_bytes < lay.total)
+      return fail(BSATTN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", lay.total, ws_bytes);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      return fail(BSATTN_ERR_INVALID, "workspace must be 256-byte aligned");
+  }
   const long long n_qt = (shape->n_ctx + 127) / 128;
-  const long long n_wg = n_qt * shape->batch * shape->n_q_heads +
-                         (long long)shape->batch * shape->n_q_heads * ((n_global + 31) / 32);
+  const long long n_wg = n_qt * shape->batch * shape->n_q_heads + lay.n_wg;
   if (n_wg > 0x7fffffffLL) return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");
   bsattn::PrefillArgs a;
   std::memset(&a, 0, sizeof(a));
@@ -307,6 +337,13 @@ bsattn_status bsattn_prefill(const bsattn_shape* shape, const void* Q, const voi
   a.scale = effective_scale(shape);
   a.n_global = n_global;
   for (int i = 0; i < n_global; ++i) a.gpos[i] = global_pos_host[i];
+  if (lay.total > 0) {
+    a.n_global_wg = lay.n_wg;
+    a.g_splits = lay.splits;
+    a.g_keys_per_split = lay.keys_per_split;
+    a.g_part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.o_off);
+    a.g_part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.ml_off);
+  }
   hipError_t e = bsattn::launch_prefill(a, (hipStream_t)hip_stream);
   if (e != hipSuccess) return fail(BSATTN_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
   return BSATTN_OK;

@@ -92,7 +92,16 @@ struct PrefillArgs {
   float scale;
   int32_t n_global;
   int32_t gpos[256];
+  // global query rows: key range split over waves, partials in the workspace
+  int32_t n_global_wg;        // workgroups (first in the grid) that run global rows
+  int32_t g_splits;           // key ranges per global row
+  int32_t g_keys_per_split;
+  float* g_part_o;            // [B*Hq, ceil(n_global/32), g_splits, 32, d]
+  float* g_part_ml;           // [B*Hq, ceil(n_global/32), g_splits, 32, 2] (max, normaliser), log2
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+// Split geometry of the global query rows (also sizes the prefill workspace).
+void prefill_global_geometry(int seq_len, int n_global, int batch, int n_q_heads, int* splits,
+                             int* keys_per_split, int* n_wg);
 
 }  // namespace bsattn

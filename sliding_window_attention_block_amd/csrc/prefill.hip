@@ -12,129 +12,176 @@
 // per-element mask.  Softmax is the online (flash) form: a running max and
 // normaliser per query row, rescaled as tiles arrive.
 //
-// Layout of the work (gfx950, v_mfma_f32_32x32x16_bf16):
+// Work layout on gfx950 (v_mfma_f32_32x32x16_bf16):
 //  * band workgroup: 128 query rows of one (b, h); wave w owns rows 32w..32w+31.
-//    K/V tiles of 64 keys are staged in LDS (XOR-swizzled 16-byte chunks) with
-//    a register prefetch of the next tile.  Per 32-key sub-tile a wave computes
-//    S^T = K Q^T (A = K from LDS, B = Q^T in registers), so lane l holds 16 of
-//    the 32 logits of query row l%32, then O^T += V^T P^T with V^T read by
+//    K/V tiles of 64 keys are copied HBM -> LDS with global_load_lds_dwordx4
+//    into double-buffered, XOR-swizzled tiles (one barrier per tile).  A wave
+//    computes S^T = K Q^T for both 32-key halves of the tile (two independent
+//    MFMA chains; A = K from LDS, B = Q^T in registers), so lane l holds 32
+//    logits of query row l%32, then O^T += V^T P^T with V^T read by
 //    ds_read_b64_tr_b16 and P^T taken straight from the logits' registers.
-//  * in local+global mode, the global key columns that fall outside a
-//    workgroup's band tiles are gathered into extra 64-key tiles, and separate
-//    workgroups compute the global query rows against all keys (the 4 waves
-//    split the keys, then merge their partial softmax states in LDS).  Band
+//    Softmax per tile: one FMA folds the scale into exp2's argument, the row
+//    max is only moved (and the accumulator rescaled, wave-uniformly) when it
+//    grows by more than 2^8, and P is rounded to bf16 by v_cvt_pk_bf16_f32.
+//    Rows that see few keys add the bf16 residual of P in a second product.
+//  * local+global: the global key columns outside a workgroup's band tiles are
+//    gathered into extra tiles.  The global query rows (every key) are split
+//    by key range over many waves (first in the grid); each writes a partial
+//    softmax state to the workspace, and a merge kernel combines them.  Band
 //    workgroups do not store global rows.
-//  * workgroup order: global-row workgroups first, then band workgroups with
-//    the K/V head varying fastest (consecutive workgroups land on different
-//    XCDs, so each XCD's L2 keeps one head's K/V), heaviest query tiles first.
+//  * band workgroup order: K/V head varying fastest (consecutive workgroups
+//    land on different XCDs, so each XCD's L2 keeps one head's K/V), heaviest
+//    query tiles first.
 #include "launch.hpp"
 
 namespace bsattn {
 namespace {
 
-constexpr int BM = 128;  // query rows per band workgroup
-constexpr int BN = 64;   // keys per LDS stage
-// Rows that see fewer keys than this get the compensated (bf16 hi + lo) PV product.
-constexpr int kCompKeys = 128;
+constexpr int BM = 128;        // query rows per band workgroup
+constexpr int BN = 64;         // keys per LDS stage
+constexpr int kCompKeys = 256; // rows seeing fewer keys take the compensated PV product
+constexpr float kHeadroom = 8.f;  // log2 units a row max may grow before the rescale
 
 template <int D>
 struct Tile {
   static constexpr int RB = D * 2;       // bytes per row
-  static constexpr int CPR = D / 8;      // 16-byte chunks per row
   static constexpr int RPL = 256 / RB;   // rows per 256-byte LDS line
   static constexpr int BYTES = BN * RB;  // one K or V stage
   // K tile: read by rows (32 rows x 2 chunks per instruction)
-  static __device__ __forceinline__ uint32_t k_off(int r, int c) {
-    const int f = (r / RPL) & (16 / RPL - 1);
-    return (uint32_t)(r * RB + ((c ^ f) << 4));
-  }
+  static __device__ __forceinline__ int k_swz(int r) { return (r / RPL) & (16 / RPL - 1); }
   // V tile: read transposed (8 rows x 4 chunks per instruction)
-  static __device__ __forceinline__ uint32_t v_off(int r, int c) {
-    const int f = 4 * ((r / RPL) & (4 / RPL - 1));
-    return (uint32_t)(r * RB + ((c ^ f) << 4));
+  static __device__ __forceinline__ int v_swz(int r) { return 4 * ((r / RPL) & (4 / RPL - 1)); }
+  static __device__ __forceinline__ uint32_t k_off(int r, int c) { return (uint32_t)(r * RB + ((c ^ k_swz(r)) << 4)); }
+  static __device__ __forceinline__ uint32_t v_off(int r, int c) { return (uint32_t)(r * RB + ((c ^ v_swz(r)) << 4)); }
+};
+
+struct RowState {
+  float m;  // running max in log2 units (may lag the true max by up to kHeadroom)
+  float l;  // normaliser relative to m (partial per lane; lanes l, l^32 sum)
+};
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
+}
+
+// Copy rows [0, 64) of a K/V stage into LDS tiles with 1 KB DMA instructions.
+// `row_pos(r)` is the token position of tile row r (already clamped into range).
+// Wave `wid` of `nw` issues its share of the chunks.
+template <int D, typename RowPos>
+__device__ __forceinline__ void dma_stage(const uint16_t* Kb, const uint16_t* Vb, uint8_t* kt, uint8_t* vt,
+                                          int wid, int nw, RowPos row_pos) {
+  using T = Tile<D>;
+  typedef __attribute__((address_space(3))) void lds_void;
+  constexpr int NCH = T::BYTES / 1024;
+  const int lane = threadIdx.x & 63;
+  for (int k = wid; k < NCH; k += nw) {
+    const int off = 1024 * k + 16 * lane;
+    const int r = off / T::RB, pc = (off % T::RB) >> 4;
+    const size_t pos = (size_t)row_pos(r);
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(Kb + pos * D + (pc ^ T::k_swz(r)) * 8),
+                                     (lds_void*)(kt + 1024 * k), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(Vb + pos * D + (pc ^ T::v_swz(r)) * 8),
+                                     (lds_void*)(vt + 1024 * k), 16, 0, 0);
   }
-};
+}
 
-struct Softmax {
-  float m, l;
-};
-
-// One 32-key sub-tile for a wave: logits, mask, online softmax update, PV.
-// `kt` / `vt` are the LDS K/V tiles, `krow0` the sub-tile's first row in them.
-// mask_fn(e) returns whether element e (key 8(e/4) + 4(l/32) + e%4) is allowed.
-// `comp` (wave-uniform) adds a second PV product with the bf16 residual of P, so
-// rows that see only a few keys are not limited by the 2^-9 rounding of P.
-template <int D, typename MaskFn>
-__device__ __forceinline__ void subtile(const uint8_t* kt, const uint8_t* vt, int krow0,
-                                        const u32x4* qop, f32x16* oacc, Softmax& st, float sl2,
-                                        bool masked, bool comp, MaskFn mask_fn) {
+// One 64-key stage held in LDS for this wave's 32 query rows.  on[u]: half u
+// (keys 32u..32u+31) has an allowed entry for some row of the wave; part[u]: it
+// needs the per-element mask allowed(u, e) (element e of lane l is key
+// 32u + 8(e/4) + 4(l/32) + e%4).  Every branch here is wave-uniform.
+template <int D, typename Allowed>
+__device__ __forceinline__ void stage(const uint8_t* kt, const uint8_t* vt, const u32x4* qop,
+                                      f32x16* oacc, RowState& st, float sl2, bool on0, bool on1,
+                                      bool part0, bool part1, bool comp, Allowed allowed) {
   using T = Tile<D>;
   const int lane = threadIdx.x & 63;
   const int r32 = lane & 31, h2 = lane >> 5;
-  f32x16 s;
+  f32x16 s[2];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) s[e] = 0.f;
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s[u][e] = 0.f;
 #pragma unroll
   for (int c = 0; c < D / 16; ++c) {
-    const u32x4 kop = *reinterpret_cast<const u32x4*>(kt + T::k_off(krow0 + r32, 2 * c + h2));
-    s = mfma32x32x16(as_bf16x8(kop), as_bf16x8(qop[c]), s);
+    if (on0) {
+      const u32x4 k0 = *reinterpret_cast<const u32x4*>(kt + T::k_off(r32, 2 * c + h2));
+      s[0] = mfma32x32x16(as_bf16x8(k0), as_bf16x8(qop[c]), s[0]);
+    }
+    if (on1) {
+      const u32x4 k1 = *reinterpret_cast<const u32x4*>(kt + T::k_off(32 + r32, 2 * c + h2));
+      s[1] = mfma32x32x16(as_bf16x8(k1), as_bf16x8(qop[c]), s[1]);
+    }
   }
+  const bool on[2] = {on0, on1}, part[2] = {part0, part1};
   float mx = -INFINITY;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    float v = s[e] * sl2;
-    if (masked && !mask_fn(e)) v = -INFINITY;
-    s[e] = v;
-    mx = fmaxf(mx, v);
+  for (int u = 0; u < 2; ++u) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float v = s[u][e];
+      if (!on[u] || (part[u] && !allowed(u, e))) v = -INFINITY;
+      s[u][e] = v;
+      mx = fmaxf(mx, v);
+    }
   }
   mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(st.m, mx);
-  // No branch on m_new: rows with nothing allowed yet keep m = -inf and l = 0 (the
-  // MFMAs below must run with every lane active).
-  const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-  const float alpha = exp2f(st.m - m_use);
-  u32x4 pop[2], plo[2];
+  const float m_cand = mx * sl2;
+  const bool need = m_cand > st.m + kHeadroom;
+  if (__ballot(need)) {
+    const float m_new = need ? m_cand : st.m;
+    const float alpha = need ? __builtin_amdgcn_exp2f(st.m - m_new) : 1.f;
+    st.l *= alpha;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) oacc[t] *= alpha;
+    st.m = m_new;
+  }
+  const float nm = (st.m == -INFINITY) ? 0.f : -st.m;
+  u32x4 pop[2][2], plo[2][2];
   float psum = 0.f;
 #pragma unroll
-  for (int kc = 0; kc < 2; ++kc) {
+  for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p0 = exp2f(s[8 * kc + 2 * i] - m_use), p1 = exp2f(s[8 * kc + 2 * i + 1] - m_use);
-      const uint32_t pk = pack_bf16x2(p0, p1);
-      pop[kc][i] = pk;
-      if (comp) {
-        plo[kc][i] = pack_bf16x2(p0 - bf16lo(pk), p1 - bf16hi(pk));
-        psum += p0 + p1;
-      } else {
-        psum += bf16lo(pk) + bf16hi(pk);  // normaliser of the rounded weights the MFMA sees
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[u][8 * kc + 2 * i], sl2, nm));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[u][8 * kc + 2 * i + 1], sl2, nm));
+        const uint32_t pk = cvt_pk_bf16(p0, p1);
+        pop[u][kc][i] = pk;
+        if (comp) {
+          plo[u][kc][i] = cvt_pk_bf16(p0 - bf16lo(pk), p1 - bf16hi(pk));
+          psum += p0 + p1;
+        } else {
+          psum += bf16lo(pk) + bf16hi(pk);  // normaliser of the rounded weights the MFMA sees
+        }
       }
-    }
-  }
-  st.l = st.l * alpha + psum;
-  st.m = m_new;
-#pragma unroll
-  for (int t = 0; t < D / 32; ++t) oacc[t] *= alpha;
+  st.l += psum;
   const int q16 = lane >> 4, a16 = lane & 15;
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
+  for (int u = 0; u < 2; ++u) {
+    if (!on[u]) continue;
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      const int row = krow0 + 16 * kc + 4 * h2 + (a16 >> 2);
-      const int col = 32 * dt + 16 * (q16 & 1) + 4 * (a16 & 3);  // element
-      const u32x2 lo = lds_read_tr16(vt, T::v_off(row, col >> 3) + ((col & 7) << 1));
-      const u32x2 hi = lds_read_tr16(vt, T::v_off(row + 8, col >> 3) + ((col & 7) << 1));
-      const u32x4 vop = u32x4{lo[0], lo[1], hi[0], hi[1]};
-      oacc[dt] = mfma32x32x16(as_bf16x8(vop), as_bf16x8(pop[kc]), oacc[dt]);
-      if (comp) oacc[dt] = mfma32x32x16(as_bf16x8(vop), as_bf16x8(plo[kc]), oacc[dt]);
-    }
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const int row = 32 * u + 16 * kc + 4 * h2 + (a16 >> 2);
+        const int col = 32 * dt + 16 * (q16 & 1) + 4 * (a16 & 3);  // element
+        const u32x2 lo = lds_read_tr16(vt, T::v_off(row, col >> 3) + ((col & 7) << 1));
+        const u32x2 hi = lds_read_tr16(vt, T::v_off(row + 8, col >> 3) + ((col & 7) << 1));
+        const u32x4 vop = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        oacc[dt] = mfma32x32x16(as_bf16x8(vop), as_bf16x8(pop[u][kc]), oacc[dt]);
+        if (comp) oacc[dt] = mfma32x32x16(as_bf16x8(vop), as_bf16x8(plo[u][kc]), oacc[dt]);
+      }
   }
 }
 
 template <int D, bool LG>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   using T = Tile<D>;
-  constexpr int LDS_BYTES = 2 * T::BYTES > 32 * D * 4 + 1024 ? 2 * T::BYTES : 32 * D * 4 + 1024;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
+  constexpr int LDS_BYTES = 4 * T::BYTES;  // K and V, double buffered
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
   __shared__ int gcols[256];
   __shared__ int s_ngcols;
 
@@ -143,17 +190,19 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const int N = a.seq_len;
   const int Hq = a.n_q_heads, Hkv = a.n_kv_heads, G = Hq / Hkv;
   const float sl2 = a.scale * kLog2e;
-  const int n_rt = (a.n_global + 31) / 32;
-  const int n_grow = LG ? a.batch * Hq * n_rt : 0;
+  const int n_gwg = LG ? a.n_global_wg : 0;
 
-  if (LG && (int)blockIdx.x < n_grow) {
-    // ---------------- global query rows against every key
-    const int rt = blockIdx.x % n_rt;
-    const int bhq = blockIdx.x / n_rt;
-    const int b = bhq / Hq, h = bhq % Hq, g = h / G;
-    const int slot = rt * 32 + r32;
-    const bool row_ok = slot < a.n_global;
-    const int row = row_ok ? a.gpos[slot] : a.gpos[0];
+  if (LG && (int)blockIdx.x < n_gwg) {
+    // ---------------- global query rows: wave = (b, h, row tile, key split)
+    const int unit = blockIdx.x * 4 + wid;
+    const int n_rt = (a.n_global + 31) / 32;
+    const int ks = unit % a.g_splits;
+    const int rt = (unit / a.g_splits) % n_rt;
+    const int bhq = unit / (a.g_splits * n_rt);
+    const bool live = bhq < a.batch * Hq;
+    const int b = live ? bhq / Hq : 0, h = live ? bhq % Hq : 0, g = h / G;
+    const int slot = min(rt * 32 + r32, a.n_global - 1);
+    const int row = a.gpos[slot];
     const uint16_t* Qp = reinterpret_cast<const uint16_t*>(a.Q) + ((size_t)(b * Hq + h) * N + row) * D;
     const uint16_t* Kb = reinterpret_cast<const uint16_t*>(a.K) + (size_t)(b * Hkv + g) * a.kv_capacity * D;
     const uint16_t* Vb = reinterpret_cast<const uint16_t*>(a.V) + (size_t)(b * Hkv + g) * a.kv_capacity * D;
@@ -165,144 +214,60 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     for (int t = 0; t < D / 32; ++t)
 #pragma unroll
       for (int e = 0; e < 16; ++e) oacc[t][e] = 0.f;
-    Softmax st{-INFINITY, 0.f};
-    uint8_t* vt = smem + wid * (32 * T::RB);
-    const int n_sub = (N + 31) / 32;
+    RowState st{-INFINITY, 0.f};
+    // this wave's key range, 32 keys at a time, through its own K and V half tiles
+    const int kr = a.g_keys_per_split;
+    const int k0 = min(N, ks * kr), k1 = min(N, k0 + kr);
+    uint8_t* kt = smem + wid * (LDS_BYTES / 4);
+    uint8_t* vt = kt + T::BYTES / 2;  // half-height tiles: 32 rows each
+    static_assert(T::BYTES % 2048 == 0, "half tiles are whole 1 KB chunks");
     const bool comp = N < kCompKeys;
-    for (int kt = wid; kt < n_sub; kt += 4) {
-      const int j0 = kt * 32;
-      // K rows straight into A operands, V into the wave's LDS tile
-      u32x4 kop[D / 16];
-      {
-        const int key = min(j0 + r32, N - 1);
+    if (live) {
+      for (int j0 = k0; j0 < k1; j0 += 32) {
+        typedef __attribute__((address_space(3))) void lds_void;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        constexpr int NCH = T::BYTES / 2048;  // 1 KB chunks per 32-row tile
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c)
-          kop[c] = *reinterpret_cast<const u32x4*>(Kb + (size_t)key * D + 16 * c + 8 * h2);
-      }
-      constexpr int VPL = 32 * T::CPR / 64;  // V chunks per lane
-      u32x4 vreg[VPL];
-#pragma unroll
-      for (int k = 0; k < VPL; ++k) {
-        const int c = lane + 64 * k;
-        const int key = min(j0 + c / T::CPR, N - 1);
-        vreg[k] = *reinterpret_cast<const u32x4*>(Vb + (size_t)key * D + (c % T::CPR) * 8);
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-      for (int k = 0; k < VPL; ++k) {
-        const int c = lane + 64 * k;
-        *reinterpret_cast<u32x4*>(vt + T::v_off(c / T::CPR, c % T::CPR)) = vreg[k];
-      }
-      f32x16 s;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[e] = 0.f;
-#pragma unroll
-      for (int c = 0; c < D / 16; ++c) s = mfma32x32x16(as_bf16x8(kop[c]), as_bf16x8(qop[c]), s);
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      // online softmax over this sub-tile (keys past N masked)
-      float mx = -INFINITY;
-      const bool tail = j0 + 32 > N;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float v = s[e] * sl2;
-        if (tail && j0 + 8 * (e >> 2) + 4 * h2 + (e & 3) >= N) v = -INFINITY;
-        s[e] = v;
-        mx = fmaxf(mx, v);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(st.m, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2f(st.m - m_use);
-      u32x4 pop[2], plo[2];
-      float psum = 0.f;
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p0 = exp2f(s[8 * kc + 2 * i] - m_use), p1 = exp2f(s[8 * kc + 2 * i + 1] - m_use);
-          const uint32_t pk = pack_bf16x2(p0, p1);
-          pop[kc][i] = pk;
-          if (comp) {
-            plo[kc][i] = pack_bf16x2(p0 - bf16lo(pk), p1 - bf16hi(pk));
-            psum += p0 + p1;
-          } else {
-            psum += bf16lo(pk) + bf16hi(pk);
-          }
+        for (int k = 0; k < NCH; ++k) {
+          const int off = 1024 * k + 16 * lane;
+          const int r = off / T::RB, pc = (off % T::RB) >> 4;
+          const size_t pos = (size_t)min(j0 + r, N - 1);
+          __builtin_amdgcn_global_load_lds(static_cast<const void*>(Kb + pos * D + (pc ^ T::k_swz(r)) * 8),
+                                           (lds_void*)(kt + 1024 * k), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(static_cast<const void*>(Vb + pos * D + (pc ^ T::v_swz(r)) * 8),
+                                           (lds_void*)(vt + 1024 * k), 16, 0, 0);
         }
-      st.l = st.l * alpha + psum;
-      st.m = m_new;
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t) oacc[t] *= alpha;
-      const int q16 = lane >> 4, a16 = lane & 15;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        const bool tail = j0 + 32 > N;
+        stage<D>(kt, vt, qop, oacc, st, sl2, true, false, tail, false, comp, [&](int u, int e) {
+          return j0 + 8 * (e >> 2) + 4 * h2 + (e & 3) < N;
+        });
+      }
+    }
+    // partial state of this wave -> workspace [b*Hq + h][rt][ks][32 rows]
+    st.l += __shfl_xor(st.l, 32);
+    if (live) {
+      const size_t prow = (((size_t)bhq * n_rt + rt) * a.g_splits + ks) * 32 + r32;
+      if (h2 == 0) {
+        a.g_part_ml[2 * prow] = st.m;
+        a.g_part_ml[2 * prow + 1] = st.l;
+      }
+      float* po = a.g_part_o + prow * D;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-          const int vr = 16 * kc + 4 * h2 + (a16 >> 2);
-          const int col = 32 * dt + 16 * (q16 & 1) + 4 * (a16 & 3);
-          const u32x2 lo = lds_read_tr16(vt, T::v_off(vr, col >> 3) + ((col & 7) << 1));
-          const u32x2 hi = lds_read_tr16(vt, T::v_off(vr + 8, col >> 3) + ((col & 7) << 1));
-          const u32x4 vop = u32x4{lo[0], lo[1], hi[0], hi[1]};
-          oacc[dt] = mfma32x32x16(as_bf16x8(vop), as_bf16x8(pop[kc]), oacc[dt]);
-          if (comp) oacc[dt] = mfma32x32x16(as_bf16x8(vop), as_bf16x8(plo[kc]), oacc[dt]);
+        for (int j = 0; j < 4; ++j) {
+          f32x4 v;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = oacc[dt][4 * j + i];
+          *reinterpret_cast<f32x4*>(po + 32 * dt + 8 * j + 4 * h2) = v;
         }
     }
-    // merge the 4 waves' states
-    st.l += __shfl_xor(st.l, 32);
-    __syncthreads();
-    float* ml = reinterpret_cast<float*>(smem);          // [4][32][2]
-    float* obuf = reinterpret_cast<float*>(smem + 1024);  // [32][D]
-    if (lane < 32) { ml[(wid * 32 + r32) * 2] = st.m; ml[(wid * 32 + r32) * 2 + 1] = st.l; }
-    __syncthreads();
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, ml[(w * 32 + r32) * 2]);
-    float L = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float mw = ml[(w * 32 + r32) * 2];
-      if (mw != -INFINITY) L += exp2f(mw - M) * ml[(w * 32 + r32) * 2 + 1];
-    }
-    const float sc = (st.m == -INFINITY) ? 0.f : exp2f(st.m - M);
-    for (int w = 0; w < 4; ++w) {
-      if (wid == w) {
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            float* dst = obuf + r32 * D + 32 * dt + 8 * j + 4 * h2;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float v = oacc[dt][4 * j + i] * sc;
-              dst[i] = (w == 0) ? v : dst[i] + v;
-            }
-          }
-      }
-      __syncthreads();
-    }
-    // write the rows: thread t -> row t / (256/32)... 32 rows x D floats
-    for (int idx = tid; idx < 32 * D; idx += 256) {
-      const int rr = idx / D, d = idx % D;
-      const int sl = rt * 32 + rr;
-      if (sl >= a.n_global) continue;
-      float Lr = 0.f, Mr = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) Mr = fmaxf(Mr, ml[(w * 32 + rr) * 2]);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float mw = ml[(w * 32 + rr) * 2];
-        if (mw != -INFINITY) Lr += exp2f(mw - Mr) * ml[(w * 32 + rr) * 2 + 1];
-      }
-      const int grow = a.gpos[sl];
-      a.O[((size_t)(b * Hq + h) * N + grow) * D + d] = obuf[rr * D + d] / Lr;
-      if (d == 0 && a.lse != nullptr) a.lse[(size_t)(b * Hq + h) * N + grow] = (Mr + log2f(Lr)) * kLn2;
-    }
-    (void)L;
     return;
   }
 
   // ---------------- band workgroup
-  const int w = blockIdx.x - n_grow;
+  const int w = blockIdx.x - n_gwg;
   const int BHkv = a.batch * Hkv;
   const int kvlin = w % BHkv;
   const int rest = w / BHkv;
@@ -347,7 +312,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   for (int t = 0; t < D / 32; ++t)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[t][e] = 0.f;
-  Softmax st{-INFINITY, 0.f};
+  RowState st{-INFINITY, 0.f};
 
   // Keys seen by the wave's rows (globals only add keys): the count is piecewise
   // linear in the row, so its minimum over the 32 rows sits at an end row.
@@ -359,82 +324,53 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const bool comp = __builtin_amdgcn_readfirstlane(
       min(band_keys(min(r0, N - 1)), band_keys(min(r0 + 31, N - 1))) < kCompKeys);
 
-  uint8_t* kt = smem;
-  uint8_t* vt = smem + T::BYTES;
-  constexpr int PT = BN * T::CPR / 256;  // chunks per thread per tile
-  u32x4 kreg[PT], vreg[PT];
-  auto load_stage = [&](int stg) {
-#pragma unroll
-    for (int k = 0; k < PT; ++k) {
-      const int c = tid + 256 * k;
-      const int rr = c / T::CPR, ch = c % T::CPR;
-      int pos;
-      bool ok;
-      if (stg < n_band) {
-        pos = (t_lo + stg) * BN + rr;
-        ok = pos < N;
-      } else {
-        const int slot = (stg - n_band) * BN + rr;
-        ok = slot < ngc;
-        pos = ok ? gcols[slot] : 0;
-      }
-      if (ok) {
-        kreg[k] = *reinterpret_cast<const u32x4*>(Kb + (size_t)pos * D + ch * 8);
-        vreg[k] = *reinterpret_cast<const u32x4*>(Vb + (size_t)pos * D + ch * 8);
-      } else {
-        kreg[k] = u32x4{0u, 0u, 0u, 0u};
-        vreg[k] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
+  auto row_pos = [&](int stg, int r) {
+    if (stg < n_band) return min((t_lo + stg) * BN + r, N - 1);
+    const int slot = (stg - n_band) * BN + r;
+    return gcols[min(slot, ngc - 1)];
   };
-  if (n_stage > 0) load_stage(0);
+  if (n_stage > 0) dma_stage<D>(Kb, Vb, smem, smem + T::BYTES, wid, 4, [&](int r) { return row_pos(0, r); });
   for (int stg = 0; stg < n_stage; ++stg) {
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < PT; ++k) {
-      const int c = tid + 256 * k;
-      const int rr = c / T::CPR, ch = c % T::CPR;
-      *reinterpret_cast<u32x4*>(kt + T::k_off(rr, ch)) = kreg[k];
-      *reinterpret_cast<u32x4*>(vt + T::v_off(rr, ch)) = vreg[k];
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's copies for `stg` landed
+    __syncthreads();  // every wave's copies landed; every wave is done with the other buffer
+    uint8_t* kt = smem + (stg & 1) * 2 * T::BYTES;
+    uint8_t* vt = kt + T::BYTES;
+    if (stg + 1 < n_stage) {
+      uint8_t* kn = smem + ((stg + 1) & 1) * 2 * T::BYTES;
+      dma_stage<D>(Kb, Vb, kn, kn + T::BYTES, wid, 4, [&](int r) { return row_pos(stg + 1, r); });
     }
-    __syncthreads();
-    if (stg + 1 < n_stage) load_stage(stg + 1);
-    const bool band_stage = stg < n_band;
-    uint64_t gbits = 0ull;
-    if (LG && band_stage) {
-      const int base = (t_lo + stg) * BN;
-      for (int i = lower_bound_i32(a.gpos, a.n_global, base); i < a.n_global && a.gpos[i] < base + BN; ++i)
-        gbits |= 1ull << (a.gpos[i] - base);
-    }
+    if (stg < n_band) {
+      const int jb = (t_lo + stg) * BN;
+      uint64_t gbits = 0ull;
+      if (LG) {
+        for (int i = lower_bound_i32(a.gpos, a.n_global, jb); i < a.n_global && a.gpos[i] < jb + BN; ++i)
+          gbits |= 1ull << (a.gpos[i] - jb);
+      }
+      bool on[2], part[2];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      if (band_stage) {
-        const int j0 = (t_lo + stg) * BN + 32 * sub;
-        if (j0 >= N) continue;
-        const uint32_t gsub = (uint32_t)(gbits >> (32 * sub));
+      for (int u = 0; u < 2; ++u) {
+        const int j0 = jb + 32 * u;
+        const uint32_t gsub = (uint32_t)(gbits >> (32 * u));
         const bool any_lo = wl < 0 || j0 + 31 >= r0 - wl;
         const bool any_hi = wr < 0 || j0 <= r0 + 31 + wr;
-        if (!(any_lo && any_hi) && gsub == 0u) continue;  // empty for this wave
+        on[u] = j0 < N && ((any_lo && any_hi) || gsub != 0u);
         const bool all_lo = wl < 0 || j0 >= r0 + 31 - wl;
         const bool all_hi = wr < 0 || j0 + 31 <= r0 + wr;
-        const bool full = all_lo && all_hi && j0 + 31 < N;
-        subtile<D>(kt, vt, 32 * sub, qop, oacc, st, sl2, !full, comp, [&](int e) {
-          const int jr = 8 * (e >> 2) + 4 * h2 + (e & 3);
-          const int j = j0 + jr;
-          const bool in_band = (wl < 0 || j >= myrow - wl) && (wr < 0 || j <= myrow + wr);
-          return j < N && (in_band || ((gsub >> jr) & 1u));
-        });
-      } else {
-        const int s0 = (stg - n_band) * BN + 32 * sub;
-        if (s0 >= ngc) continue;
-        const bool full = s0 + 31 < ngc;
-        subtile<D>(kt, vt, 32 * sub, qop, oacc, st, sl2, !full, comp, [&](int e) {
-          return s0 + 8 * (e >> 2) + 4 * h2 + (e & 3) < ngc;
-        });
+        part[u] = !(all_lo && all_hi && j0 + 31 < N);
       }
+      stage<D>(kt, vt, qop, oacc, st, sl2, on[0], on[1], part[0], part[1], comp, [&](int u, int e) {
+        const int jr = 32 * u + 8 * (e >> 2) + 4 * h2 + (e & 3);
+        const int j = jb + jr;
+        const bool in_band = (wl < 0 || j >= myrow - wl) && (wr < 0 || j <= myrow + wr);
+        return j < N && (in_band || ((gbits >> jr) & 1ull));
+      });
+    } else {
+      const int s0 = (stg - n_band) * BN;
+      stage<D>(kt, vt, qop, oacc, st, sl2, s0 < ngc, s0 + 32 < ngc, s0 + 32 > ngc, s0 + 64 > ngc, comp,
+               [&](int u, int e) { return s0 + 32 * u + 8 * (e >> 2) + 4 * h2 + (e & 3) < ngc; });
     }
   }
-  // write rows (global rows are written by their own workgroups)
+  // write rows (global rows are written by the merge of their split partials)
   st.l += __shfl_xor(st.l, 32);
   bool store = myrow < N;
   if (LG && store) {
@@ -458,17 +394,74 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   }
 }
 
+// Merge the key-split partials of every global query row: one workgroup of D
+// threads per (b, h, global row); 8 partial loads in flight per thread.
+template <int D>
+__global__ __launch_bounds__(D) void prefill_global_merge_kernel(PrefillArgs a) {
+  const int n_rt = (a.n_global + 31) / 32;
+  const int gi = blockIdx.x % a.n_global;
+  const int bhq = blockIdx.x / a.n_global;
+  const int rt = gi / 32, r = gi % 32;
+  const int dd = threadIdx.x;
+  const int KS = a.g_splits;
+  const size_t base = ((size_t)bhq * n_rt + rt) * KS;
+  float M = -INFINITY, L = 0.f, O = 0.f;
+  for (int s0 = 0; s0 < KS; s0 += 8) {
+    float ms[8], ls[8], os[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int s = s0 + u;
+      const size_t prow = (base + min(s, KS - 1)) * 32 + r;
+      ms[u] = s < KS ? a.g_part_ml[2 * prow] : -INFINITY;
+      ls[u] = s < KS ? a.g_part_ml[2 * prow + 1] : 0.f;
+      os[u] = s < KS ? a.g_part_o[prow * D + dd] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (ms[u] == -INFINITY) continue;
+      const float Mn = fmaxf(M, ms[u]);
+      const float c0 = exp2f(M - Mn), c1 = exp2f(ms[u] - Mn);
+      L = L * c0 + ls[u] * c1;
+      O = O * c0 + os[u] * c1;
+      M = Mn;
+    }
+  }
+  const size_t orow = (size_t)bhq * a.seq_len + a.gpos[gi];
+  a.O[orow * D + dd] = L > 0.f ? O / L : 0.f;
+  if (a.lse != nullptr && dd == 0) a.lse[orow] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+}
+
 template <int D, bool LG>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
   const int n_qt = (a.seq_len + BM - 1) / BM;
-  const int n_rt = (a.n_global + 31) / 32;
-  const int n_grow = LG ? a.batch * a.n_q_heads * n_rt : 0;
-  const int n_wg = n_grow + n_qt * a.batch * a.n_q_heads;
+  const int n_wg = (LG ? a.n_global_wg : 0) + n_qt * a.batch * a.n_q_heads;
   hipLaunchKernelGGL((prefill_kernel<D, LG>), dim3(n_wg), dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !LG) return e;
+  hipLaunchKernelGGL((prefill_global_merge_kernel<D>), dim3(a.batch * a.n_q_heads * a.n_global), dim3(D), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
+
+void prefill_global_geometry(int seq_len, int n_global, int batch, int n_q_heads, int* splits,
+                             int* keys_per_split, int* n_wg) {
+  if (n_global <= 0) {
+    *splits = 0;
+    *keys_per_split = 0;
+    *n_wg = 0;
+    return;
+  }
+  // about 512 keys per wave: short per-wave chains, many waves in flight
+  const int kps = 512;
+  const int ks = (seq_len + kps - 1) / kps;
+  const int n_rt = (n_global + 31) / 32;
+  const long long units = (long long)batch * n_q_heads * n_rt * ks;
+  *splits = ks;
+  *keys_per_split = kps;
+  *n_wg = (int)((units + 3) / 4);
+}
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   const bool lg = a.n_global > 0;

@@ -24,7 +24,7 @@ def _header_functions():
 def test_library_exports_every_declared_function():
     lib = api.library()
     declared = _header_functions()
-    assert len(declared) == 8
+    assert len(declared) == 9
     for name in declared:
         assert hasattr(lib, name), name
     assert set(declared) == set(_lib.EXPORTS)
@@ -140,14 +140,33 @@ def test_summaries_reject_bad_ranges():
 
 
 def test_prefill_rejects_bad_arguments():
-    st, _ = _status("bsattn_prefill", _shape(dtype=0), FAKE, FAKE, FAKE, 10, 0, 1, None, 0, FAKE, None, None)
+    P = (FAKE, FAKE, FAKE)
+    st, _ = _status("bsattn_prefill", _shape(dtype=0), *P, 10, 0, 1, None, 0, FAKE, None, None, 0, None)
     assert st == 2  # fp32 prefill is not built
-    st, msg = _status("bsattn_prefill", _shape(), FAKE, FAKE, FAKE, 10, 0, 1, G3(1, 2, 3), 3, FAKE, None, None)
+    st, msg = _status("bsattn_prefill", _shape(), *P, 10, 0, 1, G3(1, 2, 3), 3, FAKE, None, None, 0, None)
     assert st == 2 and "bidirectional" in msg
-    st, _ = _status("bsattn_prefill", _shape(), FAKE, FAKE, FAKE, 10, 0, 2, None, 0, FAKE, None, None)
+    st, _ = _status("bsattn_prefill", _shape(), *P, 10, 0, 2, None, 0, FAKE, None, None, 0, None)
     assert st == 1
-    st, _ = _status("bsattn_prefill", _shape(), FAKE, None, FAKE, 10, 0, 1, None, 0, FAKE, None, None)
+    st, _ = _status("bsattn_prefill", _shape(), FAKE, None, FAKE, 10, 0, 1, None, 0, FAKE, None, None, 0, None)
     assert st == 1
+    # globals need the workspace of the key-split global rows
+    st, msg = _status("bsattn_prefill", _shape(), *P, 8, 8, 0, G3(1, 2, 3), 3, FAKE, None, None, 0, None)
+    assert st == 4 and "workspace" in msg
+    need = api.bsattn_prefill_workspace_bytes(api.make_shape(1, 4, 1, 64, 256), 3)
+    st, _ = _status("bsattn_prefill", _shape(), *P, 8, 8, 0, G3(1, 2, 3), 3, FAKE, None, FAKE + 16, need,
+                    None)
+    assert st == 1  # misaligned workspace
+
+
+def test_prefill_workspace_size():
+    up = lambda x: -(-x // 256) * 256  # noqa: E731
+    s = api.make_shape(2, 12, 12, 64, 16384)
+    # 16 global rows -> one 32-row tile; 16384 keys in ranges of 512 -> 32 splits
+    rows = 2 * 12 * 1 * 32 * 32
+    assert api.bsattn_prefill_workspace_bytes(s, 16) == up(rows * 64 * 4) + up(rows * 8)
+    assert api.bsattn_prefill_workspace_bytes(s, 33) == 2 * up(rows * 64 * 4) + 2 * up(rows * 8)
+    assert api.bsattn_prefill_workspace_bytes(s, 0) == 0
+    assert api.bsattn_prefill_workspace_bytes(s, 257) == 0
 
 
 def test_binding_raises_with_the_library_message():

@@ -38,8 +38,11 @@ def _run(api, w, x, extra_cap=0):
     shape = api.make_shape(B, Hq, Hkv, d, N, kv_capacity=N + extra_cap, dtype="bf16")
     O = torch.full((B, Hq, N, d), float("nan"), device="cuda")
     lse = torch.full((B, Hq, N), float("nan"), device="cuda")
+    nbytes = api.bsattn_prefill_workspace_bytes(shape, len(w.global_pos))
+    # garbage contents: the workspace needs no initialisation
+    ws = torch.full((nbytes,), 255, dtype=torch.uint8, device="cuda") if nbytes else None
     api.bsattn_prefill(shape, Q, K, V, w.window_left, w.window_right, w.causal, list(w.global_pos),
-                       O, lse)
+                       O, lse, ws)
     torch.cuda.synchronize()
     return O.cpu().numpy(), lse.cpu().numpy()
 
@@ -61,6 +64,7 @@ SMALL = [
     (_pw("bidir_asym", 1, 2, 2, 500, 64, 5, 60, False, seed=37), 0),
     (_pw("dense_bidir", 1, 2, 1, 260, 128, -1, -1, False, seed=38), 0),
     (_pw("tiny_seq", 1, 2, 1, 7, 64, 3, 0, True, seed=39), 0),
+    (_pw("lg_short_seq", 1, 2, 1, 100, 128, 8, 8, False, (5, 50, 99), seed=40), 3),
 ]
 
 
