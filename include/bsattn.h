@@ -122,7 +122,8 @@ bsattn_status bsattn_select_topk(const bsattn_shape* shape, const void* Q, const
                                  const int32_t* global_pos_host, int32_t n_global, int32_t* sel,
                                  float* scores, void* hip_stream);
 
-/* Bytes of device workspace bsattn_decode needs for these arguments (0 if invalid). */
+/* Bytes of device workspace bsattn_decode needs for these arguments (0 if invalid, or
+ * when one partial per (b, K/V head) suffices and no workspace is needed). */
 size_t bsattn_decode_workspace_bytes(const bsattn_shape* shape, int32_t top_k, int32_t window,
                                      int32_t n_sink, int32_t n_global);
 
@@ -135,7 +136,7 @@ size_t bsattn_decode_workspace_bytes(const bsattn_shape* shape, int32_t top_k, i
  * bsattn_select_topk (ascending, -1 padded, each entry a complete block).
  * dtype F32 or BF16.  workspace: device memory of at least
  * bsattn_decode_workspace_bytes(...) bytes, 256-byte aligned, holding the
- * split partials; its contents need not be initialised.  lse may be NULL.
+ * split partials; its contents need not be initialised (NULL when that size is 0).  lse may be NULL.
  * Calls that share a workspace must be ordered (same stream); calls with
  * separate workspaces may overlap.
  */

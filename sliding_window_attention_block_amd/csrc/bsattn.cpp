@@ -116,15 +116,16 @@ int forced_block_bound(int32_t n_ctx, int32_t window, int32_t n_sink, int32_t n_
   return fb.r0_n + fb.r1_n + n_global;
 }
 
-// Workspace layout: partial numerators [B*Hq, n_wg, d] | partial (max, sum) [B*Hq, n_wg, 2],
+// Workspace layout: partial numerators [B*Hq, n_part, d] | partial (max, sum) [B*Hq, n_part, 2],
 // each region 256-byte aligned.
 struct WsLayout {
   size_t o_off, ml_off, total;
 };
 WsLayout workspace_layout(const bsattn_shape* s, int n_items) {
-  int ipw, n_wg;
-  bsattn::decode_split_geometry(n_items, &ipw, &n_wg);
-  const size_t rows = (size_t)s->batch * s->n_q_heads * n_wg;
+  int per_wave, n_part;
+  bsattn::decode_split_geometry(n_items, s->batch * s->n_kv_heads, s->head_dim, s->dtype == BSATTN_BF16,
+                                &per_wave, &n_part);
+  const size_t rows = n_part > 1 ? (size_t)s->batch * s->n_q_heads * n_part : 0;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   WsLayout l;
   l.o_off = 0;
@@ -271,11 +272,12 @@ bsattn_status bsattn_decode(const bsattn_shape* shape, const void* Q, const void
   a.fblocks = make_forced_blocks(a.forced);
   a.n_items = top_k + a.fblocks.r0_n + a.fblocks.r1_n + a.fblocks.n_gblk;
   const size_t need = workspace_for(shape, a.n_items);
-  if (workspace == nullptr || ws_bytes < need)
+  if (need > 0 && (workspace == nullptr || ws_bytes < need))
     return fail(BSATTN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return fail(BSATTN_ERR_INVALID, "workspace must be 256-byte aligned");
-  bsattn::decode_split_geometry(a.n_items, &a.items_per_wave, &a.n_wg);
+  bsattn::decode_split_geometry(a.n_items, shape->batch * shape->n_kv_heads, shape->head_dim,
+                                shape->dtype == BSATTN_BF16, &a.per_wave, &a.n_part);
   const WsLayout lay = workspace_layout(shape, a.n_items);
   a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.o_off);
   a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.ml_off);

@@ -11,27 +11,30 @@
 // over disjoint token sets merge exactly after rescaling by 2^(m - M).
 //
 // Work items: per (b, K/V head) the list is the top_k selected blocks, then
-// the forced blocks.  A forced block that is also selected is skipped (the
-// selected block already covers every token of it); a forced block only
-// contributes its forced tokens.
+// the forced blocks (sink range, window range, blocks holding a global token).
 //
-// Grid: (workgroups per pair, B * Hkv).  A workgroup has 4 waves; each wave
-// owns `items_per_wave` consecutive items.  The 4 waves merge in LDS into one
-// partial per workgroup.  With one workgroup per pair the kernel writes O and
-// lse itself; otherwise a small second kernel merges the partials (the kernel
-// boundary makes every workgroup's partial visible without any L2 write-back
-// inside the hot kernel; the L2s of the 8 XCDs are not coherent with each other).
-//
-// bf16 path (MFMA, gfx950 v_mfma_f32_16x16x32_bf16), per 64-token item:
+// bf16 path (MFMA, gfx950 v_mfma_f32_16x16x32_bf16): the unit is a half item
+// (32 tokens of one block).  A selected block contributes its tokens that are
+// not forced, a forced block its forced tokens, so no token is counted twice
+// and no search of `sel` is needed.  Each wave owns a run of half items of one
+// pair and pipelines them two deep (next half item's loads in flight while the
+// current one is computed); waves are independent and write one partial each.
 //   V is copied HBM -> LDS with global_load_lds_dwordx4 (no registers), into
 //   a per-wave tile with XOR-swizzled 16-byte chunks; K goes straight from HBM
-//   into MFMA A-operand registers.  All of an item's loads are issued at once.
+//   into MFMA A-operand registers.
 //   S^T = K Q^T: B = Q^T held in registers (16 query heads of the group, zero
-//   padded), so lane l holds the logits of query head l%16 for 16 tokens.
+//   padded), so lane l holds the logits of query head l%16 for 8 tokens.
 //   O^T += V^T P^T: V^T read with ds_read_b64_tr_b16.  P = P_hi + P_lo in
 //   bf16 (two products), so the result keeps ~2^-17 of P's precision.  The
 //   output tile keeps query head l%16 in lane l, so the rescale is per lane.
-// fp32 path (VALU): one token per lane, used when K/V are fp32.
+// fp32 path (VALU): one token per lane, one item per wave; a forced block that
+// is also selected is skipped there (the selected block covers it); the 4
+// waves of a workgroup merge in LDS into one partial.
+//
+// With one partial per pair the kernel writes O and lse itself; otherwise a
+// small second kernel merges the partials (the kernel boundary makes every
+// partial visible without any L2 write-back inside the hot kernel; the L2s of
+// the 8 XCDs are not coherent with each other).
 #include "launch.hpp"
 
 namespace bsattn {
@@ -109,7 +112,7 @@ struct MergeLds {
 template <int D>
 __device__ __forceinline__ void write_wg_result(const DecodeArgs& a, const MergeLds<D>* ml, int b, int g) {
   const int G = a.n_q_heads / a.n_kv_heads;
-  const int n_wg = a.n_wg, wg = blockIdx.x;
+  const int n_wg = a.n_part, wg = blockIdx.x;
   for (int idx = threadIdx.x; idx < G * D; idx += 64 * kW) {
     const int hh = idx / D, dd = idx % D;
     float M = -INFINITY;
@@ -140,149 +143,274 @@ __device__ __forceinline__ void write_wg_result(const DecodeArgs& a, const Merge
   }
 }
 
-// One wave handles one half of an item (32 tokens): small per-wave footprint (8 KB
-// of V in LDS, K in 32 registers) so 16 waves fit on a CU and keep loads in flight
-// while others compute.  Sub-item s is half s % 2 of item s / 2.
+// bf16 path.  Work unit: a half item (32 tokens of one block) of one
+// (b, K/V head) pair.  Each wave owns `per_wave` consecutive half items of one
+// pair and runs them through a two-stage register pipeline: while it computes
+// one half item, the loads of the next are already in flight.  K is loaded
+// straight into MFMA A-operand registers; V is loaded with coalesced 1 KB
+// instructions into registers and, at compute time, written to the wave's LDS
+// tile and read back transposed.  Only plain vector loads are in flight, so the
+// compiler's own waits are exact.  Waves never wait for each other (no
+// barriers), so the memory system sees a steady stream of requests instead of
+// rounds of workgroups that load, then compute, then retire together.
+//
+// Token set without any search: a selected block contributes its tokens that
+// are not forced; a forced block contributes its forced tokens.  Every token of
+// T is therefore counted exactly once, whatever `sel` holds.
 template <int D>
-__global__ __launch_bounds__(64 * kW, 4) void decode_bf16_kernel(DecodeArgs a) {
-  constexpr int DC = D / 32;              // d chunks per QK MFMA row
-  constexpr int DT = D / 16;              // output d tiles
-  constexpr int TILE = 32 * D * 2;        // V of one half item
-  constexpr int NCH = TILE / 1024;        // 1 KB LDS-DMA instructions per half item
-  constexpr int SEL_OFF = kW * TILE;      // the sel row lives after the V tiles
-  constexpr int LDS = SEL_OFF + kMaxTopK * 4;
-  static_assert(sizeof(MergeLds<D>) <= LDS, "merge buffer overlays the V tiles and sel row");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
-  int32_t* s_sel = reinterpret_cast<int32_t*>(smem + SEL_OFF);
+struct HalfItem {
+  static constexpr int DC = D / 32;        // 32-wide d chunks of the QK product
+  static constexpr int RB = D * 2;         // bytes per token row
+  static constexpr int TILE = 32 * RB;     // V bytes of a half item
+  static constexpr int NCH = TILE / 1024;  // 1 KB V load instructions per half item
+};
 
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int bh = blockIdx.y;
-  const int b = bh / a.n_kv_heads, g = bh % a.n_kv_heads;
+template <int D>
+struct Stage {
+  u32x4 k[2][HalfItem<D>::DC];  // K A-operands: tokens 16tt + h, dims 32dc + 8grp .. +8
+  u32x4 v[HalfItem<D>::NCH];    // V bytes [1024i + 16 lane, +16) of the half item
+  uint32_t hmask;               // tokens of T among the 32 (0: nothing to do)
+};
+
+// Block and 64-token mask of item `it` of a pair.  Mask 0: nothing to do (the
+// block index is then 0, so the loads that are still issued stay in bounds).
+__device__ __forceinline__ void item_entry(const DecodeArgs& a, const int32_t* selrow, int it, int& blk,
+                                           uint64_t& mask) {
+  if (it < a.top_k) {
+    blk = selrow[it];
+    // only complete blocks can be selected; anything else is ignored
+    const bool ok = blk >= 0 && blk < a.forced.n_ctx / kBlock;
+    mask = ok ? ~forced_mask(a.forced, blk) : 0ull;
+  } else if (it < a.n_items) {
+    const int f = it - a.top_k;
+    const ForcedBlocks& fb = a.fblocks;
+    if (f < fb.r0_n) blk = fb.r0_lo + f;
+    else if (f < fb.r0_n + fb.r1_n) blk = fb.r1_lo + (f - fb.r0_n);
+    else blk = fb.gblk[f - fb.r0_n - fb.r1_n];
+    mask = forced_mask(a.forced, blk);
+  } else {
+    mask = 0ull;
+  }
+  if (mask == 0ull) blk = 0;
+}
+
+template <int D>
+__device__ __forceinline__ void load_half(const uint16_t* Kb, const uint16_t* Vb, int tok0, int last,
+                                          Stage<D>& st) {
+  using H = HalfItem<D>;
+  const int lane = threadIdx.x & 63, h = lane & 15, grp = lane >> 4;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const size_t row = (size_t)min(tok0 + 16 * tt + h, last);
+#pragma unroll
+    for (int dc = 0; dc < H::DC; ++dc)
+      st.k[tt][dc] = *reinterpret_cast<const u32x4*>(Kb + row * D + 32 * dc + 8 * grp);
+  }
+#pragma unroll
+  for (int i = 0; i < H::NCH; ++i) {
+    const int off = 1024 * i + 16 * lane;
+    const size_t row = (size_t)min(tok0 + off / H::RB, last);
+    st.v[i] = *reinterpret_cast<const u32x4*>(Vb + row * D + (off % H::RB) / 2);
+  }
+}
+
+// Online-softmax update of one half item whose K and V registers have landed.
+template <int D>
+__device__ __forceinline__ void compute_half(const Stage<D>& st, uint8_t* vt, const u32x4* qop, float sl2,
+                                             float& m_run, float& l_run, f32x4* oacc) {
+  using H = HalfItem<D>;
+  constexpr int DC = H::DC, DT = D / 16;
+  const int lane = threadIdx.x & 63, h = lane & 15, grp = lane >> 4;
+  const uint32_t hmask = st.hmask;
+  // V rows into the wave's LDS tile (chunk c of row r at physical chunk c ^ swz(r))
+#pragma unroll
+  for (int i = 0; i < H::NCH; ++i) {
+    const int off = 1024 * i + 16 * lane;
+    *reinterpret_cast<u32x4*>(vt + v_off<D>(off / H::RB, (off % H::RB) >> 4)) = st.v[i];
+  }
+  // S^T = K Q^T: lane (h, grp) holds head h's logits of tokens 16tt + 4grp + r
+  f32x4 s[2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc) s[tt] = mfma16x16x32(as_bf16x8(st.k[tt][dc]), as_bf16x8(qop[dc]), s[tt]);
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float v = ((hmask >> (16 * tt + 4 * grp + r)) & 1u) ? s[tt][r] : -INFINITY;
+      s[tt][r] = v;
+      mx = fmaxf(mx, v);
+    }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  // the running max moves only when it grows by more than 2^8 (weights stay <= 2^8)
+  const float m_cand = mx * sl2;
+  const bool need = m_cand > m_run + kDecodeHeadroom;
+  if (__ballot(need)) {
+    const float m_new = need ? m_cand : m_run;
+    const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+    l_run *= alpha;
+#pragma unroll
+    for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
+    m_run = m_new;
+  }
+  const float nm = (m_run == -INFINITY) ? 0.f : -m_run;
+  // P = P_hi + P_lo, both bf16: the second PV product (free: decode is bound by
+  // HBM) keeps the result exact to ~2^-17 of P however few tokens a head sees.
+  u32x4 pop, plo;
+  float psum = 0.f;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int r = 0; r < 4; r += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[tt][r], sl2, nm));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[tt][r + 1], sl2, nm));
+      const uint32_t pk = cvt_pk_bf16(p0, p1);
+      pop[2 * tt + r / 2] = pk;
+      plo[2 * tt + r / 2] = cvt_pk_bf16(p0 - bf16lo(pk), p1 - bf16hi(pk));
+      psum += p0 + p1;
+    }
+  l_run += psum;
+  // O^T += V^T P^T.  Lane a of 16-lane group q reads 8 bytes of V row 4q + a/4
+  // (+16 for the second half of the k range), columns 16dt + 4(a%4).
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const int row = 4 * grp + (h >> 2);
+    const int col = 16 * dt + 4 * (h & 3);  // element index
+    const u32x2 lo = lds_read_tr16(vt, v_off<D>(row, col >> 3) + ((col & 7) << 1));
+    const u32x2 hi = lds_read_tr16(vt, v_off<D>(row + 16, col >> 3) + ((col & 7) << 1));
+    const u32x4 vop = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    oacc[dt] = mfma16x16x32(as_bf16x8(vop), as_bf16x8(pop), oacc[dt]);
+    oacc[dt] = mfma16x16x32(as_bf16x8(vop), as_bf16x8(plo), oacc[dt]);
+  }
+}
+
+// d = 128: two stages of K and V take 128 registers, so a wave gets the whole
+// 512-register budget of a SIMD (one workgroup of 4 waves per CU); d = 64 fits
+// two workgroups per CU.
+template <int D>
+__global__ __launch_bounds__(64 * kW, D == 128 ? 1 : 2) void decode_bf16_kernel(DecodeArgs a) {
+  using H = HalfItem<D>;
+  constexpr int DC = H::DC, DT = D / 16;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kW * H::TILE];
+
+  const int lane = threadIdx.x & 63;
+  // wave-uniform (scalar registers): every item index, block and mask below is too
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gw = blockIdx.x * kW + wid;  // global wave index
+  const int n_pairs = a.batch * a.n_kv_heads;
+  const int pair = gw / a.n_part, wi = gw % a.n_part;
+  if (pair >= n_pairs) return;  // no barriers below: waves are independent
+  const int b = pair / a.n_kv_heads, g = pair % a.n_kv_heads;
   const int G = a.n_q_heads / a.n_kv_heads;
   const int h = lane & 15, grp = lane >> 4;
-  uint8_t* vt = smem + wid * TILE;
-  typedef __attribute__((address_space(3))) void lds_void;
+  uint8_t* const vt = smem + wid * H::TILE;
 
-  const uint16_t* Kb = reinterpret_cast<const uint16_t*>(a.K) + (size_t)bh * a.kv_capacity * D;
-  const uint16_t* Vb = reinterpret_cast<const uint16_t*>(a.V) + (size_t)bh * a.kv_capacity * D;
-  // the pair's selected blocks, staged once in LDS (every search below reads LDS)
-  for (int i = threadIdx.x; i < a.top_k; i += 64 * kW) s_sel[i] = a.sel[(size_t)bh * a.top_k + i];
-  __syncthreads();
-  const int nsel = valid_prefix(s_sel, a.top_k);
-
-  const float sl2 = a.scale * kLog2e;
+  const uint16_t* Kb = reinterpret_cast<const uint16_t*>(a.K) + (size_t)pair * a.kv_capacity * D;
+  const uint16_t* Vb = reinterpret_cast<const uint16_t*>(a.V) + (size_t)pair * a.kv_capacity * D;
   const int last = a.forced.n_ctx - 1;  // rows past the context (tail block) are masked; clamp loads
+  const float sl2 = a.scale * kLog2e;
+  const int s0 = wi * a.per_wave;
+  const int s1 = min(s0 + a.per_wave, 2 * a.n_items);
+  const int it0 = s0 >> 1;
+
+  // Item table of this wave, one item per lane (at most 64 items per wave):
+  // lane j holds the block and token mask of item it0 + j.
+  int blkv;
+  uint64_t maskv;
+  item_entry(a, a.sel + (size_t)pair * a.top_k, it0 + lane, blkv, maskv);
+  const uint32_t mlo = (uint32_t)maskv, mhi = (uint32_t)(maskv >> 32);
+
+  // Q^T operand: lane (h, grp) holds Q[h][32dc + 8grp .. +8] (zero rows past G)
+  u32x4 qop[DC];
+  {
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.Q) + ((size_t)b * a.n_q_heads + g * G + h) * D;
+#pragma unroll
+    for (int dc = 0; dc < DC; ++dc)
+      qop[dc] = h < G ? *reinterpret_cast<const u32x4*>(qrow + 32 * dc + 8 * grp) : u32x4{0u, 0u, 0u, 0u};
+  }
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 oacc[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int s0 = (blockIdx.x * kW + wid) * a.items_per_wave;
-  const int s1 = min(s0 + a.items_per_wave, 2 * a.n_items);
-  for (int sub = s0; sub < s1; ++sub) {
-    const ItemInfo inf = item_info(a, s_sel, nsel, sub >> 1);
-    const int half = sub & 1;
-    const uint32_t hmask = (uint32_t)(inf.mask >> (32 * half));
-    if (inf.blk < 0 || hmask == 0u) continue;  // same value in every lane
-    const int tok0 = inf.blk * kBlock + 32 * half;
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // previous V reads done
-    // V: HBM -> LDS.  Instruction k fills tile bytes [1024k, 1024k + 1024); lane l's
-    // 16 bytes land at 1024k + 16l, i.e. physical chunk pc of row r, which holds
-    // logical chunk pc ^ swz(r).
-#pragma unroll
-    for (int k = 0; k < NCH; ++k) {
-      const int off = 1024 * k + 16 * lane;
-      const int r = off / (D * 2), pc = (off % (D * 2)) >> 4;
-      const int c = pc ^ v_swz<D>(r);
-      const size_t row = (size_t)min(tok0 + r, last);
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(Vb + row * D + c * 8),
-                                       (lds_void*)(vt + 1024 * k), 16, 0, 0);
+  // Two stages in flight over half items s0 .. s1-1 (stage A: even steps, B:
+  // odd).  Loads are issued for every half item (an empty one loads block 0
+  // and skips the compute), and every path is written out, so the compiler's
+  // waits on the stage registers count exactly the loads issued after them.
+  Stage<D> A, B;
+  auto load = [&](int s, Stage<D>& st) {
+    const int j = (s >> 1) - it0;
+    const int blk = __builtin_amdgcn_readlane(blkv, j);
+    st.hmask = (s & 1) ? __builtin_amdgcn_readlane(mhi, j) : __builtin_amdgcn_readlane(mlo, j);
+    load_half<D>(Kb, Vb, blk * kBlock + 32 * (s & 1), last, st);
+  };
+  auto comp = [&](const Stage<D>& st) {
+    if (st.hmask) compute_half<D>(st, vt, qop, sl2, m_run, l_run, oacc);
+  };
+
+  const int n = s1 - s0;
+  if (n >= 4) {
+    load(s0, A);
+    load(s0 + 1, B);
+    int s = s0;
+    for (; s + 3 < s1; s += 2) {
+      comp(A);
+      load(s + 2, A);
+      comp(B);
+      load(s + 3, B);
     }
-    // K operands straight from HBM
-    u32x4 kop[2][DC];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const size_t row = (size_t)min(tok0 + 16 * tt + h, last);
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc)
-        kop[tt][dc] = *reinterpret_cast<const u32x4*>(Kb + row * D + 32 * dc + 8 * grp);
+    if (s + 2 < s1) {  // three left: s (A), s + 1 (B), s + 2
+      comp(A);
+      load(s + 2, A);
+      comp(B);
+      comp(A);
+    } else {  // two left
+      comp(A);
+      comp(B);
     }
-    // Q^T operand: lane (h, grp) holds Q[h][32*dc + 8*grp .. +8] (reloaded per sub-item:
-    // an L2 hit, and it keeps 16 registers free across the loop)
-    u32x4 qop[DC];
-    {
-      const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.Q) + ((size_t)b * a.n_q_heads + g * G + h) * D;
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc)
-        qop[dc] = h < G ? *reinterpret_cast<const u32x4*>(qrow + 32 * dc + 8 * grp) : u32x4{0u, 0u, 0u, 0u};
-    }
-    // logits
-    f32x4 s[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int dc = 0; dc < DC; ++dc) s[tt] = mfma16x16x32(as_bf16x8(kop[tt][dc]), as_bf16x8(qop[dc]), s[tt]);
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tok = 16 * tt + 4 * grp + r;
-        const float v = ((hmask >> tok) & 1u) ? s[tt][r] * sl2 : -INFINITY;
-        s[tt][r] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
-    // P = P_hi + P_lo, both bf16: the second PV product (free: decode is bound by
-    // HBM) keeps the result exact to ~2^-17 of P however few tokens a head sees.
-    u32x4 pop, plo;
-    float psum = 0.f;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int r = 0; r < 4; r += 2) {
-        const float p0 = exp2f(s[tt][r] - m_use), p1 = exp2f(s[tt][r + 1] - m_use);
-        const uint32_t pk = pack_bf16x2(p0, p1);
-        pop[2 * tt + r / 2] = pk;
-        plo[2 * tt + r / 2] = pack_bf16x2(p0 - bf16lo(pk), p1 - bf16hi(pk));
-        psum += p0 + p1;
-      }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int t = 0; t < DT; ++t) oacc[t] *= alpha;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // V tile landed in LDS
-    // O^T += V^T P^T.  Lane a of 16-lane group q reads 8 bytes of V row 4q + a/4
-    // (+16 for the second half of the k range), columns 16dt + 4(a%4).
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int row = 4 * grp + (h >> 2);
-      const int col = 16 * dt + 4 * (h & 3);  // element index
-      const u32x2 lo = lds_read_tr16(vt, v_off<D>(row, col >> 3) + ((col & 7) << 1));
-      const u32x2 hi = lds_read_tr16(vt, v_off<D>(row + 16, col >> 3) + ((col & 7) << 1));
-      const u32x4 vop = u32x4{lo[0], lo[1], hi[0], hi[1]};
-      oacc[dt] = mfma16x16x32(as_bf16x8(vop), as_bf16x8(pop), oacc[dt]);
-      oacc[dt] = mfma16x16x32(as_bf16x8(vop), as_bf16x8(plo), oacc[dt]);
-    }
+  } else if (n == 3) {
+    load(s0, A);
+    load(s0 + 1, B);
+    comp(A);
+    load(s0 + 2, A);
+    comp(B);
+    comp(A);
+  } else if (n == 2) {
+    load(s0, A);
+    load(s0 + 1, B);
+    comp(A);
+    comp(B);
+  } else if (n == 1) {
+    load(s0, A);
+    comp(A);
   }
+
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-  __syncthreads();  // every wave done with its V tile and the sel row
-  MergeLds<D>* ml = reinterpret_cast<MergeLds<D>*>(smem);
-  if (grp == 0) {
-    ml->m[wid][h] = m_run;
-    ml->l[wid][h] = l_run;
-  }
+  if (h >= G) return;
+  // lane (h, grp) holds O[h][16dt + 4grp .. +4]
+  const size_t qrow = (size_t)b * a.n_q_heads + g * G + h;
+  if (a.n_part == 1) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(&ml->o[wid][h][16 * dt + 4 * grp]) = oacc[dt];
-  __syncthreads();
-  write_wg_result<D>(a, ml, b, g);
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<f32x4*>(a.O + qrow * D + 16 * dt + 4 * grp) = oacc[dt] * inv;
+    if (a.lse != nullptr && grp == 0) a.lse[qrow] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+  } else {
+    const size_t prow = qrow * a.n_part + wi;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<f32x4*>(a.part_o + prow * D + 16 * dt + 4 * grp) = oacc[dt];
+    if (grp == 0) {
+      a.part_ml[2 * prow] = m_run;
+      a.part_ml[2 * prow + 1] = l_run;
+    }
+  }
 }
 
 // fp32 K/V: one token per lane, VALU dot products.  GM >= G is the padded group size.
@@ -314,8 +442,8 @@ __global__ __launch_bounds__(64 * kW) void decode_f32_kernel(DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < DL; ++e) o[hh][e] = 0.f;
   }
-  const int it0 = (blockIdx.x * kW + wid) * a.items_per_wave;
-  const int it1 = min(it0 + a.items_per_wave, a.n_items);
+  const int it0 = (blockIdx.x * kW + wid) * a.per_wave;
+  const int it1 = min(it0 + a.per_wave, a.n_items);
   for (int it = it0; it < it1; ++it) {
     const ItemInfo inf = item_info(a, s_sel, nsel, it);
     if (inf.blk < 0) continue;
@@ -375,67 +503,103 @@ __global__ __launch_bounds__(64 * kW) void decode_f32_kernel(DecodeArgs a) {
   write_wg_result<D>(a, ml, b, g);
 }
 
-// Merge the workgroup partials of every query head: per dim,
+// Merge the partials of every query head: per dim,
 // O = sum_s w_s o_s / sum_s w_s l_s with w_s = 2^(m_s - M); lse = ln 2 (M + log2 L).
-// One workgroup of D threads per (b, query head); 8 partial loads in flight per thread.
+// One wave per (b, query head); lane owns dims lane + 64e; the partials are read
+// 32 at a time (all loads of a chunk in flight together) and folded online.
 template <int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
+  constexpr int DL = D / 64, CH = 32;
   const size_t qrow = blockIdx.x;  // b * Hq + h
-  const int dd = threadIdx.x;
-  const int n_wg = a.n_wg;
-  const float* pml = a.part_ml + qrow * n_wg * 2;
-  const float* po = a.part_o + qrow * n_wg * D + dd;
-  float M = -INFINITY, L = 0.f, O = 0.f;
-  for (int s0 = 0; s0 < n_wg; s0 += 8) {
-    float ms[8], ls[8], os[8];
+  const int lane = threadIdx.x;
+  const int n = a.n_part;
+  const float* pml = a.part_ml + qrow * n * 2;
+  const float* po = a.part_o + qrow * n * D + lane;
+  float M = -INFINITY, L = 0.f, O[DL];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int s = s0 + u;
-      ms[u] = s < n_wg ? pml[2 * s] : -INFINITY;
-      ls[u] = s < n_wg ? pml[2 * s + 1] : 0.f;
-      os[u] = s < n_wg ? po[(size_t)s * D] : 0.f;
-    }
+  for (int e = 0; e < DL; ++e) O[e] = 0.f;
+  for (int j0 = 0; j0 < n; j0 += CH) {
+    float ms[CH], ls[CH], os[CH][DL];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (ms[u] == -INFINITY) continue;
-      const float Mn = fmaxf(M, ms[u]);
-      const float c0 = exp2f(M - Mn), c1 = exp2f(ms[u] - Mn);
-      L = L * c0 + ls[u] * c1;
-      O = O * c0 + os[u] * c1;
-      M = Mn;
+    for (int u = 0; u < CH; ++u) {
+      const int j = min(j0 + u, n - 1);
+      ms[u] = j0 + u < n ? pml[2 * j] : -INFINITY;
+      ls[u] = pml[2 * j + 1];
+#pragma unroll
+      for (int e = 0; e < DL; ++e) os[u][e] = po[(size_t)j * D + 64 * e];
     }
+    float cm = M;
+#pragma unroll
+    for (int u = 0; u < CH; ++u) cm = fmaxf(cm, ms[u]);
+    if (cm == -INFINITY) continue;
+    const float c0 = M == -INFINITY ? 0.f : exp2f(M - cm);
+    L *= c0;
+#pragma unroll
+    for (int e = 0; e < DL; ++e) O[e] *= c0;
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const float w = ms[u] == -INFINITY ? 0.f : exp2f(ms[u] - cm);
+      L = fmaf(w, ls[u], L);
+#pragma unroll
+      for (int e = 0; e < DL; ++e) O[e] = fmaf(w, os[u][e], O[e]);
+    }
+    M = cm;
   }
-  a.O[qrow * D + dd] = L > 0.f ? O / L : 0.f;
-  if (a.lse != nullptr && dd == 0) a.lse[qrow] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+  for (int e = 0; e < DL; ++e) a.O[qrow * D + lane + 64 * e] = O[e] * inv;
+  if (a.lse != nullptr && lane == 0) a.lse[qrow] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
 template <int D>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
-  dim3 grid(a.n_wg, a.batch * a.n_kv_heads);
+  const int n_pairs = a.batch * a.n_kv_heads;
   const int G = a.n_q_heads / a.n_kv_heads;
-  if (a.bf16)
-    hipLaunchKernelGGL((decode_bf16_kernel<D>), grid, dim3(64 * kW), 0, stream, a);
-  else if (G <= 4)
-    hipLaunchKernelGGL((decode_f32_kernel<D, 4>), grid, dim3(64 * kW), 0, stream, a);
-  else if (G <= 8)
-    hipLaunchKernelGGL((decode_f32_kernel<D, 8>), grid, dim3(64 * kW), 0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_f32_kernel<D, 16>), grid, dim3(64 * kW), 0, stream, a);
+  if (a.bf16) {
+    const long long waves = (long long)n_pairs * a.n_part;
+    hipLaunchKernelGGL((decode_bf16_kernel<D>), dim3((unsigned)((waves + kW - 1) / kW)), dim3(64 * kW), 0,
+                       stream, a);
+  } else {
+    const dim3 grid(a.n_part, n_pairs);
+    if (G <= 4)
+      hipLaunchKernelGGL((decode_f32_kernel<D, 4>), grid, dim3(64 * kW), 0, stream, a);
+    else if (G <= 8)
+      hipLaunchKernelGGL((decode_f32_kernel<D, 8>), grid, dim3(64 * kW), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_f32_kernel<D, 16>), grid, dim3(64 * kW), 0, stream, a);
+  }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.n_wg == 1) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.batch * a.n_q_heads), dim3(D), 0, stream, a);
+  if (e != hipSuccess || a.n_part == 1) return e;
+  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.batch * a.n_q_heads), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// bf16: a wave takes `items_per_wave` half items (32 tokens each); fp32: whole items.
-// One geometry serves both, sized for the finer bf16 split.
-void decode_split_geometry(int n_items, int* items_per_wave, int* n_wg) {
-  const int ipw = 1;
-  *items_per_wave = ipw;
-  const int per_wg = ipw * kW;
-  *n_wg = n_items > 0 ? (2 * n_items + per_wg - 1) / per_wg : 1;
+// bf16: each wave takes `per_wave` consecutive half items (32 tokens) of one
+// pair, with as few half items per wave as keeps every wave resident at once
+// (decode_slots(d) waves).  fp32: one whole item per wave, 4 waves per
+// workgroup merged in LDS, one partial per workgroup.
+void decode_split_geometry(int n_items, int n_pairs, int head_dim, bool bf16, int* per_wave, int* n_part) {
+  const int slots = decode_slots(head_dim);
+  if (n_items <= 0 || n_pairs <= 0) {
+    *per_wave = 1;
+    *n_part = 1;
+    return;
+  }
+  if (!bf16) {
+    *per_wave = 1;
+    *n_part = (n_items + kW - 1) / kW;
+    return;
+  }
+  const long long n_sub = 2LL * n_items;
+  long long c = (n_pairs * n_sub + slots - 1) / slots;
+  if (c < 1) c = 1;
+  while (c < n_sub && (long long)n_pairs * ((n_sub + c - 1) / c) > slots) ++c;
+  // a wave's items must fit one per lane: 126 half items span at most 64 items
+  if (c > 126) c = 126;
+  *per_wave = (int)c;
+  *n_part = (int)((n_sub + c - 1) / c);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {

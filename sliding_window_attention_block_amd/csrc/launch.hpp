@@ -59,23 +59,26 @@ struct DecodeArgs {
   const int32_t* sel;
   float* O;
   float* lse;
-  float* part_o;      // [B*Hq, n_wg, d]  per-workgroup partial numerators
-  float* part_ml;     // [B*Hq, n_wg, 2]  per-workgroup (max, normaliser), log2 domain
+  float* part_o;      // [B*Hq, n_part, d]  partial numerators
+  float* part_ml;     // [B*Hq, n_part, 2]  partial (max, normaliser), log2 domain
   int32_t batch, n_q_heads, n_kv_heads, head_dim;
   int32_t kv_capacity;
   int32_t top_k;
   int32_t n_items;        // top_k + forced blocks
-  int32_t items_per_wave;
-  int32_t n_wg;           // workgroups per (b, K/V head)
+  int32_t per_wave;       // work units per wave (bf16: half items; fp32: items)
+  int32_t n_part;         // partials per (b, K/V head): bf16 waves, fp32 workgroups
   float scale;
   bool bf16;
   ForcedSet forced;
   ForcedBlocks fblocks;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
-// Split geometry the decode launch uses for a given item count (also sizes the workspace).
-void decode_split_geometry(int n_items, int* items_per_wave, int* n_wg);
+// Split geometry the decode launch uses (also sizes the workspace).
+void decode_split_geometry(int n_items, int n_pairs, int head_dim, bool bf16, int* per_wave, int* n_part);
 constexpr int kDecodeWaves = 4;  // waves per decode workgroup
+// bf16 decode waves resident at once on 256 CUs: 4 per CU at d = 128, 8 at d = 64
+constexpr int decode_slots(int head_dim) { return head_dim == 128 ? 1024 : 2048; }
+constexpr float kDecodeHeadroom = 8.f;  // log2 units a running max may lag the true max
 
 struct PrefillArgs {
   const void* Q;

@@ -60,11 +60,6 @@ struct RowState {
   float l;  // normaliser relative to m (partial per lane; lanes l, l^32 sum)
 };
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
-}
 
 // Copy rows [0, 64) of a K/V stage into LDS tiles with 1 KB DMA instructions.
 // `row_pos(r)` is the token position of tile row r (already clamped into range).
