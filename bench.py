@@ -10,8 +10,10 @@ reported separately, as are the COBS 128K decode step and the two prefills.
 
 Every timed loop cycles through R device-resident replicas of its inputs so the
 reuse distance exceeds the 256 MB Infinity Cache: each step reads HBM, not
-cache.  Kernel durations come from HIP events on the stream the library
-launches on (torch's current stream).
+cache.  Decode steps are timed as one captured HIP graph of K steps (the step
+is a few short kernels; launching them one at a time from Python would time the
+host); warmup is W eager steps plus one untimed replay.  Durations come from
+HIP events on the stream the library launches on (torch's current stream).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME] [--no-cpu-baseline]
 """
@@ -82,7 +84,7 @@ def to_dev(torch, a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def bench_decode(api, torch, w, x, steps, warmup, with_events=True):
+def bench_decode(api, torch, w, x, steps, warmup):
     B, Hq, Hkv, d, n, S = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_ctx, w.block_size
     nb = n // S
     shape = api.make_shape(B, Hq, Hkv, d, n, dtype=w.dtype)
@@ -137,41 +139,57 @@ def bench_decode(api, torch, w, x, steps, warmup, with_events=True):
     kv_bytes = tokens * d * 2 * elem
     io_bytes = B * Hq * d * elem + B * Hq * (d + 1) * 4 + B * Hkv * w.top_k * 4  # Q in, O + lse out, sel
     sel_bytes = summ_bytes + B * Hq * d * elem + B * Hkv * w.top_k * 4
-    # timed steps
-    ev_sel = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    ev_dec = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+
+    # The timed steps run as one HIP graph of `steps` steps (replica i % R at step i):
+    # a decode step is a handful of short kernels, and launching them one by one
+    # from Python would time the host, not the GPU.  Separate graphs of the select
+    # calls alone and the decode calls alone give the per-phase launch times.
+    def capture(fns):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                for f in fns:
+                    f(reps[i % R])
+        return g
+
+    def timed_replay(g):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps, (time.perf_counter() - t0) * 1e3 / steps
+
+    g_step, g_sel, g_dec = capture((select, decode)), capture((select,)), capture((decode,))
+    g_step.replay()  # untimed: the first replay of a graph uploads it
+    torch.cuda.synchronize()
+    ms_step, wall_step = timed_replay(g_step)
+    sel_ms, _ = timed_replay(g_sel)
+    dec_ms, _ = timed_replay(g_dec)
+    del g_step, g_sel, g_dec
+    # the same steps launched one call at a time from Python (context only)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        rp = reps[i % R]
-        if with_events:
-            ev_sel[i][0].record()
-        select(rp)
-        if with_events:
-            ev_sel[i][1].record()
-            ev_dec[i][0].record()
-        decode(rp)
-        if with_events:
-            ev_dec[i][1].record()
+        select(reps[i % R])
+        decode(reps[i % R])
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / steps
-    sel_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_sel])) if with_events else None
-    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_dec])) if with_events else None
+    eager_ms = (time.perf_counter() - t0) * 1e3 / steps
     res = dict(
-        workload=w.name, ms_per_step=ms_step, tokens_per_s=B / (ms_step * 1e-3),
-        replicas=R, attended_tokens=tokens, gathered_kv_bytes=kv_bytes,
+        workload=w.name, ms_per_step=ms_step, wall_ms_per_step=wall_step, tokens_per_s=B / (ms_step * 1e-3),
+        eager_ms_per_step=eager_ms, replicas=R, attended_tokens=tokens, gathered_kv_bytes=kv_bytes,
         select_ms=sel_ms, decode_ms=dec_ms,
         select_bytes=sel_bytes, decode_bytes=kv_bytes + io_bytes,
         summary_build_ms=float(np.median(build_ms)),
         summary_build_bytes=B * Hkv * nb * S * d * elem + summ_bytes,
     )
-    if with_events:
-        res["gathered_kv_GBps"] = kv_bytes / (dec_ms * 1e-3) / 1e9
-        res["gathered_kv_frac_hbm"] = res["gathered_kv_GBps"] * 1e9 / HBM_PEAK
-        res["decode_GBps"] = (kv_bytes + io_bytes) / (dec_ms * 1e-3) / 1e9
-        res["select_GBps"] = sel_bytes / (sel_ms * 1e-3) / 1e9
-        res["step_GBps"] = (kv_bytes + io_bytes + sel_bytes) / (ms_step * 1e-3) / 1e9
+    res["gathered_kv_GBps"] = kv_bytes / (dec_ms * 1e-3) / 1e9
+    res["gathered_kv_frac_hbm"] = res["gathered_kv_GBps"] * 1e9 / HBM_PEAK
+    res["decode_GBps"] = (kv_bytes + io_bytes) / (dec_ms * 1e-3) / 1e9
+    res["select_GBps"] = sel_bytes / (sel_ms * 1e-3) / 1e9
+    res["step_GBps"] = (kv_bytes + io_bytes + sel_bytes) / (ms_step * 1e-3) / 1e9
     del reps
     torch.cuda.empty_cache()
     return res

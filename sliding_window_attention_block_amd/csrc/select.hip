@@ -8,9 +8,10 @@
 // Candidates are complete blocks with a token outside the forced set (sinks,
 // window, global tokens).
 //
-// Scoring streams every summary once: 16 lanes share one block, each lane
-// owning d/16 consecutive dims of every query head in registers, so each
-// summary row is read with coalesced 16-byte loads.  All of a block's rows
+// Scoring streams every summary once: 16 lanes (one DPP row) share one block,
+// lane l owning the 4-dim chunks l, 16 + l, ... of every query head in
+// registers, so each load instruction reads 256 contiguous bytes of a summary
+// row; the 16 partial dot products are summed with DPP row rotations.  All of a block's rows
 // (mean and up to 8 factor rows) are loaded before any arithmetic, so a wave
 // waits on HBM once per block rather than once per row.
 //
@@ -24,9 +25,19 @@
 namespace bsattn {
 namespace {
 
+// Sum over the 16 lanes of a DPP row (row_ror 8, 4, 2, 1): every lane gets the total.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x122, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x121, 0xf, 0xf, false));
+  return x;
+}
+
 template <int D, int GM, int RM, bool BF16>
 __global__ __launch_bounds__(256) void select_scores_kernel(SelectArgs a) {
-  constexpr int SL = D / 16;               // dims per lane
+  constexpr int SL = D / 16;               // dims per lane: 4-dim chunks sub, 16 + sub, ...
+  constexpr int NC = SL / 4;               // 16-byte chunks per lane per row
   constexpr int PB = RM == 0 ? 4 : (RM <= 4 ? 2 : 1);  // blocks per slot, loaded together
   constexpr int BPW = 16 * PB;             // blocks per workgroup
   const int tid = threadIdx.x;
@@ -35,44 +46,30 @@ __global__ __launch_bounds__(256) void select_scores_kernel(SelectArgs a) {
   const int b = bh / a.n_kv_heads, g = bh % a.n_kv_heads;
   const int G = a.n_q_heads / a.n_kv_heads;
 
+  // lane `sub` owns dims 4(16c + sub) .. +4 for c < NC: each 16-lane row reads
+  // 256 contiguous bytes of a summary row per instruction
   float q[GM][SL];
 #pragma unroll
   for (int h = 0; h < GM; ++h) {
-    const size_t off = ((size_t)b * a.n_q_heads + g * G + h) * D + sub * SL;
-    if (h < G) {
-      if constexpr (BF16) {
-        // SL bf16 values = SL * 2 bytes, 16-byte aligned (SL is 4 or 8)
-        const uint16_t* src = reinterpret_cast<const uint16_t*>(a.Q) + off;
+    const size_t off = ((size_t)b * a.n_q_heads + g * G + h) * D;
 #pragma unroll
-        for (int c = 0; c < SL / 8 + (SL % 8 ? 1 : 0); ++c) {
-          if constexpr (SL >= 8) {
-            const u32x4 v = *reinterpret_cast<const u32x4*>(src + 8 * c);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              q[h][8 * c + 2 * t] = bf16lo(v[t]) * a.scale;
-              q[h][8 * c + 2 * t + 1] = bf16hi(v[t]) * a.scale;
-            }
-          } else {
-            const u32x2 v = *reinterpret_cast<const u32x2*>(src);
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-              q[h][2 * t] = bf16lo(v[t]) * a.scale;
-              q[h][2 * t + 1] = bf16hi(v[t]) * a.scale;
-            }
-          }
-        }
-      } else {
-        const float4* src = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.Q) + off);
-#pragma unroll
-        for (int c = 0; c < SL / 4; ++c) {
-          const float4 v = src[c];
+    for (int c = 0; c < NC; ++c) {
+      const int d0 = 4 * (16 * c + sub);
+      if (h < G) {
+        if constexpr (BF16) {
+          const u32x2 v = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(a.Q) + off + d0);
+          q[h][4 * c] = bf16lo(v[0]) * a.scale;
+          q[h][4 * c + 1] = bf16hi(v[0]) * a.scale;
+          q[h][4 * c + 2] = bf16lo(v[1]) * a.scale;
+          q[h][4 * c + 3] = bf16hi(v[1]) * a.scale;
+        } else {
+          const float4 v = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.Q) + off + d0);
           q[h][4 * c] = v.x * a.scale; q[h][4 * c + 1] = v.y * a.scale;
           q[h][4 * c + 2] = v.z * a.scale; q[h][4 * c + 3] = v.w * a.scale;
         }
+      } else {
+        q[h][4 * c] = q[h][4 * c + 1] = q[h][4 * c + 2] = q[h][4 * c + 3] = 0.f;
       }
-    } else {
-#pragma unroll
-      for (int e = 0; e < SL; ++e) q[h][e] = 0.f;
     }
   }
 
@@ -85,19 +82,19 @@ __global__ __launch_bounds__(256) void select_scores_kernel(SelectArgs a) {
     jj[p] = j;
     const int jc = min(j, a.n_blocks - 1);
     const size_t row = (size_t)bh * a.nblk_capacity + jc;
-    const float4* src = reinterpret_cast<const float4*>(a.mean + row * D + sub * SL);
+    const float4* src = reinterpret_cast<const float4*>(a.mean + row * D) + sub;
 #pragma unroll
-    for (int c = 0; c < SL / 4; ++c) {
-      const float4 v = src[c];
+    for (int c = 0; c < NC; ++c) {
+      const float4 v = src[16 * c];
       vec[p][0][4 * c] = v.x; vec[p][0][4 * c + 1] = v.y; vec[p][0][4 * c + 2] = v.z; vec[p][0][4 * c + 3] = v.w;
     }
 #pragma unroll
     for (int i = 0; i < RM; ++i) {
       if (i < a.rank) {
-        const float4* fs = reinterpret_cast<const float4*>(a.factor + (row * a.rank + i) * D + sub * SL);
+        const float4* fs = reinterpret_cast<const float4*>(a.factor + (row * a.rank + i) * D) + sub;
 #pragma unroll
-        for (int c = 0; c < SL / 4; ++c) {
-          const float4 v = fs[c];
+        for (int c = 0; c < NC; ++c) {
+          const float4 v = fs[16 * c];
           vec[p][1 + i][4 * c] = v.x; vec[p][1 + i][4 * c + 1] = v.y;
           vec[p][1 + i][4 * c + 2] = v.z; vec[p][1 + i][4 * c + 3] = v.w;
         }
@@ -116,9 +113,7 @@ __global__ __launch_bounds__(256) void select_scores_kernel(SelectArgs a) {
       s[h] = acc;
     }
 #pragma unroll
-    for (int o = 8; o > 0; o >>= 1)
-#pragma unroll
-      for (int h = 0; h < GM; ++h) s[h] += __shfl_xor(s[h], o);
+    for (int h = 0; h < GM; ++h) s[h] = row16_sum(s[h]);
 #pragma unroll
     for (int i = 0; i < RM; ++i) {
       if (i < a.rank) {
@@ -131,9 +126,7 @@ __global__ __launch_bounds__(256) void select_scores_kernel(SelectArgs a) {
           pr[h] = acc;
         }
 #pragma unroll
-        for (int o = 8; o > 0; o >>= 1)
-#pragma unroll
-          for (int h = 0; h < GM; ++h) pr[h] += __shfl_xor(pr[h], o);
+        for (int h = 0; h < GM; ++h) pr[h] = row16_sum(pr[h]);
 #pragma unroll
         for (int h = 0; h < GM; ++h) s[h] = fmaf(0.5f * pr[h], pr[h], s[h]);
       }
@@ -146,8 +139,9 @@ __global__ __launch_bounds__(256) void select_scores_kernel(SelectArgs a) {
       float sum = 0.f;
 #pragma unroll
       for (int h = 0; h < GM; ++h)
-        if (h < G) sum += expf(s[h] - mx);
-      a.scores[(size_t)bh * a.nblk_capacity + jj[p]] = mx + logf(sum);
+        if (h < G) sum += __builtin_amdgcn_exp2f((s[h] - mx) * kLog2e);
+      // sum >= 1 (the max term is exactly 1): log2 needs no range care
+      a.scores[(size_t)bh * a.nblk_capacity + jj[p]] = fmaf(__builtin_amdgcn_logf(sum), kLn2, mx);
     }
   }
 }
