@@ -39,6 +39,9 @@ struct SelectArgs {
   float scale;
   bool bf16;
   ForcedSet forced;
+  // scoring split, set by the launcher: each wave scores `per_wave` units (of
+  // 4 * PB blocks) of one pair; `n_part` waves per pair
+  int32_t per_wave, n_part;
 };
 hipError_t launch_select_topk(const SelectArgs& a, hipStream_t stream);
 

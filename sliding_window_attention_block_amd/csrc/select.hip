@@ -11,7 +11,10 @@
 // Scoring streams every summary once: 16 lanes (one DPP row) share one block,
 // lane l owning the 4-dim chunks l, 16 + l, ... of every query head in
 // registers, so each load instruction reads 256 contiguous bytes of a summary
-// row; the 16 partial dot products are summed with DPP row rotations.  All of a block's rows
+// row; the 16 partial dot products are summed with DPP row rotations.  Each
+// wave scores a run of blocks of one (b, K/V head) pair with the next group's
+// loads in flight while it computes the current one, and waves never wait for
+// each other, so the loads stream without load-then-compute rounds.  All of a block's rows
 // (mean and up to 8 factor rows) are loaded before any arithmetic, so a wave
 // waits on HBM once per block rather than once per row.
 //
@@ -34,17 +37,29 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
-template <int D, int GM, int RM, bool BF16>
-__global__ __launch_bounds__(256) void select_scores_kernel(SelectArgs a) {
-  constexpr int SL = D / 16;               // dims per lane: 4-dim chunks sub, 16 + sub, ...
-  constexpr int NC = SL / 4;               // 16-byte chunks per lane per row
-  constexpr int PB = RM == 0 ? 4 : (RM <= 4 ? 2 : 1);  // blocks per slot, loaded together
-  constexpr int BPW = 16 * PB;             // blocks per workgroup
-  const int tid = threadIdx.x;
-  const int sub = tid & 15, slot = tid >> 4;
-  const int bh = blockIdx.y;
-  const int b = bh / a.n_kv_heads, g = bh % a.n_kv_heads;
+// Scoring waves: 2 per SIMD when a lane's query values and its two stages of
+// summary rows take at most 160 registers, else 1 (the whole 512-register budget).
+constexpr bool scores_heavy(int GM, int RM, int PB, int D) {
+  return GM * (D / 16) + 2 * PB * (1 + RM) * (D / 16) > 160;
+}
+
+template <int D, int GM, int RM, int PB, bool BF16>
+__global__ __launch_bounds__(256, scores_heavy(GM, RM, PB, D) ? 1 : 2) void select_scores_kernel(SelectArgs a) {
+  constexpr int SL = D / 16;  // dims per lane: 4-dim chunks sub, 16 + sub, ...
+  constexpr int NC = SL / 4;  // 16-byte chunks per lane per row
+  constexpr int R = 1 + RM;   // rows per block: mean, then factor rows
+  constexpr int UB = 4 * PB;  // blocks per unit: PB per 16-lane row
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gw = blockIdx.x * 4 + wid;
+  const int n_pairs = a.batch * a.n_kv_heads;
+  const int pair = gw / a.n_part, wi = gw % a.n_part;
+  if (pair >= n_pairs) return;  // no barriers: waves are independent
+  const int sub = lane & 15, r16 = lane >> 4;
+  const int b = pair / a.n_kv_heads, g = pair % a.n_kv_heads;
   const int G = a.n_q_heads / a.n_kv_heads;
+  const int NB = a.n_blocks;
+  const int rank = a.rank;
 
   // lane `sub` owns dims 4(16c + sub) .. +4 for c < NC: each 16-lane row reads
   // 256 contiguous bytes of a summary row per instruction
@@ -73,76 +88,111 @@ __global__ __launch_bounds__(256) void select_scores_kernel(SelectArgs a) {
     }
   }
 
-  // load phase
-  float vec[PB][1 + RM][SL];
-  int jj[PB];
+  const float4* mean4 = reinterpret_cast<const float4*>(a.mean);
+  const float4* fac4 = reinterpret_cast<const float4*>(a.factor);
+  struct Stage {
+    float4 v[PB][R][NC];
+  };
+  // Every load is issued unconditionally (blocks past the end re-read the last
+  // block, factor rows past the rank re-read the last row, both ignored), so
+  // the compiler's waits count exactly the loads issued after each stage.
+  auto load = [&](int u, Stage& st) {
 #pragma unroll
-  for (int p = 0; p < PB; ++p) {
-    const int j = blockIdx.x * BPW + p * 16 + slot;
-    jj[p] = j;
-    const int jc = min(j, a.n_blocks - 1);
-    const size_t row = (size_t)bh * a.nblk_capacity + jc;
-    const float4* src = reinterpret_cast<const float4*>(a.mean + row * D) + sub;
+    for (int p = 0; p < PB; ++p) {
+      const int j = min(u * UB + 4 * p + r16, NB - 1);
+      const size_t row = (size_t)pair * a.nblk_capacity + j;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) st.v[p][0][c] = mean4[row * (D / 4) + 16 * c + sub];
+#pragma unroll
+      for (int i = 0; i < RM; ++i) {
+        const size_t fr = row * rank + min(i, rank - 1);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) st.v[p][1 + i][c] = fac4[fr * (D / 4) + 16 * c + sub];
+      }
+    }
+  };
+  auto dot = [&](const float4* v, int h) {
+    float acc = 0.f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const float4 v = src[16 * c];
-      vec[p][0][4 * c] = v.x; vec[p][0][4 * c + 1] = v.y; vec[p][0][4 * c + 2] = v.z; vec[p][0][4 * c + 3] = v.w;
+      acc = fmaf(q[h][4 * c], v[c].x, acc);
+      acc = fmaf(q[h][4 * c + 1], v[c].y, acc);
+      acc = fmaf(q[h][4 * c + 2], v[c].z, acc);
+      acc = fmaf(q[h][4 * c + 3], v[c].w, acc);
     }
+    return acc;
+  };
+  auto comp = [&](int u, const Stage& st) {
 #pragma unroll
-    for (int i = 0; i < RM; ++i) {
-      if (i < a.rank) {
-        const float4* fs = reinterpret_cast<const float4*>(a.factor + (row * a.rank + i) * D) + sub;
+    for (int p = 0; p < PB; ++p) {
+      const int j = u * UB + 4 * p + r16;
+      float s[GM];
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const float4 v = fs[16 * c];
-          vec[p][1 + i][4 * c] = v.x; vec[p][1 + i][4 * c + 1] = v.y;
-          vec[p][1 + i][4 * c + 2] = v.z; vec[p][1 + i][4 * c + 3] = v.w;
+      for (int h = 0; h < GM; ++h) s[h] = row16_sum(dot(st.v[p][0], h));
+#pragma unroll
+      for (int i = 0; i < RM; ++i) {
+        if (i < rank) {
+#pragma unroll
+          for (int h = 0; h < GM; ++h) {
+            const float pr = row16_sum(dot(st.v[p][1 + i], h));
+            s[h] = fmaf(0.5f * pr, pr, s[h]);
+          }
         }
       }
-    }
-  }
-  // compute phase
+      if (sub == 0 && j < NB) {
+        float mx = s[0];
 #pragma unroll
-  for (int p = 0; p < PB; ++p) {
-    float s[GM];
+        for (int h = 1; h < GM; ++h)
+          if (h < G) mx = fmaxf(mx, s[h]);
+        float sum = 0.f;
 #pragma unroll
-    for (int h = 0; h < GM; ++h) {
-      float acc = 0.f;
-#pragma unroll
-      for (int e = 0; e < SL; ++e) acc = fmaf(q[h][e], vec[p][0][e], acc);
-      s[h] = acc;
-    }
-#pragma unroll
-    for (int h = 0; h < GM; ++h) s[h] = row16_sum(s[h]);
-#pragma unroll
-    for (int i = 0; i < RM; ++i) {
-      if (i < a.rank) {
-        float pr[GM];
-#pragma unroll
-        for (int h = 0; h < GM; ++h) {
-          float acc = 0.f;
-#pragma unroll
-          for (int e = 0; e < SL; ++e) acc = fmaf(q[h][e], vec[p][1 + i][e], acc);
-          pr[h] = acc;
-        }
-#pragma unroll
-        for (int h = 0; h < GM; ++h) pr[h] = row16_sum(pr[h]);
-#pragma unroll
-        for (int h = 0; h < GM; ++h) s[h] = fmaf(0.5f * pr[h], pr[h], s[h]);
+        for (int h = 0; h < GM; ++h)
+          if (h < G) sum += __builtin_amdgcn_exp2f((s[h] - mx) * kLog2e);
+        // sum >= 1 (the max term is exactly 1): log2 needs no range care
+        a.scores[(size_t)pair * a.nblk_capacity + j] = fmaf(__builtin_amdgcn_logf(sum), kLn2, mx);
       }
     }
-    if (sub == 0 && jj[p] < a.n_blocks) {
-      float mx = s[0];
-#pragma unroll
-      for (int h = 1; h < GM; ++h)
-        if (h < G) mx = fmaxf(mx, s[h]);
-      float sum = 0.f;
-#pragma unroll
-      for (int h = 0; h < GM; ++h)
-        if (h < G) sum += __builtin_amdgcn_exp2f((s[h] - mx) * kLog2e);
-      // sum >= 1 (the max term is exactly 1): log2 needs no range care
-      a.scores[(size_t)bh * a.nblk_capacity + jj[p]] = fmaf(__builtin_amdgcn_logf(sum), kLn2, mx);
+  };
+
+  // two units in flight (A: even steps, B: odd), every path written out
+  const int n_units = (NB + UB - 1) / UB;
+  const int u0 = wi * a.per_wave, u1 = min(u0 + a.per_wave, n_units);
+  const int n = u1 - u0;
+  Stage A, B;
+  if (n >= 4) {
+    load(u0, A);
+    load(u0 + 1, B);
+    int u = u0;
+    for (; u + 3 < u1; u += 2) {
+      comp(u, A);
+      load(u + 2, A);
+      comp(u + 1, B);
+      load(u + 3, B);
     }
+    if (u + 2 < u1) {
+      comp(u, A);
+      load(u + 2, A);
+      comp(u + 1, B);
+      comp(u + 2, A);
+    } else {
+      comp(u, A);
+      comp(u + 1, B);
+    }
+  } else if (n == 3) {
+    load(u0, A);
+    load(u0 + 1, B);
+    comp(u0, A);
+    load(u0 + 2, A);
+    comp(u0 + 1, B);
+    comp(u0 + 2, A);
+  } else if (n == 2) {
+    load(u0, A);
+    load(u0 + 1, B);
+    comp(u0, A);
+    comp(u0 + 1, B);
+  } else if (n == 1) {
+    load(u0, A);
+    comp(u0, A);
   }
 }
 
@@ -281,13 +331,25 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
 }
 
 template <int D, int GM, int RM, bool BF16>
-hipError_t launch_t(const SelectArgs& a, hipStream_t stream) {
-  constexpr int BPW = 16 * (RM == 0 ? 4 : (RM <= 4 ? 2 : 1));
-  dim3 grid((a.n_blocks + BPW - 1) / BPW, a.batch * a.n_kv_heads);
-  if (a.n_blocks > 0)
-    hipLaunchKernelGGL((select_scores_kernel<D, GM, RM, BF16>), grid, dim3(256), 0, stream, a);
+hipError_t launch_t(const SelectArgs& a0, hipStream_t stream) {
+  constexpr int PB = RM == 0 ? 4 : (RM <= 2 ? 2 : 1);  // blocks per 16-lane row per unit
+  SelectArgs a = a0;
+  const int n_pairs = a.batch * a.n_kv_heads;
+  if (a.n_blocks > 0) {
+    // as few units per wave as keeps every wave resident at once
+    const int slots = 256 * (scores_heavy(GM, RM, PB, D) ? 4 : 8);
+    const long long units = (a.n_blocks + 4 * PB - 1) / (4 * PB);
+    long long c = (n_pairs * units + slots - 1) / slots;
+    if (c < 1) c = 1;
+    while (c < units && (long long)n_pairs * ((units + c - 1) / c) > slots) ++c;
+    a.per_wave = (int)c;
+    a.n_part = (int)((units + c - 1) / c);
+    const long long waves = (long long)n_pairs * a.n_part;
+    hipLaunchKernelGGL((select_scores_kernel<D, GM, RM, PB, BF16>), dim3((unsigned)((waves + 3) / 4)),
+                       dim3(256), 0, stream, a);
+  }
   const int per = (a.n_blocks + kTopkThreads - 1) / kTopkThreads;
-  const dim3 tg(a.batch * a.n_kv_heads), tb(kTopkThreads);
+  const dim3 tg(n_pairs), tb(kTopkThreads);
   if (per <= 2) hipLaunchKernelGGL(topk_kernel<2>, tg, tb, 0, stream, a);
   else if (per <= 8) hipLaunchKernelGGL(topk_kernel<8>, tg, tb, 0, stream, a);
   else if (per <= 32) hipLaunchKernelGGL(topk_kernel<32>, tg, tb, 0, stream, a);
@@ -298,6 +360,7 @@ hipError_t launch_t(const SelectArgs& a, hipStream_t stream) {
 template <int D, int GM, bool BF16>
 hipError_t launch_r(const SelectArgs& a, hipStream_t stream) {
   if (a.rank == 0) return launch_t<D, GM, 0, BF16>(a, stream);
+  if (a.rank <= 2) return launch_t<D, GM, 2, BF16>(a, stream);
   if (a.rank <= 4) return launch_t<D, GM, 4, BF16>(a, stream);
   return launch_t<D, GM, 8, BF16>(a, stream);
 }
