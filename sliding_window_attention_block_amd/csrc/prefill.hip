@@ -32,6 +32,8 @@
 //  * band workgroup order: K/V head varying fastest (consecutive workgroups
 //    land on different XCDs, so each XCD's L2 keeps one head's K/V), heaviest
 //    query tiles first.
+#include <type_traits>
+
 #include "launch.hpp"
 
 namespace bsattn {
@@ -82,41 +84,46 @@ __device__ __forceinline__ void dma_stage(const uint16_t* Kb, const uint16_t* Vb
   }
 }
 
-// One 64-key stage held in LDS for this wave's 32 query rows.  on[u]: half u
-// (keys 32u..32u+31) has an allowed entry for some row of the wave; part[u]: it
-// needs the per-element mask allowed(u, e) (element e of lane l is key
-// 32u + 8(e/4) + 4(l/32) + e%4).  Every branch here is wave-uniform.
-template <int D, typename Allowed>
+// Bits p of [lo, hi] within a 32-bit word (empty when lo > hi).
+__device__ __forceinline__ uint32_t range_bits32(int lo, int hi) {
+  lo = max(lo, 0);
+  hi = max(min(hi, 31), -1);
+  const uint32_t upto = hi >= 31 ? ~0u : ((1u << (hi + 1)) - 1u);  // bits <= hi (0 when hi < 0)
+  const uint32_t below = (1u << min(lo, 31)) - 1u;                  // bits < lo
+  return lo > hi ? 0u : (upto & ~below);
+}
+
+// One stage of NH 32-key halves held in LDS for this wave's 32 query rows.
+// am[u]: this lane's allowed keys of half u as bits p = key - 32u (the lane's
+// row is l % 32; its elements e hold keys 8(e/4) + 4(l/32) + e%4).  COMP adds
+// the product with the bf16 residual of P.  The MFMAs run unconditionally (a
+// half with nothing allowed only has its weights forced to 0), so no
+// accumulator ever sits under a branch, and the mask is two ALU ops per element.
+template <int D, int NH, bool COMP>
 __device__ __forceinline__ void stage(const uint8_t* kt, const uint8_t* vt, const u32x4* qop,
-                                      f32x16* oacc, RowState& st, float sl2, bool on0, bool on1,
-                                      bool part0, bool part1, bool comp, Allowed allowed) {
+                                      f32x16* oacc, RowState& st, float sl2, const uint32_t* am) {
   using T = Tile<D>;
   const int lane = threadIdx.x & 63;
   const int r32 = lane & 31, h2 = lane >> 5;
-  f32x16 s[2];
+  f32x16 s[NH];
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int u = 0; u < NH; ++u)
 #pragma unroll
     for (int e = 0; e < 16; ++e) s[u][e] = 0.f;
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
-    if (on0) {
-      const u32x4 k0 = *reinterpret_cast<const u32x4*>(kt + T::k_off(r32, 2 * c + h2));
-      s[0] = mfma32x32x16(as_bf16x8(k0), as_bf16x8(qop[c]), s[0]);
+  for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+    for (int u = 0; u < NH; ++u) {
+      const u32x4 k = *reinterpret_cast<const u32x4*>(kt + T::k_off(32 * u + r32, 2 * c + h2));
+      s[u] = mfma32x32x16(as_bf16x8(k), as_bf16x8(qop[c]), s[u]);
     }
-    if (on1) {
-      const u32x4 k1 = *reinterpret_cast<const u32x4*>(kt + T::k_off(32 + r32, 2 * c + h2));
-      s[1] = mfma32x32x16(as_bf16x8(k1), as_bf16x8(qop[c]), s[1]);
-    }
-  }
-  const bool on[2] = {on0, on1}, part[2] = {part0, part1};
   float mx = -INFINITY;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < NH; ++u) {
+    const uint32_t m = am[u] >> (4 * h2);
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      float v = s[u][e];
-      if (!on[u] || (part[u] && !allowed(u, e))) v = -INFINITY;
+      const float v = ((m >> (8 * (e >> 2) + (e & 3))) & 1u) ? s[u][e] : -INFINITY;
       s[u][e] = v;
       mx = fmaxf(mx, v);
     }
@@ -133,10 +140,10 @@ __device__ __forceinline__ void stage(const uint8_t* kt, const uint8_t* vt, cons
     st.m = m_new;
   }
   const float nm = (st.m == -INFINITY) ? 0.f : -st.m;
-  u32x4 pop[2][2], plo[2][2];
+  u32x4 pop[NH][2], plo[NH][2];
   float psum = 0.f;
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int u = 0; u < NH; ++u)
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
@@ -145,7 +152,7 @@ __device__ __forceinline__ void stage(const uint8_t* kt, const uint8_t* vt, cons
         const float p1 = __builtin_amdgcn_exp2f(fmaf(s[u][8 * kc + 2 * i + 1], sl2, nm));
         const uint32_t pk = cvt_pk_bf16(p0, p1);
         pop[u][kc][i] = pk;
-        if (comp) {
+        if constexpr (COMP) {
           plo[u][kc][i] = cvt_pk_bf16(p0 - bf16lo(pk), p1 - bf16hi(pk));
           psum += p0 + p1;
         } else {
@@ -155,8 +162,7 @@ __device__ __forceinline__ void stage(const uint8_t* kt, const uint8_t* vt, cons
   st.l += psum;
   const int q16 = lane >> 4, a16 = lane & 15;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    if (!on[u]) continue;
+  for (int u = 0; u < NH; ++u)
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -167,9 +173,8 @@ __device__ __forceinline__ void stage(const uint8_t* kt, const uint8_t* vt, cons
         const u32x2 hi = lds_read_tr16(vt, T::v_off(row + 8, col >> 3) + ((col & 7) << 1));
         const u32x4 vop = u32x4{lo[0], lo[1], hi[0], hi[1]};
         oacc[dt] = mfma32x32x16(as_bf16x8(vop), as_bf16x8(pop[u][kc]), oacc[dt]);
-        if (comp) oacc[dt] = mfma32x32x16(as_bf16x8(vop), as_bf16x8(plo[u][kc]), oacc[dt]);
+        if constexpr (COMP) oacc[dt] = mfma32x32x16(as_bf16x8(vop), as_bf16x8(plo[u][kc]), oacc[dt]);
       }
-  }
 }
 
 template <int D, bool LG>
@@ -180,7 +185,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   __shared__ int gcols[256];
   __shared__ int s_ngcols;
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave-uniform (scalar registers): every tile flag derived from it is too, so
+  // the MFMA chains below run under uniform branches, never under exec masks
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r32 = lane & 31, h2 = lane >> 5;
   const int N = a.seq_len;
   const int Hq = a.n_q_heads, Hkv = a.n_kv_heads, G = Hq / Hkv;
@@ -216,8 +224,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     uint8_t* kt = smem + wid * (LDS_BYTES / 4);
     uint8_t* vt = kt + T::BYTES / 2;  // half-height tiles: 32 rows each
     static_assert(T::BYTES % 2048 == 0, "half tiles are whole 1 KB chunks");
-    const bool comp = N < kCompKeys;
-    if (live) {
+    auto rows = [&](auto comp_tag) {
+      constexpr bool COMP = decltype(comp_tag)::value;
       for (int j0 = k0; j0 < k1; j0 += 32) {
         typedef __attribute__((address_space(3))) void lds_void;
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -233,11 +241,13 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
                                            (lds_void*)(vt + 1024 * k), 16, 0, 0);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        const bool tail = j0 + 32 > N;
-        stage<D>(kt, vt, qop, oacc, st, sl2, true, false, tail, false, comp, [&](int u, int e) {
-          return j0 + 8 * (e >> 2) + 4 * h2 + (e & 3) < N;
-        });
+        const uint32_t am[1] = {range_bits32(0, N - 1 - j0)};
+        stage<D, 1, COMP>(kt, vt, qop, oacc, st, sl2, am);
       }
+    };
+    if (live) {
+      if (N < kCompKeys) rows(std::true_type{});
+      else rows(std::false_type{});
     }
     // partial state of this wave -> workspace [b*Hq + h][rt][ks][32 rows]
     st.l += __shfl_xor(st.l, 32);
@@ -289,7 +299,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     }
     __syncthreads();
   }
-  const int ngc = LG ? s_ngcols : 0;
+  const int ngc = LG ? __builtin_amdgcn_readfirstlane(s_ngcols) : 0;
   const int n_stage = n_band + (ngc + BN - 1) / BN;
 
   const uint16_t* Kb = reinterpret_cast<const uint16_t*>(a.K) + (size_t)(b * Hkv + g) * a.kv_capacity * D;
@@ -325,6 +335,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     return gcols[min(slot, ngc - 1)];
   };
   if (n_stage > 0) dma_stage<D>(Kb, Vb, smem, smem + T::BYTES, wid, 4, [&](int r) { return row_pos(0, r); });
+  auto stages = [&](auto comp_tag) {
+  constexpr bool COMP = decltype(comp_tag)::value;
   for (int stg = 0; stg < n_stage; ++stg) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's copies for `stg` landed
     __syncthreads();  // every wave's copies landed; every wave is done with the other buffer
@@ -341,30 +353,30 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         for (int i = lower_bound_i32(a.gpos, a.n_global, jb); i < a.n_global && a.gpos[i] < jb + BN; ++i)
           gbits |= 1ull << (a.gpos[i] - jb);
       }
-      bool on[2], part[2];
+      // allowed keys of this lane's row: [lo, hi], plus the global columns
+      const int lo = wl < 0 ? 0 : myrow - wl;
+      const int hi = min(N - 1, wr < 0 ? N - 1 : myrow + wr);
+      uint32_t am[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int j0 = jb + 32 * u;
         const uint32_t gsub = (uint32_t)(gbits >> (32 * u));
-        const bool any_lo = wl < 0 || j0 + 31 >= r0 - wl;
-        const bool any_hi = wr < 0 || j0 <= r0 + 31 + wr;
-        on[u] = j0 < N && ((any_lo && any_hi) || gsub != 0u);
+        // wave-uniform shortcuts: every key of the half allowed for all 32 rows
         const bool all_lo = wl < 0 || j0 >= r0 + 31 - wl;
         const bool all_hi = wr < 0 || j0 + 31 <= r0 + wr;
-        part[u] = !(all_lo && all_hi && j0 + 31 < N);
+        const bool full = all_lo && all_hi && j0 + 31 < N;
+        am[u] = full ? ~0u : (range_bits32(lo - j0, hi - j0) | gsub);
       }
-      stage<D>(kt, vt, qop, oacc, st, sl2, on[0], on[1], part[0], part[1], comp, [&](int u, int e) {
-        const int jr = 32 * u + 8 * (e >> 2) + 4 * h2 + (e & 3);
-        const int j = jb + jr;
-        const bool in_band = (wl < 0 || j >= myrow - wl) && (wr < 0 || j <= myrow + wr);
-        return j < N && (in_band || ((gbits >> jr) & 1ull));
-      });
+      stage<D, 2, COMP>(kt, vt, qop, oacc, st, sl2, am);
     } else {
       const int s0 = (stg - n_band) * BN;
-      stage<D>(kt, vt, qop, oacc, st, sl2, s0 < ngc, s0 + 32 < ngc, s0 + 32 > ngc, s0 + 64 > ngc, comp,
-               [&](int u, int e) { return s0 + 32 * u + 8 * (e >> 2) + 4 * h2 + (e & 3) < ngc; });
+      const uint32_t am[2] = {range_bits32(0, ngc - 1 - s0), range_bits32(0, ngc - 1 - s0 - 32)};
+      stage<D, 2, COMP>(kt, vt, qop, oacc, st, sl2, am);
     }
   }
+  };
+  if (comp) stages(std::true_type{});
+  else stages(std::false_type{});
   // write rows (global rows are written by the merge of their split partials)
   st.l += __shfl_xor(st.l, 32);
   bool store = myrow < N;
