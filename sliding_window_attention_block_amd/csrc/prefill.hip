@@ -23,7 +23,8 @@
 //    Softmax per tile: one FMA folds the scale into exp2's argument, the row
 //    max is only moved (and the accumulator rescaled, wave-uniformly) when it
 //    grows by more than 2^8, and P is rounded to bf16 by v_cvt_pk_bf16_f32.
-//    Rows that see few keys add the bf16 residual of P in a second product.
+//    Rows that see fewer than 256 keys add the bf16 residual of P in a second
+//    product; other rows normalise by the sum of the rounded weights.
 //  * local+global: the global key columns outside a workgroup's band tiles are
 //    gathered into extra tiles.  The global query rows (every key) are split
 //    by key range over many waves (first in the grid); each writes a partial
@@ -43,6 +44,7 @@ constexpr int BM = 128;        // query rows per band workgroup
 constexpr int BN = 64;         // keys per LDS stage
 constexpr int kCompKeys = 256; // rows seeing fewer keys take the compensated PV product
 constexpr float kHeadroom = 8.f;  // log2 units a row max may grow before the rescale
+constexpr bf16x2 kOnesBf16x2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 template <int D>
 struct Tile {
@@ -84,6 +86,63 @@ __device__ __forceinline__ void dma_stage(const uint16_t* Kb, const uint16_t* Vb
   }
 }
 
+// Per-lane byte offsets, inside a 64-row tile, of the 1 KB DMA chunks a wave
+// issues for a contiguous stage (chunks wid, wid + 4, ...): with them a stage's
+// copies take one scalar base and no per-lane address arithmetic.
+template <int D>
+struct DmaLane {
+  static constexpr int NW = Tile<D>::BYTES / 1024 / 4;  // chunks per wave per tile
+  uint32_t k[NW], v[NW];
+  __device__ __forceinline__ void init(int wid) {
+    using T = Tile<D>;
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      const int off = 1024 * (wid + 4 * i) + 16 * lane;
+      const int r = off / T::RB, pc = (off % T::RB) >> 4;
+      k[i] = (uint32_t)(r * T::RB + ((pc ^ T::k_swz(r)) << 4));
+      v[i] = (uint32_t)(r * T::RB + ((pc ^ T::v_swz(r)) << 4));
+    }
+  }
+  // copy rows [row0, row0 + 64) of K and V (all < the sequence length)
+  __device__ __forceinline__ void issue(const uint8_t* Kb, const uint8_t* Vb, int row0, uint8_t* kt, uint8_t* vt,
+                                        int wid) const {
+    typedef __attribute__((address_space(3))) void lds_void;
+    const uint8_t* ks = Kb + (size_t)row0 * Tile<D>::RB;
+    const uint8_t* vs = Vb + (size_t)row0 * Tile<D>::RB;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(ks + k[i]), (lds_void*)(kt + 1024 * (wid + 4 * i)),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(vs + v[i]), (lds_void*)(vt + 1024 * (wid + 4 * i)),
+                                       16, 0, 0);
+    }
+  }
+};
+
+// The two 32-lane halves of x, each broadcast to the whole wave, by one
+// v_permlane32_swap of two copies of x: a = {x_lo, x_lo}, b = {x_hi, x_hi}.
+// Written in asm with both registers read-write: the compiler's builtin for
+// this instruction returns its first result twice.  The s_nops cover the
+// VALU-write / permlane-read hazards around it.
+__device__ __forceinline__ void halves(float x, float& a, float& b) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x), v = u;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(u), "+v"(v));
+  a = __builtin_bit_cast(float, u);
+  b = __builtin_bit_cast(float, v);
+}
+// Maximum / sum of a value over the two 32-lane halves of the wave.
+__device__ __forceinline__ float max_halves(float x) {
+  float a, b;
+  halves(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  float a, b;
+  halves(x, a, b);
+  return a + b;
+}
+
 // Bits p of [lo, hi] within a 32-bit word (empty when lo > hi).
 __device__ __forceinline__ uint32_t range_bits32(int lo, int hi) {
   lo = max(lo, 0);
@@ -101,7 +160,8 @@ __device__ __forceinline__ uint32_t range_bits32(int lo, int hi) {
 // accumulator ever sits under a branch, and the mask is two ALU ops per element.
 template <int D, int NH, bool COMP>
 __device__ __forceinline__ void stage(const uint8_t* kt, const uint8_t* vt, const u32x4* qop,
-                                      f32x16* oacc, RowState& st, float sl2, const uint32_t* am) {
+                                      f32x16* oacc, RowState& st, float sl2, const uint32_t* am,
+                                      bool masked) {
   using T = Tile<D>;
   const int lane = threadIdx.x & 63;
   const int r32 = lane & 31, h2 = lane >> 5;
@@ -117,18 +177,20 @@ __device__ __forceinline__ void stage(const uint8_t* kt, const uint8_t* vt, cons
       const u32x4 k = *reinterpret_cast<const u32x4*>(kt + T::k_off(32 * u + r32, 2 * c + h2));
       s[u] = mfma32x32x16(as_bf16x8(k), as_bf16x8(qop[c]), s[u]);
     }
-  float mx = -INFINITY;
+  if (masked) {  // wave-uniform: only tiles on a mask edge
 #pragma unroll
-  for (int u = 0; u < NH; ++u) {
-    const uint32_t m = am[u] >> (4 * h2);
+    for (int u = 0; u < NH; ++u) {
+      const uint32_t m = am[u] >> (4 * h2);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float v = ((m >> (8 * (e >> 2) + (e & 3))) & 1u) ? s[u][e] : -INFINITY;
-      s[u][e] = v;
-      mx = fmaxf(mx, v);
+      for (int e = 0; e < 16; ++e) s[u][e] = ((m >> (8 * (e >> 2) + (e & 3))) & 1u) ? s[u][e] : -INFINITY;
     }
   }
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  float mx = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < NH; ++u)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[u][e]);
+  mx = max_halves(mx);
   const float m_cand = mx * sl2;
   const bool need = m_cand > st.m + kHeadroom;
   if (__ballot(need)) {
@@ -156,7 +218,10 @@ __device__ __forceinline__ void stage(const uint8_t* kt, const uint8_t* vt, cons
           plo[u][kc][i] = cvt_pk_bf16(p0 - bf16lo(pk), p1 - bf16hi(pk));
           psum += p0 + p1;
         } else {
-          psum += bf16lo(pk) + bf16hi(pk);  // normaliser of the rounded weights the MFMA sees
+          // normaliser of the rounded weights the MFMA sees (O stays a convex
+          // combination of V rows however peaked the row's softmax is): one
+          // v_dot2_f32_bf16 with (1, 1) adds both rounded weights
+          psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), kOnesBf16x2, psum, false);
         }
       }
   st.l += psum;
@@ -242,7 +307,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         const uint32_t am[1] = {range_bits32(0, N - 1 - j0)};
-        stage<D, 1, COMP>(kt, vt, qop, oacc, st, sl2, am);
+        stage<D, 1, COMP>(kt, vt, qop, oacc, st, sl2, am, j0 + 32 > N);
       }
     };
     if (live) {
@@ -250,7 +315,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
       else rows(std::false_type{});
     }
     // partial state of this wave -> workspace [b*Hq + h][rt][ks][32 rows]
-    st.l += __shfl_xor(st.l, 32);
+    st.l = sum_halves(st.l);
     if (live) {
       const size_t prow = (((size_t)bhq * n_rt + rt) * a.g_splits + ks) * 32 + r32;
       if (h2 == 0) {
@@ -334,51 +399,69 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     const int slot = (stg - n_band) * BN + r;
     return gcols[min(slot, ngc - 1)];
   };
-  if (n_stage > 0) dma_stage<D>(Kb, Vb, smem, smem + T::BYTES, wid, 4, [&](int r) { return row_pos(0, r); });
+  DmaLane<D> dl;
+  dl.init(wid);
+  const uint8_t* Kb8 = reinterpret_cast<const uint8_t*>(Kb);
+  const uint8_t* Vb8 = reinterpret_cast<const uint8_t*>(Vb);
+  // copies of stage `stg` into (kt, vt): whole in-range band tiles take the
+  // precomputed lane offsets; the sequence's last partial tile and the gathered
+  // global columns compute each row's position
+  auto issue_stage = [&](int stg, uint8_t* kt, uint8_t* vt) {
+    const int row0 = (t_lo + stg) * BN;
+    if (stg < n_band && row0 + BN <= N) dl.issue(Kb8, Vb8, row0, kt, vt, wid);
+    else dma_stage<D>(Kb, Vb, kt, vt, wid, 4, [&](int r) { return row_pos(stg, r); });
+  };
+  uint8_t* const buf0 = smem;
+  uint8_t* const buf1 = smem + 2 * T::BYTES;
+  if (n_stage > 0) issue_stage(0, buf0, buf0 + T::BYTES);
   auto stages = [&](auto comp_tag) {
-  constexpr bool COMP = decltype(comp_tag)::value;
-  for (int stg = 0; stg < n_stage; ++stg) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's copies for `stg` landed
-    __syncthreads();  // every wave's copies landed; every wave is done with the other buffer
-    uint8_t* kt = smem + (stg & 1) * 2 * T::BYTES;
-    uint8_t* vt = kt + T::BYTES;
-    if (stg + 1 < n_stage) {
-      uint8_t* kn = smem + ((stg + 1) & 1) * 2 * T::BYTES;
-      dma_stage<D>(Kb, Vb, kn, kn + T::BYTES, wid, 4, [&](int r) { return row_pos(stg + 1, r); });
-    }
-    if (stg < n_band) {
-      const int jb = (t_lo + stg) * BN;
-      uint64_t gbits = 0ull;
-      if (LG) {
-        for (int i = lower_bound_i32(a.gpos, a.n_global, jb); i < a.n_global && a.gpos[i] < jb + BN; ++i)
-          gbits |= 1ull << (a.gpos[i] - jb);
-      }
-      // allowed keys of this lane's row: [lo, hi], plus the global columns
-      const int lo = wl < 0 ? 0 : myrow - wl;
-      const int hi = min(N - 1, wr < 0 ? N - 1 : myrow + wr);
-      uint32_t am[2];
+    constexpr bool COMP = decltype(comp_tag)::value;
+    // stage `stg` computed from buffer kt while stage stg + 1 is copied into kn
+    auto one = [&](int stg, uint8_t* kt, uint8_t* kn) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's copies for `stg` landed
+      __syncthreads();  // every wave's copies landed; every wave is done with the other buffer
+      if (stg + 1 < n_stage) issue_stage(stg + 1, kn, kn + T::BYTES);
+      uint8_t* vt = kt + T::BYTES;
+      if (stg < n_band) {
+        const int jb = (t_lo + stg) * BN;
+        uint64_t gbits = 0ull;
+        if (LG) {
+          for (int i = lower_bound_i32(a.gpos, a.n_global, jb); i < a.n_global && a.gpos[i] < jb + BN; ++i)
+            gbits |= 1ull << (a.gpos[i] - jb);
+        }
+        // allowed keys of this lane's row: [lo, hi], plus the global columns
+        const int lo = wl < 0 ? 0 : myrow - wl;
+        const int hi = min(N - 1, wr < 0 ? N - 1 : myrow + wr);
+        uint32_t am[2];
+        bool masked = false;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int j0 = jb + 32 * u;
-        const uint32_t gsub = (uint32_t)(gbits >> (32 * u));
-        // wave-uniform shortcuts: every key of the half allowed for all 32 rows
-        const bool all_lo = wl < 0 || j0 >= r0 + 31 - wl;
-        const bool all_hi = wr < 0 || j0 + 31 <= r0 + wr;
-        const bool full = all_lo && all_hi && j0 + 31 < N;
-        am[u] = full ? ~0u : (range_bits32(lo - j0, hi - j0) | gsub);
+        for (int u = 0; u < 2; ++u) {
+          const int j0 = jb + 32 * u;
+          const uint32_t gsub = (uint32_t)(gbits >> (32 * u));
+          // wave-uniform: every key of the half allowed for all 32 rows
+          const bool all_lo = wl < 0 || j0 >= r0 + 31 - wl;
+          const bool all_hi = wr < 0 || j0 + 31 <= r0 + wr;
+          const bool full = all_lo && all_hi && j0 + 31 < N;
+          masked |= !full;
+          am[u] = range_bits32(lo - j0, hi - j0) | gsub;
+        }
+        stage<D, 2, COMP>(kt, vt, qop, oacc, st, sl2, am, masked);
+      } else {
+        const int s0 = (stg - n_band) * BN;
+        const uint32_t am[2] = {range_bits32(0, ngc - 1 - s0), range_bits32(0, ngc - 1 - s0 - 32)};
+        stage<D, 2, COMP>(kt, vt, qop, oacc, st, sl2, am, s0 + 64 > ngc);
       }
-      stage<D, 2, COMP>(kt, vt, qop, oacc, st, sl2, am);
-    } else {
-      const int s0 = (stg - n_band) * BN;
-      const uint32_t am[2] = {range_bits32(0, ngc - 1 - s0), range_bits32(0, ngc - 1 - s0 - 32)};
-      stage<D, 2, COMP>(kt, vt, qop, oacc, st, sl2, am);
+    };
+    // unrolled by two so each buffer's LDS addresses are compile-time offsets
+    for (int stg = 0; stg < n_stage; stg += 2) {
+      one(stg, buf0, buf1);
+      if (stg + 1 < n_stage) one(stg + 1, buf1, buf0);
     }
-  }
   };
   if (comp) stages(std::true_type{});
   else stages(std::false_type{});
   // write rows (global rows are written by the merge of their split partials)
-  st.l += __shfl_xor(st.l, 32);
+  st.l = sum_halves(st.l);
   bool store = myrow < N;
   if (LG && store) {
     const int i = lower_bound_i32(a.gpos, a.n_global, myrow);
