@@ -33,6 +33,33 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
+CALIB_BYTES = 512 << 20    # the plain device copy --calibrate-copy runs (bytes read = bytes written)
+
+# HBM bytes per decode launch (split kernel + merge) of the 32K first-order
+# workload, from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs of
+# `bench.py --only first_order_decode_32k --calibrate-copy`, each scaled by
+# CALIB_BYTES / (the same counter for the calibration copy).  Valid only for
+# the decode sources it was taken on (their SHA-256); otherwise traffic is null.
+DECODE_TRAFFIC = {"sources_sha256": "932a9996ff3c04b77fdcd0b5197c89be42a39c10b25c187de5a7115e796bd984",
+                  "bytes_per_launch": 110205320}  # FETCH x 1.9999 (51513.8 + 1115.7 KiB) + WRITE x 1 (2096 + 272 KiB)
+DECODE_SOURCES = ("sliding_window_attention_block_amd/csrc/decode.hip",
+                  "sliding_window_attention_block_amd/csrc/device.hpp",
+                  "sliding_window_attention_block_amd/csrc/launch.hpp")
+
+
+def decode_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def decode_traffic():
+    if DECODE_TRAFFIC and DECODE_TRAFFIC["sources_sha256"] == decode_sources_sha256():
+        return DECODE_TRAFFIC["bytes_per_launch"]
+    return None
 BF16_PEAK = 2.5e15         # flop/s, MI355X dense bf16 MFMA
 MALL_BYTES = 256 << 20
 METRIC = "sparse-decode tokens/s and gathered-KV GB/s (% HBM peak); prefill % MFMA peak"
@@ -288,6 +315,9 @@ def main():
                     help="run one workload only (first_order_decode_32k, cobs_decode_128k, "
                          "swa_prefill_8k, local_global_prefill_16k); prints its result")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain 512 MiB device-to-device copy three times (the "
+                         "reference dispatch for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -302,6 +332,14 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     api.library()
+    if args.calibrate_copy:
+        src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copies done: 3 x {CALIB_BYTES} bytes")
+        del src, dst
     names = [args.only] if args.only else [HEADLINE, "cobs_decode_128k", "swa_prefill_8k",
                                             "local_global_prefill_16k"]
     results = {}
@@ -357,7 +395,7 @@ def main():
             "peak": HBM_PEAK / 1e9,
             "unit": "GB/s",
             "frac": h["decode_bytes"] / (h["decode_ms"] * 1e-3) / HBM_PEAK,
-            "traffic": None,
+            "traffic": decode_traffic(),
             "bytes_per_launch": h["decode_bytes"],
             "avg_launch_ms": h["decode_ms"],
         },

@@ -177,35 +177,34 @@ __device__ __forceinline__ void stage(const uint8_t* kt, const uint8_t* vt, cons
       const u32x4 k = *reinterpret_cast<const u32x4*>(kt + T::k_off(32 * u + r32, 2 * c + h2));
       s[u] = mfma32x32x16(as_bf16x8(k), as_bf16x8(qop[c]), s[u]);
     }
-  if (masked) {  // wave-uniform: only tiles on a mask edge
+  // Each 32-key half is its own online-softmax step, in program order
+  // QK0 QK1 | softmax0 PV0 | softmax1 PV1: the VALU work of a half runs while
+  // the MFMAs issued before it (QK1, then PV0) are still in the matrix pipe.
+  const int q16 = lane >> 4, a16 = lane & 15;
 #pragma unroll
-    for (int u = 0; u < NH; ++u) {
+  for (int u = 0; u < NH; ++u) {
+    if (masked) {  // wave-uniform: only tiles on a mask edge
       const uint32_t m = am[u] >> (4 * h2);
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[u][e] = ((m >> (8 * (e >> 2) + (e & 3))) & 1u) ? s[u][e] : -INFINITY;
     }
-  }
-  float mx = -INFINITY;
-#pragma unroll
-  for (int u = 0; u < NH; ++u)
+    float mx = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[u][e]);
-  mx = max_halves(mx);
-  const float m_cand = mx * sl2;
-  const bool need = m_cand > st.m + kHeadroom;
-  if (__ballot(need)) {
-    const float m_new = need ? m_cand : st.m;
-    const float alpha = need ? __builtin_amdgcn_exp2f(st.m - m_new) : 1.f;
-    st.l *= alpha;
+    mx = max_halves(mx);
+    const float m_cand = mx * sl2;
+    const bool need = m_cand > st.m + kHeadroom;
+    if (__ballot(need)) {
+      const float m_new = need ? m_cand : st.m;
+      const float alpha = need ? __builtin_amdgcn_exp2f(st.m - m_new) : 1.f;
+      st.l *= alpha;
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t) oacc[t] *= alpha;
-    st.m = m_new;
-  }
-  const float nm = (st.m == -INFINITY) ? 0.f : -st.m;
-  u32x4 pop[NH][2], plo[NH][2];
-  float psum = 0.f;
-#pragma unroll
-  for (int u = 0; u < NH; ++u)
+      for (int t = 0; t < D / 32; ++t) oacc[t] *= alpha;
+      st.m = m_new;
+    }
+    const float nm = (st.m == -INFINITY) ? 0.f : -st.m;
+    u32x4 pop[2], plo[2];
+    float psum = 0.f;
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
@@ -213,9 +212,9 @@ __device__ __forceinline__ void stage(const uint8_t* kt, const uint8_t* vt, cons
         const float p0 = __builtin_amdgcn_exp2f(fmaf(s[u][8 * kc + 2 * i], sl2, nm));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(s[u][8 * kc + 2 * i + 1], sl2, nm));
         const uint32_t pk = cvt_pk_bf16(p0, p1);
-        pop[u][kc][i] = pk;
+        pop[kc][i] = pk;
         if constexpr (COMP) {
-          plo[u][kc][i] = cvt_pk_bf16(p0 - bf16lo(pk), p1 - bf16hi(pk));
+          plo[kc][i] = cvt_pk_bf16(p0 - bf16lo(pk), p1 - bf16hi(pk));
           psum += p0 + p1;
         } else {
           // normaliser of the rounded weights the MFMA sees (O stays a convex
@@ -224,10 +223,7 @@ __device__ __forceinline__ void stage(const uint8_t* kt, const uint8_t* vt, cons
           psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), kOnesBf16x2, psum, false);
         }
       }
-  st.l += psum;
-  const int q16 = lane >> 4, a16 = lane & 15;
-#pragma unroll
-  for (int u = 0; u < NH; ++u)
+    st.l += psum;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -237,9 +233,10 @@ __device__ __forceinline__ void stage(const uint8_t* kt, const uint8_t* vt, cons
         const u32x2 lo = lds_read_tr16(vt, T::v_off(row, col >> 3) + ((col & 7) << 1));
         const u32x2 hi = lds_read_tr16(vt, T::v_off(row + 8, col >> 3) + ((col & 7) << 1));
         const u32x4 vop = u32x4{lo[0], lo[1], hi[0], hi[1]};
-        oacc[dt] = mfma32x32x16(as_bf16x8(vop), as_bf16x8(pop[u][kc]), oacc[dt]);
-        if constexpr (COMP) oacc[dt] = mfma32x32x16(as_bf16x8(vop), as_bf16x8(plo[u][kc]), oacc[dt]);
+        oacc[dt] = mfma32x32x16(as_bf16x8(vop), as_bf16x8(pop[kc]), oacc[dt]);
+        if constexpr (COMP) oacc[dt] = mfma32x32x16(as_bf16x8(vop), as_bf16x8(plo[kc]), oacc[dt]);
       }
+  }
 }
 
 template <int D, bool LG>
@@ -452,11 +449,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         stage<D, 2, COMP>(kt, vt, qop, oacc, st, sl2, am, s0 + 64 > ngc);
       }
     };
-    // unrolled by two so each buffer's LDS addresses are compile-time offsets
-    for (int stg = 0; stg < n_stage; stg += 2) {
+    // unrolled by two so each buffer's LDS addresses are compile-time offsets;
+    // an odd last stage runs after the loop (no branch inside the loop body)
+    int stg = 0;
+    for (; stg + 1 < n_stage; stg += 2) {
       one(stg, buf0, buf1);
-      if (stg + 1 < n_stage) one(stg + 1, buf1, buf0);
+      one(stg + 1, buf1, buf0);
     }
+    if (stg < n_stage) one(stg, buf0, buf1);
   };
   if (comp) stages(std::true_type{});
   else stages(std::false_type{});
