@@ -484,41 +484,54 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   }
 }
 
-// Merge the key-split partials of every global query row: one workgroup of D
-// threads per (b, h, global row); 8 partial loads in flight per thread.
+// Merge the key-split partials of every global query row: one wave per
+// (b, h, global row); lane owns dims lane + 64e; the partials are read 32 at a
+// time (all loads of a chunk in flight together) and folded online.
 template <int D>
-__global__ __launch_bounds__(D) void prefill_global_merge_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(64) void prefill_global_merge_kernel(PrefillArgs a) {
+  constexpr int DL = D / 64, CH = 32;
   const int n_rt = (a.n_global + 31) / 32;
   const int gi = blockIdx.x % a.n_global;
   const int bhq = blockIdx.x / a.n_global;
   const int rt = gi / 32, r = gi % 32;
-  const int dd = threadIdx.x;
+  const int lane = threadIdx.x;
   const int KS = a.g_splits;
   const size_t base = ((size_t)bhq * n_rt + rt) * KS;
-  float M = -INFINITY, L = 0.f, O = 0.f;
-  for (int s0 = 0; s0 < KS; s0 += 8) {
-    float ms[8], ls[8], os[8];
+  float M = -INFINITY, L = 0.f, O[DL];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int s = s0 + u;
-      const size_t prow = (base + min(s, KS - 1)) * 32 + r;
-      ms[u] = s < KS ? a.g_part_ml[2 * prow] : -INFINITY;
-      ls[u] = s < KS ? a.g_part_ml[2 * prow + 1] : 0.f;
-      os[u] = s < KS ? a.g_part_o[prow * D + dd] : 0.f;
-    }
+  for (int e = 0; e < DL; ++e) O[e] = 0.f;
+  for (int j0 = 0; j0 < KS; j0 += CH) {
+    float ms[CH], ls[CH], os[CH][DL];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (ms[u] == -INFINITY) continue;
-      const float Mn = fmaxf(M, ms[u]);
-      const float c0 = exp2f(M - Mn), c1 = exp2f(ms[u] - Mn);
-      L = L * c0 + ls[u] * c1;
-      O = O * c0 + os[u] * c1;
-      M = Mn;
+    for (int u = 0; u < CH; ++u) {
+      const size_t prow = (base + min(j0 + u, KS - 1)) * 32 + r;
+      ms[u] = j0 + u < KS ? a.g_part_ml[2 * prow] : -INFINITY;
+      ls[u] = a.g_part_ml[2 * prow + 1];
+#pragma unroll
+      for (int e = 0; e < DL; ++e) os[u][e] = a.g_part_o[prow * D + lane + 64 * e];
     }
+    float cm = M;
+#pragma unroll
+    for (int u = 0; u < CH; ++u) cm = fmaxf(cm, ms[u]);
+    if (cm == -INFINITY) continue;
+    const float c0 = M == -INFINITY ? 0.f : exp2f(M - cm);
+    L *= c0;
+#pragma unroll
+    for (int e = 0; e < DL; ++e) O[e] *= c0;
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const float w = ms[u] == -INFINITY ? 0.f : exp2f(ms[u] - cm);
+      L = fmaf(w, ls[u], L);
+#pragma unroll
+      for (int e = 0; e < DL; ++e) O[e] = fmaf(w, os[u][e], O[e]);
+    }
+    M = cm;
   }
   const size_t orow = (size_t)bhq * a.seq_len + a.gpos[gi];
-  a.O[orow * D + dd] = L > 0.f ? O / L : 0.f;
-  if (a.lse != nullptr && dd == 0) a.lse[orow] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+  for (int e = 0; e < DL; ++e) a.O[orow * D + lane + 64 * e] = O[e] * inv;
+  if (a.lse != nullptr && lane == 0) a.lse[orow] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
 template <int D, bool LG>
@@ -528,7 +541,7 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((prefill_kernel<D, LG>), dim3(n_wg), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !LG) return e;
-  hipLaunchKernelGGL((prefill_global_merge_kernel<D>), dim3(a.batch * a.n_q_heads * a.n_global), dim3(D), 0,
+  hipLaunchKernelGGL((prefill_global_merge_kernel<D>), dim3(a.batch * a.n_q_heads * a.n_global), dim3(64), 0,
                      stream, a);
   return hipGetLastError();
 }
