@@ -198,3 +198,14 @@ def test_repeated_calls_reuse_the_workspace(api):
                       2, 64, 0, None, O, None, ws)
     torch.cuda.synchronize()
     assert np.array_equal(O.cpu().numpy(), got["O"])
+
+
+def test_maximum_sizes(api):
+    """Every limit of the ABI at once: 65,536 complete blocks, top_k = 1024, 16 query
+    heads per K/V head and 256 global positions (d = 64, first-order selector)."""
+    n = 65536 * 64
+    w = _w("max_sizes", 1, 16, 1, 64, n, 0, 1024, 64, 64, "bf16", 24)
+    rng = np.random.default_rng(5)
+    globals_ = tuple(int(p) for p in np.sort(rng.choice(n, size=256, replace=False)))
+    ties = _check_case(api, w, globals_, 0)
+    print(f"[decode max sizes] near ties: {ties}", flush=True)
