@@ -3,8 +3,9 @@
 
 Step (the timed unit): one decode step of the first-order 32K workload (batch
 16, 32 query / 8 K/V heads, d 128, 64-token blocks, top-16 + sink block + 512-
-token window): selector scoring + top-k, then the split sparse decode and its
-merge.  `value` is tokens/s = batch / step time.  Summaries are built once
+token window), one bsattn_decode_step call: selector scoring, then the sparse
+decode whose waves take the top-k themselves, then the log-sum-exp merge.
+`value` is tokens/s = batch / step time.  Summaries are built once
 before timing (as the method builds them when blocks fill); their build time is
 reported separately, as are the COBS 128K decode step and the two prefills.
 
@@ -35,30 +36,31 @@ if ROOT not in sys.path:
 HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
 CALIB_BYTES = 512 << 20    # the plain device copy --calibrate-copy runs (bytes read = bytes written)
 
-# HBM bytes per decode launch (split kernel + merge) of the 32K first-order
-# workload, from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs of
-# `bench.py --only first_order_decode_32k --calibrate-copy`, each scaled by
+# HBM bytes per decode step (the three launches of bsattn_decode_step) of the
+# 32K first-order workload, from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs
+# of `bench.py --only first_order_decode_32k --calibrate-copy`, each scaled by
 # CALIB_BYTES / (the same counter for the calibration copy).  Valid only for
-# the decode sources it was taken on (their SHA-256); otherwise traffic is null.
-DECODE_TRAFFIC = {"sources_sha256": "932a9996ff3c04b77fdcd0b5197c89be42a39c10b25c187de5a7115e796bd984",
-                  "bytes_per_launch": 110205320}  # FETCH x 1.9999 (51513.8 + 1115.7 KiB) + WRITE x 1 (2096 + 272 KiB)
-DECODE_SOURCES = ("sliding_window_attention_block_amd/csrc/decode.hip",
-                  "sliding_window_attention_block_amd/csrc/device.hpp",
-                  "sliding_window_attention_block_amd/csrc/launch.hpp")
+# the sources it was taken on (their SHA-256); otherwise traffic is null.
+STEP_TRAFFIC = {"sources_sha256": "", "bytes_per_step": None}
+STEP_SOURCES = ("sliding_window_attention_block_amd/csrc/decode.hip",
+                "sliding_window_attention_block_amd/csrc/select.hip",
+                "sliding_window_attention_block_amd/csrc/bsattn.cpp",
+                "sliding_window_attention_block_amd/csrc/device.hpp",
+                "sliding_window_attention_block_amd/csrc/launch.hpp")
 
 
-def decode_sources_sha256():
+def step_sources_sha256():
     import hashlib
     h = hashlib.sha256()
-    for f in DECODE_SOURCES:
+    for f in STEP_SOURCES:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def decode_traffic():
-    if DECODE_TRAFFIC and DECODE_TRAFFIC["sources_sha256"] == decode_sources_sha256():
-        return DECODE_TRAFFIC["bytes_per_launch"]
+def step_traffic():
+    if STEP_TRAFFIC["sources_sha256"] == step_sources_sha256():
+        return STEP_TRAFFIC["bytes_per_step"]
     return None
 BF16_PEAK = 2.5e15         # flop/s, MI355X dense bf16 MFMA
 MALL_BYTES = 256 << 20
@@ -134,7 +136,8 @@ def bench_decode(api, torch, w, x, steps, warmup):
         ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
         O = torch.empty((B, Hq, d), device="cuda")
         lse = torch.empty((B, Hq), device="cuda")
-        reps.append(dict(K=K, V=V, Q=Q, mean=mean, factor=factor, scores=scores, sel=sel, ws=ws, O=O, lse=lse))
+        reps.append(dict(K=K, V=V, Q=Q, mean=mean, factor=factor, scores=scores, sel=sel, ws=ws,
+                         O=O, lse=lse))
     del K0, V0, Q0
     # A1: summaries (built once per block; timed on every replica)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -154,8 +157,14 @@ def bench_decode(api, torch, w, x, steps, warmup):
         api.bsattn_decode(shape, rp["Q"], rp["K"], rp["V"], rp["sel"], w.top_k, w.window, w.n_sink,
                           None, rp["O"], rp["lse"], rp["ws"])
 
+    def step(rp):
+        api.bsattn_decode_step(shape, rp["Q"], rp["K"], rp["V"], rp["mean"], rp["factor"], w.rank, nb,
+                               w.top_k, w.window, w.n_sink, None, rp["sel"], rp["scores"], rp["O"],
+                               rp["lse"], rp["ws"])
+
     for i in range(warmup):
         rp = reps[i % R]
+        step(rp)
         select(rp)
         decode(rp)
     torch.cuda.synchronize()
@@ -169,8 +178,9 @@ def bench_decode(api, torch, w, x, steps, warmup):
 
     # The timed steps run as one HIP graph of `steps` steps (replica i % R at step i):
     # a decode step is a handful of short kernels, and launching them one by one
-    # from Python would time the host, not the GPU.  Separate graphs of the select
-    # calls alone and the decode calls alone give the per-phase launch times.
+    # from Python would time the host, not the GPU.  Separate graphs give the
+    # context figures: the same step as two calls (bsattn_select_topk, then
+    # bsattn_decode), and each of those calls alone.
     def capture(fns):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
@@ -189,25 +199,27 @@ def bench_decode(api, torch, w, x, steps, warmup):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps, (time.perf_counter() - t0) * 1e3 / steps
 
-    g_step, g_sel, g_dec = capture((select, decode)), capture((select,)), capture((decode,))
-    g_step.replay()  # untimed: the first replay of a graph uploads it
+    g_step = capture((step,))
+    g_two, g_sel, g_dec = capture((select, decode)), capture((select,)), capture((decode,))
+    for g in (g_step, g_two, g_sel, g_dec):
+        g.replay()  # untimed: the first replay of a graph uploads it
     torch.cuda.synchronize()
     ms_step, wall_step = timed_replay(g_step)
+    two_ms, _ = timed_replay(g_two)
     sel_ms, _ = timed_replay(g_sel)
     dec_ms, _ = timed_replay(g_dec)
-    del g_step, g_sel, g_dec
+    del g_step, g_two, g_sel, g_dec
     # the same steps launched one call at a time from Python (context only)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        select(reps[i % R])
-        decode(reps[i % R])
+        step(reps[i % R])
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) * 1e3 / steps
     res = dict(
         workload=w.name, ms_per_step=ms_step, wall_ms_per_step=wall_step, tokens_per_s=B / (ms_step * 1e-3),
-        eager_ms_per_step=eager_ms, replicas=R, attended_tokens=tokens, gathered_kv_bytes=kv_bytes,
-        select_ms=sel_ms, decode_ms=dec_ms,
+        eager_ms_per_step=eager_ms, two_call_ms_per_step=two_ms, replicas=R, attended_tokens=tokens,
+        gathered_kv_bytes=kv_bytes, select_ms=sel_ms, decode_ms=dec_ms,
         select_bytes=sel_bytes, decode_bytes=kv_bytes + io_bytes,
         summary_build_ms=float(np.median(build_ms)),
         summary_build_bytes=B * Hkv * nb * S * d * elem + summ_bytes,
@@ -216,7 +228,10 @@ def bench_decode(api, torch, w, x, steps, warmup):
     res["gathered_kv_frac_hbm"] = res["gathered_kv_GBps"] * 1e9 / HBM_PEAK
     res["decode_GBps"] = (kv_bytes + io_bytes) / (dec_ms * 1e-3) / 1e9
     res["select_GBps"] = sel_bytes / (sel_ms * 1e-3) / 1e9
-    res["step_GBps"] = (kv_bytes + io_bytes + sel_bytes) / (ms_step * 1e-3) / 1e9
+    # algorithmic bytes of a step: summaries, Q, the gathered K/V rows, and the
+    # outputs (scores, sel, O, lse), each once
+    res["step_bytes"] = summ_bytes + kv_bytes + io_bytes + B * Hkv * nb * 4
+    res["step_GBps"] = res["step_bytes"] / (ms_step * 1e-3) / 1e9
     del reps
     torch.cuda.empty_cache()
     return res
@@ -393,15 +408,16 @@ def main():
         "gathered_kv_GBps": h.get("gathered_kv_GBps"),
         "gathered_kv_frac_hbm": h.get("gathered_kv_frac_hbm"),
         "roofline": {
-            "kernel": "bsattn_decode (sparse flash-decode split kernel + log-sum-exp merge)",
+            "kernel": "bsattn_decode_step: select_scores_kernel, decode_bf16_kernel with the "
+                      "in-wave top-k, decode_merge_kernel (one call, three launches)",
             "bound": "hbm",
-            "achieved": h["decode_bytes"] / (h["decode_ms"] * 1e-3) / 1e9,
+            "achieved": h["step_bytes"] / (h["ms_per_step"] * 1e-3) / 1e9,
             "peak": HBM_PEAK / 1e9,
             "unit": "GB/s",
-            "frac": h["decode_bytes"] / (h["decode_ms"] * 1e-3) / HBM_PEAK,
-            "traffic": decode_traffic(),
-            "bytes_per_launch": h["decode_bytes"],
-            "avg_launch_ms": h["decode_ms"],
+            "frac": h["step_bytes"] / (h["ms_per_step"] * 1e-3) / HBM_PEAK,
+            "traffic": step_traffic(),
+            "bytes_per_launch": h["step_bytes"],
+            "avg_launch_ms": h["ms_per_step"],
         },
         "cpu_baseline": cpu,
         "rows": results,

@@ -147,6 +147,29 @@ bsattn_status bsattn_decode(const bsattn_shape* shape, const void* Q, const void
                             void* hip_stream);
 
 /*
+ * One decode step in one call: the selector's scores and top-k
+ * (bsattn_select_topk) followed by the sparse decode (bsattn_decode), with the
+ * same arguments, outputs and limits as those two calls together: sel and
+ * scores are written as bsattn_select_topk writes them, O and lse as
+ * bsattn_decode writes them [COBS 1, 2.1-2.3; SWA 拡張手法; LG].  workspace:
+ * at least bsattn_decode_workspace_bytes(shape, top_k, window, n_sink,
+ * n_global) bytes, 256-byte aligned, contents need not be initialised (NULL
+ * when that size is 0).  With BF16 K/V, at most 2048 complete blocks and
+ * top_k <= 256 the top-k runs inside the decode kernel (each decode wave
+ * selects its pair's blocks while its sink and window loads are in flight),
+ * one launch fewer than the two calls; the selection is the same exact
+ * top-k (score descending, then block index ascending).  Otherwise the step
+ * runs the two calls' kernels.  Calls that share a workspace must be ordered
+ * (same stream).
+ */
+bsattn_status bsattn_decode_step(const bsattn_shape* shape, const void* Q, const void* K,
+                                 const void* V, const float* mean, const float* factor,
+                                 int32_t rank, int32_t nblk_capacity, int32_t top_k,
+                                 int32_t window, int32_t n_sink, const int32_t* global_pos_host,
+                                 int32_t n_global, int32_t* sel, float* scores, float* O,
+                                 float* lse, void* workspace, size_t ws_bytes, void* hip_stream);
+
+/*
  * Masked prefill attention, BF16 Q/K/V, fp32 O and lse.  Query i sees key j iff
  *   (i - window_left <= j <= i + window_right) [and j <= i when causal]
  *   or i is a global position or j is a global position.

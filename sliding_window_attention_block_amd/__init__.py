@@ -17,7 +17,9 @@ from ._lib import BSATTN_BF16, BSATTN_F32, Shape
 
 __all__ = [
     "BsattnError", "Shape", "make_shape", "library", "bsattn_build_summaries",
-    "bsattn_select_topk", "bsattn_decode_workspace_bytes", "bsattn_decode", "bsattn_prefill",
+    "bsattn_select_topk", "bsattn_decode_workspace_bytes", "bsattn_decode",
+    "bsattn_decode_step",
+    "bsattn_prefill",
     "bsattn_prefill_workspace_bytes",
     "bsattn_status_string", "bsattn_version", "BSATTN_F32", "BSATTN_BF16",
 ]
@@ -108,6 +110,16 @@ def bsattn_decode(shape, Q, K, V, sel, top_k, window, n_sink, global_pos, O, lse
     _check(library().bsattn_decode(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(sel),
                                    top_k, window, n_sink, g, ng, _ptr(O), _ptr(lse),
                                    _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def bsattn_decode_step(shape, Q, K, V, mean, factor, rank, nblk_capacity, top_k, window, n_sink,
+                       global_pos, sel, scores, O, lse, workspace, stream=None):
+    g, ng = _globals(global_pos)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(library().bsattn_decode_step(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(mean),
+                                        _ptr(factor), rank, nblk_capacity, top_k, window, n_sink, g,
+                                        ng, _ptr(sel), _ptr(scores), _ptr(O), _ptr(lse),
+                                        _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def bsattn_prefill_workspace_bytes(shape, n_global):

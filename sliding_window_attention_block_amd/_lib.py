@@ -25,6 +25,7 @@ EXPORTS = (
     "bsattn_select_topk",
     "bsattn_decode_workspace_bytes",
     "bsattn_decode",
+    "bsattn_decode_step",
     "bsattn_prefill",
     "bsattn_prefill_workspace_bytes",
     "bsattn_status_string",
@@ -75,6 +76,10 @@ def load():
     lib.bsattn_decode.argtypes = [_pshape, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _pi32, _i32,
                                   _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.bsattn_decode.restype = _st
+    lib.bsattn_decode_step.argtypes = [_pshape, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                       _i32, _pi32, _i32, _vp, _vp, _vp, _vp, _vp,
+                                       ctypes.c_size_t, _vp]
+    lib.bsattn_decode_step.restype = _st
     lib.bsattn_prefill.argtypes = [_pshape, _vp, _vp, _vp, _i32, _i32, _i32, _pi32, _i32,
                                    _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.bsattn_prefill.restype = _st

@@ -110,21 +110,35 @@ bsattn::ForcedBlocks make_forced_blocks(const bsattn::ForcedSet& f) {
   return fb;
 }
 
-int forced_block_bound(int32_t n_ctx, int32_t window, int32_t n_sink, int32_t n_global) {
+// Forced blocks of the sink and window ranges (exact; global tokens add up to
+// one block each on top).
+int forced_range_blocks(int32_t n_ctx, int32_t window, int32_t n_sink) {
   bsattn::ForcedSet f = make_forced(n_ctx, window, n_sink, nullptr, 0);
   bsattn::ForcedBlocks fb = make_forced_blocks(f);
-  return fb.r0_n + fb.r1_n + n_global;
+  return fb.r0_n + fb.r1_n;
 }
 
-// Workspace layout: partial numerators [B*Hq, n_part, d] | partial (max, sum) [B*Hq, n_part, 2],
-// each region 256-byte aligned.
+// Decode launch plan for top_k selected and n_forced forced items per pair:
+// n_part partials per pair (merged when more than one); bf16 waves take fh
+// forced and sh selected half items each.
+struct DecodePlan {
+  int half_items, n_part, fh, sh;
+};
+DecodePlan decode_plan(const bsattn_shape* s, int top_k, int n_forced) {
+  DecodePlan p;
+  bsattn::decode_split_geometry(top_k + n_forced, s->batch * s->n_kv_heads, s->head_dim,
+                                s->dtype == BSATTN_BF16, &p.half_items, &p.n_part);
+  p.fh = (2 * n_forced + p.n_part - 1) / p.n_part;
+  p.sh = (2 * top_k + p.n_part - 1) / p.n_part;
+  return p;
+}
+
+// Workspace layout: partial numerators [B*Hq, n_part, d] | partial (max, sum)
+// [B*Hq, n_part, 2], each region 256-byte aligned; nothing when n_part == 1.
 struct WsLayout {
   size_t o_off, ml_off, total;
 };
-WsLayout workspace_layout(const bsattn_shape* s, int n_items) {
-  int per_wave, n_part;
-  bsattn::decode_split_geometry(n_items, s->batch * s->n_kv_heads, s->head_dim, s->dtype == BSATTN_BF16,
-                                &per_wave, &n_part);
+WsLayout workspace_layout(const bsattn_shape* s, int n_part) {
   const size_t rows = n_part > 1 ? (size_t)s->batch * s->n_q_heads * n_part : 0;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   WsLayout l;
@@ -133,7 +147,20 @@ WsLayout workspace_layout(const bsattn_shape* s, int n_items) {
   l.total = l.ml_off + up(rows * 2 * sizeof(float));
   return l;
 }
-size_t workspace_for(const bsattn_shape* s, int n_items) { return workspace_layout(s, n_items).total; }
+
+// Workspace bytes that cover every forced-item count the arguments allow: the
+// sink and window blocks plus 0 .. n_global blocks of global tokens (globals
+// may share blocks or fall in the ranges, and the split geometry is not
+// monotone in the item count).
+size_t decode_workspace_bound(const bsattn_shape* s, int top_k, int window, int n_sink, int n_global) {
+  const int base = forced_range_blocks(s->n_ctx, window, n_sink);
+  size_t most = 0;
+  for (int extra = 0; extra <= n_global; ++extra) {
+    const size_t t = workspace_layout(s, decode_plan(s, top_k, base + extra).n_part).total;
+    if (t > most) most = t;
+  }
+  return most;
+}
 
 // Prefill workspace (global query rows only): partial numerators
 // [B*Hq, ceil(n_global/32), splits, 32, d] | partial (max, sum) [..., 2], 256-byte aligned.
@@ -152,6 +179,85 @@ PrefillWs prefill_workspace_layout(const bsattn_shape* s, int n_global) {
   l.total = n_global > 0 ? l.ml_off + up(rows * 2 * sizeof(float)) : 0;
   return l;
 }
+
+// Validation of the selector's arguments (bsattn_select_topk, bsattn_decode_step).
+bsattn_status select_args(const bsattn_shape* shape, const void* Q, const float* mean, const float* factor,
+                          int32_t rank, int32_t nblk_capacity, int32_t top_k, int32_t window, int32_t n_sink,
+                          const int32_t* global_pos_host, int32_t n_global, int32_t* sel, float* scores,
+                          bsattn::SelectArgs& a) {
+  bsattn_status st = check_shape(shape, true);
+  if (st != BSATTN_OK) return st;
+  if (Q == nullptr || mean == nullptr || sel == nullptr || scores == nullptr)
+    return fail(BSATTN_ERR_INVALID, "Q, mean, sel and scores must be non-NULL");
+  if (rank < 0 || rank > BSATTN_MAX_RANK) return fail(BSATTN_ERR_INVALID, "rank must be in [0, %d]", BSATTN_MAX_RANK);
+  if (rank > 0 && factor == nullptr) return fail(BSATTN_ERR_INVALID, "factor is NULL with rank > 0");
+  if (top_k < 1 || top_k > BSATTN_MAX_TOP_K) return fail(BSATTN_ERR_INVALID, "top_k must be in [1, %d]", BSATTN_MAX_TOP_K);
+  if (window < 0 || n_sink < 0) return fail(BSATTN_ERR_INVALID, "window and n_sink must be >= 0");
+  const int nb = shape->n_ctx / shape->block_size;
+  if (nb > BSATTN_MAX_BLOCKS) return fail(BSATTN_ERR_UNSUPPORTED, "more than %d complete blocks", BSATTN_MAX_BLOCKS);
+  if (nblk_capacity < nb) return fail(BSATTN_ERR_INVALID, "nblk_capacity < n_ctx / block_size");
+  st = check_globals(global_pos_host, n_global, shape->n_ctx);
+  if (st != BSATTN_OK) return st;
+  if (!aligned16(Q) || !aligned16(mean) || (factor && !aligned16(factor)))
+    return fail(BSATTN_ERR_INVALID, "device pointers must be 16-byte aligned");
+  std::memset(&a, 0, sizeof(a));
+  a.Q = Q; a.mean = mean; a.factor = rank > 0 ? factor : nullptr; a.sel = sel; a.scores = scores;
+  a.batch = shape->batch; a.n_q_heads = shape->n_q_heads; a.n_kv_heads = shape->n_kv_heads;
+  a.head_dim = shape->head_dim;
+  a.n_blocks = nb;
+  a.nblk_capacity = nblk_capacity;
+  a.rank = rank;
+  a.top_k = top_k;
+  a.scale = effective_scale(shape);
+  a.bf16 = shape->dtype == BSATTN_BF16;
+  a.forced = make_forced(shape->n_ctx, window, n_sink, global_pos_host, n_global);
+  return BSATTN_OK;
+}
+
+// Validation of the sparse decode's arguments and its launch plan (bsattn_decode,
+// bsattn_decode_step); `sel` is read by the former, written by the latter.
+bsattn_status decode_args(const bsattn_shape* shape, const void* Q, const void* K, const void* V,
+                          const int32_t* sel, int32_t top_k, int32_t window, int32_t n_sink,
+                          const int32_t* global_pos_host, int32_t n_global, float* O, float* lse,
+                          void* workspace, size_t ws_bytes, bsattn::DecodeArgs& a) {
+  bsattn_status st = check_shape(shape, true);
+  if (st != BSATTN_OK) return st;
+  if (Q == nullptr || K == nullptr || V == nullptr || sel == nullptr || O == nullptr)
+    return fail(BSATTN_ERR_INVALID, "Q, K, V, sel and O must be non-NULL");
+  if (top_k < 1 || top_k > BSATTN_MAX_TOP_K) return fail(BSATTN_ERR_INVALID, "top_k must be in [1, %d]", BSATTN_MAX_TOP_K);
+  if (window < 0 || n_sink < 0) return fail(BSATTN_ERR_INVALID, "window and n_sink must be >= 0");
+  st = check_globals(global_pos_host, n_global, shape->n_ctx);
+  if (st != BSATTN_OK) return st;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O))
+    return fail(BSATTN_ERR_INVALID, "device pointers must be 16-byte aligned");
+  std::memset(&a, 0, sizeof(a));
+  a.forced = make_forced(shape->n_ctx, window, n_sink, global_pos_host, n_global);
+  a.fblocks = make_forced_blocks(a.forced);
+  const int n_forced = a.fblocks.r0_n + a.fblocks.r1_n + a.fblocks.n_gblk;
+  a.n_items = top_k + n_forced;
+  const DecodePlan plan = decode_plan(shape, top_k, n_forced);
+  const WsLayout lay = workspace_layout(shape, plan.n_part);
+  const size_t need = plan.n_part > 1 ? lay.total : 0;
+  if (need > 0 && (workspace == nullptr || ws_bytes < need))
+    return fail(BSATTN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
+  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(BSATTN_ERR_INVALID, "workspace must be 256-byte aligned");
+  a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.o_off);
+  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.ml_off);
+  a.per_wave = 1;
+  a.fh_per_wave = plan.fh;
+  a.sh_per_wave = plan.sh;
+  a.n_part = plan.n_part;
+  a.Q = Q; a.K = K; a.V = V; a.sel = sel; a.O = O; a.lse = lse;
+  a.batch = shape->batch; a.n_q_heads = shape->n_q_heads; a.n_kv_heads = shape->n_kv_heads;
+  a.head_dim = shape->head_dim;
+  a.kv_capacity = shape->kv_capacity;
+  a.top_k = top_k;
+  a.scale = effective_scale(shape);
+  a.bf16 = shape->dtype == BSATTN_BF16;
+  return BSATTN_OK;
+}
+
 
 }  // namespace
 
@@ -210,32 +316,10 @@ bsattn_status bsattn_select_topk(const bsattn_shape* shape, const void* Q, const
                                  const int32_t* global_pos_host, int32_t n_global, int32_t* sel,
                                  float* scores, void* hip_stream) {
   g_err[0] = 0;
-  bsattn_status st = check_shape(shape, true);
-  if (st != BSATTN_OK) return st;
-  if (Q == nullptr || mean == nullptr || sel == nullptr || scores == nullptr)
-    return fail(BSATTN_ERR_INVALID, "Q, mean, sel and scores must be non-NULL");
-  if (rank < 0 || rank > BSATTN_MAX_RANK) return fail(BSATTN_ERR_INVALID, "rank must be in [0, %d]", BSATTN_MAX_RANK);
-  if (rank > 0 && factor == nullptr) return fail(BSATTN_ERR_INVALID, "factor is NULL with rank > 0");
-  if (top_k < 1 || top_k > BSATTN_MAX_TOP_K) return fail(BSATTN_ERR_INVALID, "top_k must be in [1, %d]", BSATTN_MAX_TOP_K);
-  if (window < 0 || n_sink < 0) return fail(BSATTN_ERR_INVALID, "window and n_sink must be >= 0");
-  const int nb = shape->n_ctx / shape->block_size;
-  if (nb > BSATTN_MAX_BLOCKS) return fail(BSATTN_ERR_UNSUPPORTED, "more than %d complete blocks", BSATTN_MAX_BLOCKS);
-  if (nblk_capacity < nb) return fail(BSATTN_ERR_INVALID, "nblk_capacity < n_ctx / block_size");
-  st = check_globals(global_pos_host, n_global, shape->n_ctx);
-  if (st != BSATTN_OK) return st;
-  if (!aligned16(Q) || !aligned16(mean) || (factor && !aligned16(factor)))
-    return fail(BSATTN_ERR_INVALID, "device pointers must be 16-byte aligned");
   bsattn::SelectArgs a;
-  a.Q = Q; a.mean = mean; a.factor = rank > 0 ? factor : nullptr; a.sel = sel; a.scores = scores;
-  a.batch = shape->batch; a.n_q_heads = shape->n_q_heads; a.n_kv_heads = shape->n_kv_heads;
-  a.head_dim = shape->head_dim;
-  a.n_blocks = nb;
-  a.nblk_capacity = nblk_capacity;
-  a.rank = rank;
-  a.top_k = top_k;
-  a.scale = effective_scale(shape);
-  a.bf16 = shape->dtype == BSATTN_BF16;
-  a.forced = make_forced(shape->n_ctx, window, n_sink, global_pos_host, n_global);
+  const bsattn_status st = select_args(shape, Q, mean, factor, rank, nblk_capacity, top_k, window, n_sink,
+                                       global_pos_host, n_global, sel, scores, a);
+  if (st != BSATTN_OK) return st;
   hipError_t e = bsattn::launch_select_topk(a, (hipStream_t)hip_stream);
   if (e != hipSuccess) return fail(BSATTN_ERR_HIP, "select launch: %s", hipGetErrorString(e));
   return BSATTN_OK;
@@ -247,8 +331,7 @@ size_t bsattn_decode_workspace_bytes(const bsattn_shape* shape, int32_t top_k, i
   if (top_k < 1 || top_k > BSATTN_MAX_TOP_K || window < 0 || n_sink < 0 || n_global < 0 ||
       n_global > BSATTN_MAX_GLOBAL)
     return 0;
-  const int n_items = top_k + forced_block_bound(shape->n_ctx, window, n_sink, n_global);
-  return workspace_for(shape, n_items);
+  return decode_workspace_bound(shape, top_k, window, n_sink, n_global);
 }
 
 bsattn_status bsattn_decode(const bsattn_shape* shape, const void* Q, const void* K, const void* V,
@@ -256,39 +339,45 @@ bsattn_status bsattn_decode(const bsattn_shape* shape, const void* Q, const void
                             const int32_t* global_pos_host, int32_t n_global, float* O, float* lse,
                             void* workspace, size_t ws_bytes, void* hip_stream) {
   g_err[0] = 0;
-  bsattn_status st = check_shape(shape, true);
-  if (st != BSATTN_OK) return st;
-  if (Q == nullptr || K == nullptr || V == nullptr || sel == nullptr || O == nullptr)
-    return fail(BSATTN_ERR_INVALID, "Q, K, V, sel and O must be non-NULL");
-  if (top_k < 1 || top_k > BSATTN_MAX_TOP_K) return fail(BSATTN_ERR_INVALID, "top_k must be in [1, %d]", BSATTN_MAX_TOP_K);
-  if (window < 0 || n_sink < 0) return fail(BSATTN_ERR_INVALID, "window and n_sink must be >= 0");
-  st = check_globals(global_pos_host, n_global, shape->n_ctx);
-  if (st != BSATTN_OK) return st;
-  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O))
-    return fail(BSATTN_ERR_INVALID, "device pointers must be 16-byte aligned");
   bsattn::DecodeArgs a;
-  std::memset(&a, 0, sizeof(a));
-  a.forced = make_forced(shape->n_ctx, window, n_sink, global_pos_host, n_global);
-  a.fblocks = make_forced_blocks(a.forced);
-  a.n_items = top_k + a.fblocks.r0_n + a.fblocks.r1_n + a.fblocks.n_gblk;
-  const size_t need = workspace_for(shape, a.n_items);
-  if (need > 0 && (workspace == nullptr || ws_bytes < need))
-    return fail(BSATTN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
-  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-    return fail(BSATTN_ERR_INVALID, "workspace must be 256-byte aligned");
-  bsattn::decode_split_geometry(a.n_items, shape->batch * shape->n_kv_heads, shape->head_dim,
-                                shape->dtype == BSATTN_BF16, &a.per_wave, &a.n_part);
-  const WsLayout lay = workspace_layout(shape, a.n_items);
-  a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.o_off);
-  a.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.ml_off);
-  a.Q = Q; a.K = K; a.V = V; a.sel = sel; a.O = O; a.lse = lse;
-  a.batch = shape->batch; a.n_q_heads = shape->n_q_heads; a.n_kv_heads = shape->n_kv_heads;
-  a.head_dim = shape->head_dim;
-  a.kv_capacity = shape->kv_capacity;
-  a.top_k = top_k;
-  a.scale = effective_scale(shape);
-  a.bf16 = shape->dtype == BSATTN_BF16;
+  const bsattn_status st = decode_args(shape, Q, K, V, sel, top_k, window, n_sink, global_pos_host, n_global,
+                                       O, lse, workspace, ws_bytes, a);
+  if (st != BSATTN_OK) return st;
   hipError_t e = bsattn::launch_decode(a, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return fail(BSATTN_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return BSATTN_OK;
+}
+
+bsattn_status bsattn_decode_step(const bsattn_shape* shape, const void* Q, const void* K, const void* V,
+                                 const float* mean, const float* factor, int32_t rank, int32_t nblk_capacity,
+                                 int32_t top_k, int32_t window, int32_t n_sink, const int32_t* global_pos_host,
+                                 int32_t n_global, int32_t* sel, float* scores, float* O, float* lse,
+                                 void* workspace, size_t ws_bytes, void* hip_stream) {
+  g_err[0] = 0;
+  bsattn::SelectArgs sa;
+  bsattn_status st = select_args(shape, Q, mean, factor, rank, nblk_capacity, top_k, window, n_sink,
+                                 global_pos_host, n_global, sel, scores, sa);
+  if (st != BSATTN_OK) return st;
+  bsattn::DecodeArgs da;
+  st = decode_args(shape, Q, K, V, sel, top_k, window, n_sink, global_pos_host, n_global, O, lse, workspace,
+                   ws_bytes, da);
+  if (st != BSATTN_OK) return st;
+  // bf16 with at most 2048 complete blocks and top_k <= 256: the decode waves
+  // select; otherwise the top-k kernel does, then the decode reads sel
+  const int nb = sa.n_blocks;
+  const bool fused = da.bf16 && nb >= 1 && nb <= bsattn::kFusedMaxBlocks && top_k <= bsattn::kFusedMaxTopK;
+  if (fused) {
+    sa.scores_only = true;
+    da.scores = scores;
+    da.nblk_capacity = nblk_capacity;
+    da.sel_out = sel;
+    da.key_slots = nb <= 64 * 8 ? 8 : 32;
+    for (int j = 0; j < nb; ++j)
+      if (bsattn::forced_mask(da.forced, j) == ~0ull) da.full_forced[j >> 6] |= 1ull << (j & 63);
+  }
+  hipError_t e = bsattn::launch_select_topk(sa, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return fail(BSATTN_ERR_HIP, "select launch: %s", hipGetErrorString(e));
+  e = bsattn::launch_decode(da, (hipStream_t)hip_stream);
   if (e != hipSuccess) return fail(BSATTN_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return BSATTN_OK;
 }

@@ -12,24 +12,33 @@
 //
 // Work items: per (b, K/V head) the list is the top_k selected blocks, then
 // the forced blocks (sink range, window range, blocks holding a global token).
+// A selected block contributes its tokens that are not forced, a forced block
+// its forced tokens, so no token is counted twice and no search of `sel` is
+// needed.
+//
+// Fused decode step (bf16): the top-k runs inside the decode waves.  Each
+// wave first loads its pair's group scores, then issues the loads of its
+// forced half items (which do not depend on the selection), and selects the
+// pair's top-k blocks (exact radix select, same keys and tie rule as the
+// top-k kernel) while those loads are in flight; its selected half items
+// follow.  Every wave of a pair computes the same selection; the pair's first
+// wave writes it out.
 //
 // bf16 path (MFMA, gfx950 v_mfma_f32_16x16x32_bf16): the unit is a half item
-// (32 tokens of one block).  A selected block contributes its tokens that are
-// not forced, a forced block its forced tokens, so no token is counted twice
-// and no search of `sel` is needed.  Each wave owns a run of half items of one
-// pair and pipelines them two deep (next half item's loads in flight while the
+// (32 tokens of one block).  Each wave owns a run of half items of one pair
+// and pipelines them two deep (next half item's loads in flight while the
 // current one is computed); waves are independent and write one partial each.
-//   V is copied HBM -> LDS with global_load_lds_dwordx4 (no registers), into
-//   a per-wave tile with XOR-swizzled 16-byte chunks; K goes straight from HBM
-//   into MFMA A-operand registers.
+//   K goes straight from HBM into MFMA A-operand registers; V is loaded with
+//   coalesced 1 KB instructions into registers and, at compute time, written
+//   to the wave's LDS tile (XOR-swizzled 16-byte chunks) and read back
+//   transposed.
 //   S^T = K Q^T: B = Q^T held in registers (16 query heads of the group, zero
 //   padded), so lane l holds the logits of query head l%16 for 8 tokens.
 //   O^T += V^T P^T: V^T read with ds_read_b64_tr_b16.  P = P_hi + P_lo in
 //   bf16 (two products), so the result keeps ~2^-17 of P's precision.  The
 //   output tile keeps query head l%16 in lane l, so the rescale is per lane.
-// fp32 path (VALU): one token per lane, one item per wave; a forced block that
-// is also selected is skipped there (the selected block covers it); the 4
-// waves of a workgroup merge in LDS into one partial.
+// fp32 path (VALU): one token per lane, one item per wave; the 4 waves of a
+// workgroup merge in LDS into one partial.
 //
 // With one partial per pair the kernel writes O and lse itself; otherwise a
 // small second kernel merges the partials (the kernel boundary makes every
@@ -47,30 +56,16 @@ struct ItemInfo {
   uint64_t mask;
 };
 
-// Number of leading non-negative entries of an ascending, -1-padded row.
-__device__ __forceinline__ int valid_prefix(const int32_t* sel, int k) {
-  int lo = 0, hi = k;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (sel[mid] >= 0) lo = mid + 1; else hi = mid;
-  }
-  return lo;
-}
-
-__device__ __forceinline__ bool in_sorted(const int32_t* a, int n, int x) {
-  const int i = lower_bound_i32(a, n, x);
-  return i < n && a[i] == x;
-}
-
-// Block and token mask of item `it`; blk < 0 means nothing to do.
-__device__ __forceinline__ ItemInfo item_info(const DecodeArgs& a, const int32_t* selrow, int nsel,
-                                              int it) {
+// Block and token mask of item `it` (a selected block: its tokens outside the
+// forced set; a forced block: its forced tokens); blk < 0 means nothing to do.
+__device__ __forceinline__ ItemInfo item_info(const DecodeArgs& a, const int32_t* selrow, int it) {
   ItemInfo r;
   if (it < a.top_k) {
     const int blk = selrow[it];
     // only complete blocks can be selected; anything else is ignored
-    r.blk = (blk >= 0 && blk < a.forced.n_ctx / kBlock) ? blk : -1;
-    r.mask = ~0ull;
+    const bool ok = blk >= 0 && blk < a.forced.n_ctx / kBlock;
+    r.mask = ok ? ~forced_mask(a.forced, blk) : 0ull;
+    r.blk = r.mask ? blk : -1;
     return r;
   }
   const int f = it - a.top_k;
@@ -79,10 +74,8 @@ __device__ __forceinline__ ItemInfo item_info(const DecodeArgs& a, const int32_t
   if (f < fb.r0_n) blk = fb.r0_lo + f;
   else if (f < fb.r0_n + fb.r1_n) blk = fb.r1_lo + (f - fb.r0_n);
   else blk = fb.gblk[f - fb.r0_n - fb.r1_n];
-  if (in_sorted(selrow, nsel, blk)) { r.blk = -1; r.mask = 0; return r; }
-  r.blk = blk;
   r.mask = forced_mask(a.forced, blk);
-  if (r.mask == 0ull) r.blk = -1;
+  r.blk = r.mask ? blk : -1;
   return r;
 }
 
@@ -172,26 +165,96 @@ struct Stage {
   uint32_t hmask;               // tokens of T among the 32 (0: nothing to do)
 };
 
-// Block and 64-token mask of item `it` of a pair.  Mask 0: nothing to do (the
-// block index is then 0, so the loads that are still issued stay in bounds).
-__device__ __forceinline__ void item_entry(const DecodeArgs& a, const int32_t* selrow, int it, int& blk,
-                                           uint64_t& mask) {
-  if (it < a.top_k) {
-    blk = selrow[it];
-    // only complete blocks can be selected; anything else is ignored
-    const bool ok = blk >= 0 && blk < a.forced.n_ctx / kBlock;
-    mask = ok ? ~forced_mask(a.forced, blk) : 0ull;
-  } else if (it < a.n_items) {
-    const int f = it - a.top_k;
-    const ForcedBlocks& fb = a.fblocks;
-    if (f < fb.r0_n) blk = fb.r0_lo + f;
-    else if (f < fb.r0_n + fb.r1_n) blk = fb.r1_lo + (f - fb.r0_n);
-    else blk = fb.gblk[f - fb.r0_n - fb.r1_n];
-    mask = forced_mask(a.forced, blk);
-  } else {
-    mask = 0ull;
-  }
+// Block and 64-token mask of the f-th forced item, and of a selected block.
+// Mask 0: nothing to do (the block index is then 0, so the loads that are
+// still issued stay in bounds).
+__device__ __forceinline__ void forced_item(const DecodeArgs& a, int f, int& blk, uint64_t& mask) {
+  const ForcedBlocks& fb = a.fblocks;
+  if (f < fb.r0_n) blk = fb.r0_lo + f;
+  else if (f < fb.r0_n + fb.r1_n) blk = fb.r1_lo + (f - fb.r0_n);
+  else blk = fb.gblk[f - fb.r0_n - fb.r1_n];
+  mask = forced_mask(a.forced, blk);
   if (mask == 0ull) blk = 0;
+}
+__device__ __forceinline__ void selected_item(const DecodeArgs& a, int sel_blk, int& blk, uint64_t& mask) {
+  // only complete blocks can be selected; anything else is ignored
+  const bool ok = sel_blk >= 0 && sel_blk < a.forced.n_ctx / kBlock;
+  mask = ok ? ~forced_mask(a.forced, sel_blk) : 0ull;
+  blk = mask ? sel_blk : 0;
+}
+
+// Exact top-k of one pair inside one wave.  Lane l holds the scores of blocks
+// 64t + l (t < PL), so (t, lane) order is block order.  Candidates: complete
+// blocks with a token outside the forced set; order: score descending, then
+// block index ascending.  A 4-pass radix select (8 bits a pass, 256-bin
+// histogram in this wave's LDS `hist`) finds the k-th largest key T and how
+// many keys equal to T are taken (the lowest-index ones); the selected blocks
+// go to tab[0 .. top_k) in ascending order, -1 after the last.
+template <int PL>
+__device__ __forceinline__ void wave_topk(const DecodeArgs& a, const float (&sv)[PL], uint32_t* hist, int32_t* tab) {
+  const int lane = threadIdx.x & 63;
+  const int NB = a.forced.n_ctx / kBlock;
+  uint32_t key[PL];
+  uint32_t cm = 0u;  // bit t: block 64t + lane is a candidate
+  int ncand = 0;
+#pragma unroll
+  for (int t = 0; t < PL; ++t) {
+    const int j = 64 * t + lane;
+    key[t] = order_key(sv[t]);
+    if (j < NB && !((a.full_forced[t] >> lane) & 1ull)) cm |= 1u << t;
+  }
+  ncand = wave_incl_scan(__popc(cm));
+  ncand = __shfl(ncand, 63);
+  const int kk = min(a.top_k, ncand);
+  uint32_t prefix = 0u, pmask = 0u;
+  int remaining = kk;
+  if (kk > 0) {
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      reinterpret_cast<u32x4*>(hist)[lane] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int t = 0; t < PL; ++t)
+        if (((cm >> t) & 1u) && (key[t] & pmask) == prefix) atomicAdd(&hist[(key[t] >> shift) & 255u], 1u);
+      // lane l reads digits 255-4l (c4[3]) down to 252-4l (c4[0])
+      const u32x4 c4 = reinterpret_cast<const u32x4*>(hist)[63 - lane];
+      const int sum = (int)(c4[0] + c4[1] + c4[2] + c4[3]);
+      int cum = wave_incl_scan(sum) - sum;
+      int found = -1, above = 0;
+#pragma unroll
+      for (int u = 3; u >= 0; --u) {
+        if (found < 0 && cum + (int)c4[u] >= remaining) {
+          found = 4 * (63 - lane) + u;
+          above = cum;
+        }
+        cum += (int)c4[u];
+      }
+      const uint64_t hit = __ballot(found >= 0);
+      const int src = __ffsll((unsigned long long)hit) - 1;
+      const int digit = __shfl(found, src), ab = __shfl(above, src);
+      remaining -= ab;
+      prefix |= (uint32_t)digit << shift;
+      pmask |= 255u << shift;
+    }
+  }
+  // keys > T, then the first `remaining` keys == T, in block order
+  int base = 0, eq_before = 0;
+  if (kk > 0) {
+#pragma unroll
+    for (int t = 0; t < PL; ++t) {
+      const bool c = (cm >> t) & 1u;
+      const bool eq = c && key[t] == prefix;
+      const uint64_t be = __ballot(eq);
+      const int er = eq_before + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32),
+                                                                __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0u));
+      const bool take = (c && key[t] > prefix) || (eq && er < remaining);
+      const uint64_t bt = __ballot(take);
+      const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bt >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)bt, 0u));
+      if (take) tab[pos] = 64 * t + lane;
+      base += __popcll(bt);
+      eq_before += __popcll(be);
+    }
+  }
+  for (int i = base + lane; i < a.top_k; i += 64) tab[i] = -1;
 }
 
 template <int D>
@@ -291,9 +354,16 @@ __device__ __forceinline__ void compute_half(const Stage<D>& st, uint8_t* vt, co
 
 // d = 128: two stages of K and V take 128 registers, so a wave gets the whole
 // 512-register budget of a SIMD (one workgroup of 4 waves per CU); d = 64 fits
-// two workgroups per CU.
-template <int D>
-__global__ __launch_bounds__(64 * kW, D == 128 ? 1 : 2) void decode_bf16_kernel(DecodeArgs a) {
+// two workgroups per CU.  PL > 0: fused step, PL scores per lane for the
+// in-wave top-k; PL = 0: the selection comes from `sel`.
+template <int D, int PL>
+__global__ __launch_bounds__(64 * kW, D == 128 ? 1 : 2) void decode_bf16_kernel(DecodeArgs args) {
+  // The arguments are read in place from the kernel-argument segment (the
+  // only explicit argument sits at its offset 0): per-lane lookups into the
+  // forced-token tables then stay plain constant-memory loads, where the
+  // by-value parameter could be copied to scratch first.
+  (void)args;
+  const DecodeArgs& a = *(const DecodeArgs*)__builtin_amdgcn_kernarg_segment_ptr();
   using H = HalfItem<D>;
   constexpr int DC = H::DC, DT = D / 16;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kW * H::TILE];
@@ -310,20 +380,41 @@ __global__ __launch_bounds__(64 * kW, D == 128 ? 1 : 2) void decode_bf16_kernel(
   const int h = lane & 15, grp = lane >> 4;
   uint8_t* const vt = smem + wid * H::TILE;
 
+  // fused step: the pair's group scores, loaded before anything else so the
+  // selection waits for them alone
+  float sv[PL > 0 ? PL : 1];
+  if constexpr (PL > 0) {
+    const float* sc = a.scores + (size_t)pair * a.nblk_capacity;
+    const int nb_last = a.forced.n_ctx / kBlock - 1;  // >= 0 on the fused path
+#pragma unroll
+    for (int t = 0; t < PL; ++t) sv[t] = sc[min(64 * t + lane, nb_last)];
+  }
+
   const uint16_t* Kb = reinterpret_cast<const uint16_t*>(a.K) + (size_t)pair * a.kv_capacity * D;
   const uint16_t* Vb = reinterpret_cast<const uint16_t*>(a.V) + (size_t)pair * a.kv_capacity * D;
   const int last = a.forced.n_ctx - 1;  // rows past the context (tail block) are masked; clamp loads
   const float sl2 = a.scale * kLog2e;
-  const int s0 = wi * a.per_wave;
-  const int s1 = min(s0 + a.per_wave, 2 * a.n_items);
-  const int it0 = s0 >> 1;
 
-  // Item table of this wave, one item per lane (at most 64 items per wave):
-  // lane j holds the block and token mask of item it0 + j.
-  int blkv;
-  uint64_t maskv;
-  item_entry(a, a.sel + (size_t)pair * a.top_k, it0 + lane, blkv, maskv);
-  const uint32_t mlo = (uint32_t)maskv, mhi = (uint32_t)(maskv >> 32);
+  // This wave's half items (32 tokens each): forced halves [f0, f1) of the
+  // pair's forced items, then selected halves [s0, s1) of its selected items.
+  const int nf2 = 2 * (a.n_items - a.top_k), ns2 = 2 * a.top_k;
+  const int f0 = min(wi * a.fh_per_wave, nf2), f1 = min(f0 + a.fh_per_wave, nf2);
+  const int s0 = min(wi * a.sh_per_wave, ns2), s1 = min(s0 + a.sh_per_wave, ns2);
+  const int nfh = f1 - f0, n = nfh + (s1 - s0);
+  const int fi0 = f0 >> 1, si0 = s0 >> 1;
+  const int nfi = nfh > 0 ? ((f1 - 1) >> 1) - fi0 + 1 : 0;
+
+  // Item table, one item per lane: lane j < nfi holds forced item fi0 + j,
+  // lane nfi + j selected item si0 + j (at most 64 items per wave).
+  int blkv = 0;
+  uint64_t maskv = 0ull;
+  if (lane < nfi) forced_item(a, fi0 + lane, blkv, maskv);
+  auto selected_entries = [&](const int32_t* selrow) {
+    const int it = si0 + lane - nfi;
+    if (lane >= nfi && it < a.top_k && s1 > s0) selected_item(a, selrow[it], blkv, maskv);
+  };
+  if constexpr (PL == 0) selected_entries(a.sel + (size_t)pair * a.top_k);
+  uint32_t mlo = (uint32_t)maskv, mhi = (uint32_t)(maskv >> 32);
 
   // Q^T operand: lane (h, grp) holds Q[h][32dc + 8grp .. +8] (zero rows past G)
   u32x4 qop[DC];
@@ -338,33 +429,72 @@ __global__ __launch_bounds__(64 * kW, D == 128 ? 1 : 2) void decode_bf16_kernel(
 #pragma unroll
   for (int t = 0; t < DT; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Two stages in flight over half items s0 .. s1-1 (stage A: even steps, B:
+  // Two stages in flight over the wave's half items (stage A: even steps, B:
   // odd).  Loads are issued for every half item (an empty one loads block 0
   // and skips the compute), and every path is written out, so the compiler's
   // waits on the stage registers count exactly the loads issued after them.
   Stage<D> A, B;
-  auto load = [&](int s, Stage<D>& st) {
-    const int j = (s >> 1) - it0;
+  auto load = [&](int hh, Stage<D>& st) {
+    int j, odd;
+    if (hh < nfh) {
+      const int x = f0 + hh;
+      j = (x >> 1) - fi0;
+      odd = x & 1;
+    } else {
+      const int x = s0 + (hh - nfh);
+      j = nfi + (x >> 1) - si0;
+      odd = x & 1;
+    }
     const int blk = __builtin_amdgcn_readlane(blkv, j);
-    st.hmask = (s & 1) ? __builtin_amdgcn_readlane(mhi, j) : __builtin_amdgcn_readlane(mlo, j);
-    load_half<D>(Kb, Vb, blk * kBlock + 32 * (s & 1), last, st);
+    st.hmask = odd ? __builtin_amdgcn_readlane(mhi, j) : __builtin_amdgcn_readlane(mlo, j);
+    load_half<D>(Kb, Vb, blk * kBlock + 32 * odd, last, st);
   };
   auto comp = [&](const Stage<D>& st) {
     if (st.hmask) compute_half<D>(st, vt, qop, sl2, m_run, l_run, oacc);
   };
+  // fused step: select the pair's blocks (table in this wave's V tile, which
+  // the first compute overwrites), write them out from the pair's first wave
+  // and fill the selected half of the item table
+  auto select = [&]() __attribute__((always_inline)) {
+    if constexpr (PL > 0) {
+      int32_t* tab = reinterpret_cast<int32_t*>(vt + 1024);
+      wave_topk<PL>(a, sv, reinterpret_cast<uint32_t*>(vt), tab);
+      if (wi == 0)
+        for (int i = lane; i < a.top_k; i += 64) a.sel_out[(size_t)pair * a.top_k + i] = tab[i];
+      selected_entries(tab);
+      mlo = (uint32_t)maskv;
+      mhi = (uint32_t)(maskv >> 32);
+    }
+  };
+  // the first two loads, with the selection after them when both are forced
+  // half items (so it overlaps their latency), before them otherwise
+  auto prologue2 = [&]() __attribute__((always_inline)) {
+    if constexpr (PL > 0) {
+      if (nfh >= 2) {
+        load(0, A);
+        load(1, B);
+        select();
+      } else {
+        select();
+        load(0, A);
+        load(1, B);
+      }
+    } else {
+      load(0, A);
+      load(1, B);
+    }
+  };
 
-  const int n = s1 - s0;
   if (n >= 4) {
-    load(s0, A);
-    load(s0 + 1, B);
-    int s = s0;
-    for (; s + 3 < s1; s += 2) {
+    prologue2();
+    int s = 0;
+    for (; s + 3 < n; s += 2) {
       comp(A);
       load(s + 2, A);
       comp(B);
       load(s + 3, B);
     }
-    if (s + 2 < s1) {  // three left: s (A), s + 1 (B), s + 2
+    if (s + 2 < n) {  // three left: s (A), s + 1 (B), s + 2
       comp(A);
       load(s + 2, A);
       comp(B);
@@ -374,20 +504,30 @@ __global__ __launch_bounds__(64 * kW, D == 128 ? 1 : 2) void decode_bf16_kernel(
       comp(B);
     }
   } else if (n == 3) {
-    load(s0, A);
-    load(s0 + 1, B);
+    prologue2();
     comp(A);
-    load(s0 + 2, A);
+    load(2, A);
     comp(B);
     comp(A);
   } else if (n == 2) {
-    load(s0, A);
-    load(s0 + 1, B);
+    prologue2();
     comp(A);
     comp(B);
   } else if (n == 1) {
-    load(s0, A);
+    if constexpr (PL > 0) {
+      if (nfh == 1) {
+        load(0, A);
+        select();
+      } else {
+        select();
+        load(0, A);
+      }
+    } else {
+      load(0, A);
+    }
     comp(A);
+  } else {
+    select();  // nothing to attend; the pair's first wave still writes the selection
   }
 
   l_run += __shfl_xor(l_run, 16);
@@ -433,7 +573,6 @@ __global__ __launch_bounds__(64 * kW) void decode_f32_kernel(DecodeArgs a) {
     qs[i / D][i % D] =
         (i / D < G) ? reinterpret_cast<const float*>(a.Q)[((size_t)b * a.n_q_heads + g * G) * D + i] : 0.f;
   __syncthreads();
-  const int nsel = valid_prefix(s_sel, a.top_k);
   float m_run[GM], l_run[GM], o[GM][DL];
 #pragma unroll
   for (int hh = 0; hh < GM; ++hh) {
@@ -445,7 +584,7 @@ __global__ __launch_bounds__(64 * kW) void decode_f32_kernel(DecodeArgs a) {
   const int it0 = (blockIdx.x * kW + wid) * a.per_wave;
   const int it1 = min(it0 + a.per_wave, a.n_items);
   for (int it = it0; it < it1; ++it) {
-    const ItemInfo inf = item_info(a, s_sel, nsel, it);
+    const ItemInfo inf = item_info(a, s_sel, it);
     if (inf.blk < 0) continue;
     const size_t tok = (size_t)inf.blk * kBlock + lane;
     const bool on = (inf.mask >> lane) & 1ull;
@@ -557,8 +696,10 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   const int G = a.n_q_heads / a.n_kv_heads;
   if (a.bf16) {
     const long long waves = (long long)n_pairs * a.n_part;
-    hipLaunchKernelGGL((decode_bf16_kernel<D>), dim3((unsigned)((waves + kW - 1) / kW)), dim3(64 * kW), 0,
-                       stream, a);
+    const dim3 grid((unsigned)((waves + kW - 1) / kW)), block(64 * kW);
+    if (a.key_slots == 0) hipLaunchKernelGGL((decode_bf16_kernel<D, 0>), grid, block, 0, stream, a);
+    else if (a.key_slots <= 8) hipLaunchKernelGGL((decode_bf16_kernel<D, 8>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((decode_bf16_kernel<D, 32>), grid, block, 0, stream, a);
   } else {
     const dim3 grid(a.n_part, n_pairs);
     if (G <= 4)
@@ -576,29 +717,31 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-// bf16: each wave takes `per_wave` consecutive half items (32 tokens) of one
-// pair, with as few half items per wave as keeps every wave resident at once
-// (decode_slots(d) waves).  fp32: one whole item per wave, 4 waves per
-// workgroup merged in LDS, one partial per workgroup.
-void decode_split_geometry(int n_items, int n_pairs, int head_dim, bool bf16, int* per_wave, int* n_part) {
-  const int slots = decode_slots(head_dim);
+// bf16: `half_items` = c, the fewest half items (32 tokens) per wave that keep
+// every wave resident at once (decode_slots(d) waves); n_part = ceil(2 n_items
+// / c) waves per pair.  The caller gives each wave ceil(2 forced / n_part)
+// forced and ceil(2 top_k / n_part) selected half items, at most c + 2 half
+// items spanning at most c / 2 + 3 items, so c <= 120 keeps a wave's items
+// within one per lane.  fp32: one whole item per wave, 4 waves per workgroup
+// merged in LDS, one partial per workgroup.
+void decode_split_geometry(int n_items, int n_pairs, int head_dim, bool bf16, int* half_items, int* n_part) {
   if (n_items <= 0 || n_pairs <= 0) {
-    *per_wave = 1;
+    *half_items = 1;
     *n_part = 1;
     return;
   }
   if (!bf16) {
-    *per_wave = 1;
+    *half_items = 1;
     *n_part = (n_items + kW - 1) / kW;
     return;
   }
+  const int slots = decode_slots(head_dim);
   const long long n_sub = 2LL * n_items;
   long long c = (n_pairs * n_sub + slots - 1) / slots;
   if (c < 1) c = 1;
   while (c < n_sub && (long long)n_pairs * ((n_sub + c - 1) / c) > slots) ++c;
-  // a wave's items must fit one per lane: 126 half items span at most 64 items
-  if (c > 126) c = 126;
-  *per_wave = (int)c;
+  if (c > 120) c = 120;
+  *half_items = (int)c;
   *n_part = (int)((n_sub + c - 1) / c);
 }
 

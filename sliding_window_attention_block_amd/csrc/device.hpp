@@ -99,15 +99,32 @@ struct ForcedSet {
 };
 
 // 64-bit mask of `lo <= token < hi` within block [base, base + 64).
-__device__ __forceinline__ uint64_t range_mask64(int base, int lo, int hi) {
-  int a = max(lo - base, 0), b = min(hi - base, 64);
+__host__ __device__ inline uint64_t range_mask64(int base, int lo, int hi) {
+  const int a = lo - base > 0 ? lo - base : 0, b = hi - base < 64 ? hi - base : 64;
   if (a >= b) return 0ull;
   uint64_t hiMask = (b == 64) ? ~0ull : ((1ull << b) - 1ull);
   uint64_t loMask = (a == 0) ? 0ull : ((1ull << a) - 1ull);
   return hiMask & ~loMask;
 }
 
-__device__ __forceinline__ int lower_bound_i32(const int32_t* a, int n, int x) {
+// Order-preserving 32-bit key of a float: larger float, larger unsigned key.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+__host__ __device__ inline int lower_bound_i32(const int32_t* a, int n, int x) {
   int lo = 0, hi = n;
   while (lo < hi) {
     int mid = (lo + hi) >> 1;
@@ -117,7 +134,7 @@ __device__ __forceinline__ int lower_bound_i32(const int32_t* a, int n, int x) {
 }
 
 // Forced tokens of block `blk`, restricted to tokens < n_ctx.
-__device__ __forceinline__ uint64_t forced_mask(const ForcedSet& f, int blk) {
+__host__ __device__ inline uint64_t forced_mask(const ForcedSet& f, int blk) {
   const int base = blk * kBlock;
   uint64_t m = range_mask64(base, 0, f.sink_end) | range_mask64(base, f.win_lo, f.n_ctx);
   if (f.n_global > 0) {

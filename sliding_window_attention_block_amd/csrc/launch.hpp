@@ -42,6 +42,7 @@ struct SelectArgs {
   // scoring split, set by the launcher: each wave scores `per_wave` units (of
   // 4 * PB blocks) of one pair; `n_part` waves per pair
   int32_t per_wave, n_part;
+  bool scores_only;  // skip the top-k launch (the fused decode step selects)
 };
 hipError_t launch_select_topk(const SelectArgs& a, hipStream_t stream);
 
@@ -55,6 +56,11 @@ struct ForcedBlocks {
   int32_t gblk[256];
 };
 
+// Fused decode step limits: scores held in registers (at most 32 per lane) and
+// the selection table in the wave's V tile.
+constexpr int kFusedMaxBlocks = 64 * 32;
+constexpr int kFusedMaxTopK = 256;
+
 struct DecodeArgs {
   const void* Q;
   const void* K;
@@ -67,20 +73,33 @@ struct DecodeArgs {
   int32_t batch, n_q_heads, n_kv_heads, head_dim;
   int32_t kv_capacity;
   int32_t top_k;
-  int32_t n_items;        // top_k + forced blocks
-  int32_t per_wave;       // work units per wave (bf16: half items; fp32: items)
+  int32_t n_items;        // top_k + forced blocks: a pair's item list (selected first)
+  int32_t per_wave;       // fp32: items per wave
+  int32_t fh_per_wave;    // bf16: forced half items per wave
+  int32_t sh_per_wave;    // bf16: selected half items per wave
   int32_t n_part;         // partials per (b, K/V head): bf16 waves, fp32 workgroups
+  // fused step (bf16): each wave selects its pair's top-k blocks itself from
+  // the group scores instead of reading `sel`; the first wave of a pair writes
+  // the selection to sel_out.  key_slots: scores per lane (0: not fused).
+  const float* scores;
+  int32_t nblk_capacity;
+  int32_t* sel_out;
+  int32_t key_slots;
+  uint64_t full_forced[kFusedMaxBlocks / 64];  // bit j % 64 of word j / 64: complete block j has no candidate token
   float scale;
   bool bf16;
   ForcedSet forced;
   ForcedBlocks fblocks;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
-// Split geometry the decode launch uses (also sizes the workspace).
-void decode_split_geometry(int n_items, int n_pairs, int head_dim, bool bf16, int* per_wave, int* n_part);
+// Split geometry of the decode launch (also sizes the workspace).  bf16: at most
+// `half_items` half items per wave and `n_part` waves per pair; fp32: one item
+// per wave, `n_part` workgroups per pair.
+void decode_split_geometry(int n_items, int n_pairs, int head_dim, bool bf16, int* half_items, int* n_part);
 constexpr int kDecodeWaves = 4;  // waves per decode workgroup
 // bf16 decode waves resident at once on 256 CUs: 4 per CU at d = 128, 8 at d = 64
 constexpr int decode_slots(int head_dim) { return head_dim == 128 ? 1024 : 2048; }
+
 constexpr float kDecodeHeadroom = 8.f;  // log2 units a running max may lag the true max
 
 struct PrefillArgs {

@@ -196,22 +196,6 @@ __global__ __launch_bounds__(256, scores_heavy(GM, RM, PB, D) ? 1 : 2) void sele
   }
 }
 
-__device__ __forceinline__ uint32_t order_key(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Inclusive prefix sum across the 64 lanes of a wave.
-__device__ __forceinline__ int wave_incl_scan(int x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  return x;
-}
-
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
 
@@ -348,6 +332,7 @@ hipError_t launch_t(const SelectArgs& a0, hipStream_t stream) {
     hipLaunchKernelGGL((select_scores_kernel<D, GM, RM, PB, BF16>), dim3((unsigned)((waves + 3) / 4)),
                        dim3(256), 0, stream, a);
   }
+  if (a.scores_only) return hipGetLastError();
   const int per = (a.n_blocks + kTopkThreads - 1) / kTopkThreads;
   const dim3 tg(n_pairs), tb(kTopkThreads);
   if (per <= 2) hipLaunchKernelGGL(topk_kernel<2>, tg, tb, 0, stream, a);

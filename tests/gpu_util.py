@@ -32,10 +32,13 @@ def as_f64(arr):
     return (bf16_bits_to_f32(arr) if arr.dtype == np.uint16 else np.asarray(arr, np.float32)).astype(np.float64)
 
 
-def gpu_decode_step(api, x, w, kv_capacity=None, nblk_capacity=None, global_pos=(), dev=None):
+def gpu_decode_step(api, x, w, kv_capacity=None, nblk_capacity=None, global_pos=(), dev=None,
+                    one_call=False):
     """Run summaries -> select/top-k -> decode on the GPU through the binding.
 
     ``x`` holds Q, K, V numpy arrays (float32 or bf16 bits) of workload ``w``.
+    With ``one_call`` the step is bsattn_decode_step (selection and decode in one
+    call); otherwise bsattn_select_topk, then bsattn_decode.
     Returns numpy copies of mean, factor, scores, sel, O, lse.
     """
     torch = torch_mod()
@@ -54,14 +57,18 @@ def gpu_decode_step(api, x, w, kv_capacity=None, nblk_capacity=None, global_pos=
     api.bsattn_build_summaries(shape, K, w.rank, 0, nb, max(nbcap, 1), mean, factor)
     scores = torch.full((B, Hkv, max(nbcap, 1)), float("nan"), device="cuda")
     sel = torch.full((B, Hkv, w.top_k), -7, dtype=torch.int32, device="cuda")
-    api.bsattn_select_topk(shape, Q, mean, factor, w.rank, max(nbcap, 1), w.top_k, w.window,
-                           w.n_sink, list(global_pos), sel, scores)
-    ws = torch.zeros(api.bsattn_decode_workspace_bytes(shape, w.top_k, w.window, w.n_sink,
-                                                       len(global_pos)), dtype=torch.uint8,
-                     device="cuda")
     O = torch.full((B, Hq, d), float("nan"), device="cuda")
     lse = torch.full((B, Hq), float("nan"), device="cuda")
-    api.bsattn_decode(shape, Q, K, V, sel, w.top_k, w.window, w.n_sink, list(global_pos), O, lse, ws)
+    gp = list(global_pos)
+    nbytes = api.bsattn_decode_workspace_bytes(shape, w.top_k, w.window, w.n_sink, len(gp))
+    ws = torch.full((nbytes,), 255, dtype=torch.uint8, device="cuda")  # garbage contents
+    if one_call:
+        api.bsattn_decode_step(shape, Q, K, V, mean, factor, w.rank, max(nbcap, 1), w.top_k, w.window,
+                               w.n_sink, gp, sel, scores, O, lse, ws)
+    else:
+        api.bsattn_select_topk(shape, Q, mean, factor, w.rank, max(nbcap, 1), w.top_k, w.window,
+                               w.n_sink, gp, sel, scores)
+        api.bsattn_decode(shape, Q, K, V, sel, w.top_k, w.window, w.n_sink, gp, O, lse, ws)
     torch.cuda.synchronize()
     return dict(mean=mean.cpu().numpy(), factor=None if factor is None else factor.cpu().numpy(),
                 scores=scores.cpu().numpy(), sel=sel.cpu().numpy(), O=O.cpu().numpy(),

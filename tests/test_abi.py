@@ -24,7 +24,7 @@ def _header_functions():
 def test_library_exports_every_declared_function():
     lib = api.library()
     declared = _header_functions()
-    assert len(declared) == 9
+    assert len(declared) == 10
     for name in declared:
         assert hasattr(lib, name), name
     assert set(declared) == set(_lib.EXPORTS)
@@ -52,6 +52,16 @@ def test_workspace_size_matches_split_layout():
     assert api.bsattn_decode_workspace_bytes(small, 2, 500, 10, 0) > 0
     assert api.bsattn_decode_workspace_bytes(small, 0, 10, 10, 0) == 0
     assert api.bsattn_decode_workspace_bytes(api.make_shape(1, 3, 2, 64, 10), 1, 1, 1, 0) == 0
+
+
+def test_workspace_covers_globals_sharing_blocks():
+    """Global tokens that share a block (or sit in the window) give fewer forced items
+    than the bound; the size query covers every count, so such calls pass the check."""
+    s = _shape(n_ctx=4096, kv_capacity=4096)
+    lib = api.library()
+    full = lib.bsattn_decode_workspace_bytes(s, 4, 64, 0, 3)
+    for extra in range(4):
+        assert full >= lib.bsattn_decode_workspace_bytes(s, 4, 64, 0, extra)
 
 
 def _status(fn, *args):
@@ -100,6 +110,29 @@ def test_decode_rejects_bad_arguments():
     st, _ = _status("bsattn_decode", *args[:12], FAKE + 16, 1 << 30, None)  # misaligned workspace
     assert st == 1
     st, _ = _status("bsattn_decode", s, FAKE + 4, *args[2:])             # misaligned Q
+    assert st == 1
+
+
+def test_decode_step_rejects_bad_arguments():
+    s = _shape()
+    # shape Q K V mean factor rank nblk top_k window n_sink gpos n_global sel scores O lse ws ws_bytes stream
+    args = [s, FAKE, FAKE, FAKE, FAKE, None, 0, 4, 2, 64, 0, None, 0, FAKE, FAKE, FAKE, None, FAKE,
+            1 << 30, None]
+    st, _ = _status("bsattn_decode_step", *args[:4], None, *args[5:])          # NULL mean
+    assert st == 1
+    st, _ = _status("bsattn_decode_step", *args[:6], 1, *args[7:])             # rank 1, NULL factor
+    assert st == 1
+    st, _ = _status("bsattn_decode_step", *args[:7], 3, *args[8:])             # nblk_capacity < 4 blocks
+    assert st == 1
+    st, _ = _status("bsattn_decode_step", *args[:8], 0, *args[9:])             # top_k 0
+    assert st == 1
+    st, _ = _status("bsattn_decode_step", *args[:13], None, *args[14:])        # NULL sel
+    assert st == 1
+    st, _ = _status("bsattn_decode_step", *args[:15], None, *args[16:])        # NULL O
+    assert st == 1
+    st, msg = _status("bsattn_decode_step", *args[:18], 16, None)              # workspace too small
+    assert st == 4 and "workspace" in msg
+    st, _ = _status("bsattn_decode_step", *args[:3], FAKE + 4, *args[4:])      # misaligned V
     assert st == 1
 
 

@@ -48,10 +48,10 @@ SMALL = [
 ]
 
 
-def _check_case(api, w, globals_, extra_cap):
+def _check_case(api, w, globals_, extra_cap, one_call=False):
     x = make_decode_inputs(w, kv_capacity=w.n_ctx + extra_cap)
-    print(f"[decode parity] {w.name}", flush=True)
-    got = gpu_decode_step(api, x, w, global_pos=globals_)
+    print(f"[decode parity] {w.name} one_call={one_call}", flush=True)
+    got = gpu_decode_step(api, x, w, global_pos=globals_, one_call=one_call)
     Q, K, V = as_f64(x["Q"]), as_f64(x["K"]), as_f64(x["V"])
     S, n, G, d = w.block_size, w.n_ctx, w.n_q_heads // w.n_kv_heads, w.head_dim
     scale = default_scale(d)
@@ -96,6 +96,56 @@ def _check_case(api, w, globals_, extra_cap):
 def test_decode_small_cases(api, case):
     w, globals_, extra = case
     _check_case(api, w, globals_, extra)
+
+
+NO_FORCED = _w("no_forced_tokens", 2, 8, 2, 128, 1200, 0, 4, 0, 0, "bf16", 19)
+# bsattn_decode_step selects inside the decode waves for bf16 with <= 2048 blocks and
+# top_k <= 256 (32 scores per lane from 513 blocks up), else it runs the two calls' kernels
+ONE_CALL_EXTRA = [
+    (NO_FORCED, (), 0),
+    (_w("fused_1500_blocks_g8_d64", 1, 8, 1, 64, 1500 * 64 + 17, 2, 20, 700, 64, "bf16", 25), (5, 64, 65), 0),
+    (_w("fused_2048_blocks_k256", 1, 4, 1, 128, 2048 * 64, 0, 256, 64, 64, "bf16", 26), (), 0),
+    (_w("fallback_2049_blocks", 1, 4, 1, 64, 2049 * 64, 0, 8, 64, 64, "bf16", 28), (), 0),
+    (_w("fallback_k257", 1, 4, 1, 64, 600 * 64, 0, 257, 64, 64, "bf16", 29), (), 0),
+]
+
+
+@pytest.mark.parametrize("case", SMALL + ONE_CALL_EXTRA,
+                         ids=[c[0].name for c in SMALL + ONE_CALL_EXTRA])
+def test_one_call_step_small_cases(api, case):
+    """bsattn_decode_step: the same oracle bar as the two calls, on every small case."""
+    w, globals_, extra = case
+    _check_case(api, w, globals_, extra, one_call=True)
+
+
+def test_one_call_step_breaks_ties_by_index(api):
+    """Every block holds the same keys, so every candidate's score ties exactly: both
+    selection paths must take the lowest-index candidates (the sink block is forced)."""
+    w = _w("all_ties", 1, 4, 1, 64, 64 * 300, 0, 7, 64, 64, "bf16", 27)
+    x = make_decode_inputs(w)
+    K = x["K"].copy()
+    K[:, :, :] = np.tile(K[:, :, :64], (1, 1, 300, 1))
+    x = dict(x, K=K)
+    two = gpu_decode_step(api, x, w)
+    one = gpu_decode_step(api, x, w, one_call=True)
+    assert np.array_equal(one["sel"][0, 0], np.arange(1, 8)), one["sel"][0, 0]
+    assert np.array_equal(two["sel"], one["sel"])
+    assert max_abs(two["O"], one["O"]) < 1e-5
+
+
+@pytest.mark.parametrize("name", ["first_order_decode_32k", "cobs_decode_128k"])
+def test_one_call_step_equals_two_calls(api, name):
+    """Full-size workloads: bsattn_decode_step selects exactly the blocks of
+    bsattn_select_topk and gives the decode's outputs up to rounding order."""
+    w = WORKLOADS[name]
+    x = make_decode_inputs(w)
+    print(f"[decode one call vs two] {name}", flush=True)
+    two = gpu_decode_step(api, x, w)
+    one = gpu_decode_step(api, x, w, one_call=True)
+    assert np.array_equal(two["sel"], one["sel"])
+    assert np.array_equal(two["scores"], one["scores"])
+    assert max_abs(two["O"], one["O"]) < 1e-5
+    assert max_abs(two["lse"], one["lse"]) < 1e-5
 
 
 def test_tiny_decode_workload(api):

@@ -100,3 +100,46 @@ def test_local_global_prefill_replays_bit_exactly(torch_api):
             assert np.array_equal(got.cpu().numpy(), want), f"replay {rep}"
         run()
         torch.cuda.synchronize()
+
+
+def test_one_call_decode_step_replays_bit_exactly(torch_api):
+    """bsattn_decode_step (scores, then the decode kernel that selects in its waves,
+    then the merge) captured as one graph."""
+    torch, api = torch_api
+    w = DecodeWorkload(name="graph_one_call", batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128,
+                       n_ctx=5000, block_size=64, rank=0, top_k=5, window=300, n_sink=64,
+                       dtype="bf16", seed=43)
+    x = make_decode_inputs(w)
+    Q, K, V = _dev(torch, x["Q"]), _dev(torch, x["K"]), _dev(torch, x["V"])
+    B, Hq, Hkv, d, n, nb = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_ctx, w.n_ctx // 64
+    shape = api.make_shape(B, Hq, Hkv, d, n)
+    mean = torch.empty((B, Hkv, nb, d), device="cuda")
+    api.bsattn_build_summaries(shape, K, 0, 0, nb, nb, mean, None)
+    scores = torch.empty((B, Hkv, nb), device="cuda")
+    sel = torch.empty((B, Hkv, w.top_k), dtype=torch.int32, device="cuda")
+    ws = torch.empty(api.bsattn_decode_workspace_bytes(shape, w.top_k, w.window, w.n_sink, 0),
+                     dtype=torch.uint8, device="cuda")
+    O = torch.empty((B, Hq, d), device="cuda")
+    lse = torch.empty((B, Hq), device="cuda")
+
+    def step():
+        api.bsattn_decode_step(shape, Q, K, V, mean, None, 0, nb, w.top_k, w.window, w.n_sink, None,
+                               sel, scores, O, lse, ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.cpu().numpy().copy() for t in (sel, O, lse)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for t in (O, lse):
+            t.fill_(float("nan"))
+        sel.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((sel, O, lse), ref):
+            assert np.array_equal(got.cpu().numpy(), want), f"replay {rep}"
+        step()
+        torch.cuda.synchronize()
