@@ -186,9 +186,10 @@ __device__ __forceinline__ void selected_item(const DecodeArgs& a, int sel_blk, 
 // Exact top-k of one pair inside one wave.  Lane l holds the scores of blocks
 // 64t + l (t < PL), so (t, lane) order is block order.  Candidates: complete
 // blocks with a token outside the forced set; order: score descending, then
-// block index ascending.  A 4-pass radix select (8 bits a pass, 256-bin
-// histogram in this wave's LDS `hist`) finds the k-th largest key T and how
-// many keys equal to T are taken (the lowest-index ones); the selected blocks
+// block index ascending.  A radix select (8 bits a pass, 256-bin histogram in
+// this wave's LDS `hist`) finds the k-th largest key T and how many keys equal
+// to T are taken (the lowest-index ones); bytes that every candidate key
+// shares are known from the wave's AND / OR and skipped.  The selected blocks
 // go to tab[0 .. top_k) in ascending order, -1 after the last.
 template <int PL>
 __device__ __forceinline__ void wave_topk(const DecodeArgs& a, const float (&sv)[PL], uint32_t* hist, int32_t* tab) {
@@ -196,20 +197,29 @@ __device__ __forceinline__ void wave_topk(const DecodeArgs& a, const float (&sv)
   const int NB = a.forced.n_ctx / kBlock;
   uint32_t key[PL];
   uint32_t cm = 0u;  // bit t: block 64t + lane is a candidate
-  int ncand = 0;
+  uint32_t kand = ~0u, kor = 0u;
 #pragma unroll
   for (int t = 0; t < PL; ++t) {
     const int j = 64 * t + lane;
     key[t] = order_key(sv[t]);
-    if (j < NB && !((a.full_forced[t] >> lane) & 1ull)) cm |= 1u << t;
+    if (j < NB && !((a.full_forced[t] >> lane) & 1ull)) {
+      cm |= 1u << t;
+      kand &= key[t];
+      kor |= key[t];
+    }
   }
-  ncand = wave_incl_scan(__popc(cm));
-  ncand = __shfl(ncand, 63);
+  const int ncand = __builtin_amdgcn_readlane(wave_incl_scan_dpp(__popc(cm)), 63);
   const int kk = min(a.top_k, ncand);
-  uint32_t prefix = 0u, pmask = 0u;
+  uint32_t all_and, all_or;
+  wave_and_or(kand, kor, all_and, all_or);  // (all ones / zero when there is no candidate)
+  const uint32_t diff = all_and ^ all_or;
+  // first pass: the byte holding the highest bit on which candidate keys differ
+  const int top = diff ? (31 - __clz(diff)) & ~7 : -8;
+  uint32_t pmask = top >= 24 ? 0u : ~0u << (top + 8);
+  uint32_t prefix = all_and & pmask;
   int remaining = kk;
   if (kk > 0) {
-    for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int shift = top; shift >= 0; shift -= 8) {
       reinterpret_cast<u32x4*>(hist)[lane] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int t = 0; t < PL; ++t)
@@ -217,39 +227,43 @@ __device__ __forceinline__ void wave_topk(const DecodeArgs& a, const float (&sv)
       // lane l reads digits 255-4l (c4[3]) down to 252-4l (c4[0])
       const u32x4 c4 = reinterpret_cast<const u32x4*>(hist)[63 - lane];
       const int sum = (int)(c4[0] + c4[1] + c4[2] + c4[3]);
-      int cum = wave_incl_scan(sum) - sum;
-      int found = -1, above = 0;
+      int cum = wave_incl_scan_dpp(sum) - sum;
+      int found = -1, above = 0, inbin = 0;
 #pragma unroll
       for (int u = 3; u >= 0; --u) {
         if (found < 0 && cum + (int)c4[u] >= remaining) {
           found = 4 * (63 - lane) + u;
           above = cum;
+          inbin = (int)c4[u];
         }
         cum += (int)c4[u];
       }
       const uint64_t hit = __ballot(found >= 0);
-      const int src = __ffsll((unsigned long long)hit) - 1;
-      const int digit = __shfl(found, src), ab = __shfl(above, src);
-      remaining -= ab;
+      const int src = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
+      const int digit = __builtin_amdgcn_readlane(found, src);
+      remaining -= __builtin_amdgcn_readlane(above, src);
       prefix |= (uint32_t)digit << shift;
       pmask |= 255u << shift;
+      // every key of the bin is taken: the lower bytes do not matter
+      if (__builtin_amdgcn_readlane(inbin, src) == remaining) break;
     }
   }
-  // keys > T, then the first `remaining` keys == T, in block order
+  // keys above the prefix, then the first `remaining` keys on it, in block order
   int base = 0, eq_before = 0;
   if (kk > 0) {
 #pragma unroll
     for (int t = 0; t < PL; ++t) {
       const bool c = (cm >> t) & 1u;
-      const bool eq = c && key[t] == prefix;
+      const uint32_t km = key[t] & pmask;
+      const bool eq = c && km == prefix;
       const uint64_t be = __ballot(eq);
       const int er = eq_before + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32),
                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0u));
-      const bool take = (c && key[t] > prefix) || (eq && er < remaining);
+      const bool take = (c && km > prefix) || (eq && er < remaining);
       const uint64_t bt = __ballot(take);
       const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bt >> 32),
                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)bt, 0u));
-      if (take) tab[pos] = 64 * t + lane;
+      if (take && pos < a.top_k) tab[pos] = 64 * t + lane;
       base += __popcll(bt);
       eq_before += __popcll(be);
     }

@@ -107,10 +107,43 @@ __host__ __device__ inline uint64_t range_mask64(int base, int lo, int hi) {
   return hiMask & ~loMask;
 }
 
-// Order-preserving 32-bit key of a float: larger float, larger unsigned key.
+// Order-preserving 32-bit key of a float: larger float, larger unsigned key
+// (-0 and +0 share the key of +0, as they compare equal).
 __device__ __forceinline__ uint32_t order_key(float f) {
-  const uint32_t u = __float_as_uint(f);
+  const uint32_t u = f == 0.f ? 0u : __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inclusive prefix sum across the 64 lanes of a wave with DPP: shifts of 1, 2,
+// 4, 8 within each 16-lane row, then lane 15 of rows 0 / 2 added to rows 1 / 3
+// (row_bcast:15) and lane 31 to rows 2 and 3 (row_bcast:31).  Lanes whose
+// source is outside the row or the row mask take `old` = 0.
+__device__ __forceinline__ int wave_incl_scan_dpp(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
+// Bitwise AND of x_and and OR of x_or over the 64 lanes (wave-uniform results).
+__device__ __forceinline__ void wave_and_or(uint32_t x_and, uint32_t x_or, uint32_t& all_and, uint32_t& all_or) {
+  uint32_t a = x_and, o = x_or;
+  // row_ror 8, 4, 2, 1: every lane of a row ends with the row's value
+#define BSATTN_AND_OR_STEP(c)                                                  \
+  a &= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, c, 0xf, 0xf, false); \
+  o |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)o, c, 0xf, 0xf, false);
+  BSATTN_AND_OR_STEP(0x128)
+  BSATTN_AND_OR_STEP(0x124)
+  BSATTN_AND_OR_STEP(0x122)
+  BSATTN_AND_OR_STEP(0x121)
+#undef BSATTN_AND_OR_STEP
+  all_and = __builtin_amdgcn_readlane(a, 0) & __builtin_amdgcn_readlane(a, 16) &
+            __builtin_amdgcn_readlane(a, 32) & __builtin_amdgcn_readlane(a, 48);
+  all_or = __builtin_amdgcn_readlane(o, 0) | __builtin_amdgcn_readlane(o, 16) |
+           __builtin_amdgcn_readlane(o, 32) | __builtin_amdgcn_readlane(o, 48);
 }
 
 // Inclusive prefix sum across the 64 lanes of a wave.
