@@ -41,7 +41,8 @@ CALIB_BYTES = 512 << 20    # the plain device copy --calibrate-copy runs (bytes 
 # of `bench.py --only first_order_decode_32k --calibrate-copy`, each scaled by
 # CALIB_BYTES / (the same counter for the calibration copy).  Valid only for
 # the sources it was taken on (their SHA-256); otherwise traffic is null.
-STEP_TRAFFIC = {"sources_sha256": "", "bytes_per_step": None}
+STEP_TRAFFIC = {"sources_sha256": "1b84d4ca294928507e7647a0a57e4dfce3864e2d4cbb63c8cdc589c119cf275d",
+                "bytes_per_step": 145332929}  # FETCH x 1.9999 (16715.6 + 51823.7 + 1115.6 KiB) + WRITE x 1 (262.2 + 2088.8 + 272.0 KiB)
 STEP_SOURCES = ("sliding_window_attention_block_amd/csrc/decode.hip",
                 "sliding_window_attention_block_amd/csrc/select.hip",
                 "sliding_window_attention_block_amd/csrc/bsattn.cpp",

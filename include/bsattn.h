@@ -154,7 +154,7 @@ bsattn_status bsattn_decode(const bsattn_shape* shape, const void* Q, const void
  * bsattn_decode writes them [COBS 1, 2.1-2.3; SWA 拡張手法; LG].  workspace:
  * at least bsattn_decode_workspace_bytes(shape, top_k, window, n_sink,
  * n_global) bytes, 256-byte aligned, contents need not be initialised (NULL
- * when that size is 0).  With BF16 K/V, at most 2048 complete blocks and
+ * when that size is 0).  With BF16 K/V, at most 512 complete blocks and
  * top_k <= 256 the top-k runs inside the decode kernel (each decode wave
  * selects its pair's blocks while its sink and window loads are in flight),
  * one launch fewer than the two calls; the selection is the same exact

@@ -362,7 +362,7 @@ bsattn_status bsattn_decode_step(const bsattn_shape* shape, const void* Q, const
   st = decode_args(shape, Q, K, V, sel, top_k, window, n_sink, global_pos_host, n_global, O, lse, workspace,
                    ws_bytes, da);
   if (st != BSATTN_OK) return st;
-  // bf16 with at most 2048 complete blocks and top_k <= 256: the decode waves
+  // bf16 with at most 512 complete blocks and top_k <= 256: the decode waves
   // select; otherwise the top-k kernel does, then the decode reads sel
   const int nb = sa.n_blocks;
   const bool fused = da.bf16 && nb >= 1 && nb <= bsattn::kFusedMaxBlocks && top_k <= bsattn::kFusedMaxTopK;
@@ -371,7 +371,7 @@ bsattn_status bsattn_decode_step(const bsattn_shape* shape, const void* Q, const
     da.scores = scores;
     da.nblk_capacity = nblk_capacity;
     da.sel_out = sel;
-    da.key_slots = nb <= 64 * 8 ? 8 : 32;
+    da.key_slots = 8;
     for (int j = 0; j < nb; ++j)
       if (bsattn::forced_mask(da.forced, j) == ~0ull) da.full_forced[j >> 6] |= 1ull << (j & 63);
   }

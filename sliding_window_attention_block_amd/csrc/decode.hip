@@ -712,8 +712,7 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
     const long long waves = (long long)n_pairs * a.n_part;
     const dim3 grid((unsigned)((waves + kW - 1) / kW)), block(64 * kW);
     if (a.key_slots == 0) hipLaunchKernelGGL((decode_bf16_kernel<D, 0>), grid, block, 0, stream, a);
-    else if (a.key_slots <= 8) hipLaunchKernelGGL((decode_bf16_kernel<D, 8>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((decode_bf16_kernel<D, 32>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((decode_bf16_kernel<D, 8>), grid, block, 0, stream, a);
   } else {
     const dim3 grid(a.n_part, n_pairs);
     if (G <= 4)

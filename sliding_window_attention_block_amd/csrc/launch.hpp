@@ -56,9 +56,10 @@ struct ForcedBlocks {
   int32_t gblk[256];
 };
 
-// Fused decode step limits: scores held in registers (at most 32 per lane) and
-// the selection table in the wave's V tile.
-constexpr int kFusedMaxBlocks = 64 * 32;
+// Fused decode step limits: 8 scores per lane in registers (with more blocks
+// the in-wave selection costs more than the top-k launch it saves: measured at
+// 2048 blocks) and the selection table in the wave's V tile.
+constexpr int kFusedMaxBlocks = 64 * 8;
 constexpr int kFusedMaxTopK = 256;
 
 struct DecodeArgs {
@@ -80,7 +81,7 @@ struct DecodeArgs {
   int32_t n_part;         // partials per (b, K/V head): bf16 waves, fp32 workgroups
   // fused step (bf16): each wave selects its pair's top-k blocks itself from
   // the group scores instead of reading `sel`; the first wave of a pair writes
-  // the selection to sel_out.  key_slots: scores per lane (0: not fused).
+  // the selection to sel_out.  key_slots: scores per lane (0: not fused, else 8).
   const float* scores;
   int32_t nblk_capacity;
   int32_t* sel_out;

@@ -99,13 +99,13 @@ def test_decode_small_cases(api, case):
 
 
 NO_FORCED = _w("no_forced_tokens", 2, 8, 2, 128, 1200, 0, 4, 0, 0, "bf16", 19)
-# bsattn_decode_step selects inside the decode waves for bf16 with <= 2048 blocks and
-# top_k <= 256 (32 scores per lane from 513 blocks up), else it runs the two calls' kernels
+# bsattn_decode_step selects inside the decode waves for bf16 with <= 512 blocks and
+# top_k <= 256, else it runs the two calls' kernels
 ONE_CALL_EXTRA = [
     (NO_FORCED, (), 0),
-    (_w("fused_1500_blocks_g8_d64", 1, 8, 1, 64, 1500 * 64 + 17, 2, 20, 700, 64, "bf16", 25), (5, 64, 65), 0),
-    (_w("fused_2048_blocks_k256", 1, 4, 1, 128, 2048 * 64, 0, 256, 64, 64, "bf16", 26), (), 0),
-    (_w("fallback_2049_blocks", 1, 4, 1, 64, 2049 * 64, 0, 8, 64, 64, "bf16", 28), (), 0),
+    (_w("fused_512_blocks_k256_g8_d64", 1, 8, 1, 64, 512 * 64, 2, 256, 700, 64, "bf16", 25), (5, 64, 65), 0),
+    (_w("fused_500_blocks_tail_d128", 2, 4, 1, 128, 500 * 64 + 17, 0, 24, 64, 64, "bf16", 26), (), 0),
+    (_w("fallback_513_blocks", 1, 4, 1, 64, 513 * 64, 0, 8, 64, 64, "bf16", 28), (), 0),
     (_w("fallback_k257", 1, 4, 1, 64, 600 * 64, 0, 257, 64, 64, "bf16", 29), (), 0),
 ]
 
