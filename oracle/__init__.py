@@ -32,6 +32,7 @@ from .attention import (  # noqa: F401
     prefill,
 )
 from .selector import (  # noqa: F401
+    round_to_bf16,
     block_summaries,
     head_scores,
     exact_mass_scores,

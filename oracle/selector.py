@@ -36,6 +36,11 @@ The method, as the COBS explainer states it:
 * Top-k: largest group score first, equal scores broken by the lower block
   index; the chosen indices are returned in ascending order, padded with -1
   when there are fewer than k candidates.
+* Stored summary precision (section 2.3, compression): the explainer keeps the
+  block mean in BF16.  ``block_summaries(..., mean_bf16=True)`` returns the
+  mean rounded to the nearest BF16 value (ties to even); the covariance is
+  still that of the block's keys about their exact mean (the rounding is a
+  storage step, applied after the summary is computed).
 """
 
 from __future__ import annotations
@@ -43,22 +48,38 @@ from __future__ import annotations
 import numpy as np
 
 
-def block_summaries(K, S, rank):
+def round_to_bf16(x):
+    """Nearest bfloat16 value of each entry of ``x`` (as float64), ties to even.
+
+    bfloat16 keeps 8 significant bits (1 implicit + 7 stored) and float32's
+    exponent range.  With x = m * 2^e, 0.5 <= |m| < 1 (frexp), the nearest value
+    with 8 significant bits is rint(m * 2^8) * 2^(e - 8); numpy's rint rounds
+    halves to even, which is the ties-to-even rule on the last kept bit.  Inputs
+    here are finite and far from the float32 overflow and subnormal range.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
+
+
+def block_summaries(K, S, rank, mean_bf16=False):
     """Per complete block of ``K`` [n, d]: mean [NB, d] and low-rank factor [NB, rank, d].
 
     factor[b, i] = sqrt(lambda_i) * v_i for the i-th largest eigenpair of the block's
     covariance Sigma_b = (1/L) sum_r (k_r - mean)(k_r - mean)^T, L = S.  Eigenvalues below
     zero (rounding) are clamped to 0.  Each row's sign is fixed so that its entry of
     largest magnitude (first such entry on ties) is positive; the sign never changes a
-    score because the score only uses squares of projections.
+    score because the score only uses squares of projections.  With ``mean_bf16`` the
+    returned mean is rounded to bfloat16 (``round_to_bf16``); the factor is unchanged.
     """
     K = np.asarray(K, dtype=np.float64)
     n, d = K.shape
     nb = n // S
     X = K[: nb * S].reshape(nb, S, d)
     mean = X.mean(axis=1)
+    stored = round_to_bf16(mean) if mean_bf16 else mean
     if rank == 0:
-        return mean, np.zeros((nb, 0, d))
+        return stored, np.zeros((nb, 0, d))
     if not 0 < rank <= d:
         raise ValueError("rank must be in [0, d]")
     C = X - mean[:, None, :]
@@ -71,7 +92,7 @@ def block_summaries(K, S, rank):
     big = np.argmax(np.abs(rows), axis=2)
     sign = np.sign(np.take_along_axis(rows, big[:, :, None], axis=2))
     sign[sign == 0] = 1.0
-    return mean, rows * sign
+    return stored, rows * sign
 
 
 def head_scores(q_scaled, mean, factor=None):

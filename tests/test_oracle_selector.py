@@ -16,8 +16,43 @@ import pytest
 import torch
 
 from oracle import (block_summaries, candidate_blocks, exact_mass_scores, forced_token_mask,
-                    group_scores, head_scores, top_k_blocks)
+                    group_scores, head_scores, round_to_bf16, top_k_blocks)
 from synthetic import WORKLOADS
+
+
+# ---------------------------------------------------------------- bf16 storage of the mean
+
+
+def test_bf16_rounding_worked_cases():
+    """bfloat16 keeps 8 significant bits: near 1 the spacing is 2^-7.  Halfway cases go
+    to the even last bit: 1 + 2^-8 -> 1 (even), 1 + 3 * 2^-8 -> 1 + 2^-6 (even), and a
+    hair above a halfway point rounds up."""
+    x = np.array([1.0, 1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -8 + 2.0 ** -30,
+                  -(1 + 2.0 ** -8), 0.0, 3.0, 2.0 ** -20 * (1 + 2.0 ** -9), 255.5, 256.5])
+    want = np.array([1.0, 1.0, 1 + 2.0 ** -6, 1 + 2.0 ** -7, -1.0, 0.0, 3.0, 2.0 ** -20,
+                     256.0, 256.0])
+    assert np.array_equal(round_to_bf16(x), want)
+
+
+def test_bf16_rounding_matches_torch_on_float32_values():
+    """On values that float32 holds exactly, rounding float64 straight to bfloat16 is
+    torch's float32 -> bfloat16 conversion (round to nearest, ties to even)."""
+    rng = np.random.default_rng(3)
+    x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-6, 6, 20000),
+                        (rng.integers(-2 ** 15, 2 ** 15, 5000) + 0.5) * 2.0 ** -7]).astype(np.float32)
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(round_to_bf16(x.astype(np.float64)), want)
+
+
+def test_bf16_mean_is_the_rounded_mean_and_leaves_the_factor():
+    rng = np.random.default_rng(4)
+    K = rng.standard_normal((4 * 16, 8))
+    m32, f32 = block_summaries(K, 16, 3)
+    m16, f16 = block_summaries(K, 16, 3, mean_bf16=True)
+    assert np.array_equal(m16, round_to_bf16(m32))
+    assert np.array_equal(f16, f32)
+    assert np.all(np.abs(m16 - m32) <= np.abs(m32) * 2.0 ** -8)
+    assert not np.array_equal(m16, m32)
 
 
 # ---------------------------------------------------------------- summaries
