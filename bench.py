@@ -6,8 +6,10 @@ Step (the timed unit): one decode step of the first-order 32K workload (batch
 token window), one bsattn_decode_step call: selector scoring, then the sparse
 decode whose waves take the top-k themselves, then the log-sum-exp merge.
 `value` is tokens/s = batch / step time.  Summaries are built once
-before timing (as the method builds them when blocks fill); their build time is
-reported separately, as are the COBS 128K decode step and the two prefills.
+before timing (as the method builds them when blocks fill), with the block
+means stored in bfloat16 as the COBS explainer stores them (the same step with
+fp32 means is reported beside it); their build time is reported separately,
+as are the COBS 128K decode step and the two prefills.
 
 Every timed loop cycles through R device-resident replicas of its inputs so the
 reuse distance exceeds the 256 MB Infinity Cache: each step reads HBM, not
@@ -114,13 +116,14 @@ def to_dev(torch, a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def bench_decode(api, torch, w, x, steps, warmup):
+def bench_decode(api, torch, w, x, steps, warmup, mean_dtype="bf16"):
     B, Hq, Hkv, d, n, S = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_ctx, w.block_size
     nb = n // S
     shape = api.make_shape(B, Hq, Hkv, d, n, dtype=w.dtype)
     ws_bytes = api.bsattn_decode_workspace_bytes(shape, w.top_k, w.window, w.n_sink, 0)
     elem = 2 if w.dtype == "bf16" else 4
-    summ_bytes = B * Hkv * nb * d * 4 * (1 + w.rank)
+    mean_elem = 2 if mean_dtype == "bf16" else 4
+    summ_bytes = B * Hkv * nb * d * (mean_elem + 4 * w.rank)
     kv_est = B * Hkv * (w.top_k * S + w.n_sink + w.window) * d * 2 * elem
     R = replicas_for(summ_bytes + kv_est)
     log(f"[bench] {w.name}: {R} replicas, {2 * x['K'].nbytes * R / 2**30:.1f} GiB of K/V")
@@ -130,7 +133,8 @@ def bench_decode(api, torch, w, x, steps, warmup):
         K = K0 if r == 0 else K0.clone()
         V = V0 if r == 0 else V0.clone()
         Q = Q0 if r == 0 else Q0.clone()
-        mean = torch.empty((B, Hkv, nb, d), device="cuda")
+        mean = torch.empty((B, Hkv, nb, d), device="cuda",
+                           dtype=torch.bfloat16 if mean_dtype == "bf16" else torch.float32)
         factor = torch.empty((B, Hkv, nb, w.rank, d), device="cuda") if w.rank else None
         scores = torch.empty((B, Hkv, nb), device="cuda")
         sel = torch.empty((B, Hkv, w.top_k), dtype=torch.int32, device="cuda")
@@ -218,7 +222,8 @@ def bench_decode(api, torch, w, x, steps, warmup):
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) * 1e3 / steps
     res = dict(
-        workload=w.name, ms_per_step=ms_step, wall_ms_per_step=wall_step, tokens_per_s=B / (ms_step * 1e-3),
+        workload=w.name, mean_dtype=mean_dtype, ms_per_step=ms_step, wall_ms_per_step=wall_step,
+        tokens_per_s=B / (ms_step * 1e-3),
         eager_ms_per_step=eager_ms, two_call_ms_per_step=two_ms, replicas=R, attended_tokens=tokens,
         gathered_kv_bytes=kv_bytes, select_ms=sel_ms, decode_ms=dec_ms,
         select_bytes=sel_bytes, decode_bytes=kv_bytes + io_bytes,
@@ -302,7 +307,8 @@ def cpu_baseline(w, x):
     for (b, g) in pairs:
         Kf[(b, g)] = bf16_bits_to_f32(x["K"][b, g]) if x["K"].dtype == np.uint16 else x["K"][b, g]
         Vf[(b, g)] = bf16_bits_to_f32(x["V"][b, g]) if x["V"].dtype == np.uint16 else x["V"][b, g]
-        summaries[(b, g)] = oracle.block_summaries(Kf[(b, g)].astype(np.float64), w.block_size, w.rank)
+        summaries[(b, g)] = oracle.block_summaries(Kf[(b, g)].astype(np.float64), w.block_size, w.rank,
+                                                   mean_bf16=True)
     # whole decode steps (every (b, K/V head) pair) until about 10 s of CPU work
     steps = 0
     t0 = time.perf_counter()
@@ -371,6 +377,9 @@ def main():
         log(f"[bench] {name}: inputs generated in {time.perf_counter() - t:.1f} s")
         if name.endswith(("32k", "128k")):
             results[name] = bench_decode(api, torch, w, x, args.steps, args.warmup)
+            if name == HEADLINE:  # context: the same step with fp32 block means
+                results[name + "/fp32_means"] = bench_decode(api, torch, w, x, args.steps, args.warmup,
+                                                             mean_dtype="f32")
         else:
             results[name] = bench_prefill(api, torch, w, x, args.steps, args.warmup)
         log(f"[bench] {name}: {json.dumps(results[name])}")

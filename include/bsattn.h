@@ -33,7 +33,7 @@
  *      decode  Q [B, Hq, d],          O [B, Hq, d] fp32, lse [B, Hq] fp32
  *      prefill Q [B, Hq, N, d],       O [B, Hq, N, d] fp32, lse [B, Hq, N] fp32
  *      K, V    [B, Hkv, kv_capacity, d]  (token t of (b, g) at row t)
- *      mean    [B, Hkv, nblk_capacity, d] fp32
+ *      mean    [B, Hkv, nblk_capacity, d] fp32 or bf16 (mean_dtype)
  *      factor  [B, Hkv, nblk_capacity, rank, d] fp32
  *  - GQA [ATT FAQ Q2]: query head h reads K/V head h / (Hq / Hkv).
  *  - Blocks [COBS 1, 2.1]: block j holds tokens [j*S, (j+1)*S); only complete
@@ -91,11 +91,15 @@ typedef struct {
  * K dtype: F32 or BF16.  rank in [0, BSATTN_MAX_RANK]; factor may be NULL
  * when rank == 0.  Requires (first_block + n_blocks) * S <= n_ctx and
  * first_block + n_blocks <= nblk_capacity.  n_blocks == 0 is a no-op.
+ * mean_dtype: BSATTN_F32 stores the mean in fp32; BSATTN_BF16 stores it
+ * rounded to bfloat16 (nearest, ties to even), the block-mean storage of
+ * [COBS 2.3, compression]; the covariance is taken about the unrounded mean
+ * either way.  The same mean_dtype must be passed to the calls that read it.
  */
 bsattn_status bsattn_build_summaries(const bsattn_shape* shape, const void* K, int32_t rank,
                                      int32_t first_block, int32_t n_blocks,
-                                     int32_t nblk_capacity, float* mean, float* factor,
-                                     void* hip_stream);
+                                     int32_t nblk_capacity, void* mean, int32_t mean_dtype,
+                                     float* factor, void* hip_stream);
 
 /*
  * Block selection for the decode query (the last cached token, t = n_ctx - 1).
@@ -110,14 +114,15 @@ bsattn_status bsattn_build_summaries(const bsattn_shape* shape, const void* K, i
  *  4. sel[b,g,:] = the top_k candidates by (score descending, index
  *     ascending), written in ascending order, padded with -1.
  * Q: [B,Hq,d] of shape.dtype.  mean/factor as built above (factor NULL iff
- * rank == 0).  scores: REQUIRED [B,Hkv,nblk_capacity] fp32; entries of complete
+ * rank == 0; mean_dtype as it was built with).  scores: REQUIRED [B,Hkv,nblk_capacity] fp32; entries of complete
  * blocks are written (it is also the buffer the top-k pass reads).
  * global_pos_host: sorted, unique, in [0, n_ctx), n_global <= BSATTN_MAX_GLOBAL.
  * top_k in [1, BSATTN_MAX_TOP_K]; n_ctx / S <= BSATTN_MAX_BLOCKS.
  * window >= 0 (0: no window), n_sink >= 0; sizes past n_ctx are clamped.
  */
-bsattn_status bsattn_select_topk(const bsattn_shape* shape, const void* Q, const float* mean,
-                                 const float* factor, int32_t rank, int32_t nblk_capacity,
+bsattn_status bsattn_select_topk(const bsattn_shape* shape, const void* Q, const void* mean,
+                                 int32_t mean_dtype, const float* factor, int32_t rank,
+                                 int32_t nblk_capacity,
                                  int32_t top_k, int32_t window, int32_t n_sink,
                                  const int32_t* global_pos_host, int32_t n_global, int32_t* sel,
                                  float* scores, void* hip_stream);
@@ -163,8 +168,9 @@ bsattn_status bsattn_decode(const bsattn_shape* shape, const void* Q, const void
  * (same stream).
  */
 bsattn_status bsattn_decode_step(const bsattn_shape* shape, const void* Q, const void* K,
-                                 const void* V, const float* mean, const float* factor,
-                                 int32_t rank, int32_t nblk_capacity, int32_t top_k,
+                                 const void* V, const void* mean, int32_t mean_dtype,
+                                 const float* factor, int32_t rank, int32_t nblk_capacity,
+                                 int32_t top_k,
                                  int32_t window, int32_t n_sink, const int32_t* global_pos_host,
                                  int32_t n_global, int32_t* sel, float* scores, float* O,
                                  float* lse, void* workspace, size_t ws_bytes, void* hip_stream);

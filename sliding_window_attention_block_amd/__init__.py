@@ -83,19 +83,29 @@ def bsattn_version():
     return library().bsattn_version().decode()
 
 
+def _mean_dtype(mean):
+    """bsattn dtype code of a block-mean tensor: float32 or bfloat16."""
+    import torch
+    if mean.dtype == torch.float32:
+        return BSATTN_F32
+    if mean.dtype == torch.bfloat16:
+        return BSATTN_BF16
+    raise ValueError(f"block means must be float32 or bfloat16, not {mean.dtype}")
+
+
 def bsattn_build_summaries(shape, K, rank, first_block, n_blocks, nblk_capacity, mean, factor=None,
                            stream=None):
     _check(library().bsattn_build_summaries(ctypes.byref(shape), _ptr(K), rank, first_block,
-                                            n_blocks, nblk_capacity, _ptr(mean), _ptr(factor),
-                                            _stream(stream)))
+                                            n_blocks, nblk_capacity, _ptr(mean), _mean_dtype(mean),
+                                            _ptr(factor), _stream(stream)))
 
 
 def bsattn_select_topk(shape, Q, mean, factor, rank, nblk_capacity, top_k, window, n_sink,
                        global_pos, sel, scores, stream=None):
     g, ng = _globals(global_pos)
-    _check(library().bsattn_select_topk(ctypes.byref(shape), _ptr(Q), _ptr(mean), _ptr(factor),
-                                        rank, nblk_capacity, top_k, window, n_sink, g, ng,
-                                        _ptr(sel), _ptr(scores), _stream(stream)))
+    _check(library().bsattn_select_topk(ctypes.byref(shape), _ptr(Q), _ptr(mean), _mean_dtype(mean),
+                                        _ptr(factor), rank, nblk_capacity, top_k, window, n_sink,
+                                        g, ng, _ptr(sel), _ptr(scores), _stream(stream)))
 
 
 def bsattn_decode_workspace_bytes(shape, top_k, window, n_sink, n_global=0):
@@ -117,9 +127,9 @@ def bsattn_decode_step(shape, Q, K, V, mean, factor, rank, nblk_capacity, top_k,
     g, ng = _globals(global_pos)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(library().bsattn_decode_step(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(mean),
-                                        _ptr(factor), rank, nblk_capacity, top_k, window, n_sink, g,
-                                        ng, _ptr(sel), _ptr(scores), _ptr(O), _ptr(lse),
-                                        _ptr(workspace), ws_bytes, _stream(stream)))
+                                        _mean_dtype(mean), _ptr(factor), rank, nblk_capacity, top_k,
+                                        window, n_sink, g, ng, _ptr(sel), _ptr(scores), _ptr(O),
+                                        _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def bsattn_prefill_workspace_bytes(shape, n_global):

@@ -181,14 +181,16 @@ PrefillWs prefill_workspace_layout(const bsattn_shape* s, int n_global) {
 }
 
 // Validation of the selector's arguments (bsattn_select_topk, bsattn_decode_step).
-bsattn_status select_args(const bsattn_shape* shape, const void* Q, const float* mean, const float* factor,
-                          int32_t rank, int32_t nblk_capacity, int32_t top_k, int32_t window, int32_t n_sink,
+bsattn_status select_args(const bsattn_shape* shape, const void* Q, const void* mean, int32_t mean_dtype,
+                          const float* factor, int32_t rank, int32_t nblk_capacity, int32_t top_k, int32_t window, int32_t n_sink,
                           const int32_t* global_pos_host, int32_t n_global, int32_t* sel, float* scores,
                           bsattn::SelectArgs& a) {
   bsattn_status st = check_shape(shape, true);
   if (st != BSATTN_OK) return st;
   if (Q == nullptr || mean == nullptr || sel == nullptr || scores == nullptr)
     return fail(BSATTN_ERR_INVALID, "Q, mean, sel and scores must be non-NULL");
+  if (mean_dtype != BSATTN_F32 && mean_dtype != BSATTN_BF16)
+    return fail(BSATTN_ERR_INVALID, "mean_dtype %d: must be BSATTN_F32 or BSATTN_BF16", mean_dtype);
   if (rank < 0 || rank > BSATTN_MAX_RANK) return fail(BSATTN_ERR_INVALID, "rank must be in [0, %d]", BSATTN_MAX_RANK);
   if (rank > 0 && factor == nullptr) return fail(BSATTN_ERR_INVALID, "factor is NULL with rank > 0");
   if (top_k < 1 || top_k > BSATTN_MAX_TOP_K) return fail(BSATTN_ERR_INVALID, "top_k must be in [1, %d]", BSATTN_MAX_TOP_K);
@@ -210,6 +212,7 @@ bsattn_status select_args(const bsattn_shape* shape, const void* Q, const float*
   a.top_k = top_k;
   a.scale = effective_scale(shape);
   a.bf16 = shape->dtype == BSATTN_BF16;
+  a.mean_bf16 = mean_dtype == BSATTN_BF16;
   a.forced = make_forced(shape->n_ctx, window, n_sink, global_pos_host, n_global);
   return BSATTN_OK;
 }
@@ -280,11 +283,13 @@ const char* bsattn_version(void) { return "bsattn 0.1.0 gfx950"; }
 
 bsattn_status bsattn_build_summaries(const bsattn_shape* shape, const void* K, int32_t rank,
                                      int32_t first_block, int32_t n_blocks, int32_t nblk_capacity,
-                                     float* mean, float* factor, void* hip_stream) {
+                                     void* mean, int32_t mean_dtype, float* factor, void* hip_stream) {
   g_err[0] = 0;
   bsattn_status st = check_shape(shape, false);
   if (st != BSATTN_OK) return st;
   if (K == nullptr || mean == nullptr) return fail(BSATTN_ERR_INVALID, "K and mean must be non-NULL");
+  if (mean_dtype != BSATTN_F32 && mean_dtype != BSATTN_BF16)
+    return fail(BSATTN_ERR_INVALID, "mean_dtype %d: must be BSATTN_F32 or BSATTN_BF16", mean_dtype);
   if (rank < 0 || rank > BSATTN_MAX_RANK) return fail(BSATTN_ERR_INVALID, "rank must be in [0, %d]", BSATTN_MAX_RANK);
   if (rank > 0 && factor == nullptr) return fail(BSATTN_ERR_INVALID, "factor is NULL with rank > 0");
   if (first_block < 0 || n_blocks < 0) return fail(BSATTN_ERR_INVALID, "negative block range");
@@ -305,20 +310,21 @@ bsattn_status bsattn_build_summaries(const bsattn_shape* shape, const void* K, i
   a.rank = rank;
   a.head_dim = shape->head_dim;
   a.bf16 = shape->dtype == BSATTN_BF16;
+  a.mean_bf16 = mean_dtype == BSATTN_BF16;
   hipError_t e = bsattn::launch_summaries(a, (hipStream_t)hip_stream);
   if (e != hipSuccess) return fail(BSATTN_ERR_HIP, "summaries launch: %s", hipGetErrorString(e));
   return BSATTN_OK;
 }
 
-bsattn_status bsattn_select_topk(const bsattn_shape* shape, const void* Q, const float* mean,
-                                 const float* factor, int32_t rank, int32_t nblk_capacity,
+bsattn_status bsattn_select_topk(const bsattn_shape* shape, const void* Q, const void* mean,
+                                 int32_t mean_dtype, const float* factor, int32_t rank, int32_t nblk_capacity,
                                  int32_t top_k, int32_t window, int32_t n_sink,
                                  const int32_t* global_pos_host, int32_t n_global, int32_t* sel,
                                  float* scores, void* hip_stream) {
   g_err[0] = 0;
   bsattn::SelectArgs a;
-  const bsattn_status st = select_args(shape, Q, mean, factor, rank, nblk_capacity, top_k, window, n_sink,
-                                       global_pos_host, n_global, sel, scores, a);
+  const bsattn_status st = select_args(shape, Q, mean, mean_dtype, factor, rank, nblk_capacity, top_k, window,
+                                       n_sink, global_pos_host, n_global, sel, scores, a);
   if (st != BSATTN_OK) return st;
   hipError_t e = bsattn::launch_select_topk(a, (hipStream_t)hip_stream);
   if (e != hipSuccess) return fail(BSATTN_ERR_HIP, "select launch: %s", hipGetErrorString(e));
@@ -349,13 +355,14 @@ bsattn_status bsattn_decode(const bsattn_shape* shape, const void* Q, const void
 }
 
 bsattn_status bsattn_decode_step(const bsattn_shape* shape, const void* Q, const void* K, const void* V,
-                                 const float* mean, const float* factor, int32_t rank, int32_t nblk_capacity,
+                                 const void* mean, int32_t mean_dtype, const float* factor, int32_t rank,
+                                 int32_t nblk_capacity,
                                  int32_t top_k, int32_t window, int32_t n_sink, const int32_t* global_pos_host,
                                  int32_t n_global, int32_t* sel, float* scores, float* O, float* lse,
                                  void* workspace, size_t ws_bytes, void* hip_stream) {
   g_err[0] = 0;
   bsattn::SelectArgs sa;
-  bsattn_status st = select_args(shape, Q, mean, factor, rank, nblk_capacity, top_k, window, n_sink,
+  bsattn_status st = select_args(shape, Q, mean, mean_dtype, factor, rank, nblk_capacity, top_k, window, n_sink,
                                  global_pos_host, n_global, sel, scores, sa);
   if (st != BSATTN_OK) return st;
   bsattn::DecodeArgs da;

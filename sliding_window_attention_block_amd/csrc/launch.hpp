@@ -12,7 +12,7 @@ namespace bsattn {
 
 struct SummaryArgs {
   const void* K;
-  float* mean;
+  void* mean;       // fp32, or bf16 when mean_bf16
   float* factor;
   int32_t bh;            // B * Hkv
   int32_t kv_capacity;   // token stride
@@ -22,12 +22,13 @@ struct SummaryArgs {
   int32_t rank;
   int32_t head_dim;
   bool bf16;
+  bool mean_bf16;  // store the block mean in bfloat16 (round to nearest even)
 };
 hipError_t launch_summaries(const SummaryArgs& a, hipStream_t stream);
 
 struct SelectArgs {
   const void* Q;
-  const float* mean;
+  const void* mean;  // fp32, or bf16 when mean_bf16
   const float* factor;
   int32_t* sel;
   float* scores;
@@ -43,6 +44,7 @@ struct SelectArgs {
   // 4 * PB blocks) of one pair; `n_part` waves per pair
   int32_t per_wave, n_part;
   bool scores_only;  // skip the top-k launch (the fused decode step selects)
+  bool mean_bf16;    // the block means are bfloat16
 };
 hipError_t launch_select_topk(const SelectArgs& a, hipStream_t stream);
 

@@ -11,7 +11,8 @@
 // Scoring streams every summary once: 16 lanes (one DPP row) share one block,
 // lane l owning the 4-dim chunks l, 16 + l, ... of every query head in
 // registers, so each load instruction reads 256 contiguous bytes of a summary
-// row; the 16 partial dot products are summed with DPP row rotations.  Each
+// row (128 of a bfloat16 mean row); the 16 partial dot products are summed
+// with DPP row rotations.  Each
 // wave scores a run of blocks of one (b, K/V head) pair with the next group's
 // loads in flight while it computes the current one, and waves never wait for
 // each other, so the loads stream without load-then-compute rounds.  All of a block's rows
@@ -23,6 +24,8 @@
 // a wave-wide scan to find the digit of the k-th largest key; then every lane
 // emits its candidates above the threshold, and the lowest-index ones equal
 // to it, in index order.
+#include <type_traits>
+
 #include "launch.hpp"
 
 namespace bsattn {
@@ -43,11 +46,10 @@ constexpr bool scores_heavy(int GM, int RM, int PB, int D) {
   return GM * (D / 16) + 2 * PB * (1 + RM) * (D / 16) > 160;
 }
 
-template <int D, int GM, int RM, int PB, bool BF16>
+template <int D, int GM, int RM, int PB, bool BF16, bool MB>
 __global__ __launch_bounds__(256, scores_heavy(GM, RM, PB, D) ? 1 : 2) void select_scores_kernel(SelectArgs a) {
   constexpr int SL = D / 16;  // dims per lane: 4-dim chunks sub, 16 + sub, ...
   constexpr int NC = SL / 4;  // 16-byte chunks per lane per row
-  constexpr int R = 1 + RM;   // rows per block: mean, then factor rows
   constexpr int UB = 4 * PB;  // blocks per unit: PB per 16-lane row
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -88,10 +90,14 @@ __global__ __launch_bounds__(256, scores_heavy(GM, RM, PB, D) ? 1 : 2) void sele
     }
   }
 
-  const float4* mean4 = reinterpret_cast<const float4*>(a.mean);
+  // mean rows: 4 dims per 16-byte (fp32) or 8-byte (bf16, widened at compute
+  // time so the loads stay plain) chunk
+  using MeanChunk = typename std::conditional<MB, u32x2, float4>::type;
+  const MeanChunk* mean4 = reinterpret_cast<const MeanChunk*>(a.mean);
   const float4* fac4 = reinterpret_cast<const float4*>(a.factor);
   struct Stage {
-    float4 v[PB][R][NC];
+    MeanChunk m[PB][NC];
+    float4 v[PB][RM > 0 ? RM : 1][NC];  // factor rows
   };
   // Every load is issued unconditionally (blocks past the end re-read the last
   // block, factor rows past the rank re-read the last row, both ignored), so
@@ -102,12 +108,12 @@ __global__ __launch_bounds__(256, scores_heavy(GM, RM, PB, D) ? 1 : 2) void sele
       const int j = min(u * UB + 4 * p + r16, NB - 1);
       const size_t row = (size_t)pair * a.nblk_capacity + j;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) st.v[p][0][c] = mean4[row * (D / 4) + 16 * c + sub];
+      for (int c = 0; c < NC; ++c) st.m[p][c] = mean4[row * (D / 4) + 16 * c + sub];
 #pragma unroll
       for (int i = 0; i < RM; ++i) {
         const size_t fr = row * rank + min(i, rank - 1);
 #pragma unroll
-        for (int c = 0; c < NC; ++c) st.v[p][1 + i][c] = fac4[fr * (D / 4) + 16 * c + sub];
+        for (int c = 0; c < NC; ++c) st.v[p][i][c] = fac4[fr * (D / 4) + 16 * c + sub];
       }
     }
   };
@@ -127,14 +133,24 @@ __global__ __launch_bounds__(256, scores_heavy(GM, RM, PB, D) ? 1 : 2) void sele
     for (int p = 0; p < PB; ++p) {
       const int j = u * UB + 4 * p + r16;
       float s[GM];
+      float4 mv[NC];
 #pragma unroll
-      for (int h = 0; h < GM; ++h) s[h] = row16_sum(dot(st.v[p][0], h));
+      for (int c = 0; c < NC; ++c) {
+        if constexpr (MB) {
+          const u32x2 w = st.m[p][c];
+          mv[c] = float4{bf16lo(w[0]), bf16hi(w[0]), bf16lo(w[1]), bf16hi(w[1])};
+        } else {
+          mv[c] = st.m[p][c];
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < GM; ++h) s[h] = row16_sum(dot(mv, h));
 #pragma unroll
       for (int i = 0; i < RM; ++i) {
         if (i < rank) {
 #pragma unroll
           for (int h = 0; h < GM; ++h) {
-            const float pr = row16_sum(dot(st.v[p][1 + i], h));
+            const float pr = row16_sum(dot(st.v[p][i], h));
             s[h] = fmaf(0.5f * pr, pr, s[h]);
           }
         }
@@ -329,8 +345,9 @@ hipError_t launch_t(const SelectArgs& a0, hipStream_t stream) {
     a.per_wave = (int)c;
     a.n_part = (int)((units + c - 1) / c);
     const long long waves = (long long)n_pairs * a.n_part;
-    hipLaunchKernelGGL((select_scores_kernel<D, GM, RM, PB, BF16>), dim3((unsigned)((waves + 3) / 4)),
-                       dim3(256), 0, stream, a);
+    const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+    if (a.mean_bf16) hipLaunchKernelGGL((select_scores_kernel<D, GM, RM, PB, BF16, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((select_scores_kernel<D, GM, RM, PB, BF16, false>), grid, block, 0, stream, a);
   }
   if (a.scores_only) return hipGetLastError();
   const int per = (a.n_blocks + kTopkThreads - 1) / kTopkThreads;

@@ -61,9 +61,16 @@ __global__ __launch_bounds__(256) void summaries_mean_kernel(SummaryArgs a) {
 #pragma unroll
       for (int e = 0; e < E; ++e) s[e] += red[m][e];
     }
-    float* dst = a.mean + ((size_t)bh * a.nblk_capacity + blk) * D + tid * E;
+    const size_t off = ((size_t)bh * a.nblk_capacity + blk) * D + tid * E;
+    if (a.mean_bf16) {  // round to nearest even, two values per 32-bit store
+      uint32_t* dst = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.mean) + off);
 #pragma unroll
-    for (int e = 0; e < E; ++e) dst[e] = s[e] * (1.0f / kBlock);
+      for (int e = 0; e < E; e += 2) dst[e / 2] = cvt_pk_bf16(s[e] * (1.0f / kBlock), s[e + 1] * (1.0f / kBlock));
+    } else {
+      float* dst = static_cast<float*>(a.mean) + off;
+#pragma unroll
+      for (int e = 0; e < E; ++e) dst[e] = s[e] * (1.0f / kBlock);
+    }
   }
 }
 
@@ -117,8 +124,10 @@ __global__ __launch_bounds__(256) void summaries_factor_kernel(SummaryArgs a) {
     float s = 0.f;
     for (int r = 0; r < kBlock; ++r) s += Ct[d * kCtStride + r];
     s *= (1.0f / kBlock);
-    mu[d] = s;
-    a.mean[((size_t)bh * a.nblk_capacity + blk) * D + d] = s;
+    mu[d] = s;  // the covariance is taken about the fp32 mean; only the stored copy is rounded
+    const size_t off = ((size_t)bh * a.nblk_capacity + blk) * D + d;
+    if (a.mean_bf16) static_cast<uint16_t*>(a.mean)[off] = (uint16_t)(cvt_pk_bf16(s, 0.f) & 0xffffu);
+    else static_cast<float*>(a.mean)[off] = s;
   }
   __syncthreads();
   // 3. centre

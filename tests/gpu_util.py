@@ -33,13 +33,14 @@ def as_f64(arr):
 
 
 def gpu_decode_step(api, x, w, kv_capacity=None, nblk_capacity=None, global_pos=(), dev=None,
-                    one_call=False):
+                    one_call=False, mean_dtype="f32"):
     """Run summaries -> select/top-k -> decode on the GPU through the binding.
 
     ``x`` holds Q, K, V numpy arrays (float32 or bf16 bits) of workload ``w``.
     With ``one_call`` the step is bsattn_decode_step (selection and decode in one
-    call); otherwise bsattn_select_topk, then bsattn_decode.
-    Returns numpy copies of mean, factor, scores, sel, O, lse.
+    call); otherwise bsattn_select_topk, then bsattn_decode.  ``mean_dtype`` "bf16"
+    stores the block means in bfloat16.
+    Returns numpy copies of mean (as float32), factor, scores, sel, O, lse.
     """
     torch = torch_mod()
     B, Hq, Hkv, d, n = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_ctx
@@ -51,7 +52,8 @@ def gpu_decode_step(api, x, w, kv_capacity=None, nblk_capacity=None, global_pos=
     K = dev["K"] if "K" in dev else to_dev(x["K"])
     V = dev["V"] if "V" in dev else to_dev(x["V"])
     shape = api.make_shape(B, Hq, Hkv, d, n, kv_capacity=cap, dtype=w.dtype)
-    mean = torch.full((B, Hkv, max(nbcap, 1), d), float("nan"), device="cuda")
+    mean = torch.full((B, Hkv, max(nbcap, 1), d), float("nan"), device="cuda",
+                      dtype=torch.bfloat16 if mean_dtype == "bf16" else torch.float32)
     factor = (torch.full((B, Hkv, max(nbcap, 1), w.rank, d), float("nan"), device="cuda")
               if w.rank > 0 else None)
     api.bsattn_build_summaries(shape, K, w.rank, 0, nb, max(nbcap, 1), mean, factor)
@@ -70,7 +72,7 @@ def gpu_decode_step(api, x, w, kv_capacity=None, nblk_capacity=None, global_pos=
                                w.n_sink, gp, sel, scores)
         api.bsattn_decode(shape, Q, K, V, sel, w.top_k, w.window, w.n_sink, gp, O, lse, ws)
     torch.cuda.synchronize()
-    return dict(mean=mean.cpu().numpy(), factor=None if factor is None else factor.cpu().numpy(),
+    return dict(mean=mean.float().cpu().numpy(), factor=None if factor is None else factor.cpu().numpy(),
                 scores=scores.cpu().numpy(), sel=sel.cpu().numpy(), O=O.cpu().numpy(),
                 lse=lse.cpu().numpy())
 
@@ -108,6 +110,13 @@ def oracle_decode_with_sel(q, Kbg, Vbg, n, S, window, n_sink, global_pos, sel, s
     forced = oracle.forced_token_mask(n, n_sink, window, global_pos)
     tokens = oracle.decode_token_set(n, S, forced, sel)
     return oracle.sparse_decode_group(q, Kbg[:n], Vbg[:n], tokens, scale)
+
+
+def bf16_ulp(x):
+    """Spacing of bfloat16 values at |x| (8 significant bits)."""
+    x = np.abs(np.asarray(x, dtype=np.float64))
+    _, e = np.frexp(np.where(x > 0, x, 1.0))
+    return np.ldexp(1.0, e - 8)
 
 
 def max_abs(a, b):

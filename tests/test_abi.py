@@ -115,22 +115,25 @@ def test_decode_rejects_bad_arguments():
 
 def test_decode_step_rejects_bad_arguments():
     s = _shape()
-    # shape Q K V mean factor rank nblk top_k window n_sink gpos n_global sel scores O lse ws ws_bytes stream
-    args = [s, FAKE, FAKE, FAKE, FAKE, None, 0, 4, 2, 64, 0, None, 0, FAKE, FAKE, FAKE, None, FAKE,
+    # shape Q K V mean mean_dtype factor rank nblk top_k window n_sink gpos n_global sel scores O lse
+    # ws ws_bytes stream
+    args = [s, FAKE, FAKE, FAKE, FAKE, 0, None, 0, 4, 2, 64, 0, None, 0, FAKE, FAKE, FAKE, None, FAKE,
             1 << 30, None]
     st, _ = _status("bsattn_decode_step", *args[:4], None, *args[5:])          # NULL mean
     assert st == 1
-    st, _ = _status("bsattn_decode_step", *args[:6], 1, *args[7:])             # rank 1, NULL factor
+    st, _ = _status("bsattn_decode_step", *args[:5], 2, *args[6:])             # unknown mean dtype
     assert st == 1
-    st, _ = _status("bsattn_decode_step", *args[:7], 3, *args[8:])             # nblk_capacity < 4 blocks
+    st, _ = _status("bsattn_decode_step", *args[:7], 1, *args[8:])             # rank 1, NULL factor
     assert st == 1
-    st, _ = _status("bsattn_decode_step", *args[:8], 0, *args[9:])             # top_k 0
+    st, _ = _status("bsattn_decode_step", *args[:8], 3, *args[9:])             # nblk_capacity < 4 blocks
     assert st == 1
-    st, _ = _status("bsattn_decode_step", *args[:13], None, *args[14:])        # NULL sel
+    st, _ = _status("bsattn_decode_step", *args[:9], 0, *args[10:])            # top_k 0
     assert st == 1
-    st, _ = _status("bsattn_decode_step", *args[:15], None, *args[16:])        # NULL O
+    st, _ = _status("bsattn_decode_step", *args[:14], None, *args[15:])        # NULL sel
     assert st == 1
-    st, msg = _status("bsattn_decode_step", *args[:18], 16, None)              # workspace too small
+    st, _ = _status("bsattn_decode_step", *args[:16], None, *args[17:])        # NULL O
+    assert st == 1
+    st, msg = _status("bsattn_decode_step", *args[:19], 16, None)              # workspace too small
     assert st == 4 and "workspace" in msg
     st, _ = _status("bsattn_decode_step", *args[:3], FAKE + 4, *args[4:])      # misaligned V
     assert st == 1
@@ -138,37 +141,44 @@ def test_decode_step_rejects_bad_arguments():
 
 @pytest.mark.parametrize("gpos", [(5, 3, 9), (1, 1, 2), (0, 10, 256), (-1, 2, 3)])
 def test_global_positions_are_checked(gpos):
-    st, msg = _status("bsattn_select_topk", _shape(), FAKE, FAKE, None, 0, 4, 2, 64, 0, G3(*gpos), 3,
+    st, msg = _status("bsattn_select_topk", _shape(), FAKE, FAKE, 0, None, 0, 4, 2, 64, 0, G3(*gpos), 3,
                       FAKE, FAKE, None)
     assert st == 1 and "global" in msg
 
 
 def test_select_rejects_bad_arguments():
     s = _shape()
-    st, _ = _status("bsattn_select_topk", s, FAKE, FAKE, None, 2, 4, 2, 64, 0, None, 0, FAKE, FAKE, None)
+    # shape Q mean mean_dtype factor rank nblk top_k window n_sink gpos n_global sel scores stream
+    st, _ = _status("bsattn_select_topk", s, FAKE, FAKE, 0, None, 2, 4, 2, 64, 0, None, 0, FAKE, FAKE, None)
     assert st == 1  # rank 2 without a factor
-    st, _ = _status("bsattn_select_topk", s, FAKE, FAKE, FAKE, 9, 4, 2, 64, 0, None, 0, FAKE, FAKE, None)
+    st, _ = _status("bsattn_select_topk", s, FAKE, FAKE, 0, FAKE, 9, 4, 2, 64, 0, None, 0, FAKE, FAKE, None)
     assert st == 1  # rank above 8
-    st, _ = _status("bsattn_select_topk", s, FAKE, FAKE, None, 0, 3, 2, 64, 0, None, 0, FAKE, FAKE, None)
+    st, _ = _status("bsattn_select_topk", s, FAKE, FAKE, 0, None, 0, 3, 2, 64, 0, None, 0, FAKE, FAKE, None)
     assert st == 1  # nblk_capacity below n_ctx / 64
-    st, _ = _status("bsattn_select_topk", s, FAKE, FAKE, None, 0, 4, 2, 64, 0, None, 0, FAKE, None, None)
+    st, _ = _status("bsattn_select_topk", s, FAKE, FAKE, 0, None, 0, 4, 2, 64, 0, None, 0, FAKE, None, None)
     assert st == 1  # scores is required
-    st, _ = _status("bsattn_select_topk", s, FAKE, FAKE, None, 0, 4, 2000, 64, 0, None, 0, FAKE, FAKE, None)
+    st, _ = _status("bsattn_select_topk", s, FAKE, FAKE, 0, None, 0, 4, 2000, 64, 0, None, 0, FAKE, FAKE, None)
     assert st == 1  # top_k above the maximum
+    st, msg = _status("bsattn_select_topk", s, FAKE, FAKE, 7, None, 0, 4, 2, 64, 0, None, 0, FAKE, FAKE, None)
+    assert st == 1 and "mean_dtype" in msg  # mean stored as neither fp32 nor bf16
     big = _shape(n_ctx=64 * 65537, kv_capacity=64 * 65537)
-    st, _ = _status("bsattn_select_topk", big, FAKE, FAKE, None, 0, 65537, 2, 64, 0, None, 0, FAKE, FAKE, None)
+    st, _ = _status("bsattn_select_topk", big, FAKE, FAKE, 1, None, 0, 65537, 2, 64, 0, None, 0, FAKE, FAKE,
+                    None)
     assert st == 2
 
 
 def test_summaries_reject_bad_ranges():
     s = _shape()
-    st, _ = _status("bsattn_build_summaries", s, FAKE, 0, 3, 2, 8, FAKE, None, None)
+    # shape K rank first_block n_blocks nblk mean mean_dtype factor stream
+    st, _ = _status("bsattn_build_summaries", s, FAKE, 0, 3, 2, 8, FAKE, 0, None, None)
     assert st == 1  # blocks 3..4 are not complete in 256 tokens
-    st, _ = _status("bsattn_build_summaries", s, FAKE, 0, 0, 4, 3, FAKE, None, None)
+    st, _ = _status("bsattn_build_summaries", s, FAKE, 0, 0, 4, 3, FAKE, 0, None, None)
     assert st == 1  # past nblk_capacity
-    st, _ = _status("bsattn_build_summaries", s, FAKE, 4, 0, 4, 4, FAKE, None, None)
+    st, _ = _status("bsattn_build_summaries", s, FAKE, 4, 0, 4, 4, FAKE, 0, None, None)
     assert st == 1  # rank 4 without a factor
-    st, _ = _status("bsattn_build_summaries", s, FAKE, 0, 0, 0, 4, FAKE, None, None)
+    st, _ = _status("bsattn_build_summaries", s, FAKE, 0, 0, 4, 4, FAKE, 3, None, None)
+    assert st == 1  # unknown mean dtype
+    st, _ = _status("bsattn_build_summaries", s, FAKE, 0, 0, 0, 4, FAKE, 1, None, None)
     assert st == 0  # empty range: nothing to launch
 
 

@@ -13,7 +13,7 @@ import pytest
 import oracle
 from synthetic import WORKLOADS, DecodeWorkload, make_decode_inputs
 
-from gpu_util import (OUT_TOL, as_f64, compare_selection, default_scale, gpu_decode_step,
+from gpu_util import (OUT_TOL, as_f64, bf16_ulp, compare_selection, default_scale, gpu_decode_step,
                       max_abs, oracle_decode_with_sel)
 
 pytestmark = pytest.mark.gpu
@@ -48,10 +48,11 @@ SMALL = [
 ]
 
 
-def _check_case(api, w, globals_, extra_cap, one_call=False):
+def _check_case(api, w, globals_, extra_cap, one_call=False, mean_dtype="f32"):
     x = make_decode_inputs(w, kv_capacity=w.n_ctx + extra_cap)
-    print(f"[decode parity] {w.name} one_call={one_call}", flush=True)
-    got = gpu_decode_step(api, x, w, global_pos=globals_, one_call=one_call)
+    print(f"[decode parity] {w.name} one_call={one_call} mean={mean_dtype}", flush=True)
+    got = gpu_decode_step(api, x, w, global_pos=globals_, one_call=one_call, mean_dtype=mean_dtype)
+    mb = mean_dtype == "bf16"
     Q, K, V = as_f64(x["Q"]), as_f64(x["K"]), as_f64(x["V"])
     S, n, G, d = w.block_size, w.n_ctx, w.n_q_heads // w.n_kv_heads, w.head_dim
     scale = default_scale(d)
@@ -61,8 +62,13 @@ def _check_case(api, w, globals_, extra_cap, one_call=False):
     ties = 0
     for b in range(w.batch):
         for g in range(w.n_kv_heads):
-            mean, factor = oracle.block_summaries(K[b, g, :n], S, w.rank)
-            assert max_abs(got["mean"][b, g, :nb], mean) < 1e-5
+            mean, factor = oracle.block_summaries(K[b, g, :n], S, w.rank, mean_bf16=mb)
+            if mb:
+                # both sides round once (from an fp32 and an fp64 mean): at most one step apart
+                err = np.abs(got["mean"][b, g, :nb].astype(np.float64) - mean)
+                assert np.all(err <= bf16_ulp(mean) + 1e-30)
+            else:
+                assert max_abs(got["mean"][b, g, :nb], mean) < 1e-5
             if w.rank > 0:
                 proj_gpu = np.einsum("bid,bie->bde", got["factor"][b, g, :nb].astype(np.float64),
                                      got["factor"][b, g, :nb].astype(np.float64))
@@ -166,14 +172,15 @@ def test_k_covering_all_candidates_equals_dense_causal(api):
             assert max_abs(got["lse"][b, 4 * g:4 * g + 4], lse) < OUT_TOL
 
 
-def _full_size(api, name, pairs):
+def _full_size(api, name, pairs, one_call=False, mean_dtype="f32"):
     import torch
     w = WORKLOADS[name]
     print(f"[decode full size] {name}: generating inputs", flush=True)
     x = make_decode_inputs(w)
     print(f"[decode full size] {name}: running on the GPU", flush=True)
-    got = gpu_decode_step(api, x, w)
+    got = gpu_decode_step(api, x, w, one_call=one_call, mean_dtype=mean_dtype)
     torch.cuda.empty_cache()
+    mb = mean_dtype == "bf16"
     # properties over every pair
     S, n = w.block_size, w.n_ctx
     forced = oracle.forced_token_mask(n, w.n_sink, w.window)
@@ -193,8 +200,11 @@ def _full_size(api, name, pairs):
     for (b, g) in pairs:
         print(f"[decode full size] {name}: oracle for pair ({b}, {g})", flush=True)
         Kbg, Vbg = as_f64(x["K"][b, g]), as_f64(x["V"][b, g])
-        mean, factor = oracle.block_summaries(Kbg, S, w.rank)
-        assert max_abs(got["mean"][b, g], mean) < 1e-5
+        mean, factor = oracle.block_summaries(Kbg, S, w.rank, mean_bf16=mb)
+        if mb:
+            assert np.all(np.abs(got["mean"][b, g].astype(np.float64) - mean) <= bf16_ulp(mean) + 1e-30)
+        else:
+            assert max_abs(got["mean"][b, g], mean) < 1e-5
         s_ref = oracle.group_scores(oracle.head_scores(scale * Q[b, g * G:(g + 1) * G], mean,
                                                        factor if w.rank else None))
         assert max_abs(got["scores"][b, g], s_ref) < (2e-4 if w.rank else 3e-5)
@@ -214,6 +224,21 @@ def test_first_order_decode_32k_full_size(api):
 
 def test_cobs_decode_128k_full_size(api):
     _full_size(api, "cobs_decode_128k", [(0, 0), (3, 7)])
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0].name for c in SMALL])
+def test_bf16_means_small_cases(api, case):
+    """Block means stored in bfloat16 (the COBS explainer's storage), one-call step:
+    means within one bfloat16 step of the oracle's rounded means, selection and
+    outputs to the same bar against the oracle using those means."""
+    w, globals_, extra = case
+    _check_case(api, w, globals_, extra, one_call=True, mean_dtype="bf16")
+
+
+@pytest.mark.parametrize("name,pairs", [("first_order_decode_32k", [(0, 0), (15, 7)]),
+                                        ("cobs_decode_128k", [(2, 5)])])
+def test_bf16_means_full_size(api, name, pairs):
+    _full_size(api, name, pairs, one_call=True, mean_dtype="bf16")
 
 
 def test_repeated_calls_reuse_the_workspace(api):
