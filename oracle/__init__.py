@@ -33,6 +33,9 @@ from .attention import (  # noqa: F401
 )
 from .selector import (  # noqa: F401
     round_to_bf16,
+    quantize_e2m1_rows,
+    dequantize_e2m1_rows,
+    E2M1_MAGNITUDES,
     block_summaries,
     head_scores,
     exact_mass_scores,

@@ -44,12 +44,13 @@ def sparse_decode_group(q, K, V, tokens, scale):
 
 
 def decode_step(Q, K, V, n, S, rank, top_k, window, n_sink, global_pos=(), scale=None,
-                pairs=None, summaries=None, mean_bf16=False):
+                pairs=None, summaries=None, mean_bf16=False, factor_fp4=False):
     """One decode step for the query token t = n - 1 of every (batch, K/V head) pair.
 
     Q [B, Hq, d]; K, V [B, Hkv, >= n, d].  ``pairs`` restricts the work to a list of
     (b, kv_head); ``summaries`` may map (b, kv_head) -> (mean, factor) already built;
-    ``mean_bf16`` stores the block means in bfloat16 (see ``block_summaries``).
+    ``mean_bf16`` / ``factor_fp4`` store the block means in bfloat16 / the factor rows
+    in FP4 (see ``block_summaries``).
     Returns a dict keyed by (b, kv_head) with:
       'scores'  [NB] group scores of all complete blocks,
       'cand'    candidate block indices,
@@ -73,7 +74,7 @@ def decode_step(Q, K, V, n, S, rank, top_k, window, n_sink, global_pos=(), scale
         if summaries is not None and (b, g) in summaries:
             mean, factor = summaries[(b, g)]
         else:
-            mean, factor = block_summaries(Kbg, S, rank, mean_bf16=mean_bf16)
+            mean, factor = block_summaries(Kbg, S, rank, mean_bf16=mean_bf16, factor_fp4=factor_fp4)
         q = np.asarray(Q[b, g * G:(g + 1) * G], dtype=np.float64)
         qs = scale * q
         s = group_scores(head_scores(qs, mean, factor if rank > 0 else None))

@@ -41,11 +41,56 @@ The method, as the COBS explainer states it:
   mean rounded to the nearest BF16 value (ties to even); the covariance is
   still that of the block's keys about their exact mean (the rounding is a
   storage step, applied after the summary is computed).
+* The same section stores the eigenvectors in FP4 (E2M1) with a scale.  Reading:
+  one float32 scale per factor row (the row's largest magnitude over 6, the
+  largest E2M1 value) and each entry stored as the E2M1 value nearest to
+  entry / scale (ties to the even code); the arithmetic of that decision is
+  float32.  ``quantize_e2m1_rows`` / ``dequantize_e2m1_rows``;
+  ``block_summaries(..., factor_fp4=True)`` returns the dequantized factor.
 """
 
 from __future__ import annotations
 
 import numpy as np
+
+
+# E2M1 (FP4): sign bit, 2 exponent bits (bias 1), 1 mantissa bit.  Magnitude
+# codes 0..7 in order: 0, 0.5 (subnormal), 1, 1.5, 2, 3, 4, 6.
+E2M1_MAGNITUDES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def quantize_e2m1_rows(rows):
+    """FP4 E2M1 codes of factor rows with one scale per row.
+
+    rows [..., d] (float64).  In float32, as the stored factor is float32:
+    amax = max |x| over the row, scale = amax / 6, v = x / scale.  The code's
+    magnitude is the E2M1 value nearest to |v| (on a tie, the even code: the one
+    whose mantissa bit is 0), its sign bit (8) is set when v < 0 and the magnitude
+    is not 0.  A row of zeros gets scale 0 and codes 0.  Returns (codes uint8
+    [..., d] in 0..15, scale float32 [...]).
+    """
+    x = np.asarray(rows, dtype=np.float64).astype(np.float32)
+    amax = np.max(np.abs(x), axis=-1)
+    scale = (amax / np.float32(6.0)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    v = np.where(scale[..., None] > 0, x / safe[..., None], np.float32(0.0)).astype(np.float32)
+    a = np.abs(v.astype(np.float64))
+    # nearest magnitude, written out: distance to each of the 8 values, ties to even
+    dist = np.abs(a[..., None] - E2M1_MAGNITUDES)
+    best = dist.min(axis=-1, keepdims=True)
+    near = dist == best
+    even = near & (np.arange(8) % 2 == 0)
+    idx = np.where(even.any(axis=-1), np.argmax(even, axis=-1), np.argmax(near, axis=-1))
+    sign = ((v < 0) & (idx > 0)).astype(np.uint8)
+    return (idx.astype(np.uint8) | (sign << 3)), scale
+
+
+def dequantize_e2m1_rows(codes, scale):
+    """Float64 values of E2M1 codes [..., d] with their row scales [...]."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    mag = E2M1_MAGNITUDES[codes & 7]
+    val = np.where(codes & 8, -mag, mag)
+    return val * np.asarray(scale, dtype=np.float64)[..., None]
 
 
 def round_to_bf16(x):
@@ -62,7 +107,7 @@ def round_to_bf16(x):
     return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
 
 
-def block_summaries(K, S, rank, mean_bf16=False):
+def block_summaries(K, S, rank, mean_bf16=False, factor_fp4=False):
     """Per complete block of ``K`` [n, d]: mean [NB, d] and low-rank factor [NB, rank, d].
 
     factor[b, i] = sqrt(lambda_i) * v_i for the i-th largest eigenpair of the block's
@@ -70,7 +115,8 @@ def block_summaries(K, S, rank, mean_bf16=False):
     zero (rounding) are clamped to 0.  Each row's sign is fixed so that its entry of
     largest magnitude (first such entry on ties) is positive; the sign never changes a
     score because the score only uses squares of projections.  With ``mean_bf16`` the
-    returned mean is rounded to bfloat16 (``round_to_bf16``); the factor is unchanged.
+    returned mean is rounded to bfloat16 (``round_to_bf16``); with ``factor_fp4`` the
+    returned factor is its FP4 storage, dequantized (``quantize_e2m1_rows``).
     """
     K = np.asarray(K, dtype=np.float64)
     n, d = K.shape
@@ -92,7 +138,10 @@ def block_summaries(K, S, rank, mean_bf16=False):
     big = np.argmax(np.abs(rows), axis=2)
     sign = np.sign(np.take_along_axis(rows, big[:, :, None], axis=2))
     sign[sign == 0] = 1.0
-    return stored, rows * sign
+    factor = rows * sign
+    if factor_fp4:
+        factor = dequantize_e2m1_rows(*quantize_e2m1_rows(factor))
+    return stored, factor
 
 
 def head_scores(q_scaled, mean, factor=None):

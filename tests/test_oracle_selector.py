@@ -15,8 +15,9 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import (block_summaries, candidate_blocks, exact_mass_scores, forced_token_mask,
-                    group_scores, head_scores, round_to_bf16, top_k_blocks)
+from oracle import (E2M1_MAGNITUDES, block_summaries, candidate_blocks, dequantize_e2m1_rows,
+                    exact_mass_scores, forced_token_mask, group_scores, head_scores,
+                    quantize_e2m1_rows, round_to_bf16, top_k_blocks)
 from synthetic import WORKLOADS
 
 
@@ -53,6 +54,72 @@ def test_bf16_mean_is_the_rounded_mean_and_leaves_the_factor():
     assert np.array_equal(f16, f32)
     assert np.all(np.abs(m16 - m32) <= np.abs(m32) * 2.0 ** -8)
     assert not np.array_equal(m16, m32)
+
+
+# ---------------------------------------------------------------- FP4 (E2M1) storage of the factor
+
+
+def test_e2m1_magnitudes_follow_the_format():
+    """E2M1: 2 exponent bits with bias 1 and 1 mantissa bit; exponent 0 is subnormal
+    (0.5 * m), otherwise 2^(e-1) * (1 + m/2)."""
+    want = []
+    for code in range(8):
+        e, m = code >> 1, code & 1
+        want.append(0.5 * m if e == 0 else 2.0 ** (e - 1) * (1 + m / 2))
+    assert np.array_equal(E2M1_MAGNITUDES, np.array(want))
+
+
+def test_e2m1_worked_cases():
+    """Scale 1 (the row's largest magnitude is 6).  Midpoints go to the even code:
+    0.25 -> 0, 0.75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4."""
+    row = np.array([[6.0, 0.25, 0.75, 1.25, -1.75, 2.5, 3.5, 5.0, -5.0001, 0.0, -0.1, 0.26]])
+    codes, scale = quantize_e2m1_rows(row)
+    assert scale[0] == np.float32(1.0)
+    assert codes[0].tolist() == [7, 0, 2, 2, 8 | 4, 4, 6, 6, 8 | 7, 0, 0, 1]
+    assert np.array_equal(dequantize_e2m1_rows(codes, scale)[0],
+                          [6, 0, 1, 1, -2, 2, 4, 4, -6, 0, 0, 0.5])
+
+
+def test_e2m1_matches_the_midpoint_rule_on_random_rows():
+    """An independent statement of the same rounding: the magnitude code counts the
+    midpoints below |v| (k even: strictly below; k odd: at or below, so a tie lands
+    on the even code)."""
+    rng = np.random.default_rng(7)
+    rows = rng.standard_normal((200, 128)) * rng.gamma(1.0, 1.0, (200, 1))
+    rows[:20, :8] = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0]) * (np.abs(rows[:20, 8:]).max(axis=1, keepdims=True) / 6.0)
+    codes, scale = quantize_e2m1_rows(rows)
+    x32 = rows.astype(np.float32)
+    v = (x32 / scale[:, None]).astype(np.float32).astype(np.float64)
+    a = np.abs(v)
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    mag = sum(((a > m) if k % 2 == 0 else (a >= m)).astype(int) for k, m in enumerate(mids))
+    assert np.array_equal(codes & 7, mag)
+    assert np.array_equal((codes >> 3).astype(bool), (v < 0) & (mag > 0))
+
+
+def test_e2m1_rows_keep_their_maximum_and_half_a_step():
+    rng = np.random.default_rng(8)
+    rows = rng.standard_normal((50, 64)) * 3.0
+    codes, scale = quantize_e2m1_rows(rows)
+    deq = dequantize_e2m1_rows(codes, scale)
+    big = np.argmax(np.abs(rows), axis=1)
+    assert np.all((codes[np.arange(50), big] & 7) == 7)  # the largest entry is +-6 * scale
+    # error at most half the spacing around the value (spacing 0.5, 1 or 2 times the scale)
+    spacing = np.where(np.abs(deq) < 2 * scale[:, None], 0.5, np.where(np.abs(deq) < 4 * scale[:, None], 1.0, 2.0))
+    assert np.all(np.abs(deq - rows) <= (0.5 * spacing + 1e-6) * scale[:, None])
+    c2, s2 = quantize_e2m1_rows(-rows)
+    assert np.array_equal(s2, scale) and np.array_equal(c2 & 7, codes & 7)
+    zero_c, zero_s = quantize_e2m1_rows(np.zeros((2, 8)))
+    assert np.all(zero_c == 0) and np.all(zero_s == 0)
+
+
+def test_fp4_factor_is_the_dequantized_factor():
+    rng = np.random.default_rng(9)
+    K = rng.standard_normal((4 * 16, 8))
+    m0, f0 = block_summaries(K, 16, 3)
+    m1, f1 = block_summaries(K, 16, 3, factor_fp4=True)
+    assert np.array_equal(m0, m1)
+    assert np.array_equal(f1, dequantize_e2m1_rows(*quantize_e2m1_rows(f0)))
 
 
 # ---------------------------------------------------------------- summaries
