@@ -116,14 +116,16 @@ def to_dev(torch, a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def bench_decode(api, torch, w, x, steps, warmup, mean_dtype="bf16"):
+def bench_decode(api, torch, w, x, steps, warmup, mean_dtype="bf16", factor_fp4=True):
     B, Hq, Hkv, d, n, S = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_ctx, w.block_size
     nb = n // S
     shape = api.make_shape(B, Hq, Hkv, d, n, dtype=w.dtype)
     ws_bytes = api.bsattn_decode_workspace_bytes(shape, w.top_k, w.window, w.n_sink, 0)
     elem = 2 if w.dtype == "bf16" else 4
     mean_elem = 2 if mean_dtype == "bf16" else 4
-    summ_bytes = B * Hkv * nb * d * (mean_elem + 4 * w.rank)
+    fp4 = factor_fp4 and w.rank > 0
+    factor_row_bytes = (d // 2 + 4) if fp4 else 4 * d  # FP4 codes + float32 scale, or fp32
+    summ_bytes = B * Hkv * nb * (d * mean_elem + w.rank * factor_row_bytes)
     kv_est = B * Hkv * (w.top_k * S + w.n_sink + w.window) * d * 2 * elem
     R = replicas_for(summ_bytes + kv_est)
     log(f"[bench] {w.name}: {R} replicas, {2 * x['K'].nbytes * R / 2**30:.1f} GiB of K/V")
@@ -135,28 +137,34 @@ def bench_decode(api, torch, w, x, steps, warmup, mean_dtype="bf16"):
         Q = Q0 if r == 0 else Q0.clone()
         mean = torch.empty((B, Hkv, nb, d), device="cuda",
                            dtype=torch.bfloat16 if mean_dtype == "bf16" else torch.float32)
-        factor = torch.empty((B, Hkv, nb, w.rank, d), device="cuda") if w.rank else None
+        fscale = None
+        if fp4:
+            factor = torch.empty((B, Hkv, nb, w.rank, d // 2), dtype=torch.uint8, device="cuda")
+            fscale = torch.empty((B, Hkv, nb, w.rank), device="cuda")
+        else:
+            factor = torch.empty((B, Hkv, nb, w.rank, d), device="cuda") if w.rank else None
         scores = torch.empty((B, Hkv, nb), device="cuda")
         sel = torch.empty((B, Hkv, w.top_k), dtype=torch.int32, device="cuda")
         ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
         O = torch.empty((B, Hq, d), device="cuda")
         lse = torch.empty((B, Hq), device="cuda")
-        reps.append(dict(K=K, V=V, Q=Q, mean=mean, factor=factor, scores=scores, sel=sel, ws=ws,
-                         O=O, lse=lse))
+        reps.append(dict(K=K, V=V, Q=Q, mean=mean, factor=factor, fscale=fscale, scores=scores, sel=sel,
+                         ws=ws, O=O, lse=lse))
     del K0, V0, Q0
     # A1: summaries (built once per block; timed on every replica)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     build_ms = []
     for rp in reps:
         ev[0].record()
-        api.bsattn_build_summaries(shape, rp["K"], w.rank, 0, nb, nb, rp["mean"], rp["factor"])
+        api.bsattn_build_summaries(shape, rp["K"], w.rank, 0, nb, nb, rp["mean"], rp["factor"],
+                                   factor_scale=rp["fscale"])
         ev[1].record()
         torch.cuda.synchronize()
         build_ms.append(ev[0].elapsed_time(ev[1]))
 
     def select(rp):
         api.bsattn_select_topk(shape, rp["Q"], rp["mean"], rp["factor"], w.rank, nb, w.top_k,
-                               w.window, w.n_sink, None, rp["sel"], rp["scores"])
+                               w.window, w.n_sink, None, rp["sel"], rp["scores"], factor_scale=rp["fscale"])
 
     def decode(rp):
         api.bsattn_decode(shape, rp["Q"], rp["K"], rp["V"], rp["sel"], w.top_k, w.window, w.n_sink,
@@ -165,7 +173,7 @@ def bench_decode(api, torch, w, x, steps, warmup, mean_dtype="bf16"):
     def step(rp):
         api.bsattn_decode_step(shape, rp["Q"], rp["K"], rp["V"], rp["mean"], rp["factor"], w.rank, nb,
                                w.top_k, w.window, w.n_sink, None, rp["sel"], rp["scores"], rp["O"],
-                               rp["lse"], rp["ws"])
+                               rp["lse"], rp["ws"], factor_scale=rp["fscale"])
 
     for i in range(warmup):
         rp = reps[i % R]
@@ -222,7 +230,8 @@ def bench_decode(api, torch, w, x, steps, warmup, mean_dtype="bf16"):
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) * 1e3 / steps
     res = dict(
-        workload=w.name, mean_dtype=mean_dtype, ms_per_step=ms_step, wall_ms_per_step=wall_step,
+        workload=w.name, mean_dtype=mean_dtype, factor="fp4" if fp4 else ("f32" if w.rank else None),
+        ms_per_step=ms_step, wall_ms_per_step=wall_step,
         tokens_per_s=B / (ms_step * 1e-3),
         eager_ms_per_step=eager_ms, two_call_ms_per_step=two_ms, replicas=R, attended_tokens=tokens,
         gathered_kv_bytes=kv_bytes, select_ms=sel_ms, decode_ms=dec_ms,
@@ -380,6 +389,9 @@ def main():
             if name == HEADLINE:  # context: the same step with fp32 block means
                 results[name + "/fp32_means"] = bench_decode(api, torch, w, x, args.steps, args.warmup,
                                                              mean_dtype="f32")
+            elif w.rank > 0:  # context: the same step with fp32 factor rows
+                results[name + "/fp32_factors"] = bench_decode(api, torch, w, x, args.steps, args.warmup,
+                                                               factor_fp4=False)
         else:
             results[name] = bench_prefill(api, torch, w, x, args.steps, args.warmup)
         log(f"[bench] {name}: {json.dumps(results[name])}")

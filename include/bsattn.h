@@ -34,7 +34,10 @@
  *      prefill Q [B, Hq, N, d],       O [B, Hq, N, d] fp32, lse [B, Hq, N] fp32
  *      K, V    [B, Hkv, kv_capacity, d]  (token t of (b, g) at row t)
  *      mean    [B, Hkv, nblk_capacity, d] fp32 or bf16 (mean_dtype)
- *      factor  [B, Hkv, nblk_capacity, rank, d] fp32
+ *      factor  [B, Hkv, nblk_capacity, rank, d] fp32, or FP4 (factor_dtype):
+ *              codes uint8 [B, Hkv, nblk_capacity, rank, d/2] (entry 2i in the
+ *              low nibble of byte i, 2i+1 in the high nibble) and
+ *              factor_scale [B, Hkv, nblk_capacity, rank] fp32
  *  - GQA [ATT FAQ Q2]: query head h reads K/V head h / (Hq / Hkv).
  *  - Blocks [COBS 1, 2.1]: block j holds tokens [j*S, (j+1)*S); only complete
  *    blocks ((j+1)*S <= n_ctx) have summaries and can be selected.
@@ -59,7 +62,11 @@ typedef enum {
   BSATTN_ERR_WORKSPACE = 4    /* workspace missing or smaller than required        */
 } bsattn_status;
 
-typedef enum { BSATTN_F32 = 0, BSATTN_BF16 = 1 } bsattn_dtype;
+typedef enum {
+  BSATTN_F32 = 0,
+  BSATTN_BF16 = 1,
+  BSATTN_FP4_E2M1 = 2 /* factor rows only: 4-bit codes + one float32 scale per row */
+} bsattn_dtype;
 
 typedef struct {
   int32_t batch;       /* B >= 1                                                   */
@@ -94,12 +101,18 @@ typedef struct {
  * mean_dtype: BSATTN_F32 stores the mean in fp32; BSATTN_BF16 stores it
  * rounded to bfloat16 (nearest, ties to even), the block-mean storage of
  * [COBS 2.3, compression]; the covariance is taken about the unrounded mean
- * either way.  The same mean_dtype must be passed to the calls that read it.
+ * either way.  factor_dtype: BSATTN_F32 stores the factor rows in fp32;
+ * BSATTN_FP4_E2M1 stores them as [COBS 2.3, compression] stores eigenvectors:
+ * per row a float32 scale (the row's largest magnitude / 6) in factor_scale
+ * and each entry as the E2M1 code nearest to entry / scale (ties to the even
+ * code); factor_scale is ignored for BSATTN_F32 (may be NULL).  The calls that
+ * read the summaries take the same mean_dtype, factor_dtype and factor_scale.
  */
 bsattn_status bsattn_build_summaries(const bsattn_shape* shape, const void* K, int32_t rank,
                                      int32_t first_block, int32_t n_blocks,
                                      int32_t nblk_capacity, void* mean, int32_t mean_dtype,
-                                     float* factor, void* hip_stream);
+                                     void* factor, int32_t factor_dtype, float* factor_scale,
+                                     void* hip_stream);
 
 /*
  * Block selection for the decode query (the last cached token, t = n_ctx - 1).
@@ -114,15 +127,17 @@ bsattn_status bsattn_build_summaries(const bsattn_shape* shape, const void* K, i
  *  4. sel[b,g,:] = the top_k candidates by (score descending, index
  *     ascending), written in ascending order, padded with -1.
  * Q: [B,Hq,d] of shape.dtype.  mean/factor as built above (factor NULL iff
- * rank == 0; mean_dtype as it was built with).  scores: REQUIRED [B,Hkv,nblk_capacity] fp32; entries of complete
+ * rank == 0; mean_dtype, factor_dtype and factor_scale as they were built
+ * with; an FP4 factor row enters the score as its codes' values times its
+ * scale).  scores: REQUIRED [B,Hkv,nblk_capacity] fp32; entries of complete
  * blocks are written (it is also the buffer the top-k pass reads).
  * global_pos_host: sorted, unique, in [0, n_ctx), n_global <= BSATTN_MAX_GLOBAL.
  * top_k in [1, BSATTN_MAX_TOP_K]; n_ctx / S <= BSATTN_MAX_BLOCKS.
  * window >= 0 (0: no window), n_sink >= 0; sizes past n_ctx are clamped.
  */
 bsattn_status bsattn_select_topk(const bsattn_shape* shape, const void* Q, const void* mean,
-                                 int32_t mean_dtype, const float* factor, int32_t rank,
-                                 int32_t nblk_capacity,
+                                 int32_t mean_dtype, const void* factor, int32_t factor_dtype,
+                                 const float* factor_scale, int32_t rank, int32_t nblk_capacity,
                                  int32_t top_k, int32_t window, int32_t n_sink,
                                  const int32_t* global_pos_host, int32_t n_global, int32_t* sel,
                                  float* scores, void* hip_stream);
@@ -169,7 +184,8 @@ bsattn_status bsattn_decode(const bsattn_shape* shape, const void* Q, const void
  */
 bsattn_status bsattn_decode_step(const bsattn_shape* shape, const void* Q, const void* K,
                                  const void* V, const void* mean, int32_t mean_dtype,
-                                 const float* factor, int32_t rank, int32_t nblk_capacity,
+                                 const void* factor, int32_t factor_dtype,
+                                 const float* factor_scale, int32_t rank, int32_t nblk_capacity,
                                  int32_t top_k,
                                  int32_t window, int32_t n_sink, const int32_t* global_pos_host,
                                  int32_t n_global, int32_t* sel, float* scores, float* O,

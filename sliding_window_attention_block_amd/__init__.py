@@ -13,7 +13,7 @@ import ctypes
 import math
 
 from . import _lib
-from ._lib import BSATTN_BF16, BSATTN_F32, Shape
+from ._lib import BSATTN_BF16, BSATTN_F32, BSATTN_FP4_E2M1, Shape
 
 __all__ = [
     "BsattnError", "Shape", "make_shape", "library", "bsattn_build_summaries",
@@ -21,7 +21,7 @@ __all__ = [
     "bsattn_decode_step",
     "bsattn_prefill",
     "bsattn_prefill_workspace_bytes",
-    "bsattn_status_string", "bsattn_version", "BSATTN_F32", "BSATTN_BF16",
+    "bsattn_status_string", "bsattn_version", "BSATTN_F32", "BSATTN_BF16", "BSATTN_FP4_E2M1",
 ]
 
 
@@ -93,19 +93,33 @@ def _mean_dtype(mean):
     raise ValueError(f"block means must be float32 or bfloat16, not {mean.dtype}")
 
 
+def _factor_dtype(factor, factor_scale):
+    """bsattn dtype code of a factor tensor: float32 rows, or uint8 FP4 codes (with scales)."""
+    import torch
+    if factor is None or factor.dtype == torch.float32:
+        return BSATTN_F32
+    if factor.dtype == torch.uint8:
+        if factor_scale is None:
+            raise ValueError("FP4 factor codes need factor_scale")
+        return BSATTN_FP4_E2M1
+    raise ValueError(f"factor rows must be float32 or uint8 FP4 codes, not {factor.dtype}")
+
+
 def bsattn_build_summaries(shape, K, rank, first_block, n_blocks, nblk_capacity, mean, factor=None,
-                           stream=None):
+                           stream=None, factor_scale=None):
     _check(library().bsattn_build_summaries(ctypes.byref(shape), _ptr(K), rank, first_block,
                                             n_blocks, nblk_capacity, _ptr(mean), _mean_dtype(mean),
-                                            _ptr(factor), _stream(stream)))
+                                            _ptr(factor), _factor_dtype(factor, factor_scale),
+                                            _ptr(factor_scale), _stream(stream)))
 
 
 def bsattn_select_topk(shape, Q, mean, factor, rank, nblk_capacity, top_k, window, n_sink,
-                       global_pos, sel, scores, stream=None):
+                       global_pos, sel, scores, stream=None, factor_scale=None):
     g, ng = _globals(global_pos)
     _check(library().bsattn_select_topk(ctypes.byref(shape), _ptr(Q), _ptr(mean), _mean_dtype(mean),
-                                        _ptr(factor), rank, nblk_capacity, top_k, window, n_sink,
-                                        g, ng, _ptr(sel), _ptr(scores), _stream(stream)))
+                                        _ptr(factor), _factor_dtype(factor, factor_scale),
+                                        _ptr(factor_scale), rank, nblk_capacity, top_k, window,
+                                        n_sink, g, ng, _ptr(sel), _ptr(scores), _stream(stream)))
 
 
 def bsattn_decode_workspace_bytes(shape, top_k, window, n_sink, n_global=0):
@@ -123,13 +137,15 @@ def bsattn_decode(shape, Q, K, V, sel, top_k, window, n_sink, global_pos, O, lse
 
 
 def bsattn_decode_step(shape, Q, K, V, mean, factor, rank, nblk_capacity, top_k, window, n_sink,
-                       global_pos, sel, scores, O, lse, workspace, stream=None):
+                       global_pos, sel, scores, O, lse, workspace, stream=None, factor_scale=None):
     g, ng = _globals(global_pos)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(library().bsattn_decode_step(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(mean),
-                                        _mean_dtype(mean), _ptr(factor), rank, nblk_capacity, top_k,
-                                        window, n_sink, g, ng, _ptr(sel), _ptr(scores), _ptr(O),
-                                        _ptr(lse), _ptr(workspace), ws_bytes, _stream(stream)))
+                                        _mean_dtype(mean), _ptr(factor),
+                                        _factor_dtype(factor, factor_scale), _ptr(factor_scale), rank,
+                                        nblk_capacity, top_k, window, n_sink, g, ng, _ptr(sel),
+                                        _ptr(scores), _ptr(O), _ptr(lse), _ptr(workspace), ws_bytes,
+                                        _stream(stream)))
 
 
 def bsattn_prefill_workspace_bytes(shape, n_global):

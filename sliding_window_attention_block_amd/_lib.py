@@ -19,6 +19,7 @@ BSATTN_ERR_HIP = 3
 BSATTN_ERR_WORKSPACE = 4
 BSATTN_F32 = 0
 BSATTN_BF16 = 1
+BSATTN_FP4_E2M1 = 2
 
 EXPORTS = (
     "bsattn_build_summaries",
@@ -66,18 +67,19 @@ def load():
         raise OSError(f"{LIB_PATH} is missing: build it with "
                       "`python -m sliding_window_attention_block_amd.build`")
     lib = ctypes.CDLL(LIB_PATH)
-    lib.bsattn_build_summaries.argtypes = [_pshape, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _vp]
+    lib.bsattn_build_summaries.argtypes = [_pshape, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _i32,
+                                           _vp, _vp]
     lib.bsattn_build_summaries.restype = _st
-    lib.bsattn_select_topk.argtypes = [_pshape, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
-                                       _pi32, _i32, _vp, _vp, _vp]
+    lib.bsattn_select_topk.argtypes = [_pshape, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
+                                       _i32, _pi32, _i32, _vp, _vp, _vp]
     lib.bsattn_select_topk.restype = _st
     lib.bsattn_decode_workspace_bytes.argtypes = [_pshape, _i32, _i32, _i32, _i32]
     lib.bsattn_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.bsattn_decode.argtypes = [_pshape, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _pi32, _i32,
                                   _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.bsattn_decode.restype = _st
-    lib.bsattn_decode_step.argtypes = [_pshape, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
-                                       _i32, _i32, _pi32, _i32, _vp, _vp, _vp, _vp, _vp,
+    lib.bsattn_decode_step.argtypes = [_pshape, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _i32,
+                                       _i32, _i32, _i32, _pi32, _i32, _vp, _vp, _vp, _vp, _vp,
                                        ctypes.c_size_t, _vp]
     lib.bsattn_decode_step.restype = _st
     lib.bsattn_prefill.argtypes = [_pshape, _vp, _vp, _vp, _i32, _i32, _i32, _pi32, _i32,

@@ -181,8 +181,18 @@ PrefillWs prefill_workspace_layout(const bsattn_shape* s, int n_global) {
 }
 
 // Validation of the selector's arguments (bsattn_select_topk, bsattn_decode_step).
+bsattn_status check_factor(int32_t rank, const void* factor, int32_t factor_dtype, const float* factor_scale) {
+  if (rank > 0 && factor == nullptr) return fail(BSATTN_ERR_INVALID, "factor is NULL with rank > 0");
+  if (factor_dtype != BSATTN_F32 && factor_dtype != BSATTN_FP4_E2M1)
+    return fail(BSATTN_ERR_INVALID, "factor_dtype %d: must be BSATTN_F32 or BSATTN_FP4_E2M1", factor_dtype);
+  if (rank > 0 && factor_dtype == BSATTN_FP4_E2M1 &&
+      (factor_scale == nullptr || (reinterpret_cast<uintptr_t>(factor_scale) & 3u) != 0))
+    return fail(BSATTN_ERR_INVALID, "FP4 factors need a 4-byte aligned factor_scale");
+  return BSATTN_OK;
+}
+
 bsattn_status select_args(const bsattn_shape* shape, const void* Q, const void* mean, int32_t mean_dtype,
-                          const float* factor, int32_t rank, int32_t nblk_capacity, int32_t top_k, int32_t window, int32_t n_sink,
+                          const void* factor, int32_t factor_dtype, const float* factor_scale, int32_t rank, int32_t nblk_capacity, int32_t top_k, int32_t window, int32_t n_sink,
                           const int32_t* global_pos_host, int32_t n_global, int32_t* sel, float* scores,
                           bsattn::SelectArgs& a) {
   bsattn_status st = check_shape(shape, true);
@@ -192,7 +202,8 @@ bsattn_status select_args(const bsattn_shape* shape, const void* Q, const void* 
   if (mean_dtype != BSATTN_F32 && mean_dtype != BSATTN_BF16)
     return fail(BSATTN_ERR_INVALID, "mean_dtype %d: must be BSATTN_F32 or BSATTN_BF16", mean_dtype);
   if (rank < 0 || rank > BSATTN_MAX_RANK) return fail(BSATTN_ERR_INVALID, "rank must be in [0, %d]", BSATTN_MAX_RANK);
-  if (rank > 0 && factor == nullptr) return fail(BSATTN_ERR_INVALID, "factor is NULL with rank > 0");
+  st = check_factor(rank, factor, factor_dtype, factor_scale);
+  if (st != BSATTN_OK) return st;
   if (top_k < 1 || top_k > BSATTN_MAX_TOP_K) return fail(BSATTN_ERR_INVALID, "top_k must be in [1, %d]", BSATTN_MAX_TOP_K);
   if (window < 0 || n_sink < 0) return fail(BSATTN_ERR_INVALID, "window and n_sink must be >= 0");
   const int nb = shape->n_ctx / shape->block_size;
@@ -204,6 +215,8 @@ bsattn_status select_args(const bsattn_shape* shape, const void* Q, const void* 
     return fail(BSATTN_ERR_INVALID, "device pointers must be 16-byte aligned");
   std::memset(&a, 0, sizeof(a));
   a.Q = Q; a.mean = mean; a.factor = rank > 0 ? factor : nullptr; a.sel = sel; a.scores = scores;
+  a.factor_fp4 = rank > 0 && factor_dtype == BSATTN_FP4_E2M1;
+  a.factor_scale = a.factor_fp4 ? factor_scale : nullptr;
   a.batch = shape->batch; a.n_q_heads = shape->n_q_heads; a.n_kv_heads = shape->n_kv_heads;
   a.head_dim = shape->head_dim;
   a.n_blocks = nb;
@@ -283,7 +296,8 @@ const char* bsattn_version(void) { return "bsattn 0.1.0 gfx950"; }
 
 bsattn_status bsattn_build_summaries(const bsattn_shape* shape, const void* K, int32_t rank,
                                      int32_t first_block, int32_t n_blocks, int32_t nblk_capacity,
-                                     void* mean, int32_t mean_dtype, float* factor, void* hip_stream) {
+                                     void* mean, int32_t mean_dtype, void* factor, int32_t factor_dtype,
+                                     float* factor_scale, void* hip_stream) {
   g_err[0] = 0;
   bsattn_status st = check_shape(shape, false);
   if (st != BSATTN_OK) return st;
@@ -291,7 +305,8 @@ bsattn_status bsattn_build_summaries(const bsattn_shape* shape, const void* K, i
   if (mean_dtype != BSATTN_F32 && mean_dtype != BSATTN_BF16)
     return fail(BSATTN_ERR_INVALID, "mean_dtype %d: must be BSATTN_F32 or BSATTN_BF16", mean_dtype);
   if (rank < 0 || rank > BSATTN_MAX_RANK) return fail(BSATTN_ERR_INVALID, "rank must be in [0, %d]", BSATTN_MAX_RANK);
-  if (rank > 0 && factor == nullptr) return fail(BSATTN_ERR_INVALID, "factor is NULL with rank > 0");
+  st = check_factor(rank, factor, factor_dtype, factor_scale);
+  if (st != BSATTN_OK) return st;
   if (first_block < 0 || n_blocks < 0) return fail(BSATTN_ERR_INVALID, "negative block range");
   if ((long long)(first_block + (long long)n_blocks) * shape->block_size > shape->n_ctx)
     return fail(BSATTN_ERR_INVALID, "blocks past n_ctx are not complete");
@@ -311,20 +326,24 @@ bsattn_status bsattn_build_summaries(const bsattn_shape* shape, const void* K, i
   a.head_dim = shape->head_dim;
   a.bf16 = shape->dtype == BSATTN_BF16;
   a.mean_bf16 = mean_dtype == BSATTN_BF16;
+  a.factor_fp4 = rank > 0 && factor_dtype == BSATTN_FP4_E2M1;
+  a.factor_scale = factor_scale;
   hipError_t e = bsattn::launch_summaries(a, (hipStream_t)hip_stream);
   if (e != hipSuccess) return fail(BSATTN_ERR_HIP, "summaries launch: %s", hipGetErrorString(e));
   return BSATTN_OK;
 }
 
 bsattn_status bsattn_select_topk(const bsattn_shape* shape, const void* Q, const void* mean,
-                                 int32_t mean_dtype, const float* factor, int32_t rank, int32_t nblk_capacity,
+                                 int32_t mean_dtype, const void* factor, int32_t factor_dtype,
+                                 const float* factor_scale, int32_t rank, int32_t nblk_capacity,
                                  int32_t top_k, int32_t window, int32_t n_sink,
                                  const int32_t* global_pos_host, int32_t n_global, int32_t* sel,
                                  float* scores, void* hip_stream) {
   g_err[0] = 0;
   bsattn::SelectArgs a;
-  const bsattn_status st = select_args(shape, Q, mean, mean_dtype, factor, rank, nblk_capacity, top_k, window,
-                                       n_sink, global_pos_host, n_global, sel, scores, a);
+  const bsattn_status st = select_args(shape, Q, mean, mean_dtype, factor, factor_dtype, factor_scale, rank,
+                                       nblk_capacity, top_k, window, n_sink, global_pos_host, n_global, sel,
+                                       scores, a);
   if (st != BSATTN_OK) return st;
   hipError_t e = bsattn::launch_select_topk(a, (hipStream_t)hip_stream);
   if (e != hipSuccess) return fail(BSATTN_ERR_HIP, "select launch: %s", hipGetErrorString(e));
@@ -355,15 +374,17 @@ bsattn_status bsattn_decode(const bsattn_shape* shape, const void* Q, const void
 }
 
 bsattn_status bsattn_decode_step(const bsattn_shape* shape, const void* Q, const void* K, const void* V,
-                                 const void* mean, int32_t mean_dtype, const float* factor, int32_t rank,
+                                 const void* mean, int32_t mean_dtype, const void* factor,
+                                 int32_t factor_dtype, const float* factor_scale, int32_t rank,
                                  int32_t nblk_capacity,
                                  int32_t top_k, int32_t window, int32_t n_sink, const int32_t* global_pos_host,
                                  int32_t n_global, int32_t* sel, float* scores, float* O, float* lse,
                                  void* workspace, size_t ws_bytes, void* hip_stream) {
   g_err[0] = 0;
   bsattn::SelectArgs sa;
-  bsattn_status st = select_args(shape, Q, mean, mean_dtype, factor, rank, nblk_capacity, top_k, window, n_sink,
-                                 global_pos_host, n_global, sel, scores, sa);
+  bsattn_status st = select_args(shape, Q, mean, mean_dtype, factor, factor_dtype, factor_scale, rank,
+                                 nblk_capacity, top_k, window, n_sink, global_pos_host, n_global, sel, scores,
+                                 sa);
   if (st != BSATTN_OK) return st;
   bsattn::DecodeArgs da;
   st = decode_args(shape, Q, K, V, sel, top_k, window, n_sink, global_pos_host, n_global, O, lse, workspace,

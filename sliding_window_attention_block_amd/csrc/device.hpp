@@ -107,6 +107,26 @@ __host__ __device__ inline uint64_t range_mask64(int base, int lo, int hi) {
   return hiMask & ~loMask;
 }
 
+// FP4 E2M1 (sign, 2 exponent bits with bias 1, 1 mantissa bit; magnitudes 0,
+// 0.5, 1, 1.5, 2, 3, 4, 6) as a 4-bit code: the value nearest to v, on a tie
+// the code whose mantissa bit is 0.  The magnitude code is the number of
+// midpoints between neighbouring values below |v|, counting a midpoint that
+// |v| equals only when the code above it is even.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = fabsf(v);
+  const uint32_t m = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+  return m | ((v < 0.f && m != 0u) ? 8u : 0u);
+}
+// Value of an E2M1 code (low 4 bits of c), built as float32 bits: exponent
+// e > 0 gives 2^(e-1) (1 + m/2); e = 0 gives m/2.
+__device__ __forceinline__ float e2m1_value(uint32_t c) {
+  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
+  uint32_t bits = e ? (((e + 126u) << 23) | (m << 22)) : (m ? 0x3F000000u : 0u);
+  bits |= (c & 8u) << 28;
+  return __uint_as_float(bits);
+}
+
 // Order-preserving 32-bit key of a float: larger float, larger unsigned key
 // (-0 and +0 share the key of +0, as they compare equal).
 __device__ __forceinline__ uint32_t order_key(float f) {

@@ -13,7 +13,8 @@ namespace bsattn {
 struct SummaryArgs {
   const void* K;
   void* mean;       // fp32, or bf16 when mean_bf16
-  float* factor;
+  void* factor;        // fp32 rows [.., rank, d], or FP4 E2M1 codes [.., rank, d / 2] when factor_fp4
+  float* factor_scale;  // FP4: one scale per factor row [.., rank]
   int32_t bh;            // B * Hkv
   int32_t kv_capacity;   // token stride
   int32_t nblk_capacity;
@@ -23,13 +24,15 @@ struct SummaryArgs {
   int32_t head_dim;
   bool bf16;
   bool mean_bf16;  // store the block mean in bfloat16 (round to nearest even)
+  bool factor_fp4;  // store factor rows as FP4 E2M1 codes with a float32 scale per row
 };
 hipError_t launch_summaries(const SummaryArgs& a, hipStream_t stream);
 
 struct SelectArgs {
   const void* Q;
   const void* mean;  // fp32, or bf16 when mean_bf16
-  const float* factor;
+  const void* factor;        // fp32 rows, or FP4 E2M1 codes when factor_fp4
+  const float* factor_scale;  // FP4: one scale per factor row
   int32_t* sel;
   float* scores;
   int32_t batch, n_q_heads, n_kv_heads, head_dim;
@@ -45,6 +48,7 @@ struct SelectArgs {
   int32_t per_wave, n_part;
   bool scores_only;  // skip the top-k launch (the fused decode step selects)
   bool mean_bf16;    // the block means are bfloat16
+  bool factor_fp4;   // the factor rows are FP4 E2M1 codes + row scales
 };
 hipError_t launch_select_topk(const SelectArgs& a, hipStream_t stream);
 

@@ -46,7 +46,7 @@ constexpr bool scores_heavy(int GM, int RM, int PB, int D) {
   return GM * (D / 16) + 2 * PB * (1 + RM) * (D / 16) > 160;
 }
 
-template <int D, int GM, int RM, int PB, bool BF16, bool MB>
+template <int D, int GM, int RM, int PB, bool BF16, bool MB, bool F4>
 __global__ __launch_bounds__(256, scores_heavy(GM, RM, PB, D) ? 1 : 2) void select_scores_kernel(SelectArgs a) {
   constexpr int SL = D / 16;  // dims per lane: 4-dim chunks sub, 16 + sub, ...
   constexpr int NC = SL / 4;  // 16-byte chunks per lane per row
@@ -94,10 +94,15 @@ __global__ __launch_bounds__(256, scores_heavy(GM, RM, PB, D) ? 1 : 2) void sele
   // time so the loads stay plain) chunk
   using MeanChunk = typename std::conditional<MB, u32x2, float4>::type;
   const MeanChunk* mean4 = reinterpret_cast<const MeanChunk*>(a.mean);
+  // factor rows: 4 dims per 16-byte fp32 chunk, or per 2 bytes of FP4 codes
+  // (dim k of the chunk in bits 4k .. 4k+3) with the row's scale beside them
+  using FacChunk = typename std::conditional<F4, uint32_t, float4>::type;
   const float4* fac4 = reinterpret_cast<const float4*>(a.factor);
+  const uint16_t* fac2 = reinterpret_cast<const uint16_t*>(a.factor);
   struct Stage {
     MeanChunk m[PB][NC];
-    float4 v[PB][RM > 0 ? RM : 1][NC];  // factor rows
+    FacChunk v[PB][RM > 0 ? RM : 1][NC];
+    float fs[PB][RM > 0 ? RM : 1];  // FP4 row scales
   };
   // Every load is issued unconditionally (blocks past the end re-read the last
   // block, factor rows past the rank re-read the last row, both ignored), so
@@ -112,8 +117,14 @@ __global__ __launch_bounds__(256, scores_heavy(GM, RM, PB, D) ? 1 : 2) void sele
 #pragma unroll
       for (int i = 0; i < RM; ++i) {
         const size_t fr = row * rank + min(i, rank - 1);
+        if constexpr (F4) {
 #pragma unroll
-        for (int c = 0; c < NC; ++c) st.v[p][i][c] = fac4[fr * (D / 4) + 16 * c + sub];
+          for (int c = 0; c < NC; ++c) st.v[p][i][c] = fac2[fr * (D / 4) + 16 * c + sub];
+          st.fs[p][i] = a.factor_scale[fr];
+        } else {
+#pragma unroll
+          for (int c = 0; c < NC; ++c) st.v[p][i][c] = fac4[fr * (D / 4) + 16 * c + sub];
+        }
       }
     }
   };
@@ -148,9 +159,20 @@ __global__ __launch_bounds__(256, scores_heavy(GM, RM, PB, D) ? 1 : 2) void sele
 #pragma unroll
       for (int i = 0; i < RM; ++i) {
         if (i < rank) {
+          float4 fv[NC];
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            if constexpr (F4) {
+              const uint32_t w = st.v[p][i][c];
+              fv[c] = float4{e2m1_value(w), e2m1_value(w >> 4), e2m1_value(w >> 8), e2m1_value(w >> 12)};
+            } else {
+              fv[c] = st.v[p][i][c];
+            }
+          }
 #pragma unroll
           for (int h = 0; h < GM; ++h) {
-            const float pr = row16_sum(dot(st.v[p][i], h));
+            float pr = row16_sum(dot(fv, h));
+            if constexpr (F4) pr *= st.fs[p][i];  // the row's scale, once per projection
             s[h] = fmaf(0.5f * pr, pr, s[h]);
           }
         }
@@ -210,6 +232,174 @@ __global__ __launch_bounds__(256, scores_heavy(GM, RM, PB, D) ? 1 : 2) void sele
     load(u0, A);
     comp(u0, A);
   }
+}
+
+// MFMA scoring, for bfloat16 queries and means with FP4 factor rows or none:
+// every operand is exact in bfloat16 (FP4 E2M1 values are), so the products
+// are exact and the sums are fp32, as in the VALU kernel above.  One wave
+// scores a run of 16-block units of one (b, K/V head) pair with
+// v_mfma_f32_16x16x32_bf16: the A operand holds the group's query heads (row m
+// = head m, zero past the group), the B operand the 16 blocks' summary rows
+// (column n = block n of the unit), so lane l ends with block l % 16's dot
+// products for heads 4 (l / 16) .. +3.  The softmax scale, and an FP4 row's
+// scale, multiply the fp32 dot products afterwards.
+//
+// Loads: a mean row is 2D bytes; in k-step s lane (n, kg = l / 16) reads the
+// 16 bytes of dims 32 s + 8 kg .. +7 (64 contiguous bytes per row per
+// instruction).  An FP4 row is D/2 bytes; lane kg reads its D/8 bytes at once
+// (dims kg D/4 .. +D/4) and converts 8 codes per k-step, dims kg D/4 + 8 s + t,
+// so the factor MFMAs take the queries in that order (a second A operand).
+template <int D, int RM>
+__global__ __launch_bounds__(256, 2) void select_scores_mfma_kernel(SelectArgs a) {
+  constexpr int KS = D / 32;  // k-steps
+  using FacLoad = typename std::conditional<D == 128, u32x4, u32x2>::type;  // D/8 bytes
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gw = blockIdx.x * 4 + wid;
+  const int n_pairs = a.batch * a.n_kv_heads;
+  const int pair = gw / a.n_part, wi = gw % a.n_part;
+  if (pair >= n_pairs) return;  // no barriers: waves are independent
+  const int col = lane & 15, kg = lane >> 4;
+  const int b = pair / a.n_kv_heads, g = pair % a.n_kv_heads;
+  const int G = a.n_q_heads / a.n_kv_heads;
+  const int NB = a.n_blocks;
+  const int rank = a.rank;
+
+  bf16x8 qm[KS], qf[RM > 0 ? KS : 1];
+  {
+    const uint16_t* qrow =
+        reinterpret_cast<const uint16_t*>(a.Q) + ((size_t)b * a.n_q_heads + g * G + min(col, G - 1)) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * kg);
+      if (col >= G) v = u32x4{0u, 0u, 0u, 0u};
+      qm[s] = __builtin_bit_cast(bf16x8, v);
+      if constexpr (RM > 0) {
+        u32x4 w = *reinterpret_cast<const u32x4*>(qrow + kg * (D / 4) + 8 * s);
+        if (col >= G) w = u32x4{0u, 0u, 0u, 0u};
+        qf[s] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+  }
+
+  struct Stage {
+    u32x4 m[KS];
+    FacLoad f[RM > 0 ? RM : 1];
+    float fs[RM > 0 ? RM : 1];
+  };
+  // every load is issued (blocks past the end re-read the last block, factor
+  // rows past the rank the last row; both ignored), as in the VALU kernel
+  auto load = [&](int u, Stage& st) __attribute__((always_inline)) {
+    const int j = min(u * 16 + col, NB - 1);
+    const size_t row = (size_t)pair * a.nblk_capacity + j;
+    const u32x4* mrow = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.mean) + row * D);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) st.m[s] = mrow[4 * s + kg];
+#pragma unroll
+    for (int i = 0; i < RM; ++i) {
+      const size_t fr = row * rank + min(i, rank - 1);
+      st.f[i] = reinterpret_cast<const FacLoad*>(reinterpret_cast<const uint8_t*>(a.factor) + fr * (D / 2))[kg];
+      st.fs[i] = a.factor_scale[fr];
+    }
+  };
+  auto comp = [&](int u, const Stage& st) __attribute__((always_inline)) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qm[s], __builtin_bit_cast(bf16x8, st.m[s]), acc, 0, 0, 0);
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] = acc[i] * a.scale;
+#pragma unroll
+    for (int r = 0; r < RM; ++r) {
+      if (r < rank) {
+        f32x4 pa = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const uint32_t w = st.f[r][s];  // 8 codes, dim kg D/4 + 8 s + t in bits 4t .. 4t+3
+          const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.f, 0);
+          const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.f, 1);
+          const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.f, 2);
+          const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.f, 3);
+          const bf16x8 bv = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+          pa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[s], bv, pa, 0, 0, 0);
+        }
+        const float c = a.scale * st.fs[r];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pr = pa[i] * c;
+          sc[i] = fmaf(0.5f * pr, pr, sc[i]);
+        }
+      }
+    }
+    // group score: log-sum-exp over the G heads, spread over the lane groups kg
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * kg + i < G) mx = fmaxf(mx, sc[i]);
+    if (G > 4) mx = fmaxf(mx, __shfl_xor(mx, 16));
+    if (G > 8) mx = fmaxf(mx, __shfl_xor(mx, 32));
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * kg + i < G) sum += __builtin_amdgcn_exp2f((sc[i] - mx) * kLog2e);
+    if (G > 4) sum += __shfl_xor(sum, 16);
+    if (G > 8) sum += __shfl_xor(sum, 32);
+    const int j = u * 16 + col;
+    // sum >= 1 (the max term is exactly 1): log2 needs no range care
+    if (kg == 0 && j < NB) a.scores[(size_t)pair * a.nblk_capacity + j] = fmaf(__builtin_amdgcn_logf(sum), kLn2, mx);
+  };
+
+  const int n_units = (NB + 15) / 16;
+  const int u0 = wi * a.per_wave, u1 = min(u0 + a.per_wave, n_units);
+  const int n = u1 - u0;
+  Stage A, B;
+  if (n >= 4) {
+    load(u0, A);
+    load(u0 + 1, B);
+    int u = u0;
+    for (; u + 3 < u1; u += 2) {
+      comp(u, A);
+      load(u + 2, A);
+      comp(u + 1, B);
+      load(u + 3, B);
+    }
+    if (u + 2 < u1) {
+      comp(u, A);
+      load(u + 2, A);
+      comp(u + 1, B);
+      comp(u + 2, A);
+    } else {
+      comp(u, A);
+      comp(u + 1, B);
+    }
+  } else if (n == 3) {
+    load(u0, A);
+    load(u0 + 1, B);
+    comp(u0, A);
+    load(u0 + 2, A);
+    comp(u0 + 1, B);
+    comp(u0 + 2, A);
+  } else if (n == 2) {
+    load(u0, A);
+    load(u0 + 1, B);
+    comp(u0, A);
+    comp(u0 + 1, B);
+  } else if (n == 1) {
+    load(u0, A);
+    comp(u0, A);
+  }
+}
+
+// Splits `units` per pair over the resident wave slots: as few units per wave
+// as keeps every wave resident at once.
+inline void split_units(SelectArgs& a, long long units, int slots) {
+  const int n_pairs = a.batch * a.n_kv_heads;
+  long long c = (n_pairs * units + slots - 1) / slots;
+  if (c < 1) c = 1;
+  while (c < units && (long long)n_pairs * ((units + c - 1) / c) > slots) ++c;
+  a.per_wave = (int)c;
+  a.n_part = (int)((units + c - 1) / c);
 }
 
 constexpr int kTopkThreads = 1024;
@@ -330,33 +520,55 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
   for (int i = kk + tid; i < a.top_k; i += kTopkThreads) out[i] = -1;
 }
 
+hipError_t launch_topk(const SelectArgs& a, hipStream_t stream) {
+  const int per = (a.n_blocks + kTopkThreads - 1) / kTopkThreads;
+  const dim3 tg(a.batch * a.n_kv_heads), tb(kTopkThreads);
+  if (per <= 2) hipLaunchKernelGGL(topk_kernel<2>, tg, tb, 0, stream, a);
+  else if (per <= 8) hipLaunchKernelGGL(topk_kernel<8>, tg, tb, 0, stream, a);
+  else if (per <= 32) hipLaunchKernelGGL(topk_kernel<32>, tg, tb, 0, stream, a);
+  else hipLaunchKernelGGL(topk_kernel<64>, tg, tb, 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D, int RM>
+hipError_t launch_mfma(const SelectArgs& a0, hipStream_t stream) {
+  SelectArgs a = a0;
+  if (a.n_blocks > 0) {
+    split_units(a, (a.n_blocks + 15) / 16, 256 * 8);
+    const long long waves = (long long)a.batch * a.n_kv_heads * a.n_part;
+    hipLaunchKernelGGL((select_scores_mfma_kernel<D, RM>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, a);
+  }
+  if (a.scores_only) return hipGetLastError();
+  return launch_topk(a, stream);
+}
+
+template <int D>
+hipError_t launch_mfma_r(const SelectArgs& a, hipStream_t stream) {
+  if (a.rank == 0) return launch_mfma<D, 0>(a, stream);
+  if (a.rank <= 2) return launch_mfma<D, 2>(a, stream);
+  if (a.rank <= 4) return launch_mfma<D, 4>(a, stream);
+  return launch_mfma<D, 8>(a, stream);
+}
+
 template <int D, int GM, int RM, bool BF16>
 hipError_t launch_t(const SelectArgs& a0, hipStream_t stream) {
   constexpr int PB = RM == 0 ? 4 : (RM <= 2 ? 2 : 1);  // blocks per 16-lane row per unit
   SelectArgs a = a0;
   const int n_pairs = a.batch * a.n_kv_heads;
   if (a.n_blocks > 0) {
-    // as few units per wave as keeps every wave resident at once
-    const int slots = 256 * (scores_heavy(GM, RM, PB, D) ? 4 : 8);
-    const long long units = (a.n_blocks + 4 * PB - 1) / (4 * PB);
-    long long c = (n_pairs * units + slots - 1) / slots;
-    if (c < 1) c = 1;
-    while (c < units && (long long)n_pairs * ((units + c - 1) / c) > slots) ++c;
-    a.per_wave = (int)c;
-    a.n_part = (int)((units + c - 1) / c);
+    split_units(a, (a.n_blocks + 4 * PB - 1) / (4 * PB), 256 * (scores_heavy(GM, RM, PB, D) ? 4 : 8));
     const long long waves = (long long)n_pairs * a.n_part;
     const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
-    if (a.mean_bf16) hipLaunchKernelGGL((select_scores_kernel<D, GM, RM, PB, BF16, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((select_scores_kernel<D, GM, RM, PB, BF16, false>), grid, block, 0, stream, a);
+    if (RM > 0 && a.factor_fp4) {
+      if (a.mean_bf16) hipLaunchKernelGGL((select_scores_kernel<D, GM, RM, PB, BF16, true, RM != 0>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((select_scores_kernel<D, GM, RM, PB, BF16, false, RM != 0>), grid, block, 0, stream, a);
+    } else {
+      if (a.mean_bf16) hipLaunchKernelGGL((select_scores_kernel<D, GM, RM, PB, BF16, true, false>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((select_scores_kernel<D, GM, RM, PB, BF16, false, false>), grid, block, 0, stream, a);
+    }
   }
   if (a.scores_only) return hipGetLastError();
-  const int per = (a.n_blocks + kTopkThreads - 1) / kTopkThreads;
-  const dim3 tg(n_pairs), tb(kTopkThreads);
-  if (per <= 2) hipLaunchKernelGGL(topk_kernel<2>, tg, tb, 0, stream, a);
-  else if (per <= 8) hipLaunchKernelGGL(topk_kernel<8>, tg, tb, 0, stream, a);
-  else if (per <= 32) hipLaunchKernelGGL(topk_kernel<32>, tg, tb, 0, stream, a);
-  else hipLaunchKernelGGL(topk_kernel<64>, tg, tb, 0, stream, a);
-  return hipGetLastError();
+  return launch_topk(a, stream);
 }
 
 template <int D, int GM, bool BF16>
@@ -378,6 +590,9 @@ hipError_t launch_g(const SelectArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_select_topk(const SelectArgs& a, hipStream_t stream) {
+  // every operand exact in bfloat16: the MFMA scorer
+  if (a.bf16 && a.mean_bf16 && (a.rank == 0 || a.factor_fp4))
+    return a.head_dim == 64 ? launch_mfma_r<64>(a, stream) : launch_mfma_r<128>(a, stream);
   if (a.head_dim == 64) return a.bf16 ? launch_g<64, true>(a, stream) : launch_g<64, false>(a, stream);
   return a.bf16 ? launch_g<128, true>(a, stream) : launch_g<128, false>(a, stream);
 }

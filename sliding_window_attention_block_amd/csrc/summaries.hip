@@ -270,8 +270,22 @@ __global__ __launch_bounds__(256) void summaries_factor_kernel(SummaryArgs a) {
       if (ob > best || (ob == best && oi < bidx)) { best = ob; bidx = oi; }
     }
     const float sign = F[i * D + bidx] < 0.f ? -1.f : 1.f;
-    float* dst = a.factor + (((size_t)bh * a.nblk_capacity + blk) * a.rank + i) * D;
-    for (int d = lane; d < D; d += 64) dst[d] = sign * F[i * D + d];
+    const size_t frow = ((size_t)bh * a.nblk_capacity + blk) * a.rank + i;
+    if (a.factor_fp4) {
+      // FP4 E2M1 with one scale per row: scale = row max / 6, each entry the
+      // nearest E2M1 value of entry / scale; lane l packs entries 2l (low
+      // nibble) and 2l + 1 into byte l
+      const float scale = best / 6.0f;
+      for (int l = lane; l < D / 2; l += 64) {
+        const float v0 = scale > 0.f ? (sign * F[i * D + 2 * l]) / scale : 0.f;
+        const float v1 = scale > 0.f ? (sign * F[i * D + 2 * l + 1]) / scale : 0.f;
+        static_cast<uint8_t*>(a.factor)[frow * (D / 2) + l] = (uint8_t)(e2m1_code(v0) | (e2m1_code(v1) << 4));
+      }
+      if (lane == 0) a.factor_scale[frow] = scale;
+    } else {
+      float* dst = static_cast<float*>(a.factor) + frow * D;
+      for (int d = lane; d < D; d += 64) dst[d] = sign * F[i * D + d];
+    }
   }
 }
 

@@ -33,13 +33,14 @@ def as_f64(arr):
 
 
 def gpu_decode_step(api, x, w, kv_capacity=None, nblk_capacity=None, global_pos=(), dev=None,
-                    one_call=False, mean_dtype="f32"):
+                    one_call=False, mean_dtype="f32", factor_fp4=False):
     """Run summaries -> select/top-k -> decode on the GPU through the binding.
 
     ``x`` holds Q, K, V numpy arrays (float32 or bf16 bits) of workload ``w``.
     With ``one_call`` the step is bsattn_decode_step (selection and decode in one
     call); otherwise bsattn_select_topk, then bsattn_decode.  ``mean_dtype`` "bf16"
-    stores the block means in bfloat16.
+    stores the block means in bfloat16; ``factor_fp4`` the factor rows as FP4 codes
+    (returned as ``factor`` uint8 codes plus ``factor_scale``).
     Returns numpy copies of mean (as float32), factor, scores, sel, O, lse.
     """
     torch = torch_mod()
@@ -54,9 +55,13 @@ def gpu_decode_step(api, x, w, kv_capacity=None, nblk_capacity=None, global_pos=
     shape = api.make_shape(B, Hq, Hkv, d, n, kv_capacity=cap, dtype=w.dtype)
     mean = torch.full((B, Hkv, max(nbcap, 1), d), float("nan"), device="cuda",
                       dtype=torch.bfloat16 if mean_dtype == "bf16" else torch.float32)
-    factor = (torch.full((B, Hkv, max(nbcap, 1), w.rank, d), float("nan"), device="cuda")
-              if w.rank > 0 else None)
-    api.bsattn_build_summaries(shape, K, w.rank, 0, nb, max(nbcap, 1), mean, factor)
+    factor = fscale = None
+    if w.rank > 0 and factor_fp4:
+        factor = torch.full((B, Hkv, max(nbcap, 1), w.rank, d // 2), 255, dtype=torch.uint8, device="cuda")
+        fscale = torch.full((B, Hkv, max(nbcap, 1), w.rank), float("nan"), device="cuda")
+    elif w.rank > 0:
+        factor = torch.full((B, Hkv, max(nbcap, 1), w.rank, d), float("nan"), device="cuda")
+    api.bsattn_build_summaries(shape, K, w.rank, 0, nb, max(nbcap, 1), mean, factor, factor_scale=fscale)
     scores = torch.full((B, Hkv, max(nbcap, 1)), float("nan"), device="cuda")
     sel = torch.full((B, Hkv, w.top_k), -7, dtype=torch.int32, device="cuda")
     O = torch.full((B, Hq, d), float("nan"), device="cuda")
@@ -66,13 +71,14 @@ def gpu_decode_step(api, x, w, kv_capacity=None, nblk_capacity=None, global_pos=
     ws = torch.full((nbytes,), 255, dtype=torch.uint8, device="cuda")  # garbage contents
     if one_call:
         api.bsattn_decode_step(shape, Q, K, V, mean, factor, w.rank, max(nbcap, 1), w.top_k, w.window,
-                               w.n_sink, gp, sel, scores, O, lse, ws)
+                               w.n_sink, gp, sel, scores, O, lse, ws, factor_scale=fscale)
     else:
         api.bsattn_select_topk(shape, Q, mean, factor, w.rank, max(nbcap, 1), w.top_k, w.window,
-                               w.n_sink, gp, sel, scores)
+                               w.n_sink, gp, sel, scores, factor_scale=fscale)
         api.bsattn_decode(shape, Q, K, V, sel, w.top_k, w.window, w.n_sink, gp, O, lse, ws)
     torch.cuda.synchronize()
     return dict(mean=mean.float().cpu().numpy(), factor=None if factor is None else factor.cpu().numpy(),
+                factor_scale=None if fscale is None else fscale.cpu().numpy(),
                 scores=scores.cpu().numpy(), sel=sel.cpu().numpy(), O=O.cpu().numpy(),
                 lse=lse.cpu().numpy())
 

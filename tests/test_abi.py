@@ -113,73 +113,70 @@ def test_decode_rejects_bad_arguments():
     assert st == 1
 
 
+STEP_ARGS = ("shape", "Q", "K", "V", "mean", "mean_dtype", "factor", "factor_dtype", "factor_scale",
+             "rank", "nblk", "top_k", "window", "n_sink", "gpos", "n_global", "sel", "scores", "O", "lse",
+             "ws", "ws_bytes", "stream")
+SELECT_ARGS = ("shape", "Q", "mean", "mean_dtype", "factor", "factor_dtype", "factor_scale", "rank", "nblk",
+               "top_k", "window", "n_sink", "gpos", "n_global", "sel", "scores", "stream")
+SUMMARY_ARGS = ("shape", "K", "rank", "first_block", "n_blocks", "nblk", "mean", "mean_dtype", "factor",
+                "factor_dtype", "factor_scale", "stream")
+GOOD = dict(Q=FAKE, K=FAKE, V=FAKE, mean=FAKE, mean_dtype=0, factor=None, factor_dtype=0, factor_scale=None,
+            rank=0, nblk=4, top_k=2, window=64, n_sink=0, gpos=None, n_global=0, sel=FAKE, scores=FAKE,
+            O=FAKE, lse=None, ws=FAKE, ws_bytes=1 << 30, stream=None, first_block=0, n_blocks=4)
+
+
+def _call(fn, names, **over):
+    kw = dict(GOOD, shape=_shape())
+    kw.update(over)
+    return _status(fn, *[kw[n] for n in names])
+
+
 def test_decode_step_rejects_bad_arguments():
-    s = _shape()
-    # shape Q K V mean mean_dtype factor rank nblk top_k window n_sink gpos n_global sel scores O lse
-    # ws ws_bytes stream
-    args = [s, FAKE, FAKE, FAKE, FAKE, 0, None, 0, 4, 2, 64, 0, None, 0, FAKE, FAKE, FAKE, None, FAKE,
-            1 << 30, None]
-    st, _ = _status("bsattn_decode_step", *args[:4], None, *args[5:])          # NULL mean
-    assert st == 1
-    st, _ = _status("bsattn_decode_step", *args[:5], 2, *args[6:])             # unknown mean dtype
-    assert st == 1
-    st, _ = _status("bsattn_decode_step", *args[:7], 1, *args[8:])             # rank 1, NULL factor
-    assert st == 1
-    st, _ = _status("bsattn_decode_step", *args[:8], 3, *args[9:])             # nblk_capacity < 4 blocks
-    assert st == 1
-    st, _ = _status("bsattn_decode_step", *args[:9], 0, *args[10:])            # top_k 0
-    assert st == 1
-    st, _ = _status("bsattn_decode_step", *args[:14], None, *args[15:])        # NULL sel
-    assert st == 1
-    st, _ = _status("bsattn_decode_step", *args[:16], None, *args[17:])        # NULL O
-    assert st == 1
-    st, msg = _status("bsattn_decode_step", *args[:19], 16, None)              # workspace too small
+    f = "bsattn_decode_step"
+    assert _call(f, STEP_ARGS, mean=None)[0] == 1
+    assert _call(f, STEP_ARGS, mean_dtype=2)[0] == 1                      # mean neither fp32 nor bf16
+    assert _call(f, STEP_ARGS, rank=1)[0] == 1                            # rank 1 without a factor
+    assert _call(f, STEP_ARGS, rank=1, factor=FAKE, factor_dtype=2)[0] == 1  # FP4 without scales
+    assert _call(f, STEP_ARGS, rank=1, factor=FAKE, factor_dtype=5)[0] == 1  # unknown factor dtype
+    assert _call(f, STEP_ARGS, nblk=3)[0] == 1                            # nblk_capacity < 4 blocks
+    assert _call(f, STEP_ARGS, top_k=0)[0] == 1
+    assert _call(f, STEP_ARGS, sel=None)[0] == 1
+    assert _call(f, STEP_ARGS, O=None)[0] == 1
+    st, msg = _call(f, STEP_ARGS, ws_bytes=16)                            # workspace too small
     assert st == 4 and "workspace" in msg
-    st, _ = _status("bsattn_decode_step", *args[:3], FAKE + 4, *args[4:])      # misaligned V
-    assert st == 1
+    assert _call(f, STEP_ARGS, V=FAKE + 4)[0] == 1                        # misaligned V
 
 
 @pytest.mark.parametrize("gpos", [(5, 3, 9), (1, 1, 2), (0, 10, 256), (-1, 2, 3)])
 def test_global_positions_are_checked(gpos):
-    st, msg = _status("bsattn_select_topk", _shape(), FAKE, FAKE, 0, None, 0, 4, 2, 64, 0, G3(*gpos), 3,
-                      FAKE, FAKE, None)
+    st, msg = _call("bsattn_select_topk", SELECT_ARGS, gpos=G3(*gpos), n_global=3)
     assert st == 1 and "global" in msg
 
 
 def test_select_rejects_bad_arguments():
-    s = _shape()
-    # shape Q mean mean_dtype factor rank nblk top_k window n_sink gpos n_global sel scores stream
-    st, _ = _status("bsattn_select_topk", s, FAKE, FAKE, 0, None, 2, 4, 2, 64, 0, None, 0, FAKE, FAKE, None)
-    assert st == 1  # rank 2 without a factor
-    st, _ = _status("bsattn_select_topk", s, FAKE, FAKE, 0, FAKE, 9, 4, 2, 64, 0, None, 0, FAKE, FAKE, None)
-    assert st == 1  # rank above 8
-    st, _ = _status("bsattn_select_topk", s, FAKE, FAKE, 0, None, 0, 3, 2, 64, 0, None, 0, FAKE, FAKE, None)
-    assert st == 1  # nblk_capacity below n_ctx / 64
-    st, _ = _status("bsattn_select_topk", s, FAKE, FAKE, 0, None, 0, 4, 2, 64, 0, None, 0, FAKE, None, None)
-    assert st == 1  # scores is required
-    st, _ = _status("bsattn_select_topk", s, FAKE, FAKE, 0, None, 0, 4, 2000, 64, 0, None, 0, FAKE, FAKE, None)
-    assert st == 1  # top_k above the maximum
-    st, msg = _status("bsattn_select_topk", s, FAKE, FAKE, 7, None, 0, 4, 2, 64, 0, None, 0, FAKE, FAKE, None)
-    assert st == 1 and "mean_dtype" in msg  # mean stored as neither fp32 nor bf16
+    f = "bsattn_select_topk"
+    assert _call(f, SELECT_ARGS, rank=2)[0] == 1                          # rank 2 without a factor
+    assert _call(f, SELECT_ARGS, rank=9, factor=FAKE)[0] == 1             # rank above 8
+    assert _call(f, SELECT_ARGS, nblk=3)[0] == 1                          # nblk_capacity below n_ctx / 64
+    assert _call(f, SELECT_ARGS, scores=None)[0] == 1                     # scores is required
+    assert _call(f, SELECT_ARGS, top_k=2000)[0] == 1                      # top_k above the maximum
+    st, msg = _call(f, SELECT_ARGS, mean_dtype=7)
+    assert st == 1 and "mean_dtype" in msg
+    st, msg = _call(f, SELECT_ARGS, rank=4, factor=FAKE, factor_dtype=2, factor_scale=FAKE + 2)
+    assert st == 1 and "factor_scale" in msg                              # misaligned scales
+    assert _call(f, SELECT_ARGS, rank=4, factor=FAKE, factor_dtype=1)[0] == 1  # bf16 factors are not built
     big = _shape(n_ctx=64 * 65537, kv_capacity=64 * 65537)
-    st, _ = _status("bsattn_select_topk", big, FAKE, FAKE, 1, None, 0, 65537, 2, 64, 0, None, 0, FAKE, FAKE,
-                    None)
-    assert st == 2
+    assert _call(f, SELECT_ARGS, shape=big, nblk=65537)[0] == 2
 
 
 def test_summaries_reject_bad_ranges():
-    s = _shape()
-    # shape K rank first_block n_blocks nblk mean mean_dtype factor stream
-    st, _ = _status("bsattn_build_summaries", s, FAKE, 0, 3, 2, 8, FAKE, 0, None, None)
-    assert st == 1  # blocks 3..4 are not complete in 256 tokens
-    st, _ = _status("bsattn_build_summaries", s, FAKE, 0, 0, 4, 3, FAKE, 0, None, None)
-    assert st == 1  # past nblk_capacity
-    st, _ = _status("bsattn_build_summaries", s, FAKE, 4, 0, 4, 4, FAKE, 0, None, None)
-    assert st == 1  # rank 4 without a factor
-    st, _ = _status("bsattn_build_summaries", s, FAKE, 0, 0, 4, 4, FAKE, 3, None, None)
-    assert st == 1  # unknown mean dtype
-    st, _ = _status("bsattn_build_summaries", s, FAKE, 0, 0, 0, 4, FAKE, 1, None, None)
-    assert st == 0  # empty range: nothing to launch
+    f = "bsattn_build_summaries"
+    assert _call(f, SUMMARY_ARGS, first_block=3, n_blocks=2, nblk=8)[0] == 1  # blocks 3..4 incomplete
+    assert _call(f, SUMMARY_ARGS, nblk=3)[0] == 1                             # past nblk_capacity
+    assert _call(f, SUMMARY_ARGS, rank=4)[0] == 1                             # rank 4 without a factor
+    assert _call(f, SUMMARY_ARGS, mean_dtype=3)[0] == 1                       # unknown mean dtype
+    assert _call(f, SUMMARY_ARGS, rank=4, factor=FAKE, factor_dtype=2)[0] == 1  # FP4 without scales
+    assert _call(f, SUMMARY_ARGS, n_blocks=0, mean_dtype=1)[0] == 0           # empty range: no launch
 
 
 def test_prefill_rejects_bad_arguments():

@@ -45,6 +45,9 @@ SMALL = [
     (_w("k_exceeds_candidates", 1, 4, 1, 64, 600, 0, 50, 64, 64, "bf16", 16), (), 0),
     (_w("window_covers_all", 1, 4, 1, 64, 300, 0, 4, 1000, 0, "bf16", 17), (), 0),
     (_w("short_context", 1, 8, 1, 128, 40, 1, 2, 16, 4, "bf16", 18), (), 0),
+    # groups that end inside a 4-head lane group (MFMA scorer: 3 of 4, 12 of 16 heads)
+    (_w("bf16_g3_d64_r0", 2, 6, 2, 64, 2000, 0, 9, 128, 16, "bf16", 40), (50, 1300), 0),
+    (_w("bf16_g12_d128_r3", 1, 24, 2, 128, 1900, 3, 7, 200, 64, "bf16", 41), (), 0),
 ]
 
 
@@ -239,6 +242,95 @@ def test_bf16_means_small_cases(api, case):
                                         ("cobs_decode_128k", [(2, 5)])])
 def test_bf16_means_full_size(api, name, pairs):
     _full_size(api, name, pairs, one_call=True, mean_dtype="bf16")
+
+
+E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def _unpack_fp4(codes, scale):
+    """Test-side decoding of packed FP4 codes [..., d/2] (entry 2i in the low nibble)
+    with row scales [...]: values [..., d] and the 4-bit codes."""
+    c = np.stack([codes & 15, codes >> 4], axis=-1).reshape(*codes.shape[:-1], -1)
+    val = np.where(c & 8, -E2M1[c & 7], E2M1[c & 7]) * scale.astype(np.float64)[..., None]
+    return val, c
+
+
+def _check_fp4(api, w, globals_, pairs=None, one_call=True, mean_dtype="bf16"):
+    """FP4 factor rows.  The GPU quantises its fp32 eigensolver's rows, the oracle its
+    fp64 rows, so a code can differ where the exact value sits at a rounding midpoint:
+    codes must match the oracle's except for at most 1% of entries, each one E2M1 step
+    away; scales to 1e-3.  Scores are compared with the oracle's (from its own FP4
+    rows) within a per-block bound computed here from how the two sets of codes differ
+    (1/2 |(p + e)^2 - p^2| <= (|p| + |e|/2) |e| per row, p the oracle's projection, e
+    bounded by |q| . |row difference|), and the selections may differ only within that
+    bound of the k-th score.  Outputs: the usual bar over the GPU's selection."""
+    x = make_decode_inputs(w)
+    print(f"[decode fp4] {w.name} one_call={one_call} mean={mean_dtype}", flush=True)
+    got = gpu_decode_step(api, x, w, global_pos=globals_, one_call=one_call, mean_dtype=mean_dtype,
+                          factor_fp4=True)
+    Q, K, V = as_f64(x["Q"]), as_f64(x["K"]), as_f64(x["V"])
+    S, n, G, d, r = w.block_size, w.n_ctx, w.n_q_heads // w.n_kv_heads, w.head_dim, w.rank
+    nb = n // S
+    scale = default_scale(d)
+    forced = oracle.forced_token_mask(n, w.n_sink, w.window, globals_)
+    cand = oracle.candidate_blocks(n, S, forced)
+    if pairs is None:
+        pairs = [(b, g) for b in range(w.batch) for g in range(w.n_kv_heads)]
+    n_codes = n_flips = 0
+    for (b, g) in pairs:
+        mean, f = oracle.block_summaries(K[b, g, :n], S, r, mean_bf16=mean_dtype == "bf16")
+        if nb == 0:
+            continue
+        codes_or, sc_or = oracle.quantize_e2m1_rows(f)
+        deq_or = oracle.dequantize_e2m1_rows(codes_or, sc_or)
+        deq_gpu, codes_gpu = _unpack_fp4(got["factor"][b, g, :nb], got["factor_scale"][b, g, :nb])
+        # blocks whose top r+1 eigenvalues are separated: rows defined up to sign (fixed)
+        X = K[b, g, :nb * S].reshape(nb, S, d)
+        Xc = X - X.mean(axis=1, keepdims=True)
+        lam = np.sort(np.linalg.eigvalsh(np.einsum("brd,bre->bde", Xc, Xc) / S), axis=1)[:, ::-1]
+        gaps = np.min(np.abs(np.diff(lam[:, :r + 1], axis=1)), axis=1) / np.maximum(lam[:, 0], 1e-30)
+        ok = gaps > 1e-3
+        assert np.all(np.abs(got["factor_scale"][b, g, :nb][ok] / np.where(sc_or[ok] > 0, sc_or[ok], 1) - 1) < 1e-3)
+        diff = codes_gpu[ok] != codes_or[ok]
+        n_codes += diff.size
+        n_flips += int(diff.sum())
+        assert np.all(np.abs(deq_gpu[ok] - deq_or[ok])[diff] <= 2.0 * np.max(sc_or[ok]) * 1.001)
+        qs = scale * Q[b, g * G:(g + 1) * G]
+        s_ref = oracle.group_scores(oracle.head_scores(qs, mean, deq_or))
+        p = np.einsum("hd,brd->hbr", qs, deq_or)
+        e = np.einsum("hd,brd->hbr", np.abs(qs), np.abs(deq_gpu - deq_or))
+        bound = np.max(np.sum((np.abs(p) + e / 2) * e, axis=2), axis=0) + 2e-4 * (1 + np.abs(s_ref))
+        assert np.all(np.abs(got["scores"][b, g, :nb] - s_ref)[ok] <= bound[ok])
+        # selection within the quantisation band of the k-th score
+        ref = oracle.top_k_blocks(s_ref, cand, w.top_k)
+        gsel = got["sel"][b, g]
+        assert len(gsel[gsel >= 0]) == len(ref[ref >= 0])
+        odd = set(gsel[gsel >= 0].tolist()) ^ set(ref[ref >= 0].tolist())
+        if odd:
+            ks = np.sort(s_ref[cand])[::-1][min(w.top_k, len(cand)) - 1]
+            band = 2 * np.max(bound[cand][ok[cand]]) + 1e-4 * abs(ks)
+            assert all((not ok[j]) or abs(s_ref[j] - ks) <= band for j in odd), f"selection at ({b}, {g})"
+        o_ref, lse_ref = oracle_decode_with_sel(Q[b, g * G:(g + 1) * G], K[b, g], V[b, g], n, S, w.window,
+                                                w.n_sink, globals_, gsel, scale)
+        assert max_abs(got["O"][b, g * G:(g + 1) * G], o_ref) < OUT_TOL
+        assert max_abs(got["lse"][b, g * G:(g + 1) * G], lse_ref) < OUT_TOL
+    if n_codes:
+        print(f"[decode fp4] {w.name}: {n_flips} of {n_codes} codes one step from the oracle's", flush=True)
+        assert n_flips <= 0.01 * n_codes
+
+
+FP4_CASES = [c for c in SMALL if c[0].rank > 0]
+
+
+@pytest.mark.parametrize("case", FP4_CASES, ids=[c[0].name for c in FP4_CASES])
+@pytest.mark.parametrize("one_call", [False, True])
+def test_fp4_factors_small_cases(api, case, one_call):
+    w, globals_, _ = case
+    _check_fp4(api, w, globals_, one_call=one_call, mean_dtype="bf16" if one_call else "f32")
+
+
+def test_fp4_factors_cobs_128k(api):
+    _check_fp4(api, WORKLOADS["cobs_decode_128k"], (), pairs=[(0, 0), (3, 6)])
 
 
 def test_repeated_calls_reuse_the_workspace(api):
