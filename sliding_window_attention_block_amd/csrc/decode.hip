@@ -659,10 +659,11 @@ __global__ __launch_bounds__(64 * kW) void decode_f32_kernel(DecodeArgs a) {
 // Merge the partials of every query head: per dim,
 // O = sum_s w_s o_s / sum_s w_s l_s with w_s = 2^(m_s - M); lse = ln 2 (M + log2 L).
 // One wave per (b, query head); lane owns dims lane + 64e; the partials are read
-// 32 at a time (all loads of a chunk in flight together) and folded online.
-template <int D>
+// CH at a time (all loads of a chunk in flight together; CH the smallest of 8,
+// 16, 32 that holds them all, else 32) and folded online.
+template <int D, int CH>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
-  constexpr int DL = D / 64, CH = 32;
+  constexpr int DL = D / 64;
   const size_t qrow = blockIdx.x;  // b * Hq + h
   const int lane = threadIdx.x;
   const int n = a.n_part;
@@ -724,7 +725,10 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_part == 1) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(a.batch * a.n_q_heads), dim3(64), 0, stream, a);
+  const dim3 mg(a.batch * a.n_q_heads), mb(64);
+  if (a.n_part <= 8) hipLaunchKernelGGL((decode_merge_kernel<D, 8>), mg, mb, 0, stream, a);
+  else if (a.n_part <= 16) hipLaunchKernelGGL((decode_merge_kernel<D, 16>), mg, mb, 0, stream, a);
+  else hipLaunchKernelGGL((decode_merge_kernel<D, 32>), mg, mb, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -405,32 +405,18 @@ inline void split_units(SelectArgs& a, long long units, int slots) {
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
 
-// Exclusive prefix sum over the workgroup; `tmp` holds kTopkWaves ints.  Returns the
-// exclusive prefix and writes the total.
-__device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int incl = wave_incl_scan(v);
-  if (lane == 63) tmp[wid] = incl;
-  __syncthreads();
-  int before = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kTopkWaves; ++w) {
-    const int t = tmp[w];
-    before += (w < wid) ? t : 0;
-    tot += t;
-  }
-  __syncthreads();
-  *total = tot;
-  return before + incl - v;
-}
-
-// One workgroup of 1024 threads per (b, K/V head).  Thread t owns the contiguous
-// block range [t*per, (t+1)*per); keys stay in registers when per <= KPT.
+// One workgroup of kTopkThreads threads per (b, K/V head).  Thread t owns the contiguous
+// block range [t*per, (t+1)*per); its keys stay in registers (per <= KPT).
+// Barriers: one after the candidate count / AND / OR reduction (which also
+// clears the four pass histograms), one per radix pass (every wave then finds
+// the pass's digit from the histogram itself), one for the output scan.  Bytes
+// on which all candidate keys agree are skipped, and the passes stop once the
+// k-th key's bin is taken whole.
 template <int KPT>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
-  __shared__ uint32_t hist[256];
-  __shared__ int scan_tmp[kTopkWaves];
-  __shared__ int s_digit, s_above;
+  __shared__ uint32_t hist[4][256];
+  __shared__ uint32_t red[kTopkWaves][3];  // per wave: candidates, AND, OR of their keys
+  __shared__ int part[kTopkWaves][2];      // per wave: keys above, keys on the threshold
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int bh = blockIdx.x;
   const int NB = a.n_blocks;
@@ -439,80 +425,104 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
   const float* sc = a.scores + (size_t)bh * a.nblk_capacity;
   int32_t* out = a.sel + (size_t)bh * a.top_k;
 
-  // keys of my candidates (non-candidates are never counted); registers if they fit
-  uint32_t kreg[KPT];
-  uint64_t cmask = 0ull;  // bit t: block j0 + t is a candidate
+  uint32_t key[KPT];
+  uint64_t cm = 0ull;  // bit t: block j0 + t is a candidate
+  uint32_t kand = ~0u, kor = 0u;
 #pragma unroll
   for (int t = 0; t < KPT; ++t) {
     const int j = j0 + t;
-    kreg[t] = 0u;
+    key[t] = 0u;
     if (j < j1) {
-      kreg[t] = order_key(sc[j]);
-      if (forced_mask(a.forced, j) != ~0ull) cmask |= 1ull << t;
+      key[t] = order_key(sc[j]);
+      if (forced_mask(a.forced, j) != ~0ull) {
+        cm |= 1ull << t;
+        kand &= key[t];
+        kor |= key[t];
+      }
     }
   }
-  int tot;
-  const int ncand_dummy = block_excl_scan(__popcll(cmask), scan_tmp, &tot);
-  (void)ncand_dummy;
+  for (int i = tid; i < 4 * 256; i += kTopkThreads) (&hist[0][0])[i] = 0u;
+  {
+    const int cnt = __builtin_amdgcn_readlane(wave_incl_scan_dpp(__popcll(cm)), 63);
+    uint32_t wa, wo;
+    wave_and_or(kand, kor, wa, wo);
+    if (lane == 0) { red[wid][0] = (uint32_t)cnt; red[wid][1] = wa; red[wid][2] = wo; }
+  }
+  __syncthreads();
+  int tot = 0;
+  uint32_t all_and = ~0u, all_or = 0u;
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) {
+    tot += (int)red[w][0];
+    all_and &= red[w][1];
+    all_or |= red[w][2];
+  }
   const int kk = min(a.top_k, tot);
-
-  uint32_t prefix = 0u, pmask = 0u;
+  const uint32_t diff = all_and ^ all_or;
+  // first pass: the byte holding the highest bit on which candidate keys differ
+  const int top = diff ? (31 - __clz(diff)) & ~7 : -8;
+  uint32_t pmask = top >= 24 ? 0u : ~0u << (top + 8);
+  uint32_t prefix = all_and & pmask;
   int remaining = kk;
   if (kk > 0) {
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      if (tid < 256) hist[tid] = 0u;
-      __syncthreads();
+    int pass = 0;
+    for (int shift = top; shift >= 0; shift -= 8, ++pass) {
+      uint32_t* h = hist[pass];
 #pragma unroll
       for (int t = 0; t < KPT; ++t)
-        if (((cmask >> t) & 1ull) && (kreg[t] & pmask) == prefix) atomicAdd(&hist[(kreg[t] >> shift) & 255u], 1u);
+        if (((cm >> t) & 1ull) && (key[t] & pmask) == prefix) atomicAdd(&h[(key[t] >> shift) & 255u], 1u);
       __syncthreads();
-      if (wid == 0) {
-        // lane l owns digits 255-4l .. 252-4l (descending order)
-        int c[4], sum = 0;
+      // every wave: lane l reads digits 255-4l (c4[3]) down to 252-4l (c4[0])
+      const u32x4 c4 = reinterpret_cast<const u32x4*>(h)[63 - lane];
+      const int sum = (int)(c4[0] + c4[1] + c4[2] + c4[3]);
+      int cum = wave_incl_scan_dpp(sum) - sum;
+      int found = -1, above = 0, inbin = 0;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          c[t] = (int)hist[255 - 4 * lane - t];
-          sum += c[t];
+      for (int u = 3; u >= 0; --u) {
+        if (found < 0 && cum + (int)c4[u] >= remaining) {
+          found = 4 * (63 - lane) + u;
+          above = cum;
+          inbin = (int)c4[u];
         }
-        int cum = wave_incl_scan(sum) - sum;
-        int found = -1, above = 0;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          if (found < 0 && cum + c[t] >= remaining) { found = 255 - 4 * lane - t; above = cum; }
-          cum += c[t];
-        }
-        const uint64_t hit = __ballot(found >= 0);
-        const int src = __ffsll((unsigned long long)hit) - 1;
-        if (lane == src) { s_digit = found; s_above = above; }
+        cum += (int)c4[u];
       }
-      __syncthreads();
-      remaining -= s_above;
-      prefix |= (uint32_t)s_digit << shift;
+      const uint64_t hit = __ballot(found >= 0);
+      const int src = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
+      const int digit = __builtin_amdgcn_readlane(found, src);
+      remaining -= __builtin_amdgcn_readlane(above, src);
+      prefix |= (uint32_t)digit << shift;
       pmask |= 255u << shift;
+      // the same in every wave: every key of the bin is taken, lower bytes do not matter
+      if (__builtin_amdgcn_readlane(inbin, src) == remaining) break;
     }
   }
-  // emit: keys above the threshold, then the lowest-index keys equal to it
-  const uint32_t T = prefix;
+  // keys above the prefix, then the first `remaining` keys on it, in block order
   int gt = 0, eq = 0;
-  if (kk > 0) {
 #pragma unroll
-    for (int t = 0; t < KPT; ++t) {
-      if (!((cmask >> t) & 1ull)) continue;
-      gt += kreg[t] > T;
-      eq += kreg[t] == T;
-    }
+  for (int t = 0; t < KPT; ++t) {
+    if (!((cm >> t) & 1ull)) continue;
+    const uint32_t km = key[t] & pmask;
+    gt += km > prefix;
+    eq += km == prefix;
   }
-  const int eq_before = block_excl_scan(eq, scan_tmp, &tot);
-  const int take_eq = max(0, min(eq, remaining - eq_before));
-  const int cnt = gt + take_eq;
-  int pos = block_excl_scan(cnt, scan_tmp, &tot);
-  if (kk > 0 && cnt > 0) {
+  const int igt = wave_incl_scan_dpp(gt), ieq = wave_incl_scan_dpp(eq);
+  if (lane == 63) { part[wid][0] = igt; part[wid][1] = ieq; }
+  __syncthreads();
+  int gt_before = igt - gt, eq_before = ieq - eq;
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) {
+    if (w < wid) { gt_before += part[w][0]; eq_before += part[w][1]; }
+  }
+  if (kk > 0) {
+    const int take_eq = max(0, min(eq, remaining - eq_before));
+    int pos = gt_before + min(eq_before, remaining);
     int taken = 0;
 #pragma unroll
     for (int t = 0; t < KPT; ++t) {
-      if (!((cmask >> t) & 1ull)) continue;
-      if (kreg[t] > T || (kreg[t] == T && taken < take_eq)) {
-        taken += kreg[t] == T;
+      if (!((cm >> t) & 1ull)) continue;
+      const uint32_t km = key[t] & pmask;
+      if (km > prefix || (km == prefix && taken < take_eq)) {
+        taken += km == prefix;
         out[pos++] = j0 + t;
       }
     }
