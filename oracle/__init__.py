@@ -36,6 +36,7 @@ from .selector import (  # noqa: F401
     quantize_e2m1_rows,
     dequantize_e2m1_rows,
     E2M1_MAGNITUDES,
+    query_subspace_basis,
     block_summaries,
     head_scores,
     exact_mass_scores,

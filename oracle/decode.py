@@ -44,13 +44,14 @@ def sparse_decode_group(q, K, V, tokens, scale):
 
 
 def decode_step(Q, K, V, n, S, rank, top_k, window, n_sink, global_pos=(), scale=None,
-                pairs=None, summaries=None, mean_bf16=False, factor_fp4=False):
+                pairs=None, summaries=None, mean_bf16=False, factor_fp4=False, basis=None):
     """One decode step for the query token t = n - 1 of every (batch, K/V head) pair.
 
     Q [B, Hq, d]; K, V [B, Hkv, >= n, d].  ``pairs`` restricts the work to a list of
     (b, kv_head); ``summaries`` may map (b, kv_head) -> (mean, factor) already built;
     ``mean_bf16`` / ``factor_fp4`` store the block means in bfloat16 / the factor rows
-    in FP4 (see ``block_summaries``).
+    in FP4 (see ``block_summaries``); ``basis`` [Hkv, s, d] holds each K/V head's
+    query-subspace rows (factor rows then live in that subspace).
     Returns a dict keyed by (b, kv_head) with:
       'scores'  [NB] group scores of all complete blocks,
       'cand'    candidate block indices,
@@ -74,10 +75,12 @@ def decode_step(Q, K, V, n, S, rank, top_k, window, n_sink, global_pos=(), scale
         if summaries is not None and (b, g) in summaries:
             mean, factor = summaries[(b, g)]
         else:
-            mean, factor = block_summaries(Kbg, S, rank, mean_bf16=mean_bf16, factor_fp4=factor_fp4)
+            mean, factor = block_summaries(Kbg, S, rank, mean_bf16=mean_bf16, factor_fp4=factor_fp4,
+                                           basis=None if basis is None else basis[g])
         q = np.asarray(Q[b, g * G:(g + 1) * G], dtype=np.float64)
         qs = scale * q
-        s = group_scores(head_scores(qs, mean, factor if rank > 0 else None))
+        s = group_scores(head_scores(qs, mean, factor if rank > 0 else None,
+                                     basis=None if basis is None or rank == 0 else basis[g]))
         sel = top_k_blocks(s, cand, top_k)
         tokens = decode_token_set(n, S, forced, sel)
         o, lse = sparse_decode_group(q, Kbg, Vbg, tokens, scale)

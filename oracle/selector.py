@@ -47,6 +47,17 @@ The method, as the COBS explainer states it:
   entry / scale (ties to the even code); the arithmetic of that decision is
   float32.  ``quantize_e2m1_rows`` / ``dequantize_e2m1_rows``;
   ``block_summaries(..., factor_fp4=True)`` returns the dequantized factor.
+* Subspace projection (same section): the covariance is projected onto the
+  subspace spanned by the leading eigenvectors of the queries' second moment,
+  so a factor row holds s numbers instead of d.  Readings: the second moment is
+  the uncentred M = (1/N) sum q q^T of a calibration sample of the group's
+  queries (one subspace per K/V head; the explainer's s is chosen per layer),
+  taken offline; its s leading eigenvectors are the rows of an orthonormal
+  basis P [s, d] (``query_subspace_basis``).  The projected covariance is
+  P Sigma P^T, i.e. the covariance of the projected centred keys P (k - mean);
+  the factor rows are its top-r eigenpairs sqrt(lambda_i) v_i (s numbers, the
+  same sign rule), and the score's second-order term uses the projected query
+  P q: 1/2 sum_i (factor_i . P q)^2.  The mean stays d-dimensional.
 """
 
 from __future__ import annotations
@@ -107,7 +118,28 @@ def round_to_bf16(x):
     return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
 
 
-def block_summaries(K, S, rank, mean_bf16=False, factor_fp4=False):
+def query_subspace_basis(Q_sample, s):
+    """Orthonormal rows P [s, d] spanning the query subspace of a calibration sample.
+
+    The s leading eigenvectors (eigenvalue descending) of the uncentred second
+    moment M = (1/N) sum_n q_n q_n^T of ``Q_sample`` [N, d] (COBS explainer section
+    2.3, subspace projection).  Each row's sign is fixed as for factor rows: its entry
+    of largest magnitude (first on ties) is positive.
+    """
+    Q = np.asarray(Q_sample, dtype=np.float64)
+    d = Q.shape[1]
+    if not 0 < s <= d:
+        raise ValueError("s must be in [1, d]")
+    M = Q.T @ Q / Q.shape[0]
+    _, vec = np.linalg.eigh(M)  # ascending
+    P = vec[:, ::-1][:, :s].T
+    big = np.argmax(np.abs(P), axis=1)
+    sign = np.sign(P[np.arange(s), big])
+    sign[sign == 0] = 1.0
+    return P * sign[:, None]
+
+
+def block_summaries(K, S, rank, mean_bf16=False, factor_fp4=False, basis=None):
     """Per complete block of ``K`` [n, d]: mean [NB, d] and low-rank factor [NB, rank, d].
 
     factor[b, i] = sqrt(lambda_i) * v_i for the i-th largest eigenpair of the block's
@@ -116,7 +148,9 @@ def block_summaries(K, S, rank, mean_bf16=False, factor_fp4=False):
     largest magnitude (first such entry on ties) is positive; the sign never changes a
     score because the score only uses squares of projections.  With ``mean_bf16`` the
     returned mean is rounded to bfloat16 (``round_to_bf16``); with ``factor_fp4`` the
-    returned factor is its FP4 storage, dequantized (``quantize_e2m1_rows``).
+    returned factor is its FP4 storage, dequantized (``quantize_e2m1_rows``).  With a
+    ``basis`` P [s, d] the covariance is the projected P Sigma_b P^T (that of the
+    projected centred keys P (k - mean)) and the factor is [NB, rank, s].
     """
     K = np.asarray(K, dtype=np.float64)
     n, d = K.shape
@@ -126,9 +160,14 @@ def block_summaries(K, S, rank, mean_bf16=False, factor_fp4=False):
     stored = round_to_bf16(mean) if mean_bf16 else mean
     if rank == 0:
         return stored, np.zeros((nb, 0, d))
-    if not 0 < rank <= d:
-        raise ValueError("rank must be in [0, d]")
     C = X - mean[:, None, :]
+    if basis is not None:
+        P = np.asarray(basis, dtype=np.float64)
+        if P.ndim != 2 or P.shape[1] != d:
+            raise ValueError("basis must be [s, d]")
+        C = C @ P.T  # projected centred keys, [nb, S, s]
+    if not 0 < rank <= C.shape[2]:
+        raise ValueError("rank must be in [0, d] (or [0, s] with a basis)")
     sigma = np.einsum("brd,bre->bde", C, C) / S
     lam, vec = np.linalg.eigh(sigma)  # ascending; vec[:, :, i] is the i-th eigenvector
     lam = lam[:, ::-1][:, :rank]
@@ -144,16 +183,19 @@ def block_summaries(K, S, rank, mean_bf16=False, factor_fp4=False):
     return stored, factor
 
 
-def head_scores(q_scaled, mean, factor=None):
+def head_scores(q_scaled, mean, factor=None, basis=None):
     """Per-head block scores s[h, b] for scaled queries ``q_scaled`` [G, d].
 
     First order: q.mean.  With a factor [NB, r, d] (r > 0) the COBS second-order term
-    1/2 sum_i (factor_i . q)^2 = 1/2 q^T (sum_i lambda_i v_i v_i^T) q is added.
+    1/2 sum_i (factor_i . q)^2 = 1/2 q^T (sum_i lambda_i v_i v_i^T) q is added.  With a
+    ``basis`` P [s, d] the factor rows are s-dimensional and meet the projected query
+    P q.
     """
     q = np.asarray(q_scaled, dtype=np.float64)
     s = q @ np.asarray(mean, dtype=np.float64).T
     if factor is not None and factor.shape[1] > 0:
-        proj = np.einsum("hd,brd->hbr", q, np.asarray(factor, dtype=np.float64))
+        qf = q if basis is None else q @ np.asarray(basis, dtype=np.float64).T
+        proj = np.einsum("hd,brd->hbr", qf, np.asarray(factor, dtype=np.float64))
         s = s + 0.5 * (proj ** 2).sum(axis=2)
     return s
 

@@ -17,7 +17,7 @@ import torch
 
 from oracle import (E2M1_MAGNITUDES, block_summaries, candidate_blocks, dequantize_e2m1_rows,
                     exact_mass_scores, forced_token_mask, group_scores, head_scores,
-                    quantize_e2m1_rows, round_to_bf16, top_k_blocks)
+                    quantize_e2m1_rows, round_to_bf16, top_k_blocks, query_subspace_basis)
 from synthetic import WORKLOADS
 
 
@@ -370,3 +370,94 @@ def test_top_k_with_exact_mass_captures_the_most_attention():
 def test_rank_guidance_of_the_page(golden_dir):
     facts = json.load(open(os.path.join(golden_dir, "pages_printed.json")))
     assert WORKLOADS["cobs_decode_128k"].rank <= facts["cobs_rank_guidance"]["max_rank"]
+
+
+# --- query-subspace projection (COBS explainer 2.3, covariance compression) ---
+
+def _orthonormal_rows(rng, s, d):
+    q, _ = np.linalg.qr(rng.standard_normal((d, s)))
+    return q.T  # [s, d]
+
+
+def test_identity_basis_reproduces_the_unprojected_summaries():
+    rng = np.random.default_rng(40)
+    K = rng.standard_normal((5 * 16, 12)) * rng.uniform(0.2, 3.0, 12)
+    m0, f0 = block_summaries(K, 16, 3)
+    m1, f1 = block_summaries(K, 16, 3, basis=np.eye(12))
+    np.testing.assert_allclose(m1, m0, rtol=0, atol=0)
+    np.testing.assert_allclose(f1, f0, rtol=1e-12, atol=1e-12)
+    q = rng.standard_normal((3, 12))
+    np.testing.assert_allclose(head_scores(q, m1, f1, basis=np.eye(12)), head_scores(q, m0, f0),
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_permutation_basis_permutes_the_factor_entries():
+    """Basis rows e_{pi(0)}, e_{pi(1)}, ...: the projected key has entries k[pi(j)], so
+    factor entry j is the unprojected entry pi(j).  A transposed projection (keys times
+    P instead of P^T) would apply the inverse permutation and fail."""
+    rng = np.random.default_rng(41)
+    d = 10
+    perm = np.array([3, 7, 0, 9, 1, 5, 2, 8, 4, 6])
+    assert not np.array_equal(np.argsort(perm), perm)
+    P = np.eye(d)[perm]
+    K = rng.standard_normal((4 * 16, d)) * np.linspace(0.5, 2.5, d)
+    _, f0 = block_summaries(K, 16, 4)
+    _, f1 = block_summaries(K, 16, 4, basis=P)
+    np.testing.assert_allclose(f1, f0[:, :, perm], rtol=1e-12, atol=1e-12)
+
+
+def test_projected_second_order_term_equals_the_key_average_in_the_subspace():
+    """For a query inside the subspace (q = P^T z) and rank = s, the projected term
+    1/2 sum_i (factor_i . P q)^2 is 1/2 q^T Sigma q = 1/2 mean_r (q . (k_r - mean))^2,
+    computed here straight from the keys."""
+    rng = np.random.default_rng(42)
+    d, s, S = 16, 6, 32
+    P = _orthonormal_rows(rng, s, d)
+    K = rng.standard_normal((3 * S, d)) * np.linspace(0.3, 2.0, d)
+    mean, factor = block_summaries(K, S, s, basis=P)
+    z = rng.standard_normal((2, s))
+    q = z @ P
+    got = head_scores(q, mean, factor, basis=P)
+    for b in range(3):
+        X = K[b * S:(b + 1) * S]
+        mu = X.sum(0) / S
+        for h in range(2):
+            quad = sum(float(np.dot(q[h], x - mu)) ** 2 for x in X) / S
+            assert got[h, b] == pytest.approx(float(q[h] @ mu) + 0.5 * quad, rel=1e-10, abs=1e-12)
+    # a query outside the subspace only sees its component inside it
+    q_out = q + rng.standard_normal((2, d)) @ (np.eye(d) - P.T @ P)
+    np.testing.assert_allclose(head_scores(q_out, mean, factor, basis=P) - q_out @ mean.T,
+                               got - q @ mean.T, rtol=1e-10, atol=1e-12)
+
+
+def test_query_subspace_basis_recovers_a_planted_subspace():
+    """Queries q = U z with orthonormal U [d, s0] and independent z_j of variances
+    9 > 4 > 1: the basis spans U, in variance order, with orthonormal rows."""
+    rng = np.random.default_rng(43)
+    d, s0, N = 12, 3, 4000
+    U = _orthonormal_rows(rng, s0, d).T
+    z = rng.standard_normal((N, s0)) * np.array([3.0, 2.0, 1.0])
+    z -= z.mean(0)
+    z = z @ np.linalg.inv(np.linalg.cholesky(z.T @ z / N)).T * np.array([3.0, 2.0, 1.0])
+    Q = z @ U.T
+    P = query_subspace_basis(Q, s0)
+    np.testing.assert_allclose(P @ P.T, np.eye(s0), atol=1e-12)
+    np.testing.assert_allclose(P.T @ P, U @ U.T, atol=1e-10)
+    for j in range(s0):
+        assert abs(float(P[j] @ U[:, j])) == pytest.approx(1.0, abs=1e-10)
+        assert P[j, np.argmax(np.abs(P[j]))] > 0
+    # a wider basis keeps the planted rows first
+    P5 = query_subspace_basis(Q + 1e-3 * rng.standard_normal((N, d)), 5)
+    np.testing.assert_allclose(P5[:s0].T @ P5[:s0], U @ U.T, atol=2e-4)  # noise 1e-3: measured 2.8e-5
+
+
+def test_projected_fp4_factor_rows_have_s_entries():
+    rng = np.random.default_rng(44)
+    d, s, S = 16, 8, 32
+    P = _orthonormal_rows(rng, s, d)
+    K = rng.standard_normal((2 * S, d))
+    _, f = block_summaries(K, S, 3, basis=P)
+    _, f4 = block_summaries(K, S, 3, basis=P, factor_fp4=True)
+    assert f.shape == f4.shape == (2, 3, s)
+    codes, scale = quantize_e2m1_rows(f)
+    np.testing.assert_allclose(f4, dequantize_e2m1_rows(codes, scale), rtol=0, atol=0)
