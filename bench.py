@@ -116,7 +116,7 @@ def to_dev(torch, a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def bench_decode(api, torch, w, x, steps, warmup, mean_dtype="bf16", factor_fp4=True):
+def bench_decode(api, torch, w, x, steps, warmup, mean_dtype="bf16", factor_fp4=True, subspace=True):
     B, Hq, Hkv, d, n, S = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_ctx, w.block_size
     nb = n // S
     shape = api.make_shape(B, Hq, Hkv, d, n, dtype=w.dtype)
@@ -124,12 +124,20 @@ def bench_decode(api, torch, w, x, steps, warmup, mean_dtype="bf16", factor_fp4=
     elem = 2 if w.dtype == "bf16" else 4
     mean_elem = 2 if mean_dtype == "bf16" else 4
     fp4 = factor_fp4 and w.rank > 0
-    factor_row_bytes = (d // 2 + 4) if fp4 else 4 * d  # FP4 codes + float32 scale, or fp32
+    # the page's compressed summary: bf16 mean, FP4 rows in the query subspace
+    sub = w.sub_dim if (subspace and fp4 and mean_dtype == "bf16" and w.sub_dim > 0) else 0
+    e = sub or d
+    factor_row_bytes = (e // 2 + 4) if fp4 else 4 * d  # FP4 codes + float32 scale, or fp32
+    basis_bytes = Hkv * sub * d * 4
     summ_bytes = B * Hkv * nb * (d * mean_elem + w.rank * factor_row_bytes)
     kv_est = B * Hkv * (w.top_k * S + w.n_sink + w.window) * d * 2 * elem
     R = replicas_for(summ_bytes + kv_est)
     log(f"[bench] {w.name}: {R} replicas, {2 * x['K'].nbytes * R / 2**30:.1f} GiB of K/V")
     K0, V0, Q0 = to_dev(torch, x["K"]), to_dev(torch, x["V"]), to_dev(torch, x["Q"])
+    basis = None
+    if sub:  # a random orthonormal frame per K/V head: its values do not change the timing
+        from synthetic import orthonormal_rows
+        basis = torch.from_numpy(orthonormal_rows(np.random.default_rng(w.seed + 1000), Hkv, sub, d)).cuda()
     reps = []
     for r in range(R):
         K = K0 if r == 0 else K0.clone()
@@ -139,7 +147,7 @@ def bench_decode(api, torch, w, x, steps, warmup, mean_dtype="bf16", factor_fp4=
                            dtype=torch.bfloat16 if mean_dtype == "bf16" else torch.float32)
         fscale = None
         if fp4:
-            factor = torch.empty((B, Hkv, nb, w.rank, d // 2), dtype=torch.uint8, device="cuda")
+            factor = torch.empty((B, Hkv, nb, w.rank, e // 2), dtype=torch.uint8, device="cuda")
             fscale = torch.empty((B, Hkv, nb, w.rank), device="cuda")
         else:
             factor = torch.empty((B, Hkv, nb, w.rank, d), device="cuda") if w.rank else None
@@ -157,14 +165,15 @@ def bench_decode(api, torch, w, x, steps, warmup, mean_dtype="bf16", factor_fp4=
     for rp in reps:
         ev[0].record()
         api.bsattn_build_summaries(shape, rp["K"], w.rank, 0, nb, nb, rp["mean"], rp["factor"],
-                                   factor_scale=rp["fscale"])
+                                   factor_scale=rp["fscale"], basis=basis)
         ev[1].record()
         torch.cuda.synchronize()
         build_ms.append(ev[0].elapsed_time(ev[1]))
 
     def select(rp):
         api.bsattn_select_topk(shape, rp["Q"], rp["mean"], rp["factor"], w.rank, nb, w.top_k,
-                               w.window, w.n_sink, None, rp["sel"], rp["scores"], factor_scale=rp["fscale"])
+                               w.window, w.n_sink, None, rp["sel"], rp["scores"], factor_scale=rp["fscale"],
+                               basis=basis)
 
     def decode(rp):
         api.bsattn_decode(shape, rp["Q"], rp["K"], rp["V"], rp["sel"], w.top_k, w.window, w.n_sink,
@@ -173,7 +182,7 @@ def bench_decode(api, torch, w, x, steps, warmup, mean_dtype="bf16", factor_fp4=
     def step(rp):
         api.bsattn_decode_step(shape, rp["Q"], rp["K"], rp["V"], rp["mean"], rp["factor"], w.rank, nb,
                                w.top_k, w.window, w.n_sink, None, rp["sel"], rp["scores"], rp["O"],
-                               rp["lse"], rp["ws"], factor_scale=rp["fscale"])
+                               rp["lse"], rp["ws"], factor_scale=rp["fscale"], basis=basis)
 
     for i in range(warmup):
         rp = reps[i % R]
@@ -187,7 +196,7 @@ def bench_decode(api, torch, w, x, steps, warmup, mean_dtype="bf16", factor_fp4=
                  for b in range(B) for g in range(Hkv))
     kv_bytes = tokens * d * 2 * elem
     io_bytes = B * Hq * d * elem + B * Hq * (d + 1) * 4 + B * Hkv * w.top_k * 4  # Q in, O + lse out, sel
-    sel_bytes = summ_bytes + B * Hq * d * elem + B * Hkv * w.top_k * 4
+    sel_bytes = summ_bytes + basis_bytes + B * Hq * d * elem + B * Hkv * w.top_k * 4
 
     # The timed steps run as one HIP graph of `steps` steps (replica i % R at step i):
     # a decode step is a handful of short kernels, and launching them one by one
@@ -231,6 +240,7 @@ def bench_decode(api, torch, w, x, steps, warmup, mean_dtype="bf16", factor_fp4=
     eager_ms = (time.perf_counter() - t0) * 1e3 / steps
     res = dict(
         workload=w.name, mean_dtype=mean_dtype, factor="fp4" if fp4 else ("f32" if w.rank else None),
+        sub_dim=sub or None,
         ms_per_step=ms_step, wall_ms_per_step=wall_step,
         tokens_per_s=B / (ms_step * 1e-3),
         eager_ms_per_step=eager_ms, two_call_ms_per_step=two_ms, replicas=R, attended_tokens=tokens,
@@ -245,7 +255,7 @@ def bench_decode(api, torch, w, x, steps, warmup, mean_dtype="bf16", factor_fp4=
     res["select_GBps"] = sel_bytes / (sel_ms * 1e-3) / 1e9
     # algorithmic bytes of a step: summaries, Q, the gathered K/V rows, and the
     # outputs (scores, sel, O, lse), each once
-    res["step_bytes"] = summ_bytes + kv_bytes + io_bytes + B * Hkv * nb * 4
+    res["step_bytes"] = summ_bytes + basis_bytes + kv_bytes + io_bytes + B * Hkv * nb * 4
     res["step_GBps"] = res["step_bytes"] / (ms_step * 1e-3) / 1e9
     del reps
     torch.cuda.empty_cache()
@@ -389,7 +399,10 @@ def main():
             if name == HEADLINE:  # context: the same step with fp32 block means
                 results[name + "/fp32_means"] = bench_decode(api, torch, w, x, args.steps, args.warmup,
                                                              mean_dtype="f32")
-            elif w.rank > 0:  # context: the same step with fp32 factor rows
+            elif w.rank > 0:  # context: FP4 rows without the subspace projection; fp32 rows
+                if w.sub_dim > 0:
+                    results[name + "/no_subspace"] = bench_decode(api, torch, w, x, args.steps, args.warmup,
+                                                                  subspace=False)
                 results[name + "/fp32_factors"] = bench_decode(api, torch, w, x, args.steps, args.warmup,
                                                                factor_fp4=False)
         else:

@@ -34,10 +34,12 @@
  *      prefill Q [B, Hq, N, d],       O [B, Hq, N, d] fp32, lse [B, Hq, N] fp32
  *      K, V    [B, Hkv, kv_capacity, d]  (token t of (b, g) at row t)
  *      mean    [B, Hkv, nblk_capacity, d] fp32 or bf16 (mean_dtype)
- *      factor  [B, Hkv, nblk_capacity, rank, d] fp32, or FP4 (factor_dtype):
- *              codes uint8 [B, Hkv, nblk_capacity, rank, d/2] (entry 2i in the
+ *      factor  [B, Hkv, nblk_capacity, rank, e] fp32, or FP4 (factor_dtype):
+ *              codes uint8 [B, Hkv, nblk_capacity, rank, e/2] (entry 2i in the
  *              low nibble of byte i, 2i+1 in the high nibble) and
- *              factor_scale [B, Hkv, nblk_capacity, rank] fp32
+ *              factor_scale [B, Hkv, nblk_capacity, rank] fp32; e = d, or
+ *              sub_dim with a query-subspace basis
+ *      basis   [Hkv, sub_dim, d] fp32, orthonormal rows
  *  - GQA [ATT FAQ Q2]: query head h reads K/V head h / (Hq / Hkv).
  *  - Blocks [COBS 1, 2.1]: block j holds tokens [j*S, (j+1)*S); only complete
  *    blocks ((j+1)*S <= n_ctx) have summaries and can be selected.
@@ -105,20 +107,30 @@ typedef struct {
  * BSATTN_FP4_E2M1 stores them as [COBS 2.3, compression] stores eigenvectors:
  * per row a float32 scale (the row's largest magnitude / 6) in factor_scale
  * and each entry as the E2M1 code nearest to entry / scale (ties to the even
- * code); factor_scale is ignored for BSATTN_F32 (may be NULL).  The calls that
- * read the summaries take the same mean_dtype, factor_dtype and factor_scale.
+ * code); factor_scale is ignored for BSATTN_F32 (may be NULL).
+ * Query-subspace projection [COBS 2.3, compression]: with sub_dim > 0 and a
+ * basis P_g (rows spanning K/V head g's query subspace, for instance the
+ * leading eigenvectors of its queries' second moment, taken offline) the
+ * factor rows are those of the projected covariance P_g Sigma P_g^T, i.e.
+ * of the projected centred keys P_g (k - mean): sub_dim numbers per row
+ * instead of d.  sub_dim: 0 (no basis; basis may be NULL) or a multiple of
+ * 32 in [32, d], with rank >= 1; the orthonormality of the rows is the
+ * caller's (not checked).  The mean is not projected.  The calls that read the
+ * summaries take the same mean_dtype, factor_dtype, factor_scale, basis and
+ * sub_dim.
  */
 bsattn_status bsattn_build_summaries(const bsattn_shape* shape, const void* K, int32_t rank,
                                      int32_t first_block, int32_t n_blocks,
                                      int32_t nblk_capacity, void* mean, int32_t mean_dtype,
                                      void* factor, int32_t factor_dtype, float* factor_scale,
-                                     void* hip_stream);
+                                     const float* basis, int32_t sub_dim, void* hip_stream);
 
 /*
  * Block selection for the decode query (the last cached token, t = n_ctx - 1).
  *  1. Per query head h and complete block j, with q~ = scale * Q[b,h]:
  *       s[h,j] = q~ . mean_j                                (rank == 0) [COBS 2.2]
  *       s[h,j] = q~ . mean_j + 1/2 sum_i (factor_{j,i} . q~)^2  (rank > 0) [COBS 2.3]
+ *     with a query-subspace basis the factor rows meet the projected query P_g q~.
  *  2. Group score per K/V head g: scores[b,g,j] = ln sum_{h in g} exp(s[h,j]),
  *     the log of the group's estimated attention mass [COBS 2.1].
  *  3. Forced tokens F: [0, n_sink) sinks [SWA 拡張手法], the window
@@ -129,7 +141,9 @@ bsattn_status bsattn_build_summaries(const bsattn_shape* shape, const void* K, i
  * Q: [B,Hq,d] of shape.dtype.  mean/factor as built above (factor NULL iff
  * rank == 0; mean_dtype, factor_dtype and factor_scale as they were built
  * with; an FP4 factor row enters the score as its codes' values times its
- * scale).  scores: REQUIRED [B,Hkv,nblk_capacity] fp32; entries of complete
+ * scale; basis and sub_dim as they were built with: a basis needs BF16 Q,
+ * BSATTN_BF16 means and BSATTN_FP4_E2M1 factors, the explainer's compressed
+ * summary, else BSATTN_ERR_UNSUPPORTED).  scores: REQUIRED [B,Hkv,nblk_capacity] fp32; entries of complete
  * blocks are written (it is also the buffer the top-k pass reads).
  * global_pos_host: sorted, unique, in [0, n_ctx), n_global <= BSATTN_MAX_GLOBAL.
  * top_k in [1, BSATTN_MAX_TOP_K]; n_ctx / S <= BSATTN_MAX_BLOCKS.
@@ -137,7 +151,8 @@ bsattn_status bsattn_build_summaries(const bsattn_shape* shape, const void* K, i
  */
 bsattn_status bsattn_select_topk(const bsattn_shape* shape, const void* Q, const void* mean,
                                  int32_t mean_dtype, const void* factor, int32_t factor_dtype,
-                                 const float* factor_scale, int32_t rank, int32_t nblk_capacity,
+                                 const float* factor_scale, const float* basis, int32_t sub_dim,
+                                 int32_t rank, int32_t nblk_capacity,
                                  int32_t top_k, int32_t window, int32_t n_sink,
                                  const int32_t* global_pos_host, int32_t n_global, int32_t* sel,
                                  float* scores, void* hip_stream);
@@ -185,8 +200,8 @@ bsattn_status bsattn_decode(const bsattn_shape* shape, const void* Q, const void
 bsattn_status bsattn_decode_step(const bsattn_shape* shape, const void* Q, const void* K,
                                  const void* V, const void* mean, int32_t mean_dtype,
                                  const void* factor, int32_t factor_dtype,
-                                 const float* factor_scale, int32_t rank, int32_t nblk_capacity,
-                                 int32_t top_k,
+                                 const float* factor_scale, const float* basis, int32_t sub_dim,
+                                 int32_t rank, int32_t nblk_capacity, int32_t top_k,
                                  int32_t window, int32_t n_sink, const int32_t* global_pos_host,
                                  int32_t n_global, int32_t* sel, float* scores, float* O,
                                  float* lse, void* workspace, size_t ws_bytes, void* hip_stream);

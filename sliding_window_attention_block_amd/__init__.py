@@ -105,20 +105,27 @@ def _factor_dtype(factor, factor_scale):
     raise ValueError(f"factor rows must be float32 or uint8 FP4 codes, not {factor.dtype}")
 
 
+def _sub_dim(basis):
+    """Subspace dimension of a query-subspace basis [Hkv, sub_dim, d] (0 without one)."""
+    return 0 if basis is None else int(basis.shape[1])
+
+
 def bsattn_build_summaries(shape, K, rank, first_block, n_blocks, nblk_capacity, mean, factor=None,
-                           stream=None, factor_scale=None):
+                           stream=None, factor_scale=None, basis=None):
     _check(library().bsattn_build_summaries(ctypes.byref(shape), _ptr(K), rank, first_block,
                                             n_blocks, nblk_capacity, _ptr(mean), _mean_dtype(mean),
                                             _ptr(factor), _factor_dtype(factor, factor_scale),
-                                            _ptr(factor_scale), _stream(stream)))
+                                            _ptr(factor_scale), _ptr(basis), _sub_dim(basis),
+                                            _stream(stream)))
 
 
 def bsattn_select_topk(shape, Q, mean, factor, rank, nblk_capacity, top_k, window, n_sink,
-                       global_pos, sel, scores, stream=None, factor_scale=None):
+                       global_pos, sel, scores, stream=None, factor_scale=None, basis=None):
     g, ng = _globals(global_pos)
     _check(library().bsattn_select_topk(ctypes.byref(shape), _ptr(Q), _ptr(mean), _mean_dtype(mean),
                                         _ptr(factor), _factor_dtype(factor, factor_scale),
-                                        _ptr(factor_scale), rank, nblk_capacity, top_k, window,
+                                        _ptr(factor_scale), _ptr(basis), _sub_dim(basis), rank,
+                                        nblk_capacity, top_k, window,
                                         n_sink, g, ng, _ptr(sel), _ptr(scores), _stream(stream)))
 
 
@@ -137,12 +144,14 @@ def bsattn_decode(shape, Q, K, V, sel, top_k, window, n_sink, global_pos, O, lse
 
 
 def bsattn_decode_step(shape, Q, K, V, mean, factor, rank, nblk_capacity, top_k, window, n_sink,
-                       global_pos, sel, scores, O, lse, workspace, stream=None, factor_scale=None):
+                       global_pos, sel, scores, O, lse, workspace, stream=None, factor_scale=None,
+                       basis=None):
     g, ng = _globals(global_pos)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(library().bsattn_decode_step(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(mean),
                                         _mean_dtype(mean), _ptr(factor),
-                                        _factor_dtype(factor, factor_scale), _ptr(factor_scale), rank,
+                                        _factor_dtype(factor, factor_scale), _ptr(factor_scale),
+                                        _ptr(basis), _sub_dim(basis), rank,
                                         nblk_capacity, top_k, window, n_sink, g, ng, _ptr(sel),
                                         _ptr(scores), _ptr(O), _ptr(lse), _ptr(workspace), ws_bytes,
                                         _stream(stream)))

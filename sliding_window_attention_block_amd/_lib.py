@@ -68,19 +68,19 @@ def load():
                       "`python -m sliding_window_attention_block_amd.build`")
     lib = ctypes.CDLL(LIB_PATH)
     lib.bsattn_build_summaries.argtypes = [_pshape, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _i32,
-                                           _vp, _vp]
+                                           _vp, _vp, _i32, _vp]
     lib.bsattn_build_summaries.restype = _st
-    lib.bsattn_select_topk.argtypes = [_pshape, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
-                                       _i32, _pi32, _i32, _vp, _vp, _vp]
+    lib.bsattn_select_topk.argtypes = [_pshape, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _i32, _i32,
+                                       _i32, _i32, _i32, _pi32, _i32, _vp, _vp, _vp]
     lib.bsattn_select_topk.restype = _st
     lib.bsattn_decode_workspace_bytes.argtypes = [_pshape, _i32, _i32, _i32, _i32]
     lib.bsattn_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.bsattn_decode.argtypes = [_pshape, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _pi32, _i32,
                                   _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.bsattn_decode.restype = _st
-    lib.bsattn_decode_step.argtypes = [_pshape, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _i32, _i32,
-                                       _i32, _i32, _i32, _pi32, _i32, _vp, _vp, _vp, _vp, _vp,
-                                       ctypes.c_size_t, _vp]
+    lib.bsattn_decode_step.argtypes = [_pshape, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32,
+                                       _i32, _i32, _i32, _i32, _i32, _pi32, _i32, _vp, _vp, _vp, _vp,
+                                       _vp, ctypes.c_size_t, _vp]
     lib.bsattn_decode_step.restype = _st
     lib.bsattn_prefill.argtypes = [_pshape, _vp, _vp, _vp, _i32, _i32, _i32, _pi32, _i32,
                                    _vp, _vp, _vp, ctypes.c_size_t, _vp]

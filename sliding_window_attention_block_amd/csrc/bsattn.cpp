@@ -191,8 +191,20 @@ bsattn_status check_factor(int32_t rank, const void* factor, int32_t factor_dtyp
   return BSATTN_OK;
 }
 
+// Query-subspace basis: sub_dim 0 (none), or a multiple of 32 in [32, d] with rank >= 1.
+bsattn_status check_basis(const float* basis, int32_t sub_dim, int32_t rank, int32_t head_dim) {
+  if (sub_dim == 0) return BSATTN_OK;
+  if (sub_dim < 32 || sub_dim > head_dim || sub_dim % 32 != 0)
+    return fail(BSATTN_ERR_INVALID, "sub_dim %d: must be 0 or a multiple of 32 in [32, %d]", sub_dim, head_dim);
+  if (rank < 1) return fail(BSATTN_ERR_INVALID, "a query-subspace basis needs rank >= 1");
+  if (basis == nullptr || !aligned16(basis))
+    return fail(BSATTN_ERR_INVALID, "basis must be a non-NULL, 16-byte aligned device pointer");
+  return BSATTN_OK;
+}
+
 bsattn_status select_args(const bsattn_shape* shape, const void* Q, const void* mean, int32_t mean_dtype,
-                          const void* factor, int32_t factor_dtype, const float* factor_scale, int32_t rank, int32_t nblk_capacity, int32_t top_k, int32_t window, int32_t n_sink,
+                          const void* factor, int32_t factor_dtype, const float* factor_scale,
+                          const float* basis, int32_t sub_dim, int32_t rank, int32_t nblk_capacity, int32_t top_k, int32_t window, int32_t n_sink,
                           const int32_t* global_pos_host, int32_t n_global, int32_t* sel, float* scores,
                           bsattn::SelectArgs& a) {
   bsattn_status st = check_shape(shape, true);
@@ -204,6 +216,10 @@ bsattn_status select_args(const bsattn_shape* shape, const void* Q, const void* 
   if (rank < 0 || rank > BSATTN_MAX_RANK) return fail(BSATTN_ERR_INVALID, "rank must be in [0, %d]", BSATTN_MAX_RANK);
   st = check_factor(rank, factor, factor_dtype, factor_scale);
   if (st != BSATTN_OK) return st;
+  st = check_basis(basis, sub_dim, rank, shape->head_dim);
+  if (st != BSATTN_OK) return st;
+  if (sub_dim > 0 && (shape->dtype != BSATTN_BF16 || mean_dtype != BSATTN_BF16 || factor_dtype != BSATTN_FP4_E2M1))
+    return fail(BSATTN_ERR_UNSUPPORTED, "a query-subspace basis needs BF16 Q, BF16 means and FP4 factors");
   if (top_k < 1 || top_k > BSATTN_MAX_TOP_K) return fail(BSATTN_ERR_INVALID, "top_k must be in [1, %d]", BSATTN_MAX_TOP_K);
   if (window < 0 || n_sink < 0) return fail(BSATTN_ERR_INVALID, "window and n_sink must be >= 0");
   const int nb = shape->n_ctx / shape->block_size;
@@ -217,6 +233,8 @@ bsattn_status select_args(const bsattn_shape* shape, const void* Q, const void* 
   a.Q = Q; a.mean = mean; a.factor = rank > 0 ? factor : nullptr; a.sel = sel; a.scores = scores;
   a.factor_fp4 = rank > 0 && factor_dtype == BSATTN_FP4_E2M1;
   a.factor_scale = a.factor_fp4 ? factor_scale : nullptr;
+  a.basis = sub_dim > 0 ? basis : nullptr;
+  a.sub_dim = sub_dim;
   a.batch = shape->batch; a.n_q_heads = shape->n_q_heads; a.n_kv_heads = shape->n_kv_heads;
   a.head_dim = shape->head_dim;
   a.n_blocks = nb;
@@ -297,7 +315,8 @@ const char* bsattn_version(void) { return "bsattn 0.1.0 gfx950"; }
 bsattn_status bsattn_build_summaries(const bsattn_shape* shape, const void* K, int32_t rank,
                                      int32_t first_block, int32_t n_blocks, int32_t nblk_capacity,
                                      void* mean, int32_t mean_dtype, void* factor, int32_t factor_dtype,
-                                     float* factor_scale, void* hip_stream) {
+                                     float* factor_scale, const float* basis, int32_t sub_dim,
+                                     void* hip_stream) {
   g_err[0] = 0;
   bsattn_status st = check_shape(shape, false);
   if (st != BSATTN_OK) return st;
@@ -306,6 +325,8 @@ bsattn_status bsattn_build_summaries(const bsattn_shape* shape, const void* K, i
     return fail(BSATTN_ERR_INVALID, "mean_dtype %d: must be BSATTN_F32 or BSATTN_BF16", mean_dtype);
   if (rank < 0 || rank > BSATTN_MAX_RANK) return fail(BSATTN_ERR_INVALID, "rank must be in [0, %d]", BSATTN_MAX_RANK);
   st = check_factor(rank, factor, factor_dtype, factor_scale);
+  if (st != BSATTN_OK) return st;
+  st = check_basis(basis, sub_dim, rank, shape->head_dim);
   if (st != BSATTN_OK) return st;
   if (first_block < 0 || n_blocks < 0) return fail(BSATTN_ERR_INVALID, "negative block range");
   if ((long long)(first_block + (long long)n_blocks) * shape->block_size > shape->n_ctx)
@@ -318,6 +339,7 @@ bsattn_status bsattn_build_summaries(const bsattn_shape* shape, const void* K, i
   bsattn::SummaryArgs a;
   a.K = K; a.mean = mean; a.factor = factor;
   a.bh = shape->batch * shape->n_kv_heads;
+  a.n_kv_heads = shape->n_kv_heads;
   a.kv_capacity = shape->kv_capacity;
   a.nblk_capacity = nblk_capacity;
   a.first_block = first_block;
@@ -328,6 +350,8 @@ bsattn_status bsattn_build_summaries(const bsattn_shape* shape, const void* K, i
   a.mean_bf16 = mean_dtype == BSATTN_BF16;
   a.factor_fp4 = rank > 0 && factor_dtype == BSATTN_FP4_E2M1;
   a.factor_scale = factor_scale;
+  a.basis = sub_dim > 0 ? basis : nullptr;
+  a.sub_dim = sub_dim;
   hipError_t e = bsattn::launch_summaries(a, (hipStream_t)hip_stream);
   if (e != hipSuccess) return fail(BSATTN_ERR_HIP, "summaries launch: %s", hipGetErrorString(e));
   return BSATTN_OK;
@@ -335,13 +359,15 @@ bsattn_status bsattn_build_summaries(const bsattn_shape* shape, const void* K, i
 
 bsattn_status bsattn_select_topk(const bsattn_shape* shape, const void* Q, const void* mean,
                                  int32_t mean_dtype, const void* factor, int32_t factor_dtype,
-                                 const float* factor_scale, int32_t rank, int32_t nblk_capacity,
+                                 const float* factor_scale, const float* basis, int32_t sub_dim,
+                                 int32_t rank, int32_t nblk_capacity,
                                  int32_t top_k, int32_t window, int32_t n_sink,
                                  const int32_t* global_pos_host, int32_t n_global, int32_t* sel,
                                  float* scores, void* hip_stream) {
   g_err[0] = 0;
   bsattn::SelectArgs a;
-  const bsattn_status st = select_args(shape, Q, mean, mean_dtype, factor, factor_dtype, factor_scale, rank,
+  const bsattn_status st = select_args(shape, Q, mean, mean_dtype, factor, factor_dtype, factor_scale, basis,
+                                       sub_dim, rank,
                                        nblk_capacity, top_k, window, n_sink, global_pos_host, n_global, sel,
                                        scores, a);
   if (st != BSATTN_OK) return st;
@@ -375,14 +401,15 @@ bsattn_status bsattn_decode(const bsattn_shape* shape, const void* Q, const void
 
 bsattn_status bsattn_decode_step(const bsattn_shape* shape, const void* Q, const void* K, const void* V,
                                  const void* mean, int32_t mean_dtype, const void* factor,
-                                 int32_t factor_dtype, const float* factor_scale, int32_t rank,
-                                 int32_t nblk_capacity,
+                                 int32_t factor_dtype, const float* factor_scale, const float* basis,
+                                 int32_t sub_dim, int32_t rank, int32_t nblk_capacity,
                                  int32_t top_k, int32_t window, int32_t n_sink, const int32_t* global_pos_host,
                                  int32_t n_global, int32_t* sel, float* scores, float* O, float* lse,
                                  void* workspace, size_t ws_bytes, void* hip_stream) {
   g_err[0] = 0;
   bsattn::SelectArgs sa;
-  bsattn_status st = select_args(shape, Q, mean, mean_dtype, factor, factor_dtype, factor_scale, rank,
+  bsattn_status st = select_args(shape, Q, mean, mean_dtype, factor, factor_dtype, factor_scale, basis, sub_dim,
+                                 rank,
                                  nblk_capacity, top_k, window, n_sink, global_pos_host, n_global, sel, scores,
                                  sa);
   if (st != BSATTN_OK) return st;

@@ -13,9 +13,12 @@ namespace bsattn {
 struct SummaryArgs {
   const void* K;
   void* mean;       // fp32, or bf16 when mean_bf16
-  void* factor;        // fp32 rows [.., rank, d], or FP4 E2M1 codes [.., rank, d / 2] when factor_fp4
+  void* factor;        // fp32 rows [.., rank, e], or FP4 E2M1 codes [.., rank, e / 2] when factor_fp4
   float* factor_scale;  // FP4: one scale per factor row [.., rank]
+  const float* basis;   // query-subspace rows [Hkv, sub_dim, d], or null
+  int32_t sub_dim;      // e = sub_dim with a basis, else d
   int32_t bh;            // B * Hkv
+  int32_t n_kv_heads;    // Hkv (the basis of pair bh is that of K/V head bh % Hkv)
   int32_t kv_capacity;   // token stride
   int32_t nblk_capacity;
   int32_t first_block;
@@ -33,6 +36,8 @@ struct SelectArgs {
   const void* mean;  // fp32, or bf16 when mean_bf16
   const void* factor;        // fp32 rows, or FP4 E2M1 codes when factor_fp4
   const float* factor_scale;  // FP4: one scale per factor row
+  const float* basis;         // query-subspace rows [Hkv, sub_dim, d] (FP4 rows of sub_dim), or null
+  int32_t sub_dim;
   int32_t* sel;
   float* scores;
   int32_t batch, n_q_heads, n_kv_heads, head_dim;

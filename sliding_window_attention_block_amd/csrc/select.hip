@@ -246,26 +246,101 @@ __global__ __launch_bounds__(256, scores_heavy(GM, RM, PB, D) ? 1 : 2) void sele
 //
 // Loads: a mean row is 2D bytes; in k-step s lane (n, kg = l / 16) reads the
 // 16 bytes of dims 32 s + 8 kg .. +7 (64 contiguous bytes per row per
-// instruction).  An FP4 row is D/2 bytes; lane kg reads its D/8 bytes at once
-// (dims kg D/4 .. +D/4) and converts 8 codes per k-step, dims kg D/4 + 8 s + t,
-// so the factor MFMAs take the queries in that order (a second A operand).
-template <int D, int RM>
+// instruction).  An FP4 row of E entries (E = D, or the subspace dimension)
+// is E/2 bytes; lane kg reads its E/8 bytes at once (entries kg E/4 .. +E/4)
+// and converts 8 codes per k-step, entries kg E/4 + 8 s + t, so the factor
+// MFMAs take the query in that order (a second A operand).
+//
+// With a query-subspace basis P (SK = E / 32 > 0) the factor rows meet the
+// projected query P q~ [COBS 2.3].  The four waves of a workgroup share one
+// pair and project its queries once: tile T of the projection, MFMAs with 16
+// basis rows as A (P split into bfloat16 hi + lo, 16 significant bits) and
+// the queries as B, leaves lane (head n, kg) with 4 projected entries; the
+// basis rows of tile T = 2 s + u are taken in the order that gives lane kg
+// entries kg E/4 + 8 s + 4 u + i, i.e. exactly the 8 entries its FP4 codes
+// need in factor k-step s.  Wave w computes k-step w of every tile; the
+// partial tiles meet in LDS (one barrier) and each lane sums them and splits
+// its projected query into bfloat16 hi + lo (two MFMAs per factor k-step).
+// The basis loads are issued before the first summary loads (loads complete
+// in issue order, so the projection does not wait on HBM), except for rank 8
+// at E = 128, where their registers would not fit.
+template <int KF>
+struct FacWords {
+  uint32_t w[KF];
+};
+template <>
+struct FacWords<4> {
+  u32x4 w;
+};
+template <>
+struct FacWords<2> {
+  u32x2 w;
+};
+
+template <int KF>
+__device__ __forceinline__ FacWords<KF> load_fac(const uint8_t* row, int kg) {
+  FacWords<KF> r;
+  if constexpr (KF == 4) {
+    r.w = *reinterpret_cast<const u32x4*>(row + 16 * kg);
+  } else if constexpr (KF == 2) {
+    r.w = *reinterpret_cast<const u32x2*>(row + 8 * kg);
+  } else {
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(row + 4 * KF * kg);
+#pragma unroll
+    for (int c = 0; c < KF; ++c) r.w[c] = p[c];
+  }
+  return r;
+}
+
+// x = hi + lo (+ lo2): each part the nearest bfloat16 of what the earlier parts
+// leave; two parts hold 16 significant bits, three all 24 of a float.
+template <int NP>
+__device__ __forceinline__ void split_bf16x8(const float (&x)[8], bf16x8 (&part)[NP]) {
+  float r[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) r[t] = x[t];
+#pragma unroll
+  for (int k = 0; k < NP; ++k) {
+    u32x4 w;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      w[c] = cvt_pk_bf16(r[2 * c], r[2 * c + 1]);
+      r[2 * c] -= bf16lo(w[c]);
+      r[2 * c + 1] -= bf16hi(w[c]);
+    }
+    part[k] = __builtin_bit_cast(bf16x8, w);
+  }
+}
+
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t w) {
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.f, 0);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.f, 1);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.f, 2);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.f, 3);
+  return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+template <int D, int RM, int SK>
 __global__ __launch_bounds__(256, 2) void select_scores_mfma_kernel(SelectArgs a) {
-  constexpr int KS = D / 32;  // k-steps
-  using FacLoad = typename std::conditional<D == 128, u32x4, u32x2>::type;  // D/8 bytes
+  constexpr int KS = D / 32;                 // k-steps of the mean
+  constexpr int KF = SK > 0 ? SK : D / 32;   // k-steps (dwords per lane) of a factor row
+  constexpr int E = 32 * KF;                 // entries of a factor row
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int gw = blockIdx.x * 4 + wid;
   const int n_pairs = a.batch * a.n_kv_heads;
   const int pair = gw / a.n_part, wi = gw % a.n_part;
-  if (pair >= n_pairs) return;  // no barriers: waves are independent
+  // no barriers unless SK > 0, where n_part % 4 == 0 keeps every wave of the
+  // grid (all four of a workgroup) inside [0, n_pairs)
+  if (pair >= n_pairs) return;
   const int col = lane & 15, kg = lane >> 4;
   const int b = pair / a.n_kv_heads, g = pair % a.n_kv_heads;
   const int G = a.n_q_heads / a.n_kv_heads;
   const int NB = a.n_blocks;
   const int rank = a.rank;
 
-  bf16x8 qm[KS], qf[RM > 0 ? KS : 1];
+  bf16x8 qm[KS];
+  bf16x8 qf[SK > 0 ? 2 * SK : (RM > 0 ? KS : 1)];  // SK > 0: hi, lo per k-step
   {
     const uint16_t* qrow =
         reinterpret_cast<const uint16_t*>(a.Q) + ((size_t)b * a.n_q_heads + g * G + min(col, G - 1)) * D;
@@ -274,7 +349,7 @@ __global__ __launch_bounds__(256, 2) void select_scores_mfma_kernel(SelectArgs a
       u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * kg);
       if (col >= G) v = u32x4{0u, 0u, 0u, 0u};
       qm[s] = __builtin_bit_cast(bf16x8, v);
-      if constexpr (RM > 0) {
+      if constexpr (RM > 0 && SK == 0) {
         u32x4 w = *reinterpret_cast<const u32x4*>(qrow + kg * (D / 4) + 8 * s);
         if (col >= G) w = u32x4{0u, 0u, 0u, 0u};
         qf[s] = __builtin_bit_cast(bf16x8, w);
@@ -284,7 +359,7 @@ __global__ __launch_bounds__(256, 2) void select_scores_mfma_kernel(SelectArgs a
 
   struct Stage {
     u32x4 m[KS];
-    FacLoad f[RM > 0 ? RM : 1];
+    FacWords<KF> f[RM > 0 ? RM : 1];
     float fs[RM > 0 ? RM : 1];
   };
   // every load is issued (blocks past the end re-read the last block, factor
@@ -298,8 +373,76 @@ __global__ __launch_bounds__(256, 2) void select_scores_mfma_kernel(SelectArgs a
 #pragma unroll
     for (int i = 0; i < RM; ++i) {
       const size_t fr = row * rank + min(i, rank - 1);
-      st.f[i] = reinterpret_cast<const FacLoad*>(reinterpret_cast<const uint8_t*>(a.factor) + fr * (D / 2))[kg];
+      st.f[i] = load_fac<KF>(reinterpret_cast<const uint8_t*>(a.factor) + fr * (E / 2), kg);
       st.fs[i] = a.factor_scale[fr];
+    }
+  };
+  // the pair's projected queries (SK > 0): k-step wid of every tile's basis
+  // rows, loaded by project_load() before the first summary loads
+  constexpr int NT = 2 * SK;  // projection tiles
+  constexpr bool HOIST = SK > 0 && !(RM == 8 && SK == 4);
+  float4 pv[HOIST ? NT : 1][2];
+  auto basis_row = [&](int T) __attribute__((always_inline)) {
+    const int m = lane & 15, s2 = T >> 1, u = T & 1;
+    return a.basis + ((size_t)g * E + (m >> 2) * (E / 4) + 8 * s2 + 4 * u + (m & 3)) * D + 32 * wid + 8 * kg;
+  };
+  auto project_load = [&]() __attribute__((always_inline)) {
+    if constexpr (HOIST) {
+      if (wid < KS) {
+#pragma unroll
+        for (int T = 0; T < NT; ++T) {
+          const float* prow = basis_row(T);
+          pv[T][0] = *reinterpret_cast<const float4*>(prow);
+          pv[T][1] = *reinterpret_cast<const float4*>(prow + 4);
+        }
+      }
+    }
+  };
+  auto project = [&]() __attribute__((always_inline)) {
+    if constexpr (SK > 0) {
+      __shared__ f32x4 qpart[KS][NT][64];
+      // k-step ks = wid, one uniform branch per k-step (constant register indices)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (wid == ks) {
+#pragma unroll
+          for (int T = 0; T < NT; ++T) {
+            float4 x0, x1;
+            if constexpr (HOIST) {
+              x0 = pv[T][0];
+              x1 = pv[T][1];
+            } else {
+              const float* prow = basis_row(T);
+              x0 = *reinterpret_cast<const float4*>(prow);
+              x1 = *reinterpret_cast<const float4*>(prow + 4);
+            }
+            const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            bf16x8 pp[2];
+            split_bf16x8<2>(x, pp);
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pp[0], qm[ks], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pp[1], qm[ks], acc, 0, 0, 0);
+            qpart[ks][T][lane] = acc;
+          }
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int s2 = 0; s2 < SK; ++s2) {
+        f32x4 lo4 = qpart[0][2 * s2][lane], hi4 = qpart[0][2 * s2 + 1][lane];
+#pragma unroll
+        for (int w = 1; w < KS; ++w) {
+          lo4 += qpart[w][2 * s2][lane];
+          hi4 += qpart[w][2 * s2 + 1][lane];
+        }
+        lo4 *= a.scale;
+        hi4 *= a.scale;
+        const float x[8] = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        bf16x8 pp[2];
+        split_bf16x8<2>(x, pp);
+        qf[2 * s2] = pp[0];
+        qf[2 * s2 + 1] = pp[1];
+      }
     }
   };
   auto comp = [&](int u, const Stage& st) __attribute__((always_inline)) {
@@ -315,16 +458,17 @@ __global__ __launch_bounds__(256, 2) void select_scores_mfma_kernel(SelectArgs a
       if (r < rank) {
         f32x4 pa = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const uint32_t w = st.f[r][s];  // 8 codes, dim kg D/4 + 8 s + t in bits 4t .. 4t+3
-          const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.f, 0);
-          const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.f, 1);
-          const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.f, 2);
-          const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.f, 3);
-          const bf16x8 bv = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-          pa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[s], bv, pa, 0, 0, 0);
+        for (int s = 0; s < KF; ++s) {
+          const bf16x8 bv = fp4x8_to_bf16(st.f[r].w[s]);  // 8 codes, entry kg E/4 + 8 s + t in bits 4t ..
+          if constexpr (SK > 0) {
+            pa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[2 * s], bv, pa, 0, 0, 0);
+            pa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[2 * s + 1], bv, pa, 0, 0, 0);
+          } else {
+            pa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[s], bv, pa, 0, 0, 0);
+          }
         }
-        const float c = a.scale * st.fs[r];
+        // the row's scale (the projected query already carries the softmax scale)
+        const float c = SK > 0 ? st.fs[r] : a.scale * st.fs[r];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float pr = pa[i] * c;
@@ -350,13 +494,16 @@ __global__ __launch_bounds__(256, 2) void select_scores_mfma_kernel(SelectArgs a
     if (kg == 0 && j < NB) a.scores[(size_t)pair * a.nblk_capacity + j] = fmaf(__builtin_amdgcn_logf(sum), kLn2, mx);
   };
 
+  // every path calls project() exactly once (it holds the workgroup's barrier)
   const int n_units = (NB + 15) / 16;
   const int u0 = wi * a.per_wave, u1 = min(u0 + a.per_wave, n_units);
   const int n = u1 - u0;
   Stage A, B;
+  project_load();
   if (n >= 4) {
     load(u0, A);
     load(u0 + 1, B);
+    project();
     int u = u0;
     for (; u + 3 < u1; u += 2) {
       comp(u, A);
@@ -376,6 +523,7 @@ __global__ __launch_bounds__(256, 2) void select_scores_mfma_kernel(SelectArgs a
   } else if (n == 3) {
     load(u0, A);
     load(u0 + 1, B);
+    project();
     comp(u0, A);
     load(u0 + 2, A);
     comp(u0 + 1, B);
@@ -383,11 +531,15 @@ __global__ __launch_bounds__(256, 2) void select_scores_mfma_kernel(SelectArgs a
   } else if (n == 2) {
     load(u0, A);
     load(u0 + 1, B);
+    project();
     comp(u0, A);
     comp(u0 + 1, B);
   } else if (n == 1) {
     load(u0, A);
+    project();
     comp(u0, A);
+  } else {
+    project();
   }
 }
 
@@ -540,24 +692,43 @@ hipError_t launch_topk(const SelectArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int D, int RM>
+template <int D, int RM, int SK>
 hipError_t launch_mfma(const SelectArgs& a0, hipStream_t stream) {
   SelectArgs a = a0;
   if (a.n_blocks > 0) {
-    split_units(a, (a.n_blocks + 15) / 16, 256 * 8);
+    const long long units = (a.n_blocks + 15) / 16;
+    split_units(a, units, 256 * 8);
+    if (SK > 0 && a.n_part % 4 != 0) {
+      // the four waves of a workgroup share a pair (one projection, one barrier)
+      a.n_part = (a.n_part + 3) / 4 * 4;
+      a.per_wave = (int)((units + a.n_part - 1) / a.n_part);
+    }
     const long long waves = (long long)a.batch * a.n_kv_heads * a.n_part;
-    hipLaunchKernelGGL((select_scores_mfma_kernel<D, RM>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((select_scores_mfma_kernel<D, RM, SK>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
+                       stream, a);
   }
   if (a.scores_only) return hipGetLastError();
   return launch_topk(a, stream);
 }
 
+template <int D, int RM>
+hipError_t launch_mfma_s(const SelectArgs& a, hipStream_t stream) {
+  switch (a.sub_dim / 32) {
+    case 1: return launch_mfma<D, RM, 1>(a, stream);
+    case 2: return launch_mfma<D, RM, 2>(a, stream);
+    case 3: if constexpr (D >= 96) return launch_mfma<D, RM, 3>(a, stream); else break;
+    case 4: if constexpr (D >= 128) return launch_mfma<D, RM, 4>(a, stream); else break;
+    default: break;
+  }
+  return launch_mfma<D, RM, 0>(a, stream);
+}
+
 template <int D>
 hipError_t launch_mfma_r(const SelectArgs& a, hipStream_t stream) {
-  if (a.rank == 0) return launch_mfma<D, 0>(a, stream);
-  if (a.rank <= 2) return launch_mfma<D, 2>(a, stream);
-  if (a.rank <= 4) return launch_mfma<D, 4>(a, stream);
-  return launch_mfma<D, 8>(a, stream);
+  if (a.rank == 0) return launch_mfma<D, 0, 0>(a, stream);
+  if (a.rank <= 2) return launch_mfma_s<D, 2>(a, stream);
+  if (a.rank <= 4) return launch_mfma_s<D, 4>(a, stream);
+  return launch_mfma_s<D, 8>(a, stream);
 }
 
 template <int D, int GM, int RM, bool BF16>

@@ -138,6 +138,32 @@ __global__ __launch_bounds__(256) void summaries_factor_kernel(SummaryArgs a) {
   // identity eigenvector matrix
   for (int i = tid; i < 64 * 64; i += 256) W[(i / 64) * kGStride + (i % 64)] = (i / 64 == i % 64) ? 1.f : 0.f;
   __syncthreads();
+  // 3b. query-subspace projection [COBS 2.3, compression]: the centred keys
+  // become P (k - mean), ED numbers each (rows ED .. D-1 of Ct zeroed), so the
+  // steps below factorise the projected covariance P Sigma P^T.  Wave w owns
+  // basis rows w, w + 4, ...; lane r owns token r.
+  const int ED = a.basis != nullptr ? a.sub_dim : D;
+  if (a.basis != nullptr) {
+    const float* P = a.basis + (size_t)(bh % a.n_kv_heads) * ED * D;
+    float acc[D / 4];
+#pragma unroll
+    for (int u = 0; u < D / 4; ++u) acc[u] = 0.f;
+    for (int d = 0; d < D; ++d) {
+      const float c = Ct[d * kCtStride + lane];
+#pragma unroll
+      for (int u = 0; u < D / 4; ++u) {
+        const int j = wid + 4 * u;
+        if (j < ED) acc[u] = fmaf(P[(size_t)j * D + d], c, acc[u]);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < D / 4; ++u) {
+      const int j = wid + 4 * u;
+      Ct[j * kCtStride + lane] = j < ED ? acc[u] : 0.f;
+    }
+    __syncthreads();
+  }
   // 4. Gram G = C C^T / L, thread t owns rows 4*(t/16).., cols 4*(t%16)..
   {
     const int x0 = 4 * (tid >> 4), y0 = 4 * (tid & 15);
@@ -146,7 +172,7 @@ __global__ __launch_bounds__(256) void summaries_factor_kernel(SummaryArgs a) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) g[i][j] = 0.f;
-    for (int d = 0; d < D; ++d) {
+    for (int d = 0; d < ED; ++d) {
       const float4 xa = *reinterpret_cast<const float4*>(&Ct[d * kCtStride + x0]);
       const float4 yb = *reinterpret_cast<const float4*>(&Ct[d * kCtStride + y0]);
       const float xs[4] = {xa.x, xa.y, xa.z, xa.w};
@@ -247,8 +273,8 @@ __global__ __launch_bounds__(256) void summaries_factor_kernel(SummaryArgs a) {
   }
   __syncthreads();
   // 7. factor rows sqrt(lambda_i) v_i = C^T w_i / sqrt(L)
-  for (int o = tid; o < a.rank * D; o += 256) {
-    const int i = o / D, d = o % D;
+  for (int o = tid; o < a.rank * ED; o += 256) {
+    const int i = o / ED, d = o % ED;
     const int x = pick[i];
     float s = 0.f;
     for (int r = 0; r < kBlock; ++r) s = fmaf(Ct[d * kCtStride + r], W[r * kGStride + x], s);
@@ -259,7 +285,7 @@ __global__ __launch_bounds__(256) void summaries_factor_kernel(SummaryArgs a) {
   for (int i = wid; i < a.rank; i += 4) {
     float best = -1.f;
     int bidx = D;
-    for (int d = lane; d < D; d += 64) {
+    for (int d = lane; d < ED; d += 64) {
       const float v = fabsf(F[i * D + d]);
       if (v > best) { best = v; bidx = d; }
     }
@@ -276,15 +302,15 @@ __global__ __launch_bounds__(256) void summaries_factor_kernel(SummaryArgs a) {
       // nearest E2M1 value of entry / scale; lane l packs entries 2l (low
       // nibble) and 2l + 1 into byte l
       const float scale = best / 6.0f;
-      for (int l = lane; l < D / 2; l += 64) {
+      for (int l = lane; l < ED / 2; l += 64) {
         const float v0 = scale > 0.f ? (sign * F[i * D + 2 * l]) / scale : 0.f;
         const float v1 = scale > 0.f ? (sign * F[i * D + 2 * l + 1]) / scale : 0.f;
-        static_cast<uint8_t*>(a.factor)[frow * (D / 2) + l] = (uint8_t)(e2m1_code(v0) | (e2m1_code(v1) << 4));
+        static_cast<uint8_t*>(a.factor)[frow * (ED / 2) + l] = (uint8_t)(e2m1_code(v0) | (e2m1_code(v1) << 4));
       }
       if (lane == 0) a.factor_scale[frow] = scale;
     } else {
-      float* dst = static_cast<float*>(a.factor) + frow * D;
-      for (int d = lane; d < D; d += 64) dst[d] = sign * F[i * D + d];
+      float* dst = static_cast<float*>(a.factor) + frow * ED;
+      for (int d = lane; d < ED; d += 64) dst[d] = sign * F[i * D + d];
     }
   }
 }

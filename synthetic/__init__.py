@@ -10,6 +10,7 @@ from .generators import (  # noqa: F401
     bf16_bits,
     bf16_bits_to_f32,
     normal_f32,
+    orthonormal_rows,
     sha256_hex,
 )
 from .workloads import (  # noqa: F401

@@ -53,3 +53,13 @@ def normal_f32(rng, shape, scale=1.0, out_bf16=False, chunk=CHUNK):
 def sha256_hex(arr):
     """SHA-256 of an array's raw bytes (C order), to record exactly which inputs ran."""
     return hashlib.sha256(np.ascontiguousarray(arr).tobytes()).hexdigest()
+
+
+def orthonormal_rows(rng, n_sets, s, d):
+    """``n_sets`` stacks of ``s`` orthonormal rows in R^d, float32 [n_sets, s, d]: the Q
+    factor of a Gaussian d x s matrix's QR decomposition, transposed (a random frame)."""
+    out = np.empty((n_sets, s, d), dtype=np.float32)
+    for i in range(n_sets):
+        q, _ = np.linalg.qr(rng.standard_normal((d, s)))
+        out[i] = q.T
+    return out

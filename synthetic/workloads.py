@@ -57,6 +57,7 @@ class DecodeWorkload:
     needle: str = "none"  # "none", "shifted" or "spread"
     n_needles: int = 4
     global_pos: tuple = ()
+    sub_dim: int = 0  # query-subspace dimension of the factor rows (0: none)
 
     def scaled(self, **kw):
         return dataclasses.replace(self, **kw)
@@ -99,7 +100,7 @@ WORKLOADS = {
     "cobs_decode_128k": DecodeWorkload(
         name="cobs_decode_128k", batch=4, n_q_heads=64, n_kv_heads=8, head_dim=128,
         n_ctx=131072, block_size=64, rank=4, top_k=32, window=1024, n_sink=64, dtype="bf16",
-        seed=4, needle="spread"),
+        seed=4, needle="spread", sub_dim=96),
 }
 
 

@@ -33,14 +33,15 @@ def as_f64(arr):
 
 
 def gpu_decode_step(api, x, w, kv_capacity=None, nblk_capacity=None, global_pos=(), dev=None,
-                    one_call=False, mean_dtype="f32", factor_fp4=False):
+                    one_call=False, mean_dtype="f32", factor_fp4=False, basis=None):
     """Run summaries -> select/top-k -> decode on the GPU through the binding.
 
     ``x`` holds Q, K, V numpy arrays (float32 or bf16 bits) of workload ``w``.
     With ``one_call`` the step is bsattn_decode_step (selection and decode in one
     call); otherwise bsattn_select_topk, then bsattn_decode.  ``mean_dtype`` "bf16"
     stores the block means in bfloat16; ``factor_fp4`` the factor rows as FP4 codes
-    (returned as ``factor`` uint8 codes plus ``factor_scale``).
+    (returned as ``factor`` uint8 codes plus ``factor_scale``).  ``basis`` [Hkv, s, d]
+    (numpy float32) projects the factor rows onto each K/V head's query subspace.
     Returns numpy copies of mean (as float32), factor, scores, sel, O, lse.
     """
     torch = torch_mod()
@@ -55,13 +56,17 @@ def gpu_decode_step(api, x, w, kv_capacity=None, nblk_capacity=None, global_pos=
     shape = api.make_shape(B, Hq, Hkv, d, n, kv_capacity=cap, dtype=w.dtype)
     mean = torch.full((B, Hkv, max(nbcap, 1), d), float("nan"), device="cuda",
                       dtype=torch.bfloat16 if mean_dtype == "bf16" else torch.float32)
-    factor = fscale = None
+    factor = fscale = bdev = None
+    e = d if basis is None else basis.shape[1]
+    if basis is not None:
+        bdev = torch.from_numpy(np.ascontiguousarray(basis, dtype=np.float32)).cuda()
     if w.rank > 0 and factor_fp4:
-        factor = torch.full((B, Hkv, max(nbcap, 1), w.rank, d // 2), 255, dtype=torch.uint8, device="cuda")
+        factor = torch.full((B, Hkv, max(nbcap, 1), w.rank, e // 2), 255, dtype=torch.uint8, device="cuda")
         fscale = torch.full((B, Hkv, max(nbcap, 1), w.rank), float("nan"), device="cuda")
     elif w.rank > 0:
-        factor = torch.full((B, Hkv, max(nbcap, 1), w.rank, d), float("nan"), device="cuda")
-    api.bsattn_build_summaries(shape, K, w.rank, 0, nb, max(nbcap, 1), mean, factor, factor_scale=fscale)
+        factor = torch.full((B, Hkv, max(nbcap, 1), w.rank, e), float("nan"), device="cuda")
+    api.bsattn_build_summaries(shape, K, w.rank, 0, nb, max(nbcap, 1), mean, factor, factor_scale=fscale,
+                               basis=bdev)
     scores = torch.full((B, Hkv, max(nbcap, 1)), float("nan"), device="cuda")
     sel = torch.full((B, Hkv, w.top_k), -7, dtype=torch.int32, device="cuda")
     O = torch.full((B, Hq, d), float("nan"), device="cuda")
@@ -71,10 +76,10 @@ def gpu_decode_step(api, x, w, kv_capacity=None, nblk_capacity=None, global_pos=
     ws = torch.full((nbytes,), 255, dtype=torch.uint8, device="cuda")  # garbage contents
     if one_call:
         api.bsattn_decode_step(shape, Q, K, V, mean, factor, w.rank, max(nbcap, 1), w.top_k, w.window,
-                               w.n_sink, gp, sel, scores, O, lse, ws, factor_scale=fscale)
+                               w.n_sink, gp, sel, scores, O, lse, ws, factor_scale=fscale, basis=bdev)
     else:
         api.bsattn_select_topk(shape, Q, mean, factor, w.rank, max(nbcap, 1), w.top_k, w.window,
-                               w.n_sink, gp, sel, scores, factor_scale=fscale)
+                               w.n_sink, gp, sel, scores, factor_scale=fscale, basis=bdev)
         api.bsattn_decode(shape, Q, K, V, sel, w.top_k, w.window, w.n_sink, gp, O, lse, ws)
     torch.cuda.synchronize()
     return dict(mean=mean.float().cpu().numpy(), factor=None if factor is None else factor.cpu().numpy(),

@@ -114,14 +114,15 @@ def test_decode_rejects_bad_arguments():
 
 
 STEP_ARGS = ("shape", "Q", "K", "V", "mean", "mean_dtype", "factor", "factor_dtype", "factor_scale",
-             "rank", "nblk", "top_k", "window", "n_sink", "gpos", "n_global", "sel", "scores", "O", "lse",
+             "basis", "sub_dim", "rank", "nblk", "top_k", "window", "n_sink", "gpos", "n_global", "sel", "scores", "O", "lse",
              "ws", "ws_bytes", "stream")
-SELECT_ARGS = ("shape", "Q", "mean", "mean_dtype", "factor", "factor_dtype", "factor_scale", "rank", "nblk",
+SELECT_ARGS = ("shape", "Q", "mean", "mean_dtype", "factor", "factor_dtype", "factor_scale", "basis",
+               "sub_dim", "rank", "nblk",
                "top_k", "window", "n_sink", "gpos", "n_global", "sel", "scores", "stream")
 SUMMARY_ARGS = ("shape", "K", "rank", "first_block", "n_blocks", "nblk", "mean", "mean_dtype", "factor",
-                "factor_dtype", "factor_scale", "stream")
+                "factor_dtype", "factor_scale", "basis", "sub_dim", "stream")
 GOOD = dict(Q=FAKE, K=FAKE, V=FAKE, mean=FAKE, mean_dtype=0, factor=None, factor_dtype=0, factor_scale=None,
-            rank=0, nblk=4, top_k=2, window=64, n_sink=0, gpos=None, n_global=0, sel=FAKE, scores=FAKE,
+            basis=None, sub_dim=0, rank=0, nblk=4, top_k=2, window=64, n_sink=0, gpos=None, n_global=0, sel=FAKE, scores=FAKE,
             O=FAKE, lse=None, ws=FAKE, ws_bytes=1 << 30, stream=None, first_block=0, n_blocks=4)
 
 
@@ -177,6 +178,33 @@ def test_summaries_reject_bad_ranges():
     assert _call(f, SUMMARY_ARGS, mean_dtype=3)[0] == 1                       # unknown mean dtype
     assert _call(f, SUMMARY_ARGS, rank=4, factor=FAKE, factor_dtype=2)[0] == 1  # FP4 without scales
     assert _call(f, SUMMARY_ARGS, n_blocks=0, mean_dtype=1)[0] == 0           # empty range: no launch
+
+
+FP4 = dict(rank=4, factor=FAKE, factor_dtype=2, factor_scale=FAKE, mean_dtype=1)
+
+
+@pytest.mark.parametrize("f,names", [("bsattn_build_summaries", SUMMARY_ARGS),
+                                     ("bsattn_select_topk", SELECT_ARGS),
+                                     ("bsattn_decode_step", STEP_ARGS)])
+def test_query_subspace_basis_is_checked(f, names):
+    """sub_dim: 0 or a multiple of 32 in [32, d] with rank >= 1 and an aligned basis."""
+    for bad in (48, 16, 96, -32):                              # d = 64 here
+        st, msg = _call(f, names, basis=FAKE, sub_dim=bad, **FP4)
+        assert st == 1 and "sub_dim" in msg
+    st, msg = _call(f, names, basis=None, sub_dim=32, **FP4)
+    assert st == 1 and "basis" in msg
+    st, msg = _call(f, names, basis=FAKE + 4, sub_dim=32, **FP4)
+    assert st == 1 and "basis" in msg
+    st, msg = _call(f, names, basis=FAKE, sub_dim=32, rank=0)
+    assert st == 1 and "rank" in msg
+    if f != "bsattn_build_summaries":
+        # the projected scorer takes the compressed summary only: bf16 means and FP4 rows
+        st, msg = _call(f, names, basis=FAKE, sub_dim=32, **dict(FP4, factor_dtype=0))
+        assert st == 2 and "basis" in msg
+        st, msg = _call(f, names, basis=FAKE, sub_dim=32, **dict(FP4, mean_dtype=0))
+        assert st == 2 and "basis" in msg
+        st, msg = _call(f, names, basis=FAKE, sub_dim=32, shape=_shape(dtype=0), **FP4)
+        assert st == 2 and "basis" in msg
 
 
 def test_prefill_rejects_bad_arguments():

@@ -255,7 +255,7 @@ def _unpack_fp4(codes, scale):
     return val, c
 
 
-def _check_fp4(api, w, globals_, pairs=None, one_call=True, mean_dtype="bf16"):
+def _check_fp4(api, w, globals_, pairs=None, one_call=True, mean_dtype="bf16", basis=None):
     """FP4 factor rows.  The GPU quantises its fp32 eigensolver's rows, the oracle its
     fp64 rows, so a code can differ where the exact value sits at a rounding midpoint:
     codes must match the oracle's except for at most 1% of entries, each one E2M1 step
@@ -263,11 +263,16 @@ def _check_fp4(api, w, globals_, pairs=None, one_call=True, mean_dtype="bf16"):
     rows) within a per-block bound computed here from how the two sets of codes differ
     (1/2 |(p + e)^2 - p^2| <= (|p| + |e|/2) |e| per row, p the oracle's projection, e
     bounded by |q| . |row difference|), and the selections may differ only within that
-    bound of the k-th score.  Outputs: the usual bar over the GPU's selection."""
+    bound of the k-th score.  Outputs: the usual bar over the GPU's selection.  With a
+    query-subspace ``basis`` [Hkv, s, d] the rows are the projected covariance's and
+    meet the projected query (the GPU multiplies the basis, split into two bfloat16
+    parts, with the bf16 query, and splits the projected query into two bfloat16
+    parts: 2^-17 relative each, inside the 2e-4 slack of the bound)."""
     x = make_decode_inputs(w)
-    print(f"[decode fp4] {w.name} one_call={one_call} mean={mean_dtype}", flush=True)
+    sd = None if basis is None else basis.shape[1]
+    print(f"[decode fp4] {w.name} one_call={one_call} mean={mean_dtype} sub_dim={sd}", flush=True)
     got = gpu_decode_step(api, x, w, global_pos=globals_, one_call=one_call, mean_dtype=mean_dtype,
-                          factor_fp4=True)
+                          factor_fp4=True, basis=basis)
     Q, K, V = as_f64(x["Q"]), as_f64(x["K"]), as_f64(x["V"])
     S, n, G, d, r = w.block_size, w.n_ctx, w.n_q_heads // w.n_kv_heads, w.head_dim, w.rank
     nb = n // S
@@ -278,7 +283,8 @@ def _check_fp4(api, w, globals_, pairs=None, one_call=True, mean_dtype="bf16"):
         pairs = [(b, g) for b in range(w.batch) for g in range(w.n_kv_heads)]
     n_codes = n_flips = 0
     for (b, g) in pairs:
-        mean, f = oracle.block_summaries(K[b, g, :n], S, r, mean_bf16=mean_dtype == "bf16")
+        P = None if basis is None else basis[g].astype(np.float64)
+        mean, f = oracle.block_summaries(K[b, g, :n], S, r, mean_bf16=mean_dtype == "bf16", basis=P)
         if nb == 0:
             continue
         codes_or, sc_or = oracle.quantize_e2m1_rows(f)
@@ -287,6 +293,8 @@ def _check_fp4(api, w, globals_, pairs=None, one_call=True, mean_dtype="bf16"):
         # blocks whose top r+1 eigenvalues are separated: rows defined up to sign (fixed)
         X = K[b, g, :nb * S].reshape(nb, S, d)
         Xc = X - X.mean(axis=1, keepdims=True)
+        if P is not None:
+            Xc = Xc @ P.T
         lam = np.sort(np.linalg.eigvalsh(np.einsum("brd,bre->bde", Xc, Xc) / S), axis=1)[:, ::-1]
         gaps = np.min(np.abs(np.diff(lam[:, :r + 1], axis=1)), axis=1) / np.maximum(lam[:, 0], 1e-30)
         ok = gaps > 1e-3
@@ -296,9 +304,10 @@ def _check_fp4(api, w, globals_, pairs=None, one_call=True, mean_dtype="bf16"):
         n_flips += int(diff.sum())
         assert np.all(np.abs(deq_gpu[ok] - deq_or[ok])[diff] <= 2.0 * np.max(sc_or[ok]) * 1.001)
         qs = scale * Q[b, g * G:(g + 1) * G]
-        s_ref = oracle.group_scores(oracle.head_scores(qs, mean, deq_or))
-        p = np.einsum("hd,brd->hbr", qs, deq_or)
-        e = np.einsum("hd,brd->hbr", np.abs(qs), np.abs(deq_gpu - deq_or))
+        s_ref = oracle.group_scores(oracle.head_scores(qs, mean, deq_or, basis=P))
+        qp = qs if P is None else qs @ P.T
+        p = np.einsum("hd,brd->hbr", qp, deq_or)
+        e = np.einsum("hd,brd->hbr", np.abs(qp), np.abs(deq_gpu - deq_or))
         bound = np.max(np.sum((np.abs(p) + e / 2) * e, axis=2), axis=0) + 2e-4 * (1 + np.abs(s_ref))
         assert np.all(np.abs(got["scores"][b, g, :nb] - s_ref)[ok] <= bound[ok])
         # selection within the quantisation band of the k-th score
@@ -331,6 +340,37 @@ def test_fp4_factors_small_cases(api, case, one_call):
 
 def test_fp4_factors_cobs_128k(api):
     _check_fp4(api, WORKLOADS["cobs_decode_128k"], (), pairs=[(0, 0), (3, 6)])
+
+
+def calibration_basis(w, s, seed):
+    """Per K/V head, the oracle's query-subspace basis [s, d] of a seeded calibration
+    sample: 512 Gaussian queries with a decaying spectrum in a random orientation (the
+    concentrated query distribution the subspace projection assumes)."""
+    rng = np.random.default_rng(seed)
+    d = w.head_dim
+    out = []
+    for _ in range(w.n_kv_heads):
+        R, _ = np.linalg.qr(rng.standard_normal((d, d)))
+        Qc = (rng.standard_normal((512, d)) * np.exp(-np.arange(d) / 24.0)) @ R.T
+        out.append(oracle.query_subspace_basis(Qc, s))
+    return np.stack(out).astype(np.float32)
+
+
+# sub_dim per bf16 case: 96, 32, 64, 32, 128 (every projected scorer variant)
+SUBSPACE_CASES = [(c, s) for c, s in zip([c for c in FP4_CASES if c[0].dtype == "bf16"], (96, 32, 64, 32, 128))]
+
+
+@pytest.mark.parametrize("case,sub_dim", SUBSPACE_CASES,
+                         ids=[f"{c[0].name}_s{s}" for c, s in SUBSPACE_CASES])
+@pytest.mark.parametrize("one_call", [False, True])
+def test_subspace_projection_small_cases(api, case, sub_dim, one_call):
+    w, globals_, _ = case
+    _check_fp4(api, w, globals_, one_call=one_call, basis=calibration_basis(w, sub_dim, 50 + sub_dim))
+
+
+def test_subspace_projection_cobs_128k(api):
+    w = WORKLOADS["cobs_decode_128k"]
+    _check_fp4(api, w, (), pairs=[(0, 0), (2, 5)], basis=calibration_basis(w, 96, 60))
 
 
 def test_repeated_calls_reuse_the_workspace(api):
