@@ -443,7 +443,7 @@ def main():
         "gathered_kv_GBps": h.get("gathered_kv_GBps"),
         "gathered_kv_frac_hbm": h.get("gathered_kv_frac_hbm"),
         "roofline": {
-            "kernel": "bsattn_decode_step: select_scores_kernel, decode_bf16_kernel with the "
+            "kernel": "bsattn_decode_step: select_scores_mfma_kernel, decode_bf16_kernel with the "
                       "in-wave top-k, decode_merge_kernel (one call, three launches)",
             "bound": "hbm",
             "achieved": h["step_bytes"] / (h["ms_per_step"] * 1e-3) / 1e9,
