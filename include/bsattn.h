@@ -126,6 +126,24 @@ bsattn_status bsattn_build_summaries(const bsattn_shape* shape, const void* K, i
                                      const float* basis, int32_t sub_dim, void* hip_stream);
 
 /*
+ * Append the decode token to the cache and keep the summaries current
+ * [COBS 1 (decode reads the cache block by block); ATT KV cache]: the new
+ * token is t = n_ctx - 1 (shape is the one of the decode step that follows,
+ * n_ctx counting the new token; n_ctx <= kv_capacity).  For every (b, g):
+ *   K[b,g,t,:] = K_new[b,g,:],  V[b,g,t,:] = V_new[b,g,:]
+ * with K_new, V_new [B, Hkv, d] of shape.dtype.  When t completes block
+ * j = n_ctx / S - 1 (n_ctx % S == 0), block j's summary is then built exactly
+ * as bsattn_build_summaries(shape, K, rank, j, 1, ...) builds it, with the
+ * summary arguments given here; they are read (and validated) only then.
+ * Invalid arguments launch nothing.  Ordered after earlier calls on the stream.
+ */
+bsattn_status bsattn_append_kv(const bsattn_shape* shape, const void* K_new, const void* V_new, void* K,
+                               void* V, int32_t rank, int32_t nblk_capacity, void* mean,
+                               int32_t mean_dtype, void* factor, int32_t factor_dtype,
+                               float* factor_scale, const float* basis, int32_t sub_dim,
+                               void* hip_stream);
+
+/*
  * Block selection for the decode query (the last cached token, t = n_ctx - 1).
  *  1. Per query head h and complete block j, with q~ = scale * Q[b,h]:
  *       s[h,j] = q~ . mean_j                                (rank == 0) [COBS 2.2]

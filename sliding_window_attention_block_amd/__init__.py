@@ -16,7 +16,7 @@ from . import _lib
 from ._lib import BSATTN_BF16, BSATTN_F32, BSATTN_FP4_E2M1, Shape
 
 __all__ = [
-    "BsattnError", "Shape", "make_shape", "library", "bsattn_build_summaries",
+    "BsattnError", "Shape", "make_shape", "library", "bsattn_build_summaries", "bsattn_append_kv",
     "bsattn_select_topk", "bsattn_decode_workspace_bytes", "bsattn_decode",
     "bsattn_decode_step",
     "bsattn_prefill",
@@ -117,6 +117,17 @@ def bsattn_build_summaries(shape, K, rank, first_block, n_blocks, nblk_capacity,
                                             _ptr(factor), _factor_dtype(factor, factor_scale),
                                             _ptr(factor_scale), _ptr(basis), _sub_dim(basis),
                                             _stream(stream)))
+
+
+def bsattn_append_kv(shape, K_new, V_new, K, V, rank, nblk_capacity, mean=None, factor=None, stream=None,
+                     factor_scale=None, basis=None):
+    """Write token n_ctx - 1 of every (b, K/V head) and build the summary of the block
+    it completes (summary buffers are only touched then)."""
+    _check(library().bsattn_append_kv(ctypes.byref(shape), _ptr(K_new), _ptr(V_new), _ptr(K), _ptr(V), rank,
+                                      nblk_capacity, _ptr(mean),
+                                      BSATTN_F32 if mean is None else _mean_dtype(mean), _ptr(factor),
+                                      _factor_dtype(factor, factor_scale), _ptr(factor_scale), _ptr(basis),
+                                      _sub_dim(basis), _stream(stream)))
 
 
 def bsattn_select_topk(shape, Q, mean, factor, rank, nblk_capacity, top_k, window, n_sink,

@@ -312,12 +312,15 @@ const char* bsattn_last_error(void) { return g_err; }
 
 const char* bsattn_version(void) { return "bsattn 0.1.0 gfx950"; }
 
-bsattn_status bsattn_build_summaries(const bsattn_shape* shape, const void* K, int32_t rank,
-                                     int32_t first_block, int32_t n_blocks, int32_t nblk_capacity,
-                                     void* mean, int32_t mean_dtype, void* factor, int32_t factor_dtype,
-                                     float* factor_scale, const float* basis, int32_t sub_dim,
-                                     void* hip_stream) {
-  g_err[0] = 0;
+}  // extern "C"
+
+namespace {
+
+// Validation of the summaries' arguments (bsattn_build_summaries, bsattn_append_kv).
+bsattn_status summaries_args(const bsattn_shape* shape, const void* K, int32_t rank, int32_t first_block,
+                             int32_t n_blocks, int32_t nblk_capacity, void* mean, int32_t mean_dtype, void* factor,
+                             int32_t factor_dtype, float* factor_scale, const float* basis, int32_t sub_dim,
+                             bsattn::SummaryArgs& a) {
   bsattn_status st = check_shape(shape, false);
   if (st != BSATTN_OK) return st;
   if (K == nullptr || mean == nullptr) return fail(BSATTN_ERR_INVALID, "K and mean must be non-NULL");
@@ -335,8 +338,7 @@ bsattn_status bsattn_build_summaries(const bsattn_shape* shape, const void* K, i
     return fail(BSATTN_ERR_INVALID, "block range exceeds nblk_capacity");
   if (!aligned16(K) || !aligned16(mean) || (factor && !aligned16(factor)))
     return fail(BSATTN_ERR_INVALID, "device pointers must be 16-byte aligned");
-  if (n_blocks == 0) return BSATTN_OK;
-  bsattn::SummaryArgs a;
+  std::memset(&a, 0, sizeof(a));
   a.K = K; a.mean = mean; a.factor = factor;
   a.bh = shape->batch * shape->n_kv_heads;
   a.n_kv_heads = shape->n_kv_heads;
@@ -352,8 +354,59 @@ bsattn_status bsattn_build_summaries(const bsattn_shape* shape, const void* K, i
   a.factor_scale = factor_scale;
   a.basis = sub_dim > 0 ? basis : nullptr;
   a.sub_dim = sub_dim;
+  return BSATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+bsattn_status bsattn_build_summaries(const bsattn_shape* shape, const void* K, int32_t rank,
+                                     int32_t first_block, int32_t n_blocks, int32_t nblk_capacity,
+                                     void* mean, int32_t mean_dtype, void* factor, int32_t factor_dtype,
+                                     float* factor_scale, const float* basis, int32_t sub_dim,
+                                     void* hip_stream) {
+  g_err[0] = 0;
+  bsattn::SummaryArgs a;
+  const bsattn_status st = summaries_args(shape, K, rank, first_block, n_blocks, nblk_capacity, mean, mean_dtype,
+                                          factor, factor_dtype, factor_scale, basis, sub_dim, a);
+  if (st != BSATTN_OK) return st;
+  if (n_blocks == 0) return BSATTN_OK;
   hipError_t e = bsattn::launch_summaries(a, (hipStream_t)hip_stream);
   if (e != hipSuccess) return fail(BSATTN_ERR_HIP, "summaries launch: %s", hipGetErrorString(e));
+  return BSATTN_OK;
+}
+
+bsattn_status bsattn_append_kv(const bsattn_shape* shape, const void* K_new, const void* V_new, void* K, void* V,
+                               int32_t rank, int32_t nblk_capacity, void* mean, int32_t mean_dtype, void* factor,
+                               int32_t factor_dtype, float* factor_scale, const float* basis, int32_t sub_dim,
+                               void* hip_stream) {
+  g_err[0] = 0;
+  bsattn_status st = check_shape(shape, false);
+  if (st != BSATTN_OK) return st;
+  if (K_new == nullptr || V_new == nullptr || K == nullptr || V == nullptr)
+    return fail(BSATTN_ERR_INVALID, "K_new, V_new, K and V must be non-NULL");
+  if (!aligned16(K_new) || !aligned16(V_new) || !aligned16(K) || !aligned16(V))
+    return fail(BSATTN_ERR_INVALID, "device pointers must be 16-byte aligned");
+  // the new token is t = n_ctx - 1; it completes block n_ctx / S - 1 when n_ctx % S == 0
+  const bool completes = shape->n_ctx % shape->block_size == 0;
+  bsattn::SummaryArgs sa;
+  if (completes) {
+    st = summaries_args(shape, K, rank, shape->n_ctx / shape->block_size - 1, 1, nblk_capacity, mean, mean_dtype,
+                        factor, factor_dtype, factor_scale, basis, sub_dim, sa);
+    if (st != BSATTN_OK) return st;
+  }
+  bsattn::AppendArgs aa;
+  aa.K_new = K_new; aa.V_new = V_new; aa.K = K; aa.V = V;
+  aa.kv_capacity = shape->kv_capacity;
+  aa.pos = shape->n_ctx - 1;
+  aa.row_bytes = shape->head_dim * (shape->dtype == BSATTN_BF16 ? 2 : 4);
+  hipError_t e = bsattn::launch_append(aa, shape->batch * shape->n_kv_heads, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return fail(BSATTN_ERR_HIP, "append launch: %s", hipGetErrorString(e));
+  if (completes) {
+    e = bsattn::launch_summaries(sa, (hipStream_t)hip_stream);
+    if (e != hipSuccess) return fail(BSATTN_ERR_HIP, "summaries launch: %s", hipGetErrorString(e));
+  }
   return BSATTN_OK;
 }
 

@@ -31,6 +31,18 @@ struct SummaryArgs {
 };
 hipError_t launch_summaries(const SummaryArgs& a, hipStream_t stream);
 
+// One new token per (b, K/V head): rows K_new[bh], V_new[bh] -> K, V row `pos`.
+struct AppendArgs {
+  const void* K_new;
+  const void* V_new;
+  void* K;
+  void* V;
+  int32_t kv_capacity;
+  int32_t pos;
+  int32_t row_bytes;  // d * element size (a multiple of 16)
+};
+hipError_t launch_append(const AppendArgs& a, int n_pairs, hipStream_t stream);
+
 struct SelectArgs {
   const void* Q;
   const void* mean;  // fp32, or bf16 when mean_bf16

@@ -327,6 +327,27 @@ hipError_t launch_t(const SummaryArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+// Append: one workgroup per (b, K/V head) copies the new token's K and V rows
+// (16-byte chunks) into row `pos` of the cache.
+__global__ __launch_bounds__(64) void append_kv_kernel(AppendArgs a) {
+  const size_t bh = blockIdx.x;
+  const int n16 = a.row_bytes / 16;
+  const uint4* ks = reinterpret_cast<const uint4*>(static_cast<const char*>(a.K_new) + bh * a.row_bytes);
+  const uint4* vs = reinterpret_cast<const uint4*>(static_cast<const char*>(a.V_new) + bh * a.row_bytes);
+  const size_t dst = (bh * a.kv_capacity + a.pos) * (size_t)a.row_bytes;
+  uint4* kd = reinterpret_cast<uint4*>(static_cast<char*>(a.K) + dst);
+  uint4* vd = reinterpret_cast<uint4*>(static_cast<char*>(a.V) + dst);
+  for (int i = threadIdx.x; i < n16; i += 64) {
+    kd[i] = ks[i];
+    vd[i] = vs[i];
+  }
+}
+
+hipError_t launch_append(const AppendArgs& a, int n_pairs, hipStream_t stream) {
+  hipLaunchKernelGGL(append_kv_kernel, dim3(n_pairs), dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_summaries(const SummaryArgs& a, hipStream_t stream) {
   if (a.n_blocks == 0) return hipSuccess;
   if (a.head_dim == 64) return a.bf16 ? launch_t<64, true>(a, stream) : launch_t<64, false>(a, stream);

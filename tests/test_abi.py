@@ -24,7 +24,7 @@ def _header_functions():
 def test_library_exports_every_declared_function():
     lib = api.library()
     declared = _header_functions()
-    assert len(declared) == 10
+    assert len(declared) == 11
     for name in declared:
         assert hasattr(lib, name), name
     assert set(declared) == set(_lib.EXPORTS)
@@ -242,3 +242,21 @@ def test_binding_raises_with_the_library_message():
     with pytest.raises(ValueError):
         api.bsattn_prefill(api.make_shape(1, 1, 1, 64, 8), torch.zeros(1), torch.zeros(1),
                            torch.zeros(1), 1, 0, 1, None, torch.zeros(1))
+
+
+APPEND_ARGS = ("shape", "K_new", "V_new", "K", "V", "rank", "nblk", "mean", "mean_dtype", "factor",
+               "factor_dtype", "factor_scale", "basis", "sub_dim", "stream")
+
+
+def test_append_rejects_bad_arguments():
+    f = "bsattn_append_kv"
+    kw = dict(K_new=FAKE, V_new=FAKE)
+    assert _call(f, APPEND_ARGS, **dict(kw, K_new=None))[0] == 1
+    assert _call(f, APPEND_ARGS, **dict(kw, V=FAKE + 8))[0] == 1                      # misaligned V
+    assert _call(f, APPEND_ARGS, **kw, shape=_shape(n_ctx=300, kv_capacity=299))[0] == 1  # past capacity
+    # token 256 completes block 3: the summary arguments are validated then, before any launch
+    assert _call(f, APPEND_ARGS, **kw, shape=_shape(n_ctx=256), mean=None)[0] == 1
+    assert _call(f, APPEND_ARGS, **kw, shape=_shape(n_ctx=256), nblk=3)[0] == 1      # block 3 past capacity
+    assert _call(f, APPEND_ARGS, **kw, shape=_shape(n_ctx=256), rank=2)[0] == 1      # rank 2, no factor
+    st, msg = _call(f, APPEND_ARGS, **kw, shape=_shape(n_ctx=256), basis=FAKE, sub_dim=48, **FP4)
+    assert st == 1 and "sub_dim" in msg
