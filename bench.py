@@ -116,7 +116,19 @@ def to_dev(torch, a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def bench_decode(api, torch, w, x, steps, warmup, mean_dtype="bf16", factor_fp4=True, subspace=True):
+def to_pages(torch, X, page_tokens, perm):
+    """Contiguous cache [B, Hkv, cap, d] -> page pool [n_pages, Hkv, P, d] under the
+    page assignment perm [B, cap / P] (distinct page numbers)."""
+    B, Hkv, cap, d = X.shape
+    P, mp = page_tokens, cap // page_tokens
+    pool = torch.empty((int(perm.max()) + 1, Hkv, P, d), dtype=X.dtype, device="cuda")
+    idx = torch.from_numpy(perm.reshape(-1)).cuda().long()
+    pool[idx] = X.reshape(B, Hkv, mp, P, d).permute(0, 2, 1, 3, 4).reshape(B * mp, Hkv, P, d)
+    return pool
+
+
+def bench_decode(api, torch, w, x, steps, warmup, mean_dtype="bf16", factor_fp4=True, subspace=True,
+                 page_tokens=None):
     B, Hq, Hkv, d, n, S = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_ctx, w.block_size
     nb = n // S
     shape = api.make_shape(B, Hq, Hkv, d, n, dtype=w.dtype)
@@ -143,6 +155,13 @@ def bench_decode(api, torch, w, x, steps, warmup, mean_dtype="bf16", factor_fp4=
         K = K0 if r == 0 else K0.clone()
         V = V0 if r == 0 else V0.clone()
         Q = Q0 if r == 0 else Q0.clone()
+        pg = table = None
+        if page_tokens:  # pages of every replica in a random order (a fragmented pool)
+            mp = K.shape[2] // page_tokens
+            perm = np.random.default_rng(w.seed + 2000 + r).permutation(B * mp).reshape(B, mp).astype(np.int32)
+            K, V = to_pages(torch, K, page_tokens, perm), to_pages(torch, V, page_tokens, perm)
+            table = torch.from_numpy(perm).cuda()
+            pg = api.paged_kv(table, page_tokens, B * mp)
         mean = torch.empty((B, Hkv, nb, d), device="cuda",
                            dtype=torch.bfloat16 if mean_dtype == "bf16" else torch.float32)
         fscale = None
@@ -157,7 +176,7 @@ def bench_decode(api, torch, w, x, steps, warmup, mean_dtype="bf16", factor_fp4=
         O = torch.empty((B, Hq, d), device="cuda")
         lse = torch.empty((B, Hq), device="cuda")
         reps.append(dict(K=K, V=V, Q=Q, mean=mean, factor=factor, fscale=fscale, scores=scores, sel=sel,
-                         ws=ws, O=O, lse=lse))
+                         ws=ws, O=O, lse=lse, pg=pg, table=table))
     del K0, V0, Q0
     # A1: summaries (built once per block; timed on every replica)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -165,7 +184,7 @@ def bench_decode(api, torch, w, x, steps, warmup, mean_dtype="bf16", factor_fp4=
     for rp in reps:
         ev[0].record()
         api.bsattn_build_summaries(shape, rp["K"], w.rank, 0, nb, nb, rp["mean"], rp["factor"],
-                                   factor_scale=rp["fscale"], basis=basis)
+                                   factor_scale=rp["fscale"], basis=basis, paged=rp["pg"])
         ev[1].record()
         torch.cuda.synchronize()
         build_ms.append(ev[0].elapsed_time(ev[1]))
@@ -177,12 +196,12 @@ def bench_decode(api, torch, w, x, steps, warmup, mean_dtype="bf16", factor_fp4=
 
     def decode(rp):
         api.bsattn_decode(shape, rp["Q"], rp["K"], rp["V"], rp["sel"], w.top_k, w.window, w.n_sink,
-                          None, rp["O"], rp["lse"], rp["ws"])
+                          None, rp["O"], rp["lse"], rp["ws"], paged=rp["pg"])
 
     def step(rp):
         api.bsattn_decode_step(shape, rp["Q"], rp["K"], rp["V"], rp["mean"], rp["factor"], w.rank, nb,
                                w.top_k, w.window, w.n_sink, None, rp["sel"], rp["scores"], rp["O"],
-                               rp["lse"], rp["ws"], factor_scale=rp["fscale"], basis=basis)
+                               rp["lse"], rp["ws"], factor_scale=rp["fscale"], basis=basis, paged=rp["pg"])
 
     for i in range(warmup):
         rp = reps[i % R]
@@ -240,7 +259,7 @@ def bench_decode(api, torch, w, x, steps, warmup, mean_dtype="bf16", factor_fp4=
     eager_ms = (time.perf_counter() - t0) * 1e3 / steps
     res = dict(
         workload=w.name, mean_dtype=mean_dtype, factor="fp4" if fp4 else ("f32" if w.rank else None),
-        sub_dim=sub or None,
+        sub_dim=sub or None, page_tokens=page_tokens,
         ms_per_step=ms_step, wall_ms_per_step=wall_step,
         tokens_per_s=B / (ms_step * 1e-3),
         eager_ms_per_step=eager_ms, two_call_ms_per_step=two_ms, replicas=R, attended_tokens=tokens,
@@ -396,9 +415,11 @@ def main():
         log(f"[bench] {name}: inputs generated in {time.perf_counter() - t:.1f} s")
         if name.endswith(("32k", "128k")):
             results[name] = bench_decode(api, torch, w, x, args.steps, args.warmup)
-            if name == HEADLINE:  # context: the same step with fp32 block means
+            if name == HEADLINE:  # context: fp32 block means; a paged cache of 4 KB pages
                 results[name + "/fp32_means"] = bench_decode(api, torch, w, x, args.steps, args.warmup,
                                                              mean_dtype="f32")
+                results[name + "/paged16"] = bench_decode(api, torch, w, x, args.steps, args.warmup,
+                                                          page_tokens=16)
             elif w.rank > 0:  # context: FP4 rows without the subspace projection; fp32 rows
                 if w.sub_dim > 0:
                     results[name + "/no_subspace"] = bench_decode(api, torch, w, x, args.steps, args.warmup,

@@ -82,6 +82,27 @@ typedef struct {
   int32_t dtype;       /* bsattn_dtype of Q, K, V                                   */
 } bsattn_shape;
 
+/*
+ * A paged K/V cache [ATT KV cache section: PagedAttention allocates the cache
+ * page by page]: K and V are pools of pages [n_pages, Hkv, page_tokens, d]
+ * (shape.dtype); token t of batch entry b is row t % page_tokens of page
+ * block_table[b * max_pages + t / page_tokens], the same page number for every
+ * K/V head.  page_tokens: 16, 32 or 64 (16 tokens of bf16 at d = 128 is a
+ * 4 KB page per head).  block_table: device int32 [B, max_pages]; entries for
+ * tokens < n_ctx must be page numbers in [0, n_pages) (the kernels clamp every
+ * entry into that range, so a bad entry reads a wrong row, never outside the
+ * pools).  With a paged cache shape.kv_capacity must equal max_pages *
+ * page_tokens.  Calls that take a `paged` argument use the contiguous layout
+ * [B, Hkv, kv_capacity, d] when it is NULL.  The sparse decode reads paged
+ * caches in BF16 only.
+ */
+typedef struct {
+  const int32_t* block_table;
+  int32_t page_tokens;
+  int32_t max_pages;
+  int32_t n_pages;
+} bsattn_paged_kv;
+
 #define BSATTN_MAX_RANK 8        /* [COBS 4.3]: rank <= 8 recommended               */
 #define BSATTN_MAX_GLOBAL 256    /* global token positions per call                  */
 #define BSATTN_MAX_TOP_K 1024
@@ -123,7 +144,8 @@ bsattn_status bsattn_build_summaries(const bsattn_shape* shape, const void* K, i
                                      int32_t first_block, int32_t n_blocks,
                                      int32_t nblk_capacity, void* mean, int32_t mean_dtype,
                                      void* factor, int32_t factor_dtype, float* factor_scale,
-                                     const float* basis, int32_t sub_dim, void* hip_stream);
+                                     const float* basis, int32_t sub_dim, const bsattn_paged_kv* paged,
+                                     void* hip_stream);
 
 /*
  * Append the decode token to the cache and keep the summaries current
@@ -141,7 +163,7 @@ bsattn_status bsattn_append_kv(const bsattn_shape* shape, const void* K_new, con
                                void* V, int32_t rank, int32_t nblk_capacity, void* mean,
                                int32_t mean_dtype, void* factor, int32_t factor_dtype,
                                float* factor_scale, const float* basis, int32_t sub_dim,
-                               void* hip_stream);
+                               const bsattn_paged_kv* paged, void* hip_stream);
 
 /*
  * Block selection for the decode query (the last cached token, t = n_ctx - 1).
@@ -197,7 +219,7 @@ bsattn_status bsattn_decode(const bsattn_shape* shape, const void* Q, const void
                             const void* V, const int32_t* sel, int32_t top_k, int32_t window,
                             int32_t n_sink, const int32_t* global_pos_host, int32_t n_global,
                             float* O, float* lse, void* workspace, size_t ws_bytes,
-                            void* hip_stream);
+                            const bsattn_paged_kv* paged, void* hip_stream);
 
 /*
  * One decode step in one call: the selector's scores and top-k
@@ -222,7 +244,8 @@ bsattn_status bsattn_decode_step(const bsattn_shape* shape, const void* Q, const
                                  int32_t rank, int32_t nblk_capacity, int32_t top_k,
                                  int32_t window, int32_t n_sink, const int32_t* global_pos_host,
                                  int32_t n_global, int32_t* sel, float* scores, float* O,
-                                 float* lse, void* workspace, size_t ws_bytes, void* hip_stream);
+                                 float* lse, void* workspace, size_t ws_bytes,
+                                 const bsattn_paged_kv* paged, void* hip_stream);
 
 /*
  * Masked prefill attention, BF16 Q/K/V, fp32 O and lse.  Query i sees key j iff

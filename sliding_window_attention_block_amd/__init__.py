@@ -13,10 +13,11 @@ import ctypes
 import math
 
 from . import _lib
-from ._lib import BSATTN_BF16, BSATTN_F32, BSATTN_FP4_E2M1, Shape
+from ._lib import BSATTN_BF16, BSATTN_F32, BSATTN_FP4_E2M1, PagedKV, Shape
 
 __all__ = [
-    "BsattnError", "Shape", "make_shape", "library", "bsattn_build_summaries", "bsattn_append_kv",
+    "BsattnError", "Shape", "PagedKV", "make_shape", "paged_kv", "library", "bsattn_build_summaries",
+    "bsattn_append_kv",
     "bsattn_select_topk", "bsattn_decode_workspace_bytes", "bsattn_decode",
     "bsattn_decode_step",
     "bsattn_prefill",
@@ -105,29 +106,39 @@ def _factor_dtype(factor, factor_scale):
     raise ValueError(f"factor rows must be float32 or uint8 FP4 codes, not {factor.dtype}")
 
 
+def paged_kv(block_table, page_tokens, n_pages):
+    """bsattn_paged_kv for a block table tensor (int32 [B, max_pages] on the device) over
+    K and V page pools of n_pages pages of page_tokens tokens.  Keep the tensor alive."""
+    return PagedKV(block_table.data_ptr(), page_tokens, int(block_table.shape[1]), n_pages)
+
+
+def _paged(paged):
+    return None if paged is None else ctypes.byref(paged)
+
+
 def _sub_dim(basis):
     """Subspace dimension of a query-subspace basis [Hkv, sub_dim, d] (0 without one)."""
     return 0 if basis is None else int(basis.shape[1])
 
 
 def bsattn_build_summaries(shape, K, rank, first_block, n_blocks, nblk_capacity, mean, factor=None,
-                           stream=None, factor_scale=None, basis=None):
+                           stream=None, factor_scale=None, basis=None, paged=None):
     _check(library().bsattn_build_summaries(ctypes.byref(shape), _ptr(K), rank, first_block,
                                             n_blocks, nblk_capacity, _ptr(mean), _mean_dtype(mean),
                                             _ptr(factor), _factor_dtype(factor, factor_scale),
                                             _ptr(factor_scale), _ptr(basis), _sub_dim(basis),
-                                            _stream(stream)))
+                                            _paged(paged), _stream(stream)))
 
 
 def bsattn_append_kv(shape, K_new, V_new, K, V, rank, nblk_capacity, mean=None, factor=None, stream=None,
-                     factor_scale=None, basis=None):
+                     factor_scale=None, basis=None, paged=None):
     """Write token n_ctx - 1 of every (b, K/V head) and build the summary of the block
     it completes (summary buffers are only touched then)."""
     _check(library().bsattn_append_kv(ctypes.byref(shape), _ptr(K_new), _ptr(V_new), _ptr(K), _ptr(V), rank,
                                       nblk_capacity, _ptr(mean),
                                       BSATTN_F32 if mean is None else _mean_dtype(mean), _ptr(factor),
                                       _factor_dtype(factor, factor_scale), _ptr(factor_scale), _ptr(basis),
-                                      _sub_dim(basis), _stream(stream)))
+                                      _sub_dim(basis), _paged(paged), _stream(stream)))
 
 
 def bsattn_select_topk(shape, Q, mean, factor, rank, nblk_capacity, top_k, window, n_sink,
@@ -146,17 +157,17 @@ def bsattn_decode_workspace_bytes(shape, top_k, window, n_sink, n_global=0):
 
 
 def bsattn_decode(shape, Q, K, V, sel, top_k, window, n_sink, global_pos, O, lse, workspace,
-                  stream=None):
+                  stream=None, paged=None):
     g, ng = _globals(global_pos)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(library().bsattn_decode(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(sel),
                                    top_k, window, n_sink, g, ng, _ptr(O), _ptr(lse),
-                                   _ptr(workspace), ws_bytes, _stream(stream)))
+                                   _ptr(workspace), ws_bytes, _paged(paged), _stream(stream)))
 
 
 def bsattn_decode_step(shape, Q, K, V, mean, factor, rank, nblk_capacity, top_k, window, n_sink,
                        global_pos, sel, scores, O, lse, workspace, stream=None, factor_scale=None,
-                       basis=None):
+                       basis=None, paged=None):
     g, ng = _globals(global_pos)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(library().bsattn_decode_step(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(mean),
@@ -165,7 +176,7 @@ def bsattn_decode_step(shape, Q, K, V, mean, factor, rank, nblk_capacity, top_k,
                                         _ptr(basis), _sub_dim(basis), rank,
                                         nblk_capacity, top_k, window, n_sink, g, ng, _ptr(sel),
                                         _ptr(scores), _ptr(O), _ptr(lse), _ptr(workspace), ws_bytes,
-                                        _stream(stream)))
+                                        _paged(paged), _stream(stream)))
 
 
 def bsattn_prefill_workspace_bytes(shape, n_global):

@@ -56,6 +56,15 @@ _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
 _st = ctypes.c_int
 _pshape = ctypes.POINTER(Shape)
+
+
+class PagedKV(ctypes.Structure):
+    """bsattn_paged_kv: block table (device int32 [B, max_pages]) of a paged K/V cache."""
+    _fields_ = [("block_table", ctypes.c_void_p), ("page_tokens", ctypes.c_int32),
+                ("max_pages", ctypes.c_int32), ("n_pages", ctypes.c_int32)]
+
+
+_ppaged = ctypes.POINTER(PagedKV)
 _pi32 = ctypes.POINTER(ctypes.c_int32)
 
 
@@ -69,10 +78,10 @@ def load():
                       "`python -m sliding_window_attention_block_amd.build`")
     lib = ctypes.CDLL(LIB_PATH)
     lib.bsattn_build_summaries.argtypes = [_pshape, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _i32,
-                                           _vp, _vp, _i32, _vp]
+                                           _vp, _vp, _i32, _ppaged, _vp]
     lib.bsattn_build_summaries.restype = _st
     lib.bsattn_append_kv.argtypes = [_pshape, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _vp,
-                                     _vp, _i32, _vp]
+                                     _vp, _i32, _ppaged, _vp]
     lib.bsattn_append_kv.restype = _st
     lib.bsattn_select_topk.argtypes = [_pshape, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _i32, _i32,
                                        _i32, _i32, _i32, _pi32, _i32, _vp, _vp, _vp]
@@ -80,11 +89,11 @@ def load():
     lib.bsattn_decode_workspace_bytes.argtypes = [_pshape, _i32, _i32, _i32, _i32]
     lib.bsattn_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.bsattn_decode.argtypes = [_pshape, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _pi32, _i32,
-                                  _vp, _vp, _vp, ctypes.c_size_t, _vp]
+                                  _vp, _vp, _vp, ctypes.c_size_t, _ppaged, _vp]
     lib.bsattn_decode.restype = _st
     lib.bsattn_decode_step.argtypes = [_pshape, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32,
                                        _i32, _i32, _i32, _i32, _i32, _pi32, _i32, _vp, _vp, _vp, _vp,
-                                       _vp, ctypes.c_size_t, _vp]
+                                       _vp, ctypes.c_size_t, _ppaged, _vp]
     lib.bsattn_decode_step.restype = _st
     lib.bsattn_prefill.argtypes = [_pshape, _vp, _vp, _vp, _i32, _i32, _i32, _pi32, _i32,
                                    _vp, _vp, _vp, ctypes.c_size_t, _vp]

@@ -191,6 +191,24 @@ bsattn_status check_factor(int32_t rank, const void* factor, int32_t factor_dtyp
   return BSATTN_OK;
 }
 
+// Paged K/V layout (NULL: contiguous).
+bsattn_status paged_args(const bsattn_shape* s, const bsattn_paged_kv* p, bsattn::PagedKV& out) {
+  std::memset(&out, 0, sizeof(out));
+  if (p == nullptr) return BSATTN_OK;
+  if (p->block_table == nullptr || (reinterpret_cast<uintptr_t>(p->block_table) & 3u) != 0)
+    return fail(BSATTN_ERR_INVALID, "paged: block_table must be a non-NULL, 4-byte aligned device pointer");
+  if (p->page_tokens != 16 && p->page_tokens != 32 && p->page_tokens != 64)
+    return fail(BSATTN_ERR_INVALID, "paged: page_tokens %d must be 16, 32 or 64", p->page_tokens);
+  if (p->max_pages < 1 || p->n_pages < 1) return fail(BSATTN_ERR_INVALID, "paged: max_pages and n_pages must be >= 1");
+  if ((long long)p->max_pages * p->page_tokens != s->kv_capacity)
+    return fail(BSATTN_ERR_INVALID, "paged: kv_capacity must equal max_pages * page_tokens");
+  out.block_table = p->block_table;
+  out.page_shift = p->page_tokens == 16 ? 4 : (p->page_tokens == 32 ? 5 : 6);
+  out.max_pages = p->max_pages;
+  out.n_pages = p->n_pages;
+  return BSATTN_OK;
+}
+
 // Query-subspace basis: sub_dim 0 (none), or a multiple of 32 in [32, d] with rank >= 1.
 bsattn_status check_basis(const float* basis, int32_t sub_dim, int32_t rank, int32_t head_dim) {
   if (sub_dim == 0) return BSATTN_OK;
@@ -253,9 +271,15 @@ bsattn_status select_args(const bsattn_shape* shape, const void* Q, const void* 
 bsattn_status decode_args(const bsattn_shape* shape, const void* Q, const void* K, const void* V,
                           const int32_t* sel, int32_t top_k, int32_t window, int32_t n_sink,
                           const int32_t* global_pos_host, int32_t n_global, float* O, float* lse,
-                          void* workspace, size_t ws_bytes, bsattn::DecodeArgs& a) {
+                          void* workspace, size_t ws_bytes, const bsattn_paged_kv* paged,
+                          bsattn::DecodeArgs& a) {
   bsattn_status st = check_shape(shape, true);
   if (st != BSATTN_OK) return st;
+  bsattn::PagedKV pk;
+  st = paged_args(shape, paged, pk);
+  if (st != BSATTN_OK) return st;
+  if (paged != nullptr && shape->dtype != BSATTN_BF16)
+    return fail(BSATTN_ERR_UNSUPPORTED, "paged: the sparse decode reads paged caches in BF16 only");
   if (Q == nullptr || K == nullptr || V == nullptr || sel == nullptr || O == nullptr)
     return fail(BSATTN_ERR_INVALID, "Q, K, V, sel and O must be non-NULL");
   if (top_k < 1 || top_k > BSATTN_MAX_TOP_K) return fail(BSATTN_ERR_INVALID, "top_k must be in [1, %d]", BSATTN_MAX_TOP_K);
@@ -289,6 +313,7 @@ bsattn_status decode_args(const bsattn_shape* shape, const void* Q, const void* 
   a.top_k = top_k;
   a.scale = effective_scale(shape);
   a.bf16 = shape->dtype == BSATTN_BF16;
+  a.paged = pk;
   return BSATTN_OK;
 }
 
@@ -320,7 +345,7 @@ namespace {
 bsattn_status summaries_args(const bsattn_shape* shape, const void* K, int32_t rank, int32_t first_block,
                              int32_t n_blocks, int32_t nblk_capacity, void* mean, int32_t mean_dtype, void* factor,
                              int32_t factor_dtype, float* factor_scale, const float* basis, int32_t sub_dim,
-                             bsattn::SummaryArgs& a) {
+                             const bsattn_paged_kv* paged, bsattn::SummaryArgs& a) {
   bsattn_status st = check_shape(shape, false);
   if (st != BSATTN_OK) return st;
   if (K == nullptr || mean == nullptr) return fail(BSATTN_ERR_INVALID, "K and mean must be non-NULL");
@@ -354,7 +379,7 @@ bsattn_status summaries_args(const bsattn_shape* shape, const void* K, int32_t r
   a.factor_scale = factor_scale;
   a.basis = sub_dim > 0 ? basis : nullptr;
   a.sub_dim = sub_dim;
-  return BSATTN_OK;
+  return paged_args(shape, paged, a.paged);
 }
 
 }  // namespace
@@ -365,11 +390,11 @@ bsattn_status bsattn_build_summaries(const bsattn_shape* shape, const void* K, i
                                      int32_t first_block, int32_t n_blocks, int32_t nblk_capacity,
                                      void* mean, int32_t mean_dtype, void* factor, int32_t factor_dtype,
                                      float* factor_scale, const float* basis, int32_t sub_dim,
-                                     void* hip_stream) {
+                                     const bsattn_paged_kv* paged, void* hip_stream) {
   g_err[0] = 0;
   bsattn::SummaryArgs a;
   const bsattn_status st = summaries_args(shape, K, rank, first_block, n_blocks, nblk_capacity, mean, mean_dtype,
-                                          factor, factor_dtype, factor_scale, basis, sub_dim, a);
+                                          factor, factor_dtype, factor_scale, basis, sub_dim, paged, a);
   if (st != BSATTN_OK) return st;
   if (n_blocks == 0) return BSATTN_OK;
   hipError_t e = bsattn::launch_summaries(a, (hipStream_t)hip_stream);
@@ -380,9 +405,12 @@ bsattn_status bsattn_build_summaries(const bsattn_shape* shape, const void* K, i
 bsattn_status bsattn_append_kv(const bsattn_shape* shape, const void* K_new, const void* V_new, void* K, void* V,
                                int32_t rank, int32_t nblk_capacity, void* mean, int32_t mean_dtype, void* factor,
                                int32_t factor_dtype, float* factor_scale, const float* basis, int32_t sub_dim,
-                               void* hip_stream) {
+                               const bsattn_paged_kv* paged, void* hip_stream) {
   g_err[0] = 0;
   bsattn_status st = check_shape(shape, false);
+  if (st != BSATTN_OK) return st;
+  bsattn::PagedKV pk;
+  st = paged_args(shape, paged, pk);
   if (st != BSATTN_OK) return st;
   if (K_new == nullptr || V_new == nullptr || K == nullptr || V == nullptr)
     return fail(BSATTN_ERR_INVALID, "K_new, V_new, K and V must be non-NULL");
@@ -393,7 +421,7 @@ bsattn_status bsattn_append_kv(const bsattn_shape* shape, const void* K_new, con
   bsattn::SummaryArgs sa;
   if (completes) {
     st = summaries_args(shape, K, rank, shape->n_ctx / shape->block_size - 1, 1, nblk_capacity, mean, mean_dtype,
-                        factor, factor_dtype, factor_scale, basis, sub_dim, sa);
+                        factor, factor_dtype, factor_scale, basis, sub_dim, paged, sa);
     if (st != BSATTN_OK) return st;
   }
   bsattn::AppendArgs aa;
@@ -401,6 +429,8 @@ bsattn_status bsattn_append_kv(const bsattn_shape* shape, const void* K_new, con
   aa.kv_capacity = shape->kv_capacity;
   aa.pos = shape->n_ctx - 1;
   aa.row_bytes = shape->head_dim * (shape->dtype == BSATTN_BF16 ? 2 : 4);
+  aa.n_kv_heads = shape->n_kv_heads;
+  aa.paged = pk;
   hipError_t e = bsattn::launch_append(aa, shape->batch * shape->n_kv_heads, (hipStream_t)hip_stream);
   if (e != hipSuccess) return fail(BSATTN_ERR_HIP, "append launch: %s", hipGetErrorString(e));
   if (completes) {
@@ -441,11 +471,11 @@ size_t bsattn_decode_workspace_bytes(const bsattn_shape* shape, int32_t top_k, i
 bsattn_status bsattn_decode(const bsattn_shape* shape, const void* Q, const void* K, const void* V,
                             const int32_t* sel, int32_t top_k, int32_t window, int32_t n_sink,
                             const int32_t* global_pos_host, int32_t n_global, float* O, float* lse,
-                            void* workspace, size_t ws_bytes, void* hip_stream) {
+                            void* workspace, size_t ws_bytes, const bsattn_paged_kv* paged, void* hip_stream) {
   g_err[0] = 0;
   bsattn::DecodeArgs a;
   const bsattn_status st = decode_args(shape, Q, K, V, sel, top_k, window, n_sink, global_pos_host, n_global,
-                                       O, lse, workspace, ws_bytes, a);
+                                       O, lse, workspace, ws_bytes, paged, a);
   if (st != BSATTN_OK) return st;
   hipError_t e = bsattn::launch_decode(a, (hipStream_t)hip_stream);
   if (e != hipSuccess) return fail(BSATTN_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
@@ -458,7 +488,8 @@ bsattn_status bsattn_decode_step(const bsattn_shape* shape, const void* Q, const
                                  int32_t sub_dim, int32_t rank, int32_t nblk_capacity,
                                  int32_t top_k, int32_t window, int32_t n_sink, const int32_t* global_pos_host,
                                  int32_t n_global, int32_t* sel, float* scores, float* O, float* lse,
-                                 void* workspace, size_t ws_bytes, void* hip_stream) {
+                                 void* workspace, size_t ws_bytes, const bsattn_paged_kv* paged,
+                                 void* hip_stream) {
   g_err[0] = 0;
   bsattn::SelectArgs sa;
   bsattn_status st = select_args(shape, Q, mean, mean_dtype, factor, factor_dtype, factor_scale, basis, sub_dim,
@@ -468,7 +499,7 @@ bsattn_status bsattn_decode_step(const bsattn_shape* shape, const void* Q, const
   if (st != BSATTN_OK) return st;
   bsattn::DecodeArgs da;
   st = decode_args(shape, Q, K, V, sel, top_k, window, n_sink, global_pos_host, n_global, O, lse, workspace,
-                   ws_bytes, da);
+                   ws_bytes, paged, da);
   if (st != BSATTN_OK) return st;
   // bf16 with at most 512 complete blocks and top_k <= 256: the decode waves
   // select; otherwise the top-k kernel does, then the decode reads sel

@@ -291,6 +291,37 @@ __device__ __forceinline__ void load_half(const uint16_t* Kb, const uint16_t* Vb
   }
 }
 
+// load_half for a paged cache: the item's block has its 64 / P pages p0 .. p3
+// (P = 1 << page_shift >= 16, so a 16-row K group or a V chunk never straddles
+// two pages); each lane takes the page of its own (clamped) row.
+template <int D>
+__device__ __forceinline__ void load_half_paged(const DecodeArgs& a, int g, int p0, int p1, int p2, int p3,
+                                                int tok0, int last, Stage<D>& st) {
+  using H = HalfItem<D>;
+  const int lane = threadIdx.x & 63, h = lane & 15, grp = lane >> 4;
+  const int sh = a.paged.page_shift;
+  auto row_of = [&](int t) __attribute__((always_inline)) {
+    const int s = (t & (kBlock - 1)) >> sh;
+    const int page = s == 0 ? p0 : (s == 1 ? p1 : (s == 2 ? p2 : p3));
+    return (((size_t)page * a.n_kv_heads + g) << sh) + (t & ((1 << sh) - 1));
+  };
+  const uint16_t* K = reinterpret_cast<const uint16_t*>(a.K);
+  const uint16_t* V = reinterpret_cast<const uint16_t*>(a.V);
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const size_t row = row_of(min(tok0 + 16 * tt + h, last));
+#pragma unroll
+    for (int dc = 0; dc < H::DC; ++dc)
+      st.k[tt][dc] = *reinterpret_cast<const u32x4*>(K + row * D + 32 * dc + 8 * grp);
+  }
+#pragma unroll
+  for (int i = 0; i < H::NCH; ++i) {
+    const int off = 1024 * i + 16 * lane;
+    const size_t row = row_of(min(tok0 + off / H::RB, last));
+    st.v[i] = *reinterpret_cast<const u32x4*>(V + row * D + (off % H::RB) / 2);
+  }
+}
+
 // Online-softmax update of one half item whose K and V registers have landed.
 template <int D>
 __device__ __forceinline__ void compute_half(const Stage<D>& st, uint8_t* vt, const u32x4* qop, float sl2,
@@ -369,8 +400,9 @@ __device__ __forceinline__ void compute_half(const Stage<D>& st, uint8_t* vt, co
 // d = 128: two stages of K and V take 128 registers, so a wave gets the whole
 // 512-register budget of a SIMD (one workgroup of 4 waves per CU); d = 64 fits
 // two workgroups per CU.  PL > 0: fused step, PL scores per lane for the
-// in-wave top-k; PL = 0: the selection comes from `sel`.
-template <int D, int PL>
+// in-wave top-k; PL = 0: the selection comes from `sel`.  PAGED: K and V are
+// page pools read through the block table.
+template <int D, int PL, bool PAGED>
 __global__ __launch_bounds__(64 * kW, D == 128 ? 1 : 2) void decode_bf16_kernel(DecodeArgs args) {
   // The arguments are read in place from the kernel-argument segment (the
   // only explicit argument sits at its offset 0): per-lane lookups into the
@@ -429,6 +461,20 @@ __global__ __launch_bounds__(64 * kW, D == 128 ? 1 : 2) void decode_bf16_kernel(
   };
   if constexpr (PL == 0) selected_entries(a.sel + (size_t)pair * a.top_k);
   uint32_t mlo = (uint32_t)maskv, mhi = (uint32_t)(maskv >> 32);
+  // paged K/V: the pages of lane j's item block (64 / P of them), physical numbers
+  int pgv[4] = {0, 0, 0, 0};
+  auto item_pages = [&]() __attribute__((always_inline)) {
+    if constexpr (PAGED) {
+      const int spb = kBlock >> a.paged.page_shift;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        if (s < spb) {
+          const int p = a.paged.block_table[(size_t)b * a.paged.max_pages + min(blkv * spb + s, a.paged.max_pages - 1)];
+          pgv[s] = min(max(p, 0), a.paged.n_pages - 1);
+        }
+    }
+  };
+  item_pages();
 
   // Q^T operand: lane (h, grp) holds Q[h][32dc + 8grp .. +8] (zero rows past G)
   u32x4 qop[DC];
@@ -461,7 +507,12 @@ __global__ __launch_bounds__(64 * kW, D == 128 ? 1 : 2) void decode_bf16_kernel(
     }
     const int blk = __builtin_amdgcn_readlane(blkv, j);
     st.hmask = odd ? __builtin_amdgcn_readlane(mhi, j) : __builtin_amdgcn_readlane(mlo, j);
-    load_half<D>(Kb, Vb, blk * kBlock + 32 * odd, last, st);
+    if constexpr (PAGED)
+      load_half_paged<D>(a, g, __builtin_amdgcn_readlane(pgv[0], j), __builtin_amdgcn_readlane(pgv[1], j),
+                         __builtin_amdgcn_readlane(pgv[2], j), __builtin_amdgcn_readlane(pgv[3], j),
+                         blk * kBlock + 32 * odd, last, st);
+    else
+      load_half<D>(Kb, Vb, blk * kBlock + 32 * odd, last, st);
   };
   auto comp = [&](const Stage<D>& st) {
     if (st.hmask) compute_half<D>(st, vt, qop, sl2, m_run, l_run, oacc);
@@ -478,6 +529,7 @@ __global__ __launch_bounds__(64 * kW, D == 128 ? 1 : 2) void decode_bf16_kernel(
       selected_entries(tab);
       mlo = (uint32_t)maskv;
       mhi = (uint32_t)(maskv >> 32);
+      item_pages();
     }
   };
   // the first two loads, with the selection after them when both are forced
@@ -712,8 +764,13 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   if (a.bf16) {
     const long long waves = (long long)n_pairs * a.n_part;
     const dim3 grid((unsigned)((waves + kW - 1) / kW)), block(64 * kW);
-    if (a.key_slots == 0) hipLaunchKernelGGL((decode_bf16_kernel<D, 0>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((decode_bf16_kernel<D, 8>), grid, block, 0, stream, a);
+    if (a.paged.block_table != nullptr) {
+      if (a.key_slots == 0) hipLaunchKernelGGL((decode_bf16_kernel<D, 0, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((decode_bf16_kernel<D, 8, true>), grid, block, 0, stream, a);
+    } else {
+      if (a.key_slots == 0) hipLaunchKernelGGL((decode_bf16_kernel<D, 0, false>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((decode_bf16_kernel<D, 8, false>), grid, block, 0, stream, a);
+    }
   } else {
     const dim3 grid(a.n_part, n_pairs);
     if (G <= 4)

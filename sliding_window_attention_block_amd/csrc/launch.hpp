@@ -10,6 +10,23 @@
 
 namespace bsattn {
 
+// Paged K/V (block_table non-null): token t of (b, g) is row t % P of page
+// block_table[b * max_pages + t / P] in pools [n_pages, Hkv, P, d], P = 1 << page_shift
+// (16, 32 or 64 tokens).  Page numbers are clamped to [0, n_pages).
+struct PagedKV {
+  const int32_t* block_table;
+  int32_t page_shift;
+  int32_t max_pages;
+  int32_t n_pages;
+};
+
+// Row of token t of (b, g) in its K or V pool (or the contiguous cache row).
+__host__ __device__ inline size_t paged_row(const PagedKV& p, int b, int g, int n_kv_heads, int t) {
+  int page = p.block_table[(size_t)b * p.max_pages + (t >> p.page_shift)];
+  page = page < 0 ? 0 : (page >= p.n_pages ? p.n_pages - 1 : page);
+  return (((size_t)page * n_kv_heads + g) << p.page_shift) + (t & ((1 << p.page_shift) - 1));
+}
+
 struct SummaryArgs {
   const void* K;
   void* mean;       // fp32, or bf16 when mean_bf16
@@ -28,6 +45,7 @@ struct SummaryArgs {
   bool bf16;
   bool mean_bf16;  // store the block mean in bfloat16 (round to nearest even)
   bool factor_fp4;  // store factor rows as FP4 E2M1 codes with a float32 scale per row
+  PagedKV paged;
 };
 hipError_t launch_summaries(const SummaryArgs& a, hipStream_t stream);
 
@@ -40,6 +58,8 @@ struct AppendArgs {
   int32_t kv_capacity;
   int32_t pos;
   int32_t row_bytes;  // d * element size (a multiple of 16)
+  int32_t n_kv_heads;
+  PagedKV paged;
 };
 hipError_t launch_append(const AppendArgs& a, int n_pairs, hipStream_t stream);
 
@@ -114,6 +134,7 @@ struct DecodeArgs {
   bool bf16;
   ForcedSet forced;
   ForcedBlocks fblocks;
+  PagedKV paged;  // bf16 only
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 // Split geometry of the decode launch (also sizes the workspace).  bf16: at most

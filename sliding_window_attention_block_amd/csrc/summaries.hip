@@ -14,9 +14,22 @@
 namespace bsattn {
 namespace {
 
+// 16-byte chunk c (row c / CH, chunk c % CH of it) of block blk of pair bh's keys:
+// contiguous [B*Hkv, kv_capacity, d], or through the block table of a paged cache.
+template <int D, bool BF16>
+__device__ __forceinline__ const void* key_chunk(const SummaryArgs& a, int bh, int blk, int c) {
+  constexpr int CH = D / (BF16 ? 8 : 4);
+  constexpr size_t RB = D * (BF16 ? 2 : 4);
+  const int t = blk * kBlock + c / CH;
+  const size_t row = a.paged.block_table != nullptr
+                         ? paged_row(a.paged, bh / a.n_kv_heads, bh % a.n_kv_heads, a.n_kv_heads, t)
+                         : (size_t)bh * a.kv_capacity + t;
+  return reinterpret_cast<const char*>(a.K) + row * RB + (c % CH) * 16;
+}
+
 template <bool BF16>
-__device__ __forceinline__ void load_chunk(const void* base, size_t chunk, float* out) {
-  const uint4 v = reinterpret_cast<const uint4*>(base)[chunk];
+__device__ __forceinline__ void load_chunk(const void* p, float* out) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
   if constexpr (BF16) {
     out[0] = bf16lo(v.x); out[1] = bf16hi(v.x); out[2] = bf16lo(v.y); out[3] = bf16hi(v.y);
     out[4] = bf16lo(v.z); out[5] = bf16hi(v.z); out[6] = bf16lo(v.w); out[7] = bf16hi(v.w);
@@ -37,16 +50,13 @@ __global__ __launch_bounds__(256) void summaries_mean_kernel(SummaryArgs a) {
   const int tid = threadIdx.x;
   const int blk = a.first_block + blockIdx.x;
   const int bh = blockIdx.y;
-  const size_t elem = BF16 ? 2 : 4;
-  const char* base = reinterpret_cast<const char*>(a.K) +
-                     ((size_t)bh * a.kv_capacity + (size_t)blk * kBlock) * D * elem;
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     float v[E];
-    load_chunk<BF16>(base, tid + 256 * k, v);
+    load_chunk<BF16>(key_chunk<D, BF16>(a, bh, blk, tid + 256 * k), v);
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] += v[e];
   }
@@ -104,9 +114,6 @@ __global__ __launch_bounds__(256) void summaries_factor_kernel(SummaryArgs a) {
   const int lane = tid & 63, wid = tid >> 6;
   const int blk = a.first_block + blockIdx.x;
   const int bh = blockIdx.y;
-  const size_t elem = BF16 ? 2 : 4;
-  const char* base = reinterpret_cast<const char*>(a.K) +
-                     ((size_t)bh * a.kv_capacity + (size_t)blk * kBlock) * D * elem;
 
   // 1. block -> LDS, transposed
 #pragma unroll
@@ -114,7 +121,7 @@ __global__ __launch_bounds__(256) void summaries_factor_kernel(SummaryArgs a) {
     const int c = tid + 256 * k;
     const int row = c / CH, col0 = (c % CH) * E;
     float v[E];
-    load_chunk<BF16>(base, c, v);
+    load_chunk<BF16>(key_chunk<D, BF16>(a, bh, blk, c), v);
 #pragma unroll
     for (int e = 0; e < E; ++e) Ct[(col0 + e) * kCtStride + row] = v[e];
   }
@@ -334,7 +341,10 @@ __global__ __launch_bounds__(64) void append_kv_kernel(AppendArgs a) {
   const int n16 = a.row_bytes / 16;
   const uint4* ks = reinterpret_cast<const uint4*>(static_cast<const char*>(a.K_new) + bh * a.row_bytes);
   const uint4* vs = reinterpret_cast<const uint4*>(static_cast<const char*>(a.V_new) + bh * a.row_bytes);
-  const size_t dst = (bh * a.kv_capacity + a.pos) * (size_t)a.row_bytes;
+  const size_t row = a.paged.block_table != nullptr
+                         ? paged_row(a.paged, (int)bh / a.n_kv_heads, (int)bh % a.n_kv_heads, a.n_kv_heads, a.pos)
+                         : bh * a.kv_capacity + a.pos;
+  const size_t dst = row * (size_t)a.row_bytes;
   uint4* kd = reinterpret_cast<uint4*>(static_cast<char*>(a.K) + dst);
   uint4* vd = reinterpret_cast<uint4*>(static_cast<char*>(a.V) + dst);
   for (int i = threadIdx.x; i < n16; i += 64) {

@@ -32,8 +32,30 @@ def as_f64(arr):
     return (bf16_bits_to_f32(arr) if arr.dtype == np.uint16 else np.asarray(arr, np.float32)).astype(np.float64)
 
 
+def paged_pools(K, V, page_tokens, seed, spare=5):
+    """Scatter contiguous caches K, V [B, Hkv, cap, d] (device tensors, cap a multiple
+    of page_tokens) into page pools [n_pages, Hkv, P, d] under a random assignment of
+    distinct pages; pages no token maps to hold NaN.  Returns Kp, Vp, the int32 block
+    table [B, cap / P] and n_pages."""
+    torch = torch_mod()
+    B, Hkv, cap, d = K.shape
+    P = page_tokens
+    mp = cap // P
+    n_pages = B * mp + spare
+    perm = np.random.default_rng(seed).permutation(n_pages)[:B * mp].reshape(B, mp)
+    table = torch.from_numpy(perm.astype(np.int32)).cuda()
+    idx = torch.from_numpy(perm.reshape(-1)).cuda().long()
+    out = []
+    for X in (K, V):
+        pool = torch.full((n_pages, Hkv, P, d), float("nan"), dtype=X.dtype, device="cuda")
+        pool[idx] = X.reshape(B, Hkv, mp, P, d).permute(0, 2, 1, 3, 4).reshape(B * mp, Hkv, P, d)
+        out.append(pool)
+    return out[0], out[1], table, n_pages
+
+
 def gpu_decode_step(api, x, w, kv_capacity=None, nblk_capacity=None, global_pos=(), dev=None,
-                    one_call=False, mean_dtype="f32", factor_fp4=False, basis=None):
+                    one_call=False, mean_dtype="f32", factor_fp4=False, basis=None, page_tokens=None,
+                    page_seed=0):
     """Run summaries -> select/top-k -> decode on the GPU through the binding.
 
     ``x`` holds Q, K, V numpy arrays (float32 or bf16 bits) of workload ``w``.
@@ -42,6 +64,7 @@ def gpu_decode_step(api, x, w, kv_capacity=None, nblk_capacity=None, global_pos=
     stores the block means in bfloat16; ``factor_fp4`` the factor rows as FP4 codes
     (returned as ``factor`` uint8 codes plus ``factor_scale``).  ``basis`` [Hkv, s, d]
     (numpy float32) projects the factor rows onto each K/V head's query subspace.
+    ``page_tokens`` runs every call on page pools (``paged_pools``) through a block table.
     Returns numpy copies of mean (as float32), factor, scores, sel, O, lse.
     """
     torch = torch_mod()
@@ -54,6 +77,10 @@ def gpu_decode_step(api, x, w, kv_capacity=None, nblk_capacity=None, global_pos=
     K = dev["K"] if "K" in dev else to_dev(x["K"])
     V = dev["V"] if "V" in dev else to_dev(x["V"])
     shape = api.make_shape(B, Hq, Hkv, d, n, kv_capacity=cap, dtype=w.dtype)
+    pg = None
+    if page_tokens is not None:
+        K, V, table, n_pages = paged_pools(K, V, page_tokens, page_seed)
+        pg = api.paged_kv(table, page_tokens, n_pages)
     mean = torch.full((B, Hkv, max(nbcap, 1), d), float("nan"), device="cuda",
                       dtype=torch.bfloat16 if mean_dtype == "bf16" else torch.float32)
     factor = fscale = bdev = None
@@ -66,7 +93,7 @@ def gpu_decode_step(api, x, w, kv_capacity=None, nblk_capacity=None, global_pos=
     elif w.rank > 0:
         factor = torch.full((B, Hkv, max(nbcap, 1), w.rank, e), float("nan"), device="cuda")
     api.bsattn_build_summaries(shape, K, w.rank, 0, nb, max(nbcap, 1), mean, factor, factor_scale=fscale,
-                               basis=bdev)
+                               basis=bdev, paged=pg)
     scores = torch.full((B, Hkv, max(nbcap, 1)), float("nan"), device="cuda")
     sel = torch.full((B, Hkv, w.top_k), -7, dtype=torch.int32, device="cuda")
     O = torch.full((B, Hq, d), float("nan"), device="cuda")
@@ -76,11 +103,11 @@ def gpu_decode_step(api, x, w, kv_capacity=None, nblk_capacity=None, global_pos=
     ws = torch.full((nbytes,), 255, dtype=torch.uint8, device="cuda")  # garbage contents
     if one_call:
         api.bsattn_decode_step(shape, Q, K, V, mean, factor, w.rank, max(nbcap, 1), w.top_k, w.window,
-                               w.n_sink, gp, sel, scores, O, lse, ws, factor_scale=fscale, basis=bdev)
+                               w.n_sink, gp, sel, scores, O, lse, ws, factor_scale=fscale, basis=bdev, paged=pg)
     else:
         api.bsattn_select_topk(shape, Q, mean, factor, w.rank, max(nbcap, 1), w.top_k, w.window,
                                w.n_sink, gp, sel, scores, factor_scale=fscale, basis=bdev)
-        api.bsattn_decode(shape, Q, K, V, sel, w.top_k, w.window, w.n_sink, gp, O, lse, ws)
+        api.bsattn_decode(shape, Q, K, V, sel, w.top_k, w.window, w.n_sink, gp, O, lse, ws, paged=pg)
     torch.cuda.synchronize()
     return dict(mean=mean.float().cpu().numpy(), factor=None if factor is None else factor.cpu().numpy(),
                 factor_scale=None if fscale is None else fscale.cpu().numpy(),

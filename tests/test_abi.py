@@ -92,22 +92,22 @@ G3 = (ctypes.c_int32 * 3)
 ])
 def test_decode_rejects_bad_shapes(shape_kw, code):
     st, msg = _status("bsattn_decode", _shape(**shape_kw), FAKE, FAKE, FAKE, FAKE, 4, 64, 0, None, 0,
-                      FAKE, None, FAKE, 1 << 30, None)
+                      FAKE, None, FAKE, 1 << 30, None, None)
     assert st == code and msg
 
 
 def test_decode_rejects_bad_arguments():
     s = _shape()
-    args = [s, FAKE, FAKE, FAKE, FAKE, 4, 64, 0, None, 0, FAKE, None, FAKE, 1 << 30, None]
+    args = [s, FAKE, FAKE, FAKE, FAKE, 4, 64, 0, None, 0, FAKE, None, FAKE, 1 << 30, None, None]
     st, _ = _status("bsattn_decode", *args[:1], None, *args[2:])
     assert st == 1
     st, _ = _status("bsattn_decode", *args[:5], 0, *args[6:])            # top_k 0
     assert st == 1
     st, _ = _status("bsattn_decode", *args[:6], -1, *args[7:])           # negative window
     assert st == 1
-    st, msg = _status("bsattn_decode", *args[:13], 16, None)             # workspace too small
+    st, msg = _status("bsattn_decode", *args[:13], 16, None, None)       # workspace too small
     assert st == 4 and "workspace" in msg
-    st, _ = _status("bsattn_decode", *args[:12], FAKE + 16, 1 << 30, None)  # misaligned workspace
+    st, _ = _status("bsattn_decode", *args[:12], FAKE + 16, 1 << 30, None, None)  # misaligned workspace
     assert st == 1
     st, _ = _status("bsattn_decode", s, FAKE + 4, *args[2:])             # misaligned Q
     assert st == 1
@@ -115,15 +115,15 @@ def test_decode_rejects_bad_arguments():
 
 STEP_ARGS = ("shape", "Q", "K", "V", "mean", "mean_dtype", "factor", "factor_dtype", "factor_scale",
              "basis", "sub_dim", "rank", "nblk", "top_k", "window", "n_sink", "gpos", "n_global", "sel", "scores", "O", "lse",
-             "ws", "ws_bytes", "stream")
+             "ws", "ws_bytes", "paged", "stream")
 SELECT_ARGS = ("shape", "Q", "mean", "mean_dtype", "factor", "factor_dtype", "factor_scale", "basis",
                "sub_dim", "rank", "nblk",
                "top_k", "window", "n_sink", "gpos", "n_global", "sel", "scores", "stream")
 SUMMARY_ARGS = ("shape", "K", "rank", "first_block", "n_blocks", "nblk", "mean", "mean_dtype", "factor",
-                "factor_dtype", "factor_scale", "basis", "sub_dim", "stream")
+                "factor_dtype", "factor_scale", "basis", "sub_dim", "paged", "stream")
 GOOD = dict(Q=FAKE, K=FAKE, V=FAKE, mean=FAKE, mean_dtype=0, factor=None, factor_dtype=0, factor_scale=None,
             basis=None, sub_dim=0, rank=0, nblk=4, top_k=2, window=64, n_sink=0, gpos=None, n_global=0, sel=FAKE, scores=FAKE,
-            O=FAKE, lse=None, ws=FAKE, ws_bytes=1 << 30, stream=None, first_block=0, n_blocks=4)
+            O=FAKE, lse=None, ws=FAKE, ws_bytes=1 << 30, paged=None, stream=None, first_block=0, n_blocks=4)
 
 
 def _call(fn, names, **over):
@@ -245,7 +245,7 @@ def test_binding_raises_with_the_library_message():
 
 
 APPEND_ARGS = ("shape", "K_new", "V_new", "K", "V", "rank", "nblk", "mean", "mean_dtype", "factor",
-               "factor_dtype", "factor_scale", "basis", "sub_dim", "stream")
+               "factor_dtype", "factor_scale", "basis", "sub_dim", "paged", "stream")
 
 
 def test_append_rejects_bad_arguments():
@@ -260,3 +260,25 @@ def test_append_rejects_bad_arguments():
     assert _call(f, APPEND_ARGS, **kw, shape=_shape(n_ctx=256), rank=2)[0] == 1      # rank 2, no factor
     st, msg = _call(f, APPEND_ARGS, **kw, shape=_shape(n_ctx=256), basis=FAKE, sub_dim=48, **FP4)
     assert st == 1 and "sub_dim" in msg
+
+
+
+def _pg(page_tokens=16, max_pages=16, n_pages=40, table=FAKE):
+    return ctypes.byref(_lib.PagedKV(table, page_tokens, max_pages, n_pages))
+
+
+@pytest.mark.parametrize("f,names", [("bsattn_build_summaries", SUMMARY_ARGS), ("bsattn_append_kv", APPEND_ARGS),
+                                     ("bsattn_decode_step", STEP_ARGS)])
+def test_paged_layout_is_checked(f, names):
+    """page_tokens 16, 32 or 64; kv_capacity = max_pages * page_tokens; a non-NULL,
+    aligned block table; at least one page."""
+    kw = dict(K_new=FAKE, V_new=FAKE) if f == "bsattn_append_kv" else {}
+    for bad in (_pg(page_tokens=8, max_pages=32), _pg(page_tokens=48), _pg(max_pages=8),
+                _pg(table=None), _pg(table=FAKE + 2), _pg(n_pages=0)):
+        st, msg = _call(f, names, paged=bad, **kw)
+        assert st == 1 and "paged" in msg
+
+
+def test_paged_decode_takes_bf16_only():
+    st, msg = _call("bsattn_decode_step", STEP_ARGS, paged=_pg(), shape=_shape(dtype=0))
+    assert st == 2 and "BF16" in msg
