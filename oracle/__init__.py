@@ -50,3 +50,10 @@ from .decode import (  # noqa: F401
     sparse_decode_group,
     decode_step,
 )
+from .sparse_prefill import (  # noqa: F401
+    TILE as SPARSE_PREFILL_TILE,
+    tile_candidates,
+    sparse_prefill_selection,
+    sparse_prefill_allowed,
+    sparse_prefill,
+)
