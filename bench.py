@@ -282,6 +282,86 @@ def bench_decode(api, torch, w, x, steps, warmup, mean_dtype="bf16", factor_fp4=
 
 
 # ----------------------------------------------------------------------------- prefill
+def sparse_prefill_keys(sel, N, wl, ns, tile=128, S=64):
+    """Keys each row attends in the block-sparse prefill, from a selection
+    [n_tiles, k] (window, sinks before the window, selected keys before the window
+    and past the sinks: disjoint by construction)."""
+    i = np.arange(N)
+    cnt = np.minimum(i, wl) + 1 + np.maximum(0, np.minimum(np.minimum(ns, i + 1), i - wl))
+    lim = i - wl  # keys below the window
+    for t in range(sel.shape[0]):
+        r = slice(t * tile, min(N, (t + 1) * tile))
+        for j in sel[t]:
+            if j >= 0:
+                lo, hi = max(S * j, ns), np.minimum(S * j + S, lim[r])
+                cnt[r] += np.maximum(0, hi - lo)
+    return cnt
+
+
+def bench_sparse_prefill(api, torch, w, x, steps, warmup):
+    """One call chain of the block-sparse prefill on resident inputs: block means
+    (bsattn_build_summaries), tile selection (bsattn_select_prefill) and the sparse
+    attention (bsattn_sparse_prefill)."""
+    B, Hq, Hkv, N, d = w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len, w.head_dim
+    wl, ns, k = w.window_left, w.n_sink, w.top_k
+    shape = api.make_shape(B, Hq, Hkv, d, N, dtype="bf16")
+    nb, n_tiles = N // 64, (N + 127) // 128
+    io = (x["Q"].nbytes + x["K"].nbytes + x["V"].nbytes) + B * Hq * N * (d + 1) * 4
+    R = replicas_for(io)
+    reps = []
+    for r in range(R):
+        reps.append(dict(Q=to_dev(torch, x["Q"]), K=to_dev(torch, x["K"]), V=to_dev(torch, x["V"]),
+                         mean=torch.empty((B, Hkv, nb, d), dtype=torch.bfloat16, device="cuda"),
+                         scores=torch.empty((B, Hkv, n_tiles, nb), device="cuda"),
+                         sel=torch.empty((B, Hkv, n_tiles, k), dtype=torch.int32, device="cuda"),
+                         O=torch.empty((B, Hq, N, d), device="cuda"), lse=torch.empty((B, Hq, N), device="cuda")))
+
+    def summaries(rp):
+        api.bsattn_build_summaries(shape, rp["K"], 0, 0, nb, nb, rp["mean"])
+
+    def select(rp):
+        api.bsattn_select_prefill(shape, rp["Q"], rp["mean"], nb, k, wl, ns, rp["sel"], rp["scores"])
+
+    def attend(rp):
+        api.bsattn_sparse_prefill(shape, rp["Q"], rp["K"], rp["V"], rp["sel"], k, wl, ns, rp["O"], rp["lse"])
+
+    def step(rp):
+        summaries(rp)
+        select(rp)
+        attend(rp)
+
+    for i in range(warmup):
+        step(reps[i % R])
+    torch.cuda.synchronize()
+    sel_h = reps[0]["sel"].cpu().numpy()
+    keys = sum(int(sparse_prefill_keys(sel_h[b, g], N, wl, ns).sum()) * (Hq // Hkv)
+               for b in range(B) for g in range(Hkv))
+    flops = 4.0 * d * keys  # QK and PV over the attended (query, key) pairs
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(steps):
+            fn(reps[i % R])
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    step_ms = timed(step)
+    attend_ms = timed(attend)
+    select_ms = timed(select)
+    summ_ms = timed(summaries)
+    res = dict(workload=w.name, ms_per_call=step_ms, attend_ms=attend_ms, select_ms=select_ms,
+               summaries_ms=summ_ms, attended_pairs=keys, gflop=flops / 1e9,
+               tflops=flops / (step_ms * 1e-3) / 1e12, attend_tflops=flops / (attend_ms * 1e-3) / 1e12,
+               attend_frac_mfma=flops / (attend_ms * 1e-3) / BF16_PEAK, replicas=R,
+               window=wl + 1, sinks=ns, top_k=k)
+    del reps
+    torch.cuda.empty_cache()
+    return res
+
+
 def bench_prefill(api, torch, w, x, steps, warmup):
     B, Hq, Hkv, N, d = w.batch, w.n_q_heads, w.n_kv_heads, w.seq_len, w.head_dim
     shape = api.make_shape(B, Hq, Hkv, d, N, dtype="bf16")
@@ -377,7 +457,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", default=None,
                     help="run one workload only (first_order_decode_32k, cobs_decode_128k, "
-                         "swa_prefill_8k, local_global_prefill_16k); prints its result")
+                         "swa_prefill_8k, local_global_prefill_16k, sparse_prefill_8k); prints its result")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 512 MiB device-to-device copy three times (the "
@@ -405,7 +485,7 @@ def main():
         log(f"[bench] calibration copies done: 3 x {CALIB_BYTES} bytes")
         del src, dst
     names = [args.only] if args.only else [HEADLINE, "cobs_decode_128k", "swa_prefill_8k",
-                                            "local_global_prefill_16k"]
+                                            "local_global_prefill_16k", "sparse_prefill_8k"]
     results = {}
     inputs = {}
     for name in names:
@@ -426,6 +506,8 @@ def main():
                                                                   subspace=False)
                 results[name + "/fp32_factors"] = bench_decode(api, torch, w, x, args.steps, args.warmup,
                                                                factor_fp4=False)
+        elif w.top_k > 0:
+            results[name] = bench_sparse_prefill(api, torch, w, x, args.steps, args.warmup)
         else:
             results[name] = bench_prefill(api, torch, w, x, args.steps, args.warmup)
         log(f"[bench] {name}: {json.dumps(results[name])}")

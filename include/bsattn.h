@@ -272,6 +272,45 @@ bsattn_status bsattn_prefill(const bsattn_shape* shape, const void* Q, const voi
                              float* O, float* lse, void* workspace, size_t ws_bytes,
                              void* hip_stream);
 
+/*
+ * Block-sparse causal prefill, NSA-style block selection shared by a query
+ * tile [BLOG NSA data flow: coarse compression, then fine selection; COBS 2.1,
+ * 2.2, 2.3 (COBS builds on NSA's selection branch)].  Query tiles are the
+ * BSATTN_SPARSE_TILE consecutive rows [128 t, 128 t + 128) of a sequence.
+ *
+ * bsattn_select_prefill: for every (b, K/V head g, tile t) and complete block j,
+ *   scores[b,g,t,j] = ln sum over the tile's rows i and g's query heads h of
+ *                     exp(q~_{i,h} . mean_j),  q~ = scale * Q[b,h,i]
+ * (written for the tile's candidates; other entries are left undefined), and
+ * sel[b,g,t,:] = the top_k candidates by (score descending, index ascending),
+ * ascending, -1 padded.  Candidates of tile t: complete blocks j with
+ * 64 j < i_last - window_left (a key before the window of the tile's last row
+ * i_last) and 64 (j + 1) > n_sink (not wholly inside the sinks).
+ * Q [B, Hq, n_ctx, d] BF16; mean [B, Hkv, nblk_capacity, d] BF16 as built by
+ * bsattn_build_summaries (mean_dtype must be BSATTN_BF16); scores
+ * [B, Hkv, n_tiles, nblk_capacity] fp32; sel [B, Hkv, n_tiles, top_k] int32;
+ * n_tiles = ceil(n_ctx / 128).  top_k in [1, BSATTN_SPARSE_MAX_TOP_K];
+ * window_left >= 0; n_sink in [0, BSATTN_SPARSE_MAX_SINK].
+ *
+ * bsattn_sparse_prefill: row i of every query head attends, in one softmax,
+ * the union of its causal window [i - window_left, i], the sinks
+ * [0, min(n_sink, i + 1)) and the keys <= i of its tile's selected blocks
+ * (sel as written above; entries outside the complete blocks are ignored), a
+ * key reached twice counted once.  Q, K, V BF16 (K, V [B, Hkv, kv_capacity, d]);
+ * O [B, Hq, n_ctx, d] fp32, lse [B, Hq, n_ctx] fp32 (may be NULL).
+ */
+#define BSATTN_SPARSE_TILE 128
+#define BSATTN_SPARSE_MAX_TOP_K 256
+#define BSATTN_SPARSE_MAX_SINK 256
+bsattn_status bsattn_select_prefill(const bsattn_shape* shape, const void* Q, const void* mean,
+                                    int32_t mean_dtype, int32_t nblk_capacity, int32_t top_k,
+                                    int32_t window_left, int32_t n_sink, int32_t* sel, float* scores,
+                                    void* hip_stream);
+bsattn_status bsattn_sparse_prefill(const bsattn_shape* shape, const void* Q, const void* K,
+                                    const void* V, const int32_t* sel, int32_t top_k,
+                                    int32_t window_left, int32_t n_sink, float* O, float* lse,
+                                    void* hip_stream);
+
 /* Bytes of device workspace bsattn_prefill needs with n_global global positions
  * (0 when n_global == 0 or the arguments are invalid). */
 size_t bsattn_prefill_workspace_bytes(const bsattn_shape* shape, int32_t n_global);

@@ -14,6 +14,9 @@
 
 static_assert(bsattn::kMaxTopK == BSATTN_MAX_TOP_K, "device top-k limit matches the header");
 static_assert(bsattn::kMaxBlocks == BSATTN_MAX_BLOCKS, "device block limit matches the header");
+static_assert(bsattn::kSparseTile == BSATTN_SPARSE_TILE && bsattn::kSparseMaxTopK == BSATTN_SPARSE_MAX_TOP_K &&
+                  bsattn::kSparseMaxSink == BSATTN_SPARSE_MAX_SINK,
+              "block-sparse prefill limits match the header");
 
 namespace {
 
@@ -518,6 +521,87 @@ bsattn_status bsattn_decode_step(const bsattn_shape* shape, const void* Q, const
   if (e != hipSuccess) return fail(BSATTN_ERR_HIP, "select launch: %s", hipGetErrorString(e));
   e = bsattn::launch_decode(da, (hipStream_t)hip_stream);
   if (e != hipSuccess) return fail(BSATTN_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return BSATTN_OK;
+}
+
+bsattn_status bsattn_select_prefill(const bsattn_shape* shape, const void* Q, const void* mean,
+                                    int32_t mean_dtype, int32_t nblk_capacity, int32_t top_k,
+                                    int32_t window_left, int32_t n_sink, int32_t* sel, float* scores,
+                                    void* hip_stream) {
+  g_err[0] = 0;
+  bsattn_status st = check_shape(shape, false);
+  if (st != BSATTN_OK) return st;
+  if (shape->dtype != BSATTN_BF16 || mean_dtype != BSATTN_BF16)
+    return fail(BSATTN_ERR_UNSUPPORTED, "the prefill selection takes BF16 queries and BF16 means");
+  if (Q == nullptr || mean == nullptr || sel == nullptr || scores == nullptr)
+    return fail(BSATTN_ERR_INVALID, "Q, mean, sel and scores must be non-NULL");
+  if (!aligned16(Q) || !aligned16(mean)) return fail(BSATTN_ERR_INVALID, "device pointers must be 16-byte aligned");
+  if (top_k < 1 || top_k > BSATTN_SPARSE_MAX_TOP_K)
+    return fail(BSATTN_ERR_INVALID, "top_k must be in [1, %d]", BSATTN_SPARSE_MAX_TOP_K);
+  if (window_left < 0) return fail(BSATTN_ERR_INVALID, "window_left must be >= 0");
+  if (n_sink < 0 || n_sink > BSATTN_SPARSE_MAX_SINK)
+    return fail(BSATTN_ERR_INVALID, "n_sink must be in [0, %d]", BSATTN_SPARSE_MAX_SINK);
+  const int nb = shape->n_ctx / shape->block_size;
+  if (nb > BSATTN_MAX_BLOCKS) return fail(BSATTN_ERR_UNSUPPORTED, "more than %d complete blocks", BSATTN_MAX_BLOCKS);
+  if (nblk_capacity < nb) return fail(BSATTN_ERR_INVALID, "nblk_capacity < n_ctx / block_size");
+  bsattn::SelectArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.Q = Q; a.mean = mean; a.sel = sel; a.scores = scores;
+  a.batch = shape->batch; a.n_q_heads = shape->n_q_heads; a.n_kv_heads = shape->n_kv_heads;
+  a.head_dim = shape->head_dim;
+  a.n_blocks = nb;
+  a.nblk_capacity = nblk_capacity;
+  a.top_k = top_k;
+  a.scale = effective_scale(shape);
+  a.bf16 = true;
+  a.mean_bf16 = true;
+  a.tile_rows = bsattn::kSparseTile;
+  a.n_tiles = (shape->n_ctx + bsattn::kSparseTile - 1) / bsattn::kSparseTile;
+  a.seq_len = shape->n_ctx;
+  a.window_left = window_left;
+  a.n_sink = n_sink;
+  if ((long long)a.batch * a.n_kv_heads * a.n_tiles > 0x7fffffffLL)
+    return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");
+  hipError_t e = bsattn::launch_prefill_select(a, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return fail(BSATTN_ERR_HIP, "prefill selection launch: %s", hipGetErrorString(e));
+  return BSATTN_OK;
+}
+
+bsattn_status bsattn_sparse_prefill(const bsattn_shape* shape, const void* Q, const void* K, const void* V,
+                                    const int32_t* sel, int32_t top_k, int32_t window_left, int32_t n_sink,
+                                    float* O, float* lse, void* hip_stream) {
+  g_err[0] = 0;
+  bsattn_status st = check_shape(shape, false);
+  if (st != BSATTN_OK) return st;
+  if (shape->dtype != BSATTN_BF16) return fail(BSATTN_ERR_UNSUPPORTED, "the sparse prefill takes BF16 Q/K/V only");
+  if (Q == nullptr || K == nullptr || V == nullptr || O == nullptr || sel == nullptr)
+    return fail(BSATTN_ERR_INVALID, "Q, K, V, sel and O must be non-NULL");
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O))
+    return fail(BSATTN_ERR_INVALID, "device pointers must be 16-byte aligned");
+  if (top_k < 1 || top_k > BSATTN_SPARSE_MAX_TOP_K)
+    return fail(BSATTN_ERR_INVALID, "top_k must be in [1, %d]", BSATTN_SPARSE_MAX_TOP_K);
+  if (window_left < 0) return fail(BSATTN_ERR_INVALID, "window_left must be >= 0");
+  if (n_sink < 0 || n_sink > BSATTN_SPARSE_MAX_SINK)
+    return fail(BSATTN_ERR_INVALID, "n_sink must be in [0, %d]", BSATTN_SPARSE_MAX_SINK);
+  const long long n_qt = (shape->n_ctx + 127) / 128;
+  if (n_qt * shape->batch * shape->n_q_heads > 0x7fffffffLL) return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");
+  bsattn::PrefillArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.Q = Q; a.K = K; a.V = V; a.O = O; a.lse = lse;
+  a.batch = shape->batch; a.n_q_heads = shape->n_q_heads; a.n_kv_heads = shape->n_kv_heads;
+  a.head_dim = shape->head_dim;
+  a.seq_len = shape->n_ctx;
+  a.kv_capacity = shape->kv_capacity;
+  a.window_left = window_left;
+  a.window_right = 0;
+  a.causal = 1;
+  a.scale = effective_scale(shape);
+  a.sp_sel = sel;
+  a.sp_top_k = top_k;
+  a.sp_n_sink = n_sink;
+  a.sp_n_tiles = (int32_t)n_qt;
+  hipError_t e = bsattn::launch_prefill(a, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return fail(BSATTN_ERR_HIP, "sparse prefill launch: %s", hipGetErrorString(e));
   return BSATTN_OK;
 }
 

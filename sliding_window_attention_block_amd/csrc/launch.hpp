@@ -86,7 +86,16 @@ struct SelectArgs {
   bool scores_only;  // skip the top-k launch (the fused decode step selects)
   bool mean_bf16;    // the block means are bfloat16
   bool factor_fp4;   // the factor rows are FP4 E2M1 codes + row scales
+  // block-sparse prefill (tile_rows > 0): Q is [B, Hq, seq_len, d]; scores and
+  // sel hold one row per (b, K/V head, query tile of tile_rows rows); the
+  // candidates of tile t are the complete blocks j with 64 j before the window
+  // [i - window_left, i] of the tile's last row i, and not inside the sinks
+  int32_t tile_rows, n_tiles, seq_len, window_left, n_sink;
 };
+hipError_t launch_prefill_select(const SelectArgs& a, hipStream_t stream);
+constexpr int kSparseTile = 128;      // query rows per selection tile (the prefill workgroup)
+constexpr int kSparseMaxTopK = 256;   // selected blocks per tile
+constexpr int kSparseMaxSink = 256;   // sink tokens of the block-sparse prefill
 hipError_t launch_select_topk(const SelectArgs& a, hipStream_t stream);
 
 // Forced blocks of a decode step, in the order the decode kernel visits them:
@@ -162,6 +171,10 @@ struct PrefillArgs {
   float scale;
   int32_t n_global;
   int32_t gpos[256];
+  // block-sparse prefill (sp_sel non-null): the tile's selected blocks
+  // [B, Hkv, n_tiles, sp_top_k] and the first sp_n_sink keys join the causal band
+  const int32_t* sp_sel;
+  int32_t sp_top_k, sp_n_sink, sp_n_tiles;
   // global query rows: key range split over waves, partials in the workspace
   int32_t n_global_wg;        // workgroups (first in the grid) that run global rows
   int32_t g_splits;           // key ranges per global row

@@ -41,6 +41,7 @@ namespace bsattn {
 namespace {
 
 constexpr int BM = 128;        // query rows per band workgroup
+static_assert(BM == kSparseTile, "a block-sparse selection tile is one band workgroup's rows");
 constexpr int BN = 64;         // keys per LDS stage
 constexpr int kCompKeys = 256; // rows seeing fewer keys take the compensated PV product
 constexpr float kHeadroom = 8.f;  // log2 units a row max may grow before the rescale
@@ -239,13 +240,20 @@ __device__ __forceinline__ void stage(const uint8_t* kt, const uint8_t* vt, cons
   }
 }
 
-template <int D, bool LG>
+// SP: block-sparse causal prefill [NSA block selection; COBS 2.1]: ahead of its
+// causal band, a workgroup runs one 64-key stage per block its query tile
+// selected and per sink block; a key of such a stage is allowed for row i only
+// before i's window (keys in the window come from the band), and only below
+// n_sink for a sink block the tile did not select, so no key counts twice.
+template <int D, bool LG, bool SP = false>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   using T = Tile<D>;
   constexpr int LDS_BYTES = 4 * T::BYTES;  // K and V, double buffered
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
   __shared__ int gcols[256];
   __shared__ int s_ngcols;
+  __shared__ int xblk[kSparseMaxTopK + kSparseMaxSink / 64];  // 2 block + (selected)
+  __shared__ int s_nx;
 
   const int tid = threadIdx.x, lane = tid & 63;
   // wave-uniform (scalar registers): every tile flag derived from it is too, so
@@ -362,7 +370,38 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     __syncthreads();
   }
   const int ngc = LG ? __builtin_amdgcn_readfirstlane(s_ngcols) : 0;
-  const int n_stage = n_band + (ngc + BN - 1) / BN;
+  if (SP) {
+    if (tid == 0) {
+      // merge the tile's ascending selection (-1 padded; entries outside the
+      // complete blocks skipped) with the sink blocks 0 .. nsb - 1
+      const int32_t* sel = a.sp_sel + ((size_t)kvlin * a.sp_n_tiles + qt) * a.sp_top_k;
+      const int nsb = (a.sp_n_sink + BN - 1) / BN, nbc = N / BN;
+      int n = 0, i = 0, j = 0;
+      while (i < a.sp_top_k || j < nsb) {
+        int s = 0x7fffffff;
+        while (i < a.sp_top_k) {
+          s = sel[i];
+          if (s >= 0 && s < nbc) break;
+          s = 0x7fffffff;
+          ++i;
+        }
+        const int k = j < nsb ? j : 0x7fffffff;
+        if (s == 0x7fffffff && k == 0x7fffffff) break;
+        if (s <= k) {
+          xblk[n++] = 2 * s + 1;
+          ++i;
+          if (s == k) ++j;
+        } else {
+          xblk[n++] = 2 * k;
+          ++j;
+        }
+      }
+      s_nx = n;
+    }
+    __syncthreads();
+  }
+  const int nx = SP ? __builtin_amdgcn_readfirstlane(s_nx) : 0;  // extra stages, ahead of the band
+  const int n_stage = nx + n_band + (ngc + BN - 1) / BN;
 
   const uint16_t* Kb = reinterpret_cast<const uint16_t*>(a.K) + (size_t)(b * Hkv + g) * a.kv_capacity * D;
   const uint16_t* Vb = reinterpret_cast<const uint16_t*>(a.V) + (size_t)(b * Hkv + g) * a.kv_capacity * D;
@@ -392,6 +431,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
       min(band_keys(min(r0, N - 1)), band_keys(min(r0 + 31, N - 1))) < kCompKeys);
 
   auto row_pos = [&](int stg, int r) {
+    stg -= nx;
     if (stg < n_band) return min((t_lo + stg) * BN + r, N - 1);
     const int slot = (stg - n_band) * BN + r;
     return gcols[min(slot, ngc - 1)];
@@ -404,8 +444,15 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   // precomputed lane offsets; the sequence's last partial tile and the gathered
   // global columns compute each row's position
   auto issue_stage = [&](int stg, uint8_t* kt, uint8_t* vt) {
-    const int row0 = (t_lo + stg) * BN;
-    if (stg < n_band && row0 + BN <= N) dl.issue(Kb8, Vb8, row0, kt, vt, wid);
+    if (SP && stg < nx) {  // a selected block (complete) or a sink block (the last may be partial)
+      const int jb = (__builtin_amdgcn_readfirstlane(xblk[stg]) >> 1) * BN;
+      if (jb + BN <= N) dl.issue(Kb8, Vb8, jb, kt, vt, wid);
+      else dma_stage<D>(Kb, Vb, kt, vt, wid, 4, [&](int r) { return min(jb + r, N - 1); });
+      return;
+    }
+    const int bs = stg - nx;
+    const int row0 = (t_lo + bs) * BN;
+    if (bs < n_band && row0 + BN <= N) dl.issue(Kb8, Vb8, row0, kt, vt, wid);
     else dma_stage<D>(Kb, Vb, kt, vt, wid, 4, [&](int r) { return row_pos(stg, r); });
   };
   uint8_t* const buf0 = smem;
@@ -419,7 +466,24 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
       __syncthreads();  // every wave's copies landed; every wave is done with the other buffer
       if (stg + 1 < n_stage) issue_stage(stg + 1, kn, kn + T::BYTES);
       uint8_t* vt = kt + T::BYTES;
-      if (stg < n_band) {
+      if (SP && stg < nx) {
+        const int xb = __builtin_amdgcn_readfirstlane(xblk[stg]);
+        const int jb = (xb >> 1) * BN;
+        // keys before this row's window (and below n_sink for a sink-only block);
+        // the wave's first row allows the fewest
+        const int cap = (xb & 1) ? 0x7fffffff : a.sp_n_sink - 1;
+        const int hi = min(myrow - wl - 1, cap), hi0 = min(r0 - wl - 1, cap);
+        uint32_t am[2];
+        bool masked = false;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int j0 = jb + 32 * u;
+          am[u] = range_bits32(0, hi - j0);
+          masked |= j0 + 31 > hi0;
+        }
+        stage<D, 2, COMP>(kt, vt, qop, oacc, st, sl2, am, masked);
+      } else if (stg - nx < n_band) {
+        stg -= nx;
         const int jb = (t_lo + stg) * BN;
         uint64_t gbits = 0ull;
         if (LG) {
@@ -444,7 +508,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         }
         stage<D, 2, COMP>(kt, vt, qop, oacc, st, sl2, am, masked);
       } else {
-        const int s0 = (stg - n_band) * BN;
+        const int s0 = (stg - nx - n_band) * BN;
         const uint32_t am[2] = {range_bits32(0, ngc - 1 - s0), range_bits32(0, ngc - 1 - s0 - 32)};
         stage<D, 2, COMP>(kt, vt, qop, oacc, st, sl2, am, s0 + 64 > ngc);
       }
@@ -538,6 +602,10 @@ template <int D, bool LG>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
   const int n_qt = (a.seq_len + BM - 1) / BM;
   const int n_wg = (LG ? a.n_global_wg : 0) + n_qt * a.batch * a.n_q_heads;
+  if (!LG && a.sp_sel != nullptr) {
+    hipLaunchKernelGGL((prefill_kernel<D, false, true>), dim3(n_wg), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((prefill_kernel<D, LG>), dim3(n_wg), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !LG) return e;

@@ -580,13 +580,21 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
   uint32_t key[KPT];
   uint64_t cm = 0ull;  // bit t: block j0 + t is a candidate
   uint32_t kand = ~0u, kor = 0u;
+  // prefill tiles: blocks starting before the window of the tile's last row
+  int tile_klo = 0;
+  if (a.tile_rows > 0) {
+    const int t = bh % a.n_tiles;
+    tile_klo = max(0, min(a.seq_len, (t + 1) * a.tile_rows) - 1 - a.window_left);
+  }
 #pragma unroll
   for (int t = 0; t < KPT; ++t) {
     const int j = j0 + t;
     key[t] = 0u;
     if (j < j1) {
       key[t] = order_key(sc[j]);
-      if (forced_mask(a.forced, j) != ~0ull) {
+      const bool cand = a.tile_rows > 0 ? (j * kBlock < tile_klo && (j + 1) * kBlock > a.n_sink)
+                                        : forced_mask(a.forced, j) != ~0ull;
+      if (cand) {
         cm |= 1ull << t;
         kand &= key[t];
         kor |= key[t];
@@ -684,7 +692,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
 
 hipError_t launch_topk(const SelectArgs& a, hipStream_t stream) {
   const int per = (a.n_blocks + kTopkThreads - 1) / kTopkThreads;
-  const dim3 tg(a.batch * a.n_kv_heads), tb(kTopkThreads);
+  const dim3 tg(a.batch * a.n_kv_heads * (a.tile_rows > 0 ? a.n_tiles : 1)), tb(kTopkThreads);
   if (per <= 2) hipLaunchKernelGGL(topk_kernel<2>, tg, tb, 0, stream, a);
   else if (per <= 8) hipLaunchKernelGGL(topk_kernel<8>, tg, tb, 0, stream, a);
   else if (per <= 32) hipLaunchKernelGGL(topk_kernel<32>, tg, tb, 0, stream, a);
@@ -770,12 +778,100 @@ hipError_t launch_g(const SelectArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+// Block-sparse prefill selection [COBS 2.1, 2.2; NSA's block selection]: the
+// score of block j for query tile t of pair (b, g) is ln sum over the tile's
+// rows r and the group's heads h of exp(q~_{r,h} . mean_j), the log of the
+// tile's summed estimated mass.  One wave per (pair, tile, 16-block unit):
+// v_mfma_f32_16x16x32_bf16 with 16 (row, head) pairs of the tile as A and the
+// unit's 16 bf16 means as B (exact products, fp32 sums), a running
+// log-sum-exp per lane over its rows, then across the four lane groups.
+// Units past the tile's candidates are skipped (their scores are not written).
+template <int D>
+__global__ __launch_bounds__(256) void prefill_tile_scores_kernel(SelectArgs a) {
+  constexpr int KS = D / 32;
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gw = blockIdx.x * 4 + wid;
+  const int NB = a.n_blocks;
+  const int n_units = (NB + 15) / 16;
+  const int unit = gw % n_units, rest = gw / n_units;
+  const int t = rest % a.n_tiles, pair = rest / a.n_tiles;
+  if (pair >= a.batch * a.n_kv_heads) return;  // no barriers: waves are independent
+  const int N = a.seq_len;
+  const int i0 = t * a.tile_rows, rows = min(N, i0 + a.tile_rows) - i0;
+  const int klo = max(0, i0 + rows - 1 - a.window_left);
+  if (unit * 16 * kBlock >= klo) return;  // no candidate in this unit
+  const int col = lane & 15, kg = lane >> 4;
+  const int b = pair / a.n_kv_heads, g = pair % a.n_kv_heads;
+  const int G = a.n_q_heads / a.n_kv_heads;
+
+  // B operand: the unit's means, lane (block col, kg) holding dims 32 s + 8 kg .. +7
+  bf16x8 bm[KS];
+  {
+    const int j = min(unit * 16 + col, NB - 1);
+    const u32x4* mrow = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.mean) +
+                                                       ((size_t)pair * a.nblk_capacity + j) * D);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) bm[s] = __builtin_bit_cast(bf16x8, mrow[4 * s + kg]);
+  }
+  const uint16_t* Qg = reinterpret_cast<const uint16_t*>(a.Q) + ((size_t)b * a.n_q_heads + g * G) * N * D;
+  const float sl2 = a.scale * kLog2e;
+  float m = -INFINITY, l = 0.f;  // this lane's running max and sum (log2 domain)
+  const int n_pairs_rows = rows * G;  // (row, head) pairs p = r G + h
+  for (int p0 = 0; p0 < n_pairs_rows; p0 += 16) {
+    // A operand: pair p0 + (lane % 16), dims 32 s + 8 kg .. +7
+    const int p = min(p0 + col, n_pairs_rows - 1);
+    const uint16_t* qrow = Qg + ((size_t)(p % G) * N + i0 + p / G) * D;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const bf16x8 qa = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * kg));
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, bm[s], acc, 0, 0, 0);
+    }
+    // lane (col, kg) holds pairs p0 + 4 kg + i for block unit * 16 + col
+    float x[4], mx = m;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = p0 + 4 * kg + i < n_pairs_rows ? acc[i] * sl2 : -INFINITY;
+      mx = fmaxf(mx, x[i]);
+    }
+    if (mx > -INFINITY) {
+      l *= __builtin_amdgcn_exp2f(m - mx);  // m = -inf: l is 0
+#pragma unroll
+      for (int i = 0; i < 4; ++i) l += __builtin_amdgcn_exp2f(x[i] - mx);
+      m = mx;
+    }
+  }
+  // the four lane groups hold disjoint rows of the same block
+#pragma unroll
+  for (int o = 16; o <= 32; o <<= 1) {
+    const float mo = __shfl_xor(m, o), lo = __shfl_xor(l, o);
+    const float mn = fmaxf(m, mo);
+    l = (m == -INFINITY ? 0.f : l * __builtin_amdgcn_exp2f(m - mn)) +
+        (mo == -INFINITY ? 0.f : lo * __builtin_amdgcn_exp2f(mo - mn));
+    m = mn;
+  }
+  const int j = unit * 16 + col;
+  if (kg == 0 && j < NB)
+    a.scores[((size_t)pair * a.n_tiles + t) * a.nblk_capacity + j] = (m + __builtin_amdgcn_logf(l)) * kLn2;
+}
+
 hipError_t launch_select_topk(const SelectArgs& a, hipStream_t stream) {
   // every operand exact in bfloat16: the MFMA scorer
   if (a.bf16 && a.mean_bf16 && (a.rank == 0 || a.factor_fp4))
     return a.head_dim == 64 ? launch_mfma_r<64>(a, stream) : launch_mfma_r<128>(a, stream);
   if (a.head_dim == 64) return a.bf16 ? launch_g<64, true>(a, stream) : launch_g<64, false>(a, stream);
   return a.bf16 ? launch_g<128, true>(a, stream) : launch_g<128, false>(a, stream);
+}
+
+hipError_t launch_prefill_select(const SelectArgs& a, hipStream_t stream) {
+  if (a.n_blocks > 0) {
+    const long long waves = (long long)a.batch * a.n_kv_heads * a.n_tiles * ((a.n_blocks + 15) / 16);
+    const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+    if (a.head_dim == 64) hipLaunchKernelGGL(prefill_tile_scores_kernel<64>, grid, block, 0, stream, a);
+    else hipLaunchKernelGGL(prefill_tile_scores_kernel<128>, grid, block, 0, stream, a);
+  }
+  return launch_topk(a, stream);
 }
 
 }  // namespace bsattn

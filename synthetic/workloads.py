@@ -77,6 +77,8 @@ class PrefillWorkload:
     seed: int
     input_scale: float = 1.0
     global_pos: tuple = field(default_factory=tuple)
+    top_k: int = 0   # block-sparse prefill: blocks selected per 128-row query tile (0: none)
+    n_sink: int = 0
 
     def scaled(self, **kw):
         return dataclasses.replace(self, **kw)
@@ -93,6 +95,9 @@ WORKLOADS = {
         name="local_global_prefill_16k", batch=2, n_q_heads=12, n_kv_heads=12, head_dim=64,
         seq_len=16384, window_left=256, window_right=256, causal=False, seed=2,
         global_pos=tuple(range(0, 16384, 1024))),
+    "sparse_prefill_8k": PrefillWorkload(
+        name="sparse_prefill_8k", batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128, seq_len=8192,
+        window_left=1023, window_right=0, causal=True, seed=5, input_scale=0.5, top_k=16, n_sink=64),
     "first_order_decode_32k": DecodeWorkload(
         name="first_order_decode_32k", batch=16, n_q_heads=32, n_kv_heads=8, head_dim=128,
         n_ctx=32768, block_size=64, rank=0, top_k=16, window=512, n_sink=64, dtype="bf16",

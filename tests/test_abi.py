@@ -24,7 +24,7 @@ def _header_functions():
 def test_library_exports_every_declared_function():
     lib = api.library()
     declared = _header_functions()
-    assert len(declared) == 11
+    assert len(declared) == 13
     for name in declared:
         assert hasattr(lib, name), name
     assert set(declared) == set(_lib.EXPORTS)
@@ -282,3 +282,22 @@ def test_paged_layout_is_checked(f, names):
 def test_paged_decode_takes_bf16_only():
     st, msg = _call("bsattn_decode_step", STEP_ARGS, paged=_pg(), shape=_shape(dtype=0))
     assert st == 2 and "BF16" in msg
+
+
+def test_sparse_prefill_rejects_bad_arguments():
+    f, g = "bsattn_select_prefill", "bsattn_sparse_prefill"
+    sel_args = lambda **o: [o.get("shape", _shape()), o.get("Q", FAKE), o.get("mean", FAKE), o.get("md", 1),
+                            o.get("nblk", 4), o.get("k", 2), o.get("wl", 64), o.get("ns", 0), FAKE, FAKE, None]
+    assert _status(f, *sel_args(md=0))[0] == 2                        # fp32 means
+    assert _status(f, *sel_args(shape=_shape(dtype=0)))[0] == 2       # fp32 queries
+    assert _status(f, *sel_args(k=0))[0] == 1
+    assert _status(f, *sel_args(k=257))[0] == 1
+    assert _status(f, *sel_args(wl=-1))[0] == 1
+    assert _status(f, *sel_args(ns=300))[0] == 1
+    assert _status(f, *sel_args(nblk=3))[0] == 1
+    pre = lambda **o: [o.get("shape", _shape()), FAKE, FAKE, FAKE, o.get("sel", FAKE), o.get("k", 2),
+                       o.get("wl", 64), o.get("ns", 0), FAKE, None, None]
+    assert _status(g, *pre(shape=_shape(dtype=0)))[0] == 2
+    assert _status(g, *pre(sel=None))[0] == 1
+    assert _status(g, *pre(wl=-5))[0] == 1
+    assert _status(g, *pre(k=300))[0] == 1
