@@ -781,79 +781,110 @@ hipError_t launch_g(const SelectArgs& a, hipStream_t stream) {
 // Block-sparse prefill selection [COBS 2.1, 2.2; NSA's block selection]: the
 // score of block j for query tile t of pair (b, g) is ln sum over the tile's
 // rows r and the group's heads h of exp(q~_{r,h} . mean_j), the log of the
-// tile's summed estimated mass.  One wave per (pair, tile, 16-block unit):
-// v_mfma_f32_16x16x32_bf16 with 16 (row, head) pairs of the tile as A and the
-// unit's 16 bf16 means as B (exact products, fp32 sums), a running
-// log-sum-exp per lane over its rows, then across the four lane groups.
-// Units past the tile's candidates are skipped (their scores are not written).
+// tile's summed estimated mass.  One workgroup per (pair, tile, group of 4
+// 16-block units), its 4 waves taking every fourth 16-row slice of the tile's
+// (row, head) pairs: v_mfma_f32_16x16x32_bf16 with 16 pairs as A (each A load
+// serves the 4 units) and a unit's 16 bf16 means as B (exact products, fp32
+// sums), a running log-sum-exp per lane and unit, then across the four lane
+// groups and (through LDS, one barrier) the four waves.  Units past the
+// tile's candidates are skipped (their scores are not written).
+constexpr int kTileUnits = 4;
+
 template <int D>
 __global__ __launch_bounds__(256) void prefill_tile_scores_kernel(SelectArgs a) {
-  constexpr int KS = D / 32;
+  constexpr int KS = D / 32, U = kTileUnits;
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int gw = blockIdx.x * 4 + wid;
   const int NB = a.n_blocks;
-  const int n_units = (NB + 15) / 16;
-  const int unit = gw % n_units, rest = gw / n_units;
+  const int n_groups = (NB + 16 * U - 1) / (16 * U);
+  const int grp = blockIdx.x % n_groups, rest = blockIdx.x / n_groups;
   const int t = rest % a.n_tiles, pair = rest / a.n_tiles;
-  if (pair >= a.batch * a.n_kv_heads) return;  // no barriers: waves are independent
+  // every exit below depends on the workgroup's indices only (the barrier is reached by all or none)
+  if (pair >= a.batch * a.n_kv_heads) return;
   const int N = a.seq_len;
   const int i0 = t * a.tile_rows, rows = min(N, i0 + a.tile_rows) - i0;
   const int klo = max(0, i0 + rows - 1 - a.window_left);
-  if (unit * 16 * kBlock >= klo) return;  // no candidate in this unit
+  // units of this group holding a candidate (wave-uniform)
+  const int nu = min(U, max(0, (klo + 16 * kBlock - 1) / (16 * kBlock) - grp * U));
+  if (nu == 0) return;
   const int col = lane & 15, kg = lane >> 4;
   const int b = pair / a.n_kv_heads, g = pair % a.n_kv_heads;
   const int G = a.n_q_heads / a.n_kv_heads;
 
-  // B operand: the unit's means, lane (block col, kg) holding dims 32 s + 8 kg .. +7
-  bf16x8 bm[KS];
-  {
-    const int j = min(unit * 16 + col, NB - 1);
+  // B operands: unit v's means, lane (block col, kg) holding dims 32 s + 8 kg .. +7
+  bf16x8 bm[U][KS];
+#pragma unroll
+  for (int v = 0; v < U; ++v) {
+    const int j = min((grp * U + v) * 16 + col, NB - 1);
     const u32x4* mrow = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.mean) +
                                                        ((size_t)pair * a.nblk_capacity + j) * D);
 #pragma unroll
-    for (int s = 0; s < KS; ++s) bm[s] = __builtin_bit_cast(bf16x8, mrow[4 * s + kg]);
+    for (int s = 0; s < KS; ++s) bm[v][s] = __builtin_bit_cast(bf16x8, mrow[4 * s + kg]);
   }
   const uint16_t* Qg = reinterpret_cast<const uint16_t*>(a.Q) + ((size_t)b * a.n_q_heads + g * G) * N * D;
   const float sl2 = a.scale * kLog2e;
-  float m = -INFINITY, l = 0.f;  // this lane's running max and sum (log2 domain)
+  float m[U], l[U];  // per unit: this lane's running max and sum (log2 domain)
+#pragma unroll
+  for (int v = 0; v < U; ++v) { m[v] = -INFINITY; l[v] = 0.f; }
   const int n_pairs_rows = rows * G;  // (row, head) pairs p = r G + h
-  for (int p0 = 0; p0 < n_pairs_rows; p0 += 16) {
+  for (int p0 = 16 * wid; p0 < n_pairs_rows; p0 += 64) {
     // A operand: pair p0 + (lane % 16), dims 32 s + 8 kg .. +7
     const int p = min(p0 + col, n_pairs_rows - 1);
     const uint16_t* qrow = Qg + ((size_t)(p % G) * N + i0 + p / G) * D;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    bf16x8 qa[KS];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const bf16x8 qa = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * kg));
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, bm[s], acc, 0, 0, 0);
-    }
-    // lane (col, kg) holds pairs p0 + 4 kg + i for block unit * 16 + col
-    float x[4], mx = m;
+    for (int s = 0; s < KS; ++s) qa[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * kg));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] = p0 + 4 * kg + i < n_pairs_rows ? acc[i] * sl2 : -INFINITY;
-      mx = fmaxf(mx, x[i]);
-    }
-    if (mx > -INFINITY) {
-      l *= __builtin_amdgcn_exp2f(m - mx);  // m = -inf: l is 0
+    for (int v = 0; v < U; ++v) {
+      if (v < nu) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) l += __builtin_amdgcn_exp2f(x[i] - mx);
-      m = mx;
+        for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], bm[v][s], acc, 0, 0, 0);
+        // lane (col, kg) holds pairs p0 + 4 kg + i for block (grp U + v) 16 + col
+        float x[4], mx = m[v];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[i] = p0 + 4 * kg + i < n_pairs_rows ? acc[i] * sl2 : -INFINITY;
+          mx = fmaxf(mx, x[i]);
+        }
+        if (mx > -INFINITY) {
+          l[v] *= __builtin_amdgcn_exp2f(m[v] - mx);  // m = -inf: l is 0
+#pragma unroll
+          for (int i = 0; i < 4; ++i) l[v] += __builtin_amdgcn_exp2f(x[i] - mx);
+          m[v] = mx;
+        }
+      }
     }
   }
-  // the four lane groups hold disjoint rows of the same block
+  auto combine = [](float& mm, float& ll, float mo, float lo) __attribute__((always_inline)) {
+    const float mn = fmaxf(mm, mo);
+    ll = (mm == -INFINITY ? 0.f : ll * __builtin_amdgcn_exp2f(mm - mn)) +
+         (mo == -INFINITY ? 0.f : lo * __builtin_amdgcn_exp2f(mo - mn));
+    mm = mn;
+  };
+  __shared__ float part[4][U][16][2];
 #pragma unroll
-  for (int o = 16; o <= 32; o <<= 1) {
-    const float mo = __shfl_xor(m, o), lo = __shfl_xor(l, o);
-    const float mn = fmaxf(m, mo);
-    l = (m == -INFINITY ? 0.f : l * __builtin_amdgcn_exp2f(m - mn)) +
-        (mo == -INFINITY ? 0.f : lo * __builtin_amdgcn_exp2f(mo - mn));
-    m = mn;
+  for (int v = 0; v < U; ++v) {
+    // the four lane groups hold disjoint rows of the same block
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) combine(m[v], l[v], __shfl_xor(m[v], o), __shfl_xor(l[v], o));
+    if (kg == 0) {
+      part[wid][v][col][0] = m[v];
+      part[wid][v][col][1] = l[v];
+    }
   }
-  const int j = unit * 16 + col;
-  if (kg == 0 && j < NB)
-    a.scores[((size_t)pair * a.n_tiles + t) * a.nblk_capacity + j] = (m + __builtin_amdgcn_logf(l)) * kLn2;
+  __syncthreads();
+  if (wid == 0 && kg == 0) {
+#pragma unroll
+    for (int v = 0; v < U; ++v) {
+      float mm = part[0][v][col][0], ll = part[0][v][col][1];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) combine(mm, ll, part[w][v][col][0], part[w][v][col][1]);
+      const int j = (grp * U + v) * 16 + col;
+      if (v < nu && j < NB && ll > 0.f)
+        a.scores[((size_t)pair * a.n_tiles + t) * a.nblk_capacity + j] = (mm + __builtin_amdgcn_logf(ll)) * kLn2;
+    }
+  }
 }
 
 hipError_t launch_select_topk(const SelectArgs& a, hipStream_t stream) {
@@ -866,8 +897,9 @@ hipError_t launch_select_topk(const SelectArgs& a, hipStream_t stream) {
 
 hipError_t launch_prefill_select(const SelectArgs& a, hipStream_t stream) {
   if (a.n_blocks > 0) {
-    const long long waves = (long long)a.batch * a.n_kv_heads * a.n_tiles * ((a.n_blocks + 15) / 16);
-    const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+    const long long wgs =
+        (long long)a.batch * a.n_kv_heads * a.n_tiles * ((a.n_blocks + 16 * kTileUnits - 1) / (16 * kTileUnits));
+    const dim3 grid((unsigned)wgs), block(256);
     if (a.head_dim == 64) hipLaunchKernelGGL(prefill_tile_scores_kernel<64>, grid, block, 0, stream, a);
     else hipLaunchKernelGGL(prefill_tile_scores_kernel<128>, grid, block, 0, stream, a);
   }
