@@ -281,6 +281,36 @@ def bench_decode(api, torch, w, x, steps, warmup, mean_dtype="bf16", factor_fp4=
     return res
 
 
+def bench_exact_select(api, torch, w, x, steps, warmup):
+    """The exact-mass selector (every key of the context read) on the decode workload:
+    a reference for the summary-based selection, reported as context."""
+    B, Hq, Hkv, d, n = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_ctx
+    nb = n // 64
+    shape = api.make_shape(B, Hq, Hkv, d, n, dtype=w.dtype)
+    K, Q = to_dev(torch, x["K"]), to_dev(torch, x["Q"])
+    scores = torch.empty((B, Hkv, nb), device="cuda")
+    sel = torch.empty((B, Hkv, w.top_k), dtype=torch.int32, device="cuda")
+
+    def run():
+        api.bsattn_select_exact(shape, Q, K, nb, w.top_k, w.window, w.n_sink, None, sel, scores)
+
+    for _ in range(warmup):
+        run()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    key_bytes = B * Hkv * nb * 64 * d * 2
+    del K, Q
+    torch.cuda.empty_cache()
+    return dict(workload=w.name, selector="exact block mass", ms_per_call=ms, key_bytes=key_bytes,
+                GBps=key_bytes / (ms * 1e-3) / 1e9, frac_hbm=key_bytes / (ms * 1e-3) / HBM_PEAK)
+
+
 # ----------------------------------------------------------------------------- prefill
 def sparse_prefill_keys(sel, N, wl, ns, tile=128, S=64):
     """Keys each row attends in the block-sparse prefill, from a selection
@@ -500,6 +530,8 @@ def main():
                                                              mean_dtype="f32")
                 results[name + "/paged16"] = bench_decode(api, torch, w, x, args.steps, args.warmup,
                                                           page_tokens=16)
+                results[name + "/exact_select"] = bench_exact_select(api, torch, w, x, min(args.steps, 10),
+                                                                     min(args.warmup, 2))
             elif w.rank > 0:  # context: FP4 rows without the subspace projection; fp32 rows
                 if w.sub_dim > 0:
                     results[name + "/no_subspace"] = bench_decode(api, torch, w, x, args.steps, args.warmup,

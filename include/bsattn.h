@@ -197,6 +197,21 @@ bsattn_status bsattn_select_topk(const bsattn_shape* shape, const void* Q, const
                                  const int32_t* global_pos_host, int32_t n_global, int32_t* sel,
                                  float* scores, void* hip_stream);
 
+/*
+ * Selection by exact block mass, the selection oracle [COBS 2.1]: as
+ * bsattn_select_topk (same candidates, top-k order and outputs), but the
+ * group score of block j is read from the keys themselves,
+ *   scores[b,g,j] = ln sum_{h in g} sum_{t in block j} exp(q~_h . K[b,g,t,:]),
+ * the group's exact attention mass on the block.  It reads every key of the
+ * context, so it is a reference (a quality upper bound for the summary-based
+ * selectors), not a fast path.  Q [B,Hq,d] and K [B,Hkv,kv_capacity,d] BF16
+ * (contiguous); scores [B,Hkv,nblk_capacity] fp32; sel [B,Hkv,top_k] int32.
+ */
+bsattn_status bsattn_select_exact(const bsattn_shape* shape, const void* Q, const void* K,
+                                  int32_t nblk_capacity, int32_t top_k, int32_t window, int32_t n_sink,
+                                  const int32_t* global_pos_host, int32_t n_global, int32_t* sel,
+                                  float* scores, void* hip_stream);
+
 /* Bytes of device workspace bsattn_decode needs for these arguments (0 if invalid, or
  * when one partial per (b, K/V head) suffices and no workspace is needed). */
 size_t bsattn_decode_workspace_bytes(const bsattn_shape* shape, int32_t top_k, int32_t window,

@@ -17,7 +17,7 @@ from ._lib import BSATTN_BF16, BSATTN_F32, BSATTN_FP4_E2M1, PagedKV, Shape
 
 __all__ = [
     "BsattnError", "Shape", "PagedKV", "make_shape", "paged_kv", "library", "bsattn_build_summaries",
-    "bsattn_append_kv", "bsattn_select_prefill", "bsattn_sparse_prefill",
+    "bsattn_append_kv", "bsattn_select_prefill", "bsattn_sparse_prefill", "bsattn_select_exact",
     "bsattn_select_topk", "bsattn_decode_workspace_bytes", "bsattn_decode",
     "bsattn_decode_step",
     "bsattn_prefill",
@@ -139,6 +139,13 @@ def bsattn_append_kv(shape, K_new, V_new, K, V, rank, nblk_capacity, mean=None, 
                                       BSATTN_F32 if mean is None else _mean_dtype(mean), _ptr(factor),
                                       _factor_dtype(factor, factor_scale), _ptr(factor_scale), _ptr(basis),
                                       _sub_dim(basis), _paged(paged), _stream(stream)))
+
+
+def bsattn_select_exact(shape, Q, K, nblk_capacity, top_k, window, n_sink, global_pos, sel, scores, stream=None):
+    """Top-k blocks by the group's exact attention mass, read from the keys (reference selector)."""
+    g, ng = _globals(global_pos)
+    _check(library().bsattn_select_exact(ctypes.byref(shape), _ptr(Q), _ptr(K), nblk_capacity, top_k, window,
+                                         n_sink, g, ng, _ptr(sel), _ptr(scores), _stream(stream)))
 
 
 def bsattn_select_prefill(shape, Q, mean, nblk_capacity, top_k, window_left, n_sink, sel, scores, stream=None):

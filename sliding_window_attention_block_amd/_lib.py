@@ -25,6 +25,7 @@ EXPORTS = (
     "bsattn_build_summaries",
     "bsattn_append_kv",
     "bsattn_select_prefill",
+    "bsattn_select_exact",
     "bsattn_sparse_prefill",
     "bsattn_select_topk",
     "bsattn_decode_workspace_bytes",
@@ -87,6 +88,8 @@ def load():
     lib.bsattn_append_kv.restype = _st
     lib.bsattn_select_prefill.argtypes = [_pshape, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp]
     lib.bsattn_select_prefill.restype = _st
+    lib.bsattn_select_exact.argtypes = [_pshape, _vp, _vp, _i32, _i32, _i32, _i32, _pi32, _i32, _vp, _vp, _vp]
+    lib.bsattn_select_exact.restype = _st
     lib.bsattn_sparse_prefill.argtypes = [_pshape, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]
     lib.bsattn_sparse_prefill.restype = _st
     lib.bsattn_select_topk.argtypes = [_pshape, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _i32, _i32,

@@ -462,6 +462,40 @@ bsattn_status bsattn_select_topk(const bsattn_shape* shape, const void* Q, const
   return BSATTN_OK;
 }
 
+bsattn_status bsattn_select_exact(const bsattn_shape* shape, const void* Q, const void* K, int32_t nblk_capacity,
+                                  int32_t top_k, int32_t window, int32_t n_sink, const int32_t* global_pos_host,
+                                  int32_t n_global, int32_t* sel, float* scores, void* hip_stream) {
+  g_err[0] = 0;
+  bsattn_status st = check_shape(shape, true);
+  if (st != BSATTN_OK) return st;
+  if (shape->dtype != BSATTN_BF16) return fail(BSATTN_ERR_UNSUPPORTED, "the exact-mass selector takes BF16 Q/K");
+  if (Q == nullptr || K == nullptr || sel == nullptr || scores == nullptr)
+    return fail(BSATTN_ERR_INVALID, "Q, K, sel and scores must be non-NULL");
+  if (!aligned16(Q) || !aligned16(K)) return fail(BSATTN_ERR_INVALID, "device pointers must be 16-byte aligned");
+  if (top_k < 1 || top_k > BSATTN_MAX_TOP_K) return fail(BSATTN_ERR_INVALID, "top_k must be in [1, %d]", BSATTN_MAX_TOP_K);
+  if (window < 0 || n_sink < 0) return fail(BSATTN_ERR_INVALID, "window and n_sink must be >= 0");
+  const int nb = shape->n_ctx / shape->block_size;
+  if (nb > BSATTN_MAX_BLOCKS) return fail(BSATTN_ERR_UNSUPPORTED, "more than %d complete blocks", BSATTN_MAX_BLOCKS);
+  if (nblk_capacity < nb) return fail(BSATTN_ERR_INVALID, "nblk_capacity < n_ctx / block_size");
+  st = check_globals(global_pos_host, n_global, shape->n_ctx);
+  if (st != BSATTN_OK) return st;
+  bsattn::SelectArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.Q = Q; a.K = K; a.sel = sel; a.scores = scores;
+  a.kv_capacity = shape->kv_capacity;
+  a.batch = shape->batch; a.n_q_heads = shape->n_q_heads; a.n_kv_heads = shape->n_kv_heads;
+  a.head_dim = shape->head_dim;
+  a.n_blocks = nb;
+  a.nblk_capacity = nblk_capacity;
+  a.top_k = top_k;
+  a.scale = effective_scale(shape);
+  a.bf16 = true;
+  a.forced = make_forced(shape->n_ctx, window, n_sink, global_pos_host, n_global);
+  hipError_t e = bsattn::launch_select_exact(a, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return fail(BSATTN_ERR_HIP, "exact selection launch: %s", hipGetErrorString(e));
+  return BSATTN_OK;
+}
+
 size_t bsattn_decode_workspace_bytes(const bsattn_shape* shape, int32_t top_k, int32_t window,
                                      int32_t n_sink, int32_t n_global) {
   if (check_shape(shape, true) != BSATTN_OK) return 0;

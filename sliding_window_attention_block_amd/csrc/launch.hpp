@@ -91,8 +91,12 @@ struct SelectArgs {
   // candidates of tile t are the complete blocks j with 64 j before the window
   // [i - window_left, i] of the tile's last row i, and not inside the sinks
   int32_t tile_rows, n_tiles, seq_len, window_left, n_sink;
+  // exact block mass: the keys themselves [B, Hkv, kv_capacity, d] (BF16)
+  const void* K;
+  int32_t kv_capacity;
 };
 hipError_t launch_prefill_select(const SelectArgs& a, hipStream_t stream);
+hipError_t launch_select_exact(const SelectArgs& a, hipStream_t stream);  // K, kv_capacity set
 constexpr int kSparseTile = 128;      // query rows per selection tile (the prefill workgroup)
 constexpr int kSparseMaxTopK = 256;   // selected blocks per tile
 constexpr int kSparseMaxSink = 256;   // sink tokens of the block-sparse prefill

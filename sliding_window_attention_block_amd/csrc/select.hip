@@ -895,6 +895,79 @@ hipError_t launch_select_topk(const SelectArgs& a, hipStream_t stream) {
   return a.bf16 ? launch_g<128, true>(a, stream) : launch_g<128, false>(a, stream);
 }
 
+// Exact block mass [COBS 2.1, the selection oracle]: scores[b,g,j] = ln sum over
+// the group's heads h and block j's keys k of exp(q~_h . k), read from the keys
+// themselves (a reference selector: it streams every key of the context).  One
+// wave per (pair, block): the group's heads as the MFMA A operand (rows past G
+// zero), 16 key rows at a time as B (bf16 keys and queries: exact products,
+// fp32 sums), the 64 keys x G heads reduced to one log-sum-exp (lane, then the
+// 16 lanes of a row group, then the four lane groups).
+template <int D>
+__global__ __launch_bounds__(256) void select_exact_kernel(SelectArgs a) {
+  constexpr int KS = D / 32;
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const long long gw = (long long)blockIdx.x * 4 + wid;
+  const int NB = a.n_blocks;
+  const int pair = (int)(gw / NB), j = (int)(gw % NB);
+  if (pair >= a.batch * a.n_kv_heads) return;  // no barriers: waves are independent
+  const int col = lane & 15, kg = lane >> 4;
+  const int b = pair / a.n_kv_heads, g = pair % a.n_kv_heads;
+  const int G = a.n_q_heads / a.n_kv_heads;
+  const uint16_t* Kb = reinterpret_cast<const uint16_t*>(a.K) + ((size_t)pair * a.kv_capacity + (size_t)j * kBlock) * D;
+  u32x4 kv[4][KS];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kv[c][s] = *reinterpret_cast<const u32x4*>(Kb + (16 * c + col) * D + 32 * s + 8 * kg);
+  bf16x8 qm[KS];
+  {
+    const uint16_t* qrow =
+        reinterpret_cast<const uint16_t*>(a.Q) + ((size_t)b * a.n_q_heads + g * G + min(col, G - 1)) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 32 * s + 8 * kg);
+      if (col >= G) v = u32x4{0u, 0u, 0u, 0u};
+      qm[s] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  const float sl2 = a.scale * kLog2e;
+  float x[4][4], m = -INFINITY;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qm[s], __builtin_bit_cast(bf16x8, kv[c][s]), acc, 0, 0, 0);
+    // lane (key 16 c + col, kg): heads 4 kg .. +3
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[c][i] = 4 * kg + i < G ? acc[i] * sl2 : -INFINITY;
+      m = fmaxf(m, x[c][i]);
+    }
+  }
+  // the block's max over every lane (the 64 lanes hold disjoint (key, head) pairs)
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+  float l = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) l += __builtin_amdgcn_exp2f(x[c][i] - m);  // exp2(-inf) = 0
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) l += __shfl_xor(l, o);
+  if (lane == 0) a.scores[(size_t)pair * a.nblk_capacity + j] = (m + __builtin_amdgcn_logf(l)) * kLn2;
+}
+
+hipError_t launch_select_exact(const SelectArgs& a, hipStream_t stream) {
+  if (a.n_blocks > 0) {
+    const long long waves = (long long)a.batch * a.n_kv_heads * a.n_blocks;
+    const dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+    if (a.head_dim == 64) hipLaunchKernelGGL(select_exact_kernel<64>, grid, block, 0, stream, a);
+    else hipLaunchKernelGGL(select_exact_kernel<128>, grid, block, 0, stream, a);
+  }
+  return launch_topk(a, stream);
+}
+
 hipError_t launch_prefill_select(const SelectArgs& a, hipStream_t stream) {
   if (a.n_blocks > 0) {
     const long long wgs =

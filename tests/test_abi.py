@@ -24,7 +24,7 @@ def _header_functions():
 def test_library_exports_every_declared_function():
     lib = api.library()
     declared = _header_functions()
-    assert len(declared) == 13
+    assert len(declared) == 14
     for name in declared:
         assert hasattr(lib, name), name
     assert set(declared) == set(_lib.EXPORTS)
@@ -301,3 +301,14 @@ def test_sparse_prefill_rejects_bad_arguments():
     assert _status(g, *pre(sel=None))[0] == 1
     assert _status(g, *pre(wl=-5))[0] == 1
     assert _status(g, *pre(k=300))[0] == 1
+
+
+def test_exact_selector_rejects_bad_arguments():
+    f = "bsattn_select_exact"
+    args = lambda **o: [o.get("shape", _shape()), FAKE, o.get("K", FAKE), o.get("nblk", 4), o.get("k", 2),
+                        64, 0, None, 0, FAKE, FAKE, None]
+    assert _status(f, *args(shape=_shape(dtype=0)))[0] == 2   # fp32
+    assert _status(f, *args(K=None))[0] == 1
+    assert _status(f, *args(K=FAKE + 8))[0] == 1              # misaligned
+    assert _status(f, *args(k=0))[0] == 1
+    assert _status(f, *args(nblk=3))[0] == 1
