@@ -106,3 +106,38 @@ def test_sparse_prefill_8k_sampled_rows(api):
     w = _pw("sparse_prefill_8k", 1, 32, 8, 128, 8192, 95)
     rows = np.array([0, 127, 128, 1000, 1023, 1024, 2047, 4096, 5000, 8064, 8191])
     _check(api, w, 1023, 64, 16, rows=rows, pairs=[(0, 0), (0, 5)])
+
+
+def test_random_blocks_bigbird_style(api):
+    """Random attention (the SWA glossary's BigBird extension), block-wise: each
+    query tile attends r seeded random earlier blocks besides its causal window and
+    sinks.  The blocks are an input (drawn here, not selected), passed as the tile
+    selection; outputs against the oracle with the same blocks."""
+    import torch
+    w = _pw("sp_bigbird", 1, 8, 2, 128, 1280, 96)
+    wl, ns, r = 127, 32, 3
+    N, G = w.seq_len, w.n_q_heads // w.n_kv_heads
+    n_tiles = (N + 127) // 128
+    rng = np.random.default_rng(97)
+    sel = np.full((w.batch, w.n_kv_heads, n_tiles, r), -1, dtype=np.int32)
+    for b in range(w.batch):
+        for g in range(w.n_kv_heads):
+            for t in range(n_tiles):
+                earlier = np.arange((128 * t) // 64)
+                if len(earlier):
+                    pick = np.sort(rng.choice(earlier, min(r, len(earlier)), replace=False))
+                    sel[b, g, t, :len(pick)] = pick
+    x = make_prefill_inputs(w)
+    Q, K, V = to_dev(x["Q"]), to_dev(x["K"]), to_dev(x["V"])
+    shape = api.make_shape(w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, N, dtype="bf16")
+    O = torch.full((w.batch, w.n_q_heads, N, w.head_dim), float("nan"), device="cuda")
+    lse = torch.full((w.batch, w.n_q_heads, N), float("nan"), device="cuda")
+    api.bsattn_sparse_prefill(shape, Q, K, V, torch.from_numpy(sel).cuda(), r, wl, ns, O, lse)
+    torch.cuda.synchronize()
+    Of, Lf = O.cpu().numpy(), lse.cpu().numpy()
+    selection = {(b, g): dict(sel=sel[b, g]) for b in range(w.batch) for g in range(w.n_kv_heads)}
+    ref = oracle.sparse_prefill(as_f64(x["Q"]), as_f64(x["K"]), as_f64(x["V"]), N, 64, wl, ns, selection)
+    for (b, g), (Or, Lr) in ref.items():
+        for hh in range(G):
+            assert max_abs(Of[b, g * G + hh], Or[hh]) < OUT_TOL
+            assert max_abs(Lf[b, g * G + hh], Lr[hh]) < OUT_TOL
