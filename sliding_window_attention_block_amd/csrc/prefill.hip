@@ -466,6 +466,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
       __syncthreads();  // every wave's copies landed; every wave is done with the other buffer
       if (stg + 1 < n_stage) issue_stage(stg + 1, kn, kn + T::BYTES);
       uint8_t* vt = kt + T::BYTES;
+      // this lane's allowed keys of the stage's two halves, then one stage body
+      // for every kind of stage (a single inlined copy of the MFMA / softmax code)
+      uint32_t am[2];
+      bool masked = false;
       if (SP && stg < nx) {
         const int xb = __builtin_amdgcn_readfirstlane(xblk[stg]);
         const int jb = (xb >> 1) * BN;
@@ -473,18 +477,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         // the wave's first row allows the fewest
         const int cap = (xb & 1) ? 0x7fffffff : a.sp_n_sink - 1;
         const int hi = min(myrow - wl - 1, cap), hi0 = min(r0 - wl - 1, cap);
-        uint32_t am[2];
-        bool masked = false;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int j0 = jb + 32 * u;
           am[u] = range_bits32(0, hi - j0);
           masked |= j0 + 31 > hi0;
         }
-        stage<D, 2, COMP>(kt, vt, qop, oacc, st, sl2, am, masked);
       } else if (stg - nx < n_band) {
-        stg -= nx;
-        const int jb = (t_lo + stg) * BN;
+        const int jb = (t_lo + stg - nx) * BN;
         uint64_t gbits = 0ull;
         if (LG) {
           for (int i = lower_bound_i32(a.gpos, a.n_global, jb); i < a.n_global && a.gpos[i] < jb + BN; ++i)
@@ -493,8 +493,6 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         // allowed keys of this lane's row: [lo, hi], plus the global columns
         const int lo = wl < 0 ? 0 : myrow - wl;
         const int hi = min(N - 1, wr < 0 ? N - 1 : myrow + wr);
-        uint32_t am[2];
-        bool masked = false;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int j0 = jb + 32 * u;
@@ -506,12 +504,13 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
           masked |= !full;
           am[u] = range_bits32(lo - j0, hi - j0) | gsub;
         }
-        stage<D, 2, COMP>(kt, vt, qop, oacc, st, sl2, am, masked);
       } else {
         const int s0 = (stg - nx - n_band) * BN;
-        const uint32_t am[2] = {range_bits32(0, ngc - 1 - s0), range_bits32(0, ngc - 1 - s0 - 32)};
-        stage<D, 2, COMP>(kt, vt, qop, oacc, st, sl2, am, s0 + 64 > ngc);
+        am[0] = range_bits32(0, ngc - 1 - s0);
+        am[1] = range_bits32(0, ngc - 1 - s0 - 32);
+        masked = s0 + 64 > ngc;
       }
+      stage<D, 2, COMP>(kt, vt, qop, oacc, st, sl2, am, masked);
     };
     // unrolled by two so each buffer's LDS addresses are compile-time offsets;
     // an odd last stage runs after the loop (no branch inside the loop body)
