@@ -416,3 +416,14 @@ def test_maximum_sizes(api):
     globals_ = tuple(int(p) for p in np.sort(rng.choice(n, size=256, replace=False)))
     ties = _check_case(api, w, globals_, 0)
     print(f"[decode max sizes] near ties: {ties}", flush=True)
+
+
+def test_dilated_window_as_forced_positions(api):
+    """A dilated sliding window (the SWA glossary's extension: every delta-th token
+    back from the query) expressed as forced positions: the window argument 0 and the
+    positions t, t - 4, ..., t - 4 * 39 given as global positions; checked against the
+    oracle with the same forced set."""
+    w = _w("dilated_window", 1, 8, 2, 128, 3000, 0, 6, 0, 16, "bf16", 45)
+    t = w.n_ctx - 1
+    globals_ = tuple(sorted(t - 4 * m for m in range(40)))
+    _check_case(api, w, globals_, 0, one_call=True, mean_dtype="bf16")
