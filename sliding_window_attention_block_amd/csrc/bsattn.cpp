@@ -594,7 +594,8 @@ bsattn_status bsattn_select_prefill(const bsattn_shape* shape, const void* Q, co
   a.seq_len = shape->n_ctx;
   a.window_left = window_left;
   a.n_sink = n_sink;
-  if ((long long)a.batch * a.n_kv_heads * a.n_tiles > 0x7fffffffLL)
+  // tile scorer: one workgroup per (pair, tile, 64 blocks); top-k: one per (pair, tile)
+  if ((long long)a.batch * a.n_kv_heads * a.n_tiles * ((nb + 63) / 64 > 0 ? (nb + 63) / 64 : 1) > 0x7fffffffLL)
     return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");
   hipError_t e = bsattn::launch_prefill_select(a, (hipStream_t)hip_stream);
   if (e != hipSuccess) return fail(BSATTN_ERR_HIP, "prefill selection launch: %s", hipGetErrorString(e));

@@ -295,6 +295,10 @@ def test_sparse_prefill_rejects_bad_arguments():
     assert _status(f, *sel_args(wl=-1))[0] == 1
     assert _status(f, *sel_args(ns=300))[0] == 1
     assert _status(f, *sel_args(nblk=3))[0] == 1
+    # 64K blocks (4M tokens): 32768 tiles x 1024 groups of 64 blocks per pair; 64 pairs overflow the grid
+    big = _shape(batch=8, n_q_heads=64, n_kv_heads=8, n_ctx=64 * 65536, kv_capacity=64 * 65536)
+    st, msg = _status(f, *sel_args(shape=big, nblk=65536))
+    assert st == 2 and "grid" in msg
     pre = lambda **o: [o.get("shape", _shape()), FAKE, FAKE, FAKE, o.get("sel", FAKE), o.get("k", 2),
                        o.get("wl", 64), o.get("ns", 0), FAKE, None, None]
     assert _status(g, *pre(shape=_shape(dtype=0)))[0] == 2
