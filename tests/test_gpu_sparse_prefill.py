@@ -141,3 +141,12 @@ def test_random_blocks_bigbird_style(api):
         for hh in range(G):
             assert max_abs(Of[b, g * G + hh], Or[hh]) < OUT_TOL
             assert max_abs(Lf[b, g * G + hh], Lr[hh]) < OUT_TOL
+
+
+def test_sparse_prefill_maximum_sizes(api):
+    """top_k = 256 and n_sink = 256 (the limits): late tiles of a 300-block sequence
+    have more than 256 candidates, and their extra-stage list holds 256 selected plus
+    4 sink blocks; oracle on sampled rows."""
+    w = _pw("sp_max", 1, 4, 1, 64, 64 * 300, 98)
+    rows = np.array([0, 255, 256, 4000, 16383, 17000, 19100, 64 * 300 - 1])
+    _check(api, w, 127, 256, 256, rows=rows)
