@@ -1,29 +1,27 @@
-// Block selection for a decode query (COBS explainer, technical summary):
+// Block selection (COBS explainer, technical summary):
 //  * per query head h and complete block j, the first-order score q~.mean_j
 //    (section 2.2) or the second-order COBS score q~.mean_j + 1/2 sum_i
-//    (factor_ji . q~)^2 (section 2.3, low-rank covariance);
+//    (factor_ji . q~)^2 (section 2.3, low-rank covariance; with a query
+//    subspace the factor rows meet the projected query);
 //  * the group score ln sum_h exp(s_hj) over the query heads that share the
 //    K/V head (the log of the group's estimated attention mass, section 2.1);
 //  * the top-k candidates by (score desc, index asc), written ascending.
-// Candidates are complete blocks with a token outside the forced set (sinks,
-// window, global tokens).
+// Decode candidates are complete blocks with a token outside the forced set
+// (sinks, window, global tokens); prefill tiles have their own rule (below).
 //
-// Scoring streams every summary once: 16 lanes (one DPP row) share one block,
-// lane l owning the 4-dim chunks l, 16 + l, ... of every query head in
-// registers, so each load instruction reads 256 contiguous bytes of a summary
-// row (128 of a bfloat16 mean row); the 16 partial dot products are summed
-// with DPP row rotations.  Each
-// wave scores a run of blocks of one (b, K/V head) pair with the next group's
-// loads in flight while it computes the current one, and waves never wait for
-// each other, so the loads stream without load-then-compute rounds.  All of a block's rows
-// (mean and up to 8 factor rows) are loaded before any arithmetic, so a wave
-// waits on HBM once per block rather than once per row.
-//
-// Top-k: one wave per (b, K/V head), an exact 4-pass radix select (8 bits a
-// pass) on order-preserving 32-bit keys: a 256-bin LDS histogram per pass and
-// a wave-wide scan to find the digit of the k-th largest key; then every lane
-// emits its candidates above the threshold, and the lowest-index ones equal
-// to it, in index order.
+// Kernels, in file order:
+//  * select_scores_kernel: the VALU scorer for fp32 operands.  16 lanes (one
+//    DPP row) share one block, lane l owning the 4-dim chunks l, 16 + l, ... of
+//    every query head, so each load instruction reads 256 contiguous bytes of
+//    a summary row; DPP row rotations sum the 16 partial dot products.  Waves
+//    score runs of blocks with the next group's loads in flight.
+//  * select_scores_mfma_kernel: bf16 queries and means with FP4 factor rows or
+//    none, on v_mfma_f32_16x16x32_bf16 (every operand exact in bf16), with the
+//    per-workgroup query projection when a subspace basis is given.
+//  * topk_kernel: one workgroup per (b, K/V head) or per (b, K/V head, prefill
+//    tile), an exact radix select on order-preserving 32-bit keys.
+//  * select_exact_kernel: the exact block mass, read from the keys.
+//  * prefill_tile_scores_kernel: the block-sparse prefill's tile scores.
 #include <type_traits>
 
 #include "launch.hpp"
