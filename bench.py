@@ -43,8 +43,8 @@ CALIB_BYTES = 512 << 20    # the plain device copy --calibrate-copy runs (bytes 
 # of `bench.py --only first_order_decode_32k --calibrate-copy`, each scaled by
 # CALIB_BYTES / (the same counter for the calibration copy).  Valid only for
 # the sources it was taken on (their SHA-256); otherwise traffic is null.
-STEP_TRAFFIC = {"sources_sha256": "a6926562c3ac57a69c66e5df64857594072872f28b4bd753694e53896bb61169",
-                "bytes_per_step": 128405006}  # FETCH x 1.9999 (8489.6 + 51821.7 + 1080.6 KiB) + WRITE x 1 (256.0 + 2089.1 + 272.0 KiB)
+STEP_TRAFFIC = {"sources_sha256": "156e19f75207b575e54714ee60532ff2b47e22d9e9d7205c52c3053aab7546ac",
+                "bytes_per_step": 128405211}  # FETCH x 1.9999 (8489.6 + 51821.8 + 1080.6 KiB) + WRITE x 1 (256.0 + 2089.1 + 272.0 KiB)
 STEP_SOURCES = ("sliding_window_attention_block_amd/csrc/decode.hip",
                 "sliding_window_attention_block_amd/csrc/select.hip",
                 "sliding_window_attention_block_amd/csrc/bsattn.cpp",
