@@ -154,15 +154,18 @@ __device__ __forceinline__ uint32_t range_bits32(int lo, int hi) {
 }
 
 // One stage of NH 32-key halves held in LDS for this wave's 32 query rows.
-// am[u]: this lane's allowed keys of half u as bits p = key - 32u (the lane's
-// row is l % 32; its elements e hold keys 8(e/4) + 4(l/32) + e%4).  COMP adds
-// the product with the bf16 residual of P.  The MFMAs run unconditionally (a
-// half with nothing allowed only has its weights forced to 0), so no
-// accumulator ever sits under a branch, and the mask is two ALU ops per element.
-template <int D, int NH, bool COMP>
+// Bit u of `masked` (wave-uniform) marks a half on a mask edge; only for such a
+// half is am(u) evaluated: this lane's allowed keys of half u as bits
+// p = key - 32u (the lane's row is l % 32; its elements e hold keys
+// 8(e/4) + 4(l/32) + e%4).  COMP adds the product with the bf16 residual of P.
+// The MFMAs run unconditionally (a half with nothing allowed only has its
+// weights forced to 0), so no accumulator ever sits under a branch, and the mask
+// is two ALU ops per element: a signed one-bit field extract (0 or all ones)
+// selects, bitwise, between the logit and -inf.
+template <int D, int NH, bool COMP, typename AllowedBits>
 __device__ __forceinline__ void stage(const uint8_t* kt, const uint8_t* vt, const u32x4* qop,
-                                      f32x16* oacc, RowState& st, float sl2, const uint32_t* am,
-                                      bool masked) {
+                                      f32x16* oacc, RowState& st, float sl2, AllowedBits am,
+                                      uint32_t masked) {
   using T = Tile<D>;
   const int lane = threadIdx.x & 63;
   const int r32 = lane & 31, h2 = lane >> 5;
@@ -184,10 +187,17 @@ __device__ __forceinline__ void stage(const uint8_t* kt, const uint8_t* vt, cons
   const int q16 = lane >> 4, a16 = lane & 15;
 #pragma unroll
   for (int u = 0; u < NH; ++u) {
-    if (masked) {  // wave-uniform: only tiles on a mask edge
-      const uint32_t m = am[u] >> (4 * h2);
+    if ((masked >> u) & 1u) {  // wave-uniform: only halves on a mask edge
+      const uint32_t m = am(u) >> (4 * h2);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[u][e] = ((m >> (8 * (e >> 2) + (e & 3))) & 1u) ? s[u][e] : -INFINITY;
+      for (int e = 0; e < 16; ++e) {
+        const int p = 8 * (e >> 2) + (e & 3);
+        const uint32_t keep = (uint32_t)((int)(m << (31 - p)) >> 31);
+        // copied out first: a bit-cast of a vector-element lvalue reads element 0
+        const float v = s[u][e];
+        const uint32_t x = __builtin_bit_cast(uint32_t, v);
+        s[u][e] = __builtin_bit_cast(float, (x & keep) | (0xff800000u & ~keep));
+      }
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -311,8 +321,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
                                            (lds_void*)(vt + 1024 * k), 16, 0, 0);
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        const uint32_t am[1] = {range_bits32(0, N - 1 - j0)};
-        stage<D, 1, COMP>(kt, vt, qop, oacc, st, sl2, am, j0 + 32 > N);
+        stage<D, 1, COMP>(kt, vt, qop, oacc, st, sl2, [&](int) { return range_bits32(0, N - 1 - j0); },
+                          j0 + 32 > N ? 1u : 0u);
       }
     };
     if (live) {
@@ -466,51 +476,53 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
       __syncthreads();  // every wave's copies landed; every wave is done with the other buffer
       if (stg + 1 < n_stage) issue_stage(stg + 1, kn, kn + T::BYTES);
       uint8_t* vt = kt + T::BYTES;
-      // this lane's allowed keys of the stage's two halves, then one stage body
-      // for every kind of stage (a single inlined copy of the MFMA / softmax code)
-      uint32_t am[2];
-      bool masked = false;
+      // Which halves of the stage sit on a mask edge (wave-uniform bits), and
+      // this lane's allowed keys [lo, hi] plus the global columns among the
+      // stage's keys jb .. jb + 63 (position, or gathered-column slot, of its
+      // first row); the words of allowed-key bits are built only for the edge
+      // halves.  One stage body serves every kind of stage (a single inlined
+      // copy of the MFMA / softmax code).
+      int jb, lo = 0, hi;
+      uint32_t masked = 0;
+      uint64_t gbits = 0ull;
       if (SP && stg < nx) {
         const int xb = __builtin_amdgcn_readfirstlane(xblk[stg]);
-        const int jb = (xb >> 1) * BN;
+        jb = (xb >> 1) * BN;
         // keys before this row's window (and below n_sink for a sink-only block);
         // the wave's first row allows the fewest
         const int cap = (xb & 1) ? 0x7fffffff : a.sp_n_sink - 1;
-        const int hi = min(myrow - wl - 1, cap), hi0 = min(r0 - wl - 1, cap);
+        hi = min(myrow - wl - 1, cap);
+        const int hi0 = min(r0 - wl - 1, cap);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) masked |= (jb + 32 * u + 31 > hi0 ? 1u : 0u) << u;
+      } else if (stg - nx < n_band) {
+        jb = (t_lo + stg - nx) * BN;
+        lo = wl < 0 ? 0 : myrow - wl;
+        hi = min(N - 1, wr < 0 ? N - 1 : myrow + wr);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int j0 = jb + 32 * u;
-          am[u] = range_bits32(0, hi - j0);
-          masked |= j0 + 31 > hi0;
+          // every key of the half allowed for all 32 rows
+          const bool all_lo = wl < 0 || j0 >= r0 + 31 - wl;
+          const bool all_hi = wr < 0 || j0 + 31 <= r0 + wr;
+          masked |= (all_lo && all_hi && j0 + 31 < N ? 0u : 1u) << u;
         }
-      } else if (stg - nx < n_band) {
-        const int jb = (t_lo + stg - nx) * BN;
-        uint64_t gbits = 0ull;
-        if (LG) {
+        if (LG && masked) {
           for (int i = lower_bound_i32(a.gpos, a.n_global, jb); i < a.n_global && a.gpos[i] < jb + BN; ++i)
             gbits |= 1ull << (a.gpos[i] - jb);
         }
-        // allowed keys of this lane's row: [lo, hi], plus the global columns
-        const int lo = wl < 0 ? 0 : myrow - wl;
-        const int hi = min(N - 1, wr < 0 ? N - 1 : myrow + wr);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int j0 = jb + 32 * u;
-          const uint32_t gsub = (uint32_t)(gbits >> (32 * u));
-          // wave-uniform: every key of the half allowed for all 32 rows
-          const bool all_lo = wl < 0 || j0 >= r0 + 31 - wl;
-          const bool all_hi = wr < 0 || j0 + 31 <= r0 + wr;
-          const bool full = all_lo && all_hi && j0 + 31 < N;
-          masked |= !full;
-          am[u] = range_bits32(lo - j0, hi - j0) | gsub;
-        }
       } else {
-        const int s0 = (stg - nx - n_band) * BN;
-        am[0] = range_bits32(0, ngc - 1 - s0);
-        am[1] = range_bits32(0, ngc - 1 - s0 - 32);
-        masked = s0 + 64 > ngc;
+        jb = (stg - nx - n_band) * BN;
+        hi = ngc - 1;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) masked |= (jb + 32 * u + 32 > ngc ? 1u : 0u) << u;
       }
-      stage<D, 2, COMP>(kt, vt, qop, oacc, st, sl2, am, masked);
+      stage<D, 2, COMP>(kt, vt, qop, oacc, st, sl2,
+                        [&](int u) {
+                          const int j0 = jb + 32 * u;
+                          return range_bits32(lo - j0, hi - j0) | (uint32_t)(gbits >> (32 * u));
+                        },
+                        masked);
     };
     // unrolled by two so each buffer's LDS addresses are compile-time offsets;
     // an odd last stage runs after the loop (no branch inside the loop body)
