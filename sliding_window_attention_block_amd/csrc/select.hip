@@ -190,12 +190,22 @@ __global__ __launch_bounds__(256, scores_heavy(GM, RM, PB, D) ? 1 : 2) void sele
     }
   };
 
-  // two units in flight (A: even steps, B: odd), every path written out
+  // two units in flight (A: even steps, B: odd), every path written out; one
+  // unit when a lane's query values and two stages of summary rows would pass
+  // 256 registers (16 query heads with fp32 rank-8 factor rows at D = 128):
+  // the second stage would spill
+  constexpr int kStageRegs = PB * ((MB ? SL / 2 : SL) + RM * (F4 ? NC + 1 : SL));
+  constexpr bool kOneStage = GM * SL + 2 * kStageRegs > 256;
   const int n_units = (NB + UB - 1) / UB;
   const int u0 = wi * a.per_wave, u1 = min(u0 + a.per_wave, n_units);
   const int n = u1 - u0;
   Stage A, B;
-  if (n >= 4) {
+  if constexpr (kOneStage) {
+    for (int u = u0; u < u1; ++u) {
+      load(u, A);
+      comp(u, A);
+    }
+  } else if (n >= 4) {
     load(u0, A);
     load(u0 + 1, B);
     int u = u0;
@@ -556,7 +566,9 @@ constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
 
 // One workgroup of kTopkThreads threads per (b, K/V head).  Thread t owns the contiguous
-// block range [t*per, (t+1)*per); its keys stay in registers (per <= KPT).
+// block range [t*per, (t+1)*per) (per <= KPT); up to 32 keys per thread stay in
+// registers, more (over 32,768 blocks) are read again from the scores on each
+// pass, which the L2 holds, so the kernel stays within its 128 registers.
 // Barriers: one after the candidate count / AND / OR reduction (which also
 // clears the four pass histograms), one per radix pass (every wave then finds
 // the pass's digit from the histogram itself), one for the output scan.  Bytes
@@ -575,7 +587,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
   const float* sc = a.scores + (size_t)bh * a.nblk_capacity;
   int32_t* out = a.sel + (size_t)bh * a.top_k;
 
-  uint32_t key[KPT];
+  constexpr bool kRegKeys = KPT <= 32;
+  uint32_t key[kRegKeys ? KPT : 1];
+  // key of block j0 + t (t < j1 - j0)
+  auto key_at = [&](int t) -> uint32_t {
+    if constexpr (kRegKeys) return key[t];
+    else return order_key(sc[j0 + t]);
+  };
   uint64_t cm = 0ull;  // bit t: block j0 + t is a candidate
   uint32_t kand = ~0u, kor = 0u;
   // prefill tiles: blocks starting before the window of the tile's last row
@@ -587,15 +605,16 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
 #pragma unroll
   for (int t = 0; t < KPT; ++t) {
     const int j = j0 + t;
-    key[t] = 0u;
+    if constexpr (kRegKeys) key[t] = 0u;
     if (j < j1) {
-      key[t] = order_key(sc[j]);
+      const uint32_t k = order_key(sc[j]);
+      if constexpr (kRegKeys) key[t] = k;
       const bool cand = a.tile_rows > 0 ? (j * kBlock < tile_klo && (j + 1) * kBlock > a.n_sink)
                                         : forced_mask(a.forced, j) != ~0ull;
       if (cand) {
         cm |= 1ull << t;
-        kand &= key[t];
-        kor |= key[t];
+        kand &= k;
+        kor |= k;
       }
     }
   }
@@ -628,7 +647,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
       uint32_t* h = hist[pass];
 #pragma unroll
       for (int t = 0; t < KPT; ++t)
-        if (((cm >> t) & 1ull) && (key[t] & pmask) == prefix) atomicAdd(&h[(key[t] >> shift) & 255u], 1u);
+        if ((cm >> t) & 1ull) {
+          const uint32_t k = key_at(t);
+          if ((k & pmask) == prefix) atomicAdd(&h[(k >> shift) & 255u], 1u);
+        }
       __syncthreads();
       // every wave: lane l reads digits 255-4l (c4[3]) down to 252-4l (c4[0])
       const u32x4 c4 = reinterpret_cast<const u32x4*>(h)[63 - lane];
@@ -659,7 +681,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
 #pragma unroll
   for (int t = 0; t < KPT; ++t) {
     if (!((cm >> t) & 1ull)) continue;
-    const uint32_t km = key[t] & pmask;
+    const uint32_t km = key_at(t) & pmask;
     gt += km > prefix;
     eq += km == prefix;
   }
@@ -678,7 +700,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
 #pragma unroll
     for (int t = 0; t < KPT; ++t) {
       if (!((cm >> t) & 1ull)) continue;
-      const uint32_t km = key[t] & pmask;
+      const uint32_t km = key_at(t) & pmask;
       if (km > prefix || (km == prefix && taken < take_eq)) {
         taken += km == prefix;
         out[pos++] = j0 + t;

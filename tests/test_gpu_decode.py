@@ -48,6 +48,10 @@ SMALL = [
     # groups that end inside a 4-head lane group (MFMA scorer: 3 of 4, 12 of 16 heads)
     (_w("bf16_g3_d64_r0", 2, 6, 2, 64, 2000, 0, 9, 128, 16, "bf16", 40), (50, 1300), 0),
     (_w("bf16_g12_d128_r3", 1, 24, 2, 128, 1900, 3, 7, 200, 64, "bf16", 41), (), 0),
+    # fp32 rank-8 factor rows with 16 query heads at d = 128: the VALU scorer keeps
+    # one unit of summary rows in flight instead of two (the second would spill)
+    (_w("bf16_g16_d128_r8", 1, 16, 1, 128, 1300, 8, 5, 100, 16, "bf16", 42), (), 0),
+    (_w("f32_g13_d128_r6", 2, 26, 2, 128, 700, 6, 3, 64, 8, "f32", 43), (40,), 0),
 ]
 
 
