@@ -43,8 +43,8 @@ CALIB_BYTES = 512 << 20    # the plain device copy --calibrate-copy runs (bytes 
 # of `bench.py --only first_order_decode_32k --calibrate-copy`, each scaled by
 # CALIB_BYTES / (the same counter for the calibration copy).  Valid only for
 # the sources it was taken on (their SHA-256); otherwise traffic is null.
-STEP_TRAFFIC = {"sources_sha256": "156e19f75207b575e54714ee60532ff2b47e22d9e9d7205c52c3053aab7546ac",
-                "bytes_per_step": 128405211}  # FETCH x 1.9999 (8489.6 + 51821.8 + 1080.6 KiB) + WRITE x 1 (256.0 + 2089.1 + 272.0 KiB)
+STEP_TRAFFIC = {"sources_sha256": "332ec38c7fec9baafffa038beae9cf01dea54ae2fac3a28e2c14e7e04e8118d5",
+                "bytes_per_step": 128378691}  # FETCH x 1.9999 (8487.5 + 51811.2 + 1080.5 KiB) + WRITE x 1 (256.0 + 2088.8 + 272.0 KiB)
 STEP_SOURCES = ("sliding_window_attention_block_amd/csrc/decode.hip",
                 "sliding_window_attention_block_amd/csrc/select.hip",
                 "sliding_window_attention_block_amd/csrc/bsattn.cpp",
