@@ -496,7 +496,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the block-sparse attention path here has no "
-              "multi-GPU part (see the sharding notes in DESIGN.md); run with --gpus 1.",
+              "multi-GPU part (each GPU would hold whole (batch, K/V head) pairs and run this "
+              "same path on its share); run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 

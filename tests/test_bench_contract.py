@@ -1,0 +1,29 @@
+"""The measurement script's command-line contract, checked without a GPU: more
+than one GPU is refused with a message and exit status 2 before anything
+touches the device."""
+
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _run(args, env_extra=None):
+    env = dict(os.environ)
+    env.update(env_extra or {})
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], cwd=ROOT, env=env,
+                          capture_output=True, text=True, timeout=120)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = _run(["--gpus", "2"])
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and "--gpus 1" in r.stderr
+    assert r.stdout == ""
+
+
+def test_a_multi_rank_launch_is_refused():
+    r = _run(["--gpus", "1"], {"WORLD_SIZE": "4"})
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
