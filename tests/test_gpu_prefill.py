@@ -65,6 +65,13 @@ SMALL = [
     (_pw("dense_bidir", 1, 2, 1, 260, 128, -1, -1, False, seed=38), 0),
     (_pw("tiny_seq", 1, 2, 1, 7, 64, 3, 0, True, seed=39), 0),
     (_pw("lg_short_seq", 1, 2, 1, 100, 128, 8, 8, False, (5, 50, 99), seed=40), 3),
+    # the global-position limit (256: eight 32-row global tiles; most key tiles
+    # hold globals outside the band), and a d = 128 GQA case with 100 globals
+    (_pw("lg_max_globals", 1, 2, 1, 2048, 64, 32, 32, False,
+         tuple(int(p) for p in np.sort(np.random.default_rng(42).choice(2048, 256, replace=False))), seed=41), 0),
+    (_pw("lg_d128_100_globals", 1, 4, 2, 1600, 128, 48, 20, False,
+         tuple(int(p) for p in np.sort(np.random.default_rng(43).choice(1600, 100, replace=False))), seed=42,
+         scale_in=0.5), 5),
 ]
 
 
