@@ -316,3 +316,14 @@ def test_exact_selector_rejects_bad_arguments():
     assert _status(f, *args(K=FAKE + 8))[0] == 1              # misaligned
     assert _status(f, *args(k=0))[0] == 1
     assert _status(f, *args(nblk=3))[0] == 1
+
+
+def test_a_missing_library_raises_instead_of_falling_back(tmp_path, monkeypatch):
+    """The binding has no CPU fallback: without the built library every entry
+    point's loader raises, naming the missing file."""
+    import sliding_window_attention_block_amd._lib as L
+    missing = str(tmp_path / "libbsattn.so")
+    monkeypatch.setattr(L, "LIB_PATH", missing)
+    monkeypatch.setattr(L, "_lib", None)
+    with pytest.raises(OSError, match="is missing"):
+        L.load()
