@@ -22,7 +22,11 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbsattn.so")
 
-SOURCES = ["bsattn.cpp", "summaries.hip", "select.hip", "decode.hip", "prefill.hip"]
+# (source, extra flags): the VALU scorer is compiled once per head dimension and
+# query dtype, so its many instantiations build in parallel
+SOURCES = [("bsattn.cpp", ()), ("summaries.hip", ()), ("select.hip", ()), ("decode.hip", ()),
+           ("prefill.hip", ())] + [
+    ("select_valu.hip", (f"-DBSATTN_VALU_D={d}", f"-DBSATTN_VALU_BF16={bf}")) for d in (64, 128) for bf in (0, 1)]
 ARCH = "gfx950"
 CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -39,9 +43,15 @@ def hipcc():
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src):
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *CFLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+def _object(src, flags):
+    tag = "".join("_" + f.split("=")[1] for f in flags)
+    return os.path.join(BUILD, os.path.basename(src) + tag + ".o")
+
+
+def _compile(item):
+    src, flags = item
+    obj = _object(src, flags)
+    cmd = [hipcc(), *CFLAGS, *flags, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

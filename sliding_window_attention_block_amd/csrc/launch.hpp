@@ -95,6 +95,20 @@ struct SelectArgs {
   const void* K;
   int32_t kv_capacity;
 };
+// Splits `units` per pair over the resident wave slots: as few units per wave
+// as keeps every wave resident at once.
+inline void split_units(SelectArgs& a, long long units, int slots) {
+  const int n_pairs = a.batch * a.n_kv_heads;
+  long long c = (n_pairs * units + slots - 1) / slots;
+  if (c < 1) c = 1;
+  while (c < units && (long long)n_pairs * ((units + c - 1) / c) > slots) ++c;
+  a.per_wave = (int)c;
+  a.n_part = (int)((units + c - 1) / c);
+}
+// The VALU scorer (fp32 queries, means or factor rows): scores only, the caller
+// launches the top-k.  One object per (head dim, query dtype), select_valu.hip.
+template <int D, bool BF16>
+hipError_t launch_valu_scores(const SelectArgs& a, hipStream_t stream);
 hipError_t launch_prefill_select(const SelectArgs& a, hipStream_t stream);
 hipError_t launch_select_exact(const SelectArgs& a, hipStream_t stream);  // K, kv_capacity set
 constexpr int kSparseTile = 128;      // query rows per selection tile (the prefill workgroup)
