@@ -65,6 +65,10 @@ def step_traffic():
     if STEP_TRAFFIC["sources_sha256"] == step_sources_sha256():
         return STEP_TRAFFIC["bytes_per_step"]
     return None
+# HBM bytes per launch of the prefill kernels (rocprofv3 --pmc FETCH_SIZE and
+# WRITE_SIZE, calibrated as above), keyed by workload; absent until taken on the
+# current sources
+PREFILL_TRAFFIC = {}
 BF16_PEAK = 2.5e15         # flop/s, MI355X dense bf16 MFMA
 MALL_BYTES = 256 << 20
 METRIC = "sparse-decode tokens/s and gathered-KV GB/s (% HBM peak); prefill % MFMA peak"
@@ -73,6 +77,50 @@ HEADLINE = "first_order_decode_32k"
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def dist(samples):
+    """Median and 10th / 90th percentiles of a list of durations (ms)."""
+    a = np.asarray(samples, dtype=np.float64)
+    return dict(median=float(np.median(a)), p10=float(np.percentile(a, 10)), p90=float(np.percentile(a, 90)),
+                n=int(a.size))
+
+
+def gpu_state():
+    """Power cap and graphics clocks as the driver reports them (amd-smi / rocm-smi),
+    read right after a timed region so the clock is the one the work ran at."""
+    import re
+    import subprocess
+    out = {}
+
+    def run(cmd):
+        try:
+            return subprocess.run(cmd, capture_output=True, text=True, timeout=20).stdout
+        except Exception:  # noqa: BLE001
+            return ""
+    try:
+        m = json.loads(run(["amd-smi", "metric", "-p", "-c", "--json"]) or "null")
+        g = m[0] if isinstance(m, list) else (m.get("gpu_data", [m])[0] if isinstance(m, dict) else None)
+        if g:
+            clk = g.get("clock", {})
+            gfx = [v for k, v in clk.items() if k.lower().startswith("gfx")]
+            cur = [float(v["clk"]["value"]) for v in gfx if isinstance(v.get("clk"), dict)]
+            mx = [float(v["max_clk"]["value"]) for v in gfx if isinstance(v.get("max_clk"), dict)]
+            if cur:
+                out["gfx_clk_MHz_now"] = dict(min=min(cur), max=max(cur))
+            if mx:
+                out["gfx_clk_MHz_max"] = max(mx)
+            pw = g.get("power", {})
+            sp = pw.get("socket_power")
+            if isinstance(sp, dict):
+                out["socket_power_W_now"] = float(sp["value"])
+    except Exception:  # noqa: BLE001
+        pass
+    txt = run(["rocm-smi", "--showmaxpower"])
+    mm = re.search(r"Max Graphics Package Power \(W\):\s*([0-9.]+)", txt)
+    if mm:
+        out["power_cap_W"] = float(mm.group(1))
+    return out
 
 
 # ----------------------------------------------------------------------------- models
@@ -106,7 +154,9 @@ def prefill_pairs(N, wl, wr, causal, global_pos):
 
 
 def replicas_for(step_bytes):
-    return max(2, int(np.ceil(2 * MALL_BYTES / max(step_bytes, 1))) + 1)
+    # at most 64: a step that small (the tiny workload) is bound by latency, not by
+    # where its bytes come from
+    return min(64, max(2, int(np.ceil(2 * MALL_BYTES / max(step_bytes, 1))) + 1))
 
 
 # ----------------------------------------------------------------------------- decode
@@ -127,8 +177,38 @@ def to_pages(torch, X, page_tokens, perm):
     return pool
 
 
+def bench_append(api, torch, w, rp, shape_step, mean_dtype, fp4, basis, steps):
+    """bsattn_append_kv latency: the token that completes a block for every (b, K/V
+    head) pair (the copy, then that block's summary: mean, and rank-r factor when
+    r > 0), and a token that completes none (the copy alone).  Per-call HIP events."""
+    B, Hq, Hkv, d, n = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_ctx
+    nb = n // 64
+    assert n % 64 == 0
+    Knew = rp["K"][:, :, n - 1].contiguous() if rp["pg"] is None else rp["K"][0, :, 0].expand(B, Hkv, d).contiguous()
+    Vnew = Knew.clone()
+    out = {}
+    for label, m in (("completes_block", n), ("no_block", n - 1)):
+        shape = api.make_shape(B, Hq, Hkv, d, m, dtype=w.dtype)
+        def call():
+            api.bsattn_append_kv(shape, Knew, Vnew, rp["K"], rp["V"], w.rank, nb, rp["mean"], rp["factor"],
+                                 factor_scale=rp["fscale"], basis=basis, paged=rp["pg"])
+        for _ in range(3):
+            call()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(max(10, min(steps, 50)))]
+        torch.cuda.synchronize()
+        for e0, e1 in evs:
+            e0.record()
+            call()
+            e1.record()
+        torch.cuda.synchronize()
+        out[label] = dist([a.elapsed_time(b) for a, b in evs])
+    out["pairs"] = B * Hkv
+    return out
+
+
 def bench_decode(api, torch, w, x, steps, warmup, mean_dtype="bf16", factor_fp4=True, subspace=True,
-                 page_tokens=None):
+                 page_tokens=None, append_rows=False):
     B, Hq, Hkv, d, n, S = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_ctx, w.block_size
     nb = n // S
     shape = api.make_shape(B, Hq, Hkv, d, n, dtype=w.dtype)
@@ -246,6 +326,9 @@ def bench_decode(api, torch, w, x, steps, warmup, mean_dtype="bf16", factor_fp4=
         g.replay()  # untimed: the first replay of a graph uploads it
     torch.cuda.synchronize()
     ms_step, wall_step = timed_replay(g_step)
+    # distribution: further replays of the same K-step graph (per-step mean of each)
+    step_dist = dist([timed_replay(g_step)[0] for _ in range(10)])
+    state = gpu_state()
     two_ms, _ = timed_replay(g_two)
     sel_ms, _ = timed_replay(g_sel)
     dec_ms, _ = timed_replay(g_dec)
@@ -257,16 +340,20 @@ def bench_decode(api, torch, w, x, steps, warmup, mean_dtype="bf16", factor_fp4=
         step(reps[i % R])
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) * 1e3 / steps
+    append = None
+    if append_rows:
+        append = bench_append(api, torch, w, reps[0], shape, mean_dtype, fp4, basis, steps)
     res = dict(
         workload=w.name, mean_dtype=mean_dtype, factor="fp4" if fp4 else ("f32" if w.rank else None),
         sub_dim=sub or None, page_tokens=page_tokens,
-        ms_per_step=ms_step, wall_ms_per_step=wall_step,
+        ms_per_step=ms_step, wall_ms_per_step=wall_step, step_ms_dist=step_dist, gpu_state=state,
         tokens_per_s=B / (ms_step * 1e-3),
         eager_ms_per_step=eager_ms, two_call_ms_per_step=two_ms, replicas=R, attended_tokens=tokens,
         gathered_kv_bytes=kv_bytes, select_ms=sel_ms, decode_ms=dec_ms,
         select_bytes=sel_bytes, decode_bytes=kv_bytes + io_bytes,
         summary_build_ms=float(np.median(build_ms)),
         summary_build_bytes=B * Hkv * nb * S * d * elem + summ_bytes,
+        append=append,
     )
     res["gathered_kv_GBps"] = kv_bytes / (dec_ms * 1e-3) / 1e9
     res["gathered_kv_frac_hbm"] = res["gathered_kv_GBps"] * 1e9 / HBM_PEAK
@@ -379,6 +466,15 @@ def bench_sparse_prefill(api, torch, w, x, steps, warmup):
         return e0.elapsed_time(e1) / steps
 
     step_ms = timed(step)
+    attend_samples = []
+    for i in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        attend(reps[i % R])
+        e1.record()
+        attend_samples.append((e0, e1))
+    torch.cuda.synchronize()
+    attend_dist = dist([a.elapsed_time(b) for a, b in attend_samples])
     attend_ms = timed(attend)
     select_ms = timed(select)
     summ_ms = timed(summaries)
@@ -386,7 +482,11 @@ def bench_sparse_prefill(api, torch, w, x, steps, warmup):
                summaries_ms=summ_ms, attended_pairs=keys, gflop=flops / 1e9,
                tflops=flops / (step_ms * 1e-3) / 1e12, attend_tflops=flops / (attend_ms * 1e-3) / 1e12,
                attend_frac_mfma=flops / (attend_ms * 1e-3) / BF16_PEAK, replicas=R,
-               window=wl + 1, sinks=ns, top_k=k)
+               window=wl + 1, sinks=ns, top_k=k, attend_ms_dist=attend_dist,
+               roofline=dict(bound="mfma", kernel="the sparse attention launch (prefill_kernel, block-sparse)",
+                             achieved=flops / (attend_ms * 1e-3) / 1e12, peak=BF16_PEAK / 1e12, unit="TFLOP/s",
+                             frac=flops / (attend_ms * 1e-3) / BF16_PEAK, traffic=PREFILL_TRAFFIC.get(w.name),
+                             flop_per_launch=flops, avg_launch_ms=attend_ms))
     del reps
     torch.cuda.empty_cache()
     return res
@@ -424,16 +524,65 @@ def bench_prefill(api, torch, w, x, steps, warmup):
         evs[i][1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    k_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    per_call = [a.elapsed_time(b) for a, b in evs]
+    k_ms = float(np.mean(per_call))
+    state = gpu_state()
     pairs = prefill_pairs(N, w.window_left, w.window_right, w.causal, g)
     flops = 4.0 * d * pairs * B * Hq
     del reps
     torch.cuda.empty_cache()
-    return dict(workload=w.name, kernel_ms=k_ms, wall_ms_per_call=(t1 - t0) * 1e3 / steps,
-                pairs_per_head=pairs, gflop=flops / 1e9, tflops=flops / (k_ms * 1e-3) / 1e12,
-                frac_mfma=flops / (k_ms * 1e-3) / BF16_PEAK, io_bytes=io,
-                hbm_GBps=io / (k_ms * 1e-3) / 1e9, frac_hbm=io / (k_ms * 1e-3) / HBM_PEAK,
-                replicas=R)
+    res = dict(workload=w.name, kernel_ms=k_ms, kernel_ms_dist=dist(per_call), wall_ms_per_call=(t1 - t0) * 1e3 / steps,
+               pairs_per_head=pairs, gflop=flops / 1e9, tflops=flops / (k_ms * 1e-3) / 1e12,
+               frac_mfma=flops / (k_ms * 1e-3) / BF16_PEAK, io_bytes=io,
+               hbm_GBps=io / (k_ms * 1e-3) / 1e9, frac_hbm=io / (k_ms * 1e-3) / HBM_PEAK,
+               replicas=R, gpu_state=state)
+    # the bound is the larger of the two ideal times: MFMA flops at the bf16 peak, or
+    # the inputs and fp32 outputs at the HBM peak
+    if flops / BF16_PEAK >= io / HBM_PEAK:
+        res["roofline"] = dict(bound="mfma", achieved=flops / (k_ms * 1e-3) / 1e12, peak=BF16_PEAK / 1e12,
+                               unit="TFLOP/s", frac=flops / (k_ms * 1e-3) / BF16_PEAK,
+                               traffic=PREFILL_TRAFFIC.get(w.name), flop_per_launch=flops, avg_launch_ms=k_ms)
+    else:
+        res["roofline"] = dict(bound="hbm", achieved=io / (k_ms * 1e-3) / 1e9, peak=HBM_PEAK / 1e9, unit="GB/s",
+                               frac=io / (k_ms * 1e-3) / HBM_PEAK, traffic=PREFILL_TRAFFIC.get(w.name),
+                               bytes_per_launch=io, avg_launch_ms=k_ms,
+                               mfma_frac=flops / (k_ms * 1e-3) / BF16_PEAK)
+    return res
+
+
+def traffic_ratios(results):
+    """The COBS explainer's traffic comparison (technical summary 4.1: COBS reads
+    about 1.21x the first-order selector's bytes and dense attention 15.15x COBS's)
+    computed from this byte model at the 128K shape: per decode step, the summaries
+    read by the selector plus the K/V rows gathered, with the COBS workload's own
+    token set (the same k, window and sinks for both selectors).  First order: bf16
+    means; COBS: bf16 means + FP4 rank-4 rows in the 96-dim query subspace (scales
+    included) + the basis; dense: every K/V row of the context.  The pages' numbers
+    come from a trained model on RULER; these are the same ratios for our shapes."""
+    c = results.get("cobs_decode_128k")
+    if not c:
+        return None
+    from synthetic import WORKLOADS
+    w = WORKLOADS["cobs_decode_128k"]
+    B, Hkv, Hq, d, n, r = w.batch, w.n_kv_heads, w.n_q_heads, w.head_dim, w.n_ctx, w.rank
+    nb = n // w.block_size
+    s = w.sub_dim
+    mean_b = B * Hkv * nb * d * 2
+    fac_b = B * Hkv * nb * r * (s // 2 + 4) + Hkv * s * d * 4
+    kv = c["gathered_kv_bytes"]
+    q_o = B * Hq * d * 2 + B * Hq * (d + 1) * 4
+    first = mean_b + kv + q_o
+    cobs = mean_b + fac_b + kv + q_o
+    dense = B * Hkv * n * d * 2 * 2 + q_o
+    out = dict(shape="cobs_decode_128k", first_order_bytes=first, cobs_bytes=cobs, dense_bytes=dense,
+               cobs_over_first_order=cobs / first, dense_over_cobs=dense / cobs,
+               pages=dict(cobs_over_first_order=1.21, dense_over_cobs=15.15))
+    h = results.get(HEADLINE)
+    if h:
+        wh = WORKLOADS[HEADLINE]
+        dense_h = wh.batch * wh.n_kv_heads * wh.n_ctx * wh.head_dim * 2 * 2
+        out["first_order_32k_dense_over_step"] = dense_h / h["step_bytes"]
+    return out
 
 
 # ----------------------------------------------------------------------------- CPU baseline
@@ -503,7 +652,7 @@ def main():
 
     import torch
     import sliding_window_attention_block_amd as api
-    from synthetic import WORKLOADS, make_decode_inputs, make_prefill_inputs
+    from synthetic import WORKLOADS, DecodeWorkload, make_decode_inputs, make_prefill_inputs
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     api.library()
@@ -515,17 +664,20 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] calibration copies done: 3 x {CALIB_BYTES} bytes")
         del src, dst
-    names = [args.only] if args.only else [HEADLINE, "cobs_decode_128k", "swa_prefill_8k",
+    names = [args.only] if args.only else [HEADLINE, "cobs_decode_128k", "tiny_decode_1k", "swa_prefill_8k",
                                             "local_global_prefill_16k", "sparse_prefill_8k"]
     results = {}
     inputs = {}
     for name in names:
         w = WORKLOADS[name]
+        decode = isinstance(w, DecodeWorkload)
         t = time.perf_counter()
-        x = make_decode_inputs(w) if name.endswith(("32k", "128k")) else make_prefill_inputs(w)
+        x = make_decode_inputs(w) if decode else make_prefill_inputs(w)
         log(f"[bench] {name}: inputs generated in {time.perf_counter() - t:.1f} s")
-        if name.endswith(("32k", "128k")):
-            results[name] = bench_decode(api, torch, w, x, args.steps, args.warmup)
+        if decode and w.dtype == "f32":  # the tiny fp32 workload: latency only
+            results[name] = bench_decode(api, torch, w, x, args.steps, args.warmup, mean_dtype="f32")
+        elif decode:
+            results[name] = bench_decode(api, torch, w, x, args.steps, args.warmup, append_rows=True)
             if name == HEADLINE:  # context: fp32 block means; a paged cache of 4 KB pages
                 results[name + "/fp32_means"] = bench_decode(api, torch, w, x, args.steps, args.warmup,
                                                              mean_dtype="f32")
@@ -539,6 +691,10 @@ def main():
                                                                   subspace=False)
                 results[name + "/fp32_factors"] = bench_decode(api, torch, w, x, args.steps, args.warmup,
                                                                factor_fp4=False)
+                # the configuration's own fp32 summaries (fp32 mean and fp32 rank-r rows)
+                results[name + "/fp32_summaries"] = bench_decode(api, torch, w, x, args.steps, args.warmup,
+                                                                 mean_dtype="f32", factor_fp4=False,
+                                                                 append_rows=True)
         elif w.top_k > 0:
             results[name] = bench_sparse_prefill(api, torch, w, x, args.steps, args.warmup)
         else:
@@ -591,6 +747,7 @@ def main():
             "avg_launch_ms": h["ms_per_step"],
         },
         "cpu_baseline": cpu,
+        "traffic_ratios": traffic_ratios(results),
         "rows": results,
     }
     print(json.dumps(line))

@@ -61,7 +61,8 @@ typedef enum {
   BSATTN_ERR_INVALID = 1,     /* argument out of range, NULL, inconsistent shape  */
   BSATTN_ERR_UNSUPPORTED = 2, /* valid request this build does not implement       */
   BSATTN_ERR_HIP = 3,         /* a HIP launch or runtime call failed               */
-  BSATTN_ERR_WORKSPACE = 4    /* workspace missing or smaller than required        */
+  BSATTN_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required        */
+  BSATTN_STATUS_INT32 = 0x7fffffff /* not a status: keeps every int32 value in range */
 } bsattn_status;
 
 typedef enum {
@@ -89,10 +90,12 @@ typedef struct {
  * block_table[b * max_pages + t / page_tokens], the same page number for every
  * K/V head.  page_tokens: 16, 32 or 64 (16 tokens of bf16 at d = 128 is a
  * 4 KB page per head).  block_table: device int32 [B, max_pages]; entries for
- * tokens < n_ctx must be page numbers in [0, n_pages) (the kernels clamp every
+ * tokens < n_ctx must be page numbers in [0, n_pages).  Reads clamp every
  * entry into that range, so a bad entry reads a wrong row, never outside the
- * pools).  With a paged cache shape.kv_capacity must equal max_pages *
- * page_tokens.  Calls that take a `paged` argument use the contiguous layout
+ * pools; bsattn_append_kv writes nothing for an entry outside it (an
+ * unallocated page), so a bad entry never overwrites another sequence's page.
+ * With a paged cache shape.kv_capacity must equal max_pages * page_tokens.
+ * Calls that take a `paged` argument use the contiguous layout
  * [B, Hkv, kv_capacity, d] when it is NULL.  The sparse decode reads paged
  * caches in BF16 only.
  */

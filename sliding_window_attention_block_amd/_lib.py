@@ -10,7 +10,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libbsattn.so")
+# BSATTN_LIBRARY names another build of the same library (the host-sanitizer
+# build the CPU tests load); there is no other implementation to fall back to
+LIB_PATH = os.environ.get("BSATTN_LIBRARY") or os.path.join(_HERE, "libbsattn.so")
 
 BSATTN_OK = 0
 BSATTN_ERR_INVALID = 1

@@ -332,6 +332,7 @@ const char* bsattn_status_string(bsattn_status st) {
     case BSATTN_ERR_UNSUPPORTED: return "unsupported configuration";
     case BSATTN_ERR_HIP: return "HIP error";
     case BSATTN_ERR_WORKSPACE: return "workspace too small";
+    default: break;
   }
   return "unknown status";
 }
