@@ -266,6 +266,32 @@ bsattn_status bsattn_decode_step(const bsattn_shape* shape, const void* Q, const
                                  const bsattn_paged_kv* paged, void* hip_stream);
 
 /*
+ * bsattn_decode_step without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments, outputs and limits as
+ * bsattn_decode_step, with the split partials kept in a static device array of
+ * BSATTN_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs on
+ * until the process ends (its address is looked up once per device, on the
+ * first call with that device current).  A call whose partials would exceed it
+ * (bsattn_decode_workspace_bytes(shape, top_k, window, n_sink, n_global) >
+ * BSATTN_NOALLOC_SCRATCH_BYTES) returns BSATTN_ERR_WORKSPACE and launches
+ * nothing.  The call allocates nothing.  Every call on one device shares that
+ * device's array: calls that overlap on one device (different streams without
+ * ordering) race and give undefined results; calls ordered on a stream are
+ * safe (the partials need no initialisation: each call writes every partial
+ * it reads).
+ */
+#define BSATTN_NOALLOC_SCRATCH_BYTES (16u << 20)
+bsattn_status bsattn_decode_step_noalloc(const bsattn_shape* shape, const void* Q, const void* K,
+                                         const void* V, const void* mean, int32_t mean_dtype,
+                                         const void* factor, int32_t factor_dtype,
+                                         const float* factor_scale, const float* basis, int32_t sub_dim,
+                                         int32_t rank, int32_t nblk_capacity, int32_t top_k,
+                                         int32_t window, int32_t n_sink, const int32_t* global_pos_host,
+                                         int32_t n_global, int32_t* sel, float* scores, float* O,
+                                         float* lse, const bsattn_paged_kv* paged, void* hip_stream);
+
+/*
  * Masked prefill attention, BF16 Q/K/V, fp32 O and lse.  Query i sees key j iff
  *   (i - window_left <= j <= i + window_right) [and j <= i when causal]
  *   or i is a global position or j is a global position.

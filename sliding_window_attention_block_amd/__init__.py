@@ -13,16 +13,18 @@ import ctypes
 import math
 
 from . import _lib
-from ._lib import BSATTN_BF16, BSATTN_F32, BSATTN_FP4_E2M1, PagedKV, Shape
+from ._lib import BSATTN_BF16, BSATTN_F32, BSATTN_FP4_E2M1, BSATTN_NOALLOC_SCRATCH_BYTES, PagedKV, Shape
 
 __all__ = [
     "BsattnError", "Shape", "PagedKV", "make_shape", "paged_kv", "library", "bsattn_build_summaries",
     "bsattn_append_kv", "bsattn_select_prefill", "bsattn_sparse_prefill", "bsattn_select_exact",
     "bsattn_select_topk", "bsattn_decode_workspace_bytes", "bsattn_decode",
     "bsattn_decode_step",
+    "bsattn_decode_step_noalloc",
     "bsattn_prefill",
     "bsattn_prefill_workspace_bytes",
     "bsattn_status_string", "bsattn_version", "BSATTN_F32", "BSATTN_BF16", "BSATTN_FP4_E2M1",
+    "BSATTN_NOALLOC_SCRATCH_BYTES",
 ]
 
 
@@ -197,6 +199,20 @@ def bsattn_decode_step(shape, Q, K, V, mean, factor, rank, nblk_capacity, top_k,
                                         nblk_capacity, top_k, window, n_sink, g, ng, _ptr(sel),
                                         _ptr(scores), _ptr(O), _ptr(lse), _ptr(workspace), ws_bytes,
                                         _paged(paged), _stream(stream)))
+
+
+def bsattn_decode_step_noalloc(shape, Q, K, V, mean, factor, rank, nblk_capacity, top_k, window, n_sink,
+                               global_pos, sel, scores, O, lse, stream=None, factor_scale=None, basis=None,
+                               paged=None):
+    """bsattn_decode_step with the split partials in the library's static device scratch
+    (no workspace argument; the call allocates nothing)."""
+    g, ng = _globals(global_pos)
+    _check(library().bsattn_decode_step_noalloc(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), _ptr(mean),
+                                                _mean_dtype(mean), _ptr(factor),
+                                                _factor_dtype(factor, factor_scale), _ptr(factor_scale),
+                                                _ptr(basis), _sub_dim(basis), rank,
+                                                nblk_capacity, top_k, window, n_sink, g, ng, _ptr(sel),
+                                                _ptr(scores), _ptr(O), _ptr(lse), _paged(paged), _stream(stream)))
 
 
 def bsattn_prefill_workspace_bytes(shape, n_global):

@@ -22,6 +22,7 @@ BSATTN_ERR_WORKSPACE = 4
 BSATTN_F32 = 0
 BSATTN_BF16 = 1
 BSATTN_FP4_E2M1 = 2
+BSATTN_NOALLOC_SCRATCH_BYTES = 16 << 20  # include/bsattn.h: the allocation-free step's scratch
 
 EXPORTS = (
     "bsattn_build_summaries",
@@ -33,6 +34,7 @@ EXPORTS = (
     "bsattn_decode_workspace_bytes",
     "bsattn_decode",
     "bsattn_decode_step",
+    "bsattn_decode_step_noalloc",
     "bsattn_prefill",
     "bsattn_prefill_workspace_bytes",
     "bsattn_status_string",
@@ -106,6 +108,10 @@ def load():
                                        _i32, _i32, _i32, _i32, _i32, _pi32, _i32, _vp, _vp, _vp, _vp,
                                        _vp, ctypes.c_size_t, _ppaged, _vp]
     lib.bsattn_decode_step.restype = _st
+    lib.bsattn_decode_step_noalloc.argtypes = [_pshape, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32,
+                                               _i32, _i32, _i32, _i32, _i32, _pi32, _i32, _vp, _vp, _vp, _vp,
+                                               _ppaged, _vp]
+    lib.bsattn_decode_step_noalloc.restype = _st
     lib.bsattn_prefill.argtypes = [_pshape, _vp, _vp, _vp, _i32, _i32, _i32, _pi32, _i32,
                                    _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.bsattn_prefill.restype = _st

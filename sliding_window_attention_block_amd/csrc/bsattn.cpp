@@ -13,6 +13,7 @@
 #include "launch.hpp"
 
 static_assert(bsattn::kMaxTopK == BSATTN_MAX_TOP_K, "device top-k limit matches the header");
+static_assert(bsattn::kNoAllocScratchBytes == BSATTN_NOALLOC_SCRATCH_BYTES, "scratch size matches the header");
 static_assert(bsattn::kMaxBlocks == BSATTN_MAX_BLOCKS, "device block limit matches the header");
 static_assert(bsattn::kSparseTile == BSATTN_SPARSE_TILE && bsattn::kSparseMaxTopK == BSATTN_SPARSE_MAX_TOP_K &&
                   bsattn::kSparseMaxSink == BSATTN_SPARSE_MAX_SINK,
@@ -557,6 +558,38 @@ bsattn_status bsattn_decode_step(const bsattn_shape* shape, const void* Q, const
   e = bsattn::launch_decode(da, (hipStream_t)hip_stream);
   if (e != hipSuccess) return fail(BSATTN_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return BSATTN_OK;
+}
+
+bsattn_status bsattn_decode_step_noalloc(const bsattn_shape* shape, const void* Q, const void* K,
+                                         const void* V, const void* mean, int32_t mean_dtype,
+                                         const void* factor, int32_t factor_dtype, const float* factor_scale,
+                                         const float* basis, int32_t sub_dim, int32_t rank,
+                                         int32_t nblk_capacity, int32_t top_k, int32_t window, int32_t n_sink,
+                                         const int32_t* global_pos_host, int32_t n_global, int32_t* sel,
+                                         float* scores, float* O, float* lse, const bsattn_paged_kv* paged,
+                                         void* hip_stream) {
+  g_err[0] = 0;
+  // the split partials this call needs, checked against the fixed scratch
+  // before anything else touches the device
+  const bsattn_status st = check_shape(shape, true);
+  if (st != BSATTN_OK) return st;
+  if (top_k < 1 || top_k > BSATTN_MAX_TOP_K || window < 0 || n_sink < 0 || n_global < 0 ||
+      n_global > BSATTN_MAX_GLOBAL)
+    return fail(BSATTN_ERR_INVALID, "top_k, window, n_sink or n_global out of range");
+  const size_t need = decode_workspace_bound(shape, top_k, window, n_sink, n_global);
+  if (need > bsattn::kNoAllocScratchBytes)
+    return fail(BSATTN_ERR_WORKSPACE,
+                "the split partials need %zu bytes, more than the %zu-byte static scratch of the allocation-free "
+                "step: use bsattn_decode_step with a workspace",
+                need, bsattn::kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    hipError_t e = bsattn::noalloc_scratch(&ws);
+    if (e != hipSuccess) return fail(BSATTN_ERR_HIP, "scratch address: %s", hipGetErrorString(e));
+  }
+  return bsattn_decode_step(shape, Q, K, V, mean, mean_dtype, factor, factor_dtype, factor_scale, basis, sub_dim,
+                            rank, nblk_capacity, top_k, window, n_sink, global_pos_host, n_global, sel, scores, O,
+                            lse, ws, need, paged, hip_stream);
 }
 
 bsattn_status bsattn_select_prefill(const bsattn_shape* shape, const void* Q, const void* mean,

@@ -44,6 +44,8 @@
 // small second kernel merges the partials (the kernel boundary makes every
 // partial visible without any L2 write-back inside the hot kernel; the L2s of
 // the 8 XCDs are not coherent with each other).
+#include <mutex>
+
 #include "launch.hpp"
 
 namespace bsattn {
@@ -821,6 +823,33 @@ void decode_split_geometry(int n_items, int n_pairs, int head_dim, bool bf16, in
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   return a.head_dim == 64 ? launch_t<64>(a, stream) : launch_t<128>(a, stream);
+}
+
+// Scratch of the allocation-free decode step: the split partials live in this
+// file-scope device array instead of a caller workspace.  A __device__ variable
+// exists once per device the code object is loaded on, at that device's own
+// address; host code must never pass the array's name to a kernel (in host code
+// it is only a stand-in for the symbol), only the address hipGetSymbolAddress
+// returns for the current device, looked up once per device and kept.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // with `dev` current
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace bsattn

@@ -168,6 +168,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 // `half_items` half items per wave and `n_part` waves per pair; fp32: one item
 // per wave, `n_part` workgroups per pair.
 void decode_split_geometry(int n_items, int n_pairs, int head_dim, bool bf16, int* half_items, int* n_part);
+// The allocation-free decode step's scratch (split partials): a device array of
+// this many bytes per device; *ptr = its address on the current device.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+hipError_t noalloc_scratch(void** ptr);
 constexpr int kDecodeWaves = 4;  // waves per decode workgroup
 // bf16 decode waves resident at once on 256 CUs: 4 per CU at d = 128, 8 at d = 64
 constexpr int decode_slots(int head_dim) { return head_dim == 128 ? 1024 : 2048; }

@@ -24,7 +24,7 @@ def _header_functions():
 def test_library_exports_every_declared_function():
     lib = api.library()
     declared = _header_functions()
-    assert len(declared) == 14
+    assert len(declared) == 15
     for name in declared:
         assert hasattr(lib, name), name
     assert set(declared) == set(_lib.EXPORTS)
@@ -327,3 +327,22 @@ def test_a_missing_library_raises_instead_of_falling_back(tmp_path, monkeypatch)
     monkeypatch.setattr(L, "_lib", None)
     with pytest.raises(OSError, match="is missing"):
         L.load()
+
+
+def test_noalloc_step_checks_its_arguments_and_the_scratch_limit():
+    """bsattn_decode_step_noalloc: the decode step's argument checks, and a problem
+    whose split partials pass the static scratch is refused (BSATTN_ERR_WORKSPACE)
+    before any device call."""
+    lib = _lib.load()
+    assert _lib.BSATTN_NOALLOC_SCRATCH_BYTES == 16 << 20
+    s = _lib.Shape(64, 1024, 64, 128, 4096 * 64, 4096 * 64, 64, 0.0, _lib.BSATTN_BF16)
+    p = ctypes.c_void_p(16)
+    assert lib.bsattn_decode_workspace_bytes(ctypes.byref(s), 64, 512, 64, 0) > _lib.BSATTN_NOALLOC_SCRATCH_BYTES
+    st = lib.bsattn_decode_step_noalloc(ctypes.byref(s), p, p, p, p, 1, None, 0, None, None, 0, 0, 4096, 64, 512,
+                                        64, None, 0, p, p, p, p, None, None)
+    assert st == _lib.BSATTN_ERR_WORKSPACE
+    assert b"static scratch" in lib.bsattn_last_error()
+    bad = _lib.Shape(1, 3, 2, 128, 100, 100, 64, 0.0, _lib.BSATTN_BF16)  # Hq not a multiple of Hkv
+    st = lib.bsattn_decode_step_noalloc(ctypes.byref(bad), p, p, p, p, 1, None, 0, None, None, 0, 0, 1, 4, 0,
+                                        0, None, 0, p, p, p, p, None, None)
+    assert st == _lib.BSATTN_ERR_INVALID
