@@ -69,6 +69,7 @@ struct RowState {
 // Copy rows [0, 64) of a K/V stage into LDS tiles with 1 KB DMA instructions.
 // `row_pos(r)` is the token position of tile row r (already clamped into range).
 // Wave `wid` of `nw` issues its share of the chunks.
+// kt (vt) may be null: that tile is not copied.
 template <int D, typename RowPos>
 __device__ __forceinline__ void dma_stage(const uint16_t* Kb, const uint16_t* Vb, uint8_t* kt, uint8_t* vt,
                                           int wid, int nw, RowPos row_pos) {
@@ -80,10 +81,12 @@ __device__ __forceinline__ void dma_stage(const uint16_t* Kb, const uint16_t* Vb
     const int off = 1024 * k + 16 * lane;
     const int r = off / T::RB, pc = (off % T::RB) >> 4;
     const size_t pos = (size_t)row_pos(r);
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(Kb + pos * D + (pc ^ T::k_swz(r)) * 8),
-                                     (lds_void*)(kt + 1024 * k), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(Vb + pos * D + (pc ^ T::v_swz(r)) * 8),
-                                     (lds_void*)(vt + 1024 * k), 16, 0, 0);
+    if (kt != nullptr)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(Kb + pos * D + (pc ^ T::k_swz(r)) * 8),
+                                       (lds_void*)(kt + 1024 * k), 16, 0, 0);
+    if (vt != nullptr)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(Vb + pos * D + (pc ^ T::v_swz(r)) * 8),
+                                       (lds_void*)(vt + 1024 * k), 16, 0, 0);
   }
 }
 
@@ -105,18 +108,24 @@ struct DmaLane {
       v[i] = (uint32_t)(r * T::RB + ((pc ^ T::v_swz(r)) << 4));
     }
   }
-  // copy rows [row0, row0 + 64) of K and V (all < the sequence length)
+  // copy rows [row0, row0 + 64) of K and V (all < the sequence length); a null
+  // destination tile is not copied
   __device__ __forceinline__ void issue(const uint8_t* Kb, const uint8_t* Vb, int row0, uint8_t* kt, uint8_t* vt,
                                         int wid) const {
     typedef __attribute__((address_space(3))) void lds_void;
     const uint8_t* ks = Kb + (size_t)row0 * Tile<D>::RB;
     const uint8_t* vs = Vb + (size_t)row0 * Tile<D>::RB;
+    if (kt != nullptr) {
 #pragma unroll
-    for (int i = 0; i < NW; ++i) {
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(ks + k[i]), (lds_void*)(kt + 1024 * (wid + 4 * i)),
-                                       16, 0, 0);
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(vs + v[i]), (lds_void*)(vt + 1024 * (wid + 4 * i)),
-                                       16, 0, 0);
+      for (int i = 0; i < NW; ++i)
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(ks + k[i]), (lds_void*)(kt + 1024 * (wid + 4 * i)),
+                                         16, 0, 0);
+    }
+    if (vt != nullptr) {
+#pragma unroll
+      for (int i = 0; i < NW; ++i)
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(vs + v[i]), (lds_void*)(vt + 1024 * (wid + 4 * i)),
+                                         16, 0, 0);
     }
   }
 };
@@ -248,6 +257,134 @@ __device__ __forceinline__ void stage(const uint8_t* kt, const uint8_t* vt, cons
         if constexpr (COMP) oacc[dt] = mfma32x32x16(as_bf16x8(vop), as_bf16x8(plo[kc]), oacc[dt]);
       }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Software-pipelined band stages.  A wave's work per 64-key stage j is: S_j =
+// K_j Q^T (16 MFMAs at d = 128), the row max of S_j, P_j = exp2(S_j - m) with
+// its row sums (VALU), and O += V_j P_j (16 MFMAs).  Run in that order each
+// stage is a chain the MFMA and VALU pipes take in turns.  Here stage j's
+// exponentials are issued between the MFMAs of S_{j+1} = K_{j+1} Q^T (region
+// A), and S_{j+1}'s row max between the MFMAs of O += V_j P_j (region B), so
+// one wave keeps both pipes busy: each region is straight-line code and the
+// instruction order inside it is fixed with sched_group_barrier.  A stage on a
+// mask edge applies its mask between the two regions (a wave-uniform branch);
+// the rescale of O when a row max grows past the headroom follows region B.
+
+#define BSATTN_SGB(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
+constexpr int kSgMfma = 0x008, kSgValu = 0x002, kSgDsRead = 0x100;
+
+// Region A.  QK: sn = K Q^T from the K tile kt (both 32-key halves).  Always:
+// P of the stage held in s (logits, log2 domain after the fold of sl2 into the
+// exponent's argument): bf16 hi parts in pop (lo parts in plo when COMP) and
+// the row sums of what the P.V product will see, added to psum.
+template <int D, bool COMP, bool QK, bool EXP>
+__device__ __forceinline__ void region_a(const uint8_t* kt, const u32x4* qop, f32x16 (&sn)[2], const f32x16 (&s)[2],
+                                         float sl2, float nm, u32x4 (&pop)[2][2], u32x4 (&plo)[2][2], float& psum) {
+  using T = Tile<D>;
+  const int lane = threadIdx.x & 63;
+  const int r32 = lane & 31, h2 = lane >> 5;
+  if constexpr (QK) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sn[u][e] = 0.f;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const u32x4 k = *reinterpret_cast<const u32x4*>(kt + T::k_off(32 * u + r32, 2 * c + h2));
+        sn[u] = mfma32x32x16(as_bf16x8(k), as_bf16x8(qop[c]), sn[u]);
+      }
+  }
+  if constexpr (EXP) {
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[u][8 * kc + 2 * i], sl2, nm));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[u][8 * kc + 2 * i + 1], sl2, nm));
+        const uint32_t pk = cvt_pk_bf16(p0, p1);
+        pop[u][kc][i] = pk;
+        if constexpr (COMP) {
+          plo[u][kc][i] = cvt_pk_bf16(p0 - bf16lo(pk), p1 - bf16hi(pk));
+          psum += p0 + p1;
+        } else {
+          psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), kOnesBf16x2, psum, false);
+        }
+      }
+  }
+  if constexpr (QK && EXP) {
+    // 16 (d = 128) or 8 (d = 64) MFMAs, each with the next K read and its share
+    // of the 96 (non-COMP) or 176 (COMP) VALU instructions of the exponentials
+    constexpr int NM = D / 8, NV = COMP ? 176 : 96, PER = (NV + NM - 1) / NM;
+    BSATTN_SGB(kSgDsRead, 2);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      BSATTN_SGB(kSgMfma, 1);
+      if (i + 2 < NM) BSATTN_SGB(kSgDsRead, 1);
+      BSATTN_SGB(kSgValu, PER);
+    }
+  }
+  if constexpr (EXP) {
+    // the weights are needed here: otherwise the compiler sinks their
+    // computation below the next stage's (branchy) mask, out of this region
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        asm volatile("" ::"v"(pop[u][kc]));
+        if constexpr (COMP) asm volatile("" ::"v"(plo[u][kc]));
+      }
+    asm volatile("" ::"v"(psum));
+  }
+}
+
+// Region B.  O += V P from the V tile vt (P in pop, plo); when MX, the per-lane
+// max of sn over both halves (the caller combines the wave's two lane halves).
+template <int D, bool COMP, bool PV, bool MX>
+__device__ __forceinline__ float region_b(const uint8_t* vt, const u32x4 (&pop)[2][2], const u32x4 (&plo)[2][2],
+                                          f32x16* oacc, const f32x16 (&sn)[2]) {
+  using T = Tile<D>;
+  const int lane = threadIdx.x & 63;
+  const int h2 = lane >> 5, q16 = lane >> 4, a16 = lane & 15;
+  if constexpr (PV) {
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) {
+        const int row = 32 * u + 16 * kc + 4 * h2 + (a16 >> 2);
+        const int col = 32 * dt + 16 * (q16 & 1) + 4 * (a16 & 3);  // element
+        const u32x2 lo = lds_read_tr16(vt, T::v_off(row, col >> 3) + ((col & 7) << 1));
+        const u32x2 hi = lds_read_tr16(vt, T::v_off(row + 8, col >> 3) + ((col & 7) << 1));
+        const u32x4 vop = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        oacc[dt] = mfma32x32x16(as_bf16x8(vop), as_bf16x8(pop[u][kc]), oacc[dt]);
+        if constexpr (COMP) oacc[dt] = mfma32x32x16(as_bf16x8(vop), as_bf16x8(plo[u][kc]), oacc[dt]);
+      }
+  }
+  float mx = -INFINITY;
+  if constexpr (MX) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sn[u][e]);
+  }
+  if constexpr (PV && MX) {
+    constexpr int NM = (D / 32) * 4 * (COMP ? 2 : 1), NR = (D / 32) * 8;
+    constexpr int RPER = NR / NM, VPER = (16 + NM - 1) / NM;
+    BSATTN_SGB(kSgDsRead, 4);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      BSATTN_SGB(kSgMfma, 1);
+      BSATTN_SGB(kSgDsRead, RPER);
+      BSATTN_SGB(kSgValu, VPER);
+    }
+  }
+  return mx;
 }
 
 // SP: block-sparse causal prefill [NSA block selection; COBS 2.1]: ahead of its
@@ -437,8 +574,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     const int hi = wr < 0 ? N - 1 : min(N - 1, i + wr);
     return hi - lo + 1;
   };
-  const bool comp = __builtin_amdgcn_readfirstlane(
-      min(band_keys(min(r0, N - 1)), band_keys(min(r0 + 31, N - 1))) < kCompKeys);
+  // decided for the whole workgroup (its waves must take the same stage loop:
+  // the loops differ in their barriers and copies), from its first and last row
+  const bool comp = min(band_keys(min(i0, N - 1)), band_keys(min(i0 + BM - 1, N - 1))) < kCompKeys;
 
   auto row_pos = [&](int stg, int r) {
     stg -= nx;
@@ -465,76 +603,183 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     if (bs < n_band && row0 + BN <= N) dl.issue(Kb8, Vb8, row0, kt, vt, wid);
     else dma_stage<D>(Kb, Vb, kt, vt, wid, 4, [&](int r) { return row_pos(stg, r); });
   };
-  uint8_t* const buf0 = smem;
-  uint8_t* const buf1 = smem + 2 * T::BYTES;
-  if (n_stage > 0) issue_stage(0, buf0, buf0 + T::BYTES);
-  auto stages = [&](auto comp_tag) {
-    constexpr bool COMP = decltype(comp_tag)::value;
-    // stage `stg` computed from buffer kt while stage stg + 1 is copied into kn
-    auto one = [&](int stg, uint8_t* kt, uint8_t* kn) {
+  // Stage s goes to K tile kb[s % 2] and V tile vb[s % 2]; K of stage s + 2 and
+  // V of stage s + 1 are copied while stage s is computed (K runs one stage
+  // ahead of V: the QK of stage s + 1 overlaps the exponentials of stage s).
+  uint8_t* const kb[2] = {smem, smem + 2 * T::BYTES};
+  uint8_t* const vb[2] = {smem + T::BYTES, smem + 3 * T::BYTES};
+  // Mask of stage stg on this wave's logits: which halves sit on a mask edge
+  // (wave-uniform bits), this lane's allowed keys [lo, hi] plus the global
+  // columns among the stage's keys jb .. jb + 63 (position, or gathered-column
+  // slot, of its first row); the words of allowed-key bits are built only for
+  // the edge halves.  An element is kept by two ALU ops: a signed one-bit field
+  // extract (0 or all ones) selects, bitwise, between the logit and -inf.
+  auto mask_stage = [&](int stg, f32x16(&sx)[2]) {
+    int jb, lo = 0, hi;
+    uint32_t masked = 0;
+    uint64_t gbits = 0ull;
+    if (SP && stg < nx) {
+      const int xb = __builtin_amdgcn_readfirstlane(xblk[stg]);
+      jb = (xb >> 1) * BN;
+      // keys before this row's window (and below n_sink for a sink-only block);
+      // the wave's first row allows the fewest
+      const int cap = (xb & 1) ? 0x7fffffff : a.sp_n_sink - 1;
+      hi = min(myrow - wl - 1, cap);
+      const int hi0 = min(r0 - wl - 1, cap);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) masked |= (jb + 32 * u + 31 > hi0 ? 1u : 0u) << u;
+    } else if (stg - nx < n_band) {
+      jb = (t_lo + stg - nx) * BN;
+      lo = wl < 0 ? 0 : myrow - wl;
+      hi = min(N - 1, wr < 0 ? N - 1 : myrow + wr);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int j0 = jb + 32 * u;
+        // every key of the half allowed for all 32 rows
+        const bool all_lo = wl < 0 || j0 >= r0 + 31 - wl;
+        const bool all_hi = wr < 0 || j0 + 31 <= r0 + wr;
+        masked |= (all_lo && all_hi && j0 + 31 < N ? 0u : 1u) << u;
+      }
+      if (LG && masked) {
+        for (int i = lower_bound_i32(a.gpos, a.n_global, jb); i < a.n_global && a.gpos[i] < jb + BN; ++i)
+          gbits |= 1ull << (a.gpos[i] - jb);
+      }
+    } else {
+      jb = (stg - nx - n_band) * BN;
+      hi = ngc - 1;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) masked |= (jb + 32 * u + 32 > ngc ? 1u : 0u) << u;
+    }
+    if (!masked) return;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if ((masked >> u) & 1u) {
+        const int j0 = jb + 32 * u;
+        const uint32_t m = (range_bits32(lo - j0, hi - j0) | (uint32_t)(gbits >> (32 * u))) >> (4 * h2);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int pbit = 8 * (e >> 2) + (e & 3);
+          const uint32_t keep = (uint32_t)((int)(m << (31 - pbit)) >> 31);
+          // copied out first: a bit-cast of a vector-element lvalue reads element 0
+          const float v = sx[u][e];
+          const uint32_t x = __builtin_bit_cast(uint32_t, v);
+          sx[u][e] = __builtin_bit_cast(float, (x & keep) | (0xff800000u & ~keep));
+        }
+      }
+    }
+  };
+  // Rows that see fewer than 256 keys (the first tiles of a sequence) take the
+  // compensated product; their workgroups run one stage at a time (K and V of
+  // stage s + 1 copied while stage s is computed), which keeps the extra P
+  // registers out of the pipelined loop's budget.
+  auto stages_comp = [&]() {
+    if (n_stage == 0) return;
+    issue_stage(0, kb[0], vb[0]);
+    auto one = [&](int stg, int cur) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's copies for `stg` landed
       __syncthreads();  // every wave's copies landed; every wave is done with the other buffer
-      if (stg + 1 < n_stage) issue_stage(stg + 1, kn, kn + T::BYTES);
-      uint8_t* vt = kt + T::BYTES;
-      // Which halves of the stage sit on a mask edge (wave-uniform bits), and
-      // this lane's allowed keys [lo, hi] plus the global columns among the
-      // stage's keys jb .. jb + 63 (position, or gathered-column slot, of its
-      // first row); the words of allowed-key bits are built only for the edge
-      // halves.  One stage body serves every kind of stage (a single inlined
-      // copy of the MFMA / softmax code).
-      int jb, lo = 0, hi;
-      uint32_t masked = 0;
-      uint64_t gbits = 0ull;
-      if (SP && stg < nx) {
-        const int xb = __builtin_amdgcn_readfirstlane(xblk[stg]);
-        jb = (xb >> 1) * BN;
-        // keys before this row's window (and below n_sink for a sink-only block);
-        // the wave's first row allows the fewest
-        const int cap = (xb & 1) ? 0x7fffffff : a.sp_n_sink - 1;
-        hi = min(myrow - wl - 1, cap);
-        const int hi0 = min(r0 - wl - 1, cap);
+      if (stg + 1 < n_stage) issue_stage(stg + 1, kb[cur ^ 1], vb[cur ^ 1]);
+      f32x16 sx[2];
+      float unused = 0.f;
+      u32x4 pop[2][2], plo[2][2];
+      region_a<D, true, true, false>(kb[cur], qop, sx, sx, sl2, 0.f, pop, plo, unused);
+      mask_stage(stg, sx);
+      float mx = region_b<D, true, false, true>(nullptr, pop, plo, oacc, sx);
+      mx = max_halves(mx);
+      const float m_cand = mx * sl2;
+      const bool need = m_cand > st.m + kHeadroom;
+      if (__ballot(need)) {
+        const float m_new = need ? m_cand : st.m;
+        const float alpha = need ? __builtin_amdgcn_exp2f(st.m - m_new) : 1.f;
+        st.l *= alpha;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) masked |= (jb + 32 * u + 31 > hi0 ? 1u : 0u) << u;
-      } else if (stg - nx < n_band) {
-        jb = (t_lo + stg - nx) * BN;
-        lo = wl < 0 ? 0 : myrow - wl;
-        hi = min(N - 1, wr < 0 ? N - 1 : myrow + wr);
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int j0 = jb + 32 * u;
-          // every key of the half allowed for all 32 rows
-          const bool all_lo = wl < 0 || j0 >= r0 + 31 - wl;
-          const bool all_hi = wr < 0 || j0 + 31 <= r0 + wr;
-          masked |= (all_lo && all_hi && j0 + 31 < N ? 0u : 1u) << u;
-        }
-        if (LG && masked) {
-          for (int i = lower_bound_i32(a.gpos, a.n_global, jb); i < a.n_global && a.gpos[i] < jb + BN; ++i)
-            gbits |= 1ull << (a.gpos[i] - jb);
-        }
-      } else {
-        jb = (stg - nx - n_band) * BN;
-        hi = ngc - 1;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) masked |= (jb + 32 * u + 32 > ngc ? 1u : 0u) << u;
+        for (int t = 0; t < D / 32; ++t) oacc[t] *= alpha;
+        st.m = m_new;
       }
-      stage<D, 2, COMP>(kt, vt, qop, oacc, st, sl2,
-                        [&](int u) {
-                          const int j0 = jb + 32 * u;
-                          return range_bits32(lo - j0, hi - j0) | (uint32_t)(gbits >> (32 * u));
-                        },
-                        masked);
+      float psum = 0.f;
+      region_a<D, true, false, true>(nullptr, qop, sx, sx, sl2, (st.m == -INFINITY) ? 0.f : -st.m, pop, plo, psum);
+      st.l += psum;
+      region_b<D, true, true, false>(vb[cur], pop, plo, oacc, sx);
     };
-    // unrolled by two so each buffer's LDS addresses are compile-time offsets;
-    // an odd last stage runs after the loop (no branch inside the loop body)
     int stg = 0;
     for (; stg + 1 < n_stage; stg += 2) {
-      one(stg, buf0, buf1);
-      one(stg + 1, buf1, buf0);
+      one(stg, 0);
+      one(stg + 1, 1);
     }
-    if (stg < n_stage) one(stg, buf0, buf1);
+    if (stg < n_stage) one(stg, 0);
   };
-  if (comp) stages(std::true_type{});
-  else stages(std::false_type{});
+  auto stages = [&]() {
+    constexpr bool COMP = false;
+    if (n_stage == 0) return;
+    issue_stage(0, kb[0], vb[0]);
+    if (n_stage > 1) issue_stage(1, kb[1], nullptr);
+    f32x16 sA[2], sB[2];
+    u32x4 pop[2][2], plo[2][2];
+    float nm = 0.f;
+    // the wave's new row max from the per-lane maxima of a stage's logits: the
+    // running max moves only when it grows by more than 2^8 (log2 units), and
+    // then the normaliser and O are rescaled (wave-uniform branch)
+    auto update_max = [&](float mx) {
+      mx = max_halves(mx);
+      const float m_cand = mx * sl2;
+      const bool need = m_cand > st.m + kHeadroom;
+      if (__ballot(need)) {
+        const float m_new = need ? m_cand : st.m;
+        const float alpha = need ? __builtin_amdgcn_exp2f(st.m - m_new) : 1.f;
+        st.l *= alpha;
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t) oacc[t] *= alpha;
+        st.m = m_new;
+      }
+      nm = (st.m == -INFINITY) ? 0.f : -st.m;
+    };
+    // prologue: S_0 = K_0 Q^T, its mask and max
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    {
+      float unused = 0.f;
+      region_a<D, COMP, true, false>(kb[0], qop, sA, sA, sl2, nm, pop, plo, unused);
+    }
+    mask_stage(0, sA);
+    update_max(region_b<D, COMP, false, true>(nullptr, pop, plo, oacc, sA));
+    // stage j (logits in s) with stage j + 1 (logits into sn): exponentials of j
+    // under the MFMAs of S_{j+1}, then O += V_j P_j under the max of S_{j+1}
+    auto iter = [&](int j, f32x16(&s)[2], f32x16(&sn)[2], uint8_t* kt_next, uint8_t* vt_cur, uint8_t* k_dst,
+                    uint8_t* v_dst) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's copies of K_{j+1}, V_j landed
+      __syncthreads();  // every wave's copies landed; every wave is done with K_j and V_{j-1}
+      if (j + 2 < n_stage) issue_stage(j + 2, k_dst, nullptr);
+      issue_stage(j + 1, nullptr, v_dst);
+      float psum = 0.f;
+      region_a<D, COMP, true, true>(kt_next, qop, sn, s, sl2, nm, pop, plo, psum);
+      st.l += psum;
+      mask_stage(j + 1, sn);
+      update_max(region_b<D, COMP, true, true>(vt_cur, pop, plo, oacc, sn));
+    };
+    // the last stage: its exponentials and O += V P
+    auto last = [&](f32x16(&s)[2], uint8_t* vt_cur) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      float psum = 0.f;
+      region_a<D, COMP, false, true>(nullptr, qop, s, s, sl2, nm, pop, plo, psum);
+      st.l += psum;
+      region_b<D, COMP, true, false>(vt_cur, pop, plo, oacc, s);
+    };
+    // unrolled by two so each buffer's LDS addresses are compile-time offsets
+    int j = 0;
+    for (; j + 2 < n_stage; j += 2) {
+      iter(j, sA, sB, kb[1], vb[0], kb[0], vb[1]);
+      iter(j + 1, sB, sA, kb[0], vb[1], kb[1], vb[0]);
+    }
+    if (j + 1 < n_stage) {
+      iter(j, sA, sB, kb[1], vb[0], kb[0], vb[1]);
+      last(sB, vb[1]);
+    } else {
+      last(sA, vb[0]);
+    }
+  };
+  if (comp) stages_comp();
+  else stages();
   // write rows (global rows are written by the merge of their split partials)
   st.l = sum_halves(st.l);
   bool store = myrow < N;
