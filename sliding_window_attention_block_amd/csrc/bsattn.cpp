@@ -123,27 +123,29 @@ int forced_range_blocks(int32_t n_ctx, int32_t window, int32_t n_sink) {
 }
 
 // Decode launch plan for top_k selected and n_forced forced items per pair:
-// n_part partials per pair (merged when more than one); bf16 waves take fh
-// forced and sh selected half items each.
+// n_part waves (bf16) or workgroups (fp32) per pair, n_merge partials per
+// query head (one per workgroup; merged when more than one); bf16 waves take
+// fh forced and sh selected half items each.
 struct DecodePlan {
-  int half_items, n_part, fh, sh;
+  int half_items, n_part, n_merge, fh, sh;
 };
 DecodePlan decode_plan(const bsattn_shape* s, int top_k, int n_forced) {
   DecodePlan p;
   bsattn::decode_split_geometry(top_k + n_forced, s->batch * s->n_kv_heads, s->head_dim,
                                 s->dtype == BSATTN_BF16, &p.half_items, &p.n_part);
+  p.n_merge = s->dtype == BSATTN_BF16 ? p.n_part / bsattn::kDecodeWaves : p.n_part;
   p.fh = (2 * n_forced + p.n_part - 1) / p.n_part;
   p.sh = (2 * top_k + p.n_part - 1) / p.n_part;
   return p;
 }
 
-// Workspace layout: partial numerators [B*Hq, n_part, d] | partial (max, sum)
-// [B*Hq, n_part, 2], each region 256-byte aligned; nothing when n_part == 1.
+// Workspace layout: partial numerators [B*Hq, n_merge, d] | partial (max, sum)
+// [B*Hq, n_merge, 2], each region 256-byte aligned; nothing when n_merge == 1.
 struct WsLayout {
   size_t o_off, ml_off, total;
 };
-WsLayout workspace_layout(const bsattn_shape* s, int n_part) {
-  const size_t rows = n_part > 1 ? (size_t)s->batch * s->n_q_heads * n_part : 0;
+WsLayout workspace_layout(const bsattn_shape* s, int n_merge) {
+  const size_t rows = n_merge > 1 ? (size_t)s->batch * s->n_q_heads * n_merge : 0;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   WsLayout l;
   l.o_off = 0;
@@ -160,7 +162,7 @@ size_t decode_workspace_bound(const bsattn_shape* s, int top_k, int window, int 
   const int base = forced_range_blocks(s->n_ctx, window, n_sink);
   size_t most = 0;
   for (int extra = 0; extra <= n_global; ++extra) {
-    const size_t t = workspace_layout(s, decode_plan(s, top_k, base + extra).n_part).total;
+    const size_t t = workspace_layout(s, decode_plan(s, top_k, base + extra).n_merge).total;
     if (t > most) most = t;
   }
   return most;
@@ -298,8 +300,8 @@ bsattn_status decode_args(const bsattn_shape* shape, const void* Q, const void* 
   const int n_forced = a.fblocks.r0_n + a.fblocks.r1_n + a.fblocks.n_gblk;
   a.n_items = top_k + n_forced;
   const DecodePlan plan = decode_plan(shape, top_k, n_forced);
-  const WsLayout lay = workspace_layout(shape, plan.n_part);
-  const size_t need = plan.n_part > 1 ? lay.total : 0;
+  const WsLayout lay = workspace_layout(shape, plan.n_merge);
+  const size_t need = plan.n_merge > 1 ? lay.total : 0;
   if (need > 0 && (workspace == nullptr || ws_bytes < need))
     return fail(BSATTN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
   if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
@@ -310,6 +312,7 @@ bsattn_status decode_args(const bsattn_shape* shape, const void* Q, const void* 
   a.fh_per_wave = plan.fh;
   a.sh_per_wave = plan.sh;
   a.n_part = plan.n_part;
+  a.n_merge = plan.n_merge;
   a.Q = Q; a.K = K; a.V = V; a.sel = sel; a.O = O; a.lse = lse;
   a.batch = shape->batch; a.n_q_heads = shape->n_q_heads; a.n_kv_heads = shape->n_kv_heads;
   a.head_dim = shape->head_dim;

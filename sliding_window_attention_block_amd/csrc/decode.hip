@@ -27,7 +27,8 @@
 // bf16 path (MFMA, gfx950 v_mfma_f32_16x16x32_bf16): the unit is a half item
 // (32 tokens of one block).  Each wave owns a run of half items of one pair
 // and pipelines them two deep (next half item's loads in flight while the
-// current one is computed); waves are independent and write one partial each.
+// current one is computed); waves never wait for each other until the end,
+// where the four waves of a workgroup (one pair) merge in LDS.
 //   K goes straight from HBM into MFMA A-operand registers; V is loaded with
 //   coalesced 1 KB instructions into registers and, at compute time, written
 //   to the wave's LDS tile (XOR-swizzled 16-byte chunks) and read back
@@ -40,10 +41,11 @@
 // fp32 path (VALU): one token per lane, one item per wave; the 4 waves of a
 // workgroup merge in LDS into one partial.
 //
-// With one partial per pair the kernel writes O and lse itself; otherwise a
-// small second kernel merges the partials (the kernel boundary makes every
-// partial visible without any L2 write-back inside the hot kernel; the L2s of
-// the 8 XCDs are not coherent with each other).
+// With one workgroup per pair the kernel writes O and lse itself; otherwise
+// each workgroup writes one partial and a small second kernel merges them (the
+// kernel boundary makes every partial visible; the L2s of the 8 XCDs are not
+// coherent with each other, and merging inside the kernel, through agent-scope
+// stores and an arrival counter, measured no faster than the extra launch).
 #include <mutex>
 
 #include "launch.hpp"
@@ -107,7 +109,7 @@ struct MergeLds {
 template <int D>
 __device__ __forceinline__ void write_wg_result(const DecodeArgs& a, const MergeLds<D>* ml, int b, int g) {
   const int G = a.n_q_heads / a.n_kv_heads;
-  const int n_wg = a.n_part, wg = blockIdx.x;
+  const int n_wg = a.n_merge, wg = blockIdx.x;
   for (int idx = threadIdx.x; idx < G * D; idx += 64 * kW) {
     const int hh = idx / D, dd = idx % D;
     float M = -INFINITY;
@@ -145,9 +147,10 @@ __device__ __forceinline__ void write_wg_result(const DecodeArgs& a, const Merge
 // straight into MFMA A-operand registers; V is loaded with coalesced 1 KB
 // instructions into registers and, at compute time, written to the wave's LDS
 // tile and read back transposed.  Only plain vector loads are in flight, so the
-// compiler's own waits are exact.  Waves never wait for each other (no
-// barriers), so the memory system sees a steady stream of requests instead of
-// rounds of workgroups that load, then compute, then retire together.
+// compiler's own waits are exact.  Waves never wait for each other before the
+// final merge (no barriers in the loop), so the memory system sees a steady
+// stream of requests instead of rounds of workgroups that load, then compute,
+// then retire together.
 //
 // Token set without any search: a selected block contributes its tokens that
 // are not forced; a forced block contributes its forced tokens.  Every token of
@@ -422,7 +425,9 @@ __global__ __launch_bounds__(64 * kW, D == 128 ? 1 : 2) void decode_bf16_kernel(
   const int gw = blockIdx.x * kW + wid;  // global wave index
   const int n_pairs = a.batch * a.n_kv_heads;
   const int pair = gw / a.n_part, wi = gw % a.n_part;
-  if (pair >= n_pairs) return;  // no barriers below: waves are independent
+  // n_part is a multiple of kW: the four waves of a workgroup share one pair,
+  // so this exit is uniform over the workgroup (it meets barriers at the end)
+  if (pair >= n_pairs) return;
   const int b = pair / a.n_kv_heads, g = pair % a.n_kv_heads;
   const int G = a.n_q_heads / a.n_kv_heads;
   const int h = lane & 15, grp = lane >> 4;
@@ -600,23 +605,47 @@ __global__ __launch_bounds__(64 * kW, D == 128 ? 1 : 2) void decode_bf16_kernel(
 
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-  if (h >= G) return;
-  // lane (h, grp) holds O[h][16dt + 4grp .. +4]
-  const size_t qrow = (size_t)b * a.n_q_heads + g * G + h;
-  if (a.n_part == 1) {
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  // The workgroup's four waves (one pair) merge in LDS: each wave's numerator
+  // over its own V tile (16 heads x d floats fill the 64 d bytes exactly), its
+  // max and normaliser beside.
+  __shared__ float wml[kW][2][16];
+  float* const wo = reinterpret_cast<float*>(vt);
+  if (h < G) {
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      *reinterpret_cast<f32x4*>(a.O + qrow * D + 16 * dt + 4 * grp) = oacc[dt] * inv;
-    if (a.lse != nullptr && grp == 0) a.lse[qrow] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
-  } else {
-    const size_t prow = qrow * a.n_part + wi;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      *reinterpret_cast<f32x4*>(a.part_o + prow * D + 16 * dt + 4 * grp) = oacc[dt];
+    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(wo + h * D + 16 * dt + 4 * grp) = oacc[dt];
     if (grp == 0) {
-      a.part_ml[2 * prow] = m_run;
-      a.part_ml[2 * prow + 1] = l_run;
+      wml[wid][0][h] = m_run;
+      wml[wid][1][h] = l_run;
+    }
+  }
+  __syncthreads();
+  const int n_wg = a.n_merge, wgi = wi / kW;
+  for (int idx = threadIdx.x; idx < G * D; idx += 64 * kW) {
+    const int hh = idx / D, dd = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) M = fmaxf(M, wml[w][0][hh]);
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kW; ++w) {
+        const float mw = wml[w][0][hh];
+        const float sc = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+        L = fmaf(sc, wml[w][1][hh], L);
+        O = fmaf(sc, reinterpret_cast<const float*>(smem + w * H::TILE)[hh * D + dd], O);
+      }
+    }
+    const size_t qrow = (size_t)b * a.n_q_heads + g * G + hh;
+    if (n_wg == 1) {
+      a.O[qrow * D + dd] = L > 0.f ? O / L : 0.f;
+      if (a.lse != nullptr && dd == 0) a.lse[qrow] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+    } else {
+      const size_t prow = qrow * n_wg + wgi;
+      a.part_o[prow * D + dd] = O;
+      if (dd == 0) {
+        a.part_ml[2 * prow] = M;
+        a.part_ml[2 * prow + 1] = L;
+      }
     }
   }
 }
@@ -720,7 +749,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   constexpr int DL = D / 64;
   const size_t qrow = blockIdx.x;  // b * Hq + h
   const int lane = threadIdx.x;
-  const int n = a.n_part;
+  const int n = a.n_merge;
   const float* pml = a.part_ml + qrow * n * 2;
   const float* po = a.part_o + qrow * n * D + lane;
   float M = -INFINITY, L = 0.f, O[DL];
@@ -783,27 +812,29 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL((decode_f32_kernel<D, 16>), grid, dim3(64 * kW), 0, stream, a);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.n_part == 1) return e;
+  if (e != hipSuccess || a.n_merge == 1) return e;
   const dim3 mg(a.batch * a.n_q_heads), mb(64);
-  if (a.n_part <= 8) hipLaunchKernelGGL((decode_merge_kernel<D, 8>), mg, mb, 0, stream, a);
-  else if (a.n_part <= 16) hipLaunchKernelGGL((decode_merge_kernel<D, 16>), mg, mb, 0, stream, a);
+  if (a.n_merge <= 8) hipLaunchKernelGGL((decode_merge_kernel<D, 8>), mg, mb, 0, stream, a);
+  else if (a.n_merge <= 16) hipLaunchKernelGGL((decode_merge_kernel<D, 16>), mg, mb, 0, stream, a);
   else hipLaunchKernelGGL((decode_merge_kernel<D, 32>), mg, mb, 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// bf16: `half_items` = c, the fewest half items (32 tokens) per wave that keep
-// every wave resident at once (decode_slots(d) waves); n_part = ceil(2 n_items
-// / c) waves per pair.  The caller gives each wave ceil(2 forced / n_part)
-// forced and ceil(2 top_k / n_part) selected half items, at most c + 2 half
-// items spanning at most c / 2 + 3 items, so c <= 120 keeps a wave's items
+// bf16: n_part waves per pair, a multiple of kW (a workgroup's waves share one
+// pair and merge in LDS): as many as keep every wave resident at once
+// (decode_slots(d) waves over all pairs), at most one per half item and at
+// least kW; `half_items` = c = ceil(2 n_items / n_part).  The caller gives each
+// wave ceil(2 forced / n_part) forced and ceil(2 top_k / n_part) selected half
+// items, at most c + 2 half items spanning at most c / 2 + 3 items, so c <= 120
+// (n_part grows past the resident waves when it must) keeps a wave's items
 // within one per lane.  fp32: one whole item per wave, 4 waves per workgroup
 // merged in LDS, one partial per workgroup.
 void decode_split_geometry(int n_items, int n_pairs, int head_dim, bool bf16, int* half_items, int* n_part) {
   if (n_items <= 0 || n_pairs <= 0) {
     *half_items = 1;
-    *n_part = 1;
+    *n_part = bf16 ? kW : 1;
     return;
   }
   if (!bf16) {
@@ -811,14 +842,19 @@ void decode_split_geometry(int n_items, int n_pairs, int head_dim, bool bf16, in
     *n_part = (n_items + kW - 1) / kW;
     return;
   }
-  const int slots = decode_slots(head_dim);
+  const long long slots = decode_slots(head_dim);
   const long long n_sub = 2LL * n_items;
-  long long c = (n_pairs * n_sub + slots - 1) / slots;
-  if (c < 1) c = 1;
-  while (c < n_sub && (long long)n_pairs * ((n_sub + c - 1) / c) > slots) ++c;
-  if (c > 120) c = 120;
+  long long np = slots / n_pairs / kW * kW;
+  const long long cap = (n_sub + kW - 1) / kW * kW;
+  if (np > cap) np = cap;
+  if (np < kW) np = kW;
+  long long c = (n_sub + np - 1) / np;
+  if (c > 120) {
+    c = 120;
+    np = ((n_sub + c - 1) / c + kW - 1) / kW * kW;
+  }
   *half_items = (int)c;
-  *n_part = (int)((n_sub + c - 1) / c);
+  *n_part = (int)np;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {

@@ -139,8 +139,8 @@ struct DecodeArgs {
   const int32_t* sel;
   float* O;
   float* lse;
-  float* part_o;      // [B*Hq, n_part, d]  partial numerators
-  float* part_ml;     // [B*Hq, n_part, 2]  partial (max, normaliser), log2 domain
+  float* part_o;      // [B*Hq, n_merge, d]  partial numerators
+  float* part_ml;     // [B*Hq, n_merge, 2]  partial (max, normaliser), log2 domain
   int32_t batch, n_q_heads, n_kv_heads, head_dim;
   int32_t kv_capacity;
   int32_t top_k;
@@ -148,7 +148,8 @@ struct DecodeArgs {
   int32_t per_wave;       // fp32: items per wave
   int32_t fh_per_wave;    // bf16: forced half items per wave
   int32_t sh_per_wave;    // bf16: selected half items per wave
-  int32_t n_part;         // partials per (b, K/V head): bf16 waves, fp32 workgroups
+  int32_t n_part;         // bf16: waves per (b, K/V head), a multiple of kDecodeWaves; fp32: workgroups
+  int32_t n_merge;        // partials per query head (workgroups per pair); merged when more than one
   // fused step (bf16): each wave selects its pair's top-k blocks itself from
   // the group scores instead of reading `sel`; the first wave of a pair writes
   // the selection to sel_out.  key_slots: scores per lane (0: not fused, else 8).

@@ -39,15 +39,23 @@ def test_status_strings():
 
 def test_workspace_size_matches_split_layout():
     s = api.make_shape(4, 64, 8, 128, 131072)
-    # 32 selected + sink block + 16 window blocks = 49 items = 98 half items (one per
-    # wave); 4 waves per workgroup -> 25 partials
+    # 32 selected + sink block + 16 window blocks = 49 items = 98 half items; the
+    # 1024 resident waves give each of the 32 pairs 32 waves, 4 per workgroup ->
+    # 8 partials per query head
     up = lambda x: -(-x // 256) * 256  # noqa: E731
-    rows = 4 * 64 * 25
+    rows = 4 * 64 * 8
     expect = up(rows * 128 * 4) + up(rows * 8)
     assert api.bsattn_decode_workspace_bytes(s, 32, 1024, 64, 0) == expect
-    # globals can only add blocks
+    # globals can only add blocks (the partials per head stay capped by the
+    # resident waves here)
     assert api.bsattn_decode_workspace_bytes(s, 32, 1024, 64, 5) >= expect
-    assert api.bsattn_decode_workspace_bytes(s, 32, 1024, 64, 40) > expect
+    assert api.bsattn_decode_workspace_bytes(s, 32, 1024, 64, 40) >= expect
+    # with one pair, each forced block adds waves until the cap: 49 items -> 100
+    # waves (25 partials), 89 items -> 180 waves (45 partials)
+    one = api.make_shape(1, 8, 1, 128, 131072)
+    rows1 = lambda n: up(8 * n * 128 * 4) + up(8 * n * 8)  # noqa: E731
+    assert api.bsattn_decode_workspace_bytes(one, 32, 1024, 64, 0) == rows1(25)
+    assert api.bsattn_decode_workspace_bytes(one, 32, 1024, 64, 40) == rows1(45)
     small = api.make_shape(1, 4, 1, 64, 300)
     assert api.bsattn_decode_workspace_bytes(small, 2, 500, 10, 0) > 0
     assert api.bsattn_decode_workspace_bytes(small, 0, 10, 10, 0) == 0
@@ -337,8 +345,8 @@ def test_noalloc_step_checks_its_arguments_and_the_scratch_limit():
     assert _lib.BSATTN_NOALLOC_SCRATCH_BYTES == 16 << 20
     s = _lib.Shape(64, 1024, 64, 128, 4096 * 64, 4096 * 64, 64, 0.0, _lib.BSATTN_BF16)
     p = ctypes.c_void_p(16)
-    assert lib.bsattn_decode_workspace_bytes(ctypes.byref(s), 64, 512, 64, 0) > _lib.BSATTN_NOALLOC_SCRATCH_BYTES
-    st = lib.bsattn_decode_step_noalloc(ctypes.byref(s), p, p, p, p, 1, None, 0, None, None, 0, 0, 4096, 64, 512,
+    assert lib.bsattn_decode_workspace_bytes(ctypes.byref(s), 1024, 512, 64, 0) > _lib.BSATTN_NOALLOC_SCRATCH_BYTES
+    st = lib.bsattn_decode_step_noalloc(ctypes.byref(s), p, p, p, p, 1, None, 0, None, None, 0, 0, 4096, 1024, 512,
                                         64, None, 0, p, p, p, p, None, None)
     assert st == _lib.BSATTN_ERR_WORKSPACE
     assert b"static scratch" in lib.bsattn_last_error()

@@ -81,9 +81,9 @@ def test_noalloc_step_refuses_partials_past_the_scratch(api):
     import torch
     B, Hq, Hkv, d, n = 64, 1024, 64, 128, 4096 * 64
     shape = api.make_shape(B, Hq, Hkv, d, n)
-    need = api.bsattn_decode_workspace_bytes(shape, 64, 512, 64, 0)
+    need = api.bsattn_decode_workspace_bytes(shape, 1024, 512, 64, 0)
     assert need > api.BSATTN_NOALLOC_SCRATCH_BYTES
     dummy = torch.empty(16, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(RuntimeError, match="static scratch"):
-        api.bsattn_decode_step_noalloc(shape, dummy, dummy, dummy, dummy, None, 0, n // 64, 64, 512, 64, (), dummy,
+        api.bsattn_decode_step_noalloc(shape, dummy, dummy, dummy, dummy, None, 0, n // 64, 1024, 512, 64, (), dummy,
                                        dummy, dummy, dummy)
