@@ -193,8 +193,9 @@ __device__ __forceinline__ void selected_item(const DecodeArgs& a, int sel_blk, 
 // blocks with a token outside the forced set; order: score descending, then
 // block index ascending.  A radix select (8 bits a pass, 256-bin histogram in
 // this wave's LDS `hist`) finds the k-th largest key T and how many keys equal
-// to T are taken (the lowest-index ones); bytes that every candidate key
-// shares are known from the wave's AND / OR and skipped.  The selected blocks
+// to T are taken (the lowest-index ones); bits that every candidate key
+// shares are known from the wave's AND / OR, and each pass's 8-bit digit
+// starts at the highest bit still undecided.  The selected blocks
 // go to tab[0 .. top_k) in ascending order, -1 after the last.
 template <int PL>
 __device__ __forceinline__ void wave_topk(const DecodeArgs& a, const float (&sv)[PL], uint32_t* hist, int32_t* tab) {
@@ -218,17 +219,20 @@ __device__ __forceinline__ void wave_topk(const DecodeArgs& a, const float (&sv)
   uint32_t all_and, all_or;
   wave_and_or(kand, kor, all_and, all_or);  // (all ones / zero when there is no candidate)
   const uint32_t diff = all_and ^ all_or;
-  // first pass: the byte holding the highest bit on which candidate keys differ
-  const int top = diff ? (31 - __clz(diff)) & ~7 : -8;
-  uint32_t pmask = top >= 24 ? 0u : ~0u << (top + 8);
+  // first pass: the 8 bits from the highest bit on which candidate keys differ
+  // down (bits above it are shared by every candidate), then the next 8 below
+  const int hb = diff ? 31 - __clz(diff) : -1;
+  uint32_t pmask = hb >= 31 ? 0u : ~0u << (hb + 1);
   uint32_t prefix = all_and & pmask;
   int remaining = kk;
   if (kk > 0) {
-    for (int shift = top; shift >= 0; shift -= 8) {
+    for (int hi = hb; hi >= 0;) {
+      const int lo = max(hi - 7, 0);
+      const uint32_t dmask = (2u << (hi - lo)) - 1u;
       reinterpret_cast<u32x4*>(hist)[lane] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int t = 0; t < PL; ++t)
-        if (((cm >> t) & 1u) && (key[t] & pmask) == prefix) atomicAdd(&hist[(key[t] >> shift) & 255u], 1u);
+        if (((cm >> t) & 1u) && (key[t] & pmask) == prefix) atomicAdd(&hist[(key[t] >> lo) & dmask], 1u);
       // lane l reads digits 255-4l (c4[3]) down to 252-4l (c4[0])
       const u32x4 c4 = reinterpret_cast<const u32x4*>(hist)[63 - lane];
       const int sum = (int)(c4[0] + c4[1] + c4[2] + c4[3]);
@@ -247,10 +251,11 @@ __device__ __forceinline__ void wave_topk(const DecodeArgs& a, const float (&sv)
       const int src = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
       const int digit = __builtin_amdgcn_readlane(found, src);
       remaining -= __builtin_amdgcn_readlane(above, src);
-      prefix |= (uint32_t)digit << shift;
-      pmask |= 255u << shift;
-      // every key of the bin is taken: the lower bytes do not matter
+      prefix |= (uint32_t)digit << lo;
+      pmask |= dmask << lo;
+      // every key of the bin is taken: the lower bits do not matter
       if (__builtin_amdgcn_readlane(inbin, src) == remaining) break;
+      hi = lo - 1;
     }
   }
   // keys above the prefix, then the first `remaining` keys on it, in block order

@@ -128,7 +128,7 @@ struct ForcedBlocks {
 
 // Fused decode step limits: 8 scores per lane in registers (with more blocks
 // the in-wave selection costs more than the top-k launch it saves: measured at
-// 2048 blocks) and the selection table in the wave's V tile.
+// 2048 blocks, 32 scores per lane) and the selection table in the wave's V tile.
 constexpr int kFusedMaxBlocks = 64 * 8;
 constexpr int kFusedMaxTopK = 256;
 

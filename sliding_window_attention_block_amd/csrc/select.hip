@@ -410,20 +410,24 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
   }
   const int kk = min(a.top_k, tot);
   const uint32_t diff = all_and ^ all_or;
-  // first pass: the byte holding the highest bit on which candidate keys differ
-  const int top = diff ? (31 - __clz(diff)) & ~7 : -8;
-  uint32_t pmask = top >= 24 ? 0u : ~0u << (top + 8);
+  // first pass: the 8 bits from the highest bit on which candidate keys differ
+  // down (the bits above it are shared by every candidate), then the next 8
+  // below, and so on: no pass spends digits on bits every candidate shares
+  const int hb = diff ? 31 - __clz(diff) : -1;
+  uint32_t pmask = hb >= 31 ? 0u : ~0u << (hb + 1);
   uint32_t prefix = all_and & pmask;
   int remaining = kk;
   if (kk > 0) {
     int pass = 0;
-    for (int shift = top; shift >= 0; shift -= 8, ++pass) {
+    for (int hi = hb; hi >= 0; ++pass) {
+      const int lo = max(hi - 7, 0);
+      const uint32_t dmask = (2u << (hi - lo)) - 1u;
       uint32_t* h = hist[pass];
 #pragma unroll
       for (int t = 0; t < KPT; ++t)
         if ((cm >> t) & 1ull) {
           const uint32_t k = key_at(t);
-          if ((k & pmask) == prefix) atomicAdd(&h[(k >> shift) & 255u], 1u);
+          if ((k & pmask) == prefix) atomicAdd(&h[(k >> lo) & dmask], 1u);
         }
       __syncthreads();
       // every wave: lane l reads digits 255-4l (c4[3]) down to 252-4l (c4[0])
@@ -444,10 +448,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SelectArgs a) {
       const int src = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
       const int digit = __builtin_amdgcn_readlane(found, src);
       remaining -= __builtin_amdgcn_readlane(above, src);
-      prefix |= (uint32_t)digit << shift;
-      pmask |= 255u << shift;
-      // the same in every wave: every key of the bin is taken, lower bytes do not matter
+      prefix |= (uint32_t)digit << lo;
+      pmask |= dmask << lo;
+      // the same in every wave: every key of the bin is taken, lower bits do not matter
       if (__builtin_amdgcn_readlane(inbin, src) == remaining) break;
+      hi = lo - 1;
     }
   }
   // keys above the prefix, then the first `remaining` keys on it, in block order

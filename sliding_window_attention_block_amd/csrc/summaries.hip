@@ -7,8 +7,13 @@
 // block's empirical key distribution.  The top-r eigenpairs come from the
 // L x L centred Gram matrix G = C C^T / L (same non-zero eigenvalues as
 // Sigma = C^T C / L): if G w = lambda w with |w| = 1, then sqrt(lambda) v =
-// C^T w / sqrt(L).  G is diagonalised by parallel cyclic Jacobi in LDS
-// (round-robin pairing: 32 disjoint rotations per round, 63 rounds a sweep).
+// C^T w / sqrt(L).  The symmetric eigenproblem is solved the textbook way for
+// a few extreme eigenpairs (Golub & Van Loan, the symmetric QR and tridiagonal
+// chapters): Householder reduction of G to tridiagonal T in LDS, the top r
+// eigenvalues of T by multisection on Sturm counts, their eigenvectors by
+// inverse iteration on T (pivoted elimination; the r vectors re-orthonormalised
+// after each solve, which also separates close eigenvalues), then the
+// reflections applied back.
 #include "launch.hpp"
 
 namespace bsattn {
@@ -86,14 +91,33 @@ __global__ __launch_bounds__(256) void summaries_mean_kernel(SummaryArgs a) {
 
 // ----------------------------------------------------------------- mean + factor
 constexpr int kCtStride = 68;  // floats per row of the transposed block (bank spread, 16-B aligned)
-constexpr int kGStride = 65;   // floats per row of the Gram matrix
-constexpr int kMaxSweeps = 12;
+constexpr int kGStride = 65;   // floats per row of the Gram matrix and of the eigenvector work rows
 
-// Pair i of round r in the round-robin schedule over 64 indices.
-__device__ __forceinline__ void rr_pair(int r, int i, int& p, int& q) {
-  if (i == 0) { p = r; q = 63; }
-  else { p = (r + i) % 63; q = (r - i + 63) % 63; }
+// Sum, min and max over the 64 lanes, the same value in every lane: row_ror
+// 8, 4, 2, 1 leave each 16-lane row's total in its lanes, then the four rows'
+// first lanes are combined in a fixed order.
+#define BSATTN_ROW_ALL(OP, v)                                                                      \
+  do {                                                                                             \
+    v = OP(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false))); \
+    v = OP(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xf, 0xf, false))); \
+    v = OP(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xf, 0xf, false))); \
+    v = OP(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xf, 0xf, false))); \
+  } while (0)
+__device__ __forceinline__ float rl(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
+__device__ __forceinline__ float f_add(float x, float y) { return x + y; }
+__device__ __forceinline__ float wsum(float v) {
+  BSATTN_ROW_ALL(f_add, v);
+  return (rl(v, 0) + rl(v, 16)) + (rl(v, 32) + rl(v, 48));
 }
+__device__ __forceinline__ float wmin(float v) {
+  BSATTN_ROW_ALL(fminf, v);
+  return fminf(fminf(rl(v, 0), rl(v, 16)), fminf(rl(v, 32), rl(v, 48)));
+}
+__device__ __forceinline__ float wmax(float v) {
+  BSATTN_ROW_ALL(fmaxf, v);
+  return fmaxf(fmaxf(rl(v, 0), rl(v, 16)), fmaxf(rl(v, 32), rl(v, 48)));
+}
+#undef BSATTN_ROW_ALL
 
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void summaries_factor_kernel(SummaryArgs a) {
@@ -102,12 +126,12 @@ __global__ __launch_bounds__(256) void summaries_factor_kernel(SummaryArgs a) {
   constexpr int PER = kBlock * CH / 256;
   __shared__ __attribute__((aligned(16))) float Ct[D * kCtStride];  // Ct[d][r], centred keys
   __shared__ float G[64 * kGStride];
-  __shared__ float W[64 * kGStride];                                // eigenvectors as columns
+  __shared__ __attribute__((aligned(16))) float W[64 * kGStride];  // basis chunks; eigenvector work rows
   __shared__ float mu[D];
-  __shared__ float rc[32], rs[32], rt[32];
-  __shared__ int rp[32], rq[32];
-  __shared__ float red[8];
-  __shared__ int pick[8];
+  __shared__ float td[64], te[64], tb[64], tp[128];  // T's diagonal, off-diagonal; reflector betas; p
+  __shared__ float xc[64], uw[4][128];               // current column; each wave's reflector vector
+  __shared__ __attribute__((aligned(16))) float kpart[4];  // each wave's share of u.(beta p)
+  __shared__ float lam[8];
   __shared__ float F[8 * D];
 
   const int tid = threadIdx.x;
@@ -142,28 +166,39 @@ __global__ __launch_bounds__(256) void summaries_factor_kernel(SummaryArgs a) {
     const int d = i / kBlock, r = i % kBlock;
     Ct[d * kCtStride + r] -= mu[d];
   }
-  // identity eigenvector matrix
-  for (int i = tid; i < 64 * 64; i += 256) W[(i / 64) * kGStride + (i % 64)] = (i / 64 == i % 64) ? 1.f : 0.f;
   __syncthreads();
   // 3b. query-subspace projection [COBS 2.3, compression]: the centred keys
   // become P (k - mean), ED numbers each (rows ED .. D-1 of Ct zeroed), so the
   // steps below factorise the projected covariance P Sigma P^T.  Wave w owns
-  // basis rows w, w + 4, ...; lane r owns token r.
+  // basis rows w, w + 4, ...; lane r owns token r.  P passes through LDS (W,
+  // free until the eigenvectors) 32 columns at a time; every lane of a wave
+  // reads the same P entries (broadcast), 4 columns per read.
   const int ED = a.basis != nullptr ? a.sub_dim : D;
   if (a.basis != nullptr) {
     const float* P = a.basis + (size_t)(bh % a.n_kv_heads) * ED * D;
+    float4* const Pc = reinterpret_cast<float4*>(W);  // [ED][8] float4: columns d0 .. d0 + 31
     float acc[D / 4];
 #pragma unroll
     for (int u = 0; u < D / 4; ++u) acc[u] = 0.f;
-    for (int d = 0; d < D; ++d) {
-      const float c = Ct[d * kCtStride + lane];
+    for (int d0 = 0; d0 < D; d0 += 32) {
+      for (int i = tid; i < ED * 8; i += 256)
+        Pc[i] = *reinterpret_cast<const float4*>(P + (size_t)(i >> 3) * D + d0 + 4 * (i & 7));
+      __syncthreads();
+#pragma unroll 2
+      for (int c4 = 0; c4 < 8; ++c4) {
+        const float* cr = Ct + (d0 + 4 * c4) * kCtStride + lane;
+        const float x0 = cr[0], x1 = cr[kCtStride], x2 = cr[2 * kCtStride], x3 = cr[3 * kCtStride];
 #pragma unroll
-      for (int u = 0; u < D / 4; ++u) {
-        const int j = wid + 4 * u;
-        if (j < ED) acc[u] = fmaf(P[(size_t)j * D + d], c, acc[u]);
+        for (int u = 0; u < D / 4; ++u) {
+          const int j = wid + 4 * u;
+          if (j < ED) {
+            const float4 p4 = Pc[j * 8 + c4];
+            acc[u] = fmaf(p4.w, x3, fmaf(p4.z, x2, fmaf(p4.y, x1, fmaf(p4.x, x0, acc[u]))));
+          }
+        }
       }
+      __syncthreads();
     }
-    __syncthreads();
 #pragma unroll
     for (int u = 0; u < D / 4; ++u) {
       const int j = wid + 4 * u;
@@ -179,6 +214,7 @@ __global__ __launch_bounds__(256) void summaries_factor_kernel(SummaryArgs a) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) g[i][j] = 0.f;
+#pragma unroll 4
     for (int d = 0; d < ED; ++d) {
       const float4 xa = *reinterpret_cast<const float4*>(&Ct[d * kCtStride + x0]);
       const float4 yb = *reinterpret_cast<const float4*>(&Ct[d * kCtStride + y0]);
@@ -196,103 +232,327 @@ __global__ __launch_bounds__(256) void summaries_factor_kernel(SummaryArgs a) {
   }
   __syncthreads();
 
-  // 5. Jacobi sweeps
-  for (int sweep = 0; sweep < kMaxSweeps; ++sweep) {
-    for (int r = 0; r < 63; ++r) {
-      if (tid < 32) {
-        int p, q;
-        rr_pair(r, tid, p, q);
-        const float app = G[p * kGStride + p], aqq = G[q * kGStride + q], apq = G[p * kGStride + q];
-        float c = 1.f, s = 0.f, t = 0.f;
-        if (apq != 0.f && fabsf(apq) > 1e-10f * (fabsf(app) + fabsf(aqq))) {
-          const float tau = (aqq - app) / (2.f * apq);
-          const float sg = tau >= 0.f ? 1.f : -1.f;
-          t = fabsf(tau) > 1e18f ? 0.5f / tau : sg / (fabsf(tau) + sqrtf(1.f + tau * tau));
-          c = 1.f / sqrtf(1.f + t * t);
-          s = t * c;
-        }
-        rp[tid] = p; rq[tid] = q; rc[tid] = c; rs[tid] = s; rt[tid] = t;
-      }
-      __syncthreads();
-      // G <- J^T G J on 2x2 pair blocks (P rows, Q cols); each block owned by one thread.
+  // 5. Householder tridiagonalisation, G = Q T Q^T with Q = H_0 .. H_61: the
+  //    reflection H_k = I - beta_k u u^T (u zero in rows 0 .. k) zeroes column
+  //    k below the subdiagonal; the trailing block becomes B - u w^T - w u^T
+  //    with p = beta B u, w = p - (beta/2)(u.p) u.  Thread t keeps row t / 4,
+  //    columns t % 4 + 4 (j + sh) (j < 16), of the matrix in registers for all
+  //    62 steps; every 4 steps the row shifts down one register (sh grows; the
+  //    column dropped is already reduced), so the column a step hands on
+  //    (xc) is always register 0 of its owners: no dynamic register index.
+  //    Every wave forms u itself from xc into its own copy uw[wave] (zero
+  //    past row 63, like tp), so a step needs two barriers (p and the waves'
+  //    shares of u.p complete; the next column complete).  u_k is kept in row k of G for the
+  //    back-transformation.
+  constexpr int S = kGStride;
+  const int grow = tid >> 2, gq = tid & 3;
+  float gr[16];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int blkid = tid + 256 * k;  // 0..1023
-        const int P = blkid >> 5, Q = blkid & 31;
-        const int pP = rp[P], qP = rq[P], pQ = rp[Q], qQ = rq[Q];
-        const float cP = rc[P], sP = rs[P], cQ = rc[Q], sQ = rs[Q];
-        const float g00 = G[pP * kGStride + pQ], g01 = G[pP * kGStride + qQ];
-        const float g10 = G[qP * kGStride + pQ], g11 = G[qP * kGStride + qQ];
-        // rows: new_p = c g_p - s g_q ; new_q = s g_p + c g_q
-        const float r00 = cP * g00 - sP * g10, r01 = cP * g01 - sP * g11;
-        const float r10 = sP * g00 + cP * g10, r11 = sP * g01 + cP * g11;
-        float n00 = cQ * r00 - sQ * r01, n01 = sQ * r00 + cQ * r01;
-        float n10 = cQ * r10 - sQ * r11, n11 = sQ * r10 + cQ * r11;
-        if (P == Q && (sP != 0.f)) {
-          const float tP = rt[P];
-          n00 = g00 - tP * g01;
-          n11 = g11 + tP * g01;
-          n01 = 0.f;
-          n10 = 0.f;
+  for (int j = 0; j < 16; ++j) gr[j] = G[grow * S + gq + 4 * j];
+  int sh = 0;
+  uw[wid][64 + lane] = 0.f;
+  if (tid < 64) tp[64 + tid] = 0.f;
+  if (gq == 0) xc[grow] = gr[0];  // column 0
+  __syncthreads();  // every row loaded from G (now free for u) and column 0 in xc
+  for (int k = 0; k < 62; ++k) {
+    float* const uu = uw[wid];
+    float beta = 0.f;  // the same in every wave
+    {
+      const float xl = xc[lane];
+      const float xr = lane > k ? xl : 0.f;
+      const float x0r = rl(xl, k + 1);
+      const float sr = wsum(lane > k + 1 ? xr * xr : 0.f);
+      float alpha = x0r, u = 0.f;
+      if (sr > 1e-30f && sr < 1e30f) {
+        const float mu = sqrtf(fmaf(x0r, x0r, sr));
+        const float u0 = x0r >= 0.f ? x0r + mu : x0r - mu;  // no cancellation
+        alpha = x0r >= 0.f ? -mu : mu;
+        beta = 2.f / fmaf(u0, u0, sr);
+        u = lane == k + 1 ? u0 : xr;
+      } else if (sr != 0.f) {
+        // squares near the ends of the range: u is scale-free, so the column
+        // is scaled to max-abs 1 first
+        const float xm = wmax(fabsf(xr));
+        const float x = xr / xm;
+        const float sig = wsum(lane > k + 1 ? x * x : 0.f);
+        const float x0 = rl(x, k + 1);
+        const float mu = sqrtf(fmaf(x0, x0, sig));
+        const float u0 = x0 >= 0.f ? x0 + mu : x0 - mu;
+        alpha = (x0 >= 0.f ? -mu : mu) * xm;
+        beta = 2.f / fmaf(u0, u0, sig);
+        u = lane == k + 1 ? u0 : x;
+      }  // sr == 0: the column is already reduced (beta = 0, u = 0)
+      uu[lane] = u;  // zero in rows 0 .. k
+      if (wid == 0) {
+        G[k * S + lane] = u;
+        const float dk = rl(xl, k);
+        if (lane == 0) {
+          td[k] = dk;
+          te[k] = alpha;
+          tb[k] = beta;
         }
-        G[pP * kGStride + pQ] = n00; G[pP * kGStride + qQ] = n01;
-        G[qP * kGStride + pQ] = n10; G[qP * kGStride + qQ] = n11;
       }
-      // W <- W J (columns p, q of every row)
+    }
+    // p = beta B u for this row (rows 0 .. k get 0, so they stay untouched),
+    // and this wave's share of u.(beta p)
+    const float* const uc4 = uu + gq + 4 * sh;
+    const float* const tc4 = tp + gq + 4 * sh;
+    float ucv[16];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int u = tid + 256 * k;  // 0..2047
-        const int row = u >> 5, P = u & 31;
-        const int p = rp[P], q = rq[P];
-        const float c = rc[P], s = rs[P];
-        const float wp = W[row * kGStride + p], wq = W[row * kGStride + q];
-        W[row * kGStride + p] = c * wp - s * wq;
-        W[row * kGStride + q] = s * wp + c * wq;
-      }
-      __syncthreads();
-    }
-    // convergence: off-diagonal mass against the diagonal.  In fp32 the sum of
-    // squared off-diagonal entries settles near 5e-14 of the diagonal's (the
-    // rounding floor of a 64 x 64 rotation sequence), reached after 6 or 7
-    // sweeps from a Gram of centred keys; 1e-12 (off-diagonal norm 1e-6 of the
-    // diagonal's) stops there instead of running every sweep at the floor.
-    float off = 0.f, dia = 0.f;
-    for (int i = tid; i < 64 * 64; i += 256) {
-      const int x = i >> 6, y = i & 63;
-      const float g = G[x * kGStride + y];
-      if (x == y) dia += g * g; else off += g * g;
-    }
-    off = wave_sum(off);
-    dia = wave_sum(dia);
-    if (lane == 0) { red[wid] = off; red[4 + wid] = dia; }
+    for (int j = 0; j < 16; ++j) ucv[j] = uc4[4 * j];
+    const float ur = uu[grow];
+    float pa[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 16; ++j) pa[j & 3] = fmaf(gr[j], ucv[j], pa[j & 3]);
+    float pr = (pa[0] + pa[1]) + (pa[2] + pa[3]);
+    pr += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(pr), 0xb1, 0xf, 0xf, false));  // quad_perm 1,0,3,2
+    pr += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(pr), 0x4e, 0xf, 0xf, false));  // quad_perm 2,3,0,1
+    const float tr = grow > k ? beta * pr : 0.f;
+    if (gq == 0) tp[grow] = tr;
+    const float part = wsum(gq == 0 ? ur * tr : 0.f);
+    if (lane == 0) kpart[wid] = part;
     __syncthreads();
-    const float offt = red[0] + red[1] + red[2] + red[3];
-    const float diat = red[4] + red[5] + red[6] + red[7];
+    const float4 kp = *reinterpret_cast<const float4*>(kpart);
+    const float kk = 0.5f * beta * ((kp.x + kp.y) + (kp.z + kp.w));  // (beta / 2) u.p
+    const float wr = tr - kk * ur;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float uc = ucv[j], wc = tc4[4 * j] - kk * uc;
+      gr[j] -= fmaf(ur, wc, wr * uc);
+    }
+    if (((k + 1) & 3) == 0) {
+#pragma unroll
+      for (int j = 0; j < 15; ++j) gr[j] = gr[j + 1];
+      gr[15] = 0.f;
+      ++sh;
+    }
+    if (gq == ((k + 1) & 3)) xc[grow] = gr[0];  // column k + 1
     __syncthreads();
-    if (offt <= 1e-12f * diat) break;
   }
+  // the last 2 x 2 block: column 62 is in xc; G[63][63] from its owner
+  if (tid == 0) {
+    td[62] = xc[62];
+    te[62] = xc[63];
+    tb[62] = 0.f;
+  }
+  if (grow == 63 && gq == 3) td[63] = gr[0];  // column 63 = 3 + 4 (0 + 15)
+  __syncthreads();
 
-  // 6. top-r eigenvalues (descending, lower index first on ties)
-  if (tid < 64) {
-    const float lx = G[tid * kGStride + tid];
-    int rank = 0;
-    for (int y = 0; y < 64; ++y) {
-      const float ly = G[y * kGStride + y];
-      rank += (ly > lx) || (ly == lx && y < tid);
+  // 6. top-r eigenvalues of T (d = td, off-diagonal e = te): count(x), the
+  //    number of eigenvalues below x, is the number of negative pivots of the
+  //    LDL^T factorisation of T - x I (Sturm sequence / Sylvester inertia).
+  //    Eigenvalue j (descending) is bracketed by the Gershgorin interval and
+  //    narrowed 65-fold per round: lane l counts at the l + 1-th of 64 interior
+  //    points.  Wave w takes j = w and w + 4 together.
+  const int R = a.rank;
+  const float dl = td[lane];
+  const float el = lane > 0 ? fabsf(te[lane - 1]) : 0.f, er = lane < 63 ? fabsf(te[lane]) : 0.f;
+  const float glo = wmin(dl - el - er), ghi = wmax(dl + el + er);
+  const float pivmin = 1e-30f * fmaxf(1.f, wmax(er * er));
+  const float tnorm = fmaxf(fabsf(glo), fabsf(ghi));
+  auto count_below1 = [&](float x0, int& c0) {
+    float q0 = td[0] - x0;
+    if (fabsf(q0) < pivmin) q0 = -pivmin;
+    c0 = q0 < 0.f;
+#pragma unroll 9
+    for (int i = 1; i < 64; ++i) {
+      const float e = te[i - 1];
+      q0 = fmaf(-(e * e), __builtin_amdgcn_rcpf(q0), td[i] - x0);
+      if (fabsf(q0) < pivmin) q0 = -pivmin;
+      c0 += q0 < 0.f;
     }
-    if (rank < a.rank) pick[rank] = tid;
+  };
+  // counts at two points (two independent recurrences side by side)
+  auto count_below2 = [&](float x0, float x1, int& c0, int& c1) {
+    float q0 = td[0] - x0, q1 = td[0] - x1;
+    if (fabsf(q0) < pivmin) q0 = -pivmin;
+    if (fabsf(q1) < pivmin) q1 = -pivmin;
+    c0 = q0 < 0.f;
+    c1 = q1 < 0.f;
+#pragma unroll 9
+    for (int i = 1; i < 64; ++i) {
+      const float e = te[i - 1], d = td[i];
+      q0 = fmaf(-(e * e), __builtin_amdgcn_rcpf(q0), d - x0);
+      q1 = fmaf(-(e * e), __builtin_amdgcn_rcpf(q1), d - x1);
+      if (fabsf(q0) < pivmin) q0 = -pivmin;
+      if (fabsf(q1) < pivmin) q1 = -pivmin;
+      c0 += q0 < 0.f;
+      c1 += q1 < 0.f;
+    }
+  };
+  if (wid < R) {
+    const int j0 = wid, j1 = wid + 4;  // ranks from the top; j1 only when r > 4
+    const int t0 = 63 - j0, t1 = 63 - j1;
+    const float tol = 2e-7f * tnorm;
+    float lo0 = glo - 1e-6f * tnorm - pivmin, hi0 = ghi + 1e-6f * tnorm + pivmin;  // count(lo) = 0, count(hi) = 64
+    float lo1 = lo0, hi1 = hi0;
+    for (int it = 0; it < 8; ++it) {
+      const bool go0 = hi0 - lo0 > tol, go1 = j1 < R && hi1 - lo1 > tol;
+      if (!go0 && !go1) break;
+      const float f = (float)(lane + 1) * (1.f / 65.f);
+      const float x0 = fmaf(hi0 - lo0, f, lo0), x1 = fmaf(hi1 - lo1, f, lo1);
+      int c0, c1 = 0;
+      if (j1 < R) count_below2(x0, x1, c0, c1);
+      else count_below1(x0, c0);
+      if (go0) {
+        const uint64_t above = __ballot(c0 > t0);
+        const int L = above ? __ffsll((unsigned long long)above) - 1 : 64;
+        const float nhi = L < 64 ? rl(x0, L) : hi0;
+        lo0 = L > 0 ? rl(x0, L - 1) : lo0;
+        hi0 = nhi;
+      }
+      if (go1) {
+        const uint64_t above = __ballot(c1 > t1);
+        const int L = above ? __ffsll((unsigned long long)above) - 1 : 64;
+        const float nhi = L < 64 ? rl(x1, L) : hi1;
+        lo1 = L > 0 ? rl(x1, L - 1) : lo1;
+        hi1 = nhi;
+      }
+    }
+    if (lane == 0) {
+      lam[j0] = 0.5f * (lo0 + hi0);
+      if (j1 < R) lam[j1] = 0.5f * (lo1 + hi1);
+    }
   }
   __syncthreads();
-  // 7. factor rows sqrt(lambda_i) v_i = C^T w_i / sqrt(L)
-  for (int o = tid; o < a.rank * ED; o += 256) {
+
+  // 7. eigenvectors of T by inverse iteration: lane j < r of wave 0 factors
+  //    T - lambda_j I with partial pivoting (rows i, i + 1; the upper factor
+  //    has two superdiagonals), then two solves from a fixed start vector;
+  //    after each solve the wave orthonormalises the r vectors in order (lane i
+  //    holds entry i).  Work rows (stride S): u0 (reciprocal pivots), u1, u2
+  //    (upper factor), ml (multipliers), z (vectors), 8 rows each, in W.
+  float* const U0 = W;
+  float* const U1 = W + 8 * S;
+  float* const U2 = W + 16 * S;
+  float* const ML = W + 24 * S;
+  float* const Z = W + 32 * S;
+  const float tiny = 1e-7f * tnorm + 1e-30f;
+  if (wid == 0) {
+    uint64_t swp = 0ull;
+    if (lane < R) {
+      const float lmb = lam[lane];
+      float* const u0 = U0 + lane * S;
+      float* const u1 = U1 + lane * S;
+      float* const u2 = U2 + lane * S;
+      float* const ml = ML + lane * S;
+      float* const z = Z + lane * S;
+      float ad = td[0] - lmb, cu = te[0];
+      // u0 keeps the reciprocal pivots
+      for (int i = 0; i < 63; ++i) {
+        const float b = te[i], an = td[i + 1] - lmb, cn = i < 62 ? te[i + 1] : 0.f;
+        const bool keep = fabsf(ad) >= fabsf(b);  // pivot on the current row
+        const float pv = keep ? (fabsf(ad) < tiny ? copysignf(tiny, ad) : ad) : b;
+        const float ri = 1.f / pv;
+        const float mt = (keep ? b : ad) * ri;
+        u0[i] = ri;
+        u1[i] = keep ? cu : an;
+        u2[i] = keep ? 0.f : cn;
+        ml[i] = mt;
+        swp |= (uint64_t)(!keep) << i;
+        const float nad = keep ? fmaf(-mt, cu, an) : fmaf(-mt, an, cu);
+        cu = keep ? cn : -mt * cn;
+        ad = nad;
+      }
+      u0[63] = 1.f / (fabsf(ad) < tiny ? copysignf(tiny, ad) : ad);
+      for (int i = 0; i < 64; ++i) z[i] = 1.f + (float)((37 * i + 11 * lane) % 17) * (1.f / 34.f);
+    }
+    for (int it = 0; it < 2; ++it) {
+      if (lane < R) {
+        const float* const u0 = U0 + lane * S;
+        const float* const u1 = U1 + lane * S;
+        const float* const u2 = U2 + lane * S;
+        const float* const ml = ML + lane * S;
+        float* const z = Z + lane * S;
+        // forward: the row swaps and multipliers, 9 rows a batch (loads first)
+        float yi = z[0];
+        for (int i0 = 0; i0 < 63; i0 += 9) {
+          float zn[9], mm[9];
+#pragma unroll
+          for (int t = 0; t < 9; ++t) {
+            zn[t] = z[i0 + t + 1];
+            mm[t] = ml[i0 + t];
+          }
+#pragma unroll
+          for (int t = 0; t < 9; ++t) {
+            const bool sw = (swp >> (i0 + t)) & 1ull;
+            const float piv = sw ? zn[t] : yi, oth = sw ? yi : zn[t];
+            z[i0 + t] = piv;
+            yi = fmaf(-mm[t], piv, oth);
+          }
+        }
+        // back substitution, 9 rows a batch (rows 62 .. 0)
+        float x1 = yi * u0[63], x2 = 0.f;
+        z[63] = x1;
+        for (int i0 = 62; i0 >= 0; i0 -= 9) {
+          float zz[9], a0[9], a1[9], a2[9];
+#pragma unroll
+          for (int t = 0; t < 9; ++t) {
+            zz[t] = z[i0 - t];
+            a0[t] = u0[i0 - t];
+            a1[t] = u1[i0 - t];
+            a2[t] = u2[i0 - t];
+          }
+#pragma unroll
+          for (int t = 0; t < 9; ++t) {
+            const float x = (zz[t] - a1[t] * x1 - a2[t] * x2) * a0[t];
+            z[i0 - t] = x;
+            x2 = x1;
+            x1 = x;
+          }
+        }
+      }
+      // orthonormalise in order (modified Gram-Schmidt; each vector first
+      // scaled to max-abs 1 so the squares cannot overflow); lane = entry
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = j < R ? Z[j * S + lane] : 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j < R) {
+          const float mx = wmax(fabsf(v[j]));
+          v[j] *= mx > 0.f ? 1.f / mx : 0.f;
+#pragma unroll
+          for (int jj = 0; jj < j; ++jj) v[j] = fmaf(-wsum(v[j] * v[jj]), v[jj], v[j]);
+          const float nn = wsum(v[j] * v[j]);
+          v[j] *= nn > 0.f ? rsqrtf(nn) : 0.f;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j < R) Z[j * S + lane] = v[j];
+    }
+  }
+  __syncthreads();
+  // back to G's basis: w = H_0 .. H_61 z (H_61 first); wave w takes vectors
+  // w and w + 4, lane = entry
+  {
+    const int j0 = wid, j1 = wid + 4;
+    float y0 = j0 < R ? Z[j0 * S + lane] : 0.f, y1 = j1 < R ? Z[j1 * S + lane] : 0.f;
+    if (j0 < R) {
+#pragma unroll 2
+      for (int k = 61; k >= 0; --k) {
+        const float beta = tb[k];
+        const float u = G[k * S + lane];  // zero in rows 0 .. k (all zero when beta = 0)
+        const float d0 = wsum(u * y0), d1 = wsum(u * y1);
+        y0 = fmaf(-beta * d0, u, y0);
+        y1 = fmaf(-beta * d1, u, y1);
+      }
+    }
+    __syncthreads();  // every wave has read Z before any writes its result back
+    if (j0 < R) Z[j0 * S + lane] = y0;
+    if (j1 < R) Z[j1 * S + lane] = y1;
+  }
+  __syncthreads();
+  // 8. factor rows sqrt(lambda_i) v_i = C^T w_i / sqrt(L)
+  for (int o = tid; o < R * ED; o += 256) {
     const int i = o / ED, d = o % ED;
-    const int x = pick[i];
     float s = 0.f;
-    for (int r = 0; r < kBlock; ++r) s = fmaf(Ct[d * kCtStride + r], W[r * kGStride + x], s);
+    for (int r = 0; r < kBlock; ++r) s = fmaf(Ct[d * kCtStride + r], Z[i * S + r], s);
     F[i * D + d] = s * 0.125f;  // 1/sqrt(64)
   }
   __syncthreads();
-  // 8. sign: entry of largest magnitude (first on ties) made positive; one wave per row
+  // 9. sign: entry of largest magnitude (first on ties) made positive; one wave per row
   for (int i = wid; i < a.rank; i += 4) {
     float best = -1.f;
     int bidx = D;
