@@ -38,13 +38,15 @@ if ROOT not in sys.path:
 HBM_PEAK = 8.0e12          # B/s, MI355X HBM3E
 CALIB_BYTES = 512 << 20    # the plain device copy --calibrate-copy runs (bytes read = bytes written)
 
-# HBM bytes per decode step (the three launches of bsattn_decode_step) of the
-# 32K first-order workload, from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs
-# of `bench.py --only first_order_decode_32k --calibrate-copy`, each scaled by
-# CALIB_BYTES / (the same counter for the calibration copy).  Valid only for
-# the sources it was taken on (their SHA-256); otherwise traffic is null.
-STEP_TRAFFIC = {"sources_sha256": "332ec38c7fec9baafffa038beae9cf01dea54ae2fac3a28e2c14e7e04e8118d5",
-                "bytes_per_step": 128378691}  # FETCH x 1.9999 (8487.5 + 51811.2 + 1080.5 KiB) + WRITE x 1 (256.0 + 2088.8 + 272.0 KiB)
+# HBM bytes per decode step (the launches of bsattn_decode_step), from
+# rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs of `bench.py --only <workload>
+# --calibrate-copy`, each scaled by CALIB_BYTES / (the same counter for the
+# calibration copy: FETCH x 1.9999, WRITE x 1.0), summed over the step's
+# launches.  Valid only for the sources they were taken on (their SHA-256);
+# otherwise traffic is null.
+STEP_TRAFFIC = {"sources_sha256": "bdb4d6f67b8d9c8f787824d64d9a7efa73ac0838faf91fa176951fe636936f60",
+                "bytes_per_step": {"first_order_decode_32k": 125222074,
+                                   "cobs_decode_128k": 89536619}}
 STEP_SOURCES = ("sliding_window_attention_block_amd/csrc/decode.hip",
                 "sliding_window_attention_block_amd/csrc/select.hip",
                 "sliding_window_attention_block_amd/csrc/bsattn.cpp",
@@ -52,23 +54,38 @@ STEP_SOURCES = ("sliding_window_attention_block_amd/csrc/decode.hip",
                 "sliding_window_attention_block_amd/csrc/launch.hpp")
 
 
-def step_sources_sha256():
+def sources_sha256(files):
     import hashlib
     h = hashlib.sha256()
-    for f in STEP_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def step_traffic():
-    if STEP_TRAFFIC["sources_sha256"] == step_sources_sha256():
-        return STEP_TRAFFIC["bytes_per_step"]
+def step_traffic(name=None):
+    if STEP_TRAFFIC["sources_sha256"] == sources_sha256(STEP_SOURCES):
+        return STEP_TRAFFIC["bytes_per_step"].get(name or HEADLINE)
     return None
-# HBM bytes per launch of the prefill kernels (rocprofv3 --pmc FETCH_SIZE and
-# WRITE_SIZE, calibrated as above), keyed by workload; absent until taken on the
-# current sources
-PREFILL_TRAFFIC = {}
+# HBM bytes per call of the prefill kernels (rocprofv3 --pmc FETCH_SIZE and
+# WRITE_SIZE, calibrated as above, summed over the call's launches), keyed by
+# workload; valid only for the sources they were taken on, otherwise null.
+PREFILL_TRAFFIC = {"sources_sha256": "2ffebe020af819403925e52db8235d72d5aefa4b8b3a423427c83c647768e45d",
+                   "bytes_per_call": {"swa_prefill_8k": 280330389,
+                                      "local_global_prefill_16k": 441188952,
+                                      "sparse_prefill_8k": 285970125}}
+PREFILL_SOURCES = ("sliding_window_attention_block_amd/csrc/prefill.hip",
+                   "sliding_window_attention_block_amd/csrc/select.hip",
+                   "sliding_window_attention_block_amd/csrc/summaries.hip",
+                   "sliding_window_attention_block_amd/csrc/bsattn.cpp",
+                   "sliding_window_attention_block_amd/csrc/device.hpp",
+                   "sliding_window_attention_block_amd/csrc/launch.hpp")
+
+
+def prefill_traffic(name):
+    if PREFILL_TRAFFIC["sources_sha256"] == sources_sha256(PREFILL_SOURCES):
+        return PREFILL_TRAFFIC["bytes_per_call"].get(name)
+    return None
 BF16_PEAK = 2.5e15         # flop/s, MI355X dense bf16 MFMA
 MALL_BYTES = 256 << 20
 METRIC = "sparse-decode tokens/s and gathered-KV GB/s (% HBM peak); prefill % MFMA peak"
@@ -92,6 +109,10 @@ def gpu_state():
     import re
     import subprocess
     out = {}
+    if "rocprof" in os.environ.get("LD_PRELOAD", ""):
+        # under rocprofv3 the smi tools (python scripts) would start with the
+        # profiler's library preloaded; the profile has its own clock counters
+        return {"skipped": "run under rocprofv3"}
 
     def run(cmd):
         try:
@@ -363,6 +384,9 @@ def bench_decode(api, torch, w, x, steps, warmup, mean_dtype="bf16", factor_fp4=
     # outputs (scores, sel, O, lse), each once
     res["step_bytes"] = summ_bytes + basis_bytes + kv_bytes + io_bytes + B * Hkv * nb * 4
     res["step_GBps"] = res["step_bytes"] / (ms_step * 1e-3) / 1e9
+    # measured HBM bytes of the step (counters; the workload's default row only)
+    default_row = mean_dtype == "bf16" and factor_fp4 and subspace and not page_tokens
+    res["traffic_bytes"] = step_traffic(w.name) if default_row else None
     del reps
     torch.cuda.empty_cache()
     return res
@@ -485,7 +509,7 @@ def bench_sparse_prefill(api, torch, w, x, steps, warmup):
                window=wl + 1, sinks=ns, top_k=k, attend_ms_dist=attend_dist,
                roofline=dict(bound="mfma", kernel="the sparse attention launch (prefill_kernel, block-sparse)",
                              achieved=flops / (attend_ms * 1e-3) / 1e12, peak=BF16_PEAK / 1e12, unit="TFLOP/s",
-                             frac=flops / (attend_ms * 1e-3) / BF16_PEAK, traffic=PREFILL_TRAFFIC.get(w.name),
+                             frac=flops / (attend_ms * 1e-3) / BF16_PEAK, traffic=prefill_traffic(w.name),
                              flop_per_launch=flops, avg_launch_ms=attend_ms))
     del reps
     torch.cuda.empty_cache()
@@ -541,10 +565,10 @@ def bench_prefill(api, torch, w, x, steps, warmup):
     if flops / BF16_PEAK >= io / HBM_PEAK:
         res["roofline"] = dict(bound="mfma", achieved=flops / (k_ms * 1e-3) / 1e12, peak=BF16_PEAK / 1e12,
                                unit="TFLOP/s", frac=flops / (k_ms * 1e-3) / BF16_PEAK,
-                               traffic=PREFILL_TRAFFIC.get(w.name), flop_per_launch=flops, avg_launch_ms=k_ms)
+                               traffic=prefill_traffic(w.name), flop_per_launch=flops, avg_launch_ms=k_ms)
     else:
         res["roofline"] = dict(bound="hbm", achieved=io / (k_ms * 1e-3) / 1e9, peak=HBM_PEAK / 1e9, unit="GB/s",
-                               frac=io / (k_ms * 1e-3) / HBM_PEAK, traffic=PREFILL_TRAFFIC.get(w.name),
+                               frac=io / (k_ms * 1e-3) / HBM_PEAK, traffic=prefill_traffic(w.name),
                                bytes_per_launch=io, avg_launch_ms=k_ms,
                                mfma_frac=flops / (k_ms * 1e-3) / BF16_PEAK)
     return res
