@@ -504,7 +504,9 @@ hipError_t launch_mfma(const SelectArgs& a0, hipStream_t stream) {
   SelectArgs a = a0;
   if (a.n_blocks > 0) {
     const long long units = (a.n_blocks + 15) / 16;
-    split_units(a, units, 256 * 8);
+    // with a query subspace every workgroup projects its pair's queries, so
+    // fewer, longer workgroups (half the resident waves) measured faster
+    split_units(a, units, SK > 0 ? 256 * 4 : 256 * 8);
     if (SK > 0 && a.n_part % 4 != 0) {
       // the four waves of a workgroup share a pair (one projection, one barrier)
       a.n_part = (a.n_part + 3) / 4 * 4;
