@@ -3,8 +3,9 @@
 
 Step (the timed unit): one decode step of the first-order 32K workload (batch
 16, 32 query / 8 K/V heads, d 128, 64-token blocks, top-16 + sink block + 512-
-token window), one bsattn_decode_step call: selector scoring, then the sparse
-decode whose waves take the top-k themselves, then the log-sum-exp merge.
+token window), one bsattn_decode_step call: the sparse decode kernel, whose
+workgroups score their pair's blocks and whose waves take the top-k
+themselves, then the log-sum-exp merge.
 `value` is tokens/s = batch / step time.  Summaries are built once
 before timing (as the method builds them when blocks fill), with the block
 means stored in bfloat16 as the COBS explainer stores them (the same step with
@@ -759,8 +760,8 @@ def main():
         "gathered_kv_GBps": h.get("gathered_kv_GBps"),
         "gathered_kv_frac_hbm": h.get("gathered_kv_frac_hbm"),
         "roofline": {
-            "kernel": "bsattn_decode_step: select_scores_mfma_kernel, decode_bf16_kernel with the "
-                      "in-wave top-k, decode_merge_kernel (one call, three launches)",
+            "kernel": "bsattn_decode_step: decode_bf16_kernel with in-kernel scoring and the in-wave "
+                      "top-k, decode_merge_kernel (one call, two launches)",
             "bound": "hbm",
             "achieved": h["step_bytes"] / (h["ms_per_step"] * 1e-3) / 1e9,
             "peak": HBM_PEAK / 1e9,

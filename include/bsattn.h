@@ -251,9 +251,11 @@ bsattn_status bsattn_decode(const bsattn_shape* shape, const void* Q, const void
  * top_k <= 256 the top-k runs inside the decode kernel (each decode wave
  * selects its pair's blocks while its sink and window loads are in flight),
  * one launch fewer than the two calls; the selection is the same exact
- * top-k (score descending, then block index ascending).  Otherwise the step
- * runs the two calls' kernels.  Calls that share a workspace must be ordered
- * (same stream).
+ * top-k (score descending, then block index ascending).  When in addition
+ * rank == 0 and the means are BF16, the decode workgroups also compute the
+ * scores (the same products and sums as the scoring kernel), so the step has
+ * no scoring launch.  Otherwise the step runs the two calls' kernels.  Calls
+ * that share a workspace must be ordered (same stream).
  */
 bsattn_status bsattn_decode_step(const bsattn_shape* shape, const void* Q, const void* K,
                                  const void* V, const void* mean, int32_t mean_dtype,

@@ -556,8 +556,17 @@ bsattn_status bsattn_decode_step(const bsattn_shape* shape, const void* Q, const
     for (int j = 0; j < nb; ++j)
       if (bsattn::forced_mask(da.forced, j) == ~0ull) da.full_forced[j >> 6] |= 1ull << (j & 63);
   }
-  hipError_t e = bsattn::launch_select_topk(sa, (hipStream_t)hip_stream);
-  if (e != hipSuccess) return fail(BSATTN_ERR_HIP, "select launch: %s", hipGetErrorString(e));
+  // first order with bfloat16 means: the decode workgroups score the blocks
+  // themselves (one launch, plus the merge when a pair has several workgroups)
+  const bool scored_in_decode = fused && sa.rank == 0 && sa.mean_bf16;
+  hipError_t e = hipSuccess;
+  if (scored_in_decode) {
+    da.mean = mean;
+    da.scores_out = scores;
+  } else {
+    e = bsattn::launch_select_topk(sa, (hipStream_t)hip_stream);
+    if (e != hipSuccess) return fail(BSATTN_ERR_HIP, "select launch: %s", hipGetErrorString(e));
+  }
   e = bsattn::launch_decode(da, (hipStream_t)hip_stream);
   if (e != hipSuccess) return fail(BSATTN_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return BSATTN_OK;

@@ -411,8 +411,19 @@ __device__ __forceinline__ void compute_half(const Stage<D>& st, uint8_t* vt, co
 // 512-register budget of a SIMD (one workgroup of 4 waves per CU); d = 64 fits
 // two workgroups per CU.  PL > 0: fused step, PL scores per lane for the
 // in-wave top-k; PL = 0: the selection comes from `sel`.  PAGED: K and V are
-// page pools read through the block table.
-template <int D, int PL, bool PAGED>
+// page pools read through the block table.  SC (with PL > 0): the workgroup
+// also scores its pair's blocks (first-order score from bfloat16 block means,
+// COBS explainer technical summary 2.1; group score = log of the summed
+// exponentials over the group's query heads), so the step needs no scoring
+// launch: each wave scores 64 PL / 4 blocks on v_mfma_f32_16x16x32_bf16 (A =
+// the group's queries, B = 16 mean rows; products exact in bfloat16, sums in
+// fp32, the same operations as the scoring kernel), the scores meet in LDS,
+// and every wave then selects from them.  The mean loads are issued before
+// the first forced half items' loads, so the scoring waits for the means
+// alone while the forced K/V rows stream in.  The workgroups of one pair are
+// placed on one XCD (workgroups are dispatched to the 8 XCDs round robin), so
+// the second read of the pair's means hits that XCD's L2.
+template <int D, int PL, bool PAGED, bool SC = false>
 __global__ __launch_bounds__(64 * kW, D == 128 ? 1 : 2) void decode_bf16_kernel(DecodeArgs args) {
   // The arguments are read in place from the kernel-argument segment (the
   // only explicit argument sits at its offset 0): per-lane lookups into the
@@ -427,9 +438,19 @@ __global__ __launch_bounds__(64 * kW, D == 128 ? 1 : 2) void decode_bf16_kernel(
   const int lane = threadIdx.x & 63;
   // wave-uniform (scalar registers): every item index, block and mask below is too
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int gw = blockIdx.x * kW + wid;  // global wave index
   const int n_pairs = a.batch * a.n_kv_heads;
-  const int pair = gw / a.n_part, wi = gw % a.n_part;
+  int pair, wi;
+  if (SC && n_pairs % 8 == 0) {
+    // workgroup wg runs on XCD wg % 8: slot wg / 8 of that XCD holds workgroup
+    // slot % n_merge of pair 8 (slot / n_merge) + wg % 8
+    const int wg = blockIdx.x, xcd = wg & 7, slot = wg >> 3;
+    pair = (slot / a.n_merge) * 8 + xcd;
+    wi = (slot % a.n_merge) * kW + wid;
+  } else {
+    const int gw = blockIdx.x * kW + wid;  // global wave index
+    pair = gw / a.n_part;
+    wi = gw % a.n_part;
+  }
   // n_part is a multiple of kW: the four waves of a workgroup share one pair,
   // so this exit is uniform over the workgroup (it meets barriers at the end)
   if (pair >= n_pairs) return;
@@ -441,7 +462,7 @@ __global__ __launch_bounds__(64 * kW, D == 128 ? 1 : 2) void decode_bf16_kernel(
   // fused step: the pair's group scores, loaded before anything else so the
   // selection waits for them alone
   float sv[PL > 0 ? PL : 1];
-  if constexpr (PL > 0) {
+  if constexpr (PL > 0 && !SC) {
     const float* sc = a.scores + (size_t)pair * a.nblk_capacity;
     const int nb_last = a.forced.n_ctx / kBlock - 1;  // >= 0 on the fused path
 #pragma unroll
@@ -529,6 +550,69 @@ __global__ __launch_bounds__(64 * kW, D == 128 ? 1 : 2) void decode_bf16_kernel(
   auto comp = [&](const Stage<D>& st) {
     if (st.hmask) compute_half<D>(st, vt, qop, sl2, m_run, l_run, oacc);
   };
+  // SC: this wave's 16-block units of the pair's means (unit t = blocks
+  // 16 (ST wid + t) .. +15, lane (col, kg) reads dims 32 s + 8 kg .. +7 of block
+  // col of the unit; blocks past the last complete one re-read it, unused)
+  constexpr int KS = D / 32;
+  constexpr int ST = SC ? PL : 1;  // units per wave: 4 waves x PL units x 16 = 64 PL blocks
+  __shared__ float s_scores[SC ? 64 * PL : 1];
+  u32x4 mv[ST][KS];
+  auto issue_means = [&]() __attribute__((always_inline)) {
+    if constexpr (SC) {
+      const int nb_last = a.forced.n_ctx / kBlock - 1;
+      const u32x4* mb = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.mean) +
+                                                       (size_t)pair * a.nblk_capacity * D);
+#pragma unroll
+      for (int t = 0; t < ST; ++t) {
+        const int j = min(16 * (ST * wid + t) + h, nb_last);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) mv[t][s] = mb[(size_t)j * (D / 8) + 4 * s + grp];
+      }
+    }
+  };
+  // SC: S^T = Q M^T per unit (lane (col, kg) ends with block col's dot products
+  // for heads 4 kg .. +3), scaled; the group score is the log-sum-exp over the
+  // G heads; the scores meet in LDS (and the pair's first workgroup writes
+  // them out), then every wave takes its PL scores per lane from there
+  auto score = [&]() __attribute__((always_inline)) {
+    if constexpr (SC) {
+      const int NB = a.forced.n_ctx / kBlock;
+#pragma unroll
+      for (int t = 0; t < ST; ++t) {
+        const int j0 = 16 * (ST * wid + t);
+        if (j0 < NB) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < KS; ++s) acc = mfma16x16x32(as_bf16x8(qop[s]), as_bf16x8(mv[t][s]), acc);
+          float sc4[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sc4[i] = acc[i] * a.scale;
+          float mx = -INFINITY;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (4 * grp + i < G) mx = fmaxf(mx, sc4[i]);
+          if (G > 4) mx = fmaxf(mx, __shfl_xor(mx, 16));
+          if (G > 8) mx = fmaxf(mx, __shfl_xor(mx, 32));
+          float sum = 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (4 * grp + i < G) sum += __builtin_amdgcn_exp2f((sc4[i] - mx) * kLog2e);
+          if (G > 4) sum += __shfl_xor(sum, 16);
+          if (G > 8) sum += __shfl_xor(sum, 32);
+          const int j = j0 + h;
+          // sum >= 1 (the max term is exactly 1): log2 needs no range care
+          const float sj = fmaf(__builtin_amdgcn_logf(sum), kLn2, mx);
+          if (grp == 0 && j < NB) {
+            s_scores[j] = sj;
+            if (wi < kW && a.scores_out != nullptr) a.scores_out[(size_t)pair * a.nblk_capacity + j] = sj;
+          }
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int t = 0; t < PL; ++t) sv[t] = s_scores[min(64 * t + lane, NB - 1)];
+    }
+  };
   // fused step: select the pair's blocks (table in this wave's V tile, which
   // the first compute overwrites), write them out from the pair's first wave
   // and fill the selected half of the item table
@@ -544,27 +628,27 @@ __global__ __launch_bounds__(64 * kW, D == 128 ? 1 : 2) void decode_bf16_kernel(
       item_pages();
     }
   };
-  // the first two loads, with the selection after them when both are forced
-  // half items (so it overlaps their latency), before them otherwise
-  auto prologue2 = [&]() __attribute__((always_inline)) {
+  // the first nl (<= 2) loads: on the fused step the forced ones among them
+  // go before the scoring and selection (so those overlap their latency), the
+  // others after; every path runs score() (its barrier) and select() once
+  auto prologue = [&](int nl) __attribute__((always_inline)) {
     if constexpr (PL > 0) {
-      if (nfh >= 2) {
-        load(0, A);
-        load(1, B);
-        select();
-      } else {
-        select();
-        load(0, A);
-        load(1, B);
-      }
+      issue_means();
+      const int pre = min(nfh, nl);
+      if (pre >= 1) load(0, A);
+      if (pre >= 2) load(1, B);
+      score();
+      select();
+      if (nl >= 1 && pre < 1) load(0, A);
+      if (nl >= 2 && pre < 2) load(1, B);
     } else {
-      load(0, A);
-      load(1, B);
+      if (nl >= 1) load(0, A);
+      if (nl >= 2) load(1, B);
     }
   };
 
   if (n >= 4) {
-    prologue2();
+    prologue(2);
     int s = 0;
     for (; s + 3 < n; s += 2) {
       comp(A);
@@ -582,30 +666,20 @@ __global__ __launch_bounds__(64 * kW, D == 128 ? 1 : 2) void decode_bf16_kernel(
       comp(B);
     }
   } else if (n == 3) {
-    prologue2();
+    prologue(2);
     comp(A);
     load(2, A);
     comp(B);
     comp(A);
   } else if (n == 2) {
-    prologue2();
+    prologue(2);
     comp(A);
     comp(B);
   } else if (n == 1) {
-    if constexpr (PL > 0) {
-      if (nfh == 1) {
-        load(0, A);
-        select();
-      } else {
-        select();
-        load(0, A);
-      }
-    } else {
-      load(0, A);
-    }
+    prologue(1);
     comp(A);
   } else {
-    select();  // nothing to attend; the pair's first wave still writes the selection
+    prologue(0);  // nothing to attend; the pair's first wave still writes the selection
   }
 
   l_run += __shfl_xor(l_run, 16);
@@ -802,9 +876,11 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)((waves + kW - 1) / kW)), block(64 * kW);
     if (a.paged.block_table != nullptr) {
       if (a.key_slots == 0) hipLaunchKernelGGL((decode_bf16_kernel<D, 0, true>), grid, block, 0, stream, a);
+      else if (a.mean != nullptr) hipLaunchKernelGGL((decode_bf16_kernel<D, 8, true, true>), grid, block, 0, stream, a);
       else hipLaunchKernelGGL((decode_bf16_kernel<D, 8, true>), grid, block, 0, stream, a);
     } else {
       if (a.key_slots == 0) hipLaunchKernelGGL((decode_bf16_kernel<D, 0, false>), grid, block, 0, stream, a);
+      else if (a.mean != nullptr) hipLaunchKernelGGL((decode_bf16_kernel<D, 8, false, true>), grid, block, 0, stream, a);
       else hipLaunchKernelGGL((decode_bf16_kernel<D, 8, false>), grid, block, 0, stream, a);
     }
   } else {

@@ -157,6 +157,11 @@ struct DecodeArgs {
   int32_t nblk_capacity;
   int32_t* sel_out;
   int32_t key_slots;
+  // scoring in the decode kernel (fused step, bfloat16 means, first order):
+  // the means [B, Hkv, nblk_capacity, d]; the scores go to scores_out (may be
+  // null).  Null mean: the scores come from `scores`.
+  const void* mean;
+  float* scores_out;
   uint64_t full_forced[kFusedMaxBlocks / 64];  // bit j % 64 of word j / 64: complete block j has no candidate token
   float scale;
   bool bf16;
