@@ -247,14 +247,14 @@ bsattn_status bsattn_decode(const bsattn_shape* shape, const void* Q, const void
  * bsattn_decode writes them [COBS 1, 2.1-2.3; SWA 拡張手法; LG].  workspace:
  * at least bsattn_decode_workspace_bytes(shape, top_k, window, n_sink,
  * n_global) bytes, 256-byte aligned, contents need not be initialised (NULL
- * when that size is 0).  With BF16 K/V, at most 512 complete blocks and
- * top_k <= 256 the top-k runs inside the decode kernel (each decode wave
- * selects its pair's blocks while its sink and window loads are in flight),
- * one launch fewer than the two calls; the selection is the same exact
- * top-k (score descending, then block index ascending).  When in addition
- * rank == 0 and the means are BF16, the decode workgroups also compute the
- * scores (the same products and sums as the scoring kernel), so the step has
- * no scoring launch.  Otherwise the step runs the two calls' kernels.  Calls
+ * when that size is 0).  With BF16 K/V and top_k <= 256 the top-k runs inside
+ * the decode kernel while the sink and window loads are in flight (each
+ * decode wave selects its pair's blocks alone up to 512 complete blocks, each
+ * decode workgroup selects them together up to 2048), one launch fewer than
+ * the two calls; the selection is the same exact top-k (score descending,
+ * then block index ascending).  With at most 512 blocks, rank == 0 and BF16
+ * means, the decode workgroups also compute the scores (the same products and
+ * sums as the scoring kernel), so the step has no scoring launch.  Otherwise the step runs the two calls' kernels.  Calls
  * that share a workspace must be ordered (same stream).
  */
 bsattn_status bsattn_decode_step(const bsattn_shape* shape, const void* Q, const void* K,

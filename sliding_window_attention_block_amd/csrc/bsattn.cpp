@@ -544,15 +544,19 @@ bsattn_status bsattn_decode_step(const bsattn_shape* shape, const void* Q, const
                    ws_bytes, paged, da);
   if (st != BSATTN_OK) return st;
   // bf16 with at most 512 complete blocks and top_k <= 256: the decode waves
-  // select; otherwise the top-k kernel does, then the decode reads sel
+  // select (each wave alone); up to 2048 blocks the decode workgroups select
+  // (together); otherwise the top-k kernel does, then the decode reads sel
   const int nb = sa.n_blocks;
   const bool fused = da.bf16 && nb >= 1 && nb <= bsattn::kFusedMaxBlocks && top_k <= bsattn::kFusedMaxTopK;
-  if (fused) {
+  const bool fused_wg = da.bf16 && !fused && nb <= bsattn::kFusedWgMaxBlocks && top_k <= bsattn::kFusedMaxTopK;
+  if (fused || fused_wg) {
     sa.scores_only = true;
     da.scores = scores;
     da.nblk_capacity = nblk_capacity;
     da.sel_out = sel;
-    da.key_slots = 8;
+    da.key_slots = fused ? 8 : -8;
+  }
+  if (fused) {
     for (int j = 0; j < nb; ++j)
       if (bsattn::forced_mask(da.forced, j) == ~0ull) da.full_forced[j >> 6] |= 1ull << (j & 63);
   }

@@ -281,6 +281,138 @@ __device__ __forceinline__ void wave_topk(const DecodeArgs& a, const float (&sv)
   for (int i = base + lane; i < a.top_k; i += 64) tab[i] = -1;
 }
 
+// Exact top-k of one pair by the whole workgroup (kW waves), for up to 64 kW KPT
+// blocks: thread t holds the keys of its contiguous block range [t per,
+// (t + 1) per) (per <= KPT, loaded into `key` by the caller), so thread order
+// is block order.  A radix select over the 256-bin LDS histograms (one per
+// pass, cleared up front; one barrier per pass, after which every wave finds
+// the pass's digit itself), the same keys, candidates and tie rule as the
+// in-wave select; then each thread's taken blocks go to tab[rank] in LDS, the
+// ranks from the waves' prefix counts (one barrier), -1 after the last.  Ends
+// with a barrier: tab is complete for every wave.
+struct WgTopkLds {
+  uint32_t hist[4][256];
+  uint32_t red[kW][3];  // per wave: candidates, AND, OR of their keys
+  int part[kW][2];      // per wave: keys above, keys on the threshold
+};
+template <int KPT>
+__device__ __forceinline__ void wg_topk(const DecodeArgs& a, const uint32_t (&key)[KPT], int j0, int j1,
+                                        WgTopkLds& l, int32_t* tab) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  uint32_t cm = 0u;  // bit t: block j0 + t is a candidate
+  uint32_t kand = ~0u, kor = 0u;
+#pragma unroll
+  for (int t = 0; t < KPT; ++t) {
+    const int j = j0 + t;
+    if (j < j1 && forced_mask(a.forced, j) != ~0ull) {
+      cm |= 1u << t;
+      kand &= key[t];
+      kor |= key[t];
+    }
+  }
+  for (int i = tid; i < 4 * 256; i += 64 * kW) (&l.hist[0][0])[i] = 0u;
+  {
+    const int cnt = __builtin_amdgcn_readlane(wave_incl_scan_dpp(__popc(cm)), 63);
+    uint32_t wa, wo;
+    wave_and_or(kand, kor, wa, wo);
+    if (lane == 0) {
+      l.red[wid][0] = (uint32_t)cnt;
+      l.red[wid][1] = wa;
+      l.red[wid][2] = wo;
+    }
+  }
+  __syncthreads();
+  int tot = 0;
+  uint32_t all_and = ~0u, all_or = 0u;
+#pragma unroll
+  for (int w = 0; w < kW; ++w) {
+    tot += (int)l.red[w][0];
+    all_and &= l.red[w][1];
+    all_or |= l.red[w][2];
+  }
+  const int kk = min(a.top_k, tot);
+  const uint32_t diff = all_and ^ all_or;
+  // 8-bit digits from the highest bit on which candidate keys differ down
+  const int hb = diff ? 31 - __clz(diff) : -1;
+  uint32_t pmask = hb >= 31 ? 0u : ~0u << (hb + 1);
+  uint32_t prefix = all_and & pmask;
+  int remaining = kk;
+  if (kk > 0) {
+    int pass = 0;
+    for (int hi = hb; hi >= 0; ++pass) {
+      const int lo = max(hi - 7, 0);
+      const uint32_t dmask = (2u << (hi - lo)) - 1u;
+      uint32_t* h = l.hist[pass];
+#pragma unroll
+      for (int t = 0; t < KPT; ++t)
+        if (((cm >> t) & 1u) && (key[t] & pmask) == prefix) atomicAdd(&h[(key[t] >> lo) & dmask], 1u);
+      __syncthreads();
+      // every wave: lane l reads digits 255-4l (c4[3]) down to 252-4l (c4[0])
+      const u32x4 c4 = reinterpret_cast<const u32x4*>(h)[63 - lane];
+      const int sum = (int)(c4[0] + c4[1] + c4[2] + c4[3]);
+      int cum = wave_incl_scan_dpp(sum) - sum;
+      int found = -1, above = 0, inbin = 0;
+#pragma unroll
+      for (int u = 3; u >= 0; --u) {
+        if (found < 0 && cum + (int)c4[u] >= remaining) {
+          found = 4 * (63 - lane) + u;
+          above = cum;
+          inbin = (int)c4[u];
+        }
+        cum += (int)c4[u];
+      }
+      const uint64_t hit = __ballot(found >= 0);
+      const int src = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
+      const int digit = __builtin_amdgcn_readlane(found, src);
+      remaining -= __builtin_amdgcn_readlane(above, src);
+      prefix |= (uint32_t)digit << lo;
+      pmask |= dmask << lo;
+      // the same in every wave: every key of the bin is taken, lower bits do not matter
+      if (__builtin_amdgcn_readlane(inbin, src) == remaining) break;
+      hi = lo - 1;
+    }
+  }
+  // keys above the prefix, then the first `remaining` keys on it, in block order
+  int gt = 0, eq = 0;
+#pragma unroll
+  for (int t = 0; t < KPT; ++t) {
+    if (!((cm >> t) & 1u)) continue;
+    const uint32_t km = key[t] & pmask;
+    gt += km > prefix;
+    eq += km == prefix;
+  }
+  const int igt = wave_incl_scan_dpp(gt), ieq = wave_incl_scan_dpp(eq);
+  if (lane == 63) {
+    l.part[wid][0] = igt;
+    l.part[wid][1] = ieq;
+  }
+  __syncthreads();
+  int gt_before = igt - gt, eq_before = ieq - eq;
+#pragma unroll
+  for (int w = 0; w < kW; ++w) {
+    if (w < wid) {
+      gt_before += l.part[w][0];
+      eq_before += l.part[w][1];
+    }
+  }
+  if (kk > 0) {
+    const int take_eq = max(0, min(eq, remaining - eq_before));
+    int pos = gt_before + min(eq_before, remaining);
+    int taken = 0;
+#pragma unroll
+    for (int t = 0; t < KPT; ++t) {
+      if (!((cm >> t) & 1u)) continue;
+      const uint32_t km = key[t] & pmask;
+      if (km > prefix || (km == prefix && taken < take_eq)) {
+        taken += km == prefix;
+        tab[pos++] = j0 + t;
+      }
+    }
+  }
+  for (int i = kk + tid; i < a.top_k; i += 64 * kW) tab[i] = -1;
+  __syncthreads();
+}
+
 template <int D>
 __device__ __forceinline__ void load_half(const uint16_t* Kb, const uint16_t* Vb, int tok0, int last,
                                           Stage<D>& st) {
@@ -423,6 +555,11 @@ __device__ __forceinline__ void compute_half(const Stage<D>& st, uint8_t* vt, co
 // alone while the forced K/V rows stream in.  The workgroups of one pair are
 // placed on one XCD (workgroups are dispatched to the 8 XCDs round robin), so
 // the second read of the pair's means hits that XCD's L2.
+//
+// PL < 0: fused step for up to 64 kW (-PL) blocks: the workgroup selects
+// together (wg_topk, -PL keys per thread, from `scores`), so a pair's
+// selection costs each wave a few barriers instead of a radix select over all
+// its blocks.
 template <int D, int PL, bool PAGED, bool SC = false>
 __global__ __launch_bounds__(64 * kW, D == 128 ? 1 : 2) void decode_bf16_kernel(DecodeArgs args) {
   // The arguments are read in place from the kernel-argument segment (the
@@ -467,6 +604,19 @@ __global__ __launch_bounds__(64 * kW, D == 128 ? 1 : 2) void decode_bf16_kernel(
     const int nb_last = a.forced.n_ctx / kBlock - 1;  // >= 0 on the fused path
 #pragma unroll
     for (int t = 0; t < PL; ++t) sv[t] = sc[min(64 * t + lane, nb_last)];
+  }
+  // PL < 0: this thread's keys, blocks [wj0, wj1) of the pair
+  constexpr int KPT = PL < 0 ? -PL : 1;
+  uint32_t wkey[KPT];
+  int wj0 = 0, wj1 = 0;
+  if constexpr (PL < 0) {
+    const int NB = a.forced.n_ctx / kBlock;
+    const int per = (NB + 64 * kW - 1) / (64 * kW);
+    wj0 = min((int)threadIdx.x * per, NB);
+    wj1 = min(wj0 + per, NB);
+    const float* sc = a.scores + (size_t)pair * a.nblk_capacity;
+#pragma unroll
+    for (int t = 0; t < KPT; ++t) wkey[t] = order_key(sc[min(wj0 + t, NB - 1)]);
   }
 
   const uint16_t* Kb = reinterpret_cast<const uint16_t*>(a.K) + (size_t)pair * a.kv_capacity * D;
@@ -616,7 +766,18 @@ __global__ __launch_bounds__(64 * kW, D == 128 ? 1 : 2) void decode_bf16_kernel(
   // fused step: select the pair's blocks (table in this wave's V tile, which
   // the first compute overwrites), write them out from the pair's first wave
   // and fill the selected half of the item table
+  __shared__ WgTopkLds wg_lds;  // (PL < 0 only; unused LDS objects are not allocated)
+  __shared__ int32_t wg_tab[PL < 0 ? kFusedMaxTopK : 1];
   auto select = [&]() __attribute__((always_inline)) {
+    if constexpr (PL < 0) {
+      wg_topk<KPT>(a, wkey, wj0, wj1, wg_lds, wg_tab);
+      if (wi < kW)
+        for (int i = threadIdx.x; i < a.top_k; i += 64 * kW) a.sel_out[(size_t)pair * a.top_k + i] = wg_tab[i];
+      selected_entries(wg_tab);
+      mlo = (uint32_t)maskv;
+      mhi = (uint32_t)(maskv >> 32);
+      item_pages();
+    }
     if constexpr (PL > 0) {
       int32_t* tab = reinterpret_cast<int32_t*>(vt + 1024);
       wave_topk<PL>(a, sv, reinterpret_cast<uint32_t*>(vt), tab);
@@ -632,7 +793,7 @@ __global__ __launch_bounds__(64 * kW, D == 128 ? 1 : 2) void decode_bf16_kernel(
   // go before the scoring and selection (so those overlap their latency), the
   // others after; every path runs score() (its barrier) and select() once
   auto prologue = [&](int nl) __attribute__((always_inline)) {
-    if constexpr (PL > 0) {
+    if constexpr (PL != 0) {
       issue_means();
       const int pre = min(nfh, nl);
       if (pre >= 1) load(0, A);
@@ -876,10 +1037,12 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)((waves + kW - 1) / kW)), block(64 * kW);
     if (a.paged.block_table != nullptr) {
       if (a.key_slots == 0) hipLaunchKernelGGL((decode_bf16_kernel<D, 0, true>), grid, block, 0, stream, a);
+      else if (a.key_slots < 0) hipLaunchKernelGGL((decode_bf16_kernel<D, -8, true>), grid, block, 0, stream, a);
       else if (a.mean != nullptr) hipLaunchKernelGGL((decode_bf16_kernel<D, 8, true, true>), grid, block, 0, stream, a);
       else hipLaunchKernelGGL((decode_bf16_kernel<D, 8, true>), grid, block, 0, stream, a);
     } else {
       if (a.key_slots == 0) hipLaunchKernelGGL((decode_bf16_kernel<D, 0, false>), grid, block, 0, stream, a);
+      else if (a.key_slots < 0) hipLaunchKernelGGL((decode_bf16_kernel<D, -8, false>), grid, block, 0, stream, a);
       else if (a.mean != nullptr) hipLaunchKernelGGL((decode_bf16_kernel<D, 8, false, true>), grid, block, 0, stream, a);
       else hipLaunchKernelGGL((decode_bf16_kernel<D, 8, false>), grid, block, 0, stream, a);
     }

@@ -131,6 +131,8 @@ struct ForcedBlocks {
 // 2048 blocks, 32 scores per lane) and the selection table in the wave's V tile.
 constexpr int kFusedMaxBlocks = 64 * 8;
 constexpr int kFusedMaxTopK = 256;
+// Workgroup-selected fused step: 8 scores per thread of a decode workgroup.
+constexpr int kFusedWgMaxBlocks = 8 * 64 * 4;
 
 struct DecodeArgs {
   const void* Q;
@@ -152,7 +154,9 @@ struct DecodeArgs {
   int32_t n_merge;        // partials per query head (workgroups per pair); merged when more than one
   // fused step (bf16): each wave selects its pair's top-k blocks itself from
   // the group scores instead of reading `sel`; the first wave of a pair writes
-  // the selection to sel_out.  key_slots: scores per lane (0: not fused, else 8).
+  // the selection to sel_out.  key_slots: scores per lane (0: not fused, 8:
+  // each wave selects alone; -8: each workgroup selects together, 8 scores
+  // per thread).
   const float* scores;
   int32_t nblk_capacity;
   int32_t* sel_out;

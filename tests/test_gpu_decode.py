@@ -62,13 +62,18 @@ def test_decode_small_cases(api, case):
 
 
 NO_FORCED = _w("no_forced_tokens", 2, 8, 2, 128, 1200, 0, 4, 0, 0, "bf16", 19)
-# bsattn_decode_step selects inside the decode waves for bf16 with <= 512 blocks and
-# top_k <= 256, else it runs the two calls' kernels
+# bsattn_decode_step selects inside the decode kernel for bf16 with top_k <= 256: each
+# wave alone up to 512 blocks, each workgroup together up to 2048 blocks; else it runs
+# the two calls' kernels
 ONE_CALL_EXTRA = [
     (NO_FORCED, (), 0),
     (_w("fused_512_blocks_k256_g8_d64", 1, 8, 1, 64, 512 * 64, 2, 256, 700, 64, "bf16", 25), (5, 64, 65), 0),
     (_w("fused_500_blocks_tail_d128", 2, 4, 1, 128, 500 * 64 + 17, 0, 24, 64, 64, "bf16", 26), (), 0),
-    (_w("fallback_513_blocks", 1, 4, 1, 64, 513 * 64, 0, 8, 64, 64, "bf16", 28), (), 0),
+    (_w("wg_select_513_blocks", 1, 4, 1, 64, 513 * 64, 0, 8, 64, 64, "bf16", 28), (), 0),
+    (_w("wg_select_2048_blocks_g8_d128_r2", 1, 8, 1, 128, 2048 * 64, 2, 40, 300, 10, "bf16", 30),
+     (7, 5000, 90000), 0),
+    (_w("wg_select_1500_blocks_tail_k256_d64", 2, 4, 2, 64, 1500 * 64 + 33, 0, 256, 64, 64, "bf16", 31), (), 0),
+    (_w("fallback_2049_blocks", 1, 4, 1, 64, 2049 * 64, 0, 8, 64, 64, "bf16", 32), (), 0),
     (_w("fallback_k257", 1, 4, 1, 64, 600 * 64, 0, 257, 64, 64, "bf16", 29), (), 0),
 ]
 
@@ -92,6 +97,21 @@ def test_one_call_step_breaks_ties_by_index(api):
     two = gpu_decode_step(api, x, w)
     one = gpu_decode_step(api, x, w, one_call=True)
     assert np.array_equal(one["sel"][0, 0], np.arange(1, 8)), one["sel"][0, 0]
+    assert np.array_equal(two["sel"], one["sel"])
+    assert max_abs(two["O"], one["O"]) < 1e-5
+
+
+def test_workgroup_select_breaks_ties_by_index(api):
+    """1000 blocks (the workgroup-wide selection): every candidate's score ties
+    exactly, so the lowest-index candidates are taken, as by the two calls."""
+    w = _w("all_ties_wg", 1, 4, 1, 64, 64 * 1000, 0, 11, 64, 64, "bf16", 33)
+    x = make_decode_inputs(w)
+    K = x["K"].copy()
+    K[:, :, :] = np.tile(K[:, :, :64], (1, 1, 1000, 1))
+    x = dict(x, K=K)
+    two = gpu_decode_step(api, x, w)
+    one = gpu_decode_step(api, x, w, one_call=True)
+    assert np.array_equal(one["sel"][0, 0], np.arange(1, 12)), one["sel"][0, 0]
     assert np.array_equal(two["sel"], one["sel"])
     assert max_abs(two["O"], one["O"]) < 1e-5
 
