@@ -605,8 +605,8 @@ __global__ __launch_bounds__(64 * kW, D == 128 ? 1 : 2) void decode_bf16_kernel(
 #pragma unroll
     for (int t = 0; t < PL; ++t) sv[t] = sc[min(64 * t + lane, nb_last)];
   }
-  // PL < 0: this thread's keys, blocks [wj0, wj1) of the pair
-  constexpr int KPT = PL < 0 ? -PL : 1;
+  // PL < 0 (and SC): this thread's keys, blocks [wj0, wj1) of the pair
+  constexpr int KPT = PL < 0 ? -PL : (SC ? kFusedMaxBlocks / (64 * kW) : 1);
   uint32_t wkey[KPT];
   int wj0 = 0, wj1 = 0;
   if constexpr (PL < 0) {
@@ -759,17 +759,20 @@ __global__ __launch_bounds__(64 * kW, D == 128 ? 1 : 2) void decode_bf16_kernel(
         }
       }
       __syncthreads();
+      const int per = (NB + 64 * kW - 1) / (64 * kW);
+      wj0 = min((int)threadIdx.x * per, NB);
+      wj1 = min(wj0 + per, NB);
 #pragma unroll
-      for (int t = 0; t < PL; ++t) sv[t] = s_scores[min(64 * t + lane, NB - 1)];
+      for (int t = 0; t < KPT; ++t) wkey[t] = order_key(s_scores[min(wj0 + t, NB - 1)]);
     }
   };
   // fused step: select the pair's blocks (table in this wave's V tile, which
   // the first compute overwrites), write them out from the pair's first wave
   // and fill the selected half of the item table
   __shared__ WgTopkLds wg_lds;  // (PL < 0 only; unused LDS objects are not allocated)
-  __shared__ int32_t wg_tab[PL < 0 ? kFusedMaxTopK : 1];
+  __shared__ int32_t wg_tab[PL < 0 || SC ? kFusedMaxTopK : 1];
   auto select = [&]() __attribute__((always_inline)) {
-    if constexpr (PL < 0) {
+    if constexpr (PL < 0 || SC) {
       wg_topk<KPT>(a, wkey, wj0, wj1, wg_lds, wg_tab);
       if (wi < kW)
         for (int i = threadIdx.x; i < a.top_k; i += 64 * kW) a.sel_out[(size_t)pair * a.top_k + i] = wg_tab[i];
@@ -778,7 +781,7 @@ __global__ __launch_bounds__(64 * kW, D == 128 ? 1 : 2) void decode_bf16_kernel(
       mhi = (uint32_t)(maskv >> 32);
       item_pages();
     }
-    if constexpr (PL > 0) {
+    if constexpr (PL > 0 && !SC) {
       int32_t* tab = reinterpret_cast<int32_t*>(vt + 1024);
       wave_topk<PL>(a, sv, reinterpret_cast<uint32_t*>(vt), tab);
       if (wi == 0)
