@@ -897,7 +897,7 @@ __global__ __launch_bounds__(64 * kW, D == 128 ? 1 : 2) void decode_bf16_kernel(
 template <int D, int GM>
 __global__ __launch_bounds__(64 * kW) void decode_f32_kernel(DecodeArgs a) {
   constexpr int DL = D / 64;  // output dims per lane
-  __shared__ float qs[GM][D];
+  __shared__ __attribute__((aligned(16))) float qs[GM][D];
   __shared__ float ps[kW][GM][64];
   __shared__ __attribute__((aligned(16))) uint8_t mbuf[sizeof(MergeLds<D>)];
   __shared__ int32_t s_sel[kMaxTopK];
@@ -923,24 +923,28 @@ __global__ __launch_bounds__(64 * kW) void decode_f32_kernel(DecodeArgs a) {
   }
   const int it0 = (blockIdx.x * kW + wid) * a.per_wave;
   const int it1 = min(it0 + a.per_wave, a.n_items);
+  const int last = a.forced.n_ctx - 1;  // rows are clamped into the context; masked tokens weigh 0
   for (int it = it0; it < it1; ++it) {
     const ItemInfo inf = item_info(a, s_sel, it);
     if (inf.blk < 0) continue;
-    const size_t tok = (size_t)inf.blk * kBlock + lane;
     const bool on = (inf.mask >> lane) & 1ull;
+    // this lane's K row, loaded once (whole row in flight), then one dot
+    // product per query head from registers
+    const float4* kr = reinterpret_cast<const float4*>(Kb + (size_t)min(inf.blk * kBlock + lane, last) * D);
+    float4 kv[D / 4];
+#pragma unroll
+    for (int c = 0; c < D / 4; ++c) kv[c] = kr[c];
 #pragma unroll
     for (int hh = 0; hh < GM; ++hh) {
       if (hh >= G) break;
       float acc = 0.f;
-      if (on) {
-        const float4* kr = reinterpret_cast<const float4*>(Kb + tok * D);
-        for (int c = 0; c < D / 4; ++c) {
-          const float4 kv = kr[c];
-          acc = fmaf(kv.x, qs[hh][4 * c], acc);
-          acc = fmaf(kv.y, qs[hh][4 * c + 1], acc);
-          acc = fmaf(kv.z, qs[hh][4 * c + 2], acc);
-          acc = fmaf(kv.w, qs[hh][4 * c + 3], acc);
-        }
+#pragma unroll
+      for (int c = 0; c < D / 4; ++c) {
+        const float4 q4 = reinterpret_cast<const float4*>(qs[hh])[c];
+        acc = fmaf(kv[c].x, q4.x, acc);
+        acc = fmaf(kv[c].y, q4.y, acc);
+        acc = fmaf(kv[c].z, q4.z, acc);
+        acc = fmaf(kv[c].w, q4.w, acc);
       }
       const float lg = on ? acc * sl2 : -INFINITY;
       const float mx = wave_max(lg);
@@ -955,15 +959,23 @@ __global__ __launch_bounds__(64 * kW) void decode_f32_kernel(DecodeArgs a) {
       ps[wid][hh][lane] = p;
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    for (int t = 0; t < 64; ++t) {
-      if (!((inf.mask >> t) & 1ull)) continue;
-      const float* vr = Vb + ((size_t)inf.blk * kBlock + t) * D;
+    // O += P V over the block's 64 rows, 16 rows at a time with the batch's
+    // loads in flight together (a masked token's weight is 0)
 #pragma unroll
-      for (int e = 0; e < DL; ++e) {
-        const float v = vr[lane + 64 * e];
+    for (int t0 = 0; t0 < 64; t0 += 16) {
+      float vv[16][DL];
 #pragma unroll
-        for (int hh = 0; hh < GM; ++hh) o[hh][e] = fmaf(ps[wid][hh][t], v, o[hh][e]);
+      for (int u = 0; u < 16; ++u) {
+        const float* vr = Vb + (size_t)min(inf.blk * kBlock + t0 + u, last) * D;
+#pragma unroll
+        for (int e = 0; e < DL; ++e) vv[u][e] = vr[lane + 64 * e];
       }
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+#pragma unroll
+        for (int e = 0; e < DL; ++e)
+#pragma unroll
+          for (int hh = 0; hh < GM; ++hh) o[hh][e] = fmaf(ps[wid][hh][t0 + u], vv[u][e], o[hh][e]);
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
