@@ -20,6 +20,7 @@ host); warmup is W eager steps plus one untimed replay.  Durations come from
 HIP events on the stream the library launches on (torch's current stream).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME] [--no-cpu-baseline]
+                      [--no-context] [--calibrate-copy]
 """
 
 from __future__ import annotations
@@ -45,9 +46,9 @@ CALIB_BYTES = 512 << 20    # the plain device copy --calibrate-copy runs (bytes 
 # calibration copy: FETCH x 1.9999, WRITE x 1.0), summed over the step's
 # launches.  Valid only for the sources they were taken on (their SHA-256);
 # otherwise traffic is null.
-STEP_TRAFFIC = {"sources_sha256": "bdb4d6f67b8d9c8f787824d64d9a7efa73ac0838faf91fa176951fe636936f60",
-                "bytes_per_step": {"first_order_decode_32k": 125222074,
-                                   "cobs_decode_128k": 89536619}}
+STEP_TRAFFIC = {"sources_sha256": "3e5ad937037e71afadc23073d786f092028e6e2aea914e104232c8da31f8464c",
+                "bytes_per_step": {"first_order_decode_32k": 124236208,
+                                   "cobs_decode_128k": 91446464}}
 STEP_SOURCES = ("sliding_window_attention_block_amd/csrc/decode.hip",
                 "sliding_window_attention_block_amd/csrc/select.hip",
                 "sliding_window_attention_block_amd/csrc/bsattn.cpp",
@@ -71,10 +72,10 @@ def step_traffic(name=None):
 # HBM bytes per call of the prefill kernels (rocprofv3 --pmc FETCH_SIZE and
 # WRITE_SIZE, calibrated as above, summed over the call's launches), keyed by
 # workload; valid only for the sources they were taken on, otherwise null.
-PREFILL_TRAFFIC = {"sources_sha256": "2ffebe020af819403925e52db8235d72d5aefa4b8b3a423427c83c647768e45d",
-                   "bytes_per_call": {"swa_prefill_8k": 280330389,
-                                      "local_global_prefill_16k": 441188952,
-                                      "sparse_prefill_8k": 285970125}}
+PREFILL_TRAFFIC = {"sources_sha256": "0158b7976a64f34e58ef2139e9c12a5c5b30666859c4fa0a44f16f284f31c9f3",
+                   "bytes_per_call": {"swa_prefill_8k": 280365450,
+                                      "local_global_prefill_16k": 436759159,
+                                      "sparse_prefill_8k": 285960158}}
 PREFILL_SOURCES = ("sliding_window_attention_block_amd/csrc/prefill.hip",
                    "sliding_window_attention_block_amd/csrc/select.hip",
                    "sliding_window_attention_block_amd/csrc/summaries.hip",
@@ -663,6 +664,9 @@ def main():
                     help="run one workload only (first_order_decode_32k, cobs_decode_128k, "
                          "swa_prefill_8k, local_global_prefill_16k, sparse_prefill_8k); prints its result")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-context", action="store_true",
+                    help="time each workload's own row only (no fp32, paged, exact-selector or append "
+                         "context rows): for profiler runs")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 512 MiB device-to-device copy three times (the "
                          "reference dispatch for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -701,6 +705,8 @@ def main():
         log(f"[bench] {name}: inputs generated in {time.perf_counter() - t:.1f} s")
         if decode and w.dtype == "f32":  # the tiny fp32 workload: latency only
             results[name] = bench_decode(api, torch, w, x, args.steps, args.warmup, mean_dtype="f32")
+        elif decode and args.no_context:
+            results[name] = bench_decode(api, torch, w, x, args.steps, args.warmup)
         elif decode:
             results[name] = bench_decode(api, torch, w, x, args.steps, args.warmup, append_rows=True)
             if name == HEADLINE:  # context: fp32 block means; a paged cache of 4 KB pages
