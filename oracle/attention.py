@@ -23,6 +23,13 @@ What is computed, and from where:
   and is seen by every token.  Reading: "window 512 (+-256)" means
   -256 <= j - i <= 256 (both ends included), and a pair allowed by both the
   band and a global token is one pair (the mask is a boolean union).
+* Dilated SWA, SWA glossary "SWAの拡張手法": the positions inside the window
+  are thinned out (dilation) so the same amount of computation covers a wider
+  range.  Reading: with dilation s the window's keys are every s-th position
+  counted from the query, i.e. j is allowed for row i when the band above
+  allows it and i - j is a multiple of s (s = 1 is the plain band).  A causal
+  window of w keys at spacing s is window_left = (w - 1) s.  Global tokens are
+  not combined with dilation here.
 
 A row with no allowed key has output 0 and log-sum-exp -inf (never happens
 for the masks above: the diagonal is always allowed).
@@ -33,14 +40,16 @@ from __future__ import annotations
 import numpy as np
 
 
-def prefill_allowed(rows, cols, window_left, window_right, causal, global_pos=()):
+def prefill_allowed(rows, cols, window_left, window_right, causal, global_pos=(), dilation=1):
     """Boolean mask allowed[r, c] for query positions ``rows`` and key positions ``cols``.
 
-    allowed(i, j) = (i - window_left <= j <= i + window_right [and j <= i if causal])
+    allowed(i, j) = (i - window_left <= j <= i + window_right [and j <= i if causal]
+                     [and (i - j) % dilation == 0])
                     or i in G or j in G.
     A negative ``window_left`` / ``window_right`` means no limit on that side.
     Global tokens are bidirectional only (local-global glossary, global attention
-    section: they attend to and from all tokens); with ``causal`` they are refused.
+    section: they attend to and from all tokens); with ``causal`` they are refused,
+    and so they are with a dilation above 1.
     """
     rows = np.asarray(rows, dtype=np.int64)
     cols = np.asarray(cols, dtype=np.int64)
@@ -52,10 +61,16 @@ def prefill_allowed(rows, cols, window_left, window_right, causal, global_pos=()
         ok &= diff <= window_right
     if causal:
         ok &= diff <= 0
+    if dilation < 1:
+        raise ValueError("dilation must be >= 1")
+    if dilation > 1:
+        ok &= diff % dilation == 0
     g = np.asarray(global_pos, dtype=np.int64)
     if g.size:
         if causal:
             raise ValueError("global tokens are bidirectional; causal masks take none")
+        if dilation > 1:
+            raise ValueError("global tokens are not combined with a dilated window")
         ok |= np.isin(rows, g)[:, None]
         ok |= np.isin(cols, g)[None, :]
     return ok
@@ -87,12 +102,14 @@ def masked_attention_rows(q, k, v, allowed, scale):
 
 
 def prefill(Q, K, V, window_left, window_right, causal, global_pos=(), scale=None,
-            rows=None, batches=None, heads=None, tile=512):
+            rows=None, batches=None, heads=None, tile=512, dilation=1):
     """Masked attention for every (or a sample of) query row of a prefill.
 
     Q [B, Hq, N, d]; K, V [B, Hkv, N, d] (any float dtype; upcast to float64).
     ``rows`` / ``batches`` / ``heads`` restrict the output to those indices (default all).
     ``scale`` defaults to 1/sqrt(d) (attention glossary, step 2).
+    ``dilation`` thins the window to every s-th key counted from the query (SWA
+    glossary, dilated SWA).
     Returns O [nb, nh, nr, d] and lse [nb, nh, nr] in float64.
     """
     B, Hq, N, d = Q.shape
@@ -116,7 +133,7 @@ def prefill(Q, K, V, window_left, window_right, causal, global_pos=(), scale=Non
             vb = np.asarray(V[b, kv], dtype=np.float64)
             for r0 in range(0, len(rows), tile):
                 r = rows[r0:r0 + tile]
-                allowed = prefill_allowed(r, cols, window_left, window_right, causal, global_pos)
+                allowed = prefill_allowed(r, cols, window_left, window_right, causal, global_pos, dilation)
                 o, lse = masked_attention_rows(Q[b, h, r], kb, vb, allowed, scale)
                 O[bi, hi, r0:r0 + tile] = o
                 L[bi, hi, r0:r0 + tile] = lse

@@ -203,3 +203,60 @@ def test_swa_window_cost_shape(golden_dir):
 def test_causal_with_globals_is_refused():
     with pytest.raises(ValueError):
         prefill_allowed(np.arange(4), np.arange(4), 2, 0, True, (1,))
+
+
+def test_dilated_causal_pair_count_closed_form():
+    """Dilated SWA (SWA glossary, SWAの拡張手法): w keys at spacing s counted from the
+    query.  Row i sees the multiples of s in [i - (w-1)s, i] that are >= 0, i.e.
+    min(w, i // s + 1) keys; over n >= s w rows the total is s w (w+1)/2 + (n - s w) w
+    (each value q = i // s < w repeats s times)."""
+    for n, w, s in ((1000, 7, 3), (4096, 64, 2), (777, 5, 11)):
+        total, per_row = _pair_count(n, window_left=(w - 1) * s, window_right=0, causal=True, dilation=s)
+        np.testing.assert_array_equal(per_row, np.minimum(w, np.arange(n) // s + 1))
+        assert n >= s * w
+        assert total == s * w * (w + 1) // 2 + (n - s * w) * w
+
+
+def test_dilation_one_is_the_plain_band_and_dilated_rows_split_by_residue():
+    """Dilation 1 is the plain mask.  With dilation s, rows and keys of one residue
+    mod s form a plain band over that subsequence with window floor(wl / s) (and
+    floor(wr / s)): i - j = s (i' - j') for i = r + s i', j = r + s j'."""
+    rng = np.random.default_rng(5)
+    n, d = 203, 16
+    q, k, v = (rng.standard_normal((1, 1, n, d)) for _ in range(3))
+    for wl, wr, causal in ((60, 0, True), (37, 22, False)):
+        a = prefill(q, k, v, wl, wr, causal)
+        b = prefill(q, k, v, wl, wr, causal, dilation=1)
+        np.testing.assert_array_equal(a[0], b[0])
+        s = 4
+        O, L = prefill(q, k, v, wl, wr, causal, dilation=s)
+        for r in range(s):
+            sub = slice(r, None, s)
+            Or, Lr = prefill(q[:, :, sub], k[:, :, sub], v[:, :, sub], wl // s, wr // s, causal,
+                             scale=1.0 / np.sqrt(d))
+            np.testing.assert_allclose(O[0, 0, sub], Or[0, 0], rtol=0, atol=1e-12)
+            np.testing.assert_allclose(L[0, 0, sub], Lr[0, 0], rtol=0, atol=1e-12)
+
+
+def test_dilated_mask_matches_brute_force_and_sdpa():
+    """Tiny case: the mask from explicit loops over (i, j), and torch SDPA (float64,
+    CPU) under that mask."""
+    import torch
+    rng = np.random.default_rng(6)
+    n, d, wl, s = 40, 8, 14, 3
+    allowed = prefill_allowed(np.arange(n), np.arange(n), wl, 0, True, dilation=s)
+    brute = np.zeros((n, n), dtype=bool)
+    for i in range(n):
+        for j in range(n):
+            brute[i, j] = j <= i and i - j <= wl and (i - j) % s == 0
+    np.testing.assert_array_equal(allowed, brute)
+    q, k, v = (rng.standard_normal((1, 1, n, d)) for _ in range(3))
+    O, _ = prefill(q, k, v, wl, 0, True, dilation=s)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), attn_mask=torch.from_numpy(brute))
+    np.testing.assert_allclose(O, ref.numpy(), rtol=0, atol=1e-12)
+
+
+def test_dilation_with_globals_is_refused():
+    with pytest.raises(ValueError):
+        prefill_allowed(np.arange(8), np.arange(8), 4, 4, False, global_pos=(3,), dilation=2)
