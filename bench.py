@@ -161,13 +161,14 @@ def attended_tokens(n, S, window, n_sink, global_pos, sel_row):
     return int(inT.sum())
 
 
-def prefill_pairs(N, wl, wr, causal, global_pos):
-    """Allowed (query, key) pairs per (b, h) of the prefill mask, by per-row closed form."""
+def prefill_pairs(N, wl, wr, causal, global_pos, dilation=1):
+    """Allowed (query, key) pairs per (b, h) of the prefill mask, by per-row closed form
+    (with a dilation s: the multiples of s between the window ends and the row)."""
     i = np.arange(N, dtype=np.int64)
     lo = np.zeros(N, np.int64) if wl < 0 else np.maximum(0, i - wl)
     right = 0 if causal else wr
     hi = np.full(N, N - 1, np.int64) if right < 0 else np.minimum(N - 1, i + right)
-    cnt = hi - lo + 1
+    cnt = (i - lo) // dilation + (hi - i) // dilation + 1
     g = np.asarray(sorted(global_pos), dtype=np.int64)
     if g.size:
         inside = np.searchsorted(g, hi, side="right") - np.searchsorted(g, lo, side="left")
@@ -536,8 +537,12 @@ def bench_prefill(api, torch, w, x, steps, warmup):
         rp["ws"] = torch.empty((ws_bytes,), dtype=torch.uint8, device="cuda") if ws_bytes else None
 
     def run(rp):
-        api.bsattn_prefill(shape, rp["Q"], rp["K"], rp["V"], w.window_left, w.window_right,
-                           w.causal, g, rp["O"], rp["lse"], rp["ws"])
+        if w.dilation > 1:
+            api.bsattn_prefill_dilated(shape, rp["Q"], rp["K"], rp["V"], w.window_left, w.window_right,
+                                       w.causal, w.dilation, rp["O"], rp["lse"])
+        else:
+            api.bsattn_prefill(shape, rp["Q"], rp["K"], rp["V"], w.window_left, w.window_right,
+                               w.causal, g, rp["O"], rp["lse"], rp["ws"])
 
     for i in range(warmup):
         run(reps[i % R])
@@ -572,7 +577,7 @@ def bench_prefill(api, torch, w, x, steps, warmup):
     del gr
     k_ms = float(np.median(graph_ms))
     state = gpu_state()
-    pairs = prefill_pairs(N, w.window_left, w.window_right, w.causal, g)
+    pairs = prefill_pairs(N, w.window_left, w.window_right, w.causal, g, w.dilation)
     flops = 4.0 * d * pairs * B * Hq
     del reps
     torch.cuda.empty_cache()
@@ -750,6 +755,11 @@ def main():
             results[name] = bench_sparse_prefill(api, torch, w, x, args.steps, args.warmup)
         else:
             results[name] = bench_prefill(api, torch, w, x, args.steps, args.warmup)
+            if name == "swa_prefill_8k" and not args.no_context:
+                # context: the SWA glossary's dilated window on the same inputs, 4096
+                # keys at spacing 2 (every other key over 8191 positions)
+                wd = w.scaled(name="swa_prefill_8k_dilated2", window_left=2 * 4095, dilation=2)
+                results[name + "/dilated2"] = bench_prefill(api, torch, wd, x, args.steps, args.warmup)
         log(f"[bench] {name}: {json.dumps(results[name])}")
         if name == HEADLINE:
             inputs[name] = x

@@ -111,6 +111,7 @@ typedef struct {
 #define BSATTN_MAX_TOP_K 1024
 #define BSATTN_MAX_BLOCKS 65536  /* complete blocks per (b, kv head) for selection   */
 #define BSATTN_MAX_GROUP 16      /* query heads per K/V head (Hq / Hkv)              */
+#define BSATTN_MAX_DILATION 65536 /* key spacing of a dilated prefill window         */
 
 /*
  * Per-block key summaries [COBS 2.2, 2.3].
@@ -317,6 +318,27 @@ bsattn_status bsattn_prefill(const bsattn_shape* shape, const void* Q, const voi
                              int32_t causal, const int32_t* global_pos_host, int32_t n_global,
                              float* O, float* lse, void* workspace, size_t ws_bytes,
                              void* hip_stream);
+
+/*
+ * Dilated sliding-window prefill [SWA 拡張手法: dilated SWA thins the window's
+ * positions so the same computation covers a wider range], BF16 Q/K/V, fp32 O
+ * and lse.  Query i sees key j iff
+ *   (i - window_left <= j <= i + window_right) [and j <= i when causal]
+ *   and (i - j) is a multiple of `dilation`.
+ * A causal window of w keys at spacing s is window_left = (w - 1) s,
+ * window_right = 0, causal = 1.  dilation in [1, BSATTN_MAX_DILATION]
+ * (1: the plain band of bsattn_prefill); a negative window side is unlimited.
+ * No global tokens.  Computed as one launch per residue class r of the
+ * positions mod s: the rows and keys r, r + s, r + 2s, ... form a plain band
+ * with the windows divided by s (rounded down), run by the band kernel over a
+ * strided view, so the work is the allowed pairs' and no stride test runs per
+ * element.  lse may be NULL.  Q/O row stride is N = n_ctx; K/V row stride is
+ * kv_capacity.  Layouts and ownership as bsattn_prefill; no workspace.
+ */
+bsattn_status bsattn_prefill_dilated(const bsattn_shape* shape, const void* Q, const void* K,
+                                     const void* V, int32_t window_left, int32_t window_right,
+                                     int32_t causal, int32_t dilation, float* O, float* lse,
+                                     void* hip_stream);
 
 /*
  * Block-sparse causal prefill, NSA-style block selection shared by a query

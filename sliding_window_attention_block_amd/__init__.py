@@ -22,6 +22,7 @@ __all__ = [
     "bsattn_decode_step",
     "bsattn_decode_step_noalloc",
     "bsattn_prefill",
+    "bsattn_prefill_dilated",
     "bsattn_prefill_workspace_bytes",
     "bsattn_status_string", "bsattn_version", "BSATTN_F32", "BSATTN_BF16", "BSATTN_FP4_E2M1",
     "BSATTN_NOALLOC_SCRATCH_BYTES",
@@ -226,6 +227,13 @@ def bsattn_prefill(shape, Q, K, V, window_left, window_right, causal, global_pos
     _check(library().bsattn_prefill(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), window_left,
                                     window_right, int(bool(causal)), g, ng, _ptr(O), _ptr(lse),
                                     _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def bsattn_prefill_dilated(shape, Q, K, V, window_left, window_right, causal, dilation, O, lse=None,
+                           stream=None):
+    _check(library().bsattn_prefill_dilated(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), window_left,
+                                            window_right, int(bool(causal)), int(dilation), _ptr(O), _ptr(lse),
+                                            _stream(stream)))
 
 
 def default_scale(head_dim):

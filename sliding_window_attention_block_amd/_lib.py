@@ -37,6 +37,7 @@ EXPORTS = (
     "bsattn_decode_step_noalloc",
     "bsattn_prefill",
     "bsattn_prefill_workspace_bytes",
+    "bsattn_prefill_dilated",
     "bsattn_status_string",
     "bsattn_last_error",
     "bsattn_version",
@@ -115,6 +116,8 @@ def load():
     lib.bsattn_prefill.argtypes = [_pshape, _vp, _vp, _vp, _i32, _i32, _i32, _pi32, _i32,
                                    _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.bsattn_prefill.restype = _st
+    lib.bsattn_prefill_dilated.argtypes = [_pshape, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]
+    lib.bsattn_prefill_dilated.restype = _st
     lib.bsattn_prefill_workspace_bytes.argtypes = [_pshape, _i32]
     lib.bsattn_prefill_workspace_bytes.restype = ctypes.c_size_t
     lib.bsattn_status_string.argtypes = [_st]

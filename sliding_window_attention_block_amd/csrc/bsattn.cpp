@@ -748,4 +748,49 @@ bsattn_status bsattn_prefill(const bsattn_shape* shape, const void* Q, const voi
   return BSATTN_OK;
 }
 
+bsattn_status bsattn_prefill_dilated(const bsattn_shape* shape, const void* Q, const void* K, const void* V,
+                                     int32_t window_left, int32_t window_right, int32_t causal,
+                                     int32_t dilation, float* O, float* lse, void* hip_stream) {
+  g_err[0] = 0;
+  bsattn_status st = check_shape(shape, false);
+  if (st != BSATTN_OK) return st;
+  if (shape->dtype != BSATTN_BF16) return fail(BSATTN_ERR_UNSUPPORTED, "prefill takes bf16 Q/K/V only");
+  if (Q == nullptr || K == nullptr || V == nullptr || O == nullptr)
+    return fail(BSATTN_ERR_INVALID, "Q, K, V and O must be non-NULL");
+  if (causal != 0 && causal != 1) return fail(BSATTN_ERR_INVALID, "causal must be 0 or 1");
+  if (dilation < 1 || dilation > BSATTN_MAX_DILATION)
+    return fail(BSATTN_ERR_INVALID, "dilation must be in [1, %d]", BSATTN_MAX_DILATION);
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O))
+    return fail(BSATTN_ERR_INVALID, "device pointers must be 16-byte aligned");
+  const int N = shape->n_ctx;
+  // residue class r: logical rows x < ceil((N - r) / s), physical rows r + s x;
+  // the dilated band is the plain band of the logical rows with the windows
+  // divided by s (rounded down: i - j = s (x_i - x_j))
+  const int s = dilation;
+  for (int r = 0; r < s && r < N; ++r) {
+    const int nr = (N - r + s - 1) / s;
+    const long long n_wg = (long long)((nr + 127) / 128) * shape->batch * shape->n_q_heads;
+    if (n_wg > 0x7fffffffLL) return fail(BSATTN_ERR_UNSUPPORTED, "grid too large");
+  }
+  bsattn::PrefillArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.Q = Q; a.K = K; a.V = V; a.O = O; a.lse = lse;
+  a.batch = shape->batch; a.n_q_heads = shape->n_q_heads; a.n_kv_heads = shape->n_kv_heads;
+  a.head_dim = shape->head_dim;
+  a.kv_capacity = shape->kv_capacity;
+  a.window_left = window_left < 0 ? -1 : window_left / s;
+  a.window_right = window_right < 0 ? -1 : window_right / s;
+  a.causal = causal;
+  a.scale = effective_scale(shape);
+  a.dil = s;
+  a.seq_phys = N;
+  for (int r = 0; r < s && r < N; ++r) {
+    a.dil_off = r;
+    a.seq_len = (N - r + s - 1) / s;
+    hipError_t e = bsattn::launch_prefill(a, (hipStream_t)hip_stream);
+    if (e != hipSuccess) return fail(BSATTN_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+  }
+  return BSATTN_OK;
+}
+
 }  // extern "C"

@@ -213,6 +213,10 @@ struct PrefillArgs {
   int32_t g_keys_per_split;
   float* g_part_o;            // [B*Hq, ceil(n_global/32), g_splits, 32, d]
   float* g_part_ml;           // [B*Hq, ceil(n_global/32), g_splits, 32, 2] (max, normaliser), log2
+  // dilated window (dil > 1): the launch covers the rows and keys of one residue
+  // class, physical row dil_off + dil * x for logical row x < seq_len; the
+  // windows are in logical rows; Q, O and lse hold seq_phys rows per (b, h)
+  int32_t dil, dil_off, seq_phys;
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 // Split geometry of the global query rows (also sizes the prefill workspace).

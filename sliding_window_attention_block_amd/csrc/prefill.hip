@@ -72,7 +72,7 @@ struct RowState {
 // kt (vt) may be null: that tile is not copied.
 template <int D, typename RowPos>
 __device__ __forceinline__ void dma_stage(const uint16_t* Kb, const uint16_t* Vb, uint8_t* kt, uint8_t* vt,
-                                          int wid, int nw, RowPos row_pos) {
+                                          int wid, int nw, RowPos row_pos, size_t pitch = D) {
   using T = Tile<D>;
   typedef __attribute__((address_space(3))) void lds_void;
   constexpr int NCH = T::BYTES / 1024;
@@ -82,10 +82,10 @@ __device__ __forceinline__ void dma_stage(const uint16_t* Kb, const uint16_t* Vb
     const int r = off / T::RB, pc = (off % T::RB) >> 4;
     const size_t pos = (size_t)row_pos(r);
     if (kt != nullptr)
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(Kb + pos * D + (pc ^ T::k_swz(r)) * 8),
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(Kb + pos * pitch + (pc ^ T::k_swz(r)) * 8),
                                        (lds_void*)(kt + 1024 * k), 16, 0, 0);
     if (vt != nullptr)
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(Vb + pos * D + (pc ^ T::v_swz(r)) * 8),
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(Vb + pos * pitch + (pc ^ T::v_swz(r)) * 8),
                                        (lds_void*)(vt + 1024 * k), 16, 0, 0);
   }
 }
@@ -97,24 +97,26 @@ template <int D>
 struct DmaLane {
   static constexpr int NW = Tile<D>::BYTES / 1024 / 4;  // chunks per wave per tile
   uint32_t k[NW], v[NW];
-  __device__ __forceinline__ void init(int wid) {
+  // pitch: bytes between consecutive rows of the copied view (the row size, or
+  // a multiple of it for a dilated window's residue class)
+  __device__ __forceinline__ void init(int wid, uint32_t pitch = Tile<D>::RB) {
     using T = Tile<D>;
     const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
       const int off = 1024 * (wid + 4 * i) + 16 * lane;
       const int r = off / T::RB, pc = (off % T::RB) >> 4;
-      k[i] = (uint32_t)(r * T::RB + ((pc ^ T::k_swz(r)) << 4));
-      v[i] = (uint32_t)(r * T::RB + ((pc ^ T::v_swz(r)) << 4));
+      k[i] = (uint32_t)(r * pitch + ((pc ^ T::k_swz(r)) << 4));
+      v[i] = (uint32_t)(r * pitch + ((pc ^ T::v_swz(r)) << 4));
     }
   }
   // copy rows [row0, row0 + 64) of K and V (all < the sequence length); a null
   // destination tile is not copied
   __device__ __forceinline__ void issue(const uint8_t* Kb, const uint8_t* Vb, int row0, uint8_t* kt, uint8_t* vt,
-                                        int wid) const {
+                                        int wid, size_t pitch = Tile<D>::RB) const {
     typedef __attribute__((address_space(3))) void lds_void;
-    const uint8_t* ks = Kb + (size_t)row0 * Tile<D>::RB;
-    const uint8_t* vs = Vb + (size_t)row0 * Tile<D>::RB;
+    const uint8_t* ks = Kb + (size_t)row0 * pitch;
+    const uint8_t* vs = Vb + (size_t)row0 * pitch;
     if (kt != nullptr) {
 #pragma unroll
       for (int i = 0; i < NW; ++i)
@@ -392,7 +394,13 @@ __device__ __forceinline__ float region_b(const uint8_t* vt, const u32x4 (&pop)[
 // selected and per sink block; a key of such a stage is allowed for row i only
 // before i's window (keys in the window come from the band), and only below
 // n_sink for a sink block the tile did not select, so no key counts twice.
-template <int D, bool LG, bool SP = false>
+//
+// DIL: dilated causal or bidirectional window [SWA 拡張手法, dilated SWA]: the
+// launch takes one residue class r of the rows and keys (physical position
+// r + s x for logical position x), where the dilated mask is the plain band
+// of the logical positions, so every stage is the band kernel's own (no
+// per-element stride test); only the row addressing uses the pitch s d.
+template <int D, bool LG, bool SP = false, bool DIL = false>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   using T = Tile<D>;
   constexpr int LDS_BYTES = 4 * T::BYTES;  // K and V, double buffered
@@ -550,13 +558,20 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   const int nx = SP ? __builtin_amdgcn_readfirstlane(s_nx) : 0;  // extra stages, ahead of the band
   const int n_stage = nx + n_band + (ngc + BN - 1) / BN;
 
-  const uint16_t* Kb = reinterpret_cast<const uint16_t*>(a.K) + (size_t)(b * Hkv + g) * a.kv_capacity * D;
-  const uint16_t* Vb = reinterpret_cast<const uint16_t*>(a.V) + (size_t)(b * Hkv + g) * a.kv_capacity * D;
+  // DIL: logical row x is physical row dil_off + dil * x (Q, K, V, O, lse); the
+  // pitches below are then dil rows, else one row
+  const int dil = DIL ? a.dil : 1;
+  const size_t NP = DIL ? (size_t)a.seq_phys : (size_t)N;              // rows of Q, O, lse per (b, h)
+  const size_t roff = DIL ? (size_t)a.dil_off : 0;
+  const size_t kpitch = DIL ? (size_t)dil * D : (size_t)D;           // elements between logical rows
+  const uint16_t* Kb = reinterpret_cast<const uint16_t*>(a.K) + ((size_t)(b * Hkv + g) * a.kv_capacity + roff) * D;
+  const uint16_t* Vb = reinterpret_cast<const uint16_t*>(a.V) + ((size_t)(b * Hkv + g) * a.kv_capacity + roff) * D;
   const int r0 = i0 + 32 * wid;
   const int myrow = r0 + r32;
   u32x4 qop[D / 16];
   {
-    const uint16_t* Qp = reinterpret_cast<const uint16_t*>(a.Q) + ((size_t)(b * Hq + h) * N + min(myrow, N - 1)) * D;
+    const uint16_t* Qp = reinterpret_cast<const uint16_t*>(a.Q) +
+                         ((size_t)(b * Hq + h) * NP + roff + (size_t)dil * min(myrow, N - 1)) * D;
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) qop[c] = *reinterpret_cast<const u32x4*>(Qp + 16 * c + 8 * h2);
   }
@@ -585,7 +600,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     return gcols[min(slot, ngc - 1)];
   };
   DmaLane<D> dl;
-  dl.init(wid);
+  dl.init(wid, (uint32_t)(kpitch * 2));
   const uint8_t* Kb8 = reinterpret_cast<const uint8_t*>(Kb);
   const uint8_t* Vb8 = reinterpret_cast<const uint8_t*>(Vb);
   // copies of stage `stg` into (kt, vt): whole in-range band tiles take the
@@ -600,8 +615,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
     }
     const int bs = stg - nx;
     const int row0 = (t_lo + bs) * BN;
-    if (bs < n_band && row0 + BN <= N) dl.issue(Kb8, Vb8, row0, kt, vt, wid);
-    else dma_stage<D>(Kb, Vb, kt, vt, wid, 4, [&](int r) { return row_pos(stg, r); });
+    if (bs < n_band && row0 + BN <= N) dl.issue(Kb8, Vb8, row0, kt, vt, wid, kpitch * 2);
+    else dma_stage<D>(Kb, Vb, kt, vt, wid, 4, [&](int r) { return row_pos(stg, r); }, kpitch);
   };
   // Stage s goes to K tile kb[s % 2] and V tile vb[s % 2]; K of stage s + 2 and
   // V of stage s + 1 are copied while stage s is computed (K runs one stage
@@ -789,7 +804,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   }
   if (store) {
     const float inv = st.l > 0.f ? 1.f / st.l : 0.f;
-    float* orow = a.O + ((size_t)(b * Hq + h) * N + myrow) * D;
+    float* orow = a.O + ((size_t)(b * Hq + h) * NP + roff + (size_t)dil * myrow) * D;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -800,7 +815,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         *reinterpret_cast<f32x4*>(orow + 32 * dt + 8 * j + 4 * h2) = v;
       }
     if (a.lse != nullptr && h2 == 0)
-      a.lse[(size_t)(b * Hq + h) * N + myrow] = st.l > 0.f ? (st.m + log2f(st.l)) * kLn2 : -INFINITY;
+      a.lse[(size_t)(b * Hq + h) * NP + roff + (size_t)dil * myrow] =
+          st.l > 0.f ? (st.m + log2f(st.l)) * kLn2 : -INFINITY;
   }
 }
 
@@ -858,6 +874,10 @@ template <int D, bool LG>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t stream) {
   const int n_qt = (a.seq_len + BM - 1) / BM;
   const int n_wg = (LG ? a.n_global_wg : 0) + n_qt * a.batch * a.n_q_heads;
+  if (!LG && a.dil > 1) {
+    hipLaunchKernelGGL((prefill_kernel<D, false, false, true>), dim3(n_wg), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
   if (!LG && a.sp_sel != nullptr) {
     hipLaunchKernelGGL((prefill_kernel<D, false, true>), dim3(n_wg), dim3(256), 0, stream, a);
     return hipGetLastError();

@@ -79,6 +79,7 @@ class PrefillWorkload:
     global_pos: tuple = field(default_factory=tuple)
     top_k: int = 0   # block-sparse prefill: blocks selected per 128-row query tile (0: none)
     n_sink: int = 0
+    dilation: int = 1  # dilated window: every dilation-th key counted from the query
 
     def scaled(self, **kw):
         return dataclasses.replace(self, **kw)

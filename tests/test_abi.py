@@ -24,7 +24,7 @@ def _header_functions():
 def test_library_exports_every_declared_function():
     lib = api.library()
     declared = _header_functions()
-    assert len(declared) == 15
+    assert len(declared) == 16
     for name in declared:
         assert hasattr(lib, name), name
     assert set(declared) == set(_lib.EXPORTS)
@@ -232,6 +232,21 @@ def test_prefill_rejects_bad_arguments():
     st, _ = _status("bsattn_prefill", _shape(), *P, 8, 8, 0, G3(1, 2, 3), 3, FAKE, None, FAKE + 16, need,
                     None)
     assert st == 1  # misaligned workspace
+
+
+def test_dilated_prefill_rejects_bad_arguments():
+    P = (FAKE, FAKE, FAKE)
+    st, _ = _status("bsattn_prefill_dilated", _shape(dtype=0), *P, 10, 0, 1, 2, FAKE, None, None)
+    assert st == 2  # bf16 only
+    for dil in (0, -3, 65537):
+        st, msg = _status("bsattn_prefill_dilated", _shape(), *P, 10, 0, 1, dil, FAKE, None, None)
+        assert st == 1 and "dilation" in msg
+    st, _ = _status("bsattn_prefill_dilated", _shape(), *P, 10, 0, 2, 2, FAKE, None, None)
+    assert st == 1  # causal must be 0 or 1
+    st, _ = _status("bsattn_prefill_dilated", _shape(), FAKE, FAKE, FAKE, 10, 0, 1, 2, None, None, None)
+    assert st == 1  # O must be non-NULL
+    st, _ = _status("bsattn_prefill_dilated", _shape(), FAKE + 8, FAKE, FAKE, 10, 0, 1, 2, FAKE, None, None)
+    assert st == 1  # misaligned
 
 
 def test_prefill_workspace_size():

@@ -27,3 +27,17 @@ def test_a_multi_rank_launch_is_refused():
     r = _run(["--gpus", "1"], {"WORLD_SIZE": "4"})
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_prefill_pair_counts_match_the_oracle_mask():
+    """bench.py's per-row closed form of the allowed pairs (the FLOP count of the
+    prefill rows) against the oracle's mask, with and without a dilation."""
+    import numpy as np
+
+    import bench
+    from oracle import prefill_allowed
+    for N, wl, wr, causal, s, g in ((300, 20, 0, True, 3, ()), (257, 31, 17, False, 4, ()),
+                                    (100, -1, 0, True, 7, ()), (90, 10, -1, False, 2, ()),
+                                    (400, 37, 0, True, 1, ()), (500, 16, 16, False, 1, (0, 77, 499))):
+        m = prefill_allowed(np.arange(N), np.arange(N), wl, wr, causal, g, dilation=s)
+        assert bench.prefill_pairs(N, wl, wr, causal, g, s) == int(m.sum()), (N, wl, wr, causal, s, g)
