@@ -626,9 +626,30 @@ __global__ __launch_bounds__(64 * kW, D == 128 ? 1 : 2) void decode_bf16_kernel(
 
   // This wave's half items (32 tokens each): forced halves [f0, f1) of the
   // pair's forced items, then selected halves [s0, s1) of its selected items.
+  // Each workgroup of a pair takes an even share of the forced and of the
+  // selected half items; inside it the forced ones go in runs to its first
+  // kW - 1 waves (the last wave issues no forced load ahead of the selection)
+  // and the selected ones are split over all its waves.  With the workgroup
+  // selection (PL < 0) the pair's waves take runs of fh / sh half items
+  // instead (measured faster there: the selection, not the loads, sets that
+  // step's pace).
   const int nf2 = 2 * (a.n_items - a.top_k), ns2 = 2 * a.top_k;
-  const int f0 = min(wi * a.fh_per_wave, nf2), f1 = min(f0 + a.fh_per_wave, nf2);
-  const int s0 = min(wi * a.sh_per_wave, ns2), s1 = min(s0 + a.sh_per_wave, ns2);
+  int f0, f1, s0, s1;
+  if constexpr (PL < 0) {
+    f0 = min(wi * a.fh_per_wave, nf2);
+    f1 = min(f0 + a.fh_per_wave, nf2);
+    s0 = min(wi * a.sh_per_wave, ns2);
+    s1 = min(s0 + a.sh_per_wave, ns2);
+  } else {
+    const int M = a.n_merge, wgp = wi / kW, wv = wi % kW;
+    const int F0 = nf2 * wgp / M, nF = nf2 * (wgp + 1) / M - F0;
+    const int S0 = ns2 * wgp / M, nS = ns2 * (wgp + 1) / M - S0;
+    constexpr int kFw = kW - 1;
+    f0 = F0 + (wv < kFw ? nF * wv / kFw : nF);
+    f1 = F0 + (wv < kFw ? nF * (wv + 1) / kFw : nF);
+    s0 = S0 + nS * wv / kW;
+    s1 = S0 + nS * (wv + 1) / kW;
+  }
   const int nfh = f1 - f0, n = nfh + (s1 - s0);
   const int fi0 = f0 >> 1, si0 = s0 >> 1;
   const int nfi = nfh > 0 ? ((f1 - 1) >> 1) - fi0 + 1 : 0;
