@@ -46,9 +46,9 @@ CALIB_BYTES = 512 << 20    # the plain device copy --calibrate-copy runs (bytes 
 # calibration copy: FETCH x 1.9999, WRITE x 1.0), summed over the step's
 # launches.  Valid only for the sources they were taken on (their SHA-256);
 # otherwise traffic is null.
-STEP_TRAFFIC = {"sources_sha256": "3e5ad937037e71afadc23073d786f092028e6e2aea914e104232c8da31f8464c",
-                "bytes_per_step": {"first_order_decode_32k": 124236208,
-                                   "cobs_decode_128k": 91446464}}
+STEP_TRAFFIC = {"sources_sha256": "53866fdb25f77516b981d289b911673408243404e27de0c18945f71e89bb6267",
+                "bytes_per_step": {"first_order_decode_32k": 124026735,
+                                   "cobs_decode_128k": 91443672}}
 STEP_SOURCES = ("sliding_window_attention_block_amd/csrc/decode.hip",
                 "sliding_window_attention_block_amd/csrc/select.hip",
                 "sliding_window_attention_block_amd/csrc/bsattn.cpp",
@@ -72,10 +72,10 @@ def step_traffic(name=None):
 # HBM bytes per call of the prefill kernels (rocprofv3 --pmc FETCH_SIZE and
 # WRITE_SIZE, calibrated as above, summed over the call's launches), keyed by
 # workload; valid only for the sources they were taken on, otherwise null.
-PREFILL_TRAFFIC = {"sources_sha256": "0158b7976a64f34e58ef2139e9c12a5c5b30666859c4fa0a44f16f284f31c9f3",
-                   "bytes_per_call": {"swa_prefill_8k": 280365450,
-                                      "local_global_prefill_16k": 436759159,
-                                      "sparse_prefill_8k": 285960158}}
+PREFILL_TRAFFIC = {"sources_sha256": "d116dcf687d3fcc093e59cc1c8eab3c980d450a203da27278737bc555e5e7d1f",
+                   "bytes_per_call": {"swa_prefill_8k": 280283319,
+                                      "local_global_prefill_16k": 436002267,
+                                      "sparse_prefill_8k": 285974525}}
 PREFILL_SOURCES = ("sliding_window_attention_block_amd/csrc/prefill.hip",
                    "sliding_window_attention_block_amd/csrc/select.hip",
                    "sliding_window_attention_block_amd/csrc/summaries.hip",
