@@ -232,7 +232,7 @@ def bench_append(api, torch, w, rp, shape_step, mean_dtype, fp4, basis, steps):
 
 
 def bench_decode(api, torch, w, x, steps, warmup, mean_dtype="bf16", factor_fp4=True, subspace=True,
-                 page_tokens=None, append_rows=False):
+                 page_tokens=None, append_rows=False, replicas=None):
     B, Hq, Hkv, d, n, S = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_ctx, w.block_size
     nb = n // S
     shape = api.make_shape(B, Hq, Hkv, d, n, dtype=w.dtype)
@@ -247,7 +247,9 @@ def bench_decode(api, torch, w, x, steps, warmup, mean_dtype="bf16", factor_fp4=
     basis_bytes = Hkv * sub * d * 4
     summ_bytes = B * Hkv * nb * (d * mean_elem + w.rank * factor_row_bytes)
     kv_est = B * Hkv * (w.top_k * S + w.n_sink + w.window) * d * 2 * elem
-    R = replicas_for(summ_bytes + kv_est)
+    # replicas: enough that the working set exceeds the 256 MB Infinity Cache
+    # (every step reads HBM), or the caller's count (1: the warm context row)
+    R = replicas or replicas_for(summ_bytes + kv_est)
     log(f"[bench] {w.name}: {R} replicas, {2 * x['K'].nbytes * R / 2**30:.1f} GiB of K/V")
     K0, V0, Q0 = to_dev(torch, x["K"]), to_dev(torch, x["V"]), to_dev(torch, x["Q"])
     basis = None
@@ -739,6 +741,9 @@ def main():
                                                              mean_dtype="f32")
                 results[name + "/paged16"] = bench_decode(api, torch, w, x, args.steps, args.warmup,
                                                           page_tokens=16)
+                # warm: one input replica, so the Infinity Cache keeps most of a step's bytes
+                results[name + "/warm_one_replica"] = bench_decode(api, torch, w, x, args.steps, args.warmup,
+                                                                   replicas=1)
                 results[name + "/exact_select"] = bench_exact_select(api, torch, w, x, min(args.steps, 10),
                                                                      min(args.warmup, 2))
             elif w.rank > 0:  # context: FP4 rows without the subspace projection; fp32 rows
