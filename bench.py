@@ -231,8 +231,42 @@ def bench_append(api, torch, w, rp, shape_step, mean_dtype, fp4, basis, steps):
     return out
 
 
+def bench_gather_probe(api, torch, w, reps, shape, steps, R):
+    """The loads-only gather ceiling for this step's own token set (bsattn_probe_gather):
+    the same K/V blocks (sink, window and selected blocks of every pair) read from the
+    same rotating replicas with the decode's placement of two workgroups per pair,
+    nothing computed, as one captured graph of `steps` calls per setting."""
+    B, Hkv, n, S = w.batch, w.n_kv_heads, w.n_ctx, w.block_size
+    forced = sorted(set(range(0, (min(w.n_sink, n) + S - 1) // S)) | set(range(max(0, n - w.window) // S, n // S)))
+    sel_h = reps[0]["sel"].cpu().numpy().reshape(B * Hkv, -1)
+    rows = [forced + sorted(int(j) for j in r if j >= 0 and j not in forced) for r in sel_h]
+    nbl = min(len(r) for r in rows)
+    blocks = torch.from_numpy(np.asarray([r[:nbl] for r in rows], dtype=np.int32)).cuda()
+    nbytes = B * Hkv * nbl * S * w.head_dim * 2 * 2
+    out = {"blocks_per_pair": nbl, "bytes": nbytes}
+    for wg, depth in ((2, 2), (2, 4), (1, 4)):
+        cks = torch.empty((B * Hkv * wg * 256,), dtype=torch.int32, device="cuda")
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                rp = reps[i % R]
+                api.bsattn_probe_gather(shape, rp["K"], rp["V"], blocks, wg, depth, cks)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        out[f"wg{wg}_depth{depth}"] = dict(ms=ms, GBps=nbytes / (ms * 1e-3) / 1e9,
+                                           frac_hbm=nbytes / (ms * 1e-3) / HBM_PEAK)
+        del g
+    return out
+
+
 def bench_decode(api, torch, w, x, steps, warmup, mean_dtype="bf16", factor_fp4=True, subspace=True,
-                 page_tokens=None, append_rows=False, replicas=None):
+                 page_tokens=None, append_rows=False, replicas=None, gather_probe=False):
     B, Hq, Hkv, d, n, S = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_ctx, w.block_size
     nb = n // S
     shape = api.make_shape(B, Hq, Hkv, d, n, dtype=w.dtype)
@@ -366,6 +400,9 @@ def bench_decode(api, torch, w, x, steps, warmup, mean_dtype="bf16", factor_fp4=
         step(reps[i % R])
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t0) * 1e3 / steps
+    probe = None
+    if gather_probe:
+        probe = bench_gather_probe(api, torch, w, reps, shape, steps, R)
     append = None
     if append_rows:
         append = bench_append(api, torch, w, reps[0], shape, mean_dtype, fp4, basis, steps)
@@ -380,6 +417,7 @@ def bench_decode(api, torch, w, x, steps, warmup, mean_dtype="bf16", factor_fp4=
         summary_build_ms=float(np.median(build_ms)),
         summary_build_bytes=B * Hkv * nb * S * d * elem + summ_bytes,
         append=append,
+        gather_probe=probe,
     )
     res["gathered_kv_GBps"] = kv_bytes / (dec_ms * 1e-3) / 1e9
     res["gathered_kv_frac_hbm"] = res["gathered_kv_GBps"] * 1e9 / HBM_PEAK
@@ -733,9 +771,10 @@ def main():
         if decode and w.dtype == "f32":  # the tiny fp32 workload: latency only
             results[name] = bench_decode(api, torch, w, x, args.steps, args.warmup, mean_dtype="f32")
         elif decode and args.no_context:
-            results[name] = bench_decode(api, torch, w, x, args.steps, args.warmup)
+            results[name] = bench_decode(api, torch, w, x, args.steps, args.warmup, gather_probe=name == HEADLINE)
         elif decode:
-            results[name] = bench_decode(api, torch, w, x, args.steps, args.warmup, append_rows=True)
+            results[name] = bench_decode(api, torch, w, x, args.steps, args.warmup, append_rows=True,
+                                         gather_probe=name == HEADLINE)
             if name == HEADLINE:  # context: fp32 block means; a paged cache of 4 KB pages
                 results[name + "/fp32_means"] = bench_decode(api, torch, w, x, args.steps, args.warmup,
                                                              mean_dtype="f32")
@@ -800,6 +839,9 @@ def main():
                    "rank": w.rank, "parallelism": "single GPU"},
         "gathered_kv_GBps": h.get("gathered_kv_GBps"),
         "gathered_kv_frac_hbm": h.get("gathered_kv_frac_hbm"),
+        # the loads-only gather of the same blocks (bsattn_probe_gather), best setting
+        "gather_ceiling_GBps": max((v["GBps"] for k, v in (h.get("gather_probe") or {}).items()
+                                    if k.startswith("wg")), default=None),
         "roofline": {
             "kernel": "bsattn_decode_step: decode_bf16_kernel with in-kernel scoring and the in-wave "
                       "top-k, decode_merge_kernel (one call, two launches)",

@@ -379,6 +379,28 @@ bsattn_status bsattn_sparse_prefill(const bsattn_shape* shape, const void* Q, co
                                     int32_t window_left, int32_t n_sink, float* O, float* lse,
                                     void* hip_stream);
 
+/*
+ * Gather probe, a measurement aid rather than a step of the method: the HBM
+ * bandwidth a loads-only gather of K/V blocks reaches, the ceiling against
+ * which the sparse decode's gathered bytes are judged (decode is bound by the
+ * KV bytes it reads [COBS 1]).  For every (b, K/V head) pair p = b * Hkv + g it
+ * reads the K and V rows of the blocks blocks[p, 0 .. n_blocks - 1] (device
+ * int32 [B * Hkv, n_blocks]; each entry is clamped into [0, kv_capacity / 64),
+ * so every access stays inside the cache; list a block twice and it is read
+ * twice) and does no arithmetic with them: each thread folds the 32-bit words
+ * it loaded into one XOR, written to checksum (device uint32
+ * [B * Hkv * wg_per_pair * 256]); the XOR of all entries is the XOR of every
+ * word of the listed blocks.  The pair's 32-token half blocks are dealt in even
+ * runs to the 4 * wg_per_pair waves of its wg_per_pair workgroups (1 .. 16;
+ * the decode uses 2 at the 32K, 8 K/V-head, batch-16 shape), each keeping depth
+ * (1 .. 4) half blocks of K and V in flight.  shape: dtype BF16, d 64 or 128,
+ * the decode's limits; the cache is contiguous [B, Hkv, kv_capacity, d].
+ * Caller-owned device memory, asynchronous on hip_stream.
+ */
+bsattn_status bsattn_probe_gather(const bsattn_shape* shape, const void* K, const void* V,
+                                  const int32_t* blocks, int32_t n_blocks, int32_t wg_per_pair,
+                                  int32_t depth, uint32_t* checksum, void* hip_stream);
+
 /* Bytes of device workspace bsattn_prefill needs with n_global global positions
  * (0 when n_global == 0 or the arguments are invalid). */
 size_t bsattn_prefill_workspace_bytes(const bsattn_shape* shape, int32_t n_global);

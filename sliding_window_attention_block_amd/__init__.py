@@ -24,6 +24,7 @@ __all__ = [
     "bsattn_prefill",
     "bsattn_prefill_dilated",
     "bsattn_prefill_workspace_bytes",
+    "bsattn_probe_gather",
     "bsattn_status_string", "bsattn_version", "BSATTN_F32", "BSATTN_BF16", "BSATTN_FP4_E2M1",
     "BSATTN_NOALLOC_SCRATCH_BYTES",
 ]
@@ -234,6 +235,13 @@ def bsattn_prefill_dilated(shape, Q, K, V, window_left, window_right, causal, di
     _check(library().bsattn_prefill_dilated(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), window_left,
                                             window_right, int(bool(causal)), int(dilation), _ptr(O), _ptr(lse),
                                             _stream(stream)))
+
+
+def bsattn_probe_gather(shape, K, V, blocks, wg_per_pair, depth, checksum, stream=None):
+    """Loads-only gather of the listed blocks' K/V rows (bandwidth ceiling; XOR per thread)."""
+    _check(library().bsattn_probe_gather(ctypes.byref(shape), _ptr(K), _ptr(V), _ptr(blocks),
+                                         int(blocks.shape[-1]), int(wg_per_pair), int(depth), _ptr(checksum),
+                                         _stream(stream)))
 
 
 def default_scale(head_dim):

@@ -38,6 +38,7 @@ EXPORTS = (
     "bsattn_prefill",
     "bsattn_prefill_workspace_bytes",
     "bsattn_prefill_dilated",
+    "bsattn_probe_gather",
     "bsattn_status_string",
     "bsattn_last_error",
     "bsattn_version",
@@ -120,6 +121,8 @@ def load():
     lib.bsattn_prefill_dilated.restype = _st
     lib.bsattn_prefill_workspace_bytes.argtypes = [_pshape, _i32]
     lib.bsattn_prefill_workspace_bytes.restype = ctypes.c_size_t
+    lib.bsattn_probe_gather.argtypes = [_pshape, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp]
+    lib.bsattn_probe_gather.restype = _st
     lib.bsattn_status_string.argtypes = [_st]
     lib.bsattn_status_string.restype = ctypes.c_char_p
     lib.bsattn_last_error.argtypes = []

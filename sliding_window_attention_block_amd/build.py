@@ -25,7 +25,7 @@ LIB = os.path.join(PKG, "libbsattn.so")
 # (source, extra flags): the VALU scorer is compiled once per head dimension and
 # query dtype, so its many instantiations build in parallel
 SOURCES = [("bsattn.cpp", ()), ("summaries.hip", ()), ("select.hip", ()), ("decode.hip", ()),
-           ("prefill.hip", ())] + [
+           ("prefill.hip", ()), ("probe.hip", ())] + [
     ("select_valu.hip", (f"-DBSATTN_VALU_D={d}", f"-DBSATTN_VALU_BF16={bf}")) for d in (64, 128) for bf in (0, 1)]
 ARCH = "gfx950"
 CFLAGS = [

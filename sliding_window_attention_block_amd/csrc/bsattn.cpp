@@ -345,6 +345,36 @@ const char* bsattn_last_error(void) { return g_err; }
 
 const char* bsattn_version(void) { return "bsattn 0.1.0 gfx950"; }
 
+bsattn_status bsattn_probe_gather(const bsattn_shape* shape, const void* K, const void* V, const int32_t* blocks,
+                                  int32_t n_blocks, int32_t wg_per_pair, int32_t depth, uint32_t* checksum,
+                                  void* hip_stream) {
+  g_err[0] = 0;
+  bsattn_status st = check_shape(shape, true);
+  if (st != BSATTN_OK) return st;
+  if (shape->dtype != BSATTN_BF16) return fail(BSATTN_ERR_UNSUPPORTED, "the gather probe reads BF16 caches");
+  if (K == nullptr || V == nullptr || blocks == nullptr || checksum == nullptr)
+    return fail(BSATTN_ERR_INVALID, "K, V, blocks and checksum must be non-NULL");
+  if (shape->kv_capacity < bsattn::kBlock) return fail(BSATTN_ERR_INVALID, "kv_capacity holds no block");
+  if (n_blocks < 1 || n_blocks > bsattn::kMaxBlocks)
+    return fail(BSATTN_ERR_INVALID, "n_blocks must be in [1, %d]", bsattn::kMaxBlocks);
+  if (wg_per_pair < 1 || wg_per_pair > 16) return fail(BSATTN_ERR_INVALID, "wg_per_pair must be in [1, 16]");
+  if (depth < 1 || depth > 4) return fail(BSATTN_ERR_INVALID, "depth must be in [1, 4]");
+  bsattn::ProbeArgs a;
+  a.K = K;
+  a.V = V;
+  a.blocks = blocks;
+  a.checksum = checksum;
+  a.n_pairs = shape->batch * shape->n_kv_heads;
+  a.n_blocks = n_blocks;
+  a.kv_capacity = shape->kv_capacity;
+  a.head_dim = shape->head_dim;
+  a.wg_per_pair = wg_per_pair;
+  a.depth = depth;
+  const hipError_t e = bsattn::launch_gather_probe(a, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return fail(BSATTN_ERR_HIP, "gather probe launch: %s", hipGetErrorString(e));
+  return BSATTN_OK;
+}
+
 }  // extern "C"
 
 namespace {

@@ -223,4 +223,18 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 void prefill_global_geometry(int seq_len, int n_global, int batch, int n_q_heads, int* splits,
                              int* keys_per_split, int* n_wg);
 
+// Gather probe (a measurement aid): loads-only gather of listed K/V blocks, one
+// XOR of the loaded words per thread.  blocks [n_pairs, n_blocks] (entries
+// clamped into the cache), checksum [n_pairs * wg_per_pair * 256].
+struct ProbeArgs {
+  const void* K;
+  const void* V;
+  const int32_t* blocks;
+  uint32_t* checksum;
+  int32_t n_pairs, n_blocks, kv_capacity, head_dim;
+  int32_t wg_per_pair;  // 1 .. 16
+  int32_t depth;        // half blocks in flight per wave, 1 .. 4
+};
+hipError_t launch_gather_probe(const ProbeArgs& a, hipStream_t stream);
+
 }  // namespace bsattn

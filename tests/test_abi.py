@@ -24,7 +24,7 @@ def _header_functions():
 def test_library_exports_every_declared_function():
     lib = api.library()
     declared = _header_functions()
-    assert len(declared) == 16
+    assert len(declared) == 17
     for name in declared:
         assert hasattr(lib, name), name
     assert set(declared) == set(_lib.EXPORTS)
@@ -339,6 +339,23 @@ def test_exact_selector_rejects_bad_arguments():
     assert _status(f, *args(K=FAKE + 8))[0] == 1              # misaligned
     assert _status(f, *args(k=0))[0] == 1
     assert _status(f, *args(nblk=3))[0] == 1
+
+
+def test_gather_probe_rejects_bad_arguments():
+    f = "bsattn_probe_gather"
+    args = lambda **o: [o.get("shape", _shape()), o.get("K", FAKE), FAKE, o.get("blocks", FAKE), o.get("nb", 4),
+                        o.get("wg", 2), o.get("depth", 2), o.get("out", FAKE), None]
+    assert _status(f, *args(shape=_shape(dtype=0)))[0] == 2   # fp32 cache
+    assert _status(f, *args(shape=_shape(head_dim=96)))[0] == 2
+    assert _status(f, *args(K=None))[0] == 1
+    assert _status(f, *args(blocks=None))[0] == 1
+    assert _status(f, *args(out=None))[0] == 1
+    assert _status(f, *args(nb=0))[0] == 1
+    assert _status(f, *args(wg=0))[0] == 1
+    assert _status(f, *args(wg=17))[0] == 1
+    assert _status(f, *args(depth=0))[0] == 1
+    st, msg = _status(f, *args(depth=5))
+    assert st == 1 and "depth" in msg
 
 
 def test_a_missing_library_raises_instead_of_falling_back(tmp_path, monkeypatch):
