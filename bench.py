@@ -46,9 +46,9 @@ CALIB_BYTES = 512 << 20    # the plain device copy --calibrate-copy runs (bytes 
 # calibration copy: FETCH x 1.9999, WRITE x 1.0), summed over the step's
 # launches.  Valid only for the sources they were taken on (their SHA-256);
 # otherwise traffic is null.
-STEP_TRAFFIC = {"sources_sha256": "53866fdb25f77516b981d289b911673408243404e27de0c18945f71e89bb6267",
-                "bytes_per_step": {"first_order_decode_32k": 124026735,
-                                   "cobs_decode_128k": 91443672}}
+STEP_TRAFFIC = {"sources_sha256": "08bca70963c39e4522aa5bea831f1d0ef6f6515e34297d98006a7e3138dab6b5",
+                "bytes_per_step": {"first_order_decode_32k": 124026095,
+                                   "cobs_decode_128k": 91443249}}
 STEP_SOURCES = ("sliding_window_attention_block_amd/csrc/decode.hip",
                 "sliding_window_attention_block_amd/csrc/select.hip",
                 "sliding_window_attention_block_amd/csrc/bsattn.cpp",
@@ -72,10 +72,10 @@ def step_traffic(name=None):
 # HBM bytes per call of the prefill kernels (rocprofv3 --pmc FETCH_SIZE and
 # WRITE_SIZE, calibrated as above, summed over the call's launches), keyed by
 # workload; valid only for the sources they were taken on, otherwise null.
-PREFILL_TRAFFIC = {"sources_sha256": "d116dcf687d3fcc093e59cc1c8eab3c980d450a203da27278737bc555e5e7d1f",
-                   "bytes_per_call": {"swa_prefill_8k": 280283319,
-                                      "local_global_prefill_16k": 436002267,
-                                      "sparse_prefill_8k": 285974525}}
+PREFILL_TRAFFIC = {"sources_sha256": "5f865d7a316179da7fcd7c719d6da3b1cbc5f952944215f2c3b55fe0af296c83",
+                   "bytes_per_call": {"swa_prefill_8k": 280401493,
+                                      "local_global_prefill_16k": 437721606,
+                                      "sparse_prefill_8k": 285975597}}
 PREFILL_SOURCES = ("sliding_window_attention_block_amd/csrc/prefill.hip",
                    "sliding_window_attention_block_amd/csrc/select.hip",
                    "sliding_window_attention_block_amd/csrc/summaries.hip",
