@@ -72,10 +72,10 @@ def step_traffic(name=None):
 # HBM bytes per call of the prefill kernels (rocprofv3 --pmc FETCH_SIZE and
 # WRITE_SIZE, calibrated as above, summed over the call's launches), keyed by
 # workload; valid only for the sources they were taken on, otherwise null.
-PREFILL_TRAFFIC = {"sources_sha256": "5f865d7a316179da7fcd7c719d6da3b1cbc5f952944215f2c3b55fe0af296c83",
-                   "bytes_per_call": {"swa_prefill_8k": 280401493,
-                                      "local_global_prefill_16k": 437721606,
-                                      "sparse_prefill_8k": 285975597}}
+PREFILL_TRAFFIC = {"sources_sha256": "7a20051507f5dba49b561c35bc66015f36f1bde7b578f1afe27193d6efe10427",
+                   "bytes_per_call": {"swa_prefill_8k": 280375382,
+                                      "local_global_prefill_16k": 559841254,
+                                      "sparse_prefill_8k": 285971194}}
 PREFILL_SOURCES = ("sliding_window_attention_block_amd/csrc/prefill.hip",
                    "sliding_window_attention_block_amd/csrc/select.hip",
                    "sliding_window_attention_block_amd/csrc/summaries.hip",

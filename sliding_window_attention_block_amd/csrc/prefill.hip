@@ -400,8 +400,13 @@ __device__ __forceinline__ float region_b(const uint8_t* vt, const u32x4 (&pop)[
 // r + s x for logical position x), where the dilated mask is the plain band
 // of the logical positions, so every stage is the band kernel's own (no
 // per-element stride test); only the row addressing uses the pitch s d.
+// Occupancy: two workgroups (eight waves) per CU, except local+global at
+// d = 64, which runs its stages one at a time (no software pipeline, one tile
+// of logits live) in at most 128 registers, four workgroups per CU: at
+// d = 64 the softmax outweighs the MFMAs, and four waves per SIMD hide each
+// stage's dependent chain better than one wave's pipeline with three.
 template <int D, bool LG, bool SP = false, bool DIL = false>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, (LG && D == 64) ? 4 : 2) void prefill_kernel(PrefillArgs a) {
   using T = Tile<D>;
   constexpr int LDS_BYTES = 4 * T::BYTES;  // K and V, double buffered
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
@@ -683,11 +688,13 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
       }
     }
   };
-  // Rows that see fewer than 256 keys (the first tiles of a sequence) take the
-  // compensated product; their workgroups run one stage at a time (K and V of
-  // stage s + 1 copied while stage s is computed), which keeps the extra P
-  // registers out of the pipelined loop's budget.
-  auto stages_comp = [&]() {
+  // One stage at a time (K and V of stage s + 1 copied while stage s is
+  // computed): for rows that see fewer than 256 keys (the first tiles of a
+  // sequence), which take the compensated product (CP) and so keep its extra
+  // P registers out of the pipelined loop's budget, and for every local+global
+  // workgroup at d = 64 (one tile of logits live: four waves per SIMD).
+  auto stages_single = [&](auto comp_tag) {
+    constexpr bool CP = decltype(comp_tag)::value;
     if (n_stage == 0) return;
     issue_stage(0, kb[0], vb[0]);
     auto one = [&](int stg, int cur) {
@@ -697,9 +704,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
       f32x16 sx[2];
       float unused = 0.f;
       u32x4 pop[2][2], plo[2][2];
-      region_a<D, true, true, false>(kb[cur], qop, sx, sx, sl2, 0.f, pop, plo, unused);
+      region_a<D, CP, true, false>(kb[cur], qop, sx, sx, sl2, 0.f, pop, plo, unused);
       mask_stage(stg, sx);
-      float mx = region_b<D, true, false, true>(nullptr, pop, plo, oacc, sx);
+      float mx = region_b<D, CP, false, true>(nullptr, pop, plo, oacc, sx);
       mx = max_halves(mx);
       const float m_cand = mx * sl2;
       const bool need = m_cand > st.m + kHeadroom;
@@ -712,9 +719,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
         st.m = m_new;
       }
       float psum = 0.f;
-      region_a<D, true, false, true>(nullptr, qop, sx, sx, sl2, (st.m == -INFINITY) ? 0.f : -st.m, pop, plo, psum);
+      region_a<D, CP, false, true>(nullptr, qop, sx, sx, sl2, (st.m == -INFINITY) ? 0.f : -st.m, pop, plo, psum);
       st.l += psum;
-      region_b<D, true, true, false>(vb[cur], pop, plo, oacc, sx);
+      region_b<D, CP, true, false>(vb[cur], pop, plo, oacc, sx);
     };
     int stg = 0;
     for (; stg + 1 < n_stage; stg += 2) {
@@ -793,7 +800,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
       last(sA, vb[0]);
     }
   };
-  if (comp) stages_comp();
+  if (comp) stages_single(std::true_type{});
+  else if constexpr (LG && D == 64) stages_single(std::false_type{});
   else stages();
   // write rows (global rows are written by the merge of their split partials)
   st.l = sum_halves(st.l);
