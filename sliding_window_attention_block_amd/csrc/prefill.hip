@@ -276,11 +276,13 @@ __device__ __forceinline__ void stage(const uint8_t* kt, const uint8_t* vt, cons
 #define BSATTN_SGB(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
 constexpr int kSgMfma = 0x008, kSgValu = 0x002, kSgDsRead = 0x100;
 
-// Region A.  QK: sn = K Q^T from the K tile kt (both 32-key halves).  Always:
+// Region A.  QK: sn = K Q^T from the K tile kt (its first NH 32-key halves:
+// both, or the first alone for a gathered-column stage whose second half is
+// padding).  Always:
 // P of the stage held in s (logits, log2 domain after the fold of sl2 into the
 // exponent's argument): bf16 hi parts in pop (lo parts in plo when COMP) and
 // the row sums of what the P.V product will see, added to psum.
-template <int D, bool COMP, bool QK, bool EXP>
+template <int D, bool COMP, bool QK, bool EXP, int NH = 2>
 __device__ __forceinline__ void region_a(const uint8_t* kt, const u32x4* qop, f32x16 (&sn)[2], const f32x16 (&s)[2],
                                          float sl2, float nm, u32x4 (&pop)[2][2], u32x4 (&plo)[2][2], float& psum) {
   using T = Tile<D>;
@@ -288,20 +290,20 @@ __device__ __forceinline__ void region_a(const uint8_t* kt, const u32x4* qop, f3
   const int r32 = lane & 31, h2 = lane >> 5;
   if constexpr (QK) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < NH; ++u)
 #pragma unroll
       for (int e = 0; e < 16; ++e) sn[u][e] = 0.f;
 #pragma unroll
     for (int c = 0; c < D / 16; ++c)
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < NH; ++u) {
         const u32x4 k = *reinterpret_cast<const u32x4*>(kt + T::k_off(32 * u + r32, 2 * c + h2));
         sn[u] = mfma32x32x16(as_bf16x8(k), as_bf16x8(qop[c]), sn[u]);
       }
   }
   if constexpr (EXP) {
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int u = 0; u < NH; ++u)
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
@@ -334,7 +336,7 @@ __device__ __forceinline__ void region_a(const uint8_t* kt, const u32x4* qop, f3
     // the weights are needed here: otherwise the compiler sinks their
     // computation below the next stage's (branchy) mask, out of this region
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < NH; ++u)
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
         asm volatile("" ::"v"(pop[u][kc]));
@@ -346,7 +348,7 @@ __device__ __forceinline__ void region_a(const uint8_t* kt, const u32x4* qop, f3
 
 // Region B.  O += V P from the V tile vt (P in pop, plo); when MX, the per-lane
 // max of sn over both halves (the caller combines the wave's two lane halves).
-template <int D, bool COMP, bool PV, bool MX>
+template <int D, bool COMP, bool PV, bool MX, int NH = 2>
 __device__ __forceinline__ float region_b(const uint8_t* vt, const u32x4 (&pop)[2][2], const u32x4 (&plo)[2][2],
                                           f32x16* oacc, const f32x16 (&sn)[2]) {
   using T = Tile<D>;
@@ -354,7 +356,7 @@ __device__ __forceinline__ float region_b(const uint8_t* vt, const u32x4 (&pop)[
   const int h2 = lane >> 5, q16 = lane >> 4, a16 = lane & 15;
   if constexpr (PV) {
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int u = 0; u < NH; ++u)
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -371,7 +373,7 @@ __device__ __forceinline__ float region_b(const uint8_t* vt, const u32x4 (&pop)[
   float mx = -INFINITY;
   if constexpr (MX) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < NH; ++u)
 #pragma unroll
       for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sn[u][e]);
   }
@@ -634,7 +636,7 @@ __global__ __launch_bounds__(256, (LG && D == 64) ? 4 : 2) void prefill_kernel(P
   // slot, of its first row); the words of allowed-key bits are built only for
   // the edge halves.  An element is kept by two ALU ops: a signed one-bit field
   // extract (0 or all ones) selects, bitwise, between the logit and -inf.
-  auto mask_stage = [&](int stg, f32x16(&sx)[2]) {
+  auto mask_stage = [&](int stg, f32x16(&sx)[2], int nh = 2) {
     int jb, lo = 0, hi;
     uint32_t masked = 0;
     uint64_t gbits = 0ull;
@@ -673,7 +675,7 @@ __global__ __launch_bounds__(256, (LG && D == 64) ? 4 : 2) void prefill_kernel(P
     if (!masked) return;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      if ((masked >> u) & 1u) {
+      if (u < nh && ((masked >> u) & 1u)) {
         const int j0 = jb + 32 * u;
         const uint32_t m = (range_bits32(lo - j0, hi - j0) | (uint32_t)(gbits >> (32 * u))) >> (4 * h2);
 #pragma unroll
@@ -697,16 +699,15 @@ __global__ __launch_bounds__(256, (LG && D == 64) ? 4 : 2) void prefill_kernel(P
     constexpr bool CP = decltype(comp_tag)::value;
     if (n_stage == 0) return;
     issue_stage(0, kb[0], vb[0]);
-    auto one = [&](int stg, int cur) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's copies for `stg` landed
-      __syncthreads();  // every wave's copies landed; every wave is done with the other buffer
-      if (stg + 1 < n_stage) issue_stage(stg + 1, kb[cur ^ 1], vb[cur ^ 1]);
+    // stage stg from the tiles kb[cur], vb[cur]: its first NH 32-key halves
+    auto body = [&](int stg, int cur, auto nh_tag) {
+      constexpr int NH = decltype(nh_tag)::value;
       f32x16 sx[2];
       float unused = 0.f;
       u32x4 pop[2][2], plo[2][2];
-      region_a<D, CP, true, false>(kb[cur], qop, sx, sx, sl2, 0.f, pop, plo, unused);
-      mask_stage(stg, sx);
-      float mx = region_b<D, CP, false, true>(nullptr, pop, plo, oacc, sx);
+      region_a<D, CP, true, false, NH>(kb[cur], qop, sx, sx, sl2, 0.f, pop, plo, unused);
+      mask_stage(stg, sx, NH);
+      float mx = region_b<D, CP, false, true, NH>(nullptr, pop, plo, oacc, sx);
       mx = max_halves(mx);
       const float m_cand = mx * sl2;
       const bool need = m_cand > st.m + kHeadroom;
@@ -719,16 +720,36 @@ __global__ __launch_bounds__(256, (LG && D == 64) ? 4 : 2) void prefill_kernel(P
         st.m = m_new;
       }
       float psum = 0.f;
-      region_a<D, CP, false, true>(nullptr, qop, sx, sx, sl2, (st.m == -INFINITY) ? 0.f : -st.m, pop, plo, psum);
+      region_a<D, CP, false, true, NH>(nullptr, qop, sx, sx, sl2, (st.m == -INFINITY) ? 0.f : -st.m, pop, plo,
+                                      psum);
       st.l += psum;
-      region_b<D, CP, true, false>(vb[cur], pop, plo, oacc, sx);
+      region_b<D, CP, true, false, NH>(vb[cur], pop, plo, oacc, sx);
     };
+    auto one = [&](int stg, int cur, auto nh_tag) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's copies for `stg` landed
+      __syncthreads();  // every wave's copies landed; every wave is done with the other buffer
+      if (stg + 1 < n_stage) issue_stage(stg + 1, kb[cur ^ 1], vb[cur ^ 1]);
+      body(stg, cur, nh_tag);
+    };
+    constexpr std::integral_constant<int, 2> kBoth{};
+    // The last stage, when it is a gathered global-column stage holding at
+    // most 32 columns, has a second half of padding for every row: the
+    // workgroup computes its first half alone (after the loop, so the loop
+    // body keeps one shape)
+    const int last = n_stage - 1;
+    const bool last_half = LG && last - nx >= n_band && (last - nx - n_band) * BN + 32 >= ngc;
+    const int n_loop = last_half ? last : n_stage;
     int stg = 0;
-    for (; stg + 1 < n_stage; stg += 2) {
-      one(stg, 0);
-      one(stg + 1, 1);
+    for (; stg + 1 < n_loop; stg += 2) {
+      one(stg, 0, kBoth);
+      one(stg + 1, 1, kBoth);
     }
-    if (stg < n_stage) one(stg, 0);
+    if (stg < n_loop) one(stg, 0, kBoth);
+    if (last_half) {
+      constexpr std::integral_constant<int, 1> kFirst{};
+      if (last & 1) one(last, 1, kFirst);
+      else one(last, 0, kFirst);
+    }
   };
   auto stages = [&]() {
     constexpr bool COMP = false;
