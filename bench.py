@@ -72,10 +72,10 @@ def step_traffic(name=None):
 # HBM bytes per call of the prefill kernels (rocprofv3 --pmc FETCH_SIZE and
 # WRITE_SIZE, calibrated as above, summed over the call's launches), keyed by
 # workload; valid only for the sources they were taken on, otherwise null.
-PREFILL_TRAFFIC = {"sources_sha256": "7a20051507f5dba49b561c35bc66015f36f1bde7b578f1afe27193d6efe10427",
-                   "bytes_per_call": {"swa_prefill_8k": 280375382,
-                                      "local_global_prefill_16k": 559841254,
-                                      "sparse_prefill_8k": 285971194}}
+PREFILL_TRAFFIC = {"sources_sha256": "c7ff5f337b2778f35ef3eb96bdef7d81c527dc95222c3ec0bb9e8cea5a39cb28",
+                   "bytes_per_call": {"swa_prefill_8k": 280507780,
+                                      "local_global_prefill_16k": 561940875,
+                                      "sparse_prefill_8k": 285965869}}
 PREFILL_SOURCES = ("sliding_window_attention_block_amd/csrc/prefill.hip",
                    "sliding_window_attention_block_amd/csrc/select.hip",
                    "sliding_window_attention_block_amd/csrc/summaries.hip",
