@@ -593,8 +593,22 @@ bsattn_status bsattn_decode_step(const bsattn_shape* shape, const void* Q, const
   // first order with bfloat16 means: the decode workgroups score the blocks
   // themselves (one launch, plus the merge when a pair has several workgroups)
   const bool scored_in_decode = fused && sa.rank == 0 && sa.mean_bf16;
+  // a small fp32 step (first order, fp32 means, at most 256 complete blocks
+  // and 16 items per pair): one decode workgroup per pair scores, selects and
+  // attends, and writes O itself (one launch, no merge)
+  const bool fused_f32 = !da.bf16 && sa.rank == 0 && !sa.mean_bf16 && nb >= 1 &&
+                         nb <= 64 * bsattn::kDecodeWaves && top_k <= bsattn::kFusedMaxTopK &&
+                         da.n_items <= 4 * bsattn::kDecodeWaves;
   hipError_t e = hipSuccess;
-  if (scored_in_decode) {
+  if (fused_f32) {
+    da.mean = mean;
+    da.scores_out = scores;
+    da.sel_out = sel;
+    da.nblk_capacity = nblk_capacity;
+    da.n_part = 1;
+    da.n_merge = 1;
+    da.per_wave = (da.n_items + bsattn::kDecodeWaves - 1) / bsattn::kDecodeWaves;
+  } else if (scored_in_decode) {
     da.mean = mean;
     da.scores_out = scores;
   } else {

@@ -915,7 +915,14 @@ __global__ __launch_bounds__(64 * kW, D == 128 ? 1 : 2) void decode_bf16_kernel(
 }
 
 // fp32 K/V: one token per lane, VALU dot products.  GM >= G is the padded group size.
-template <int D, int GM>
+// FUSED (the one-call step on a small fp32 problem, one workgroup per pair):
+// the workgroup first scores its pair's complete blocks from the fp32 means,
+// one block per thread (the selector's first-order score, COBS explainer
+// technical summary sections 2.1-2.2: the group log-sum-exp of the scaled
+// q . mean), writes them to scores_out, and takes the top-k itself (wg_topk:
+// score descending, then block index ascending, the top-k kernel's order),
+// which it writes to sel_out and attends.
+template <int D, int GM, bool FUSED = false>
 __global__ __launch_bounds__(64 * kW) void decode_f32_kernel(DecodeArgs a) {
   constexpr int DL = D / 64;  // output dims per lane
   __shared__ __attribute__((aligned(16))) float qs[GM][D];
@@ -928,12 +935,52 @@ __global__ __launch_bounds__(64 * kW) void decode_f32_kernel(DecodeArgs a) {
   const int G = a.n_q_heads / a.n_kv_heads;
   const float* Kb = reinterpret_cast<const float*>(a.K) + (size_t)bh * a.kv_capacity * D;
   const float* Vb = reinterpret_cast<const float*>(a.V) + (size_t)bh * a.kv_capacity * D;
-  for (int i = tid; i < a.top_k; i += 64 * kW) s_sel[i] = a.sel[(size_t)bh * a.top_k + i];
+  if constexpr (!FUSED)
+    for (int i = tid; i < a.top_k; i += 64 * kW) s_sel[i] = a.sel[(size_t)bh * a.top_k + i];
   const float sl2 = a.scale * kLog2e;
   for (int i = tid; i < GM * D; i += 64 * kW)
     qs[i / D][i % D] =
         (i / D < G) ? reinterpret_cast<const float*>(a.Q)[((size_t)b * a.n_q_heads + g * G) * D + i] : 0.f;
   __syncthreads();
+  if constexpr (FUSED) {
+    __shared__ WgTopkLds wl;
+    const int NB = a.forced.n_ctx / kBlock;  // <= 64 * kW (host check)
+    const int j = tid;
+    uint32_t key[1] = {0u};
+    if (j < NB) {
+      const float4* mr =
+          reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.mean) + ((size_t)bh * a.nblk_capacity + j) * D);
+      float4 mv[D / 4];
+#pragma unroll
+      for (int c = 0; c < D / 4; ++c) mv[c] = mr[c];
+      float sc[GM];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int hh = 0; hh < GM; ++hh) {
+        float acc = 0.f;
+#pragma unroll
+        for (int c = 0; c < D / 4; ++c) {
+          const float4 q4 = reinterpret_cast<const float4*>(qs[hh])[c];
+          acc = fmaf(mv[c].x, q4.x, acc);
+          acc = fmaf(mv[c].y, q4.y, acc);
+          acc = fmaf(mv[c].z, q4.z, acc);
+          acc = fmaf(mv[c].w, q4.w, acc);
+        }
+        sc[hh] = acc * a.scale;
+        if (hh < G) mx = fmaxf(mx, sc[hh]);
+      }
+      float sum = 0.f;
+#pragma unroll
+      for (int hh = 0; hh < GM; ++hh)
+        if (hh < G) sum += __builtin_amdgcn_exp2f((sc[hh] - mx) * kLog2e);
+      // sum >= 1 (the max term is exactly 1): log2 needs no range care
+      const float score = fmaf(__builtin_amdgcn_logf(sum), kLn2, mx);
+      if (a.scores_out != nullptr) a.scores_out[(size_t)bh * a.nblk_capacity + j] = score;
+      key[0] = order_key(score);
+    }
+    wg_topk<1>(a, key, min(j, NB), min(j + 1, NB), wl, s_sel);  // ends at a barrier
+    for (int i = tid; i < a.top_k; i += 64 * kW) a.sel_out[(size_t)bh * a.top_k + i] = s_sel[i];
+  }
   float m_run[GM], l_run[GM], o[GM][DL];
 #pragma unroll
   for (int hh = 0; hh < GM; ++hh) {
@@ -950,11 +997,26 @@ __global__ __launch_bounds__(64 * kW) void decode_f32_kernel(DecodeArgs a) {
     if (inf.blk < 0) continue;
     const bool on = (inf.mask >> lane) & 1ull;
     // this lane's K row, loaded once (whole row in flight), then one dot
-    // product per query head from registers
+    // product per query head from registers; at d = 64 the item's 64 V rows
+    // are loaded with it (V does not wait for the weights), so an item costs
+    // one round trip to memory (at d = 128 the K row alone takes 128 registers
+    // and V follows the weights, 16 rows at a time)
     const float4* kr = reinterpret_cast<const float4*>(Kb + (size_t)min(inf.blk * kBlock + lane, last) * D);
     float4 kv[D / 4];
 #pragma unroll
     for (int c = 0; c < D / 4; ++c) kv[c] = kr[c];
+    constexpr bool EARLY_V = D == 64;
+    constexpr int VB = EARLY_V ? 64 : 16;  // V rows per batch: 64 / 32 registers
+    float vv[VB][DL];
+    auto load_v = [&](int t0) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < VB; ++u) {
+        const float* vr = Vb + (size_t)min(inf.blk * kBlock + t0 + u, last) * D;
+#pragma unroll
+        for (int e = 0; e < DL; ++e) vv[u][e] = vr[lane + 64 * e];
+      }
+    };
+    if constexpr (EARLY_V) load_v(0);
 #pragma unroll
     for (int hh = 0; hh < GM; ++hh) {
       if (hh >= G) break;
@@ -980,19 +1042,13 @@ __global__ __launch_bounds__(64 * kW) void decode_f32_kernel(DecodeArgs a) {
       ps[wid][hh][lane] = p;
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    // O += P V over the block's 64 rows, 16 rows at a time with the batch's
-    // loads in flight together (a masked token's weight is 0)
+    // O += P V over the block's 64 rows, VB rows at a time (a masked token's
+    // weight is 0)
 #pragma unroll
-    for (int t0 = 0; t0 < 64; t0 += 16) {
-      float vv[16][DL];
+    for (int t0 = 0; t0 < 64; t0 += VB) {
+      if (!EARLY_V || t0 > 0) load_v(t0);
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const float* vr = Vb + (size_t)min(inf.blk * kBlock + t0 + u, last) * D;
-#pragma unroll
-        for (int e = 0; e < DL; ++e) vv[u][e] = vr[lane + 64 * e];
-      }
-#pragma unroll
-      for (int u = 0; u < 16; ++u)
+      for (int u = 0; u < VB; ++u)
 #pragma unroll
         for (int e = 0; e < DL; ++e)
 #pragma unroll
@@ -1084,12 +1140,17 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
     }
   } else {
     const dim3 grid(a.n_part, n_pairs);
-    if (G <= 4)
-      hipLaunchKernelGGL((decode_f32_kernel<D, 4>), grid, dim3(64 * kW), 0, stream, a);
-    else if (G <= 8)
-      hipLaunchKernelGGL((decode_f32_kernel<D, 8>), grid, dim3(64 * kW), 0, stream, a);
-    else
-      hipLaunchKernelGGL((decode_f32_kernel<D, 16>), grid, dim3(64 * kW), 0, stream, a);
+    const bool fz = a.mean != nullptr;  // the fused fp32 step (one workgroup per pair)
+    if (G <= 4) {
+      if (fz) hipLaunchKernelGGL((decode_f32_kernel<D, 4, true>), grid, dim3(64 * kW), 0, stream, a);
+      else hipLaunchKernelGGL((decode_f32_kernel<D, 4>), grid, dim3(64 * kW), 0, stream, a);
+    } else if (G <= 8) {
+      if (fz) hipLaunchKernelGGL((decode_f32_kernel<D, 8, true>), grid, dim3(64 * kW), 0, stream, a);
+      else hipLaunchKernelGGL((decode_f32_kernel<D, 8>), grid, dim3(64 * kW), 0, stream, a);
+    } else {
+      if (fz) hipLaunchKernelGGL((decode_f32_kernel<D, 16, true>), grid, dim3(64 * kW), 0, stream, a);
+      else hipLaunchKernelGGL((decode_f32_kernel<D, 16>), grid, dim3(64 * kW), 0, stream, a);
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_merge == 1) return e;

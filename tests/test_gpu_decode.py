@@ -75,6 +75,13 @@ ONE_CALL_EXTRA = [
     (_w("wg_select_1500_blocks_tail_k256_d64", 2, 4, 2, 64, 1500 * 64 + 33, 0, 256, 64, 64, "bf16", 31), (), 0),
     (_w("fallback_2049_blocks", 1, 4, 1, 64, 2049 * 64, 0, 8, 64, 64, "bf16", 32), (), 0),
     (_w("fallback_k257", 1, 4, 1, 64, 600 * 64, 0, 257, 64, 64, "bf16", 29), (), 0),
+    # fp32, first order, fp32 means: up to 256 complete blocks and 16 items per pair the
+    # step is one decode workgroup per pair that scores, selects and attends
+    (WORKLOADS["tiny_decode_1k"], (), 0),
+    (_w("f32_fused_256_blocks_tail_g16_d128", 1, 16, 1, 128, 256 * 64 + 40, 0, 8, 64, 64, "f32", 33), (), 0),
+    (_w("f32_fused_globals_g8_d64", 2, 16, 2, 64, 5000, 0, 5, 100, 3, "f32", 34), (10, 2500, 4999), 0),
+    (_w("f32_fallback_257_blocks", 1, 4, 1, 64, 257 * 64, 0, 4, 64, 64, "f32", 35), (), 0),
+    (_w("f32_fallback_17_items", 1, 4, 1, 64, 3000, 0, 14, 64, 64, "f32", 36), (), 0),
 ]
 
 
@@ -93,6 +100,21 @@ def test_one_call_step_breaks_ties_by_index(api):
     x = make_decode_inputs(w)
     K = x["K"].copy()
     K[:, :, :] = np.tile(K[:, :, :64], (1, 1, 300, 1))
+    x = dict(x, K=K)
+    two = gpu_decode_step(api, x, w)
+    one = gpu_decode_step(api, x, w, one_call=True)
+    assert np.array_equal(one["sel"][0, 0], np.arange(1, 8)), one["sel"][0, 0]
+    assert np.array_equal(two["sel"], one["sel"])
+    assert max_abs(two["O"], one["O"]) < 1e-5
+
+
+def test_fp32_one_call_step_breaks_ties_by_index(api):
+    """The fused fp32 step (one workgroup per pair scores and selects): with every
+    candidate's score tied it takes the lowest-index candidates, as the top-k kernel."""
+    w = _w("all_ties_f32", 1, 4, 1, 64, 64 * 200, 0, 7, 64, 64, "f32", 37)
+    x = make_decode_inputs(w)
+    K = x["K"].copy()
+    K[:, :, :] = np.tile(K[:, :, :64], (1, 1, 200, 1))
     x = dict(x, K=K)
     two = gpu_decode_step(api, x, w)
     one = gpu_decode_step(api, x, w, one_call=True)
