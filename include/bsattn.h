@@ -255,7 +255,12 @@ bsattn_status bsattn_decode(const bsattn_shape* shape, const void* Q, const void
  * the two calls; the selection is the same exact top-k (score descending,
  * then block index ascending).  With at most 512 blocks, rank == 0 and BF16
  * means, the decode workgroups also compute the scores (the same products and
- * sums as the scoring kernel), so the step has no scoring launch.  Otherwise the step runs the two calls' kernels.  Calls
+ * sums as the scoring kernel), so the step has no scoring launch.  With FP32
+ * K/V, rank == 0, FP32 means, at most 256 complete blocks and at most 16
+ * items per pair (top_k plus the blocks holding forced tokens), the step is
+ * one launch: one decode workgroup per (b, K/V head) scores the blocks,
+ * selects (the same exact order) and attends, and writes O itself.
+ * Otherwise the step runs the two calls' kernels.  Calls
  * that share a workspace must be ordered (same stream).
  */
 bsattn_status bsattn_decode_step(const bsattn_shape* shape, const void* Q, const void* K,
