@@ -46,9 +46,9 @@ CALIB_BYTES = 512 << 20    # the plain device copy --calibrate-copy runs (bytes 
 # calibration copy: FETCH x 1.9999, WRITE x 1.0), summed over the step's
 # launches.  Valid only for the sources they were taken on (their SHA-256);
 # otherwise traffic is null.
-STEP_TRAFFIC = {"sources_sha256": "08bca70963c39e4522aa5bea831f1d0ef6f6515e34297d98006a7e3138dab6b5",
-                "bytes_per_step": {"first_order_decode_32k": 124026095,
-                                   "cobs_decode_128k": 91443249}}
+STEP_TRAFFIC = {"sources_sha256": "45cf49a237957ceb282fa31596d2c8a622e5f6b5fd73d16ad28ddab6d6927520",
+                "bytes_per_step": {"first_order_decode_32k": 124020156,
+                                   "cobs_decode_128k": 91439870}}
 STEP_SOURCES = ("sliding_window_attention_block_amd/csrc/decode.hip",
                 "sliding_window_attention_block_amd/csrc/select.hip",
                 "sliding_window_attention_block_amd/csrc/bsattn.cpp",
@@ -72,10 +72,10 @@ def step_traffic(name=None):
 # HBM bytes per call of the prefill kernels (rocprofv3 --pmc FETCH_SIZE and
 # WRITE_SIZE, calibrated as above, summed over the call's launches), keyed by
 # workload; valid only for the sources they were taken on, otherwise null.
-PREFILL_TRAFFIC = {"sources_sha256": "c7ff5f337b2778f35ef3eb96bdef7d81c527dc95222c3ec0bb9e8cea5a39cb28",
-                   "bytes_per_call": {"swa_prefill_8k": 280507780,
-                                      "local_global_prefill_16k": 561940875,
-                                      "sparse_prefill_8k": 285965869}}
+PREFILL_TRAFFIC = {"sources_sha256": "5673afc19e58880636df07ec08e5d27dac4c02920cd92005ae02d3cda8437953",
+                   "bytes_per_call": {"swa_prefill_8k": 280444601,
+                                      "local_global_prefill_16k": 562533642,
+                                      "sparse_prefill_8k": 285985836}}
 PREFILL_SOURCES = ("sliding_window_attention_block_amd/csrc/prefill.hip",
                    "sliding_window_attention_block_amd/csrc/select.hip",
                    "sliding_window_attention_block_amd/csrc/summaries.hip",
