@@ -59,7 +59,7 @@ extern "C" {
 typedef enum {
   BSATTN_OK = 0,
   BSATTN_ERR_INVALID = 1,     /* argument out of range, NULL, inconsistent shape  */
-  BSATTN_ERR_UNSUPPORTED = 2, /* valid request this build does not implement       */
+  BSATTN_ERR_UNSUPPORTED = 2, /* valid request the library does not implement      */
   BSATTN_ERR_HIP = 3,         /* a HIP launch or runtime call failed               */
   BSATTN_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required        */
   BSATTN_STATUS_INT32 = 0x7fffffff /* not a status: keeps every int32 value in range */
@@ -387,7 +387,7 @@ bsattn_status bsattn_sparse_prefill(const bsattn_shape* shape, const void* Q, co
 /*
  * Gather probe, a measurement aid rather than a step of the method: the HBM
  * bandwidth a loads-only gather of K/V blocks reaches, the ceiling against
- * which the sparse decode's gathered bytes are judged (decode is bound by the
+ * which the sparse decode's gathered bytes are compared (decode is bound by the
  * KV bytes it reads [COBS 1]).  For every (b, K/V head) pair p = b * Hkv + g it
  * reads the K and V rows of the blocks blocks[p, 0 .. n_blocks - 1] (device
  * int32 [B * Hkv, n_blocks]; each entry is clamped into [0, kv_capacity / 64),
