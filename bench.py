@@ -265,6 +265,45 @@ def bench_gather_probe(api, torch, w, reps, shape, steps, R):
     return out
 
 
+def gather_chunk_sweep(api, torch, w, steps):
+    """The gather probe's rate against the contiguous chunk size: 24 blocks per
+    (b, K/V head) pair of the workload's shape listed as runs of 1, 2, 4 or 8
+    adjacent blocks at random places (16 to 128 KB contiguous K and V reads at
+    d = 128), over 6 rotating replicas of N(0,1) bf16 caches, each setting one
+    captured graph of `steps` launches timed with HIP events."""
+    B, Hq, Hkv, d, n = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_ctx
+    R, nbl, nb = 6, 24, n // 64
+    shape = api.make_shape(B, Hq, Hkv, d, n, dtype="bf16")
+    reps = [(torch.randn(B, Hkv, n, d, device="cuda").to(torch.bfloat16),
+             torch.randn(B, Hkv, n, d, device="cuda").to(torch.bfloat16)) for _ in range(R)]
+    rng = np.random.default_rng(0)
+    nbytes = B * Hkv * nbl * 64 * d * 2 * 2
+    out = {"bytes_per_launch": nbytes}
+    for run in (1, 2, 4, 8):
+        rows = []
+        for _ in range(B * Hkv):
+            starts = rng.choice(nb // run, size=nbl // run, replace=False) * run
+            rows.append(np.concatenate([np.arange(st, st + run) for st in sorted(starts)]))
+        blocks = torch.from_numpy(np.asarray(rows, dtype=np.int32)).cuda()
+        for wg, depth in ((2, 2), (2, 4)):
+            cks = torch.empty(B * Hkv * wg * 256, dtype=torch.int32, device="cuda")
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(steps):
+                    api.bsattn_probe_gather(shape, reps[i % R][0], reps[i % R][1], blocks, wg, depth, cks)
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+            out[f"chunk_{16 * run}KB_wg{wg}_depth{depth}"] = dict(us=ms * 1e3, GBps=nbytes / (ms * 1e-3) / 1e9)
+            del g
+    return out
+
+
 def bench_decode(api, torch, w, x, steps, warmup, mean_dtype="bf16", factor_fp4=True, subspace=True,
                  page_tokens=None, append_rows=False, replicas=None, gather_probe=False):
     B, Hq, Hkv, d, n, S = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_ctx, w.block_size
@@ -732,6 +771,9 @@ def main():
     ap.add_argument("--no-context", action="store_true",
                     help="time each workload's own row only (no fp32, paged, exact-selector or append "
                          "context rows): for profiler runs")
+    ap.add_argument("--gather-chunks", action="store_true",
+                    help="only the gather probe's rate against the contiguous chunk size on the headline "
+                         "workload's shape (runs of 1, 2, 4, 8 adjacent blocks); prints its result")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 512 MiB device-to-device copy three times (the "
                          "reference dispatch for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -750,6 +792,10 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     api.library()
+    if args.gather_chunks:
+        print(json.dumps({"workload": HEADLINE, "gather_chunk_sweep":
+                          gather_chunk_sweep(api, torch, WORKLOADS[HEADLINE], args.steps)}))
+        return
     if args.calibrate_copy:
         src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
