@@ -266,11 +266,12 @@ def bench_gather_probe(api, torch, w, reps, shape, steps, R):
 
 
 def gather_chunk_sweep(api, torch, w, steps):
-    """The gather probe's rate against the contiguous chunk size: 24 blocks per
-    (b, K/V head) pair of the workload's shape listed as runs of 1, 2, 4 or 8
-    adjacent blocks at random places (16 to 128 KB contiguous K and V reads at
-    d = 128), over 6 rotating replicas of N(0,1) bf16 caches, each setting one
-    captured graph of `steps` launches timed with HIP events."""
+    """The gather probe's rate against the contiguous chunk size and against the
+    waves per pair: 24 blocks per (b, K/V head) pair of the workload's shape
+    listed as runs of 1, 2, 4 or 8 adjacent blocks at random places (16 to 128
+    KB contiguous K and V reads at d = 128), then single blocks read by 1 to 16
+    workgroups per pair; over 6 rotating replicas of N(0,1) bf16 caches, each
+    setting one captured graph of `steps` launches timed with HIP events."""
     B, Hq, Hkv, d, n = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.n_ctx
     R, nbl, nb = 6, 24, n // 64
     shape = api.make_shape(B, Hq, Hkv, d, n, dtype="bf16")
@@ -279,13 +280,15 @@ def gather_chunk_sweep(api, torch, w, steps):
     rng = np.random.default_rng(0)
     nbytes = B * Hkv * nbl * 64 * d * 2 * 2
     out = {"bytes_per_launch": nbytes}
+    settings = [(run, wg, depth) for run in (1, 2, 4, 8) for wg, depth in ((2, 2), (2, 4))]
+    settings += [(1, wg, 2) for wg in (1, 4, 6, 12, 16)]
     for run in (1, 2, 4, 8):
         rows = []
         for _ in range(B * Hkv):
             starts = rng.choice(nb // run, size=nbl // run, replace=False) * run
             rows.append(np.concatenate([np.arange(st, st + run) for st in sorted(starts)]))
         blocks = torch.from_numpy(np.asarray(rows, dtype=np.int32)).cuda()
-        for wg, depth in ((2, 2), (2, 4)):
+        for wg, depth in [(wg, dp) for r, wg, dp in settings if r == run]:
             cks = torch.empty(B * Hkv * wg * 256, dtype=torch.int32, device="cuda")
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
