@@ -824,11 +824,12 @@ def main():
         elif decode:
             results[name] = bench_decode(api, torch, w, x, args.steps, args.warmup, append_rows=True,
                                          gather_probe=name == HEADLINE)
-            if name == HEADLINE:  # context: fp32 block means; a paged cache of 4 KB pages
+            if name == HEADLINE:  # context: fp32 block means; paged caches of 4 to 16 KB pages
                 results[name + "/fp32_means"] = bench_decode(api, torch, w, x, args.steps, args.warmup,
                                                              mean_dtype="f32")
-                results[name + "/paged16"] = bench_decode(api, torch, w, x, args.steps, args.warmup,
-                                                          page_tokens=16)
+                for pt in (16, 32, 64):  # 4, 8 and 16 KB pages of one K/V head
+                    results[name + f"/paged{pt}"] = bench_decode(api, torch, w, x, args.steps, args.warmup,
+                                                                 page_tokens=pt)
                 # warm: one input replica, so the Infinity Cache keeps most of a step's bytes
                 results[name + "/warm_one_replica"] = bench_decode(api, torch, w, x, args.steps, args.warmup,
                                                                    replicas=1)
