@@ -46,9 +46,9 @@ CALIB_BYTES = 512 << 20    # the plain device copy --calibrate-copy runs (bytes 
 # calibration copy: FETCH x 1.9999, WRITE x 1.0), summed over the step's
 # launches.  Valid only for the sources they were taken on (their SHA-256);
 # otherwise traffic is null.
-STEP_TRAFFIC = {"sources_sha256": "45cf49a237957ceb282fa31596d2c8a622e5f6b5fd73d16ad28ddab6d6927520",
-                "bytes_per_step": {"first_order_decode_32k": 124020156,
-                                   "cobs_decode_128k": 91439870}}
+STEP_TRAFFIC = {"sources_sha256": "3dcfc467e2774249af4dde74abdf60aad24f754f555b1cce8b7f87124472b791",
+                "bytes_per_step": {"first_order_decode_32k": 124015919,
+                                   "cobs_decode_128k": 91442392}}
 STEP_SOURCES = ("sliding_window_attention_block_amd/csrc/decode.hip",
                 "sliding_window_attention_block_amd/csrc/select.hip",
                 "sliding_window_attention_block_amd/csrc/bsattn.cpp",

@@ -1074,8 +1074,8 @@ __global__ __launch_bounds__(64 * kW) void decode_f32_kernel(DecodeArgs a) {
 // Merge the partials of every query head: per dim,
 // O = sum_s w_s o_s / sum_s w_s l_s with w_s = 2^(m_s - M); lse = ln 2 (M + log2 L).
 // One wave per (b, query head); lane owns dims lane + 64e; the partials are read
-// CH at a time (all loads of a chunk in flight together; CH the smallest of 8,
-// 16, 32 that holds them all, else 32) and folded online.
+// CH at a time (all loads of a chunk in flight together; CH the smallest of 2,
+// 4, 8, 16, 32 that holds them all, else 32) and folded online.
 template <int D, int CH>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   constexpr int DL = D / 64;
@@ -1155,7 +1155,9 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_merge == 1) return e;
   const dim3 mg(a.batch * a.n_q_heads), mb(64);
-  if (a.n_merge <= 8) hipLaunchKernelGGL((decode_merge_kernel<D, 8>), mg, mb, 0, stream, a);
+  if (a.n_merge <= 2) hipLaunchKernelGGL((decode_merge_kernel<D, 2>), mg, mb, 0, stream, a);
+  else if (a.n_merge <= 4) hipLaunchKernelGGL((decode_merge_kernel<D, 4>), mg, mb, 0, stream, a);
+  else if (a.n_merge <= 8) hipLaunchKernelGGL((decode_merge_kernel<D, 8>), mg, mb, 0, stream, a);
   else if (a.n_merge <= 16) hipLaunchKernelGGL((decode_merge_kernel<D, 16>), mg, mb, 0, stream, a);
   else hipLaunchKernelGGL((decode_merge_kernel<D, 32>), mg, mb, 0, stream, a);
   return hipGetLastError();
